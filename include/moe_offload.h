@@ -1,0 +1,208 @@
+/*
+ * moe_offload.h - C ABI of libmoe_offload.so, the routed-expert MoE mat-mul
+ * (MUL_MAT_ID) over 4-bit block-quantised expert weights for one MI355X
+ * (gfx950), with hot experts in an HBM pool and cold experts read zero-copy
+ * from pinned host RAM.
+ *
+ * Sources for what each call computes (page titles as published):
+ *  [A6000]  "a6000-custom-kernels" README (Zapdev-labs): the pointer-table
+ *           GEMV diagram and the paragraph under it (one table, pool and stamp
+ *           array per expert tensor; miss recorder packing tensor_id<<12|expert;
+ *           promotion between decode steps on the 2nd sighting; eviction by
+ *           stamp scan; pools seeded from a routing-frequency file; capacity from
+ *           free memory minus a safety margin), and the "-lm none" section
+ *           (cold experts must sit in pinned host buffers to be read zero-copy).
+ *  [FORK]   "llama.cpp: fork with multi gpu acceleration even for models bigger
+ *           than total gpu mem" README, "How it works": admission after repeated
+ *           use within the last 64 tokens; prompt passes stream the experts the
+ *           GPU does not hold and return the borrowed blocks afterwards.
+ *  [MAC]    "llama.cpp - very large MoE models on a 64 GB Mac" README, "Metal
+ *           kernels": MUL_MAT_ID over used (expert, tile) pairs only.
+ *
+ * Conventions for every function:
+ *  - Returns MOE_OK (0) or a negative MOE_E_* code. Nothing aborts, throws or
+ *    prints. moe_last_error(ctx) returns a NUL-terminated message for the last
+ *    failing call on ctx; the string is owned by ctx and valid until the next
+ *    call on ctx.
+ *  - "host" pointers are ordinary CPU pointers; "device" pointers are HIP
+ *    device addresses on the context's device (for example torch.Tensor
+ *    data_ptr() of a cuda tensor). The library never frees caller memory.
+ *  - The library owns the HBM pool, the pinned host arena, the slot tables,
+ *    stamps, the miss log and all scratch; they live until moe_destroy.
+ *  - A context is used by one host thread at a time; calls are not re-entrant.
+ *  - Device work is issued on the context stream (moe_config.stream, or a
+ *    stream the library creates when that is NULL) in call order.
+ *
+ * Weight format (MOE_Q4_32_F16): each matrix row is a run of 18-byte blocks
+ * along the reduction axis; a block is a little-endian IEEE fp16 scale d
+ * followed by 16 bytes qs; element j (0..15) of the block is qs[j] & 0xF and
+ * element j+16 is qs[j] >> 4; the weight is d * (q - 8). This is the Q4_0
+ * layout that [A6000] lists among its dot kernels, with the public GGUF nibble
+ * order. gate and up are [ffn][hidden] (blocks along hidden), down is
+ * [hidden][ffn] (blocks along ffn). hidden and ffn must be multiples of 32.
+ */
+#ifndef MOE_OFFLOAD_H
+#define MOE_OFFLOAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK            0
+#define MOE_E_INVAL      (-1) /* bad argument, shape or call order          */
+#define MOE_E_NOMEM      (-2) /* HBM or pinned host allocation failed        */
+#define MOE_E_HIP        (-3) /* a HIP runtime call failed                   */
+#define MOE_E_STATE      (-4) /* call not allowed in the current state       */
+#define MOE_E_CAPTURING  (-5) /* call not allowed while the stream captures  */
+
+#define MOE_Q4_32_F16     1   /* the only weight format */
+
+#define MOE_ACCUMULATE    1u  /* moe_forward / moe_prefill: y += result      */
+
+/* Pinned host arena flavour (moe_config.host_alloc). */
+#define MOE_HOST_COHERENT     0 /* hipHostMalloc default: fine-grained      */
+#define MOE_HOST_NONCOHERENT  1 /* hipHostMallocNonCoherent: GPU may cache  */
+
+typedef struct moe_ctx moe_ctx;
+
+typedef struct {
+  int32_t n_layers;        /* L >= 1                                          */
+  int32_t n_experts;       /* E, 1..4096 (the miss log keeps e in 12 bits)    */
+  int32_t top_k;           /* k, 1..min(E, 32)                                */
+  int32_t hidden;          /* H, multiple of 32                               */
+  int32_t ffn;             /* F, multiple of 32                               */
+  int32_t quant;           /* MOE_Q4_32_F16                                   */
+  int64_t pool_budget_bytes; /* >= 0: HBM pool budget; < 0: free HBM at create
+                                time minus reserve_bytes. Slots per layer
+                                S = min(E, budget / (L * expert_bytes)).      */
+  int64_t reserve_bytes;   /* HBM left free when pool_budget_bytes < 0        */
+  int32_t window_tokens;   /* admission window in tokens (64 in [FORK])       */
+  int32_t admit_misses;    /* 2: admit on the 2nd miss inside the window
+                              ([A6000] "2nd sighting"); 1: admit every miss  */
+  int32_t max_batch_tokens;   /* largest T for moe_forward, 1..256            */
+  int32_t max_prefill_tokens; /* largest T for moe_prefill (0: no prefill)    */
+  int32_t device;          /* HIP device ordinal                              */
+  int32_t host_alloc;      /* MOE_HOST_COHERENT or MOE_HOST_NONCOHERENT       */
+  void*   stream;          /* hipStream_t to issue on; NULL: library-owned    */
+} moe_config;
+
+typedef struct {
+  int64_t slots_per_layer;    /* S                                            */
+  int64_t expert_bytes;       /* bytes of gate+up+down of one expert          */
+  int64_t pool_bytes;         /* HBM pool size, L * S * expert_bytes          */
+  int64_t host_bytes;         /* pinned arena size, L * E * expert_bytes      */
+  int64_t staging_experts;    /* HBM blocks lent to a prefill pass            */
+  int64_t clock;              /* token clock of the next step (starts at 1)   */
+  int64_t steps;              /* cache steps run since the last seed          */
+} moe_info;
+
+typedef struct {
+  int64_t step;               /* index of the step just closed (0-based)      */
+  int64_t tokens;             /* tokens in that step (clock advance)          */
+  int64_t hits;               /* picks served from the HBM pool               */
+  int64_t misses;             /* picks served from pinned host (log entries)  */
+  int64_t admissions;         /* experts promoted into the pool               */
+  int64_t evictions;          /* resident experts displaced by admissions     */
+  int64_t hot_bytes;          /* expert bytes read from HBM by the step       */
+  int64_t cold_bytes;         /* expert bytes read over PCIe by the step      */
+  int64_t copied_bytes;       /* host->HBM promotion copies issued            */
+} moe_step_stats;
+
+/* Size in bytes of one expert (gate + up + down) in MOE_Q4_32_F16. */
+int64_t moe_expert_bytes(int32_t hidden, int32_t ffn);
+
+/* Create a context. Allocates the HBM pool (pool_budget_bytes, [A6000]
+ * capacity rule), the pinned host arena for L*E experts, prefill staging, the
+ * slot tables (all -1), stamps, the miss log and scratch, all once: no call
+ * below allocates memory. *out is set on success. MOE_E_NOMEM if the pool or
+ * the arena cannot be allocated; MOE_E_INVAL on a bad config. */
+int moe_create(const moe_config* cfg, moe_ctx** out);
+
+/* Release everything the context owns; waits for its stream. NULL is a no-op. */
+int moe_destroy(moe_ctx* ctx);
+
+/* Copy one layer's expert weights into the pinned arena, repacking them into
+ * the device layout. gate, up, down are host pointers to E consecutive
+ * matrices each, in the canonical format above (gate/up: E*F*(H/32) blocks,
+ * down: E*H*(F/32) blocks). The caller may free them on return. Allowed until
+ * moe_seed; MOE_E_STATE afterwards. */
+int moe_register_layer(moe_ctx* ctx, int32_t layer,
+                       const void* gate, const void* up, const void* down);
+
+/* Optional router for one layer: host fp32 [E][H], row e is expert e. With a
+ * router, moe_forward and moe_prefill may take logits == NULL, and logits are
+ * z_e = fmaf chain over j = 0..H-1 of x_j * W[e][j] in fp32, from 0.          */
+int moe_register_router(moe_ctx* ctx, int32_t layer, const float* w_router);
+
+/* Seed the pools and reset the cache policy ([A6000]: pools are seeded from a
+ * routing-frequency table). freq is host uint32 [L][E] or NULL. Per layer the
+ * S experts with the highest count (ties: lower id first) take slots 0..S-1 in
+ * that order; with freq == NULL every slot stays free (cold start). Resets
+ * stamps to 0, the per-expert last-miss times to 0, the miss log, and the token
+ * clock to 1. Requires every layer registered (MOE_E_STATE). Synchronises. */
+int moe_seed(moe_ctx* ctx, const uint32_t* freq);
+
+/* MoE FFN of one layer for a decode batch of n_tokens (1..max_batch_tokens):
+ *   ids, w = top-k softmax routing of logits (device fp32 [T][E], or NULL when
+ *            a router is registered): k largest logits, ties to the lower id,
+ *            in that order; w = softmax over the k chosen logits;
+ *   per pick: the expert is found through the layer's slot table ([A6000]
+ *            pointer table): resident -> its HBM slot, its use-stamp raised to
+ *            the pick's token clock; else -> zero-copy read of pinned host
+ *            memory and an entry (t<<32 | layer<<12 | expert) appended to the
+ *            miss log;
+ *   h = silu(W_gate x) * (W_up x); y_pick = W_down h;
+ *   y[t] (=|+=) sum over picks i = 0..k-1 of w_i * y_pick_i, in pick order.
+ * Token t of the batch carries clock c + t where c is the context clock.
+ * x, y: device fp32 [T][H]; y may equal x only with MOE_ACCUMULATE (residual
+ * update in place). ids (int32 [T][k]) and w (fp32 [T][k]) are optional device
+ * outputs. Asynchronous on the context stream; allocates nothing and may be
+ * captured into a HIP graph. Call it at most once per layer per step. */
+int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
+                const float* x, const float* logits, float* y,
+                int32_t* ids, float* w, uint32_t flags);
+
+/* Prompt pass of one layer for n_tokens (1..max_prefill_tokens): same result
+ * as moe_forward, computed as a grouped GEMM over the tokens sorted by expert
+ * ([MAC]: only (expert, tile) pairs that hold tokens are computed). Experts
+ * the pass touches that are not resident are copied into borrowed HBM staging
+ * blocks for the pass and the blocks are returned at its end ([FORK]). The
+ * cache policy is untouched: no stamps, no miss log, no counts, no clock.
+ * Synchronises the stream; not capturable (MOE_E_CAPTURING). */
+int moe_prefill(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
+                const float* x, const float* logits, float* y, uint32_t flags);
+
+/* Close the current step ([A6000]: promotion pass between decode steps, never
+ * graph-captured). Waits for the stream, reads the miss log, sorts it
+ * ascending, and walks it in that order: an entry whose expert became resident
+ * earlier in this walk is skipped; otherwise, with admit_misses == 2, the
+ * expert is admitted if it missed before at t' with t - t' < window_tokens,
+ * else t is remembered as its last miss ([FORK] window + admission). An
+ * admitted expert takes the lowest free slot, else the slot with the smallest
+ * stamp (ties: highest slot index), whose expert is evicted and forgets its
+ * last miss; the new slot's stamp is t, and the expert forgets its last miss.
+ * Weights are copied pinned -> slot on the stream, tables, stamps and the
+ * clock (advanced by the step's token count) are uploaded, and the log is
+ * cleared. out may be NULL. MOE_E_CAPTURING if the stream is capturing. */
+int moe_cache_step(moe_ctx* ctx, moe_step_stats* out);
+
+/* Introspection (host outputs; each synchronises the stream). */
+int moe_get_info(moe_ctx* ctx, moe_info* out);
+/* int32 [E]: slot of each expert of the layer, -1 when not resident. */
+int moe_get_slot_table(moe_ctx* ctx, int32_t layer, int32_t* out);
+/* uint32 [S]: use-stamps of the layer's slots. */
+int moe_get_stamps(moe_ctx* ctx, int32_t layer, uint32_t* out);
+/* uint64: the miss log of the last closed step, ascending; *n = its length.
+ * Writes min(cap, n) entries. */
+int moe_get_miss_log(moe_ctx* ctx, uint64_t* out, int64_t cap, int64_t* n);
+/* uint32 [L][E]: picks per expert since the last seed (moe_forward only). */
+int moe_get_counts(moe_ctx* ctx, uint32_t* out);
+
+const char* moe_last_error(moe_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_OFFLOAD_H */
