@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the routed-expert MoE layer on one MI355X.
+
+Workload (default): 48 MoE layers of 512 experts, top-8, hidden 2048, expert
+FFN 1024, 4-bit blocks; batch-1 decode over 256 steps with Zipf(1.1) expert
+popularity; an HBM pool of 256 slots per layer (half the experts) seeded from
+a routing-frequency table; cold experts read zero-copy from pinned host RAM;
+the cache step runs between decode steps.
+
+A step is one decode token through all 48 layers (routing, lookup + stamps +
+miss log, gate/up GEMV + SwiGLU, down GEMV + weighted combine, residual in
+place), followed by the host cache step (promotions). The timed region replays
+a HIP graph of the 48-layer forward per step; inputs are resident in HBM.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+PCIE_PEAK_GBPS = 64.0       # PCIe Gen5 x16, one direction
+METRIC = "MoE-layer decode tokens/s + effective weight GB/s vs HBM/PCIe roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def setup_ctx(moe, wl, slots, stream, host_alloc, layers=None, progress=True):
+    from workload import frequency_table, layer_weights
+
+    L = wl.n_layers if layers is None else layers
+    ctx = moe.moe_create(L, wl.n_experts, wl.top_k, wl.hidden, wl.ffn,
+                         pool_budget_bytes=L * slots * wl.expert_bytes, window_tokens=wl.window,
+                         admit_misses=wl.admit_misses, max_batch_tokens=wl.tokens, host_alloc=host_alloc,
+                         host_sets=min(wl.weight_layers, L), stream=stream)
+    buf = None
+    t0 = time.time()
+    for layer in range(min(wl.weight_layers, L)):  # layer l reads host set l % weight_layers
+        buf = layer_weights(wl, layer, out=buf)
+        moe.moe_register_layer(ctx, layer, *buf)
+        if progress and (layer % 8 == 7 or layer == min(wl.weight_layers, L) - 1):
+            log(f"registered host set {layer + 1}/{min(wl.weight_layers, L)} ({time.time() - t0:.1f} s)")
+    freq = frequency_table(wl)[:L]
+    return ctx, freq
+
+
+def run_steps(moe, ctx, n, step_fn, stats_acc=None):
+    for i in range(n):
+        step_fn(i)
+        st = moe.moe_cache_step(ctx)
+        if stats_acc is not None:
+            for k_, v in st.items():
+                stats_acc[k_] = stats_acc.get(k_, 0) + v
+
+
+def kernel_pass(moe, torch, wl, slots, layers, steps, stream, host_alloc, logits_all, x0_all):
+    """Time the forward kernels on a small context (all hot or all cold)."""
+    ctx, freq = setup_ctx(moe, wl, slots, stream, host_alloc, layers=layers, progress=False)
+    moe.moe_seed(ctx, freq)
+    T, H = wl.tokens, wl.hidden
+    x = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(stream):
+        moe.moe_profile(ctx, 1)
+
+        def step(i):
+            x.copy_(x0_all[i % wl.steps])
+            for layer in range(layers):
+                moe.moe_forward(ctx, layer, T, x, logits_all[i % wl.steps, layer], x, flags=moe.MOE_ACCUMULATE)
+
+        run_steps(moe, ctx, steps, step)
+        prof = moe.moe_profile(ctx, 0)
+    moe.moe_destroy(ctx)
+    return prof
+
+
+def cpu_baseline(wl, seconds, logits):
+    """The oracle on the host cores: decode tokens through all layers, fp64."""
+    import numpy as np
+
+    import oracle
+    from workload import activations, expert_weights
+
+    oracle.lib()
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    spent = 0.0
+    tokens = 0
+    step = 0
+    while spent < seconds and step < wl.steps:
+        x = activations(wl, step).astype(np.float64)
+        for layer in range(wl.n_layers):
+            z = logits[step, layer]
+            ids, _ = oracle.route(z, wl.top_k)
+            experts = {int(e): expert_weights(wl, layer, int(e)) for e in np.unique(ids)}
+            t0 = time.perf_counter()
+            y, _, _ = oracle.moe_layer(wl.n_experts, wl.top_k, wl.hidden, wl.ffn, experts, x, logits=z)
+            spent += time.perf_counter() - t0
+            x = x + y
+        tokens += wl.tokens
+        step += 1
+    return dict(value=tokens / spent, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"first {tokens} decode tokens through all {wl.n_layers} layers (fp64 oracle, "
+                       f"{spent:.1f} s of oracle time; weight generation excluded)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="decode-e512k8-h2048f1024-l48-b1")
+    ap.add_argument("--eager", action="store_true", help="launch per step instead of replaying a HIP graph")
+    ap.add_argument("--host-alloc", choices=["coherent", "noncoherent"], default="coherent")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side-passes", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards per GPU with no "
+              f"exchange, so a multi-GPU figure is N independent copies of this one.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_expert_offload_gemv_amd as moe
+    from workload import WORKLOADS, activations, zipf_logits
+
+    wl = WORKLOADS[args.workload]
+    host_alloc = moe.MOE_HOST_NONCOHERENT if args.host_alloc == "noncoherent" else moe.MOE_HOST_COHERENT
+    T, L, H, E, k = wl.tokens, wl.n_layers, wl.hidden, wl.n_experts, wl.top_k
+    B = wl.expert_bytes
+    log(f"workload {wl.name}: L={L} E={E} k={k} H={H} F={wl.ffn} T={T} slots={wl.slots} "
+        f"expert={B} B host sets={wl.weight_layers} pinned={wl.weight_layers * E * B / 1e9:.1f} GB "
+        f"pool={L * wl.slots * B / 1e9:.1f} GB")
+
+    stream = torch.cuda.Stream()
+    t_setup = time.time()
+    log(f"creating the context: pinning {wl.weight_layers * E * B / 1e9:.1f} GB of host memory")
+    ctx, freq = setup_ctx(moe, wl, wl.slots, stream, host_alloc)
+    logits_np = zipf_logits(wl)
+    logits_all = torch.from_numpy(logits_np).cuda()                       # [steps][L][T][E]
+    x0_all = torch.from_numpy(np.stack([activations(wl, s) for s in range(wl.steps)])).cuda()  # [steps][T][H]
+    xs = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+    zs = torch.zeros((L, T, E), dtype=torch.float32, device="cuda")
+    moe.moe_seed(ctx, freq)
+    log(f"setup {time.time() - t_setup:.1f} s")
+
+    def forward_all():
+        for layer in range(L):
+            moe.moe_forward(ctx, layer, T, xs, zs[layer], xs, flags=moe.MOE_ACCUMULATE)
+
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                forward_all()
+
+    def step(i):
+        s = i % wl.steps
+        xs.copy_(x0_all[s])
+        zs.copy_(logits_all[s])
+        if graph is not None:
+            graph.replay()
+        else:
+            forward_all()
+
+    with torch.cuda.stream(stream):
+        run_steps(moe, ctx, args.warmup, step)
+        moe.moe_seed(ctx, freq)  # the timed region starts from the seeded pool at step 0
+        torch.cuda.synchronize()
+        acc = {}
+        t0 = time.perf_counter()
+        run_steps(moe, ctx, args.steps, step, acc)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    tokens = args.steps * T
+    tps = tokens / elapsed
+    log(f"timed: {args.steps} steps in {elapsed * 1e3:.1f} ms -> {tps:.1f} tokens/s; stats {acc}")
+
+    # kernel timing over the same steps, eager launches bracketed by HIP events on the context stream
+    with torch.cuda.stream(stream):
+        moe.moe_seed(ctx, freq)
+        moe.moe_profile(ctx, 1)
+        prof_steps = min(args.steps, 64)
+        t1 = time.perf_counter()
+        run_steps(moe, ctx, prof_steps, lambda i: (xs.copy_(x0_all[i % wl.steps]), zs.copy_(
+            logits_all[i % wl.steps]), forward_all()))
+        t_prof = time.perf_counter() - t1
+        prof = moe.moe_profile(ctx, 0)
+    fw = max(prof["forwards"], 1)
+    gu_ms = prof["gateup_ms"] / fw
+    gu_bytes = prof["gateup_bytes"] / fw
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    log(f"kernel timing ({prof_steps} eager steps, {prof_steps * T / t_prof:.1f} tokens/s): {prof}")
+    moe.moe_destroy(ctx)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tps, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "experts": E, "top_k": k, "hidden": H, "ffn": wl.ffn,
+                   "tokens_per_step": T, "pool_slots_per_layer": wl.slots, "weights": "q4 blocks (18 B / 32)",
+                   "host_alloc": args.host_alloc, "host_weight_sets": wl.weight_layers,
+                   "launch": "eager" if args.eager else "hip-graph"},
+        "effective_weight_GBps": round((acc["hot_bytes"] + acc["cold_bytes"]) / elapsed / 1e9, 2),
+        "hot_GBps_over_step": round(acc["hot_bytes"] / elapsed / 1e9, 2),
+        "cold_GBps_over_step": round(acc["cold_bytes"] / elapsed / 1e9, 2),
+        "hit_rate": round(acc["hits"] / max(acc["hits"] + acc["misses"], 1), 4),
+        "admissions_per_step": round(acc["admissions"] / args.steps, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "gemv_gateup_kernel (decode workload, hot and cold picks)",
+                     "avg_launch_us": round(gu_ms * 1e3, 2), "bytes_per_launch": int(gu_bytes)},
+    }
+
+    if not args.no_side_passes:
+        side = min(4, L)
+        hot = kernel_pass(moe, torch, wl, E, side, 32, stream, host_alloc, logits_all, x0_all)
+        cold = kernel_pass(moe, torch, wl, 0, side, 8, stream, host_alloc, logits_all, x0_all)
+
+        def rate(p, key, bkey):
+            return p[bkey] / max(p[key], 1e-9) / 1e6  # bytes / ms -> GB/s
+
+        result["kernels_all_hot"] = {
+            "gateup_GBps": round(rate(hot, "gateup_ms", "gateup_bytes"), 1),
+            "down_GBps": round(rate(hot, "down_ms", "down_bytes"), 1),
+            "gateup_us": round(hot["gateup_ms"] / hot["forwards"] * 1e3, 2),
+            "down_us": round(hot["down_ms"] / hot["forwards"] * 1e3, 2),
+            "route_us": round(hot["route_ms"] / hot["forwards"] * 1e3, 2),
+            "frac_of_hbm": round(rate(hot, "gateup_ms", "gateup_bytes") / HBM_PEAK_GBPS, 4)}
+        result["kernels_all_cold"] = {
+            "gateup_GBps": round(rate(cold, "gateup_ms", "gateup_bytes"), 2),
+            "down_GBps": round(rate(cold, "down_ms", "down_bytes"), 2),
+            "frac_of_pcie": round(rate(cold, "gateup_ms", "gateup_bytes") / PCIE_PEAK_GBPS, 4)}
+        # DMA ceiling: pinned host -> HBM copy of 1 GiB
+        src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(3):
+            dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        result["pcie_dma_h2d_GBps"] = round(3 * (1 << 30) / (time.perf_counter() - t2) / 1e9, 2)
+        del src, dst
+        log(f"side passes: hot {result['kernels_all_hot']} cold {result['kernels_all_cold']} "
+            f"dma {result['pcie_dma_h2d_GBps']} GB/s")
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, logits_np)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

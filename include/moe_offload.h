@@ -30,8 +30,8 @@
  *  - The library owns the HBM pool, the pinned host arena, the slot tables,
  *    stamps, the miss log and all scratch; they live until moe_destroy.
  *  - A context is used by one host thread at a time; calls are not re-entrant.
- *  - Device work is issued on the context stream (moe_config.stream, or a
- *    stream the library creates when that is NULL) in call order.
+ *  - Device work is issued on the context stream (moe_config.stream; NULL is
+ *    the device's null stream) in call order.
  *
  * Weight format (MOE_Q4_32_F16): each matrix row is a run of 18-byte blocks
  * along the reduction axis; a block is a little-endian IEEE fp16 scale d
@@ -48,6 +48,12 @@
 
 #ifdef __cplusplus
 extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
 #endif
 
 #define MOE_OK            0
@@ -85,14 +91,19 @@ typedef struct {
   int32_t max_prefill_tokens; /* largest T for moe_prefill (0: no prefill)    */
   int32_t device;          /* HIP device ordinal                              */
   int32_t host_alloc;      /* MOE_HOST_COHERENT or MOE_HOST_NONCOHERENT       */
-  void*   stream;          /* hipStream_t to issue on; NULL: library-owned    */
+  int32_t host_sets;       /* distinct pinned expert sets, 1..L (0: L). Layer
+                              l reads its cold experts from set l % host_sets,
+                              so layers that share a set share host weights
+                              (their HBM pools stay separate). Bounds the
+                              pinned arena where host memory is short.       */
+  void*   stream;          /* hipStream_t to issue on; NULL: the null stream  */
 } moe_config;
 
 typedef struct {
   int64_t slots_per_layer;    /* S                                            */
   int64_t expert_bytes;       /* bytes of gate+up+down of one expert          */
   int64_t pool_bytes;         /* HBM pool size, L * S * expert_bytes          */
-  int64_t host_bytes;         /* pinned arena size, L * E * expert_bytes      */
+  int64_t host_bytes;         /* pinned arena size, host_sets*E*expert_bytes  */
   int64_t staging_experts;    /* HBM blocks lent to a prefill pass            */
   int64_t clock;              /* token clock of the next step (starts at 1)   */
   int64_t steps;              /* cache steps run since the last seed          */
@@ -110,39 +121,50 @@ typedef struct {
   int64_t copied_bytes;       /* host->HBM promotion copies issued            */
 } moe_step_stats;
 
+typedef struct {
+  int64_t forwards;           /* moe_forward calls timed                      */
+  double  route_ms;           /* summed durations of the routing kernel       */
+  double  gateup_ms;          /* ... of the gate/up GEMV (+ SwiGLU)           */
+  double  down_ms;            /* ... of the down GEMV (+ weighted combine)    */
+  int64_t gateup_bytes;       /* expert bytes the timed gate/up GEMVs read    */
+  int64_t down_bytes;         /* expert bytes the timed down GEMVs read       */
+} moe_profile_stats;
+
 /* Size in bytes of one expert (gate + up + down) in MOE_Q4_32_F16. */
-int64_t moe_expert_bytes(int32_t hidden, int32_t ffn);
+MOE_API int64_t moe_expert_bytes(int32_t hidden, int32_t ffn);
 
 /* Create a context. Allocates the HBM pool (pool_budget_bytes, [A6000]
- * capacity rule), the pinned host arena for L*E experts, prefill staging, the
- * slot tables (all -1), stamps, the miss log and scratch, all once: no call
- * below allocates memory. *out is set on success. MOE_E_NOMEM if the pool or
- * the arena cannot be allocated; MOE_E_INVAL on a bad config. */
-int moe_create(const moe_config* cfg, moe_ctx** out);
+ * capacity rule), the pinned host arena (host_sets*E experts), prefill
+ * staging, the slot tables (all -1), stamps, the miss log and scratch, all
+ * once: no call below allocates memory (except moe_register_router). *out is
+ * set on success. MOE_E_NOMEM if the pool or the arena cannot be allocated;
+ * MOE_E_INVAL on a bad config; moe_last_error(NULL) then tells which. */
+MOE_API int moe_create(const moe_config* cfg, moe_ctx** out);
 
 /* Release everything the context owns; waits for its stream. NULL is a no-op. */
-int moe_destroy(moe_ctx* ctx);
+MOE_API int moe_destroy(moe_ctx* ctx);
 
-/* Copy one layer's expert weights into the pinned arena, repacking them into
- * the device layout. gate, up, down are host pointers to E consecutive
- * matrices each, in the canonical format above (gate/up: E*F*(H/32) blocks,
- * down: E*H*(F/32) blocks). The caller may free them on return. Allowed until
- * moe_seed; MOE_E_STATE afterwards. */
-int moe_register_layer(moe_ctx* ctx, int32_t layer,
+/* Copy one layer's expert weights into its pinned host set (layer %
+ * host_sets), repacking them into the device layout. gate, up, down are host
+ * pointers to E consecutive matrices each, in the canonical format above
+ * (gate/up: E*F*(H/32) blocks, down: E*H*(F/32) blocks). The caller may free
+ * them on return. Allowed until moe_seed; MOE_E_STATE afterwards. */
+MOE_API int moe_register_layer(moe_ctx* ctx, int32_t layer,
                        const void* gate, const void* up, const void* down);
 
 /* Optional router for one layer: host fp32 [E][H], row e is expert e. With a
  * router, moe_forward and moe_prefill may take logits == NULL, and logits are
  * z_e = fmaf chain over j = 0..H-1 of x_j * W[e][j] in fp32, from 0.          */
-int moe_register_router(moe_ctx* ctx, int32_t layer, const float* w_router);
+MOE_API int moe_register_router(moe_ctx* ctx, int32_t layer, const float* w_router);
 
 /* Seed the pools and reset the cache policy ([A6000]: pools are seeded from a
  * routing-frequency table). freq is host uint32 [L][E] or NULL. Per layer the
  * S experts with the highest count (ties: lower id first) take slots 0..S-1 in
  * that order; with freq == NULL every slot stays free (cold start). Resets
- * stamps to 0, the per-expert last-miss times to 0, the miss log, and the token
- * clock to 1. Requires every layer registered (MOE_E_STATE). Synchronises. */
-int moe_seed(moe_ctx* ctx, const uint32_t* freq);
+ * stamps to 0, the per-expert last-miss times to 0, the miss log, the counts
+ * and the token clock to 1. Requires every host set registered (MOE_E_STATE).
+ * Synchronises. */
+MOE_API int moe_seed(moe_ctx* ctx, const uint32_t* freq);
 
 /* MoE FFN of one layer for a decode batch of n_tokens (1..max_batch_tokens):
  *   ids, w = top-k softmax routing of logits (device fp32 [T][E], or NULL when
@@ -160,7 +182,7 @@ int moe_seed(moe_ctx* ctx, const uint32_t* freq);
  * update in place). ids (int32 [T][k]) and w (fp32 [T][k]) are optional device
  * outputs. Asynchronous on the context stream; allocates nothing and may be
  * captured into a HIP graph. Call it at most once per layer per step. */
-int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
+MOE_API int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
                 const float* x, const float* logits, float* y,
                 int32_t* ids, float* w, uint32_t flags);
 
@@ -171,7 +193,7 @@ int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
  * blocks for the pass and the blocks are returned at its end ([FORK]). The
  * cache policy is untouched: no stamps, no miss log, no counts, no clock.
  * Synchronises the stream; not capturable (MOE_E_CAPTURING). */
-int moe_prefill(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
+MOE_API int moe_prefill(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
                 const float* x, const float* logits, float* y, uint32_t flags);
 
 /* Close the current step ([A6000]: promotion pass between decode steps, never
@@ -186,21 +208,28 @@ int moe_prefill(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
  * Weights are copied pinned -> slot on the stream, tables, stamps and the
  * clock (advanced by the step's token count) are uploaded, and the log is
  * cleared. out may be NULL. MOE_E_CAPTURING if the stream is capturing. */
-int moe_cache_step(moe_ctx* ctx, moe_step_stats* out);
+MOE_API int moe_cache_step(moe_ctx* ctx, moe_step_stats* out);
+
+/* Kernel timing for measurement: enable = 1 turns it on and clears the
+ * totals, 0 turns it off, -1 leaves it as is; out (may be NULL) receives the
+ * totals accumulated so far. While on, moe_forward brackets its three kernels
+ * with HIP events (so it must not be captured: MOE_E_CAPTURING) and
+ * moe_cache_step adds their durations once the stream has drained. */
+MOE_API int moe_profile(moe_ctx* ctx, int32_t enable, moe_profile_stats* out);
 
 /* Introspection (host outputs; each synchronises the stream). */
-int moe_get_info(moe_ctx* ctx, moe_info* out);
+MOE_API int moe_get_info(moe_ctx* ctx, moe_info* out);
 /* int32 [E]: slot of each expert of the layer, -1 when not resident. */
-int moe_get_slot_table(moe_ctx* ctx, int32_t layer, int32_t* out);
+MOE_API int moe_get_slot_table(moe_ctx* ctx, int32_t layer, int32_t* out);
 /* uint32 [S]: use-stamps of the layer's slots. */
-int moe_get_stamps(moe_ctx* ctx, int32_t layer, uint32_t* out);
+MOE_API int moe_get_stamps(moe_ctx* ctx, int32_t layer, uint32_t* out);
 /* uint64: the miss log of the last closed step, ascending; *n = its length.
  * Writes min(cap, n) entries. */
-int moe_get_miss_log(moe_ctx* ctx, uint64_t* out, int64_t cap, int64_t* n);
+MOE_API int moe_get_miss_log(moe_ctx* ctx, uint64_t* out, int64_t cap, int64_t* n);
 /* uint32 [L][E]: picks per expert since the last seed (moe_forward only). */
-int moe_get_counts(moe_ctx* ctx, uint32_t* out);
+MOE_API int moe_get_counts(moe_ctx* ctx, uint32_t* out);
 
-const char* moe_last_error(moe_ctx* ctx);
+MOE_API const char* moe_last_error(moe_ctx* ctx);  /* ctx NULL: the last failed moe_create of this thread */
 
 #ifdef __cplusplus
 }

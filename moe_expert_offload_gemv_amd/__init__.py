@@ -1,0 +1,244 @@
+"""Python binding of libmoe_offload.so (include/moe_offload.h).
+
+Argument marshalling only: every step of the MoE layer runs in the HIP
+kernels and the host runtime of the shared library. Device buffers are torch
+cuda tensors (passed by data_ptr()); host buffers are numpy arrays. The
+functions keep the C names and raise MoeError on a negative return code.
+If the library has not been built this module raises on first use; there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmoe_offload.so")
+
+MOE_OK = 0
+MOE_E_INVAL = -1
+MOE_E_NOMEM = -2
+MOE_E_HIP = -3
+MOE_E_STATE = -4
+MOE_E_CAPTURING = -5
+MOE_Q4_32_F16 = 1
+MOE_ACCUMULATE = 1
+MOE_HOST_COHERENT = 0
+MOE_HOST_NONCOHERENT = 1
+
+EXPORTED = [
+    "moe_expert_bytes", "moe_create", "moe_destroy", "moe_register_layer", "moe_register_router", "moe_seed",
+    "moe_forward", "moe_prefill", "moe_cache_step", "moe_get_info", "moe_get_slot_table", "moe_get_stamps",
+    "moe_get_miss_log", "moe_get_counts", "moe_last_error", "moe_profile",
+]
+
+
+class moe_config(C.Structure):
+    _fields_ = [
+        ("n_layers", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32), ("hidden", C.c_int32),
+        ("ffn", C.c_int32), ("quant", C.c_int32), ("pool_budget_bytes", C.c_int64), ("reserve_bytes", C.c_int64),
+        ("window_tokens", C.c_int32), ("admit_misses", C.c_int32), ("max_batch_tokens", C.c_int32),
+        ("max_prefill_tokens", C.c_int32), ("device", C.c_int32), ("host_alloc", C.c_int32),
+        ("host_sets", C.c_int32), ("stream", C.c_void_p),
+    ]
+
+
+class moe_info(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("slots_per_layer", "expert_bytes", "pool_bytes", "host_bytes",
+                                        "staging_experts", "clock", "steps")]
+
+
+class moe_step_stats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("step", "tokens", "hits", "misses", "admissions", "evictions",
+                                        "hot_bytes", "cold_bytes", "copied_bytes")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class moe_profile_stats(C.Structure):
+    _fields_ = [("forwards", C.c_int64), ("route_ms", C.c_double), ("gateup_ms", C.c_double),
+                ("down_ms", C.c_double), ("gateup_bytes", C.c_int64), ("down_bytes", C.c_int64)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded shared library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m moe_expert_offload_gemv_amd.build")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, u32 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32
+        sig = {
+            "moe_expert_bytes": (i64, [i32, i32]),
+            "moe_create": (C.c_int, [C.POINTER(moe_config), C.POINTER(vp)]),
+            "moe_destroy": (C.c_int, [vp]),
+            "moe_register_layer": (C.c_int, [vp, i32, vp, vp, vp]),
+            "moe_register_router": (C.c_int, [vp, i32, vp]),
+            "moe_seed": (C.c_int, [vp, vp]),
+            "moe_forward": (C.c_int, [vp, i32, i32, vp, vp, vp, vp, vp, u32]),
+            "moe_prefill": (C.c_int, [vp, i32, i32, vp, vp, vp, u32]),
+            "moe_cache_step": (C.c_int, [vp, C.POINTER(moe_step_stats)]),
+            "moe_get_info": (C.c_int, [vp, C.POINTER(moe_info)]),
+            "moe_get_slot_table": (C.c_int, [vp, i32, vp]),
+            "moe_get_stamps": (C.c_int, [vp, i32, vp]),
+            "moe_get_miss_log": (C.c_int, [vp, vp, i64, C.POINTER(i64)]),
+            "moe_get_counts": (C.c_int, [vp, vp]),
+            "moe_last_error": (C.c_char_p, [vp]),
+            "moe_profile": (C.c_int, [vp, i32, C.POINTER(moe_profile_stats)]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(ctx, rc: int) -> None:
+    if rc != MOE_OK:
+        msg = lib().moe_last_error(ctx) if ctx else b""
+        raise MoeError(rc, (msg or b"").decode(errors="replace"))
+
+
+def _dptr(t):
+    """Device address of a torch cuda tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("device arguments must be contiguous cuda tensors")
+    return t.data_ptr()
+
+
+def _hptr(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+# ---------------------------------------------------------------------------
+
+def moe_expert_bytes(hidden: int, ffn: int) -> int:
+    return int(lib().moe_expert_bytes(hidden, ffn))
+
+
+def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reserve_bytes=0, window_tokens=64,
+               admit_misses=2, max_batch_tokens=64, max_prefill_tokens=0, device=0, host_alloc=MOE_HOST_COHERENT,
+               host_sets=0, stream=None):
+    """Returns an opaque context handle.
+
+    stream: a torch.cuda.Stream, a raw hipStream_t int, or None for torch's
+    current stream on the device (0, the null stream, is a valid handle).
+    """
+    if stream is None:
+        stream = 0
+        try:
+            import torch
+
+            if torch.cuda.is_available():
+                stream = torch.cuda.current_stream(device).cuda_stream
+        except ImportError:
+            pass
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    cfg = moe_config(n_layers, n_experts, top_k, hidden, ffn, MOE_Q4_32_F16, pool_budget_bytes, reserve_bytes,
+                     window_tokens, admit_misses, max_batch_tokens, max_prefill_tokens, device, host_alloc,
+                     host_sets, stream)
+    out = C.c_void_p()
+    rc = lib().moe_create(C.byref(cfg), C.byref(out))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_create: " + (lib().moe_last_error(None) or b"").decode(errors="replace"))
+    return out.value
+
+
+def moe_destroy(ctx) -> None:
+    _check(None, lib().moe_destroy(ctx))
+
+
+def moe_register_layer(ctx, layer: int, gate, up, down) -> None:
+    g, gp = _hptr(gate, np.uint8)
+    u, up_ = _hptr(up, np.uint8)
+    d, dp = _hptr(down, np.uint8)
+    _check(ctx, lib().moe_register_layer(ctx, layer, gp, up_, dp))
+
+
+def moe_register_router(ctx, layer: int, w_router) -> None:
+    w, wp = _hptr(w_router, np.float32)
+    _check(ctx, lib().moe_register_router(ctx, layer, wp))
+
+
+def moe_seed(ctx, freq=None) -> None:
+    if freq is None:
+        _check(ctx, lib().moe_seed(ctx, None))
+    else:
+        f, fp = _hptr(freq, np.uint32)
+        _check(ctx, lib().moe_seed(ctx, fp))
+
+
+def moe_forward(ctx, layer: int, n_tokens: int, x, logits, y, ids=None, w=None, flags: int = 0) -> None:
+    _check(ctx, lib().moe_forward(ctx, layer, n_tokens, _dptr(x), _dptr(logits), _dptr(y), _dptr(ids), _dptr(w),
+                                  flags))
+
+
+def moe_prefill(ctx, layer: int, n_tokens: int, x, logits, y, flags: int = 0) -> None:
+    _check(ctx, lib().moe_prefill(ctx, layer, n_tokens, _dptr(x), _dptr(logits), _dptr(y), flags))
+
+
+def moe_cache_step(ctx) -> dict:
+    s = moe_step_stats()
+    _check(ctx, lib().moe_cache_step(ctx, C.byref(s)))
+    return s.as_dict()
+
+
+def moe_get_info(ctx) -> dict:
+    s = moe_info()
+    _check(ctx, lib().moe_get_info(ctx, C.byref(s)))
+    return {n: int(getattr(s, n)) for n, _ in s._fields_}
+
+
+def moe_get_slot_table(ctx, layer: int, n_experts: int) -> np.ndarray:
+    out = np.empty(n_experts, np.int32)
+    _check(ctx, lib().moe_get_slot_table(ctx, layer, out.ctypes.data))
+    return out
+
+
+def moe_get_stamps(ctx, layer: int, slots: int) -> np.ndarray:
+    out = np.zeros(max(slots, 1), np.uint32)
+    _check(ctx, lib().moe_get_stamps(ctx, layer, out.ctypes.data))
+    return out[:slots]
+
+
+def moe_get_miss_log(ctx) -> np.ndarray:
+    n = C.c_int64()
+    _check(ctx, lib().moe_get_miss_log(ctx, None, 0, C.byref(n)))
+    out = np.empty(max(n.value, 1), np.uint64)
+    _check(ctx, lib().moe_get_miss_log(ctx, out.ctypes.data, n.value, C.byref(n)))
+    return out[: n.value]
+
+
+def moe_get_counts(ctx, n_layers: int, n_experts: int) -> np.ndarray:
+    out = np.empty((n_layers, n_experts), np.uint32)
+    _check(ctx, lib().moe_get_counts(ctx, out.ctypes.data))
+    return out
+
+
+def moe_profile(ctx, enable: int = -1) -> dict:
+    s = moe_profile_stats()
+    _check(ctx, lib().moe_profile(ctx, enable, C.byref(s)))
+    return s.as_dict()
+
+
+def moe_last_error(ctx) -> str:
+    return (lib().moe_last_error(ctx) or b"").decode(errors="replace")

@@ -1,0 +1,81 @@
+// kernels.h - host-side launchers of the gfx950 kernels (internal to
+// libmoe_offload.so; the public boundary is include/moe_offload.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Per-device control words read and written by the kernels. Living in device
+// memory, they keep their current values across HIP graph replays.
+struct Ctrl {
+  uint32_t clock;        // token clock of token 0 of the current step
+  uint32_t step_tokens;  // max n_tokens over the forwards of the step
+  uint32_t log_count;    // miss-log entries appended in the step (may exceed capacity)
+  uint32_t hits;         // picks served from the pool in the step
+};
+
+// Device layout of one expert (gate, up, down; each a nibble plane of
+// [rows][k/32][16 B] followed by a scale plane of [rows][k/32] fp16).
+struct ExpertLayout {
+  int32_t H, F;
+  int64_t gate_nib, gate_scl, up_nib, up_scl, down_nib, down_scl, bytes;
+  static ExpertLayout make(int32_t H, int32_t F) {
+    ExpertLayout l;
+    l.H = H, l.F = F;
+    int64_t kbh = H / 32, kbf = F / 32;
+    l.gate_nib = 0;
+    l.gate_scl = l.gate_nib + (int64_t)F * kbh * 16;
+    l.up_nib = l.gate_scl + (int64_t)F * kbh * 2;
+    l.up_scl = l.up_nib + (int64_t)F * kbh * 16;
+    l.down_nib = l.up_scl + (int64_t)F * kbh * 2;
+    l.down_scl = l.down_nib + (int64_t)H * kbf * 16;
+    l.bytes = l.down_scl + (int64_t)H * kbf * 2;
+    return l;
+  }
+};
+
+// Lane mapping of the GEMVs over a reduction of kb blocks: lpr lanes share a
+// row (a power of two, 8..64), each lane owns bpl blocks (1..4).
+struct GemvShape {
+  int lpr, bpl;
+};
+bool gemv_shape(int kb, GemvShape* out);
+
+struct RouteArgs {
+  const float* logits;   // [T][E] or nullptr (router)
+  const float* x;        // [T][H] (router input)
+  const float* wr;       // [E][H] router weights of the layer or nullptr
+  int32_t T, E, k, H, S, layer;
+  const int32_t* tbl;    // [E] slot table row of the layer
+  uint32_t* stamps;      // [S] stamps of the layer
+  uint32_t* counts;      // [E] pick counts of the layer
+  uint64_t* log;         // miss log
+  uint32_t log_cap;
+  Ctrl* ctrl;
+  const uint8_t* pool;   // first slot of the layer
+  const uint8_t* host;   // device address of the layer's pinned experts
+  const uint8_t* const* pass_addr;  // prefill: per-expert address for the pass (overrides tbl)
+  int64_t expert_bytes;
+  int32_t* ids;          // [T][k] internal
+  float* w;              // [T][k] internal
+  const uint8_t** addr;  // [T][k] per-pick expert address
+  int32_t* ids_user;     // optional copies for the caller
+  float* w_user;
+  int32_t policy;        // 1: stamps, miss log, counts, step tokens; 0: none
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct GemvArgs {
+  const float* x;               // gate/up: activations [T][H]; down: h [P][F]
+  const uint8_t* const* addr;   // [P] expert base address per pick
+  const float* w;               // down: routing weights [P]
+  float* out;                   // gate/up: h [P][F]; down: y [T][H]
+  int32_t T, k, H, F;
+  int32_t accumulate;           // down: y += result
+  ExpertLayout lay;
+};
+hipError_t launch_gemv_gateup(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_down_combine(const GemvArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,607 @@
+// runtime.cpp - the host side of libmoe_offload.so behind include/moe_offload.h:
+// context, HBM pool, pinned host arena, registration (repack into the device
+// layout), seeding, the decode forward (three kernel launches), and the
+// between-step cache policy.
+//
+// The cache policy is the one the "a6000-custom-kernels" README describes
+// under its pointer-table GEMV diagram (table, pool and stamp array per
+// expert tensor; cold reads logged by a miss recorder; a promotion pass
+// between decode steps, outside graph capture, admitting experts seen
+// missing a second time and evicting by a scan of the use-stamps; pools
+// seeded from routing frequencies; capacity from free memory minus a margin),
+// with the admission window of the "llama.cpp: fork with multi gpu
+// acceleration ..." README ("How it works": admission only after repeated use
+// within the last 64 tokens).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/moe_offload.h"
+#include "kernels.h"
+#include "runtime.h"
+
+using moe::Ctrl;
+using moe::ExpertLayout;
+
+// ---------------------------------------------------------------------------
+// error plumbing
+
+static thread_local std::string g_create_error;
+
+int moe_ctx_fail(moe_ctx* c, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  return code;
+}
+
+#define HIP_TRY(ctx, expr)                                                                             \
+  do {                                                                                                 \
+    hipError_t e_ = (expr);                                                                            \
+    if (e_ != hipSuccess) return moe_ctx_fail((ctx), MOE_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+
+unsigned host_threads() {
+  unsigned n = std::thread::hardware_concurrency();
+  return std::max(1u, std::min(16u, n ? n : 1u));
+}
+
+// Repack E experts of one matrix kind from canonical 18-byte blocks into
+// the device layout (nibble plane + scale plane per expert) at dst + e*B.
+void repack_matrix(const uint8_t* src, int E, int64_t rows, int64_t kb, uint8_t* dst, int64_t expert_bytes,
+                   int64_t nib_off, int64_t scl_off) {
+  auto work = [&](int e0, int e1) {
+    for (int e = e0; e < e1; ++e) {
+      const uint8_t* s = src + (int64_t)e * rows * kb * 18;
+      uint8_t* nib = dst + (int64_t)e * expert_bytes + nib_off;
+      uint8_t* scl = dst + (int64_t)e * expert_bytes + scl_off;
+      const int64_t nb = rows * kb;
+      for (int64_t b = 0; b < nb; ++b) {
+        std::memcpy(scl + 2 * b, s + 18 * b, 2);
+        std::memcpy(nib + 16 * b, s + 18 * b + 2, 16);
+      }
+    }
+  };
+  unsigned nt = std::min<unsigned>(host_threads(), (unsigned)E);
+  if (nt <= 1) {
+    work(0, E);
+    return;
+  }
+  std::vector<std::thread> th;
+  for (unsigned i = 0; i < nt; ++i) {
+    int e0 = (int)((int64_t)E * i / nt), e1 = (int)((int64_t)E * (i + 1) / nt);
+    th.emplace_back(work, e0, e1);
+  }
+  for (auto& t : th) t.join();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+
+extern "C" int64_t moe_expert_bytes(int32_t hidden, int32_t ffn) {
+  if (hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32) return -1;
+  return ExpertLayout::make(hidden, ffn).bytes;
+}
+
+static void ctx_release(moe_ctx* c) {
+  if (!c) return;
+  DeviceGuard g(c->device);
+  (void)hipStreamSynchronize(c->stream);
+  for (void* p : c->dev_allocs) (void)hipFree(p);
+  for (void* p : c->host_allocs) (void)hipHostFree(p);
+  for (void* r : c->routers)
+    if (r) (void)hipFree(r);
+  for (hipEvent_t e : c->events) (void)hipEventDestroy(e);
+  delete c;
+}
+
+int moe_ctx_dev_alloc(moe_ctx* c, void** p, size_t bytes, const char* what) {
+  *p = nullptr;
+  if (bytes == 0) return MOE_OK;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return moe_ctx_fail(c, MOE_E_NOMEM, "hipMalloc(%zu) for %s failed: %s", bytes, what, hipGetErrorString(e));
+  }
+  c->dev_allocs.push_back(*p);
+  return MOE_OK;
+}
+
+int moe_ctx_host_alloc(moe_ctx* c, void** p, size_t bytes, unsigned flags, const char* what) {
+  *p = nullptr;
+  if (bytes == 0) return MOE_OK;
+  hipError_t e = hipHostMalloc(p, bytes, flags);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return moe_ctx_fail(c, MOE_E_NOMEM, "hipHostMalloc(%zu) for %s failed: %s", bytes, what,
+                        hipGetErrorString(e));
+  }
+  c->host_allocs.push_back(*p);
+  return MOE_OK;
+}
+
+extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
+  g_create_error.clear();
+  if (!cfg || !out) return g_create_error = "null config or output", MOE_E_INVAL;
+  *out = nullptr;
+  const moe_config& k = *cfg;
+  if (k.host_sets < 0 || k.host_sets > k.n_layers) return g_create_error = "host_sets outside 0..n_layers", MOE_E_INVAL;
+  if (k.n_layers < 1 || k.n_experts < 1 || k.n_experts > 4096 || k.top_k < 1 || k.top_k > 32 ||
+      k.top_k > k.n_experts || k.hidden < 32 || k.ffn < 32 || k.hidden % 32 || k.ffn % 32 ||
+      k.quant != MOE_Q4_32_F16 || k.window_tokens < 1 || (k.admit_misses != 1 && k.admit_misses != 2) ||
+      k.max_batch_tokens < 1 || k.max_batch_tokens > 256 || k.max_prefill_tokens < 0 || k.n_layers > (1 << 20) ||
+      (k.host_alloc != MOE_HOST_COHERENT && k.host_alloc != MOE_HOST_NONCOHERENT))
+    return g_create_error = "config field out of range", MOE_E_INVAL;
+  moe::GemvShape s1, s2;
+  if (!moe::gemv_shape(k.hidden / 32, &s1) || !moe::gemv_shape(k.ffn / 32, &s2))
+    return g_create_error = "hidden/32 and ffn/32 must each be 2^a*b with 2^a >= 8 (capped at 64) and b <= 4",
+           MOE_E_INVAL;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || k.device < 0 || k.device >= ndev)
+    return g_create_error = "no such HIP device", MOE_E_INVAL;
+
+  moe_ctx* c = new moe_ctx();
+  c->cfg = k;
+  c->device = k.device;
+  c->L = k.n_layers, c->E = k.n_experts, c->k = k.top_k, c->H = k.hidden, c->F = k.ffn;
+  c->lay = ExpertLayout::make(k.hidden, k.ffn);
+  c->B = c->lay.bytes;
+  DeviceGuard g(c->device);
+
+  auto fail = [&](int rc) {
+    g_create_error = c->err.empty() ? "a HIP call failed during create" : c->err;
+    ctx_release(c);
+    return rc;
+  };
+
+  c->stream = (hipStream_t)k.stream;  // NULL: the null stream
+  c->own_stream = false;
+
+  // small device state first, so the pool sizing sees what is left
+  const int64_t L = c->L, E = c->E, K = c->k;
+  c->log_cap = (uint32_t)std::min<int64_t>((int64_t)k.max_batch_tokens * L * K, 0xffffffffLL);
+  int rc;
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_tbl, sizeof(int32_t) * L * E, "slot tables"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_counts, sizeof(uint32_t) * L * E, "counts"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_log, sizeof(uint64_t) * c->log_cap, "miss log"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ctrl, sizeof(Ctrl), "control"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_host_base, sizeof(uint8_t*) * L, "host bases"))) return fail(rc);
+  const int64_t P = (int64_t)k.max_batch_tokens * K;
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ids, sizeof(int32_t) * P, "ids"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_w, sizeof(float) * P, "weights"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_addr, sizeof(uint8_t*) * P, "addresses"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_h, sizeof(float) * P * c->F, "h"))) return fail(rc);
+  if ((rc = moe_prefill_alloc(c))) return fail(rc);
+
+  // pinned host staging for the small transfers of the cache step
+  const unsigned pin = hipHostMallocDefault;
+  if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_ctrl, sizeof(Ctrl), pin, "ctrl staging"))) return fail(rc);
+  if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_log, sizeof(uint64_t) * c->log_cap, pin, "log staging")))
+    return fail(rc);
+  if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_tbl, sizeof(int32_t) * L * E, pin, "table staging")))
+    return fail(rc);
+
+  // HBM pool: S slots per layer
+  int64_t budget = k.pool_budget_bytes;
+  if (budget < 0) {
+    size_t fr = 0, tot = 0;
+    if (hipMemGetInfo(&fr, &tot) != hipSuccess) return fail(moe_ctx_fail(c, MOE_E_HIP, "hipMemGetInfo failed"));
+    budget = std::max<int64_t>(0, (int64_t)fr - k.reserve_bytes);
+  }
+  c->S = (int32_t)std::min<int64_t>(E, budget / (L * c->B));
+  const int64_t S = c->S;
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->pool, (size_t)(L * S * c->B), "expert pool"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_stamps, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), "stamps")))
+    return fail(rc);
+  if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_stamps, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), pin,
+                               "stamp staging")))
+    return fail(rc);
+
+  // pinned host arena, one allocation per host set, mapped for zero-copy reads
+  const unsigned hflags =
+      hipHostMallocMapped | (k.host_alloc == MOE_HOST_NONCOHERENT ? hipHostMallocNonCoherent : hipHostMallocCoherent);
+  c->host_sets = k.host_sets ? k.host_sets : c->L;
+  std::vector<uint8_t*> set_host(c->host_sets), set_dev(c->host_sets);
+  for (int64_t hs = 0; hs < c->host_sets; ++hs) {
+    if ((rc = moe_ctx_host_alloc(c, (void**)&set_host[hs], (size_t)(E * c->B), hflags, "pinned experts")))
+      return fail(rc);
+    void* dp = nullptr;
+    if (hipHostGetDevicePointer(&dp, set_host[hs], 0) != hipSuccess)
+      return fail(moe_ctx_fail(c, MOE_E_HIP, "hipHostGetDevicePointer failed"));
+    set_dev[hs] = (uint8_t*)dp;
+  }
+  c->host_layers.assign(L, nullptr);
+  c->host_layers_dev.assign(L, nullptr);
+  for (int64_t l = 0; l < L; ++l) {
+    c->host_layers[l] = set_host[l % c->host_sets];
+    c->host_layers_dev[l] = set_dev[l % c->host_sets];
+  }
+  if (hipMemcpy(c->d_host_base, c->host_layers_dev.data(), sizeof(uint8_t*) * L, hipMemcpyHostToDevice) !=
+      hipSuccess)
+    return fail(MOE_E_HIP);
+
+  c->routers.assign(L, nullptr);
+  c->registered.assign(c->host_sets, 0);
+  c->tbl.assign(L * E, -1);
+  c->owner.assign(L * std::max<int64_t>(S, 1), -1);
+  c->stamps.assign(L * std::max<int64_t>(S, 1), 0);
+  c->last_miss.assign(L * E, 0);
+  if (hipMemset(c->d_tbl, 0xff, sizeof(int32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
+  if (hipMemset(c->d_counts, 0, sizeof(uint32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
+  if (hipMemset(c->d_stamps, 0, sizeof(uint32_t) * L * std::max<int64_t>(S, 1)) != hipSuccess)
+    return fail(MOE_E_HIP);
+  Ctrl z{1, 0, 0, 0};
+  if (hipMemcpy(c->d_ctrl, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return fail(MOE_E_HIP);
+  // events for kernel timing: four per forward, enough for one step of every layer
+  const int64_t n_timed = L + 16;
+  c->events.reserve(4 * n_timed);
+  for (int64_t i = 0; i < 4 * n_timed; ++i) {
+    hipEvent_t ev;
+    if (hipEventCreate(&ev) != hipSuccess) return fail(MOE_E_HIP);
+    c->events.push_back(ev);
+  }
+  c->timed_tokens.assign(n_timed, 0);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_E_HIP);
+  c->clock = 1;
+  *out = c;
+  return MOE_OK;
+}
+
+extern "C" int moe_destroy(moe_ctx* c) {
+  ctx_release(c);
+  return MOE_OK;
+}
+
+extern "C" const char* moe_last_error(moe_ctx* c) { return c ? c->err.c_str() : g_create_error.c_str(); }
+
+extern "C" int moe_register_layer(moe_ctx* c, int32_t layer, const void* gate, const void* up, const void* down) {
+  if (!c) return MOE_E_INVAL;
+  if (layer < 0 || layer >= c->L || !gate || !up || !down)
+    return moe_ctx_fail(c, MOE_E_INVAL, "register_layer: bad layer %d or null weights", layer);
+  if (c->seeded) return moe_ctx_fail(c, MOE_E_STATE, "register_layer after moe_seed");
+  const int64_t kbh = c->H / 32, kbf = c->F / 32;
+  uint8_t* dst = c->host_layers[layer];
+  repack_matrix((const uint8_t*)gate, c->E, c->F, kbh, dst, c->B, c->lay.gate_nib, c->lay.gate_scl);
+  repack_matrix((const uint8_t*)up, c->E, c->F, kbh, dst, c->B, c->lay.up_nib, c->lay.up_scl);
+  repack_matrix((const uint8_t*)down, c->E, c->H, kbf, dst, c->B, c->lay.down_nib, c->lay.down_scl);
+  c->registered[layer % c->host_sets] = 1;
+  return MOE_OK;
+}
+
+extern "C" int moe_register_router(moe_ctx* c, int32_t layer, const float* w) {
+  if (!c) return MOE_E_INVAL;
+  if (layer < 0 || layer >= c->L || !w) return moe_ctx_fail(c, MOE_E_INVAL, "register_router: bad arguments");
+  DeviceGuard g(c->device);
+  if (!c->routers[layer]) {
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, sizeof(float) * (size_t)c->E * c->H);
+    if (e != hipSuccess) return moe_ctx_fail(c, MOE_E_NOMEM, "router alloc failed");
+    c->routers[layer] = p;
+  }
+  HIP_TRY(c, hipMemcpy(c->routers[layer], w, sizeof(float) * (size_t)c->E * c->H, hipMemcpyHostToDevice));
+  return MOE_OK;
+}
+
+extern "C" int moe_seed(moe_ctx* c, const uint32_t* freq) {
+  if (!c) return MOE_E_INVAL;
+  DeviceGuard g(c->device);
+  for (int l = 0; l < c->host_sets; ++l)
+    if (!c->registered[l]) return moe_ctx_fail(c, MOE_E_STATE, "seed: host set %d (layer %d) not registered", l, l);
+  if (stream_capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "seed while capturing");
+  const int64_t L = c->L, E = c->E, S = c->S;
+  std::fill(c->tbl.begin(), c->tbl.end(), -1);
+  std::fill(c->owner.begin(), c->owner.end(), -1);
+  std::fill(c->stamps.begin(), c->stamps.end(), 0u);
+  std::fill(c->last_miss.begin(), c->last_miss.end(), 0u);
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  if (freq) {
+    std::vector<int32_t> order(E);
+    for (int64_t l = 0; l < L; ++l) {
+      for (int64_t e = 0; e < E; ++e) order[e] = (int32_t)e;
+      const uint32_t* f = freq + l * E;
+      std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return f[a] > f[b]; });
+      for (int64_t s = 0; s < S; ++s) {
+        const int32_t e = order[s];
+        c->tbl[l * E + e] = (int32_t)s;
+        c->owner[l * S + s] = e;
+        HIP_TRY(c, hipMemcpyAsync(c->pool + (l * S + s) * c->B, c->host_layers[l] + (int64_t)e * c->B, c->B,
+                                  hipMemcpyHostToDevice, c->stream));
+      }
+    }
+  }
+  std::memcpy(c->h_tbl, c->tbl.data(), sizeof(int32_t) * L * E);
+  HIP_TRY(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * L * E, hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(c, hipMemsetAsync(c->d_stamps, 0, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), c->stream));
+  HIP_TRY(c, hipMemsetAsync(c->d_counts, 0, sizeof(uint32_t) * L * E, c->stream));
+  *c->h_ctrl = Ctrl{1, 0, 0, 0};
+  HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  c->clock = 1;
+  c->steps = 0;
+  c->last_log.clear();
+  c->seeded = true;
+  return MOE_OK;
+}
+
+static int check_act(moe_ctx* c, const void* p, const char* what) {
+  if (!p || ((uintptr_t)p & 15)) return moe_ctx_fail(c, MOE_E_INVAL, "%s must be a non-null 16-byte aligned pointer", what);
+  return MOE_OK;
+}
+
+extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const float* x, const float* logits,
+                           float* y, int32_t* ids, float* w, uint32_t flags) {
+  if (!c) return MOE_E_INVAL;
+  if (layer < 0 || layer >= c->L) return moe_ctx_fail(c, MOE_E_INVAL, "forward: bad layer %d", layer);
+  if (n_tokens < 1 || n_tokens > c->cfg.max_batch_tokens)
+    return moe_ctx_fail(c, MOE_E_INVAL, "forward: n_tokens %d outside 1..%d", n_tokens, c->cfg.max_batch_tokens);
+  int rc;
+  if ((rc = check_act(c, x, "x")) || (rc = check_act(c, y, "y"))) return rc;
+  if (y == x && !(flags & MOE_ACCUMULATE))
+    return moe_ctx_fail(c, MOE_E_INVAL, "forward: y may alias x only with MOE_ACCUMULATE");
+  if (!logits && !c->routers[layer]) return moe_ctx_fail(c, MOE_E_INVAL, "forward: no logits and no router");
+  if (!c->seeded) return moe_ctx_fail(c, MOE_E_STATE, "forward before moe_seed");
+  DeviceGuard g(c->device);
+  hipEvent_t* ev = nullptr;
+  if (c->profiling) {
+    if (stream_capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "forward with timing on while capturing");
+    if ((size_t)c->timed_pending < c->timed_tokens.size()) {
+      ev = &c->events[4 * (size_t)c->timed_pending];
+      c->timed_tokens[c->timed_pending++] = n_tokens;
+    }
+  }
+  if (ev) HIP_TRY(c, hipEventRecord(ev[0], c->stream));
+
+  moe::RouteArgs ra{};
+  ra.logits = logits;
+  ra.x = x;
+  ra.wr = (const float*)c->routers[layer];
+  ra.T = n_tokens, ra.E = c->E, ra.k = c->k, ra.H = c->H, ra.S = c->S, ra.layer = layer;
+  ra.tbl = c->d_tbl + (int64_t)layer * c->E;
+  ra.stamps = c->d_stamps + (int64_t)layer * std::max(c->S, 1);
+  ra.counts = c->d_counts + (int64_t)layer * c->E;
+  ra.log = c->d_log;
+  ra.log_cap = c->log_cap;
+  ra.ctrl = c->d_ctrl;
+  ra.pool = c->pool + (int64_t)layer * c->S * c->B;
+  ra.host = c->host_layers_dev[layer];
+  ra.expert_bytes = c->B;
+  ra.ids = c->d_ids, ra.w = c->d_w, ra.addr = c->d_addr;
+  ra.ids_user = ids, ra.w_user = w;
+  ra.policy = 1;
+  HIP_TRY(c, moe::launch_route(ra, c->stream));
+  if (ev) HIP_TRY(c, hipEventRecord(ev[1], c->stream));
+
+  moe::GemvArgs ga{};
+  ga.x = x;
+  ga.addr = c->d_addr;
+  ga.out = c->d_h;
+  ga.T = n_tokens, ga.k = c->k, ga.H = c->H, ga.F = c->F;
+  ga.lay = c->lay;
+  HIP_TRY(c, moe::launch_gemv_gateup(ga, c->stream));
+  if (ev) HIP_TRY(c, hipEventRecord(ev[2], c->stream));
+
+  moe::GemvArgs da = ga;
+  da.x = c->d_h;
+  da.w = c->d_w;
+  da.out = y;
+  da.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+  HIP_TRY(c, moe::launch_gemv_down_combine(da, c->stream));
+  if (ev) HIP_TRY(c, hipEventRecord(ev[3], c->stream));
+  return MOE_OK;
+}
+
+// Add the durations of the pending timed forwards (the stream must be drained).
+static int flush_profile(moe_ctx* c) {
+  for (int32_t i = 0; i < c->timed_pending; ++i) {
+    float t[3] = {0, 0, 0};
+    for (int j = 0; j < 3; ++j)
+      HIP_TRY(c, hipEventElapsedTime(&t[j], c->events[4 * (size_t)i + j], c->events[4 * (size_t)i + j + 1]));
+    const int64_t picks = (int64_t)c->timed_tokens[i] * c->k;
+    c->prof.forwards += 1;
+    c->prof.route_ms += t[0];
+    c->prof.gateup_ms += t[1];
+    c->prof.down_ms += t[2];
+    c->prof.gateup_bytes += picks * (c->lay.down_nib - c->lay.gate_nib);
+    c->prof.down_bytes += picks * (c->lay.bytes - c->lay.down_nib);
+  }
+  c->timed_pending = 0;
+  return MOE_OK;
+}
+
+extern "C" int moe_profile(moe_ctx* c, int32_t enable, moe_profile_stats* out) {
+  if (!c || enable < -1 || enable > 1) return MOE_E_INVAL;
+  DeviceGuard g(c->device);
+  if (c->timed_pending > 0) {
+    HIP_TRY(c, hipStreamSynchronize(c->stream));
+    int rc = flush_profile(c);
+    if (rc) return rc;
+  }
+  if (enable == 1) {
+    c->profiling = true;
+    c->prof = moe_profile_stats{};
+  } else if (enable == 0) {
+    c->profiling = false;
+  }
+  if (out) *out = c->prof;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// the between-step cache policy
+
+extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
+  if (!c) return MOE_E_INVAL;
+  if (!c->seeded) return moe_ctx_fail(c, MOE_E_STATE, "cache_step before moe_seed");
+  DeviceGuard g(c->device);
+  if (stream_capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "cache_step while capturing");
+  const int64_t L = c->L, E = c->E, S = c->S, B = c->B;
+
+  HIP_TRY(c, hipMemcpyAsync(c->h_ctrl, c->d_ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost, c->stream));
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  const Ctrl st = *c->h_ctrl;
+  if (c->timed_pending > 0) {
+    int rc = flush_profile(c);
+    if (rc) return rc;
+  }
+  const uint32_t n = std::min(st.log_count, c->log_cap);
+  if (n > 0) {
+    HIP_TRY(c, hipMemcpyAsync(c->h_log, c->d_log, sizeof(uint64_t) * n, hipMemcpyDeviceToHost, c->stream));
+    if (S > 0)
+      HIP_TRY(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * L * S, hipMemcpyDeviceToHost,
+                                c->stream));
+    HIP_TRY(c, hipStreamSynchronize(c->stream));
+    if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * L * S);
+  }
+  // canonical order: ascending 64-bit entries (clock, then layer, then expert)
+  c->last_log.assign(c->h_log, c->h_log + n);
+  std::sort(c->last_log.begin(), c->last_log.end());
+
+  int64_t admissions = 0, evictions = 0;
+  for (uint64_t entry : c->last_log) {
+    const uint32_t t = (uint32_t)(entry >> 32);
+    const int64_t l = (int64_t)((entry >> 12) & 0xfffff);
+    const int64_t e = (int64_t)(entry & 0xfff);
+    if (l >= L || e >= E) continue;
+    const int64_t te = l * E + e;
+    if (c->tbl[te] >= 0) continue;  // admitted earlier in this walk
+    bool admit;
+    if (c->cfg.admit_misses == 1) {
+      admit = true;
+    } else {
+      const uint32_t prev = c->last_miss[te];
+      admit = prev != 0 && (int64_t)t - (int64_t)prev < (int64_t)c->cfg.window_tokens;
+      if (!admit) c->last_miss[te] = t;
+    }
+    if (!admit || S == 0) continue;
+    // victim: lowest free slot, else the smallest stamp (ties: highest slot)
+    int64_t v = -1;
+    for (int64_t s = 0; s < S; ++s)
+      if (c->owner[l * S + s] < 0) {
+        v = s;
+        break;
+      }
+    if (v < 0) {
+      uint32_t best = 0xffffffffu;
+      for (int64_t s = 0; s < S; ++s)
+        if (c->stamps[l * S + s] <= best) best = c->stamps[l * S + s], v = s;
+      const int32_t old = c->owner[l * S + v];
+      c->tbl[l * E + old] = -1;
+      c->last_miss[l * E + old] = 0;
+      ++evictions;
+    }
+    c->owner[l * S + v] = (int32_t)e;
+    c->tbl[te] = (int32_t)v;
+    c->stamps[l * S + v] = t;
+    c->last_miss[te] = 0;
+    ++admissions;
+    HIP_TRY(c, hipMemcpyAsync(c->pool + (l * S + v) * B, c->host_layers[l] + e * B, B, hipMemcpyHostToDevice,
+                              c->stream));
+  }
+  if (admissions > 0) {
+    std::memcpy(c->h_tbl, c->tbl.data(), sizeof(int32_t) * L * E);
+    HIP_TRY(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * L * E, hipMemcpyHostToDevice, c->stream));
+    std::memcpy(c->h_stamps, c->stamps.data(), sizeof(uint32_t) * L * S);
+    HIP_TRY(c, hipMemcpyAsync(c->d_stamps, c->h_stamps, sizeof(uint32_t) * L * S, hipMemcpyHostToDevice,
+                              c->stream));
+  }
+  c->clock += st.step_tokens;
+  *c->h_ctrl = Ctrl{(uint32_t)c->clock, 0, 0, 0};
+  HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
+
+  if (out) {
+    out->step = c->steps;
+    out->tokens = st.step_tokens;
+    out->hits = st.hits;
+    out->misses = st.log_count;
+    out->admissions = admissions;
+    out->evictions = evictions;
+    out->hot_bytes = (int64_t)st.hits * B;
+    out->cold_bytes = (int64_t)st.log_count * B;
+    out->copied_bytes = admissions * B;
+  }
+  c->steps += 1;
+  if (st.log_count > c->log_cap)
+    return moe_ctx_fail(c, MOE_E_STATE, "miss log overflow: %u entries, capacity %u (one forward per layer per step)",
+                        st.log_count, c->log_cap);
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// introspection
+
+extern "C" int moe_get_info(moe_ctx* c, moe_info* out) {
+  if (!c || !out) return MOE_E_INVAL;
+  out->slots_per_layer = c->S;
+  out->expert_bytes = c->B;
+  out->pool_bytes = (int64_t)c->L * c->S * c->B;
+  out->host_bytes = (int64_t)c->host_sets * c->E * c->B;
+  out->staging_experts = c->n_staging;
+  out->clock = c->clock;
+  out->steps = c->steps;
+  return MOE_OK;
+}
+
+extern "C" int moe_get_slot_table(moe_ctx* c, int32_t layer, int32_t* out) {
+  if (!c || !out || layer < 0 || layer >= c->L) return MOE_E_INVAL;
+  DeviceGuard g(c->device);
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  HIP_TRY(c, hipMemcpy(out, c->d_tbl + (int64_t)layer * c->E, sizeof(int32_t) * c->E, hipMemcpyDeviceToHost));
+  return MOE_OK;
+}
+
+extern "C" int moe_get_stamps(moe_ctx* c, int32_t layer, uint32_t* out) {
+  if (!c || !out || layer < 0 || layer >= c->L) return MOE_E_INVAL;
+  if (c->S == 0) return MOE_OK;
+  DeviceGuard g(c->device);
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  HIP_TRY(c, hipMemcpy(out, c->d_stamps + (int64_t)layer * c->S, sizeof(uint32_t) * c->S, hipMemcpyDeviceToHost));
+  return MOE_OK;
+}
+
+extern "C" int moe_get_miss_log(moe_ctx* c, uint64_t* out, int64_t cap, int64_t* n) {
+  if (!c || !n || cap < 0 || (cap > 0 && !out)) return MOE_E_INVAL;
+  *n = (int64_t)c->last_log.size();
+  const int64_t m = std::min<int64_t>(cap, *n);
+  if (m > 0) std::memcpy(out, c->last_log.data(), sizeof(uint64_t) * m);
+  return MOE_OK;
+}
+
+extern "C" int moe_get_counts(moe_ctx* c, uint32_t* out) {
+  if (!c || !out) return MOE_E_INVAL;
+  DeviceGuard g(c->device);
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  HIP_TRY(c, hipMemcpy(out, c->d_counts, sizeof(uint32_t) * (size_t)c->L * c->E, hipMemcpyDeviceToHost));
+  return MOE_OK;
+}

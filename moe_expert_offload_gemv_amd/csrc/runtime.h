@@ -1,0 +1,78 @@
+// runtime.h - the context structure shared by the host sources of
+// libmoe_offload.so (internal; the public boundary is include/moe_offload.h).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/moe_offload.h"
+#include "kernels.h"
+
+struct moe_ctx {
+  moe_config cfg{};
+  int device = 0;
+  int32_t L = 0, E = 0, k = 0, H = 0, F = 0, S = 0;
+  moe::ExpertLayout lay{};
+  int64_t B = 0;
+  hipStream_t stream = nullptr;  // caller's stream (nullptr: the null stream)
+  bool own_stream = false;
+
+  // device memory
+  uint8_t* pool = nullptr;             // [L][S] experts
+  int32_t* d_tbl = nullptr;            // [L][E] slot or -1
+  uint32_t* d_stamps = nullptr;        // [L][S]
+  uint32_t* d_counts = nullptr;        // [L][E]
+  uint64_t* d_log = nullptr;           // miss log
+  uint32_t log_cap = 0;
+  moe::Ctrl* d_ctrl = nullptr;
+  uint8_t** d_host_base = nullptr;     // [L] device addresses of the pinned layers
+  int32_t* d_ids = nullptr;            // [max_batch][k]
+  float* d_w = nullptr;
+  const uint8_t** d_addr = nullptr;
+  float* d_h = nullptr;                // [max_batch*k][F]
+  std::vector<void*> routers;          // per layer fp32 [E][H] or null
+
+  // pinned host memory (host_sets distinct sets; layer l uses set l % host_sets)
+  int32_t host_sets = 0;
+  std::vector<uint8_t*> host_layers;      // [L] -> E experts in the device layout
+  std::vector<uint8_t*> host_layers_dev;  // device addresses of the same
+  moe::Ctrl* h_ctrl = nullptr;
+  uint64_t* h_log = nullptr;
+  int32_t* h_tbl = nullptr;
+  uint32_t* h_stamps = nullptr;
+
+  // prefill (borrowed staging blocks and per-pass scratch)
+  int64_t n_staging = 0;
+  uint8_t* staging = nullptr;
+  struct Prefill* pf = nullptr;
+
+  // host mirror of the cache state
+  std::vector<int32_t> tbl, owner;
+  std::vector<uint32_t> stamps, last_miss;
+  std::vector<uint64_t> last_log;
+  std::vector<char> registered;        // per host set
+  bool seeded = false;
+  int64_t clock = 1;
+  int64_t steps = 0;
+
+  // kernel timing (moe_profile)
+  bool profiling = false;
+  std::vector<hipEvent_t> events;      // 4 per timed forward
+  std::vector<int32_t> timed_tokens;   // n_tokens of each pending timed forward
+  int32_t timed_pending = 0;
+  moe_profile_stats prof{};
+
+  std::vector<void*> dev_allocs, host_allocs;
+  std::string err;
+};
+
+int moe_ctx_fail(moe_ctx* c, int code, const char* fmt, ...);
+int moe_ctx_dev_alloc(moe_ctx* c, void** p, size_t bytes, const char* what);
+int moe_ctx_host_alloc(moe_ctx* c, void** p, size_t bytes, unsigned flags, const char* what);
+
+// prefill.cpp
+int moe_prefill_alloc(moe_ctx* c);
+void moe_prefill_release(moe_ctx* c);

@@ -1,0 +1,255 @@
+"""GPU parity of the decode path through the C ABI against the oracle.
+
+Routing ids, miss logs, slot tables, stamps, counts and step statistics are
+compared bit for bit with the oracle's step-by-step policy simulation; layer
+outputs within 2e-3 of the oracle's fp64 result (per token, max abs error
+over max abs value).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import moe_expert_offload_gemv_amd as moe  # noqa: E402
+import oracle  # noqa: E402
+from tests._gpu import TOL, Decode, oracle_policy, token_rel_err  # noqa: E402
+from workload import WORKLOADS, Workload, activations, router_weights, zipf_logits  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _compare_policy(d: Decode, pol, st_gpu, st_orc, layers):
+    wl = d.wl
+    for key in ("hits", "misses", "admissions", "evictions", "tokens"):
+        assert st_gpu[key] == st_orc[key], (key, st_gpu, st_orc)
+    assert st_gpu["hot_bytes"] == st_orc["hits"] * d.B and st_gpu["cold_bytes"] == st_orc["misses"] * d.B
+    tabs = pol.tables()
+    for layer in layers:
+        assert np.array_equal(moe.moe_get_slot_table(d.ctx, layer, wl.n_experts), tabs["table"][layer]), layer
+        assert np.array_equal(moe.moe_get_stamps(d.ctx, layer, d.S), tabs["stamps"][layer]), layer
+    assert np.array_equal(moe.moe_get_miss_log(d.ctx), pol.last_log())
+
+
+def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_alloc=moe.MOE_HOST_COHERENT):
+    d = Decode(wl, slots=slots, seed=seed, host_alloc=host_alloc)
+    pol = oracle_policy(wl, slots, seed=seed)
+    logits = zipf_logits(wl)
+    L, T, k, H = wl.n_layers, wl.tokens, wl.top_k, wl.hidden
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    worst = 0.0
+    for step in range(wl.steps):
+        x0 = activations(wl, step)
+        x = _dev(x0)
+        x64 = x0.astype(np.float64)
+        check = step % check_every == 0
+        for layer in range(L):
+            z = logits[step, layer]
+            moe.moe_forward(d.ctx, layer, T, x, _dev(z), y, ids, w)
+            ids_h = ids.cpu().numpy()
+            ids_o, w_o = oracle.route(z, k)
+            assert np.array_equal(ids_h, ids_o), (step, layer)
+            np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=2e-6, atol=1e-7)
+            pol.forward(layer, ids_o)
+            if check:
+                y_ref, _, _ = oracle.moe_layer(wl.n_experts, k, H, wl.ffn, d.experts(layer, ids_o), x64, logits=z)
+                err = token_rel_err(y.cpu().numpy(), y_ref)
+                worst = max(worst, err)
+                assert err < TOL, (step, layer, err)
+                x64 = x64 + y_ref
+            x += y
+        st_g = moe.moe_cache_step(d.ctx)
+        st_o = pol.step()
+        _compare_policy(d, pol, st_g, st_o, range(L))
+    assert np.array_equal(moe.moe_get_counts(d.ctx, L, wl.n_experts), pol.counts())
+    d.close()
+    return worst
+
+
+def test_tiny_layer_router_in_the_loop():
+    wl = WORKLOADS["tiny-e8k2-h256f512-t4"]
+    d = Decode(wl)
+    moe.moe_register_router(d.ctx, 0, router_weights(wl, 0))  # allowed after seed: no weights move
+    x32 = activations(wl, 0)
+    y = torch.empty((4, 256), dtype=torch.float32, device="cuda")
+    ids = torch.empty((4, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((4, 2), dtype=torch.float32, device="cuda")
+    moe.moe_forward(d.ctx, 0, 4, _dev(x32), None, y, ids, w)
+    W = router_weights(wl, 0)
+    g, u, dn = d.weights[0]
+    y_ref, ids_ref, w_ref = oracle.moe_layer(8, 2, 256, 512, {e: (g[e], u[e], dn[e]) for e in range(8)},
+                                             x32.astype(np.float64), w_router=W, x32=x32)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=2e-6)
+    assert token_rel_err(y.cpu().numpy(), y_ref) < TOL
+    st = moe.moe_cache_step(d.ctx)
+    assert st["misses"] == 0 and st["hits"] == 8 and st["admissions"] == 0 and st["tokens"] == 4
+    assert moe.moe_get_miss_log(d.ctx).size == 0
+    # logits handed in give the same result
+    z = oracle.router_logits(x32, W)
+    y2 = torch.empty_like(y)
+    moe.moe_forward(d.ctx, 0, 4, _dev(x32), _dev(z), y2)
+    assert torch.equal(y, y2)
+    d.close()
+
+
+REDUCED = Workload("decode-e64k8-h2048f1024-l4-b1-rot16", 101, 4, 64, 8, 2048, 1024, tokens=1, steps=40,
+                   zipf_s=1.1, slots=26, rotation=16)
+
+
+def test_decode_reduced_layers_bit_exact_policy():
+    worst = _run_decode(REDUCED, slots=26, check_every=8)
+    print("worst token error", worst)
+
+
+def test_decode_batch_of_five_tokens():
+    wl = Workload("decode-e64k8-h2048f1024-l2-b5", 102, 2, 64, 8, 2048, 1024, tokens=5, steps=12, zipf_s=1.1,
+                  slots=20, rotation=20)
+    _run_decode(wl, slots=20, check_every=3)
+
+
+def test_decode_other_shapes_ragged_lanes():
+    # hidden 4096 (two blocks per lane), ffn 1536 (48 blocks: 16 lanes x 3)
+    wl = Workload("decode-e16k4-h4096f1536-l2-b3", 103, 2, 16, 4, 4096, 1536, tokens=3, steps=6, zipf_s=1.0,
+                  slots=6)
+    _run_decode(wl, slots=6, check_every=2)
+
+
+def test_forced_cold_every_pick_over_pcie():
+    wl = Workload("decode-e32k8-h2048f1024-l2-b2-cold", 104, 2, 32, 8, 2048, 1024, tokens=2, steps=6, zipf_s=1.1)
+    _run_decode(wl, slots=0, check_every=2)
+
+
+def test_noncoherent_pinned_arena():
+    wl = Workload("decode-e32k8-h2048f1024-l2-b1-nc", 105, 2, 32, 8, 2048, 1024, tokens=1, steps=8, zipf_s=1.1,
+                  slots=12)
+    _run_decode(wl, slots=12, check_every=4, host_alloc=moe.MOE_HOST_NONCOHERENT)
+
+
+def test_cold_start_without_seed():
+    wl = Workload("decode-e32k4-h256f512-l3-b2-noseed", 106, 3, 32, 4, 256, 512, tokens=2, steps=40, zipf_s=1.1,
+                  slots=8, rotation=30)
+    _run_decode(wl, slots=8, check_every=10, seed=False)
+
+
+def test_full_pool_never_misses():
+    wl = Workload("decode-e16k4-h256f512-l2-b3-full", 107, 2, 16, 4, 256, 512, tokens=3, steps=5, zipf_s=1.1,
+                  slots=16)
+    d = Decode(wl)
+    logits = zipf_logits(wl)
+    y = torch.empty((3, 256), dtype=torch.float32, device="cuda")
+    for step in range(5):
+        x = _dev(activations(wl, step))
+        for layer in range(2):
+            moe.moe_forward(d.ctx, layer, 3, x, _dev(logits[step, layer]), y)
+        st = moe.moe_cache_step(d.ctx)
+        assert st["misses"] == 0 and st["hits"] == 2 * 3 * 4
+    d.close()
+
+
+def test_accumulate_in_place():
+    wl = Workload("decode-e16k4-h256f512-l1-b2-acc", 108, 1, 16, 4, 256, 512, tokens=2, zipf_s=1.1, slots=8)
+    d = Decode(wl)
+    z = _dev(zipf_logits(wl)[0, 0])
+    x = _dev(activations(wl, 0))
+    y = torch.empty_like(x)
+    moe.moe_forward(d.ctx, 0, 2, x, z, y)
+    x2 = x.clone()
+    moe.moe_forward(d.ctx, 0, 2, x2, z, x2, flags=moe.MOE_ACCUMULATE)
+    torch.testing.assert_close(x2, x + y, rtol=0, atol=0)
+    d.close()
+
+
+def test_graph_capture_replays_match_eager():
+    wl = Workload("decode-e64k8-h2048f1024-l3-b1-graph", 109, 3, 64, 8, 2048, 1024, tokens=1, steps=10,
+                  zipf_s=1.1, slots=24, rotation=4)
+    s = torch.cuda.Stream()
+    eager = Decode(wl, stream=s)
+    graph = Decode(wl, stream=s)
+    logits = zipf_logits(wl)
+    L, H = wl.n_layers, wl.hidden
+    xs = torch.zeros((1, H), dtype=torch.float32, device="cuda")
+    zs = torch.zeros((L, 1, wl.n_experts), dtype=torch.float32, device="cuda")
+    ys = [torch.zeros((1, H), dtype=torch.float32, device="cuda") for _ in range(L)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for layer in range(L):
+                moe.moe_forward(graph.ctx, layer, 1, xs, zs[layer], ys[layer])
+                xs.add_(ys[layer])
+    pol = oracle_policy(wl, 24)
+    for step in range(wl.steps):
+        with torch.cuda.stream(s):
+            xs.copy_(_dev(activations(wl, step)))
+            zs.copy_(_dev(logits[step]))
+            g.replay()
+            st_g = moe.moe_cache_step(graph.ctx)
+            xe = _dev(activations(wl, step))
+            ye = torch.empty_like(xe)
+            for layer in range(L):
+                moe.moe_forward(eager.ctx, layer, 1, xe, _dev(logits[step, layer]), ye)
+                assert torch.equal(ye, ys[layer]), (step, layer)
+                xe += ye
+                pol.forward(layer, oracle.route(logits[step, layer], wl.top_k)[0])
+            st_e = moe.moe_cache_step(eager.ctx)
+        s.synchronize()
+        st_o = pol.step()
+        assert st_g == st_e
+        _compare_policy(graph, pol, st_g, st_o, range(L))
+    eager.close()
+    graph.close()
+
+
+def test_error_codes():
+    wl = Workload("decode-e16k4-h256f512-l2-b2-err", 110, 2, 16, 4, 256, 512, tokens=2, zipf_s=1.1, slots=4)
+    d = Decode(wl, seed=None)
+    x = torch.zeros((2, 256), dtype=torch.float32, device="cuda")
+    z = torch.zeros((2, 16), dtype=torch.float32, device="cuda")
+    y = torch.zeros_like(x)
+
+    def code(fn, *a, **kw):
+        with pytest.raises(moe.MoeError) as ei:
+            fn(*a, **kw)
+        return ei.value.code
+
+    assert code(moe.moe_forward, d.ctx, 0, 2, x, z, y) == moe.MOE_E_STATE  # before seed
+    assert code(moe.moe_cache_step, d.ctx) == moe.MOE_E_STATE
+    moe.moe_seed(d.ctx, d.freq)
+    g = d.weights[0]
+    assert code(moe.moe_register_layer, d.ctx, 0, *g) == moe.MOE_E_STATE  # after seed
+    assert code(moe.moe_forward, d.ctx, 2, 2, x, z, y) == moe.MOE_E_INVAL  # layer out of range
+    assert code(moe.moe_forward, d.ctx, 0, 3, x, z, y) == moe.MOE_E_INVAL  # more tokens than max_batch
+    assert code(moe.moe_forward, d.ctx, 0, 0, x, z, y) == moe.MOE_E_INVAL
+    assert code(moe.moe_forward, d.ctx, 0, 2, x, z, x) == moe.MOE_E_INVAL  # alias without accumulate
+    xb = torch.zeros(2 * 256 + 1, dtype=torch.float32, device="cuda")[1:].view(2, 256)
+    assert code(moe.moe_forward, d.ctx, 0, 2, xb, z, y) == moe.MOE_E_INVAL  # misaligned
+    assert code(moe.moe_forward, d.ctx, 0, 2, x, None, y) == moe.MOE_E_INVAL  # no router
+    assert "router" in moe.moe_last_error(d.ctx)
+    # cache step inside a capture
+    s = torch.cuda.Stream()
+    d2 = Decode(wl, stream=s)
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(cg, stream=s):
+            x.mul_(1.0)
+            rc = moe.lib().moe_cache_step(d2.ctx, None)
+            rc_seed = moe.lib().moe_seed(d2.ctx, None)
+    assert rc == moe.MOE_E_CAPTURING and rc_seed == moe.MOE_E_CAPTURING
+    d2.close()
+    # a pool larger than the device
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_create(64, 4096, 4, 4096, 4096, pool_budget_bytes=1 << 50)  # 7.4 TB pool
+    assert ei.value.code in (moe.MOE_E_NOMEM,)
+    d.close()
+
+
+def test_shared_host_sets():
+    # 5 layers over 2 pinned host sets: layer l reads set l % 2 (weights of layer l % 2)
+    wl = Workload("decode-e32k8-h2048f1024-l5-b2-sets", 111, 5, 32, 8, 2048, 1024, tokens=2, steps=10, zipf_s=1.1,
+                  slots=10, rotation=5, distinct_layers=2)
+    _run_decode(wl, slots=10, check_every=3)

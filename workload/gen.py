@@ -91,20 +91,22 @@ WORKLOADS = {
     for w in [
         # single MoE layer, router in the loop, every expert resident
         Workload("tiny-e8k2-h256f512-t4", 1, 1, 8, 2, 256, 512, tokens=4, steps=1, slots=8),
-        # batch-1 decode, 48 layers, half the experts in HBM
+        # batch-1 decode, 48 layers, half the experts in HBM; 32 distinct host
+        # weight sets (58 GB pinned: the host allows about 66 GiB of pinned memory)
         Workload("decode-e512k8-h2048f1024-l48-b1", 2, 48, 512, 8, 2048, 1024, tokens=1, steps=256,
-                 zipf_s=1.1, slots=256),
+                 zipf_s=1.1, slots=256, distinct_layers=32),
         # one layer of the same shape, 4096-token prompt pass, half the experts resident
         Workload("prefill-e512k8-h2048f1024-t4096", 3, 1, 512, 8, 2048, 1024, tokens=4096, zipf_s=1.1,
                  slots=256, prefill=True),
         # 2048 decode steps, popularity permutation re-drawn every 512 tokens, 40% pool
         Workload("policy-e512k8-h2048f1024-l48-rot512", 4, 48, 512, 8, 2048, 1024, tokens=1, steps=2048,
-                 zipf_s=1.1, slots=204, rotation=512),
-        # 60 layers of 256 experts (hidden 4096, ffn 1536): 163 GB of experts, 251 slots per layer
+                 zipf_s=1.1, slots=204, rotation=512, distinct_layers=32),
+        # 60 layers of 256 experts (hidden 4096, ffn 1536): 163 GB of experts, 251 slots per layer;
+        # 20 distinct host weight sets (54 GB pinned)
         Workload("large-e256k8-h4096f1536-l60-b1", 5, 60, 256, 8, 4096, 1536, tokens=1, steps=256,
-                 zipf_s=1.0, slots=251),
+                 zipf_s=1.0, slots=251, distinct_layers=20),
         Workload("large-e256k8-h4096f1536-l60-b32", 6, 60, 256, 8, 4096, 1536, tokens=32, steps=256,
-                 zipf_s=1.0, slots=251),
+                 zipf_s=1.0, slots=251, distinct_layers=20),
         Workload("large-e256k8-h4096f1536-t12288", 7, 1, 256, 8, 4096, 1536, tokens=12288, zipf_s=1.0,
                  slots=251, prefill=True),
     ]
