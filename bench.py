@@ -198,9 +198,12 @@ def main():
         t_prof = time.perf_counter() - t1
         prof = moe.moe_profile(ctx, 0)
     fw = max(prof["forwards"], 1)
-    gu_ms = prof["gateup_ms"] / fw
-    gu_bytes = prof["gateup_bytes"] / fw
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    gu_bytes = prof["gateup_bytes_per_pick"]
+    hot_gu_us = prof["hot_gateup_ms"] / fw * 1e3
+    hot_gu_bytes = prof["hot_picks"] * gu_bytes / fw
+    achieved = hot_gu_bytes / (hot_gu_us * 1e-6) / 1e9
+    cold_rate = prof["cold_picks"] * gu_bytes / max(prof["cold_gateup_ms"], 1e-9) / 1e6
+    cold_dn_rate = prof["cold_picks"] * prof["down_bytes_per_pick"] / max(prof["cold_down_ms"], 1e-9) / 1e6
     log(f"kernel timing ({prof_steps} eager steps, {prof_steps * T / t_prof:.1f} tokens/s): {prof}")
     moe.moe_destroy(ctx)
 
@@ -228,8 +231,13 @@ def main():
         "admissions_per_step": round(acc["admissions"] / args.steps, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "gemv_gateup_kernel (decode workload, hot and cold picks)",
-                     "avg_launch_us": round(gu_ms * 1e3, 2), "bytes_per_launch": int(gu_bytes)},
+                     "kernel": "gemv_gateup_kernel, hot picks (gate+up+SwiGLU from the HBM pool)",
+                     "avg_launch_us": round(hot_gu_us, 2), "bytes_per_launch": int(hot_gu_bytes)},
+        "pcie": {"cold_gateup_GBps": round(cold_rate, 2), "cold_down_GBps": round(cold_dn_rate, 2),
+                 "peak": PCIE_PEAK_GBPS, "frac": round(cold_rate / PCIE_PEAK_GBPS, 4),
+                 "kernel": "gemv_gateup_kernel, cold picks (zero-copy reads of pinned host memory)"},
+        "per_layer_us": {k_: round(prof[k_ + "_ms"] / fw * 1e3, 2)
+                         for k_ in ("route", "hot_gateup", "hot_down", "cold_gateup", "cold_down")},
     }
 
     if not args.no_side_passes:
@@ -237,20 +245,23 @@ def main():
         hot = kernel_pass(moe, torch, wl, E, side, 32, stream, host_alloc, logits_all, x0_all)
         cold = kernel_pass(moe, torch, wl, 0, side, 8, stream, host_alloc, logits_all, x0_all)
 
-        def rate(p, key, bkey):
-            return p[bkey] / max(p[key], 1e-9) / 1e6  # bytes / ms -> GB/s
+        def rate(p, ms_key, picks_key, bytes_key):
+            return p[picks_key] * p[bytes_key] / max(p[ms_key], 1e-9) / 1e6  # bytes / ms -> GB/s
 
+        hgu = rate(hot, "hot_gateup_ms", "hot_picks", "gateup_bytes_per_pick")
         result["kernels_all_hot"] = {
-            "gateup_GBps": round(rate(hot, "gateup_ms", "gateup_bytes"), 1),
-            "down_GBps": round(rate(hot, "down_ms", "down_bytes"), 1),
-            "gateup_us": round(hot["gateup_ms"] / hot["forwards"] * 1e3, 2),
-            "down_us": round(hot["down_ms"] / hot["forwards"] * 1e3, 2),
-            "route_us": round(hot["route_ms"] / hot["forwards"] * 1e3, 2),
-            "frac_of_hbm": round(rate(hot, "gateup_ms", "gateup_bytes") / HBM_PEAK_GBPS, 4)}
+            "gateup_GBps": round(hgu, 1),
+            "down_GBps": round(rate(hot, "hot_down_ms", "hot_picks", "down_bytes_per_pick"), 1),
+            "per_layer_us": {k_: round(hot[k_ + "_ms"] / hot["forwards"] * 1e3, 2)
+                             for k_ in ("route", "hot_gateup", "hot_down", "cold_gateup", "cold_down")},
+            "frac_of_hbm": round(hgu / HBM_PEAK_GBPS, 4)}
+        cgu = rate(cold, "cold_gateup_ms", "cold_picks", "gateup_bytes_per_pick")
         result["kernels_all_cold"] = {
-            "gateup_GBps": round(rate(cold, "gateup_ms", "gateup_bytes"), 2),
-            "down_GBps": round(rate(cold, "down_ms", "down_bytes"), 2),
-            "frac_of_pcie": round(rate(cold, "gateup_ms", "gateup_bytes") / PCIE_PEAK_GBPS, 4)}
+            "gateup_GBps": round(cgu, 2),
+            "down_GBps": round(rate(cold, "cold_down_ms", "cold_picks", "down_bytes_per_pick"), 2),
+            "per_layer_us": {k_: round(cold[k_ + "_ms"] / cold["forwards"] * 1e3, 2)
+                             for k_ in ("route", "hot_gateup", "hot_down", "cold_gateup", "cold_down")},
+            "frac_of_pcie": round(cgu / PCIE_PEAK_GBPS, 4)}
         # DMA ceiling: pinned host -> HBM copy of 1 GiB
         src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
         dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -74,7 +74,7 @@ extern "C" {
 typedef struct moe_ctx moe_ctx;
 
 typedef struct {
-  int32_t n_layers;        /* L >= 1                                          */
+  int32_t n_layers;        /* L, 1..2^19 (the miss log keeps l in 19 bits)    */
   int32_t n_experts;       /* E, 1..4096 (the miss log keeps e in 12 bits)    */
   int32_t top_k;           /* k, 1..min(E, 32)                                */
   int32_t hidden;          /* H, multiple of 32                               */
@@ -123,11 +123,15 @@ typedef struct {
 
 typedef struct {
   int64_t forwards;           /* moe_forward calls timed                      */
-  double  route_ms;           /* summed durations of the routing kernel       */
-  double  gateup_ms;          /* ... of the gate/up GEMV (+ SwiGLU)           */
-  double  down_ms;            /* ... of the down GEMV (+ weighted combine)    */
-  int64_t gateup_bytes;       /* expert bytes the timed gate/up GEMVs read    */
-  int64_t down_bytes;         /* expert bytes the timed down GEMVs read       */
+  double  route_ms;           /* summed durations: routing + lookup kernel    */
+  double  hot_gateup_ms;      /* gate/up GEMV + SwiGLU of the hot picks (HBM) */
+  double  hot_down_ms;        /* down GEMV of the hot picks (HBM)             */
+  double  cold_gateup_ms;     /* gate/up GEMV + SwiGLU of the cold picks (PCIe) */
+  double  cold_down_ms;       /* down GEMV of the cold picks + combine        */
+  int64_t hot_picks;          /* picks the timed forwards served from HBM     */
+  int64_t cold_picks;         /* picks they served over PCIe                  */
+  int64_t gateup_bytes_per_pick; /* expert bytes of gate + up                 */
+  int64_t down_bytes_per_pick;   /* expert bytes of down                      */
 } moe_profile_stats;
 
 /* Size in bytes of one expert (gate + up + down) in MOE_Q4_32_F16. */
@@ -173,8 +177,8 @@ MOE_API int moe_seed(moe_ctx* ctx, const uint32_t* freq);
  *   per pick: the expert is found through the layer's slot table ([A6000]
  *            pointer table): resident -> its HBM slot, its use-stamp raised to
  *            the pick's token clock; else -> zero-copy read of pinned host
- *            memory and an entry (t<<32 | layer<<12 | expert) appended to the
- *            miss log;
+ *            memory and a miss (t<<32 | layer<<12 | expert) recorded for the
+ *            step's miss log;
  *   h = silu(W_gate x) * (W_up x); y_pick = W_down h;
  *   y[t] (=|+=) sum over picks i = 0..k-1 of w_i * y_pick_i, in pick order.
  * Token t of the batch carries clock c + t where c is the context clock.
@@ -212,9 +216,10 @@ MOE_API int moe_cache_step(moe_ctx* ctx, moe_step_stats* out);
 
 /* Kernel timing for measurement: enable = 1 turns it on and clears the
  * totals, 0 turns it off, -1 leaves it as is; out (may be NULL) receives the
- * totals accumulated so far. While on, moe_forward brackets its three kernels
- * with HIP events (so it must not be captured: MOE_E_CAPTURING) and
- * moe_cache_step adds their durations once the stream has drained. */
+ * totals accumulated so far. While on, moe_forward launches each of its
+ * kernels with start/stop events timed by the dispatch (so it must not be
+ * captured: MOE_E_CAPTURING), and moe_cache_step adds their durations and the
+ * step's hot and cold pick counts once the stream has drained. */
 MOE_API int moe_profile(moe_ctx* ctx, int32_t enable, moe_profile_stats* out);
 
 /* Introspection (host outputs; each synchronises the stream). */

@@ -59,8 +59,10 @@ class moe_step_stats(C.Structure):
 
 
 class moe_profile_stats(C.Structure):
-    _fields_ = [("forwards", C.c_int64), ("route_ms", C.c_double), ("gateup_ms", C.c_double),
-                ("down_ms", C.c_double), ("gateup_bytes", C.c_int64), ("down_bytes", C.c_int64)]
+    _fields_ = [("forwards", C.c_int64), ("route_ms", C.c_double), ("hot_gateup_ms", C.c_double),
+                ("hot_down_ms", C.c_double), ("cold_gateup_ms", C.c_double), ("cold_down_ms", C.c_double),
+                ("hot_picks", C.c_int64), ("cold_picks", C.c_int64), ("gateup_bytes_per_pick", C.c_int64),
+                ("down_bytes_per_pick", C.c_int64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

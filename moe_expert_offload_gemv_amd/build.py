@@ -17,7 +17,7 @@ LIB = os.path.join(LIBDIR, "libmoe_offload.so")
 OBJDIR = os.path.join(ROOT, "_build", "moe_offload")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["decode.hip", "prefill_kernels.hip", "runtime.cpp", "prefill.cpp"]
+SOURCES = ["route.hip", "decode.hip", "prefill_kernels.hip", "runtime.cpp", "prefill.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

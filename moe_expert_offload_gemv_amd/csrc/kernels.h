@@ -1,6 +1,7 @@
 // kernels.h - host-side launchers of the gfx950 kernels (internal to
 // libmoe_offload.so; the public boundary is include/moe_offload.h).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -11,9 +12,12 @@ namespace moe {
 struct Ctrl {
   uint32_t clock;        // token clock of token 0 of the current step
   uint32_t step_tokens;  // max n_tokens over the forwards of the step
-  uint32_t log_count;    // miss-log entries appended in the step (may exceed capacity)
-  uint32_t hits;         // picks served from the pool in the step
+  uint32_t reserved[2];
 };
+
+// A pick record: (clock << 32) | hit << 31 | layer << 12 | expert. The miss
+// log of a step is its records without the hit bit, in ascending order.
+constexpr uint64_t kRecordHit = 1ull << 31;
 
 // Device layout of one expert (gate, up, down; each a nibble plane of
 // [rows][k/32][16 B] followed by a scale plane of [rows][k/32] fp16).
@@ -42,6 +46,19 @@ struct GemvShape {
 };
 bool gemv_shape(int kb, GemvShape* out);
 
+// Tag of a pick: where its expert's weights are read from.
+constexpr uint8_t kHot = 0;   // HBM pool slot (or prefill staging)
+constexpr uint8_t kCold = 1;  // pinned host memory, zero-copy over PCIe
+// which picks a GEMV launch computes
+enum { kAll = 0, kOnlyHot = 1, kOnlyCold = 2 };
+
+// Stream of a launch; with start/stop events the launch is timed by the
+// dispatch itself (hipExtLaunchKernelGGL).
+struct Launch {
+  hipStream_t stream = nullptr;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 struct RouteArgs {
   const float* logits;   // [T][E] or nullptr (router)
   const float* x;        // [T][H] (router input)
@@ -50,8 +67,7 @@ struct RouteArgs {
   const int32_t* tbl;    // [E] slot table row of the layer
   uint32_t* stamps;      // [S] stamps of the layer
   uint32_t* counts;      // [E] pick counts of the layer
-  uint64_t* log;         // miss log
-  uint32_t log_cap;
+  uint64_t* records;     // [T][k] pick records of the layer
   Ctrl* ctrl;
   const uint8_t* pool;   // first slot of the layer
   const uint8_t* host;   // device address of the layer's pinned experts
@@ -60,22 +76,36 @@ struct RouteArgs {
   int32_t* ids;          // [T][k] internal
   float* w;              // [T][k] internal
   const uint8_t** addr;  // [T][k] per-pick expert address
+  uint8_t* kind;         // [T][k] kHot / kCold
   int32_t* ids_user;     // optional copies for the caller
   float* w_user;
   int32_t policy;        // 1: stamps, miss log, counts, step tokens; 0: none
 };
-hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, const Launch& l);
+
+// Launch on l.stream; timed by the dispatch itself when l carries events.
+template <typename... Args, typename... P>
+inline hipError_t launch(void (*kern)(Args...), dim3 grid, dim3 block, const Launch& l, P... params) {
+  if (l.start)
+    hipExtLaunchKernelGGL(kern, grid, block, 0, l.stream, l.start, l.stop, 0, params...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, 0, l.stream, params...);
+  return hipGetLastError();
+}
 
 struct GemvArgs {
   const float* x;               // gate/up: activations [T][H]; down: h [P][F]
   const uint8_t* const* addr;   // [P] expert base address per pick
+  const uint8_t* kind;          // [P] tag of each pick
   const float* w;               // down: routing weights [P]
-  float* out;                   // gate/up: h [P][F]; down: y [T][H]
+  float* out;                   // gate/up: h [P][F]; down+combine: y [T][H]
+  float* ypick;                 // [P][H] down output of the picks another launch computed
   int32_t T, k, H, F;
-  int32_t accumulate;           // down: y += result
+  int32_t accumulate;           // combine: y += result
   ExpertLayout lay;
 };
-hipError_t launch_gemv_gateup(const GemvArgs& a, hipStream_t s);
-hipError_t launch_gemv_down_combine(const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv_gateup(const GemvArgs& a, const Launch& l, int mode);
+hipError_t launch_gemv_down_pick(const GemvArgs& a, const Launch& l, int mode);
+hipError_t launch_gemv_down_combine(const GemvArgs& a, const Launch& l, int mode);
 
 }  // namespace moe

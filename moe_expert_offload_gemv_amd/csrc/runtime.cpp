@@ -158,7 +158,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   *out = nullptr;
   const moe_config& k = *cfg;
   if (k.host_sets < 0 || k.host_sets > k.n_layers) return g_create_error = "host_sets outside 0..n_layers", MOE_E_INVAL;
-  if (k.n_layers < 1 || k.n_experts < 1 || k.n_experts > 4096 || k.top_k < 1 || k.top_k > 32 ||
+  if (k.n_layers < 1 || k.n_layers > (1 << 19) || k.n_experts < 1 || k.n_experts > 4096 || k.top_k < 1 || k.top_k > 32 ||
       k.top_k > k.n_experts || k.hidden < 32 || k.ffn < 32 || k.hidden % 32 || k.ffn % 32 ||
       k.quant != MOE_Q4_32_F16 || k.window_tokens < 1 || (k.admit_misses != 1 && k.admit_misses != 2) ||
       k.max_batch_tokens < 1 || k.max_batch_tokens > 256 || k.max_prefill_tokens < 0 || k.n_layers > (1 << 20) ||
@@ -191,11 +191,12 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
 
   // small device state first, so the pool sizing sees what is left
   const int64_t L = c->L, E = c->E, K = c->k;
-  c->log_cap = (uint32_t)std::min<int64_t>((int64_t)k.max_batch_tokens * L * K, 0xffffffffLL);
+  c->rec_stride = (int64_t)k.max_batch_tokens * K;
   int rc;
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_tbl, sizeof(int32_t) * L * E, "slot tables"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_counts, sizeof(uint32_t) * L * E, "counts"))) return fail(rc);
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_log, sizeof(uint64_t) * c->log_cap, "miss log"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_records, sizeof(uint64_t) * L * c->rec_stride, "pick records")))
+    return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ctrl, sizeof(Ctrl), "control"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_host_base, sizeof(uint8_t*) * L, "host bases"))) return fail(rc);
   const int64_t P = (int64_t)k.max_batch_tokens * K;
@@ -203,12 +204,15 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_w, sizeof(float) * P, "weights"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_addr, sizeof(uint8_t*) * P, "addresses"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_h, sizeof(float) * P * c->F, "h"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_kind, P, "pick tags"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ypick, sizeof(float) * P * c->H, "pick outputs"))) return fail(rc);
   if ((rc = moe_prefill_alloc(c))) return fail(rc);
 
   // pinned host staging for the small transfers of the cache step
   const unsigned pin = hipHostMallocDefault;
   if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_ctrl, sizeof(Ctrl), pin, "ctrl staging"))) return fail(rc);
-  if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_log, sizeof(uint64_t) * c->log_cap, pin, "log staging")))
+  if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_records, sizeof(uint64_t) * L * c->rec_stride, pin,
+                               "record staging")))
     return fail(rc);
   if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_tbl, sizeof(int32_t) * L * E, pin, "table staging")))
     return fail(rc);
@@ -260,16 +264,19 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->last_miss.assign(L * E, 0);
   if (hipMemset(c->d_tbl, 0xff, sizeof(int32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_counts, 0, sizeof(uint32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
+  if (hipMemset(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_stamps, 0, sizeof(uint32_t) * L * std::max<int64_t>(S, 1)) != hipSuccess)
     return fail(MOE_E_HIP);
-  Ctrl z{1, 0, 0, 0};
+  Ctrl z{1, 0, {0, 0}};
   if (hipMemcpy(c->d_ctrl, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return fail(MOE_E_HIP);
-  // events for kernel timing: four per forward, enough for one step of every layer
+  // events for kernel timing: a start/stop pair per kernel of a forward,
+  // enough for one step of every layer
   const int64_t n_timed = L + 16;
-  c->events.reserve(4 * n_timed);
-  for (int64_t i = 0; i < 4 * n_timed; ++i) {
+  c->events.reserve(2 * kTimedKernels * n_timed);
+  for (int64_t i = 0; i < 2 * kTimedKernels * n_timed; ++i) {
     hipEvent_t ev;
-    if (hipEventCreate(&ev) != hipSuccess) return fail(MOE_E_HIP);
+    // timing only: no system-scope release fence when the event completes
+    if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return fail(MOE_E_HIP);
     c->events.push_back(ev);
   }
   c->timed_tokens.assign(n_timed, 0);
@@ -345,7 +352,8 @@ extern "C" int moe_seed(moe_ctx* c, const uint32_t* freq) {
   HIP_TRY(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * L * E, hipMemcpyHostToDevice, c->stream));
   HIP_TRY(c, hipMemsetAsync(c->d_stamps, 0, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), c->stream));
   HIP_TRY(c, hipMemsetAsync(c->d_counts, 0, sizeof(uint32_t) * L * E, c->stream));
-  *c->h_ctrl = Ctrl{1, 0, 0, 0};
+  HIP_TRY(c, hipMemsetAsync(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride, c->stream));
+  *c->h_ctrl = Ctrl{1, 0, {0, 0}};
   HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   c->clock = 1;
@@ -373,15 +381,21 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   if (!logits && !c->routers[layer]) return moe_ctx_fail(c, MOE_E_INVAL, "forward: no logits and no router");
   if (!c->seeded) return moe_ctx_fail(c, MOE_E_STATE, "forward before moe_seed");
   DeviceGuard g(c->device);
-  hipEvent_t* ev = nullptr;
+  hipEvent_t* ev = nullptr;  // kTimedKernels start/stop pairs
   if (c->profiling) {
     if (stream_capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "forward with timing on while capturing");
     if ((size_t)c->timed_pending < c->timed_tokens.size()) {
-      ev = &c->events[4 * (size_t)c->timed_pending];
+      ev = &c->events[2 * kTimedKernels * (size_t)c->timed_pending];
       c->timed_tokens[c->timed_pending++] = n_tokens;
     }
   }
-  if (ev) HIP_TRY(c, hipEventRecord(ev[0], c->stream));
+  auto on = [&](hipStream_t s, int kernel) {
+    moe::Launch l;
+    l.stream = s;
+    if (ev) l.start = ev[2 * kernel], l.stop = ev[2 * kernel + 1];
+    return l;
+  };
+  hipStream_t A = c->stream;
 
   moe::RouteArgs ra{};
   ra.logits = logits;
@@ -391,50 +405,56 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   ra.tbl = c->d_tbl + (int64_t)layer * c->E;
   ra.stamps = c->d_stamps + (int64_t)layer * std::max(c->S, 1);
   ra.counts = c->d_counts + (int64_t)layer * c->E;
-  ra.log = c->d_log;
-  ra.log_cap = c->log_cap;
+  ra.records = c->d_records + (int64_t)layer * c->rec_stride;
   ra.ctrl = c->d_ctrl;
   ra.pool = c->pool + (int64_t)layer * c->S * c->B;
   ra.host = c->host_layers_dev[layer];
   ra.expert_bytes = c->B;
-  ra.ids = c->d_ids, ra.w = c->d_w, ra.addr = c->d_addr;
+  ra.ids = c->d_ids, ra.w = c->d_w, ra.addr = c->d_addr, ra.kind = c->d_kind;
   ra.ids_user = ids, ra.w_user = w;
   ra.policy = 1;
-  HIP_TRY(c, moe::launch_route(ra, c->stream));
-  if (ev) HIP_TRY(c, hipEventRecord(ev[1], c->stream));
+  HIP_TRY(c, moe::launch_route(ra, on(A, kRoute)));
 
   moe::GemvArgs ga{};
   ga.x = x;
   ga.addr = c->d_addr;
+  ga.kind = c->d_kind;
+  ga.w = c->d_w;
   ga.out = c->d_h;
+  ga.ypick = c->d_ypick;
   ga.T = n_tokens, ga.k = c->k, ga.H = c->H, ga.F = c->F;
   ga.lay = c->lay;
-  HIP_TRY(c, moe::launch_gemv_gateup(ga, c->stream));
-  if (ev) HIP_TRY(c, hipEventRecord(ev[2], c->stream));
-
-  moe::GemvArgs da = ga;
-  da.x = c->d_h;
-  da.w = c->d_w;
-  da.out = y;
-  da.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
-  HIP_TRY(c, moe::launch_gemv_down_combine(da, c->stream));
-  if (ev) HIP_TRY(c, hipEventRecord(ev[3], c->stream));
+  moe::GemvArgs dn = ga;
+  dn.x = c->d_h;
+  dn.out = y;
+  dn.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+  if (!ev) {
+    // hot picks stream from HBM while cold picks stream over PCIe, in one launch
+    HIP_TRY(c, moe::launch_gemv_gateup(ga, on(A, 0), moe::kAll));
+    HIP_TRY(c, moe::launch_gemv_down_combine(dn, on(A, 0), moe::kAll));
+  } else {
+    // timing: the same work split by tag, one launch each, in stream order
+    HIP_TRY(c, moe::launch_gemv_gateup(ga, on(A, kColdGateUp), moe::kOnlyCold));
+    HIP_TRY(c, moe::launch_gemv_gateup(ga, on(A, kHotGateUp), moe::kOnlyHot));
+    HIP_TRY(c, moe::launch_gemv_down_pick(dn, on(A, kHotDown), moe::kOnlyHot));
+    HIP_TRY(c, moe::launch_gemv_down_combine(dn, on(A, kColdDownCombine), moe::kOnlyCold));
+  }
   return MOE_OK;
 }
 
 // Add the durations of the pending timed forwards (the stream must be drained).
 static int flush_profile(moe_ctx* c) {
   for (int32_t i = 0; i < c->timed_pending; ++i) {
-    float t[3] = {0, 0, 0};
-    for (int j = 0; j < 3; ++j)
-      HIP_TRY(c, hipEventElapsedTime(&t[j], c->events[4 * (size_t)i + j], c->events[4 * (size_t)i + j + 1]));
-    const int64_t picks = (int64_t)c->timed_tokens[i] * c->k;
+    float t[kTimedKernels];
+    for (int j = 0; j < kTimedKernels; ++j)
+      HIP_TRY(c, hipEventElapsedTime(&t[j], c->events[2 * (kTimedKernels * (size_t)i + j)],
+                                     c->events[2 * (kTimedKernels * (size_t)i + j) + 1]));
     c->prof.forwards += 1;
-    c->prof.route_ms += t[0];
-    c->prof.gateup_ms += t[1];
-    c->prof.down_ms += t[2];
-    c->prof.gateup_bytes += picks * (c->lay.down_nib - c->lay.gate_nib);
-    c->prof.down_bytes += picks * (c->lay.bytes - c->lay.down_nib);
+    c->prof.route_ms += t[kRoute];
+    c->prof.hot_gateup_ms += t[kHotGateUp];
+    c->prof.hot_down_ms += t[kHotDown];
+    c->prof.cold_gateup_ms += t[kColdGateUp];
+    c->prof.cold_down_ms += t[kColdDownCombine];
   }
   c->timed_pending = 0;
   return MOE_OK;
@@ -451,6 +471,8 @@ extern "C" int moe_profile(moe_ctx* c, int32_t enable, moe_profile_stats* out) {
   if (enable == 1) {
     c->profiling = true;
     c->prof = moe_profile_stats{};
+    c->prof.gateup_bytes_per_pick = c->lay.down_nib - c->lay.gate_nib;
+    c->prof.down_bytes_per_pick = c->lay.bytes - c->lay.down_nib;
   } else if (enable == 0) {
     c->profiling = false;
   }
@@ -468,30 +490,44 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
   if (stream_capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "cache_step while capturing");
   const int64_t L = c->L, E = c->E, S = c->S, B = c->B;
 
+  // one round trip: the control words, every layer's pick records, the stamps
   HIP_TRY(c, hipMemcpyAsync(c->h_ctrl, c->d_ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost, c->stream));
+  HIP_TRY(c, hipMemcpyAsync(c->h_records, c->d_records, sizeof(uint64_t) * L * c->rec_stride, hipMemcpyDeviceToHost,
+                            c->stream));
+  if (S > 0)
+    HIP_TRY(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * L * S, hipMemcpyDeviceToHost, c->stream));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   const Ctrl st = *c->h_ctrl;
-  if (c->timed_pending > 0) {
-    int rc = flush_profile(c);
-    if (rc) return rc;
+  if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * L * S);
+  // records of this step carry clocks in [clock, clock + step tokens); older ones are stale
+  int64_t hits = 0;
+  c->last_log.clear();
+  const uint64_t t_lo = (uint64_t)c->clock, t_hi = (uint64_t)c->clock + st.step_tokens;
+  for (int64_t i = 0; i < L * c->rec_stride; ++i) {
+    const uint64_t r = c->h_records[i];
+    const uint64_t t = r >> 32;
+    if (t < t_lo || t >= t_hi) continue;
+    if (r & moe::kRecordHit)
+      ++hits;
+    else
+      c->last_log.push_back(r);
   }
-  const uint32_t n = std::min(st.log_count, c->log_cap);
-  if (n > 0) {
-    HIP_TRY(c, hipMemcpyAsync(c->h_log, c->d_log, sizeof(uint64_t) * n, hipMemcpyDeviceToHost, c->stream));
-    if (S > 0)
-      HIP_TRY(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * L * S, hipMemcpyDeviceToHost,
-                                c->stream));
-    HIP_TRY(c, hipStreamSynchronize(c->stream));
-    if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * L * S);
+  const int64_t misses = (int64_t)c->last_log.size();
+  if (c->profiling) {
+    if (c->timed_pending > 0) {
+      int rc = flush_profile(c);
+      if (rc) return rc;
+    }
+    c->prof.hot_picks += hits;
+    c->prof.cold_picks += misses;
   }
   // canonical order: ascending 64-bit entries (clock, then layer, then expert)
-  c->last_log.assign(c->h_log, c->h_log + n);
   std::sort(c->last_log.begin(), c->last_log.end());
 
   int64_t admissions = 0, evictions = 0;
   for (uint64_t entry : c->last_log) {
     const uint32_t t = (uint32_t)(entry >> 32);
-    const int64_t l = (int64_t)((entry >> 12) & 0xfffff);
+    const int64_t l = (int64_t)((entry >> 12) & 0x7ffff);
     const int64_t e = (int64_t)(entry & 0xfff);
     if (l >= L || e >= E) continue;
     const int64_t te = l * E + e;
@@ -537,24 +573,21 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
                               c->stream));
   }
   c->clock += st.step_tokens;
-  *c->h_ctrl = Ctrl{(uint32_t)c->clock, 0, 0, 0};
+  *c->h_ctrl = Ctrl{(uint32_t)c->clock, 0, {0, 0}};
   HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
 
   if (out) {
     out->step = c->steps;
     out->tokens = st.step_tokens;
-    out->hits = st.hits;
-    out->misses = st.log_count;
+    out->hits = hits;
+    out->misses = misses;
     out->admissions = admissions;
     out->evictions = evictions;
-    out->hot_bytes = (int64_t)st.hits * B;
-    out->cold_bytes = (int64_t)st.log_count * B;
+    out->hot_bytes = hits * B;
+    out->cold_bytes = misses * B;
     out->copied_bytes = admissions * B;
   }
   c->steps += 1;
-  if (st.log_count > c->log_cap)
-    return moe_ctx_fail(c, MOE_E_STATE, "miss log overflow: %u entries, capacity %u (one forward per layer per step)",
-                        st.log_count, c->log_cap);
   return MOE_OK;
 }
 

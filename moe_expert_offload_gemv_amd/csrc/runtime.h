@@ -11,6 +11,9 @@
 #include "../../include/moe_offload.h"
 #include "kernels.h"
 
+// kernels of a forward, in the order of their timing events
+enum { kRoute = 0, kHotGateUp, kHotDown, kColdGateUp, kColdDownCombine, kTimedKernels };
+
 struct moe_ctx {
   moe_config cfg{};
   int device = 0;
@@ -25,14 +28,16 @@ struct moe_ctx {
   int32_t* d_tbl = nullptr;            // [L][E] slot or -1
   uint32_t* d_stamps = nullptr;        // [L][S]
   uint32_t* d_counts = nullptr;        // [L][E]
-  uint64_t* d_log = nullptr;           // miss log
-  uint32_t log_cap = 0;
+  uint64_t* d_records = nullptr;       // [L][max_batch*k] pick records of the step
+  int64_t rec_stride = 0;              // records per layer
   moe::Ctrl* d_ctrl = nullptr;
   uint8_t** d_host_base = nullptr;     // [L] device addresses of the pinned layers
   int32_t* d_ids = nullptr;            // [max_batch][k]
   float* d_w = nullptr;
   const uint8_t** d_addr = nullptr;
   float* d_h = nullptr;                // [max_batch*k][F]
+  uint8_t* d_kind = nullptr;           // [max_batch*k] hot / cold tag
+  float* d_ypick = nullptr;            // [max_batch*k][H] down output of hot picks
   std::vector<void*> routers;          // per layer fp32 [E][H] or null
 
   // pinned host memory (host_sets distinct sets; layer l uses set l % host_sets)
@@ -40,7 +45,7 @@ struct moe_ctx {
   std::vector<uint8_t*> host_layers;      // [L] -> E experts in the device layout
   std::vector<uint8_t*> host_layers_dev;  // device addresses of the same
   moe::Ctrl* h_ctrl = nullptr;
-  uint64_t* h_log = nullptr;
+  uint64_t* h_records = nullptr;
   int32_t* h_tbl = nullptr;
   uint32_t* h_stamps = nullptr;
 
@@ -60,7 +65,7 @@ struct moe_ctx {
 
   // kernel timing (moe_profile)
   bool profiling = false;
-  std::vector<hipEvent_t> events;      // 4 per timed forward
+  std::vector<hipEvent_t> events;      // start/stop per kernel per timed forward
   std::vector<int32_t> timed_tokens;   // n_tokens of each pending timed forward
   int32_t timed_pending = 0;
   moe_profile_stats prof{};

@@ -253,3 +253,42 @@ def test_shared_host_sets():
     wl = Workload("decode-e32k8-h2048f1024-l5-b2-sets", 111, 5, 32, 8, 2048, 1024, tokens=2, steps=10, zipf_s=1.1,
                   slots=10, rotation=5, distinct_layers=2)
     _run_decode(wl, slots=10, check_every=3)
+
+
+def test_kernel_timing_hook():
+    wl = Workload("decode-e32k8-h2048f1024-l3-b2-prof", 112, 3, 32, 8, 2048, 1024, tokens=2, steps=4, zipf_s=1.1,
+                  slots=12)
+    d = Decode(wl)
+    logits = zipf_logits(wl)
+    y = torch.empty((2, 2048), dtype=torch.float32, device="cuda")
+    moe.moe_profile(d.ctx, 1)
+    tot = {"hits": 0, "misses": 0}
+    for step in range(wl.steps):
+        x = _dev(activations(wl, step))
+        for layer in range(3):
+            moe.moe_forward(d.ctx, layer, 2, x, _dev(logits[step, layer]), y)
+        st = moe.moe_cache_step(d.ctx)
+        tot["hits"] += st["hits"]
+        tot["misses"] += st["misses"]
+    prof = moe.moe_profile(d.ctx, 0)
+    assert prof["forwards"] == 3 * wl.steps
+    assert prof["hot_picks"] == tot["hits"] and prof["cold_picks"] == tot["misses"]
+    assert tot["hits"] + tot["misses"] == wl.steps * 3 * 2 * 8
+    for key in ("route_ms", "hot_gateup_ms", "hot_down_ms", "cold_gateup_ms", "cold_down_ms"):
+        assert prof[key] > 0, key
+    assert prof["gateup_bytes_per_pick"] + prof["down_bytes_per_pick"] == wl.expert_bytes
+    # timing on: the forward refuses graph capture
+    s = torch.cuda.Stream()
+    d2 = Decode(wl, stream=s)
+    moe.moe_profile(d2.ctx, 1)
+    g = torch.cuda.CUDAGraph()
+    xs = torch.zeros((2, 2048), dtype=torch.float32, device="cuda")
+    zs = torch.zeros((2, 32), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            xs.mul_(1.0)
+            rc = moe.lib().moe_forward(d2.ctx, 0, 2, xs.data_ptr(), zs.data_ptr(), xs.data_ptr(), None, None,
+                                       moe.MOE_ACCUMULATE)
+    assert rc == moe.MOE_E_CAPTURING
+    d2.close()
+    d.close()
