@@ -132,6 +132,12 @@ typedef struct {
   int64_t cold_picks;         /* picks they served over PCIe                  */
   int64_t gateup_bytes_per_pick; /* expert bytes of gate + up                 */
   int64_t down_bytes_per_pick;   /* expert bytes of down                      */
+  int64_t prefill_passes;     /* moe_prefill calls timed                      */
+  double  prefill_gateup_ms;  /* grouped gate/up GEMM (+ SwiGLU)              */
+  double  prefill_down_ms;    /* grouped down GEMM                            */
+  int64_t prefill_pairs;      /* (token, pick) pairs the timed passes computed */
+  int64_t prefill_tiles;      /* 64-row (expert, tile) pairs launched         */
+  int64_t prefill_staged;     /* experts copied into borrowed staging blocks  */
 } moe_profile_stats;
 
 /* Size in bytes of one expert (gate + up + down) in MOE_Q4_32_F16. */
@@ -219,7 +225,8 @@ MOE_API int moe_cache_step(moe_ctx* ctx, moe_step_stats* out);
  * totals accumulated so far. While on, moe_forward launches each of its
  * kernels with start/stop events timed by the dispatch (so it must not be
  * captured: MOE_E_CAPTURING), and moe_cache_step adds their durations and the
- * step's hot and cold pick counts once the stream has drained. */
+ * step's hot and cold pick counts once the stream has drained; moe_prefill
+ * times its two grouped GEMMs the same way. */
 MOE_API int moe_profile(moe_ctx* ctx, int32_t enable, moe_profile_stats* out);
 
 /* Introspection (host outputs; each synchronises the stream). */

@@ -62,7 +62,9 @@ class moe_profile_stats(C.Structure):
     _fields_ = [("forwards", C.c_int64), ("route_ms", C.c_double), ("hot_gateup_ms", C.c_double),
                 ("hot_down_ms", C.c_double), ("cold_gateup_ms", C.c_double), ("cold_down_ms", C.c_double),
                 ("hot_picks", C.c_int64), ("cold_picks", C.c_int64), ("gateup_bytes_per_pick", C.c_int64),
-                ("down_bytes_per_pick", C.c_int64)]
+                ("down_bytes_per_pick", C.c_int64), ("prefill_passes", C.c_int64),
+                ("prefill_gateup_ms", C.c_double), ("prefill_down_ms", C.c_double), ("prefill_pairs", C.c_int64),
+                ("prefill_tiles", C.c_int64), ("prefill_staged", C.c_int64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -71,15 +71,14 @@ struct RouteArgs {
   Ctrl* ctrl;
   const uint8_t* pool;   // first slot of the layer
   const uint8_t* host;   // device address of the layer's pinned experts
-  const uint8_t* const* pass_addr;  // prefill: per-expert address for the pass (overrides tbl)
   int64_t expert_bytes;
   int32_t* ids;          // [T][k] internal
   float* w;              // [T][k] internal
-  const uint8_t** addr;  // [T][k] per-pick expert address
+  const uint8_t** addr;  // [T][k] per-pick expert address (nullptr: not written)
   uint8_t* kind;         // [T][k] kHot / kCold
   int32_t* ids_user;     // optional copies for the caller
   float* w_user;
-  int32_t policy;        // 1: stamps, miss log, counts, step tokens; 0: none
+  int32_t policy;        // 1: lookup, stamps, records, counts, step tokens; 0: routing only
 };
 hipError_t launch_route(const RouteArgs& a, const Launch& l);
 
@@ -107,5 +106,29 @@ struct GemvArgs {
 hipError_t launch_gemv_gateup(const GemvArgs& a, const Launch& l, int mode);
 hipError_t launch_gemv_down_pick(const GemvArgs& a, const Launch& l, int mode);
 hipError_t launch_gemv_down_combine(const GemvArgs& a, const Launch& l, int mode);
+
+// ---------------------------------------------------------------------------
+// prompt pass (prefill_kernels.hip)
+
+struct GemmArgs {
+  const uint16_t* ah;           // A hi plane (bf16 bits), rows of K in operand order
+  const uint16_t* al;           // A lo plane
+  const int32_t* arow;          // gate/up: perm (A row = arow[pos] / arow_div); down: nullptr (A row = pos)
+  int32_t arow_div;
+  const int4* tiles;            // (expert, first sorted position, rows <= 64, 0)
+  const uint8_t* const* eaddr;  // [E] device address of each expert for the pass
+  int32_t K, N;                 // reduction length, output features
+  ExpertLayout lay;
+  uint16_t* hh;                 // gate/up output: h hi plane [P][N]
+  uint16_t* hl;                 // h lo plane
+  float* y;                     // down output: y_pair [P][N]
+};
+hipError_t launch_expert_histogram(const int32_t* ids, int32_t n_pairs, int32_t E, int32_t* counts, hipStream_t s);
+hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E, const int32_t* offsets,
+                                 int32_t* perm, int32_t* inv, hipStream_t s);
+hipError_t launch_split_rows(const float* src, int64_t rows, int32_t K, uint16_t* hi, uint16_t* lo, hipStream_t s);
+hipError_t launch_grouped_gemm(const GemmArgs& a, int mode, int n_tiles, const Launch& l);
+hipError_t launch_combine_pairs(const float* ypair, const int32_t* inv, const float* w, int32_t T, int32_t k,
+                                int32_t H, float* y, int32_t accumulate, hipStream_t s);
 
 }  // namespace moe

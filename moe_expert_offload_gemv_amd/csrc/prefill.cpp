@@ -1,21 +1,208 @@
-// prefill.cpp - prompt pass of one layer (grouped GEMM over tokens sorted by
-// expert, staging of non-resident experts into borrowed HBM blocks).
+// prefill.cpp - host side of the prompt pass of one MoE layer: route the
+// micro-batch, sort the (token, pick) pairs by expert on the GPU, copy the
+// touched experts that are not resident into borrowed HBM staging blocks
+// (the "llama.cpp: fork with multi gpu acceleration ..." README, "How it
+// works": a prompt pass streams the experts the GPU does not hold and gives
+// the borrowed blocks back afterwards), run the grouped gate/up and down
+// GEMMs over the used (expert, tile) pairs only, and combine in pick order.
+// The cache policy is not touched: no stamps, records, counts or clock.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
 #include "runtime.h"
 
-struct Prefill {};
+namespace {
+constexpr int kTileRows = 64;
+
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+}  // namespace
+
+struct Prefill {
+  int64_t max_tokens = 0, max_pairs = 0, max_tiles = 0;
+  int32_t* ids = nullptr;       // [P]
+  float* w = nullptr;           // [P]
+  int32_t* perm = nullptr;      // [P] sorted position -> pair
+  int32_t* inv = nullptr;       // [P] pair -> sorted position
+  int32_t* counts = nullptr;    // [E]
+  int32_t* offsets = nullptr;   // [E + 1]
+  int4* tiles = nullptr;        // [max_tiles]
+  const uint8_t** eaddr = nullptr;  // [E]
+  uint16_t *xh = nullptr, *xl = nullptr;  // [T][H]
+  uint16_t *hh = nullptr, *hl = nullptr;  // [P][F]
+  float* ypair = nullptr;       // [P][H]
+  // pinned staging of the small transfers
+  int32_t* h_counts = nullptr;
+  int32_t* h_offsets = nullptr;
+  int4* h_tiles = nullptr;
+  const uint8_t** h_eaddr = nullptr;
+};
+
+#define PF_HIP(ctx, expr)                                                                                \
+  do {                                                                                                   \
+    hipError_t e_ = (expr);                                                                              \
+    if (e_ != hipSuccess) return moe_ctx_fail((ctx), MOE_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
 
 int moe_prefill_alloc(moe_ctx* c) {
-  (void)c;
+  const int64_t T = c->cfg.max_prefill_tokens;
+  if (T <= 0) return MOE_OK;
+  Prefill* p = new Prefill();
+  c->pf = p;
+  const int64_t E = c->E, P = T * c->k;
+  p->max_tokens = T, p->max_pairs = P;
+  p->max_tiles = E + P / kTileRows + 1;
+  int rc;
+  auto dev = [&](void** q, size_t bytes, const char* what) { return moe_ctx_dev_alloc(c, q, bytes, what); };
+  if ((rc = dev((void**)&p->ids, sizeof(int32_t) * P, "prefill ids")) ||
+      (rc = dev((void**)&p->w, sizeof(float) * P, "prefill weights")) ||
+      (rc = dev((void**)&p->perm, sizeof(int32_t) * P, "prefill perm")) ||
+      (rc = dev((void**)&p->inv, sizeof(int32_t) * P, "prefill inverse perm")) ||
+      (rc = dev((void**)&p->counts, sizeof(int32_t) * E, "prefill counts")) ||
+      (rc = dev((void**)&p->offsets, sizeof(int32_t) * (E + 1), "prefill offsets")) ||
+      (rc = dev((void**)&p->tiles, sizeof(int4) * p->max_tiles, "prefill tiles")) ||
+      (rc = dev((void**)&p->eaddr, sizeof(uint8_t*) * E, "prefill addresses")) ||
+      (rc = dev((void**)&p->xh, sizeof(uint16_t) * T * c->H, "prefill x hi")) ||
+      (rc = dev((void**)&p->xl, sizeof(uint16_t) * T * c->H, "prefill x lo")) ||
+      (rc = dev((void**)&p->hh, sizeof(uint16_t) * P * c->F, "prefill h hi")) ||
+      (rc = dev((void**)&p->hl, sizeof(uint16_t) * P * c->F, "prefill h lo")) ||
+      (rc = dev((void**)&p->ypair, sizeof(float) * P * c->H, "prefill pair outputs")))
+    return rc;
+  const unsigned pin = hipHostMallocDefault;
+  if ((rc = moe_ctx_host_alloc(c, (void**)&p->h_counts, sizeof(int32_t) * E, pin, "prefill count staging")) ||
+      (rc = moe_ctx_host_alloc(c, (void**)&p->h_offsets, sizeof(int32_t) * (E + 1), pin, "prefill offsets staging")) ||
+      (rc = moe_ctx_host_alloc(c, (void**)&p->h_tiles, sizeof(int4) * p->max_tiles, pin, "prefill tile staging")) ||
+      (rc = moe_ctx_host_alloc(c, (void**)&p->h_eaddr, sizeof(uint8_t*) * E, pin, "prefill address staging")))
+    return rc;
   return MOE_OK;
 }
 
-void moe_prefill_release(moe_ctx* c) { (void)c; }
+// HBM blocks lent to a prompt pass for the touched experts that are not
+// resident: E - S of them hold every expert a pass can miss.
+int moe_prefill_alloc_staging(moe_ctx* c) {
+  if (c->cfg.max_prefill_tokens <= 0) return MOE_OK;
+  c->n_staging = std::max<int64_t>(0, (int64_t)c->E - c->S);
+  return moe_ctx_dev_alloc(c, (void**)&c->staging, (size_t)(c->n_staging * c->B), "prefill staging blocks");
+}
+
+void moe_prefill_release(moe_ctx* c) {
+  delete c->pf;
+  c->pf = nullptr;
+}
 
 extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const float* x, const float* logits,
                            float* y, uint32_t flags) {
-  (void)layer, (void)n_tokens, (void)x, (void)logits, (void)y, (void)flags;
   if (!c) return MOE_E_INVAL;
-  return moe_ctx_fail(c, MOE_E_STATE, "prefill is not available in this build");
+  Prefill* p = c->pf;
+  if (!p) return moe_ctx_fail(c, MOE_E_STATE, "prefill: created with max_prefill_tokens = 0");
+  if (layer < 0 || layer >= c->L) return moe_ctx_fail(c, MOE_E_INVAL, "prefill: bad layer %d", layer);
+  if (n_tokens < 1 || n_tokens > p->max_tokens)
+    return moe_ctx_fail(c, MOE_E_INVAL, "prefill: n_tokens %d outside 1..%lld", n_tokens, (long long)p->max_tokens);
+  if (!x || !y || ((uintptr_t)x & 15) || ((uintptr_t)y & 15))
+    return moe_ctx_fail(c, MOE_E_INVAL, "prefill: x and y must be non-null 16-byte aligned pointers");
+  if (y == x && !(flags & MOE_ACCUMULATE))
+    return moe_ctx_fail(c, MOE_E_INVAL, "prefill: y may alias x only with MOE_ACCUMULATE");
+  if (!logits && !c->routers[layer]) return moe_ctx_fail(c, MOE_E_INVAL, "prefill: no logits and no router");
+  if (!c->seeded) return moe_ctx_fail(c, MOE_E_STATE, "prefill before moe_seed");
+  if (capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "prefill while capturing");
+  hipStream_t s = c->stream;
+  const int32_t E = c->E, k = c->k, H = c->H, F = c->F, T = n_tokens;
+  const int32_t P = T * k;
+
+  // 1. routing only (no lookup, no policy side effects)
+  moe::RouteArgs ra{};
+  ra.logits = logits;
+  ra.x = x;
+  ra.wr = (const float*)c->routers[layer];
+  ra.T = T, ra.E = E, ra.k = k, ra.H = H, ra.S = c->S, ra.layer = layer;
+  ra.ids = p->ids, ra.w = p->w;
+  ra.policy = 0;
+  moe::Launch ls;
+  ls.stream = s;
+  PF_HIP(c, moe::launch_route(ra, ls));
+
+  // 2. pairs per expert, to the host
+  PF_HIP(c, hipMemsetAsync(p->counts, 0, sizeof(int32_t) * E, s));
+  PF_HIP(c, moe::launch_expert_histogram(p->ids, P, E, p->counts, s));
+  PF_HIP(c, hipMemcpyAsync(p->h_counts, p->counts, sizeof(int32_t) * E, hipMemcpyDeviceToHost, s));
+  PF_HIP(c, hipStreamSynchronize(s));
+
+  // 3. offsets, tiles of the used experts, and where each expert is read from
+  int64_t n_tiles = 0, staged = 0, pos = 0;
+  const int64_t S = c->S;
+  for (int32_t e = 0; e < E; ++e) {
+    const int32_t m = p->h_counts[e];
+    p->h_offsets[e] = (int32_t)pos;
+    p->h_eaddr[e] = nullptr;
+    if (m > 0) {
+      const int32_t slot = c->tbl[(int64_t)layer * E + e];
+      if (slot >= 0) {
+        p->h_eaddr[e] = c->pool + ((int64_t)layer * S + slot) * c->B;
+      } else if (staged < c->n_staging) {
+        uint8_t* blk = c->staging + staged * c->B;
+        PF_HIP(c, hipMemcpyAsync(blk, c->host_layers[layer] + (int64_t)e * c->B, c->B, hipMemcpyHostToDevice, s));
+        p->h_eaddr[e] = blk;
+        ++staged;
+      } else {
+        p->h_eaddr[e] = c->host_layers_dev[layer] + (int64_t)e * c->B;  // no block left: read zero-copy
+      }
+      for (int32_t m0 = 0; m0 < m; m0 += kTileRows)
+        p->h_tiles[n_tiles++] = int4{e, (int32_t)(pos + m0), std::min(kTileRows, m - m0), 0};
+    }
+    pos += m;
+  }
+  p->h_offsets[E] = (int32_t)pos;
+  c->last_prefill_staged = staged;
+  if (pos != P) return moe_ctx_fail(c, MOE_E_HIP, "prefill: pair count mismatch (%lld != %d)", (long long)pos, P);
+  PF_HIP(c, hipMemcpyAsync(p->offsets, p->h_offsets, sizeof(int32_t) * (E + 1), hipMemcpyHostToDevice, s));
+  PF_HIP(c, hipMemcpyAsync(p->tiles, p->h_tiles, sizeof(int4) * n_tiles, hipMemcpyHostToDevice, s));
+  PF_HIP(c, hipMemcpyAsync(p->eaddr, p->h_eaddr, sizeof(uint8_t*) * E, hipMemcpyHostToDevice, s));
+
+  // 4. stable sort of the pairs by expert
+  PF_HIP(c, moe::launch_expert_scatter(p->ids, P, E, p->offsets, p->perm, p->inv, s));
+
+  // 5. activations as bf16 hi/lo planes
+  PF_HIP(c, moe::launch_split_rows(x, T, H, p->xh, p->xl, s));
+
+  // 6. grouped GEMMs over the used tiles
+  hipEvent_t* ev = nullptr;
+  if (c->profiling && c->prefill_events.size() >= 4) ev = c->prefill_events.data();
+  moe::GemmArgs g{};
+  g.ah = p->xh, g.al = p->xl, g.arow = p->perm, g.arow_div = k;
+  g.tiles = p->tiles, g.eaddr = p->eaddr;
+  g.K = H, g.N = F;
+  g.lay = c->lay;
+  g.hh = p->hh, g.hl = p->hl;
+  moe::Launch l1 = ls, l2 = ls;
+  if (ev) l1.start = ev[0], l1.stop = ev[1], l2.start = ev[2], l2.stop = ev[3];
+  PF_HIP(c, moe::launch_grouped_gemm(g, 0, (int)n_tiles, l1));
+  moe::GemmArgs d = g;
+  d.ah = p->hh, d.al = p->hl, d.arow = nullptr, d.arow_div = 1;
+  d.K = F, d.N = H;
+  d.y = p->ypair;
+  PF_HIP(c, moe::launch_grouped_gemm(d, 1, (int)n_tiles, l2));
+
+  // 7. weighted combine in pick order
+  PF_HIP(c, moe::launch_combine_pairs(p->ypair, p->inv, p->w, T, k, H, y, (flags & MOE_ACCUMULATE) ? 1 : 0, s));
+  PF_HIP(c, hipStreamSynchronize(s));  // the pass is over: the staging blocks are free again
+
+  if (ev) {
+    float t1 = 0, t2 = 0;
+    PF_HIP(c, hipEventElapsedTime(&t1, ev[0], ev[1]));
+    PF_HIP(c, hipEventElapsedTime(&t2, ev[2], ev[3]));
+    c->prof.prefill_passes += 1;
+    c->prof.prefill_gateup_ms += t1;
+    c->prof.prefill_down_ms += t2;
+    c->prof.prefill_pairs += P;
+    c->prof.prefill_tiles += n_tiles;
+    c->prof.prefill_staged += staged;
+  }
+  return MOE_OK;
 }

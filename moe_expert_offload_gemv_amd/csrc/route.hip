@@ -164,13 +164,12 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
       a.records[p] = rec;
       atomicAdd(&a.counts[e], 1u);
     } else {
-      addr = a.pass_addr[e];
+      addr = nullptr;  // a prompt pass addresses experts after sorting
       kind = kHot;
     }
     a.ids[p] = e;
     a.w[p] = w;
-    a.addr[p] = addr;
-    a.kind[p] = kind;
+    if (a.addr) a.addr[p] = addr, a.kind[p] = kind;
     if (a.ids_user) a.ids_user[p] = e;
     if (a.w_user) a.w_user[p] = w;
   }

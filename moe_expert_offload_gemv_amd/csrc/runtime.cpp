@@ -122,6 +122,8 @@ static void ctx_release(moe_ctx* c) {
   for (void* r : c->routers)
     if (r) (void)hipFree(r);
   for (hipEvent_t e : c->events) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->prefill_events) (void)hipEventDestroy(e);
+  moe_prefill_release(c);
   delete c;
 }
 
@@ -227,6 +229,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->S = (int32_t)std::min<int64_t>(E, budget / (L * c->B));
   const int64_t S = c->S;
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->pool, (size_t)(L * S * c->B), "expert pool"))) return fail(rc);
+  if ((rc = moe_prefill_alloc_staging(c))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_stamps, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), "stamps")))
     return fail(rc);
   if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_stamps, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), pin,
@@ -280,6 +283,11 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
     c->events.push_back(ev);
   }
   c->timed_tokens.assign(n_timed, 0);
+  for (int i = 0; i < 4 && k.max_prefill_tokens > 0; ++i) {
+    hipEvent_t ev;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return fail(MOE_E_HIP);
+    c->prefill_events.push_back(ev);
+  }
   if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_E_HIP);
   c->clock = 1;
   *out = c;

@@ -53,6 +53,8 @@ struct moe_ctx {
   int64_t n_staging = 0;
   uint8_t* staging = nullptr;
   struct Prefill* pf = nullptr;
+  int64_t last_prefill_staged = 0;
+  std::vector<hipEvent_t> prefill_events;  // timing of the two grouped GEMMs
 
   // host mirror of the cache state
   std::vector<int32_t> tbl, owner;
@@ -80,4 +82,5 @@ int moe_ctx_host_alloc(moe_ctx* c, void** p, size_t bytes, unsigned flags, const
 
 // prefill.cpp
 int moe_prefill_alloc(moe_ctx* c);
+int moe_prefill_alloc_staging(moe_ctx* c);
 void moe_prefill_release(moe_ctx* c);

@@ -1,0 +1,120 @@
+"""GPU parity of the prompt pass (sort by expert, staging, bf16-MFMA grouped
+GEMMs, combine) through the C ABI against the oracle, and its neutrality
+towards the cache policy."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import moe_expert_offload_gemv_amd as moe  # noqa: E402
+import oracle  # noqa: E402
+from tests._gpu import TOL, Decode, token_rel_err  # noqa: E402
+from workload import WORKLOADS, Workload, activations, router_weights, zipf_logits  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _prefill_check(wl: Workload, slots: int, sample=None, flags=0):
+    d = Decode(wl, slots=slots, max_batch=1, max_prefill=wl.tokens)
+    T, H = wl.tokens, wl.hidden
+    x32 = activations(wl, 0, tokens=T)
+    z = zipf_logits(wl, steps=1, tokens=T)[0, 0]
+    x = _dev(x32)
+    y = _dev(np.full((T, H), 0.25, np.float32)) if flags else torch.empty((T, H), dtype=torch.float32, device="cuda")
+    tbl0 = [moe.moe_get_slot_table(d.ctx, layer, wl.n_experts) for layer in range(wl.n_layers)]
+    moe.moe_profile(d.ctx, 1)
+    moe.moe_prefill(d.ctx, 0, T, x, _dev(z), y, flags)
+    prof = moe.moe_profile(d.ctx, 0)
+    yh = y.cpu().numpy().astype(np.float64)
+    if flags:
+        yh -= 0.25
+    rows = np.arange(T) if sample is None else np.random.default_rng(0).choice(T, size=sample, replace=False)
+    ids, _ = oracle.route(z[rows], wl.top_k)
+    y_ref, ids_ref, _ = oracle.moe_layer(wl.n_experts, wl.top_k, H, wl.ffn, d.experts(0, ids), x32[rows].astype(
+        np.float64), logits=z[rows])
+    err = token_rel_err(yh[rows], y_ref)
+    assert err < TOL, err
+    # policy neutral: tables, stamps, counts, clock untouched
+    for layer in range(wl.n_layers):
+        assert np.array_equal(moe.moe_get_slot_table(d.ctx, layer, wl.n_experts), tbl0[layer])
+        assert not moe.moe_get_stamps(d.ctx, layer, d.S).any()
+    assert not moe.moe_get_counts(d.ctx, wl.n_layers, wl.n_experts).any()
+    assert moe.moe_get_info(d.ctx)["clock"] == 1
+    assert prof["prefill_passes"] == 1 and prof["prefill_pairs"] == T * wl.top_k
+    d.close()
+    return err, prof
+
+
+def test_prefill_small_ragged_tiles_with_staging():
+    wl = Workload("prefill-e16k4-h256f512-t37", 201, 1, 16, 4, 256, 512, tokens=37, zipf_s=1.1)
+    err, prof = _prefill_check(wl, slots=8)
+    assert prof["prefill_staged"] > 0
+    print("err", err, prof)
+
+
+def test_prefill_many_tiles_per_expert():
+    wl = Workload("prefill-e8k2-h256f512-t1000", 202, 1, 8, 2, 256, 512, tokens=1000, zipf_s=1.1)
+    err, prof = _prefill_check(wl, slots=3, sample=200)
+    assert prof["prefill_tiles"] > 8
+
+
+def test_prefill_decode_shape():
+    wl = Workload("prefill-e64k8-h2048f1024-t300", 203, 1, 64, 8, 2048, 1024, tokens=300, zipf_s=1.1)
+    _prefill_check(wl, slots=26, sample=48)
+
+
+def test_prefill_wide_shape_all_resident():
+    wl = Workload("prefill-e16k8-h4096f1536-t90", 204, 1, 16, 8, 4096, 1536, tokens=90, zipf_s=1.0)
+    err, prof = _prefill_check(wl, slots=16, sample=24)
+    assert prof["prefill_staged"] == 0
+
+
+def test_prefill_all_cold_and_accumulate():
+    wl = Workload("prefill-e16k4-h256f512-t20-cold", 205, 1, 16, 4, 256, 512, tokens=20, zipf_s=1.1)
+    err, prof = _prefill_check(wl, slots=0, flags=moe.MOE_ACCUMULATE)
+    assert prof["prefill_staged"] == len(set(oracle.route(zipf_logits(wl, steps=1, tokens=20)[0, 0], 4)[0].ravel()))
+
+
+def test_prefill_router_in_the_loop_matches_decode():
+    wl = WORKLOADS["tiny-e8k2-h256f512-t4"]
+    d = Decode(wl, max_batch=4, max_prefill=4)
+    moe.moe_register_router(d.ctx, 0, router_weights(wl, 0))
+    x = _dev(activations(wl, 0))
+    y1 = torch.empty_like(x)
+    y2 = torch.empty_like(x)
+    moe.moe_prefill(d.ctx, 0, 4, x, None, y1)
+    moe.moe_forward(d.ctx, 0, 4, x, None, y2)
+    # two different kernels (MFMA grouped GEMM vs fp32 GEMV) on the same routing
+    assert token_rel_err(y1.cpu().numpy(), y2.cpu().numpy().astype(np.float64)) < 1e-4
+    d.close()
+
+
+def test_prefill_between_decode_steps_leaves_policy_identical():
+    wl = Workload("decode-e32k8-h256f512-l2-b1-pf", 206, 2, 32, 8, 256, 512, tokens=1, steps=12, zipf_s=1.1,
+                  slots=10, rotation=4)
+    logits = zipf_logits(wl)
+    xp = _dev(activations(wl, 99, tokens=50))
+    zp = _dev(zipf_logits(wl, steps=1, tokens=50)[0, 1])
+    yp = torch.empty_like(xp)
+    runs = []
+    for with_prefill in (False, True):
+        d = Decode(wl, max_prefill=50)
+        y = torch.empty((1, 256), dtype=torch.float32, device="cuda")
+        out = []
+        for step in range(wl.steps):
+            x = _dev(activations(wl, step))
+            for layer in range(2):
+                moe.moe_forward(d.ctx, layer, 1, x, _dev(logits[step, layer]), y)
+                x += y
+            if with_prefill and step % 3 == 1:
+                moe.moe_prefill(d.ctx, 1, 50, xp, zp, yp)
+            st = moe.moe_cache_step(d.ctx)
+            out.append((st, [moe.moe_get_slot_table(d.ctx, layer, 32).tolist() for layer in range(2)],
+                        moe.moe_get_miss_log(d.ctx).tolist(), x.cpu().numpy().tolist()))
+        runs.append(out)
+        d.close()
+    assert runs[0] == runs[1]
