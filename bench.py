@@ -8,9 +8,12 @@ a routing-frequency table; cold experts read zero-copy from pinned host RAM;
 the cache step runs between decode steps.
 
 A step is one decode token through all 48 layers (routing, lookup + stamps +
-miss log, gate/up GEMV + SwiGLU, down GEMV + weighted combine, residual in
-place), followed by the host cache step (promotions). The timed region replays
-a HIP graph of the 48-layer forward per step; inputs are resident in HBM.
+miss record, gate/up GEMV + SwiGLU, down GEMV + weighted combine added into
+a residual buffer), followed by the host cache step (promotions). Every
+(step, layer) has its own N(0, 1) input, as the router logits are drawn
+independently of the activations; inputs of 32 distinct steps are resident
+in HBM and reused cyclically (the logits of all 256 steps are resident). The
+timed region replays a HIP graph of the 48-layer forward per step.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -27,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 PCIE_PEAK_GBPS = 64.0       # PCIe Gen5 x16, one direction
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 METRIC = "MoE-layer decode tokens/s + effective weight GB/s vs HBM/PCIe roofline"
 
 
@@ -62,24 +66,69 @@ def run_steps(moe, ctx, n, step_fn, stats_acc=None):
                 stats_acc[k_] = stats_acc.get(k_, 0) + v
 
 
-def kernel_pass(moe, torch, wl, slots, layers, steps, stream, host_alloc, logits_all, x0_all):
+def kernel_pass(moe, torch, wl, slots, layers, steps, stream, host_alloc, logits_all, x_all):
     """Time the forward kernels on a small context (all hot or all cold)."""
     ctx, freq = setup_ctx(moe, wl, slots, stream, host_alloc, layers=layers, progress=False)
     moe.moe_seed(ctx, freq)
     T, H = wl.tokens, wl.hidden
-    x = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    res = torch.empty((T, H), dtype=torch.float32, device="cuda")
     with torch.cuda.stream(stream):
         moe.moe_profile(ctx, 1)
 
         def step(i):
-            x.copy_(x0_all[i % wl.steps])
+            res.zero_()
             for layer in range(layers):
-                moe.moe_forward(ctx, layer, T, x, logits_all[i % wl.steps, layer], x, flags=moe.MOE_ACCUMULATE)
+                moe.moe_forward(ctx, layer, T, x_all[i % x_all.shape[0], layer], logits_all[i % wl.steps, layer], res,
+                                flags=moe.MOE_ACCUMULATE)
 
         run_steps(moe, ctx, steps, step)
         prof = moe.moe_profile(ctx, 0)
     moe.moe_destroy(ctx)
     return prof
+
+
+def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3):
+    """A prompt pass of one layer: end-to-end time and the grouped GEMMs against the bf16 MFMA peak."""
+    import numpy as np
+
+    from workload import activations, frequency_table, layer_weights, zipf_logits
+
+    T, H, F, E, k = wl.tokens, wl.hidden, wl.ffn, wl.n_experts, wl.top_k
+    ctx = moe.moe_create(1, E, k, H, F, pool_budget_bytes=wl.slots * wl.expert_bytes, max_batch_tokens=1,
+                         max_prefill_tokens=T, host_alloc=host_alloc, host_sets=1, stream=stream)
+    moe.moe_register_layer(ctx, 0, *layer_weights(wl, 0))
+    moe.moe_seed(ctx, frequency_table(wl))
+    x = torch.from_numpy(activations(wl, 0, tokens=T)).cuda()
+    z = torch.from_numpy(np.ascontiguousarray(zipf_logits(wl, steps=1, tokens=T)[0, 0])).cuda()
+    y = torch.empty_like(x)
+    with torch.cuda.stream(stream):
+        moe.moe_prefill(ctx, 0, T, x, z, y)  # warm-up
+        moe.moe_profile(ctx, 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            moe.moe_prefill(ctx, 0, T, x, z, y)
+        torch.cuda.synchronize()
+        elapsed = (time.perf_counter() - t0) / reps
+        prof = moe.moe_profile(ctx, 0)
+    moe.moe_destroy(ctx)
+    n = max(prof["prefill_passes"], 1)
+    pairs = prof["prefill_pairs"] / n
+    gu_ms, dn_ms = prof["prefill_gateup_ms"] / n, prof["prefill_down_ms"] / n
+    flops_gu = 2.0 * pairs * 2 * H * F
+    flops_dn = 2.0 * pairs * H * F
+    tflops = (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / 1e12
+    return {
+        "workload": wl.name, "tokens_per_s": round(T / elapsed, 1), "ms_per_pass": round(elapsed * 1e3, 3),
+        "staged_experts": int(prof["prefill_staged"] / n),
+        "staged_GB": round(prof["prefill_staged"] / n * wl.expert_bytes / 1e9, 3),
+        "tiles": int(prof["prefill_tiles"] / n),
+        "gateup_gemm_ms": round(gu_ms, 4), "down_gemm_ms": round(dn_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "grouped_gemm_kernel (gate/up + down), algorithmic flops 6*H*F per pair",
+                     "mfma_flops_per_algorithmic_flop": 2},
+    }
 
 
 def cpu_baseline(wl, seconds, logits):
@@ -95,15 +144,14 @@ def cpu_baseline(wl, seconds, logits):
     tokens = 0
     step = 0
     while spent < seconds and step < wl.steps:
-        x = activations(wl, step).astype(np.float64)
         for layer in range(wl.n_layers):
+            x = activations(wl, step, layer=layer).astype(np.float64)
             z = logits[step, layer]
             ids, _ = oracle.route(z, wl.top_k)
             experts = {int(e): expert_weights(wl, layer, int(e)) for e in np.unique(ids)}
             t0 = time.perf_counter()
-            y, _, _ = oracle.moe_layer(wl.n_experts, wl.top_k, wl.hidden, wl.ffn, experts, x, logits=z)
+            oracle.moe_layer(wl.n_experts, wl.top_k, wl.hidden, wl.ffn, experts, x, logits=z)
             spent += time.perf_counter() - t0
-            x = x + y
         tokens += wl.tokens
         step += 1
     return dict(value=tokens / spent, unit="tokens/s", cores=threads, kind="oracle",
@@ -132,7 +180,7 @@ def main():
     import torch
 
     import moe_expert_offload_gemv_amd as moe
-    from workload import WORKLOADS, activations, zipf_logits
+    from workload import WORKLOADS, step_activations, zipf_logits
 
     wl = WORKLOADS[args.workload]
     host_alloc = moe.MOE_HOST_NONCOHERENT if args.host_alloc == "noncoherent" else moe.MOE_HOST_COHERENT
@@ -148,15 +196,17 @@ def main():
     ctx, freq = setup_ctx(moe, wl, wl.slots, stream, host_alloc)
     logits_np = zipf_logits(wl)
     logits_all = torch.from_numpy(logits_np).cuda()                       # [steps][L][T][E]
-    x0_all = torch.from_numpy(np.stack([activations(wl, s) for s in range(wl.steps)])).cuda()  # [steps][T][H]
-    xs = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+    x_steps = min(wl.steps, 32)
+    x_all = torch.from_numpy(np.stack([step_activations(wl, s) for s in range(x_steps)])).cuda()  # [32][L][T][H]
+    xs = torch.zeros((L, T, H), dtype=torch.float32, device="cuda")
     zs = torch.zeros((L, T, E), dtype=torch.float32, device="cuda")
+    res = torch.zeros((T, H), dtype=torch.float32, device="cuda")
     moe.moe_seed(ctx, freq)
     log(f"setup {time.time() - t_setup:.1f} s")
 
     def forward_all():
         for layer in range(L):
-            moe.moe_forward(ctx, layer, T, xs, zs[layer], xs, flags=moe.MOE_ACCUMULATE)
+            moe.moe_forward(ctx, layer, T, xs[layer], zs[layer], res, flags=moe.MOE_ACCUMULATE)
 
     graph = None
     if not args.eager:
@@ -167,8 +217,9 @@ def main():
 
     def step(i):
         s = i % wl.steps
-        xs.copy_(x0_all[s])
+        xs.copy_(x_all[s % x_steps])
         zs.copy_(logits_all[s])
+        res.zero_()
         if graph is not None:
             graph.replay()
         else:
@@ -193,8 +244,8 @@ def main():
         moe.moe_profile(ctx, 1)
         prof_steps = min(args.steps, 64)
         t1 = time.perf_counter()
-        run_steps(moe, ctx, prof_steps, lambda i: (xs.copy_(x0_all[i % wl.steps]), zs.copy_(
-            logits_all[i % wl.steps]), forward_all()))
+        run_steps(moe, ctx, prof_steps, lambda i: (xs.copy_(x_all[i % x_steps]), zs.copy_(
+            logits_all[i % wl.steps]), res.zero_(), forward_all()))
         t_prof = time.perf_counter() - t1
         prof = moe.moe_profile(ctx, 0)
     fw = max(prof["forwards"], 1)
@@ -242,8 +293,8 @@ def main():
 
     if not args.no_side_passes:
         side = min(4, L)
-        hot = kernel_pass(moe, torch, wl, E, side, 32, stream, host_alloc, logits_all, x0_all)
-        cold = kernel_pass(moe, torch, wl, 0, side, 8, stream, host_alloc, logits_all, x0_all)
+        hot = kernel_pass(moe, torch, wl, E, side, 32, stream, host_alloc, logits_all, x_all)
+        cold = kernel_pass(moe, torch, wl, 0, side, 8, stream, host_alloc, logits_all, x_all)
 
         def rate(p, ms_key, picks_key, bytes_key):
             return p[picks_key] * p[bytes_key] / max(p[ms_key], 1e-9) / 1e6  # bytes / ms -> GB/s
@@ -275,6 +326,11 @@ def main():
         del src, dst
         log(f"side passes: hot {result['kernels_all_hot']} cold {result['kernels_all_cold']} "
             f"dma {result['pcie_dma_h2d_GBps']} GB/s")
+
+    if not args.no_side_passes:
+        result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc)
+                             for name in ("prefill-e512k8-h2048f1024-t4096", "large-e256k8-h4096f1536-t12288")]
+        log(f"prefill: {result['prefill']}")
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, logits_np)

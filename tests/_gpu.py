@@ -74,3 +74,67 @@ def oracle_policy(wl: Workload, slots: int, seed: bool = True):
     pol = oracle.Policy(wl.n_layers, wl.n_experts, slots, wl.top_k, window=wl.window, admit_misses=wl.admit_misses)
     pol.seed(frequency_table(wl) if seed else None)
     return pol
+
+
+class GraphDecode:
+    """The decode step as bench.py runs it: one HIP graph of the L-layer
+    forward, every layer adding its output into one residual buffer
+    (MOE_ACCUMULATE), replayed per step, then the cache step. With
+    snapshots the graph also copies the residual after every layer, so each
+    layer's output is the difference of two snapshots."""
+
+    def __init__(self, wl: Workload, snapshots: bool = True, max_batch: int | None = None):
+        import torch
+
+        self.torch = torch
+        self.wl = wl
+        self.stream = torch.cuda.Stream()
+        self.d = Decode(wl, stream=self.stream, max_batch=max_batch or wl.tokens, keep_weights=False)
+        L, T, H, E = wl.n_layers, wl.tokens, wl.hidden, wl.n_experts
+        self.xs = torch.zeros((L, T, H), dtype=torch.float32, device="cuda")
+        self.zs = torch.zeros((L, T, E), dtype=torch.float32, device="cuda")
+        self.res = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+        self.snap = torch.zeros((L, T, H), dtype=torch.float32, device="cuda") if snapshots else None
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(self.graph, stream=self.stream):
+                for layer in range(L):
+                    moe.moe_forward(self.d.ctx, layer, T, self.xs[layer], self.zs[layer], self.res,
+                                    flags=moe.MOE_ACCUMULATE)
+                    if snapshots:
+                        self.snap[layer].copy_(self.res)
+
+    def step(self, xs_step, logits_step):
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            self.xs.copy_(torch.from_numpy(np.ascontiguousarray(xs_step)).cuda())
+            self.zs.copy_(torch.from_numpy(np.ascontiguousarray(logits_step)).cuda())
+            self.res.zero_()
+            self.graph.replay()
+            st = moe.moe_cache_step(self.d.ctx)
+        return st
+
+    def layer_outputs(self):
+        """fp64 [L][T][H]: each layer's output of the last replay."""
+        s = self.snap.cpu().numpy().astype(np.float64)
+        prev = np.concatenate([np.zeros_like(s[:1]), s[:-1]], axis=0)
+        return s - prev
+
+    def close(self):
+        self.d.close()
+
+
+def oracle_layers(wl: Workload, xs_step, logits_step, layers=None):
+    """fp64 outputs [L][T][H] of the layers of one step through the oracle,
+    regenerating the picked experts' weights."""
+    from workload import expert_weights
+
+    out = []
+    for layer in range(wl.n_layers) if layers is None else layers:
+        z = logits_step[layer]
+        ids, _ = oracle.route(z, wl.top_k)
+        experts = {int(e): expert_weights(wl, layer, int(e)) for e in np.unique(ids)}
+        y, _, _ = oracle.moe_layer(wl.n_experts, wl.top_k, wl.hidden, wl.ffn, experts,
+                                   np.asarray(xs_step[layer], np.float64), logits=z)
+        out.append(y)
+    return np.stack(out)

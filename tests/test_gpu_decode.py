@@ -13,7 +13,7 @@ torch = pytest.importorskip("torch")
 import moe_expert_offload_gemv_amd as moe  # noqa: E402
 import oracle  # noqa: E402
 from tests._gpu import TOL, Decode, oracle_policy, token_rel_err  # noqa: E402
-from workload import WORKLOADS, Workload, activations, router_weights, zipf_logits  # noqa: E402
+from workload import WORKLOADS, Workload, activations, router_weights, step_activations, zipf_logits  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -44,11 +44,10 @@ def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_allo
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
     worst = 0.0
     for step in range(wl.steps):
-        x0 = activations(wl, step)
-        x = _dev(x0)
-        x64 = x0.astype(np.float64)
         check = step % check_every == 0
         for layer in range(L):
+            x32 = activations(wl, step, layer=layer)
+            x = _dev(x32)
             z = logits[step, layer]
             moe.moe_forward(d.ctx, layer, T, x, _dev(z), y, ids, w)
             ids_h = ids.cpu().numpy()
@@ -57,12 +56,11 @@ def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_allo
             np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=2e-6, atol=1e-7)
             pol.forward(layer, ids_o)
             if check:
-                y_ref, _, _ = oracle.moe_layer(wl.n_experts, k, H, wl.ffn, d.experts(layer, ids_o), x64, logits=z)
+                y_ref, _, _ = oracle.moe_layer(wl.n_experts, k, H, wl.ffn, d.experts(layer, ids_o),
+                                               x32.astype(np.float64), logits=z)
                 err = token_rel_err(y.cpu().numpy(), y_ref)
                 worst = max(worst, err)
                 assert err < TOL, (step, layer, err)
-                x64 = x64 + y_ref
-            x += y
         st_g = moe.moe_cache_step(d.ctx)
         st_o = pol.step()
         _compare_policy(d, pol, st_g, st_o, range(L))
@@ -173,28 +171,26 @@ def test_graph_capture_replays_match_eager():
     graph = Decode(wl, stream=s)
     logits = zipf_logits(wl)
     L, H = wl.n_layers, wl.hidden
-    xs = torch.zeros((1, H), dtype=torch.float32, device="cuda")
+    xs = torch.zeros((L, 1, H), dtype=torch.float32, device="cuda")
     zs = torch.zeros((L, 1, wl.n_experts), dtype=torch.float32, device="cuda")
     ys = [torch.zeros((1, H), dtype=torch.float32, device="cuda") for _ in range(L)]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             for layer in range(L):
-                moe.moe_forward(graph.ctx, layer, 1, xs, zs[layer], ys[layer])
-                xs.add_(ys[layer])
+                moe.moe_forward(graph.ctx, layer, 1, xs[layer], zs[layer], ys[layer])
     pol = oracle_policy(wl, 24)
     for step in range(wl.steps):
         with torch.cuda.stream(s):
-            xs.copy_(_dev(activations(wl, step)))
+            xs.copy_(_dev(step_activations(wl, step)))
             zs.copy_(_dev(logits[step]))
             g.replay()
             st_g = moe.moe_cache_step(graph.ctx)
-            xe = _dev(activations(wl, step))
-            ye = torch.empty_like(xe)
+            ye = torch.empty((1, H), dtype=torch.float32, device="cuda")
             for layer in range(L):
+                xe = _dev(activations(wl, step, layer=layer))
                 moe.moe_forward(eager.ctx, layer, 1, xe, _dev(logits[step, layer]), ye)
                 assert torch.equal(ye, ys[layer]), (step, layer)
-                xe += ye
                 pol.forward(layer, oracle.route(logits[step, layer], wl.top_k)[0])
             st_e = moe.moe_cache_step(eager.ctx)
         s.synchronize()

@@ -14,6 +14,7 @@ from .gen import (  # noqa: F401
     layer_weights,
     router_weights,
     activations,
+    step_activations,
     zipf_logits,
     zipf_popularity,
     rank_permutation,

@@ -13,7 +13,7 @@ trained model or dataset is used):
     0..15); the block is d (little endian) followed by the 16 bytes, element j
     in the low nibble of byte j and element j+16 in its high nibble;
   * router weights N(0, 0.02^2) fp32 (tiny workload) and activations N(0, 1)
-    fp32;
+    fp32, one independent draw per (step, layer);
   * router logits with Zipf(s) expert popularity: for layer l and epoch r a
     permutation maps popularity rank -> expert, and the logit of expert e is
     ln p(rank(e)) + Gumbel(0, 1), computed in fp64 and stored as fp32;
@@ -182,10 +182,20 @@ def router_weights(wl: Workload, layer: int) -> np.ndarray:
     return _rng(_P_ROUTER, wl.wid, layer).normal(0.0, 0.02, size=(wl.n_experts, wl.hidden)).astype(np.float32)
 
 
-def activations(wl: Workload, step: int = 0, tokens: int | None = None) -> np.ndarray:
-    """fp32 [T][H] ~ N(0, 1): the layer-0 input of a step (or of a prefill pass)."""
+def activations(wl: Workload, step: int = 0, tokens: int | None = None, layer: int = 0) -> np.ndarray:
+    """fp32 [T][H] ~ N(0, 1): the input of one layer in one decode step (or of a prefill pass).
+
+    Every (step, layer) has its own input, like the router logits, which are
+    drawn independently of the activations too.
+    """
     T = wl.tokens if tokens is None else tokens
-    return _rng(_P_X, wl.wid, step).standard_normal((T, wl.hidden)).astype(np.float32)
+    return _rng(_P_X, wl.wid, step, layer).standard_normal((T, wl.hidden)).astype(np.float32)
+
+
+def step_activations(wl: Workload, step: int, layers=None) -> np.ndarray:
+    """fp32 [L][T][H]: the inputs of every layer of one decode step."""
+    layers = range(wl.n_layers) if layers is None else layers
+    return np.stack([activations(wl, step, layer=layer) for layer in layers])
 
 
 # ---------------------------------------------------------------------------
