@@ -170,7 +170,20 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side-passes", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=64, help="steps of the kernel-timing pass")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 4 times (the reference for counter scaling)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 4 x 1 GiB")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards per GPU with no "
               f"exchange, so a multi-GPU figure is N independent copies of this one.", file=sys.stderr)
@@ -242,7 +255,7 @@ def main():
     with torch.cuda.stream(stream):
         moe.moe_seed(ctx, freq)
         moe.moe_profile(ctx, 1)
-        prof_steps = min(args.steps, 64)
+        prof_steps = min(args.steps, args.profile_steps)
         t1 = time.perf_counter()
         run_steps(moe, ctx, prof_steps, lambda i: (xs.copy_(x_all[i % x_steps]), zs.copy_(
             logits_all[i % wl.steps]), res.zero_(), forward_all()))
