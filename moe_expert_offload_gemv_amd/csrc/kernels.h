@@ -115,19 +115,23 @@ struct GemmArgs {
   const uint16_t* al;           // A lo plane
   const int32_t* arow;          // gate/up: perm (A row = arow[pos] / arow_div); down: nullptr (A row = pos)
   int32_t arow_div;
+  const float* asum;            // [A rows][K/32]: -136 * sum of (hi + lo) over each block
   const int4* tiles;            // (expert, first sorted position, rows <= 64, 0)
   const uint8_t* const* eaddr;  // [E] device address of each expert for the pass
   int32_t K, N;                 // reduction length, output features
   ExpertLayout lay;
   uint16_t* hh;                 // gate/up output: h hi plane [P][N]
   uint16_t* hl;                 // h lo plane
+  float* hsum;                  // gate/up output: [P][N/32] block sums of h (as asum)
   float* y;                     // down output: y_pair [P][N]
+  int32_t work, work_padded;    // set by the launcher: tile x n-tile items, padded to a multiple of 8
 };
 hipError_t launch_expert_histogram(const int32_t* ids, int32_t n_pairs, int32_t E, int32_t* counts, hipStream_t s);
 hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E, const int32_t* offsets,
                                  int32_t* perm, int32_t* inv, hipStream_t s);
-hipError_t launch_split_rows(const float* src, int64_t rows, int32_t K, uint16_t* hi, uint16_t* lo, hipStream_t s);
-hipError_t launch_grouped_gemm(const GemmArgs& a, int mode, int n_tiles, const Launch& l);
+hipError_t launch_split_rows(const float* src, int64_t rows, int32_t K, uint16_t* hi, uint16_t* lo, float* bsum,
+                             hipStream_t s);
+hipError_t launch_grouped_gemm(GemmArgs a, int mode, int n_tiles, const Launch& l);
 hipError_t launch_combine_pairs(const float* ypair, const int32_t* inv, const float* w, int32_t T, int32_t k,
                                 int32_t H, float* y, int32_t accumulate, hipStream_t s);
 

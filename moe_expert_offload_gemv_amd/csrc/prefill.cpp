@@ -36,7 +36,9 @@ struct Prefill {
   int4* tiles = nullptr;        // [max_tiles]
   const uint8_t** eaddr = nullptr;  // [E]
   uint16_t *xh = nullptr, *xl = nullptr;  // [T][H]
+  float* xsum = nullptr;                  // [T][H/32]
   uint16_t *hh = nullptr, *hl = nullptr;  // [P][F]
+  float* hsum = nullptr;                  // [P][F/32]
   float* ypair = nullptr;       // [P][H]
   // pinned staging of the small transfers
   int32_t* h_counts = nullptr;
@@ -71,6 +73,8 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = dev((void**)&p->eaddr, sizeof(uint8_t*) * E, "prefill addresses")) ||
       (rc = dev((void**)&p->xh, sizeof(uint16_t) * T * c->H, "prefill x hi")) ||
       (rc = dev((void**)&p->xl, sizeof(uint16_t) * T * c->H, "prefill x lo")) ||
+      (rc = dev((void**)&p->xsum, sizeof(float) * T * (c->H / 32), "prefill x block sums")) ||
+      (rc = dev((void**)&p->hsum, sizeof(float) * P * (c->F / 32), "prefill h block sums")) ||
       (rc = dev((void**)&p->hh, sizeof(uint16_t) * P * c->F, "prefill h hi")) ||
       (rc = dev((void**)&p->hl, sizeof(uint16_t) * P * c->F, "prefill h lo")) ||
       (rc = dev((void**)&p->ypair, sizeof(float) * P * c->H, "prefill pair outputs")))
@@ -169,22 +173,22 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   PF_HIP(c, moe::launch_expert_scatter(p->ids, P, E, p->offsets, p->perm, p->inv, s));
 
   // 5. activations as bf16 hi/lo planes
-  PF_HIP(c, moe::launch_split_rows(x, T, H, p->xh, p->xl, s));
+  PF_HIP(c, moe::launch_split_rows(x, T, H, p->xh, p->xl, p->xsum, s));
 
   // 6. grouped GEMMs over the used tiles
   hipEvent_t* ev = nullptr;
   if (c->profiling && c->prefill_events.size() >= 4) ev = c->prefill_events.data();
   moe::GemmArgs g{};
-  g.ah = p->xh, g.al = p->xl, g.arow = p->perm, g.arow_div = k;
+  g.ah = p->xh, g.al = p->xl, g.asum = p->xsum, g.arow = p->perm, g.arow_div = k;
   g.tiles = p->tiles, g.eaddr = p->eaddr;
   g.K = H, g.N = F;
   g.lay = c->lay;
-  g.hh = p->hh, g.hl = p->hl;
+  g.hh = p->hh, g.hl = p->hl, g.hsum = p->hsum;
   moe::Launch l1 = ls, l2 = ls;
   if (ev) l1.start = ev[0], l1.stop = ev[1], l2.start = ev[2], l2.stop = ev[3];
   PF_HIP(c, moe::launch_grouped_gemm(g, 0, (int)n_tiles, l1));
   moe::GemmArgs d = g;
-  d.ah = p->hh, d.al = p->hl, d.arow = nullptr, d.arow_div = 1;
+  d.ah = p->hh, d.al = p->hl, d.asum = p->hsum, d.arow = nullptr, d.arow_div = 1;
   d.K = F, d.N = H;
   d.y = p->ypair;
   PF_HIP(c, moe::launch_grouped_gemm(d, 1, (int)n_tiles, l2));

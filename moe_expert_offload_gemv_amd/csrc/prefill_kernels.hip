@@ -110,153 +110,254 @@ __global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* ids,
   }
 }
 
-// rows of fp32 [R][K] -> bf16 hi and lo planes [R][K] in operand order
-__global__ __launch_bounds__(256) void split_rows_kernel(const float* src, int64_t n, int32_t K, uint16_t* hi,
-                                                         uint16_t* lo) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float v = src[i];
-  const uint16_t h = bf16_bits_rne(v);
-  const uint16_t l = bf16_bits_rne(v - bf16_to_float(h));
-  const int64_t row = i / K;
-  const int k = (int)(i - row * K);
-  const int64_t o = row * K + (k & ~31) + plane_pos(k & 31);
-  hi[o] = h;
-  lo[o] = l;
+// rows of fp32 [R][K] -> bf16 hi and lo planes [R][K] in operand order, and
+// per (row, 32-block) -136 * sum of (hi + lo): one thread per block
+__global__ __launch_bounds__(256) void split_rows_kernel(const float* src, int64_t nblocks, int32_t K, uint16_t* hi,
+                                                         uint16_t* lo, float* bsum) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const float4* s4 = reinterpret_cast<const float4*>(src + b * 32);
+  uint16_t h[32], l[32];
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float4 q = s4[c];
+    const float v[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = 4 * c + j;
+      const uint16_t hh = bf16_bits_rne(v[j]);
+      const uint16_t ll = bf16_bits_rne(v[j] - bf16_to_float(hh));
+      h[plane_pos(k)] = hh;
+      l[plane_pos(k)] = ll;
+      sum += bf16_to_float(hh) + bf16_to_float(ll);
+    }
+  }
+  uint4* ph = reinterpret_cast<uint4*>(hi + b * 32);
+  uint4* pl = reinterpret_cast<uint4*>(lo + b * 32);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t wh[4], wl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wh[j] = (uint32_t)h[8 * c + 2 * j] | ((uint32_t)h[8 * c + 2 * j + 1] << 16);
+      wl[j] = (uint32_t)l[8 * c + 2 * j] | ((uint32_t)l[8 * c + 2 * j + 1] << 16);
+    }
+    ph[c] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    pl[c] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+  }
+  bsum[b] = -136.0f * sum;
+  (void)K;
 }
 
-// MODE 0: gate/up (two weight matrices, SwiGLU, writes h planes)
-// MODE 1: down (one matrix, writes y_pair)
+namespace {
+// GFX9 DPP controls (butterflies inside a 16-lane row)
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over the 16 lanes of a DPP row; every lane of the row gets it
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dppf<0x141>(v);  // row_half_mirror
+  v += dppf<0x140>(v);  // row_mirror
+  return v;
+}
+constexpr int kDepth = 1;  // blocks of A and B in flight ahead of the one computed
+}  // namespace
+
+// One workgroup computes a 64-row tile of one expert's pairs against
+// 4 waves x NSUB x 16 output features.
+// MODE 0: gate/up (two weight matrices, SwiGLU, writes h planes and their
+//         per-block -136 * sums); NSUB = 2, so each wave owns one 32-feature
+//         block of h.
+// MODE 1: down (one matrix, writes y_pair); NSUB = 4.
+// Work items are numbered so that each XCD (work item id mod 8 of the launch
+// order) gets a contiguous range: the n-tiles of one row tile, then the next
+// row tile of the same expert, share an L2.
 template <int MODE>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int NMAT = MODE == 0 ? 2 : 1;
+  constexpr int NSUB = MODE == 0 ? 2 : 4;
+  constexpr int WN = 16 * NSUB;  // features per wave
+  constexpr int BNW = 4 * WN;    // features per workgroup
   __shared__ uint16_t sA[2][2][BM][LDS_ROW];  // [stage][hi/lo][row][k]
   __shared__ float sC[2][BM];                 // -136 * sum_k x_k per row and stage
 
-  const int4 tile = a.tiles[blockIdx.y];
+  // XCD-contiguous work numbering
+  const int L = blockIdx.x;
+  const int per = a.work_padded / 8;
+  const int W = (L & 7) * per + (L >> 3);
+  if (W >= a.work) return;
+  const int n_tiles_n = (a.N + BNW - 1) / BNW;
+  const int4 tile = a.tiles[W / n_tiles_n];
   const int e = tile.x, pos0 = tile.y, rows = tile.z;
-  const int n0 = blockIdx.x * BN;
+  const int n0 = (W % n_tiles_n) * BNW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = a.K, N = a.N, nkb = K / KB;
   const uint8_t* base = a.eaddr[e];
 
-  // A staging: thread -> (row ar, eighth-of-block aq): 8 elements of each plane
+  // A staging: thread -> (row ar, quarter aq of the block): 8 elements of each plane
   const int ar = tid >> 2, aq = tid & 3;
   const bool arow_ok = ar < rows;
-  const uint16_t* pah = a.ah;
-  const uint16_t* pal = a.al;
-  if (arow_ok) {
-    const int64_t src_row = a.arow ? (int64_t)(a.arow[pos0 + ar] / a.arow_div) : (int64_t)(pos0 + ar);
-    pah += src_row * K + aq * 8;
-    pal += src_row * K + aq * 8;
-  }
+  int64_t src_row = 0;
+  if (arow_ok) src_row = a.arow ? (int64_t)(a.arow[pos0 + ar] / a.arow_div) : (int64_t)(pos0 + ar);
+  const uint16_t* pah = a.ah + src_row * K + aq * 8;
+  const uint16_t* pal = a.al + src_row * K + aq * 8;
+  const float* psum = a.asum + src_row * nkb;
 
-  // B: lane -> (feature bn = lane % 16 of the wave's 16, k-quarter kq = lane / 16)
-  const int bn = n0 + wave * 16 + (lane & 15);
+  // B: lane -> (feature lane % 16 of each of the wave's NSUB subtiles, k-quarter kq)
   const int kq = lane >> 4;
-  const bool bn_ok = bn < N;
   const int shift = (kq >> 1) * 4;
-  const int64_t brow = bn_ok ? (int64_t)bn * nkb : 0;
-  const uint8_t* nib0 = base + (MODE == 0 ? a.lay.gate_nib : a.lay.down_nib) + brow * 16 + (kq & 1) * 8;
-  const uint16_t* scl0 = reinterpret_cast<const uint16_t*>(base + (MODE == 0 ? a.lay.gate_scl : a.lay.down_scl)) + brow;
-  const uint8_t* nib1 = base + a.lay.up_nib + brow * 16 + (kq & 1) * 8;
-  const uint16_t* scl1 = reinterpret_cast<const uint16_t*>(base + a.lay.up_scl) + brow;
-
-  f32x4_t acc0[4], acc1[4];
+  // per-matrix planes (uniform) and per-subtile block index of this lane's row (32-bit)
+  const uint8_t* nibm[NMAT];
+  const uint16_t* sclm[NMAT];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc0[s] = acc1[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 ra_hi = make_uint4(0, 0, 0, 0), ra_lo = make_uint4(0, 0, 0, 0);
-  uint2 rb0 = make_uint2(0, 0), rb1 = make_uint2(0, 0);
-  uint32_t rd0 = 0, rd1 = 0;
-
-#define MOE_LOAD_A(KBI)                                                                  \
-  if (arow_ok) {                                                                         \
-    ra_hi = *reinterpret_cast<const uint4*>(pah + (int64_t)(KBI) * KB);                  \
-    ra_lo = *reinterpret_cast<const uint4*>(pal + (int64_t)(KBI) * KB);                  \
+  for (int m = 0; m < NMAT; ++m) {
+    nibm[m] = base + (MODE == 1 ? a.lay.down_nib : (m == 0 ? a.lay.gate_nib : a.lay.up_nib)) + (kq & 1) * 8;
+    sclm[m] = reinterpret_cast<const uint16_t*>(base + (MODE == 1 ? a.lay.down_scl : (m == 0 ? a.lay.gate_scl
+                                                                                              : a.lay.up_scl)));
   }
-#define MOE_LOAD_B(KBI)                                                                  \
-  if (bn_ok) {                                                                           \
-    rb0 = *reinterpret_cast<const uint2*>(nib0 + (int64_t)(KBI) * 16);                   \
-    rd0 = scl0[KBI];                                                                     \
-    if (NMAT == 2) {                                                                     \
-      rb1 = *reinterpret_cast<const uint2*>(nib1 + (int64_t)(KBI) * 16);                 \
-      rd1 = scl1[KBI];                                                                   \
-    }                                                                                    \
+  uint32_t brow[NSUB];  // block index of (row, k-block 0); every expert matrix is < 4 GiB
+  bool bok[NSUB];
+#pragma unroll
+  for (int ns = 0; ns < NSUB; ++ns) {
+    const int bn = n0 + wave * WN + ns * 16 + (lane & 15);
+    bok[ns] = bn < N;
+    brow[ns] = bok[ns] ? (uint32_t)bn * (uint32_t)nkb : 0u;
   }
 
-  MOE_LOAD_A(0)
-  MOE_LOAD_B(0)
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int stage = kb & 1;
-    {
-      // stage this block's A rows and their sums
-      *reinterpret_cast<uint4*>(&sA[stage][0][ar][aq * 8]) = ra_hi;
-      *reinterpret_cast<uint4*>(&sA[stage][1][ar][aq * 8]) = ra_lo;
-      const uint32_t h[4] = {ra_hi.x, ra_hi.y, ra_hi.z, ra_hi.w};
-      const uint32_t l[4] = {ra_lo.x, ra_lo.y, ra_lo.z, ra_lo.w};
-      float sum = 0.f;
+  f32x4_t acc[NMAT][NSUB][4];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int ns = 0; ns < NSUB; ++ns)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc[m][ns][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // register ring: block kb lives in set kb % kDepth
+  uint4 ra_hi[kDepth], ra_lo[kDepth];
+  float ra_sum[kDepth];
+  uint2 rb[kDepth][NMAT][NSUB];
+  uint32_t rd[kDepth][NMAT][NSUB];
+
+  auto issue = [&](int set, int kb) __attribute__((always_inline)) {
+    if (kb < nkb) {
+      if (arow_ok) {
+        ra_hi[set] = *reinterpret_cast<const uint4*>(pah + (int64_t)kb * KB);
+        ra_lo[set] = *reinterpret_cast<const uint4*>(pal + (int64_t)kb * KB);
+        ra_sum[set] = aq == 0 ? psum[kb] : 0.f;
+      } else {
+        ra_hi[set] = ra_lo[set] = make_uint4(0, 0, 0, 0);
+        ra_sum[set] = 0.f;
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ++ns) {
+          if (bok[ns]) {
+            const uint32_t blk = brow[ns] + (uint32_t)kb;
+            rb[set][m][ns] = *reinterpret_cast<const uint2*>(nibm[m] + blk * 16u);
+            rd[set][m][ns] = sclm[m][blk];
+          } else {
+            rb[set][m][ns] = make_uint2(0, 0);
+            rd[set][m][ns] = 0;
+          }
+        }
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j) issue(j, j);
+
+  for (int kb0 = 0; kb0 < nkb; kb0 += kDepth) {
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      const int kb = kb0 + j;
+      if (kb >= nkb) break;
+      const int stage = kb & 1;
+      *reinterpret_cast<uint4*>(&sA[stage][0][ar][aq * 8]) = ra_hi[j];
+      *reinterpret_cast<uint4*>(&sA[stage][1][ar][aq * 8]) = ra_lo[j];
+      if (aq == 0) sC[stage][ar] = ra_sum[j];
+      bf16x8_t bop[NMAT][NSUB];
+      float dsc[NMAT][NSUB];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ++ns) {
+          bop[m][ns] = weight_operand(rb[j][m][ns].x, rb[j][m][ns].y, shift);
+          dsc[m][ns] = half_bits_to_float(rd[j][m][ns]);
+        }
+      issue(j, kb + kDepth);  // refill this set while the block computes
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r = s * 16 + (lane & 15);
+        const bf16x8_t ahi = *reinterpret_cast<const bf16x8_t*>(&sA[stage][0][r][kq * 8]);
+        const bf16x8_t alo = *reinterpret_cast<const bf16x8_t*>(&sA[stage][1][r][kq * 8]);
+        const f32x4_t cinit = *reinterpret_cast<const f32x4_t*>(&sC[stage][s * 16 + kq * 4]);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int ns = 0; ns < NSUB; ++ns) {
+            f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bop[m][ns], cinit, 0, 0, 0);
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bop[m][ns], t, 0, 0, 0);
+            acc[m][ns][s] += dsc[m][ns] * t;
+          }
+      }
+    }
+  }
+
+  // epilogue: lane holds rows s*16 + kq*4 + i of feature n0 + wave*WN + ns*16 + lane%16
+  if (MODE == 0) {
+    float bs[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sum += __uint_as_float(h[i] << 16) + __uint_as_float(h[i] & 0xFFFF0000u);
-        sum += __uint_as_float(l[i] << 16) + __uint_as_float(l[i] & 0xFFFF0000u);
-      }
-      sum += __shfl_xor(sum, 1, 64);
-      sum += __shfl_xor(sum, 2, 64);
-      if (aq == 0) sC[stage][ar] = -136.0f * sum;
-    }
-    const bf16x8_t b0 = weight_operand(rb0.x, rb0.y, shift);
-    const float d0 = half_bits_to_float(rd0);
-    bf16x8_t b1 = b0;
-    float d1 = 0.f;
-    if (NMAT == 2) {
-      b1 = weight_operand(rb1.x, rb1.y, shift);
-      d1 = half_bits_to_float(rd1);
-    }
-    __syncthreads();
-    if (kb + 1 < nkb) {  // prefetch the next block while this one computes
-      MOE_LOAD_A(kb + 1)
-      MOE_LOAD_B(kb + 1)
-    }
+        const int r = s * 16 + kq * 4 + i;
+        const int64_t pos = pos0 + r;
+        float part = 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int r = s * 16 + (lane & 15);
-      const bf16x8_t ahi = *reinterpret_cast<const bf16x8_t*>(&sA[stage][0][r][kq * 8]);
-      const bf16x8_t alo = *reinterpret_cast<const bf16x8_t*>(&sA[stage][1][r][kq * 8]);
-      const int rc = s * 16 + kq * 4;  // accumulator rows of this lane
-      const f32x4_t cinit = {sC[stage][rc + 0], sC[stage][rc + 1], sC[stage][rc + 2], sC[stage][rc + 3]};
-      f32x4_t t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b0, cinit, 0, 0, 0);
-      t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b0, t0, 0, 0, 0);
-      acc0[s] += d0 * t0;
-      if (NMAT == 2) {
-        f32x4_t t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b1, cinit, 0, 0, 0);
-        t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b1, t1, 0, 0, 0);
-        acc1[s] += d1 * t1;
+        for (int ns = 0; ns < NSUB; ++ns) {
+          const int bn = n0 + wave * WN + ns * 16 + (lane & 15);
+          const float h = silu(acc[0][ns][s][i]) * acc[1][ns][s][i];
+          const uint16_t hh = bf16_bits_rne(h);
+          const uint16_t hl = bf16_bits_rne(h - bf16_to_float(hh));
+          if (r < rows && bok[ns]) {
+            const int64_t o = pos * N + (bn & ~31) + plane_pos(bn & 31);
+            a.hh[o] = hh;
+            a.hl[o] = hl;
+            part += bf16_to_float(hh) + bf16_to_float(hl);
+          }
+        }
+        bs[s][i] = row16_sum(part);  // every feature of this wave's 32-block
       }
+    // the wave's 32 features form h block (n0 + wave*WN) / 32 of each row
+    const int blk = (n0 + wave * WN) >> 5;
+    const int nkb_out = N >> 5;
+    if ((lane & 15) == 0 && n0 + wave * WN < N) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = s * 16 + kq * 4 + i;
+          if (r < rows) a.hsum[(int64_t)(pos0 + r) * nkb_out + blk] = -136.0f * bs[s][i];
+        }
     }
-  }
-#undef MOE_LOAD_A
-#undef MOE_LOAD_B
-
-  // epilogue: lane holds rows s*16 + kq*4 + i of feature bn
-  if (!bn_ok) return;
+  } else {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+    for (int ns = 0; ns < NSUB; ++ns) {
+      const int bn = n0 + wave * WN + ns * 16 + (lane & 15);
+      if (!bok[ns]) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = s * 16 + kq * 4 + i;
-      if (r >= rows) continue;
-      const int64_t pos = pos0 + r;
-      if (MODE == 0) {
-        const float h = silu(acc0[s][i]) * acc1[s][i];
-        const uint16_t hh = bf16_bits_rne(h);
-        const uint16_t hl = bf16_bits_rne(h - bf16_to_float(hh));
-        const int64_t o = pos * N + (bn & ~31) + plane_pos(bn & 31);
-        a.hh[o] = hh;
-        a.hl[o] = hl;
-      } else {
-        a.y[pos * N + bn] = acc0[s][i];
-      }
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = s * 16 + kq * 4 + i;
+          if (r < rows) a.y[(int64_t)(pos0 + r) * N + bn] = acc[0][ns][s][i];
+        }
     }
   }
 }
@@ -287,16 +388,20 @@ hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E,
   hipLaunchKernelGGL(expert_scatter_kernel, dim3(E), dim3(256), 0, s, ids, n_pairs, offsets, perm, inv);
   return hipGetLastError();
 }
-hipError_t launch_split_rows(const float* src, int64_t rows, int32_t K, uint16_t* hi, uint16_t* lo, hipStream_t s) {
-  const int64_t n = rows * K;
-  hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, n, K, hi, lo);
+hipError_t launch_split_rows(const float* src, int64_t rows, int32_t K, uint16_t* hi, uint16_t* lo, float* bsum,
+                             hipStream_t s) {
+  if (K % 32) return hipErrorInvalidValue;
+  const int64_t nb = rows * (K / 32);
+  hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, src, nb, K, hi, lo, bsum);
   return hipGetLastError();
 }
-hipError_t launch_grouped_gemm(const GemmArgs& a, int mode, int n_tiles, const Launch& l) {
-  if (a.K % 32 || n_tiles <= 0) return hipErrorInvalidValue;
-  const dim3 grid((a.N + BN - 1) / BN, n_tiles);
-  if (mode == 0) return launch(grouped_gemm_kernel<0>, grid, dim3(256), l, a);
-  return launch(grouped_gemm_kernel<1>, grid, dim3(256), l, a);
+hipError_t launch_grouped_gemm(GemmArgs a, int mode, int n_tiles, const Launch& l) {
+  if (a.K % 32 || a.N % 32 || n_tiles <= 0) return hipErrorInvalidValue;
+  const int bnw = mode == 0 ? 128 : 256;
+  a.work = n_tiles * ((a.N + bnw - 1) / bnw);
+  a.work_padded = (a.work + 7) / 8 * 8;
+  if (mode == 0) return launch(grouped_gemm_kernel<0>, dim3(a.work_padded), dim3(256), l, a);
+  return launch(grouped_gemm_kernel<1>, dim3(a.work_padded), dim3(256), l, a);
 }
 hipError_t launch_combine_pairs(const float* ypair, const int32_t* inv, const float* w, int32_t T, int32_t k,
                                 int32_t H, float* y, int32_t accumulate, hipStream_t s) {
