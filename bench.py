@@ -127,7 +127,7 @@ def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "grouped_gemm_kernel (gate/up + down), algorithmic flops 6*H*F per pair",
-                     "mfma_flops_per_algorithmic_flop": 2},
+                     "mfma_flops_per_algorithmic_flop": 1},
     }
 
 

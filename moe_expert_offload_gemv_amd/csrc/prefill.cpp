@@ -16,7 +16,20 @@
 #include "runtime.h"
 
 namespace {
-constexpr int kTileRows = 64;
+constexpr int kMinTileRows = 64;  // tiles hold 64 or 128 pairs of one expert
+
+// Rows per tile for a pass: 128-row tiles halve the weight conversions per
+// MFMA but pad small experts further. A 64-row tile step is taken to cost
+// 0.6 of a 128-row one (its weight conversion does not shrink with the
+// rows), so 128 is used when it needs fewer than 0.6 x as many tiles.
+int tile_rows(const int32_t* counts, int32_t E) {
+  int64_t t64 = 0, t128 = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    t64 += (counts[e] + 63) / 64;
+    t128 += (counts[e] + 127) / 128;
+  }
+  return 10 * t128 < 6 * t64 ? 128 : 64;
+}
 
 bool capturing(hipStream_t s) {
   hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
@@ -35,10 +48,8 @@ struct Prefill {
   int32_t* offsets = nullptr;   // [E + 1]
   int4* tiles = nullptr;        // [max_tiles]
   const uint8_t** eaddr = nullptr;  // [E]
-  uint16_t *xh = nullptr, *xl = nullptr;  // [T][H]
-  float* xsum = nullptr;                  // [T][H/32]
-  uint16_t *hh = nullptr, *hl = nullptr;  // [P][F]
-  float* hsum = nullptr;                  // [P][F/32]
+  _Float16* x16 = nullptr;      // [T][H] activations, fp16 in operand order
+  _Float16* h16 = nullptr;      // [P][F] SwiGLU outputs, fp16 in operand order
   float* ypair = nullptr;       // [P][H]
   // pinned staging of the small transfers
   int32_t* h_counts = nullptr;
@@ -60,7 +71,7 @@ int moe_prefill_alloc(moe_ctx* c) {
   c->pf = p;
   const int64_t E = c->E, P = T * c->k;
   p->max_tokens = T, p->max_pairs = P;
-  p->max_tiles = E + P / kTileRows + 1;
+  p->max_tiles = E + P / kMinTileRows + 1;
   int rc;
   auto dev = [&](void** q, size_t bytes, const char* what) { return moe_ctx_dev_alloc(c, q, bytes, what); };
   if ((rc = dev((void**)&p->ids, sizeof(int32_t) * P, "prefill ids")) ||
@@ -71,12 +82,8 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = dev((void**)&p->offsets, sizeof(int32_t) * (E + 1), "prefill offsets")) ||
       (rc = dev((void**)&p->tiles, sizeof(int4) * p->max_tiles, "prefill tiles")) ||
       (rc = dev((void**)&p->eaddr, sizeof(uint8_t*) * E, "prefill addresses")) ||
-      (rc = dev((void**)&p->xh, sizeof(uint16_t) * T * c->H, "prefill x hi")) ||
-      (rc = dev((void**)&p->xl, sizeof(uint16_t) * T * c->H, "prefill x lo")) ||
-      (rc = dev((void**)&p->xsum, sizeof(float) * T * (c->H / 32), "prefill x block sums")) ||
-      (rc = dev((void**)&p->hsum, sizeof(float) * P * (c->F / 32), "prefill h block sums")) ||
-      (rc = dev((void**)&p->hh, sizeof(uint16_t) * P * c->F, "prefill h hi")) ||
-      (rc = dev((void**)&p->hl, sizeof(uint16_t) * P * c->F, "prefill h lo")) ||
+      (rc = dev((void**)&p->x16, sizeof(_Float16) * T * c->H, "prefill x fp16")) ||
+      (rc = dev((void**)&p->h16, sizeof(_Float16) * P * c->F, "prefill h fp16")) ||
       (rc = dev((void**)&p->ypair, sizeof(float) * P * c->H, "prefill pair outputs")))
     return rc;
   const unsigned pin = hipHostMallocDefault;
@@ -141,6 +148,7 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   // 3. offsets, tiles of the used experts, and where each expert is read from
   int64_t n_tiles = 0, staged = 0, pos = 0;
   const int64_t S = c->S;
+  const int bm = tile_rows(p->h_counts, E);
   for (int32_t e = 0; e < E; ++e) {
     const int32_t m = p->h_counts[e];
     p->h_offsets[e] = (int32_t)pos;
@@ -157,8 +165,7 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
       } else {
         p->h_eaddr[e] = c->host_layers_dev[layer] + (int64_t)e * c->B;  // no block left: read zero-copy
       }
-      for (int32_t m0 = 0; m0 < m; m0 += kTileRows)
-        p->h_tiles[n_tiles++] = int4{e, (int32_t)(pos + m0), std::min(kTileRows, m - m0), 0};
+      for (int32_t m0 = 0; m0 < m; m0 += bm) p->h_tiles[n_tiles++] = int4{e, (int32_t)(pos + m0), std::min(bm, m - m0), 0};
     }
     pos += m;
   }
@@ -172,26 +179,26 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   // 4. stable sort of the pairs by expert
   PF_HIP(c, moe::launch_expert_scatter(p->ids, P, E, p->offsets, p->perm, p->inv, s));
 
-  // 5. activations as bf16 hi/lo planes
-  PF_HIP(c, moe::launch_split_rows(x, T, H, p->xh, p->xl, p->xsum, s));
+  // 5. activations as fp16 rows in operand order
+  PF_HIP(c, moe::launch_convert_rows(x, T, H, p->x16, s));
 
   // 6. grouped GEMMs over the used tiles
   hipEvent_t* ev = nullptr;
   if (c->profiling && c->prefill_events.size() >= 4) ev = c->prefill_events.data();
   moe::GemmArgs g{};
-  g.ah = p->xh, g.al = p->xl, g.asum = p->xsum, g.arow = p->perm, g.arow_div = k;
+  g.a16 = p->x16, g.arow = p->perm, g.arow_div = k;
   g.tiles = p->tiles, g.eaddr = p->eaddr;
   g.K = H, g.N = F;
   g.lay = c->lay;
-  g.hh = p->hh, g.hl = p->hl, g.hsum = p->hsum;
+  g.h16 = p->h16;
   moe::Launch l1 = ls, l2 = ls;
   if (ev) l1.start = ev[0], l1.stop = ev[1], l2.start = ev[2], l2.stop = ev[3];
-  PF_HIP(c, moe::launch_grouped_gemm(g, 0, (int)n_tiles, l1));
+  PF_HIP(c, moe::launch_grouped_gemm(g, 0, bm, (int)n_tiles, l1));
   moe::GemmArgs d = g;
-  d.ah = p->hh, d.al = p->hl, d.asum = p->hsum, d.arow = nullptr, d.arow_div = 1;
+  d.a16 = p->h16, d.arow = nullptr, d.arow_div = 1;
   d.K = F, d.N = H;
   d.y = p->ypair;
-  PF_HIP(c, moe::launch_grouped_gemm(d, 1, (int)n_tiles, l2));
+  PF_HIP(c, moe::launch_grouped_gemm(d, 1, bm, (int)n_tiles, l2));
 
   // 7. weighted combine in pick order
   PF_HIP(c, moe::launch_combine_pairs(p->ypair, p->inv, p->w, T, k, H, y, (flags & MOE_ACCUMULATE) ? 1 : 0, s));

@@ -6,20 +6,20 @@
 //
 //   expert_histogram_kernel  pair counts per expert
 //   expert_scatter_kernel    stable counting sort: perm[pos] = pair, inv[pair] = pos
-//   split_rows_kernel        fp32 rows -> bf16 hi and lo planes (x = hi + lo + O(2^-16 x))
-//   grouped_gemm_kernel      per tile of one expert: gate/up -> h = silu(g) * u as
-//                            bf16 hi/lo planes, or down -> y_pair (fp32)
+//   convert_rows_kernel      fp32 rows -> fp16 rows in operand order
+//   grouped_gemm_kernel      per tile of one expert: gate/up -> h = silu(g) * u
+//                            (fp16 rows in operand order), or down -> y_pair (fp32)
 //   combine_pairs_kernel     y[t] = sum_i w_i y_pair[inv[t, i]] in pick order
 //
-// MFMA form (v_mfma_f32_16x16x32_bf16, one 32-weight quant block per
-// instruction): the weight operand holds 128 + q exactly (bf16 bits 0x4300 | q,
-// built from two nibbles per v_and_or), the accumulator enters each block
-// holding -136 * sum_k x_k, so the block result is sum_k (q_k - 8) x_k; the
-// block's fp16 scale multiplies it in fp32. The activations enter twice, as
-// the bf16 hi and lo parts, so the product carries ~16 bits of x while the
-// weight codes stay exact. Within every group of four k the operand order is
-// (0, 2, 1, 3), which is how two nibbles per dword land in the weight
-// operand; the activation planes are stored in that order.
+// MFMA form: v_mfma_f32_16x16x32_f16 with fp32 accumulation straight through
+// K. The weight operand is built in registers from the quant blocks as
+// fp16(d * (q - 8)): each nibble pair becomes 1024 + q by one v_and_or into
+// the fp16 mantissa, 1032 is subtracted exactly and the block scale d
+// multiplies, so every weight is rounded once. The activations enter as fp16.
+// One K step is 64 (two quant blocks); within a step lane group g of the
+// wave reads 8 bytes (16 nibbles) of block g/2 and feeds the low nibbles to
+// the first MFMA and the high nibbles to the second. The activation rows are
+// stored in the matching order (step_pos), so LDS reads are 16-byte vectors.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,47 +29,71 @@ namespace moe {
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 64;   // pair rows per tile
-constexpr int BN = 64;   // output features per workgroup (16 per wave)
-constexpr int KB = 32;   // one quant block per MFMA step
-constexpr int LDS_ROW = KB + 8;  // padded bf16 row in LDS
+constexpr int KS = 64;             // k per step: two quant blocks
+constexpr int LDS_ROW = KS + 8;    // padded fp16 row in LDS: 144 B, rows 4 banks apart
 
-__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (finite inputs)
-  return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ float bf16_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// (0,2,1,3,4,6,5,7): order of eight consecutive weights in an operand (an involution)
+__device__ __forceinline__ int ord8(int i) { return (i & 4) | ((i & 1) << 1) | ((i >> 1) & 1); }
 
-// position of logical element k inside its 32-block of an activation plane
-__device__ __forceinline__ int plane_pos(int k) { return (k & ~3) | ((k & 1) << 1) | ((k >> 1) & 1); }
-
-__device__ __forceinline__ float half_bits_to_float(uint32_t bits) {
-  _Float16 h;
-  uint16_t b = (uint16_t)bits;
-  __builtin_memcpy(&h, &b, 2);
-  return (float)h;
+// position of element e (0..63) of a K step inside the stored row: operand
+// half h = low/high nibble, lane group g = 2 * block + byte half, slot i
+__device__ __forceinline__ int step_pos(int e) {
+  const int bl = e >> 5, eb = e & 31, h = eb >> 4, r = eb & 15;
+  return 32 * h + 8 * (2 * bl + (r >> 3)) + ord8(r & 7);
 }
 
-// eight nibbles (low halves when shift == 0, high halves when shift == 4) of
-// the 8 bytes w0,w1 as bf16(128 + q) in operand order (0,2,1,3),(4,6,5,7)
-__device__ __forceinline__ bf16x8_t weight_operand(uint32_t w0, uint32_t w1, int shift) {
-  w0 >>= shift;
-  w1 >>= shift;
-  uint32_t p[4];
-  p[0] = (w0 & 0x000F000Fu) | 0x43004300u;
-  p[1] = ((w0 >> 8) & 0x000F000Fu) | 0x43004300u;
-  p[2] = (w1 & 0x000F000Fu) | 0x43004300u;
-  p[3] = ((w1 >> 8) & 0x000F000Fu) | 0x43004300u;
-  bf16x8_t r;
-  __builtin_memcpy(&r, p, 16);
-  return r;
+__device__ __forceinline__ f16x2_t as_h2(uint32_t u) {
+  f16x2_t v;
+  __builtin_memcpy(&v, &u, 4);
+  return v;
+}
+
+// 16 weights of one column from 8 bytes of a quant block: bytes jb..jb+7
+// hold elements jb..jb+7 (low nibbles) and jb+16..jb+23 (high nibbles).
+// lo gets jb + (0,2,1,3,4,6,5,7), hi the same + 16; value fp16(d * (q - 8)).
+__device__ __forceinline__ void weight_operands(u32x2_t w, f16x2_t d2, f16x8_t& lo, f16x8_t& hi) {
+  constexpr uint32_t M = 0x000F000Fu, MAGIC = 0x64006400u;  // fp16 1024 in both halves
+  const f16x2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  uint32_t p[8];
+  p[0] = (w.x & M) | MAGIC;
+  p[1] = ((w.x >> 8) & M) | MAGIC;
+  p[2] = (w.y & M) | MAGIC;
+  p[3] = ((w.y >> 8) & M) | MAGIC;
+  p[4] = ((w.x >> 4) & M) | MAGIC;
+  p[5] = ((w.x >> 12) & M) | MAGIC;
+  p[6] = ((w.y >> 4) & M) | MAGIC;
+  p[7] = ((w.y >> 12) & M) | MAGIC;
+  f16x2_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (as_h2(p[j]) - off) * d2;  // q - 8 exact, one rounding
+  __builtin_memcpy(&lo, &v[0], 16);
+  __builtin_memcpy(&hi, &v[4], 16);
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// global loads of K step j: A pieces, weight bytes and block scales
+template <int AV, int NMAT, int NSUB>
+__device__ __forceinline__ void gemm_load(u32x4_t (&ra)[AV], u32x2_t (&rb)[NMAT][NSUB], uint32_t (&rd)[NMAT][NSUB],
+                                          const u32x4_t* const (&asrc)[AV], const uint8_t* const (&nibm)[NMAT],
+                                          const uint16_t* const (&sclm)[NMAT], const uint32_t (&brow)[NSUB], int j) {
+#pragma unroll
+  for (int v = 0; v < AV; ++v) ra[v] = asrc[v][(int64_t)j * (KS / 8)];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int ns = 0; ns < NSUB; ++ns) {
+      const uint32_t blk = brow[ns] + 2u * (uint32_t)j;
+      rb[m][ns] = *reinterpret_cast<const u32x2_t*>(nibm[m] + blk * 16u);
+      rd[m][ns] = sclm[m][blk];
+    }
+}
 
 }  // namespace
 
@@ -110,80 +134,47 @@ __global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* ids,
   }
 }
 
-// rows of fp32 [R][K] -> bf16 hi and lo planes [R][K] in operand order, and
-// per (row, 32-block) -136 * sum of (hi + lo): one thread per block
-__global__ __launch_bounds__(256) void split_rows_kernel(const float* src, int64_t nblocks, int32_t K, uint16_t* hi,
-                                                         uint16_t* lo, float* bsum) {
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblocks) return;
-  const float4* s4 = reinterpret_cast<const float4*>(src + b * 32);
-  uint16_t h[32], l[32];
-  float sum = 0.f;
+// fp32 rows [R][K] -> fp16 rows [R][K] in operand order; one thread per 8
+// stored halves, which come from 8 consecutive elements (in ord8 order)
+__global__ __launch_bounds__(256) void convert_rows_kernel(const float* src, int64_t n_oct, uint4* dst) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= n_oct) return;
+  const int64_t step = o >> 3;       // K % 64 == 0: steps never straddle rows
+  const int oq = (int)(o & 7);       // stored positions 8*oq .. 8*oq+7
+  const int h = oq >> 2, g = oq & 3;
+  const int e0 = 32 * (g >> 1) + 16 * h + 8 * (g & 1);
+  const float4* s4 = reinterpret_cast<const float4*>(src + step * KS + e0);
+  const float4 a = s4[0], b = s4[1];
+  const float v[8] = {a.x, a.z, a.y, a.w, b.x, b.z, b.y, b.w};  // ord8
+  uint32_t u[4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float4 q = s4[c];
-    const float v[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = 4 * c + j;
-      const uint16_t hh = bf16_bits_rne(v[j]);
-      const uint16_t ll = bf16_bits_rne(v[j] - bf16_to_float(hh));
-      h[plane_pos(k)] = hh;
-      l[plane_pos(k)] = ll;
-      sum += bf16_to_float(hh) + bf16_to_float(ll);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const f16x2_t t = {(_Float16)v[2 * j], (_Float16)v[2 * j + 1]};
+    __builtin_memcpy(&u[j], &t, 4);
   }
-  uint4* ph = reinterpret_cast<uint4*>(hi + b * 32);
-  uint4* pl = reinterpret_cast<uint4*>(lo + b * 32);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t wh[4], wl[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wh[j] = (uint32_t)h[8 * c + 2 * j] | ((uint32_t)h[8 * c + 2 * j + 1] << 16);
-      wl[j] = (uint32_t)l[8 * c + 2 * j] | ((uint32_t)l[8 * c + 2 * j + 1] << 16);
-    }
-    ph[c] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    pl[c] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-  }
-  bsum[b] = -136.0f * sum;
-  (void)K;
+  dst[o] = make_uint4(u[0], u[1], u[2], u[3]);
 }
 
-namespace {
-// GFX9 DPP controls (butterflies inside a 16-lane row)
-template <int CTRL>
-__device__ __forceinline__ float dppf(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-// sum over the 16 lanes of a DPP row; every lane of the row gets it
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dppf<0x141>(v);  // row_half_mirror
-  v += dppf<0x140>(v);  // row_mirror
-  return v;
-}
-constexpr int kDepth = 1;  // blocks of A and B in flight ahead of the one computed
-}  // namespace
-
-// One workgroup computes a 64-row tile of one expert's pairs against
-// 4 waves x NSUB x 16 output features.
-// MODE 0: gate/up (two weight matrices, SwiGLU, writes h planes and their
-//         per-block -136 * sums); NSUB = 2, so each wave owns one 32-feature
-//         block of h.
-// MODE 1: down (one matrix, writes y_pair); NSUB = 4.
+// One workgroup computes a BM-row tile of one expert's pairs against
+// 4 waves x NSUB x 16 output features of NMAT weight matrices; every wave
+// covers all BM rows, so each weight is converted once per workgroup.
+// MODE 0: gate/up (two matrices, SwiGLU epilogue, writes h as fp16 rows in
+//         operand order); MODE 1: down (one matrix, writes y_pair).
+// NSUB is chosen so every wave holds at most 128 accumulators and at most
+// four subtiles per matrix (the prefetch registers of a step).
 // Work items are numbered so that each XCD (work item id mod 8 of the launch
 // order) gets a contiguous range: the n-tiles of one row tile, then the next
 // row tile of the same expert, share an L2.
-template <int MODE>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
+template <int BM, int MODE>
+__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   constexpr int NMAT = MODE == 0 ? 2 : 1;
-  constexpr int NSUB = MODE == 0 ? 2 : 4;
-  constexpr int WN = 16 * NSUB;  // features per wave
-  constexpr int BNW = 4 * WN;    // features per workgroup
-  __shared__ uint16_t sA[2][2][BM][LDS_ROW];  // [stage][hi/lo][row][k]
-  __shared__ float sC[2][BM];                 // -136 * sum_k x_k per row and stage
+  constexpr int RB = BM / 16;              // 16-row blocks
+  constexpr int NSUB = 32 / (RB * NMAT) < 4 ? 32 / (RB * NMAT) : 4;  // 16-feature subtiles per wave and matrix
+  constexpr int WN = 16 * NSUB;            // features per wave
+  constexpr int BNW = 4 * WN;              // features per workgroup
+  constexpr int AV = BM * KS / 8 / 256;    // 16-byte pieces of A per thread and step
+  static_assert(NSUB >= 1 && AV >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM][LDS_ROW];
 
   // XCD-contiguous work numbering
   const int L = blockIdx.x;
@@ -195,31 +186,38 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
   const int e = tile.x, pos0 = tile.y, rows = tile.z;
   const int n0 = (W % n_tiles_n) * BNW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.K, N = a.N, nkb = K / KB;
+  const int K = a.K, N = a.N, nks = K / KS, nkb = K / 32;
   const uint8_t* base = a.eaddr[e];
 
-  // A staging: thread -> (row ar, quarter aq of the block): 8 elements of each plane
-  const int ar = tid >> 2, aq = tid & 3;
-  const bool arow_ok = ar < rows;
-  int64_t src_row = 0;
-  if (arow_ok) src_row = a.arow ? (int64_t)(a.arow[pos0 + ar] / a.arow_div) : (int64_t)(pos0 + ar);
-  const uint16_t* pah = a.ah + src_row * K + aq * 8;
-  const uint16_t* pal = a.al + src_row * K + aq * 8;
-  const float* psum = a.asum + src_row * nkb;
+  // A staging: piece t + 256 v is (row (t >> 3) + 32 v, 16-byte column t & 7).
+  // Rows past the tile read the tile's first row: they only feed accumulator
+  // rows that are never stored, so the loads need no guard.
+  const int ac = tid & 7;
+  const u32x4_t* asrc[AV];
+#pragma unroll
+  for (int v = 0; v < AV; ++v) {
+    int r = (tid >> 3) + 32 * v;
+    r = r < rows ? r : 0;
+    const int64_t src_row = a.arow ? (int64_t)(a.arow[pos0 + r] / a.arow_div) : (int64_t)(pos0 + r);
+    asrc[v] = reinterpret_cast<const u32x4_t*>(a.a16 + src_row * K) + ac;
+  }
 
-  // B: lane -> (feature lane % 16 of each of the wave's NSUB subtiles, k-quarter kq)
-  const int kq = lane >> 4;
-  const int shift = (kq >> 1) * 4;
-  // per-matrix planes (uniform) and per-subtile block index of this lane's row (32-bit)
+  // B: lane -> feature lane % 16 of each subtile; lane group g reads bytes
+  // 8 (g & 1) .. +7 of block 2 j + g / 2 of step j
+  const int g = lane >> 4;
   const uint8_t* nibm[NMAT];
   const uint16_t* sclm[NMAT];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
-    nibm[m] = base + (MODE == 1 ? a.lay.down_nib : (m == 0 ? a.lay.gate_nib : a.lay.up_nib)) + (kq & 1) * 8;
-    sclm[m] = reinterpret_cast<const uint16_t*>(base + (MODE == 1 ? a.lay.down_scl : (m == 0 ? a.lay.gate_scl
-                                                                                              : a.lay.up_scl)));
+    nibm[m] = base + (MODE == 1 ? a.lay.down_nib : (m == 0 ? a.lay.gate_nib : a.lay.up_nib)) + 16 * (g >> 1) +
+              8 * (g & 1);
+    sclm[m] = reinterpret_cast<const uint16_t*>(base + (MODE == 1 ? a.lay.down_scl
+                                                                  : (m == 0 ? a.lay.gate_scl : a.lay.up_scl))) +
+              (g >> 1);
   }
-  uint32_t brow[NSUB];  // block index of (row, k-block 0); every expert matrix is < 4 GiB
+  // block index of (feature, block 0), every expert matrix being < 4 GiB;
+  // features past N read feature 0 and are never stored
+  uint32_t brow[NSUB];
   bool bok[NSUB];
 #pragma unroll
   for (int ns = 0; ns < NSUB; ++ns) {
@@ -228,134 +226,68 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     brow[ns] = bok[ns] ? (uint32_t)bn * (uint32_t)nkb : 0u;
   }
 
-  f32x4_t acc[NMAT][NSUB][4];
+  f32x4_t acc[NMAT][NSUB][RB];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
     for (int ns = 0; ns < NSUB; ++ns)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc[m][ns][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < RB; ++s) acc[m][ns][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // register ring: block kb lives in set kb % kDepth
-  uint4 ra_hi[kDepth], ra_lo[kDepth];
-  float ra_sum[kDepth];
-  uint2 rb[kDepth][NMAT][NSUB];
-  uint32_t rd[kDepth][NMAT][NSUB];
+  // registers of the next step
+  u32x4_t ra[AV];
+  u32x2_t rb[NMAT][NSUB];
+  uint32_t rd[NMAT][NSUB];
 
-  auto issue = [&](int set, int kb) __attribute__((always_inline)) {
-    if (kb < nkb) {
-      if (arow_ok) {
-        ra_hi[set] = *reinterpret_cast<const uint4*>(pah + (int64_t)kb * KB);
-        ra_lo[set] = *reinterpret_cast<const uint4*>(pal + (int64_t)kb * KB);
-        ra_sum[set] = aq == 0 ? psum[kb] : 0.f;
-      } else {
-        ra_hi[set] = ra_lo[set] = make_uint4(0, 0, 0, 0);
-        ra_sum[set] = 0.f;
+  gemm_load<AV, NMAT, NSUB>(ra, rb, rd, asrc, nibm, sclm, brow, 0);
+  for (int j = 0; j < nks; ++j) {
+    const int stage = j & 1;
+#pragma unroll
+    for (int v = 0; v < AV; ++v)
+      *reinterpret_cast<u32x4_t*>(&sA[stage][(tid >> 3) + 32 * v][ac * 8]) = ra[v];
+    f16x8_t bop[NMAT][NSUB][2];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int ns = 0; ns < NSUB; ++ns) {
+        const f16x2_t d2 = as_h2(rd[m][ns] | (rd[m][ns] << 16));
+        weight_operands(rb[m][ns], d2, bop[m][ns][0], bop[m][ns][1]);
       }
+    gemm_load<AV, NMAT, NSUB>(ra, rb, rd, asrc, nibm, sclm, brow, j + 1 < nks ? j + 1 : j);  // last step reloads itself
+    __syncthreads();
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m)
+    for (int s = 0; s < RB; ++s)
 #pragma unroll
-        for (int ns = 0; ns < NSUB; ++ns) {
-          if (bok[ns]) {
-            const uint32_t blk = brow[ns] + (uint32_t)kb;
-            rb[set][m][ns] = *reinterpret_cast<const uint2*>(nibm[m] + blk * 16u);
-            rd[set][m][ns] = sclm[m][blk];
-          } else {
-            rb[set][m][ns] = make_uint2(0, 0);
-            rd[set][m][ns] = 0;
-          }
-        }
-    }
-  };
-
-#pragma unroll
-  for (int j = 0; j < kDepth; ++j) issue(j, j);
-
-  for (int kb0 = 0; kb0 < nkb; kb0 += kDepth) {
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-      const int kb = kb0 + j;
-      if (kb >= nkb) break;
-      const int stage = kb & 1;
-      *reinterpret_cast<uint4*>(&sA[stage][0][ar][aq * 8]) = ra_hi[j];
-      *reinterpret_cast<uint4*>(&sA[stage][1][ar][aq * 8]) = ra_lo[j];
-      if (aq == 0) sC[stage][ar] = ra_sum[j];
-      bf16x8_t bop[NMAT][NSUB];
-      float dsc[NMAT][NSUB];
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int ns = 0; ns < NSUB; ++ns) {
-          bop[m][ns] = weight_operand(rb[j][m][ns].x, rb[j][m][ns].y, shift);
-          dsc[m][ns] = half_bits_to_float(rd[j][m][ns]);
-        }
-      issue(j, kb + kDepth);  // refill this set while the block computes
-      __syncthreads();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int r = s * 16 + (lane & 15);
-        const bf16x8_t ahi = *reinterpret_cast<const bf16x8_t*>(&sA[stage][0][r][kq * 8]);
-        const bf16x8_t alo = *reinterpret_cast<const bf16x8_t*>(&sA[stage][1][r][kq * 8]);
-        const f32x4_t cinit = *reinterpret_cast<const f32x4_t*>(&sC[stage][s * 16 + kq * 4]);
+      for (int h = 0; h < 2; ++h) {
+        const f16x8_t av = *reinterpret_cast<const f16x8_t*>(&sA[stage][s * 16 + (lane & 15)][32 * h + 8 * g]);
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int ns = 0; ns < NSUB; ++ns) {
-            f32x4_t t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bop[m][ns], cinit, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bop[m][ns], t, 0, 0, 0);
-            acc[m][ns][s] += dsc[m][ns] * t;
-          }
+          for (int ns = 0; ns < NSUB; ++ns)
+            acc[m][ns][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bop[m][ns][h], acc[m][ns][s], 0, 0, 0);
       }
-    }
   }
 
-  // epilogue: lane holds rows s*16 + kq*4 + i of feature n0 + wave*WN + ns*16 + lane%16
-  if (MODE == 0) {
-    float bs[4][4];
+  // epilogue: lane holds rows s*16 + g*4 + i of feature n0 + wave*WN + ns*16 + lane%16
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+  for (int ns = 0; ns < NSUB; ++ns) {
+    const int bn = n0 + wave * WN + ns * 16 + (lane & 15);
+    if (!bok[ns]) continue;
+    if (MODE == 0) {
+      const int64_t col = (bn & ~(KS - 1)) + step_pos(bn & (KS - 1));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = s * 16 + kq * 4 + i;
-        const int64_t pos = pos0 + r;
-        float part = 0.f;
-#pragma unroll
-        for (int ns = 0; ns < NSUB; ++ns) {
-          const int bn = n0 + wave * WN + ns * 16 + (lane & 15);
-          const float h = silu(acc[0][ns][s][i]) * acc[1][ns][s][i];
-          const uint16_t hh = bf16_bits_rne(h);
-          const uint16_t hl = bf16_bits_rne(h - bf16_to_float(hh));
-          if (r < rows && bok[ns]) {
-            const int64_t o = pos * N + (bn & ~31) + plane_pos(bn & 31);
-            a.hh[o] = hh;
-            a.hl[o] = hl;
-            part += bf16_to_float(hh) + bf16_to_float(hl);
-          }
-        }
-        bs[s][i] = row16_sum(part);  // every feature of this wave's 32-block
-      }
-    // the wave's 32 features form h block (n0 + wave*WN) / 32 of each row
-    const int blk = (n0 + wave * WN) >> 5;
-    const int nkb_out = N >> 5;
-    if ((lane & 15) == 0 && n0 + wave * WN < N) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < RB; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = s * 16 + kq * 4 + i;
-          if (r < rows) a.hsum[(int64_t)(pos0 + r) * nkb_out + blk] = -136.0f * bs[s][i];
+          const int r = s * 16 + g * 4 + i;
+          if (r < rows) a.h16[(int64_t)(pos0 + r) * N + col] = (_Float16)(silu(acc[0][ns][s][i]) * acc[NMAT - 1][ns][s][i]);
         }
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int ns = 0; ns < NSUB; ++ns) {
-      const int bn = n0 + wave * WN + ns * 16 + (lane & 15);
-      if (!bok[ns]) continue;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < RB; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = s * 16 + kq * 4 + i;
+          const int r = s * 16 + g * 4 + i;
           if (r < rows) a.y[(int64_t)(pos0 + r) * N + bn] = acc[0][ns][s][i];
         }
     }
@@ -388,20 +320,29 @@ hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E,
   hipLaunchKernelGGL(expert_scatter_kernel, dim3(E), dim3(256), 0, s, ids, n_pairs, offsets, perm, inv);
   return hipGetLastError();
 }
-hipError_t launch_split_rows(const float* src, int64_t rows, int32_t K, uint16_t* hi, uint16_t* lo, float* bsum,
-                             hipStream_t s) {
-  if (K % 32) return hipErrorInvalidValue;
-  const int64_t nb = rows * (K / 32);
-  hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, src, nb, K, hi, lo, bsum);
+hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, hipStream_t s) {
+  if (K % KS || rows <= 0) return hipErrorInvalidValue;
+  const int64_t n_oct = rows * (K / 8);
+  hipLaunchKernelGGL(convert_rows_kernel, dim3((unsigned)((n_oct + 255) / 256)), dim3(256), 0, s, src, n_oct,
+                     reinterpret_cast<uint4*>(dst));
   return hipGetLastError();
 }
-hipError_t launch_grouped_gemm(GemmArgs a, int mode, int n_tiles, const Launch& l) {
-  if (a.K % 32 || a.N % 32 || n_tiles <= 0) return hipErrorInvalidValue;
-  const int bnw = mode == 0 ? 128 : 256;
+int gemm_features_per_tile(int mode, int bm) {
+  const int rb = bm / 16, nmat = mode == 0 ? 2 : 1;
+  const int nsub = 32 / (rb * nmat) < 4 ? 32 / (rb * nmat) : 4;
+  return 4 * 16 * nsub;
+}
+hipError_t launch_grouped_gemm(GemmArgs a, int mode, int bm, int n_tiles, const Launch& l) {
+  if (a.K % KS || a.N % KS || n_tiles <= 0 || (bm != 64 && bm != 128) || (mode != 0 && mode != 1))
+    return hipErrorInvalidValue;
+  const int bnw = gemm_features_per_tile(mode, bm);
   a.work = n_tiles * ((a.N + bnw - 1) / bnw);
   a.work_padded = (a.work + 7) / 8 * 8;
-  if (mode == 0) return launch(grouped_gemm_kernel<0>, dim3(a.work_padded), dim3(256), l, a);
-  return launch(grouped_gemm_kernel<1>, dim3(a.work_padded), dim3(256), l, a);
+  const dim3 grid(a.work_padded), block(256);
+  if (mode == 0) return bm == 64 ? launch(grouped_gemm_kernel<64, 0>, grid, block, l, a)
+                                 : launch(grouped_gemm_kernel<128, 0>, grid, block, l, a);
+  return bm == 64 ? launch(grouped_gemm_kernel<64, 1>, grid, block, l, a)
+                  : launch(grouped_gemm_kernel<128, 1>, grid, block, l, a);
 }
 hipError_t launch_combine_pairs(const float* ypair, const int32_t* inv, const float* w, int32_t T, int32_t k,
                                 int32_t H, float* y, int32_t accumulate, hipStream_t s) {

@@ -1,4 +1,4 @@
-"""GPU parity of the prompt pass (sort by expert, staging, bf16-MFMA grouped
+"""GPU parity of the prompt pass (sort by expert, staging, fp16-MFMA grouped
 GEMMs, combine) through the C ABI against the oracle, and its neutrality
 towards the cache policy."""
 import numpy as np
@@ -88,8 +88,10 @@ def test_prefill_router_in_the_loop_matches_decode():
     y2 = torch.empty_like(x)
     moe.moe_prefill(d.ctx, 0, 4, x, None, y1)
     moe.moe_forward(d.ctx, 0, 4, x, None, y2)
-    # two different kernels (MFMA grouped GEMM vs fp32 GEMV) on the same routing
-    assert token_rel_err(y1.cpu().numpy(), y2.cpu().numpy().astype(np.float64)) < 1e-4
+    # two different kernels on the same routing: the fp32 GEMV and the grouped
+    # GEMM on fp16 operands (weights and activations rounded once each, ~5e-4
+    # apart at this shape), so the bar is the one both meet against the oracle
+    assert token_rel_err(y1.cpu().numpy(), y2.cpu().numpy().astype(np.float64)) < TOL
     d.close()
 
 
