@@ -20,6 +20,14 @@
 // wave reads 8 bytes (16 nibbles) of block g/2 and feeds the low nibbles to
 // the first MFMA and the high nibbles to the second. The activation rows are
 // stored in the matching order (step_pos), so LDS reads are 16-byte vectors.
+//
+// Staging: every operand byte of a K step (the A rows, the weight nibbles,
+// the block scales) travels global -> LDS by the LDS-DMA form of the global
+// load (global_load_lds_dwordx4 / _dword: lane l of a wave writes 16 or 4
+// bytes at M0 + 16 l or + 4 l), into a ring of three stages, issued two steps
+// ahead of its use; no VGPR holds data in flight. A rows sit in LDS with their
+// 16-byte chunks XOR-swizzled by (row & 7), so the 16-row fragment reads are
+// free of bank conflicts without padding.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,22 +86,53 @@ __device__ __forceinline__ void weight_operands(u32x2_t w, f16x2_t d2, f16x8_t& 
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// global loads of K step j: A pieces, weight bytes and block scales
-template <int AV, int NMAT, int NSUB>
-__device__ __forceinline__ void gemm_load(u32x4_t (&ra)[AV], u32x2_t (&rb)[NMAT][NSUB], uint32_t (&rd)[NMAT][NSUB],
-                                          const u32x4_t* const (&asrc)[AV], const uint8_t* const (&nibm)[NMAT],
-                                          const uint16_t* const (&sclm)[NMAT], const uint32_t (&brow)[NSUB], int j) {
-#pragma unroll
-  for (int v = 0; v < AV; ++v) ra[v] = asrc[v][(int64_t)j * (KS / 8)];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int ns = 0; ns < NSUB; ++ns) {
-      const uint32_t blk = brow[ns] + 2u * (uint32_t)j;
-      rb[m][ns] = *reinterpret_cast<const u32x2_t*>(nibm[m] + blk * 16u);
-      rd[m][ns] = sclm[m][blk];
-    }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// LDS-DMA loads: lane l writes its bytes at lds + 16 l (or + 4 l); lds must
+// be wave-uniform (it goes to M0)
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds, 16, 0, 0);
 }
+__device__ __forceinline__ void dma4(const void* src, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds, 4, 0, 0);
+}
+
+// s_waitcnt immediate (GFX9 encoding) waiting for vmcnt <= n only
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// workgroup barrier over LDS: this wave's LDS reads are complete, then
+// s_barrier. The DMA completions are waited for with vmcnt before it; a
+// fence here would make the compiler drain every DMA in flight (vmcnt(0)).
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+constexpr int kStages = 3;  // LDS ring: loads run two K steps ahead
+
+// Shape of a workgroup tile: BM rows x 4 waves x NSUB x 16 features of NMAT
+// matrices, and the LDS stage holding one K step of its operands:
+//   [A: BM rows x 128 B][nibbles: NMAT x BNW features x 32 B][scales: NMAT x BNW x 4 B]
+// DA, DB, DS: LDS-DMA instructions per wave and step for each part.
+template <int BM, int MODE>
+struct GemmTile {
+  static constexpr int NMAT = MODE == 0 ? 2 : 1;
+  static constexpr int RB = BM / 16;
+  static constexpr int NSUB = 32 / (RB * NMAT) < 4 ? 32 / (RB * NMAT) : 4;
+  static constexpr int WN = 16 * NSUB;
+  static constexpr int BNW = 4 * WN;
+  static constexpr int A_BYTES = BM * 2 * KS;
+  static constexpr int BN_BYTES = BNW * 32;
+  static constexpr int BS_BYTES = BNW * 4;
+  static constexpr int OFF_BN = A_BYTES;
+  static constexpr int OFF_BS = A_BYTES + NMAT * BN_BYTES;
+  static constexpr int STAGE = OFF_BS + NMAT * BS_BYTES;
+  static constexpr int DA = A_BYTES / 1024 / 4;
+  static constexpr int DB = NMAT * BN_BYTES / 1024 / 4;
+  static constexpr int DS = NMAT * BS_BYTES / 256 / 4;
+  static constexpr int D = DA + DB + DS;
+  static_assert(DA * 4096 == A_BYTES && DB * 4096 == NMAT * BN_BYTES && DS * 1024 == NMAT * BS_BYTES,
+                "every wave issues whole DMA instructions");
+};
 
 }  // namespace
 
@@ -160,21 +199,15 @@ __global__ __launch_bounds__(256) void convert_rows_kernel(const float* src, int
 // covers all BM rows, so each weight is converted once per workgroup.
 // MODE 0: gate/up (two matrices, SwiGLU epilogue, writes h as fp16 rows in
 //         operand order); MODE 1: down (one matrix, writes y_pair).
-// NSUB is chosen so every wave holds at most 128 accumulators and at most
-// four subtiles per matrix (the prefetch registers of a step).
+// NSUB is chosen so every wave holds at most 128 accumulators.
 // Work items are numbered so that each XCD (work item id mod 8 of the launch
 // order) gets a contiguous range: the n-tiles of one row tile, then the next
 // row tile of the same expert, share an L2.
 template <int BM, int MODE>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
-  constexpr int NMAT = MODE == 0 ? 2 : 1;
-  constexpr int RB = BM / 16;              // 16-row blocks
-  constexpr int NSUB = 32 / (RB * NMAT) < 4 ? 32 / (RB * NMAT) : 4;  // 16-feature subtiles per wave and matrix
-  constexpr int WN = 16 * NSUB;            // features per wave
-  constexpr int BNW = 4 * WN;              // features per workgroup
-  constexpr int AV = BM * KS / 8 / 256;    // 16-byte pieces of A per thread and step
-  static_assert(NSUB >= 1 && AV >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) _Float16 sA[2][BM][LDS_ROW];
+  using C = GemmTile<BM, MODE>;
+  constexpr int NMAT = C::NMAT, RB = C::RB, NSUB = C::NSUB, WN = C::WN, BNW = C::BNW;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * C::STAGE];
 
   // XCD-contiguous work numbering
   const int L = blockIdx.x;
@@ -186,45 +219,56 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   const int e = tile.x, pos0 = tile.y, rows = tile.z;
   const int n0 = (W % n_tiles_n) * BNW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4;
   const int K = a.K, N = a.N, nks = K / KS, nkb = K / 32;
   const uint8_t* base = a.eaddr[e];
 
-  // A staging: piece t + 256 v is (row (t >> 3) + 32 v, 16-byte column t & 7).
-  // Rows past the tile read the tile's first row: they only feed accumulator
-  // rows that are never stored, so the loads need no guard.
-  const int ac = tid & 7;
-  const u32x4_t* asrc[AV];
+  // DMA sources of this lane at step 0 (step j adds 128 B, 32 B, 4 B).
+  // A: instruction i of the wave fills rows 8 (wave DA + i) .. +7; lane l
+  // lands in row + l / 8, physical chunk l % 8 = logical chunk ^ (row & 7).
+  // Rows past the tile fetch the tile's first row: they only feed
+  // accumulator rows that are never stored.
+  const uint8_t* asrc[C::DA];
 #pragma unroll
-  for (int v = 0; v < AV; ++v) {
-    int r = (tid >> 3) + 32 * v;
+  for (int i = 0; i < C::DA; ++i) {
+    int r = 8 * (wave * C::DA + i) + (lane >> 3);
     r = r < rows ? r : 0;
     const int64_t src_row = a.arow ? (int64_t)(a.arow[pos0 + r] / a.arow_div) : (int64_t)(pos0 + r);
-    asrc[v] = reinterpret_cast<const u32x4_t*>(a.a16 + src_row * K) + ac;
+    asrc[i] = reinterpret_cast<const uint8_t*>(a.a16 + src_row * K) + 16 * ((lane & 7) ^ (lane >> 3));
+  }
+  // nibbles: instruction q covers features 32 (q % (BNW/32)) .. +31 of matrix
+  // q / (BNW/32); lane l fetches block half l / 32 of feature l % 32 (slot l).
+  // Features past N fetch feature 0 and are never stored.
+  const int64_t nib_plane[2] = {MODE == 1 ? a.lay.down_nib : a.lay.gate_nib, a.lay.up_nib};
+  const int64_t scl_plane[2] = {MODE == 1 ? a.lay.down_scl : a.lay.gate_scl, a.lay.up_scl};
+  uint32_t bsrc[C::DB];
+#pragma unroll
+  for (int i = 0; i < C::DB; ++i) {
+    const int q = wave * C::DB + i, m = q / (BNW / 32);
+    int col = n0 + 32 * (q % (BNW / 32)) + (lane & 31);
+    col = col < N ? col : 0;
+    bsrc[i] = (uint32_t)(nib_plane[m] + ((int64_t)col * nkb + (lane >> 5)) * 16);
+  }
+  // scales: instruction q covers features 64 (q % (BNW/64)) .. +63 of matrix
+  // q / (BNW/64); lane l fetches the two scales of feature l
+  uint32_t ssrc[C::DS];
+#pragma unroll
+  for (int i = 0; i < C::DS; ++i) {
+    const int q = wave * C::DS + i, m = q / (BNW / 64);
+    int col = n0 + 64 * (q % (BNW / 64)) + lane;
+    col = col < N ? col : 0;
+    ssrc[i] = (uint32_t)(scl_plane[m] + (int64_t)col * nkb * 2);
   }
 
-  // B: lane -> feature lane % 16 of each subtile; lane group g reads bytes
-  // 8 (g & 1) .. +7 of block 2 j + g / 2 of step j
-  const int g = lane >> 4;
-  const uint8_t* nibm[NMAT];
-  const uint16_t* sclm[NMAT];
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    uint8_t* S = smem + (j % kStages) * C::STAGE;
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) {
-    nibm[m] = base + (MODE == 1 ? a.lay.down_nib : (m == 0 ? a.lay.gate_nib : a.lay.up_nib)) + 16 * (g >> 1) +
-              8 * (g & 1);
-    sclm[m] = reinterpret_cast<const uint16_t*>(base + (MODE == 1 ? a.lay.down_scl
-                                                                  : (m == 0 ? a.lay.gate_scl : a.lay.up_scl))) +
-              (g >> 1);
-  }
-  // block index of (feature, block 0), every expert matrix being < 4 GiB;
-  // features past N read feature 0 and are never stored
-  uint32_t brow[NSUB];
-  bool bok[NSUB];
+    for (int i = 0; i < C::DA; ++i) dma16(asrc[i] + (int64_t)j * (2 * KS), S + (wave * C::DA + i) * 1024);
 #pragma unroll
-  for (int ns = 0; ns < NSUB; ++ns) {
-    const int bn = n0 + wave * WN + ns * 16 + (lane & 15);
-    bok[ns] = bn < N;
-    brow[ns] = bok[ns] ? (uint32_t)bn * (uint32_t)nkb : 0u;
-  }
+    for (int i = 0; i < C::DB; ++i) dma16(base + bsrc[i] + 32u * (uint32_t)j, S + C::OFF_BN + (wave * C::DB + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::DS; ++i) dma4(base + ssrc[i] + 4u * (uint32_t)j, S + C::OFF_BS + (wave * C::DS + i) * 256);
+  };
 
   f32x4_t acc[NMAT][NSUB][RB];
 #pragma unroll
@@ -234,32 +278,36 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int s = 0; s < RB; ++s) acc[m][ns][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // registers of the next step
-  u32x4_t ra[AV];
-  u32x2_t rb[NMAT][NSUB];
-  uint32_t rd[NMAT][NSUB];
-
-  gemm_load<AV, NMAT, NSUB>(ra, rb, rd, asrc, nibm, sclm, brow, 0);
+  issue(0);
+  if (nks > 1) issue(1);
   for (int j = 0; j < nks; ++j) {
-    const int stage = j & 1;
-#pragma unroll
-    for (int v = 0; v < AV; ++v)
-      *reinterpret_cast<u32x4_t*>(&sA[stage][(tid >> 3) + 32 * v][ac * 8]) = ra[v];
+    // this wave's DMAs of step j are done when at most step j+1's are pending
+    if (j + 1 < nks)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::D));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();  // every wave's step j landed; step j-1's stage is free
+    if (j + 2 < nks) issue(j + 2);
+    const uint8_t* S = smem + (j % kStages) * C::STAGE;
+
     f16x8_t bop[NMAT][NSUB][2];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int ns = 0; ns < NSUB; ++ns) {
-        const f16x2_t d2 = as_h2(rd[m][ns] | (rd[m][ns] << 16));
-        weight_operands(rb[m][ns], d2, bop[m][ns][0], bop[m][ns][1]);
+        const int wn = wave * WN + ns * 16 + (lane & 15);
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(S + C::OFF_BN + m * C::BN_BYTES + (wn >> 5) * 1024 +
+                                                            ((wn & 31) + 32 * (g >> 1)) * 16 + 8 * (g & 1));
+        const uint32_t d = *reinterpret_cast<const uint16_t*>(S + C::OFF_BS + m * C::BS_BYTES + wn * 4 + 2 * (g >> 1));
+        weight_operands(w, as_h2(d | (d << 16)), bop[m][ns][0], bop[m][ns][1]);
       }
-    gemm_load<AV, NMAT, NSUB>(ra, rb, rd, asrc, nibm, sclm, brow, j + 1 < nks ? j + 1 : j);  // last step reloads itself
-    __syncthreads();
 #pragma unroll
     for (int s = 0; s < RB; ++s)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const f16x8_t av = *reinterpret_cast<const f16x8_t*>(&sA[stage][s * 16 + (lane & 15)][32 * h + 8 * g]);
+        // row s*16 + lane%16 (row & 7 == lane & 7), logical chunk 4h + g
+        const f16x8_t av = *reinterpret_cast<const f16x8_t*>(S + (s * 16 + (lane & 15)) * (2 * KS) +
+                                                             16 * ((4 * h + g) ^ (lane & 7)));
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -272,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int ns = 0; ns < NSUB; ++ns) {
     const int bn = n0 + wave * WN + ns * 16 + (lane & 15);
-    if (!bok[ns]) continue;
+    if (bn >= N) continue;
     if (MODE == 0) {
       const int64_t col = (bn & ~(KS - 1)) + step_pos(bn & (KS - 1));
 #pragma unroll
@@ -280,7 +328,8 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = s * 16 + g * 4 + i;
-          if (r < rows) a.h16[(int64_t)(pos0 + r) * N + col] = (_Float16)(silu(acc[0][ns][s][i]) * acc[NMAT - 1][ns][s][i]);
+          if (r < rows)
+            a.h16[(int64_t)(pos0 + r) * N + col] = (_Float16)(silu(acc[0][ns][s][i]) * acc[NMAT - 1][ns][s][i]);
         }
     } else {
 #pragma unroll
@@ -328,9 +377,8 @@ hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float
   return hipGetLastError();
 }
 int gemm_features_per_tile(int mode, int bm) {
-  const int rb = bm / 16, nmat = mode == 0 ? 2 : 1;
-  const int nsub = 32 / (rb * nmat) < 4 ? 32 / (rb * nmat) : 4;
-  return 4 * 16 * nsub;
+  if (mode == 0) return bm == 64 ? GemmTile<64, 0>::BNW : GemmTile<128, 0>::BNW;
+  return bm == 64 ? GemmTile<64, 1>::BNW : GemmTile<128, 1>::BNW;
 }
 hipError_t launch_grouped_gemm(GemmArgs a, int mode, int bm, int n_tiles, const Launch& l) {
   if (a.K % KS || a.N % KS || n_tiles <= 0 || (bm != 64 && bm != 128) || (mode != 0 && mode != 1))
