@@ -295,11 +295,13 @@ def main():
         "admissions_per_step": round(acc["admissions"] / args.steps, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "gemv_gateup_kernel, hot picks (gate+up+SwiGLU from the HBM pool)",
+                     "kernel": "gemv_route_gateup_kernel, hot picks (routing + slot lookup + gate/up + SwiGLU "
+                               "from the HBM pool; the launch includes the routing)",
                      "avg_launch_us": round(hot_gu_us, 2), "bytes_per_launch": int(hot_gu_bytes)},
         "pcie": {"cold_gateup_GBps": round(cold_rate, 2), "cold_down_GBps": round(cold_dn_rate, 2),
                  "peak": PCIE_PEAK_GBPS, "frac": round(cold_rate / PCIE_PEAK_GBPS, 4),
-                 "kernel": "gemv_gateup_kernel, cold picks (zero-copy reads of pinned host memory)"},
+                 "kernel": "gemv_route_gateup_kernel, cold picks (zero-copy reads of pinned host memory)"},
+        # route is 0 where the routing runs inside the gate/up launches (logits given, E <= 512)
         "per_layer_us": {k_: round(prof[k_ + "_ms"] / fw * 1e3, 2)
                          for k_ in ("route", "hot_gateup", "hot_down", "cold_gateup", "cold_down")},
     }

@@ -1,10 +1,17 @@
-// decode.hip - gfx950 GEMV kernels of the decode path of one MoE layer
-// (routing and the slot-table lookup that tag each pick hot or cold are in
-// route.hip).
+// decode.hip - gfx950 GEMV kernels of the decode path of one MoE layer.
 //
-//   gemv_gateup_kernel    h = silu(W_gate x) * (W_up x) per pick; hot picks
-//                         stream from HBM while cold picks stream over PCIe
-//                         in the same launch.
+//   gemv_route_gateup_kernel
+//                         with logits given (E <= 512): every wave routes its
+//                         token itself (top-k, slot-table lookup) while its
+//                         activation loads are in flight, then runs the
+//                         gate/up GEMV below; one wave per pick applies the
+//                         lookup's side effects (stamp, pick record, count)
+//                         and publishes the pick for the down GEMV. This
+//                         saves the routing launch and the dependent read of
+//                         its output on the decode critical path.
+//   gemv_gateup_kernel    h = silu(W_gate x) * (W_up x) per pick, picks routed
+//                         by route.hip; hot picks stream from HBM while cold
+//                         picks stream over PCIe in the same launch.
 //   gemv_down_combine_kernel
 //                         y_pick = W_down h, then the weighted sum over the
 //                         picks of a token in pick order (+ the old y with
@@ -33,6 +40,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 
@@ -135,6 +143,86 @@ __device__ __forceinline__ bool wanted(uint8_t kind) {
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// routing + lookup + gate/up GEMV + SwiGLU; grid = (row chunks of F, picks).
+// r.policy = 1: wave 0 of work-group x = 0 of each pick applies the pick's
+// side effects (the same as route_kernel's); 0: none (a second launch of the
+// same step, in the timing split).
+template <int LPR, int BPL, int NIT, int MODE>
+__global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, RouteArgs r) {
+  constexpr int NJ = kFusedRouteMaxExperts / 64;
+  constexpr int RPW = 64 / LPR;
+  constexpr int ROWS_WG = 4 * NIT * RPW;
+  const int p = blockIdx.y;
+  const int t = p / a.k, pick = p - t * a.k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lb = lane % LPR, rg = lane / LPR;
+  const int E = r.E;
+
+  // loads that do not depend on the routing: logits, table entries, activations
+  float z[NJ];
+  int32_t tb[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    z[j] = e < E ? r.logits[(int64_t)t * E + e] : 0.f;
+    tb[j] = e < E ? r.tbl[e] : -1;
+  }
+  float xs[BPL][32], sx[BPL];
+  load_slice<LPR, BPL>(a.x + (int64_t)t * a.H, lb, xs, sx);
+
+  uint64_t key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) key[j] = (lane + 64 * j < E) ? route_dev::route_key(z[j], lane + 64 * j) : 0;
+  int my_e;
+  uint64_t my_key;
+  route_dev::wave_topk<NJ>(key, E, a.k, lane, my_e, my_key);
+  const int e = __builtin_amdgcn_readlane(my_e, pick);
+  int slot_l = -1;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) slot_l = j == (e >> 6) ? tb[j] : slot_l;
+  const int slot = __builtin_amdgcn_readlane(slot_l, e & 63);
+  const bool hot = slot >= 0;
+  const uint8_t* base = hot ? r.pool + (int64_t)slot * r.expert_bytes : r.host + (int64_t)e * r.expert_bytes;
+
+  if (r.policy && blockIdx.x == 0 && wave == 0) {
+    const float wl = route_dev::wave_pick_weight(my_key, a.k, lane);
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), pick));
+    if (lane == 0) {
+      const uint32_t clk = r.ctrl->clock + (uint32_t)t;
+      uint64_t rec = ((uint64_t)clk << 32) | ((uint64_t)r.layer << 12) | (uint64_t)e;
+      if (hot) {
+        rec |= kRecordHit;
+        atomicMax(&r.stamps[slot], clk);
+      }
+      r.records[p] = rec;
+      atomicAdd(&r.counts[e], 1u);
+      r.ids[p] = e;
+      r.w[p] = w;
+      r.addr[p] = base;
+      r.kind[p] = hot ? kHot : kCold;
+      if (r.ids_user) r.ids_user[p] = e;
+      if (r.w_user) r.w_user[p] = w;
+      if (p == 0) atomicMax(&r.ctrl->step_tokens, (uint32_t)r.T);
+    }
+  }
+  if (!wanted<MODE>(hot ? kHot : kCold)) return;
+
+  const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
+  RowTile<LPR, BPL, NIT> g, u;
+  g.load(reinterpret_cast<const uint4*>(base + a.lay.gate_nib),
+         reinterpret_cast<const uint16_t*>(base + a.lay.gate_scl), row0, a.F, lb);
+  u.load(reinterpret_cast<const uint4*>(base + a.lay.up_nib), reinterpret_cast<const uint16_t*>(base + a.lay.up_scl),
+         row0, a.F, lb);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const float gv = g.dot(it, xs, sx);
+    const float uv = u.dot(it, xs, sx);
+    const int rr = row0 + it * RPW;
+    if (lb == 0 && rr < a.F) a.out[(int64_t)p * a.F + rr] = silu(gv) * uv;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // gate/up GEMV + SwiGLU for the picks tagged `want`. grid = (row chunks of F,
@@ -263,6 +351,16 @@ hipError_t gateup_t(const GemvArgs& a, const Launch& l, int mode) {
   return launch(gemv_gateup_kernel<LPR, BPL, kNitGateUp, kAll>, grid, dim3(256), l, a);
 }
 template <int LPR, int BPL>
+hipError_t route_gateup_t(const GemvArgs& a, const RouteArgs& r, const Launch& l, int mode) {
+  constexpr int ROWS_WG = 4 * kNitGateUp * (64 / LPR);
+  const dim3 grid((a.F + ROWS_WG - 1) / ROWS_WG, a.T * a.k);
+  if (mode == kOnlyHot)
+    return launch(gemv_route_gateup_kernel<LPR, BPL, kNitGateUp, kOnlyHot>, grid, dim3(256), l, a, r);
+  if (mode == kOnlyCold)
+    return launch(gemv_route_gateup_kernel<LPR, BPL, kNitGateUp, kOnlyCold>, grid, dim3(256), l, a, r);
+  return launch(gemv_route_gateup_kernel<LPR, BPL, kNitGateUp, kAll>, grid, dim3(256), l, a, r);
+}
+template <int LPR, int BPL>
 hipError_t down_pick_t(const GemvArgs& a, const Launch& l, int mode) {
   constexpr int ROWS_WG = 4 * kNitDown * (64 / LPR);
   const dim3 grid((a.H + ROWS_WG - 1) / ROWS_WG, a.T * a.k);
@@ -279,27 +377,27 @@ hipError_t down_combine_t(const GemvArgs& a, const Launch& l, int mode) {
   return launch(gemv_down_combine_kernel<LPR, BPL, kNitCombine, kAll>, grid, dim3(256), l, a);
 }
 
-#define MOE_DISPATCH_GEMV(FN, KB, ARGS, L, MODE)              \
+#define MOE_DISPATCH_GEMV(FN, KB, ARGS, L, MODE, ...)         \
   do {                                                        \
     GemvShape sh;                                             \
     if (!gemv_shape((KB), &sh)) return hipErrorInvalidValue;  \
     switch (sh.lpr * 8 + sh.bpl) {                            \
-      case 8 * 8 + 1: return FN<8, 1>(ARGS, L, MODE);         \
-      case 8 * 8 + 2: return FN<8, 2>(ARGS, L, MODE);         \
-      case 8 * 8 + 3: return FN<8, 3>(ARGS, L, MODE);         \
-      case 8 * 8 + 4: return FN<8, 4>(ARGS, L, MODE);         \
-      case 16 * 8 + 1: return FN<16, 1>(ARGS, L, MODE);       \
-      case 16 * 8 + 2: return FN<16, 2>(ARGS, L, MODE);       \
-      case 16 * 8 + 3: return FN<16, 3>(ARGS, L, MODE);       \
-      case 16 * 8 + 4: return FN<16, 4>(ARGS, L, MODE);       \
-      case 32 * 8 + 1: return FN<32, 1>(ARGS, L, MODE);       \
-      case 32 * 8 + 2: return FN<32, 2>(ARGS, L, MODE);       \
-      case 32 * 8 + 3: return FN<32, 3>(ARGS, L, MODE);       \
-      case 32 * 8 + 4: return FN<32, 4>(ARGS, L, MODE);       \
-      case 64 * 8 + 1: return FN<64, 1>(ARGS, L, MODE);       \
-      case 64 * 8 + 2: return FN<64, 2>(ARGS, L, MODE);       \
-      case 64 * 8 + 3: return FN<64, 3>(ARGS, L, MODE);       \
-      case 64 * 8 + 4: return FN<64, 4>(ARGS, L, MODE);       \
+      case 8 * 8 + 1: return FN<8, 1>(ARGS, ##__VA_ARGS__, L, MODE);         \
+      case 8 * 8 + 2: return FN<8, 2>(ARGS, ##__VA_ARGS__, L, MODE);         \
+      case 8 * 8 + 3: return FN<8, 3>(ARGS, ##__VA_ARGS__, L, MODE);         \
+      case 8 * 8 + 4: return FN<8, 4>(ARGS, ##__VA_ARGS__, L, MODE);         \
+      case 16 * 8 + 1: return FN<16, 1>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 16 * 8 + 2: return FN<16, 2>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 16 * 8 + 3: return FN<16, 3>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 16 * 8 + 4: return FN<16, 4>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 32 * 8 + 1: return FN<32, 1>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 32 * 8 + 2: return FN<32, 2>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 32 * 8 + 3: return FN<32, 3>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 32 * 8 + 4: return FN<32, 4>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 64 * 8 + 1: return FN<64, 1>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 64 * 8 + 2: return FN<64, 2>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 64 * 8 + 3: return FN<64, 3>(ARGS, ##__VA_ARGS__, L, MODE);       \
+      case 64 * 8 + 4: return FN<64, 4>(ARGS, ##__VA_ARGS__, L, MODE);       \
       default: return hipErrorInvalidValue;                   \
     }                                                         \
   } while (0)
@@ -307,6 +405,11 @@ hipError_t down_combine_t(const GemvArgs& a, const Launch& l, int mode) {
 
 hipError_t launch_gemv_gateup(const GemvArgs& a, const Launch& l, int mode) {
   MOE_DISPATCH_GEMV(gateup_t, a.H / 32, a, l, mode);
+}
+hipError_t launch_gemv_route_gateup(const GemvArgs& a, const RouteArgs& r, const Launch& l, int mode) {
+  if (!r.logits || r.E < 1 || r.E > kFusedRouteMaxExperts || a.k < 1 || a.k > 32 || a.k > r.E || a.T < 1)
+    return hipErrorInvalidValue;
+  MOE_DISPATCH_GEMV(route_gateup_t, a.H / 32, a, l, mode, r);
 }
 hipError_t launch_gemv_down_pick(const GemvArgs& a, const Launch& l, int mode) {
   MOE_DISPATCH_GEMV(down_pick_t, a.F / 32, a, l, mode);

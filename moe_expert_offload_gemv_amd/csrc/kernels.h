@@ -79,6 +79,7 @@ struct RouteArgs {
   int32_t* ids_user;     // optional copies for the caller
   float* w_user;
   int32_t policy;        // 1: lookup, stamps, records, counts, step tokens; 0: routing only
+                         // (fused with the gate/up GEMV: 0 = lookup without side effects)
 };
 hipError_t launch_route(const RouteArgs& a, const Launch& l);
 
@@ -104,6 +105,9 @@ struct GemvArgs {
   ExpertLayout lay;
 };
 hipError_t launch_gemv_gateup(const GemvArgs& a, const Launch& l, int mode);
+// routing fused into the gate/up GEMV: needs logits and E <= kFusedRouteMaxExperts
+constexpr int kFusedRouteMaxExperts = 512;
+hipError_t launch_gemv_route_gateup(const GemvArgs& a, const RouteArgs& r, const Launch& l, int mode);
 hipError_t launch_gemv_down_pick(const GemvArgs& a, const Launch& l, int mode);
 hipError_t launch_gemv_down_combine(const GemvArgs& a, const Launch& l, int mode);
 

@@ -283,6 +283,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
     c->events.push_back(ev);
   }
   c->timed_tokens.assign(n_timed, 0);
+  c->timed_fused.assign(n_timed, 0);
   for (int i = 0; i < 4 && k.max_prefill_tokens > 0; ++i) {
     hipEvent_t ev;
     if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return fail(MOE_E_HIP);
@@ -421,7 +422,11 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   ra.ids = c->d_ids, ra.w = c->d_w, ra.addr = c->d_addr, ra.kind = c->d_kind;
   ra.ids_user = ids, ra.w_user = w;
   ra.policy = 1;
-  HIP_TRY(c, moe::launch_route(ra, on(A, kRoute)));
+  // with logits at hand the gate/up GEMV routes by itself (one launch less on
+  // the critical path); a router chain runs in its own launch first
+  const bool fused = logits && c->E <= moe::kFusedRouteMaxExperts;
+  if (ev) c->timed_fused[c->timed_pending - 1] = fused ? 1 : 0;
+  if (!fused) HIP_TRY(c, moe::launch_route(ra, on(A, kRoute)));
 
   moe::GemvArgs ga{};
   ga.x = x;
@@ -438,12 +443,24 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   dn.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
   if (!ev) {
     // hot picks stream from HBM while cold picks stream over PCIe, in one launch
-    HIP_TRY(c, moe::launch_gemv_gateup(ga, on(A, 0), moe::kAll));
+    if (fused)
+      HIP_TRY(c, moe::launch_gemv_route_gateup(ga, ra, on(A, 0), moe::kAll));
+    else
+      HIP_TRY(c, moe::launch_gemv_gateup(ga, on(A, 0), moe::kAll));
     HIP_TRY(c, moe::launch_gemv_down_combine(dn, on(A, 0), moe::kAll));
   } else {
-    // timing: the same work split by tag, one launch each, in stream order
-    HIP_TRY(c, moe::launch_gemv_gateup(ga, on(A, kColdGateUp), moe::kOnlyCold));
-    HIP_TRY(c, moe::launch_gemv_gateup(ga, on(A, kHotGateUp), moe::kOnlyHot));
+    // timing: the same work split by tag, one launch each, in stream order;
+    // fused, both gate/up launches route and only the hot one applies the
+    // side effects, and there is no routing interval
+    if (fused) {
+      moe::RouteArgs quiet = ra;
+      quiet.policy = 0;
+      HIP_TRY(c, moe::launch_gemv_route_gateup(ga, quiet, on(A, kColdGateUp), moe::kOnlyCold));
+      HIP_TRY(c, moe::launch_gemv_route_gateup(ga, ra, on(A, kHotGateUp), moe::kOnlyHot));
+    } else {
+      HIP_TRY(c, moe::launch_gemv_gateup(ga, on(A, kColdGateUp), moe::kOnlyCold));
+      HIP_TRY(c, moe::launch_gemv_gateup(ga, on(A, kHotGateUp), moe::kOnlyHot));
+    }
     HIP_TRY(c, moe::launch_gemv_down_pick(dn, on(A, kHotDown), moe::kOnlyHot));
     HIP_TRY(c, moe::launch_gemv_down_combine(dn, on(A, kColdDownCombine), moe::kOnlyCold));
   }
@@ -454,9 +471,12 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
 static int flush_profile(moe_ctx* c) {
   for (int32_t i = 0; i < c->timed_pending; ++i) {
     float t[kTimedKernels];
-    for (int j = 0; j < kTimedKernels; ++j)
+    for (int j = 0; j < kTimedKernels; ++j) {
+      t[j] = 0.f;
+      if (j == kRoute && c->timed_fused[i]) continue;
       HIP_TRY(c, hipEventElapsedTime(&t[j], c->events[2 * (kTimedKernels * (size_t)i + j)],
                                      c->events[2 * (kTimedKernels * (size_t)i + j) + 1]));
+    }
     c->prof.forwards += 1;
     c->prof.route_ms += t[kRoute];
     c->prof.hot_gateup_ms += t[kHotGateUp];

@@ -69,6 +69,7 @@ struct moe_ctx {
   bool profiling = false;
   std::vector<hipEvent_t> events;      // start/stop per kernel per timed forward
   std::vector<int32_t> timed_tokens;   // n_tokens of each pending timed forward
+  std::vector<uint8_t> timed_fused;    // 1: its routing ran inside the gate/up GEMV (no routing interval)
   int32_t timed_pending = 0;
   moe_profile_stats prof{};
 
