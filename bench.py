@@ -293,6 +293,9 @@ def main():
         "cold_GBps_over_step": round(acc["cold_bytes"] / elapsed / 1e9, 2),
         "hit_rate": round(acc["hits"] / max(acc["hits"] + acc["misses"], 1), 4),
         "admissions_per_step": round(acc["admissions"] / args.steps, 3),
+        # promotions copied from the HBM capture of their cold reads vs from pinned memory (PCIe)
+        "promotion_GB": round(acc["copied_bytes"] / 1e9, 3),
+        "promotion_GB_over_pcie": round(acc["copied_pcie_bytes"] / 1e9, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "gemv_route_gateup_kernel, hot picks (routing + slot lookup + gate/up + SwiGLU "

@@ -97,6 +97,17 @@ typedef struct {
                               (their HBM pools stay separate). Bounds the
                               pinned arena where host memory is short.       */
   void*   stream;          /* hipStream_t to issue on; NULL: the null stream  */
+  int32_t capture_picks;   /* 0..max_batch_tokens*top_k (0: off). A cold pick
+                              p < capture_picks of a layer (p = token * k +
+                              pick) also writes the weight bytes it reads over
+                              PCIe into an HBM capture block (L * capture_picks
+                              blocks of expert_bytes, allocated before the
+                              pool). When the cache step admits that expert,
+                              the promotion copies from the capture block
+                              (HBM to HBM) instead of from pinned memory.
+                              Same bytes, same decisions; applies to forwards
+                              that route inside the gate/up GEMV (logits
+                              given, E <= 512), others copy from pinned.     */
 } moe_config;
 
 typedef struct {
@@ -118,7 +129,9 @@ typedef struct {
   int64_t evictions;          /* resident experts displaced by admissions     */
   int64_t hot_bytes;          /* expert bytes read from HBM by the step       */
   int64_t cold_bytes;         /* expert bytes read over PCIe by the step      */
-  int64_t copied_bytes;       /* host->HBM promotion copies issued            */
+  int64_t copied_bytes;       /* promotion copies into pool slots issued      */
+  int64_t copied_pcie_bytes;  /* the part copied from pinned host memory (the
+                                 rest came from capture blocks in HBM)        */
 } moe_step_stats;
 
 typedef struct {
@@ -215,7 +228,9 @@ MOE_API int moe_prefill(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
  * admitted expert takes the lowest free slot, else the slot with the smallest
  * stamp (ties: highest slot index), whose expert is evicted and forgets its
  * last miss; the new slot's stamp is t, and the expert forgets its last miss.
- * Weights are copied pinned -> slot on the stream, tables, stamps and the
+ * Weights are copied into the slot on the stream (from the expert's capture
+ * block when a cold read of this step captured it, see capture_picks; else
+ * from pinned memory), tables, stamps and the
  * clock (advanced by the step's token count) are uploaded, and the log is
  * cleared. out may be NULL. MOE_E_CAPTURING if the stream is capturing. */
 MOE_API int moe_cache_step(moe_ctx* ctx, moe_step_stats* out);

@@ -41,7 +41,7 @@ class moe_config(C.Structure):
         ("ffn", C.c_int32), ("quant", C.c_int32), ("pool_budget_bytes", C.c_int64), ("reserve_bytes", C.c_int64),
         ("window_tokens", C.c_int32), ("admit_misses", C.c_int32), ("max_batch_tokens", C.c_int32),
         ("max_prefill_tokens", C.c_int32), ("device", C.c_int32), ("host_alloc", C.c_int32),
-        ("host_sets", C.c_int32), ("stream", C.c_void_p),
+        ("host_sets", C.c_int32), ("stream", C.c_void_p), ("capture_picks", C.c_int32),
     ]
 
 
@@ -52,7 +52,7 @@ class moe_info(C.Structure):
 
 class moe_step_stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("step", "tokens", "hits", "misses", "admissions", "evictions",
-                                        "hot_bytes", "cold_bytes", "copied_bytes")]
+                                        "hot_bytes", "cold_bytes", "copied_bytes", "copied_pcie_bytes")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -140,12 +140,15 @@ def moe_expert_bytes(hidden: int, ffn: int) -> int:
 
 def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reserve_bytes=0, window_tokens=64,
                admit_misses=2, max_batch_tokens=64, max_prefill_tokens=0, device=0, host_alloc=MOE_HOST_COHERENT,
-               host_sets=0, stream=None):
+               host_sets=0, stream=None, capture_picks=None):
     """Returns an opaque context handle.
 
     stream: a torch.cuda.Stream, a raw hipStream_t int, or None for torch's
     current stream on the device (0, the null stream, is a valid handle).
+    capture_picks: None for top_k (one token's picks per layer), 0 for off.
     """
+    if capture_picks is None:
+        capture_picks = top_k
     if stream is None:
         stream = 0
         try:
@@ -159,7 +162,7 @@ def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reser
         stream = stream.cuda_stream
     cfg = moe_config(n_layers, n_experts, top_k, hidden, ffn, MOE_Q4_32_F16, pool_budget_bytes, reserve_bytes,
                      window_tokens, admit_misses, max_batch_tokens, max_prefill_tokens, device, host_alloc,
-                     host_sets, stream)
+                     host_sets, stream, capture_picks)
     out = C.c_void_p()
     rc = lib().moe_create(C.byref(cfg), C.byref(out))
     if rc != MOE_OK:

@@ -9,6 +9,11 @@
 //                         and publishes the pick for the down GEMV. This
 //                         saves the routing launch and the dependent read of
 //                         its output on the decode critical path.
+//                         Cold picks p < capture_picks also write the bytes
+//                         they read over PCIe into the layer's capture block
+//                         p (the down GEMV adds the down matrix), so a
+//                         promotion of that expert at the cache step is an
+//                         HBM-to-HBM copy instead of a second PCIe transfer.
 //   gemv_gateup_kernel    h = silu(W_gate x) * (W_up x) per pick, picks routed
 //                         by route.hip; hot picks stream from HBM while cold
 //                         picks stream over PCIe in the same launch.
@@ -127,6 +132,23 @@ struct RowTile {
       }
     }
   }
+  // the same bytes, written at the same place of another copy of the matrix
+  __device__ __forceinline__ void store(uint4* __restrict__ nib, uint16_t* __restrict__ scl, int row0, int nrows,
+                                        int lb) const {
+    constexpr int RPW = 64 / LPR;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int r = row0 + it * RPW;
+#pragma unroll
+      for (int j = 0; j < BPL; ++j) {
+        if (r < nrows) {
+          const int64_t idx = (int64_t)r * (LPR * BPL) + lb + LPR * j;
+          nib[idx] = q[it][j];
+          scl[idx] = (uint16_t)d[it][j];
+        }
+      }
+    }
+  }
   __device__ __forceinline__ float dot(int it, const float (&xs)[BPL][32], const float (&sx)[BPL]) const {
     float acc = 0.f;
 #pragma unroll
@@ -202,6 +224,7 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
       r.w[p] = w;
       r.addr[p] = base;
       r.kind[p] = hot ? kHot : kCold;
+      if (!hot && p < r.capture_picks) r.cap_tag[p] = clk;
       if (r.ids_user) r.ids_user[p] = e;
       if (r.w_user) r.w_user[p] = w;
       if (p == 0) atomicMax(&r.ctrl->step_tokens, (uint32_t)r.T);
@@ -215,6 +238,13 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
          reinterpret_cast<const uint16_t*>(base + a.lay.gate_scl), row0, a.F, lb);
   u.load(reinterpret_cast<const uint4*>(base + a.lay.up_nib), reinterpret_cast<const uint16_t*>(base + a.lay.up_scl),
          row0, a.F, lb);
+  if (!hot && p < a.capture_picks) {
+    uint8_t* cap = a.capture + (int64_t)p * a.lay.bytes;
+    g.store(reinterpret_cast<uint4*>(cap + a.lay.gate_nib), reinterpret_cast<uint16_t*>(cap + a.lay.gate_scl), row0,
+            a.F, lb);
+    u.store(reinterpret_cast<uint4*>(cap + a.lay.up_nib), reinterpret_cast<uint16_t*>(cap + a.lay.up_scl), row0, a.F,
+            lb);
+  }
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const float gv = g.dot(it, xs, sx);
@@ -300,6 +330,11 @@ __global__ __launch_bounds__(256) void gemv_down_combine_kernel(GemvArgs a) {
     RowTile<LPR, BPL, NIT> d;
     d.load(reinterpret_cast<const uint4*>(base + a.lay.down_nib),
            reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0 + rg, a.H, lb);
+    if (a.kind[p] == kCold && p < a.capture_picks) {
+      uint8_t* cap = a.capture + p * a.lay.bytes;
+      d.store(reinterpret_cast<uint4*>(cap + a.lay.down_nib), reinterpret_cast<uint16_t*>(cap + a.lay.down_scl),
+              row0 + rg, a.H, lb);
+    }
     float hs[BPL][32], sh[BPL];
     load_slice<LPR, BPL>(a.x + p * a.F, lb, hs, sh);
 #pragma unroll

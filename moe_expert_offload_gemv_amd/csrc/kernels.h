@@ -80,6 +80,8 @@ struct RouteArgs {
   float* w_user;
   int32_t policy;        // 1: lookup, stamps, records, counts, step tokens; 0: routing only
                          // (fused with the gate/up GEMV: 0 = lookup without side effects)
+  uint32_t* cap_tag;     // [T][k] fused: clock of a cold pick whose bytes the step captured
+  int32_t capture_picks; // picks p < capture_picks of a layer capture their cold reads
 };
 hipError_t launch_route(const RouteArgs& a, const Launch& l);
 
@@ -103,6 +105,8 @@ struct GemvArgs {
   int32_t T, k, H, F;
   int32_t accumulate;           // combine: y += result
   ExpertLayout lay;
+  uint8_t* capture;             // layer's capture blocks: a cold pick p < capture_picks writes the
+  int32_t capture_picks;        //   weight bytes it reads into block p (same layout as a slot)
 };
 hipError_t launch_gemv_gateup(const GemvArgs& a, const Launch& l, int mode);
 // routing fused into the gate/up GEMV: needs logits and E <= kFusedRouteMaxExperts

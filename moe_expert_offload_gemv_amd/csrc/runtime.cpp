@@ -164,6 +164,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
       k.top_k > k.n_experts || k.hidden < 32 || k.ffn < 32 || k.hidden % 32 || k.ffn % 32 ||
       k.quant != MOE_Q4_32_F16 || k.window_tokens < 1 || (k.admit_misses != 1 && k.admit_misses != 2) ||
       k.max_batch_tokens < 1 || k.max_batch_tokens > 256 || k.max_prefill_tokens < 0 || k.n_layers > (1 << 20) ||
+      k.capture_picks < 0 || k.capture_picks > k.max_batch_tokens * k.top_k ||
       (k.host_alloc != MOE_HOST_COHERENT && k.host_alloc != MOE_HOST_NONCOHERENT))
     return g_create_error = "config field out of range", MOE_E_INVAL;
   moe::GemvShape s1, s2;
@@ -208,6 +209,13 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_h, sizeof(float) * P * c->F, "h"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_kind, P, "pick tags"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ypick, sizeof(float) * P * c->H, "pick outputs"))) return fail(rc);
+  c->capture_picks = k.capture_picks;
+  if (c->capture_picks > 0) {
+    if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_capture, (size_t)(L * c->capture_picks * c->B), "capture blocks")))
+      return fail(rc);
+    if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_cap_tag, sizeof(uint32_t) * L * c->rec_stride, "capture tags")))
+      return fail(rc);
+  }
   if ((rc = moe_prefill_alloc(c))) return fail(rc);
 
   // pinned host staging for the small transfers of the cache step
@@ -217,6 +225,9 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
                                "record staging")))
     return fail(rc);
   if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_tbl, sizeof(int32_t) * L * E, pin, "table staging")))
+    return fail(rc);
+  if (c->capture_picks > 0 &&
+      (rc = moe_ctx_host_alloc(c, (void**)&c->h_cap_tag, sizeof(uint32_t) * L * c->rec_stride, pin, "tag staging")))
     return fail(rc);
 
   // HBM pool: S slots per layer
@@ -265,6 +276,9 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->owner.assign(L * std::max<int64_t>(S, 1), -1);
   c->stamps.assign(L * std::max<int64_t>(S, 1), 0);
   c->last_miss.assign(L * E, 0);
+  c->cap_of.assign(L * E, -1);
+  if (c->d_cap_tag && hipMemset(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride) != hipSuccess)
+    return fail(MOE_E_HIP);
   if (hipMemset(c->d_tbl, 0xff, sizeof(int32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_counts, 0, sizeof(uint32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride) != hipSuccess) return fail(MOE_E_HIP);
@@ -362,6 +376,7 @@ extern "C" int moe_seed(moe_ctx* c, const uint32_t* freq) {
   HIP_TRY(c, hipMemsetAsync(c->d_stamps, 0, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), c->stream));
   HIP_TRY(c, hipMemsetAsync(c->d_counts, 0, sizeof(uint32_t) * L * E, c->stream));
   HIP_TRY(c, hipMemsetAsync(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride, c->stream));
+  if (c->d_cap_tag) HIP_TRY(c, hipMemsetAsync(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride, c->stream));
   *c->h_ctrl = Ctrl{1, 0, {0, 0}};
   HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
@@ -422,6 +437,8 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   ra.ids = c->d_ids, ra.w = c->d_w, ra.addr = c->d_addr, ra.kind = c->d_kind;
   ra.ids_user = ids, ra.w_user = w;
   ra.policy = 1;
+  ra.capture_picks = c->capture_picks;
+  ra.cap_tag = c->d_cap_tag ? c->d_cap_tag + (int64_t)layer * c->rec_stride : nullptr;
   // with logits at hand the gate/up GEMV routes by itself (one launch less on
   // the critical path); a router chain runs in its own launch first
   const bool fused = logits && c->E <= moe::kFusedRouteMaxExperts;
@@ -437,6 +454,8 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   ga.ypick = c->d_ypick;
   ga.T = n_tokens, ga.k = c->k, ga.H = c->H, ga.F = c->F;
   ga.lay = c->lay;
+  ga.capture_picks = c->capture_picks;
+  ga.capture = c->d_capture ? c->d_capture + (int64_t)layer * c->capture_picks * c->B : nullptr;
   moe::GemvArgs dn = ga;
   dn.x = c->d_h;
   dn.out = y;
@@ -511,6 +530,11 @@ extern "C" int moe_profile(moe_ctx* c, int32_t enable, moe_profile_stats* out) {
 // ---------------------------------------------------------------------------
 // the between-step cache policy
 
+static void forget_captures(moe_ctx* c) {
+  for (int64_t te : c->cap_touched) c->cap_of[te] = -1;
+  c->cap_touched.clear();
+}
+
 extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
   if (!c) return MOE_E_INVAL;
   if (!c->seeded) return moe_ctx_fail(c, MOE_E_STATE, "cache_step before moe_seed");
@@ -524,21 +548,34 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
                             c->stream));
   if (S > 0)
     HIP_TRY(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * L * S, hipMemcpyDeviceToHost, c->stream));
+  if (c->d_cap_tag)
+    HIP_TRY(c, hipMemcpyAsync(c->h_cap_tag, c->d_cap_tag, sizeof(uint32_t) * L * c->rec_stride, hipMemcpyDeviceToHost,
+                              c->stream));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   const Ctrl st = *c->h_ctrl;
   if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * L * S);
   // records of this step carry clocks in [clock, clock + step tokens); older ones are stale
   int64_t hits = 0;
   c->last_log.clear();
+  forget_captures(c);  // left over if an earlier step stopped on an error
   const uint64_t t_lo = (uint64_t)c->clock, t_hi = (uint64_t)c->clock + st.step_tokens;
   for (int64_t i = 0; i < L * c->rec_stride; ++i) {
     const uint64_t r = c->h_records[i];
     const uint64_t t = r >> 32;
     if (t < t_lo || t >= t_hi) continue;
-    if (r & moe::kRecordHit)
+    if (r & moe::kRecordHit) {
       ++hits;
-    else
-      c->last_log.push_back(r);
+      continue;
+    }
+    c->last_log.push_back(r);
+    // a cold pick p < capture_picks whose tag carries its clock left the
+    // expert's bytes in capture block p of its layer
+    const int64_t p = i % c->rec_stride;
+    const int64_t e = (int64_t)(r & 0xfff);
+    if (p < c->capture_picks && c->h_cap_tag[i] == (uint32_t)t && e < E) {
+      const int64_t te = (i / c->rec_stride) * E + e;
+      if (c->cap_of[te] < 0) c->cap_of[te] = (int32_t)p, c->cap_touched.push_back(te);
+    }
   }
   const int64_t misses = (int64_t)c->last_log.size();
   if (c->profiling) {
@@ -552,7 +589,7 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
   // canonical order: ascending 64-bit entries (clock, then layer, then expert)
   std::sort(c->last_log.begin(), c->last_log.end());
 
-  int64_t admissions = 0, evictions = 0;
+  int64_t admissions = 0, evictions = 0, copied_pcie = 0;
   for (uint64_t entry : c->last_log) {
     const uint32_t t = (uint32_t)(entry >> 32);
     const int64_t l = (int64_t)((entry >> 12) & 0x7ffff);
@@ -590,9 +627,16 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     c->stamps[l * S + v] = t;
     c->last_miss[te] = 0;
     ++admissions;
-    HIP_TRY(c, hipMemcpyAsync(c->pool + (l * S + v) * B, c->host_layers[l] + e * B, B, hipMemcpyHostToDevice,
-                              c->stream));
+    uint8_t* dst = c->pool + (l * S + v) * B;
+    if (c->cap_of[te] >= 0) {
+      HIP_TRY(c, hipMemcpyAsync(dst, c->d_capture + (l * c->capture_picks + c->cap_of[te]) * B, B,
+                                hipMemcpyDeviceToDevice, c->stream));
+    } else {
+      HIP_TRY(c, hipMemcpyAsync(dst, c->host_layers[l] + e * B, B, hipMemcpyHostToDevice, c->stream));
+      ++copied_pcie;
+    }
   }
+  forget_captures(c);
   if (admissions > 0) {
     std::memcpy(c->h_tbl, c->tbl.data(), sizeof(int32_t) * L * E);
     HIP_TRY(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * L * E, hipMemcpyHostToDevice, c->stream));
@@ -614,6 +658,7 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     out->hot_bytes = hits * B;
     out->cold_bytes = misses * B;
     out->copied_bytes = admissions * B;
+    out->copied_pcie_bytes = copied_pcie * B;
   }
   c->steps += 1;
   return MOE_OK;

@@ -38,6 +38,9 @@ struct moe_ctx {
   float* d_h = nullptr;                // [max_batch*k][F]
   uint8_t* d_kind = nullptr;           // [max_batch*k] hot / cold tag
   float* d_ypick = nullptr;            // [max_batch*k][H] down output of hot picks
+  int32_t capture_picks = 0;           // picks per layer whose cold reads are captured
+  uint8_t* d_capture = nullptr;        // [L][capture_picks] expert blocks
+  uint32_t* d_cap_tag = nullptr;       // [L][rec_stride] clock of a captured cold pick
   std::vector<void*> routers;          // per layer fp32 [E][H] or null
 
   // pinned host memory (host_sets distinct sets; layer l uses set l % host_sets)
@@ -46,6 +49,7 @@ struct moe_ctx {
   std::vector<uint8_t*> host_layers_dev;  // device addresses of the same
   moe::Ctrl* h_ctrl = nullptr;
   uint64_t* h_records = nullptr;
+  uint32_t* h_cap_tag = nullptr;
   int32_t* h_tbl = nullptr;
   uint32_t* h_stamps = nullptr;
 
@@ -60,6 +64,8 @@ struct moe_ctx {
   std::vector<int32_t> tbl, owner;
   std::vector<uint32_t> stamps, last_miss;
   std::vector<uint64_t> last_log;
+  std::vector<int32_t> cap_of;         // [L][E] captured pick of the expert in the step, or -1
+  std::vector<int64_t> cap_touched;    // entries of cap_of set in the step
   std::vector<char> registered;        // per host set
   bool seeded = false;
   int64_t clock = 1;

@@ -27,7 +27,8 @@ class Decode:
     """
 
     def __init__(self, wl: Workload, slots: int | None = None, seed=True, max_batch: int | None = None,
-                 host_alloc: int = moe.MOE_HOST_COHERENT, stream=None, max_prefill: int = 0, keep_weights=True):
+                 host_alloc: int = moe.MOE_HOST_COHERENT, stream=None, max_prefill: int = 0, keep_weights=True,
+                 capture_picks=None):
         import torch
 
         self.wl = wl
@@ -38,7 +39,7 @@ class Decode:
                                   pool_budget_bytes=wl.n_layers * self.S * self.B, window_tokens=wl.window,
                                   admit_misses=wl.admit_misses, max_batch_tokens=max_batch or max(wl.tokens, 1),
                                   max_prefill_tokens=max_prefill, host_alloc=host_alloc,
-                                  host_sets=wl.distinct_layers, stream=self.stream)
+                                  host_sets=wl.distinct_layers, stream=self.stream, capture_picks=capture_picks)
         info = moe.moe_get_info(self.ctx)
         assert info["slots_per_layer"] == self.S, info
         self.weights = {}

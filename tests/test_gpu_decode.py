@@ -34,8 +34,9 @@ def _compare_policy(d: Decode, pol, st_gpu, st_orc, layers):
     assert np.array_equal(moe.moe_get_miss_log(d.ctx), pol.last_log())
 
 
-def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_alloc=moe.MOE_HOST_COHERENT):
-    d = Decode(wl, slots=slots, seed=seed, host_alloc=host_alloc)
+def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_alloc=moe.MOE_HOST_COHERENT,
+                capture_picks=None, copies=None):
+    d = Decode(wl, slots=slots, seed=seed, host_alloc=host_alloc, capture_picks=capture_picks)
     pol = oracle_policy(wl, slots, seed=seed)
     logits = zipf_logits(wl)
     L, T, k, H = wl.n_layers, wl.tokens, wl.top_k, wl.hidden
@@ -64,6 +65,10 @@ def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_allo
         st_g = moe.moe_cache_step(d.ctx)
         st_o = pol.step()
         _compare_policy(d, pol, st_g, st_o, range(L))
+        assert 0 <= st_g["copied_pcie_bytes"] <= st_g["copied_bytes"] == st_o["admissions"] * d.B
+        if copies is not None:
+            copies["copied"] = copies.get("copied", 0) + st_g["copied_bytes"]
+            copies["pcie"] = copies.get("pcie", 0) + st_g["copied_pcie_bytes"]
     assert np.array_equal(moe.moe_get_counts(d.ctx, L, wl.n_experts), pol.counts())
     d.close()
     return worst
@@ -101,8 +106,24 @@ REDUCED = Workload("decode-e64k8-h2048f1024-l4-b1-rot16", 101, 4, 64, 8, 2048, 1
 
 
 def test_decode_reduced_layers_bit_exact_policy():
-    worst = _run_decode(REDUCED, slots=26, check_every=8)
-    print("worst token error", worst)
+    copies = {}
+    worst = _run_decode(REDUCED, slots=26, check_every=8, copies=copies)
+    print("worst token error", worst, "promotion bytes", copies)
+    # batch 1 with logits: every cold pick captured its bytes, so no promotion
+    # crossed PCIe a second time
+    assert copies["copied"] > 0 and copies["pcie"] == 0
+
+
+@pytest.mark.parametrize("capture_picks", [None, 0])
+def test_promotions_every_miss_checked_every_step(capture_picks):
+    # admit on the first miss: every step promotes, and every step's outputs
+    # are checked, so an expert copied from its capture block (or from pinned
+    # memory with capture off) is read from its new slot right away
+    wl = REDUCED.with_(name="decode-e64k8-h2048f1024-l4-b1-admit1", steps=10, admit_misses=1)
+    copies = {}
+    _run_decode(wl, slots=26, check_every=1, capture_picks=capture_picks, copies=copies)
+    assert copies["copied"] > 0
+    assert copies["pcie"] == (0 if capture_picks is None else copies["copied"]), copies
 
 
 def test_decode_batch_of_five_tokens():
@@ -270,9 +291,20 @@ def test_kernel_timing_hook():
     assert prof["forwards"] == 3 * wl.steps
     assert prof["hot_picks"] == tot["hits"] and prof["cold_picks"] == tot["misses"]
     assert tot["hits"] + tot["misses"] == wl.steps * 3 * 2 * 8
-    for key in ("route_ms", "hot_gateup_ms", "hot_down_ms", "cold_gateup_ms", "cold_down_ms"):
+    for key in ("hot_gateup_ms", "hot_down_ms", "cold_gateup_ms", "cold_down_ms"):
         assert prof[key] > 0, key
+    assert prof["route_ms"] == 0  # with logits the gate/up launches route by themselves
     assert prof["gateup_bytes_per_pick"] + prof["down_bytes_per_pick"] == wl.expert_bytes
+    # a router chain runs (and is timed) in its own launch
+    tiny = WORKLOADS["tiny-e8k2-h256f512-t4"]
+    dt = Decode(tiny)
+    moe.moe_register_router(dt.ctx, 0, router_weights(tiny, 0))
+    moe.moe_profile(dt.ctx, 1)
+    yt = torch.empty((4, 256), dtype=torch.float32, device="cuda")
+    moe.moe_forward(dt.ctx, 0, 4, _dev(activations(tiny, 0)), None, yt)
+    moe.moe_cache_step(dt.ctx)
+    assert moe.moe_profile(dt.ctx, 0)["route_ms"] > 0
+    dt.close()
     # timing on: the forward refuses graph capture
     s = torch.cuda.Stream()
     d2 = Decode(wl, stream=s)
