@@ -99,8 +99,10 @@ typedef struct {
   void*   stream;          /* hipStream_t to issue on; NULL: the null stream  */
   int32_t capture_picks;   /* 0..max_batch_tokens*top_k (0: off). A cold pick
                               p < capture_picks of a layer (p = token * k +
-                              pick) also writes the weight bytes it reads over
-                              PCIe into an HBM capture block (L * capture_picks
+                              pick) that the cache step will admit (judged
+                              from the last-miss clocks the step began with)
+                              also writes the weight bytes it reads over PCIe
+                              into an HBM capture block (L * capture_picks
                               blocks of expert_bytes, allocated before the
                               pool). When the cache step admits that expert,
                               the promotion copies from the capture block

@@ -9,11 +9,13 @@
 //                         and publishes the pick for the down GEMV. This
 //                         saves the routing launch and the dependent read of
 //                         its output on the decode critical path.
-//                         Cold picks p < capture_picks also write the bytes
-//                         they read over PCIe into the layer's capture block
-//                         p (the down GEMV adds the down matrix), so a
-//                         promotion of that expert at the cache step is an
-//                         HBM-to-HBM copy instead of a second PCIe transfer.
+//                         A cold pick p < capture_picks that the cache step
+//                         will admit (its previous miss lies inside the
+//                         window, from the last-miss clocks the step began
+//                         with) also writes the bytes it reads over PCIe into
+//                         the layer's capture block p (the down GEMV adds the
+//                         down matrix), so its promotion is an HBM-to-HBM copy
+//                         instead of a second PCIe transfer.
 //   gemv_gateup_kernel    h = silu(W_gate x) * (W_up x) per pick, picks routed
 //                         by route.hip; hot picks stream from HBM while cold
 //                         picks stream over PCIe in the same launch.
@@ -161,7 +163,7 @@ struct RowTile {
 // which picks a launch computes: every pick, or only the hot / cold ones
 template <int MODE>
 __device__ __forceinline__ bool wanted(uint8_t kind) {
-  return MODE == kAll || (MODE == kOnlyHot && kind == kHot) || (MODE == kOnlyCold && kind == kCold);
+  return MODE == kAll || (MODE == kOnlyHot && (kind & kCold) == 0) || (MODE == kOnlyCold && (kind & kCold) != 0);
 }
 
 }  // namespace
@@ -185,12 +187,16 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
   // loads that do not depend on the routing: logits, table entries, activations
   float z[NJ];
   int32_t tb[NJ];
+  uint32_t lm[NJ];
+  const bool may_capture = p < r.capture_picks;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
     z[j] = e < E ? r.logits[(int64_t)t * E + e] : 0.f;
     tb[j] = e < E ? r.tbl[e] : -1;
+    lm[j] = (may_capture && e < E) ? r.last_miss[e] : 0u;
   }
+  const uint32_t clk = r.ctrl->clock + (uint32_t)t;
   float xs[BPL][32], sx[BPL];
   load_slice<LPR, BPL>(a.x + (int64_t)t * a.H, lb, xs, sx);
 
@@ -202,17 +208,25 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
   route_dev::wave_topk<NJ>(key, E, a.k, lane, my_e, my_key);
   const int e = __builtin_amdgcn_readlane(my_e, pick);
   int slot_l = -1;
+  uint32_t lm_l = 0;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) slot_l = j == (e >> 6) ? tb[j] : slot_l;
+  for (int j = 0; j < NJ; ++j) {
+    slot_l = j == (e >> 6) ? tb[j] : slot_l;
+    lm_l = j == (e >> 6) ? lm[j] : lm_l;
+  }
   const int slot = __builtin_amdgcn_readlane(slot_l, e & 63);
+  const uint32_t prev = (uint32_t)__builtin_amdgcn_readlane((int)lm_l, e & 63);
   const bool hot = slot >= 0;
+  // the cache step admits a cold pick on its first miss, or on a repeat
+  // inside the window (a repeat earlier in this same step is not seen here)
+  const bool capture = !hot && may_capture && r.S > 0 &&
+                       (r.admit_misses == 1 || (prev != 0 && clk - prev < (uint32_t)r.window));
   const uint8_t* base = hot ? r.pool + (int64_t)slot * r.expert_bytes : r.host + (int64_t)e * r.expert_bytes;
 
   if (r.policy && blockIdx.x == 0 && wave == 0) {
     const float wl = route_dev::wave_pick_weight(my_key, a.k, lane);
     const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), pick));
     if (lane == 0) {
-      const uint32_t clk = r.ctrl->clock + (uint32_t)t;
       uint64_t rec = ((uint64_t)clk << 32) | ((uint64_t)r.layer << 12) | (uint64_t)e;
       if (hot) {
         rec |= kRecordHit;
@@ -223,8 +237,8 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
       r.ids[p] = e;
       r.w[p] = w;
       r.addr[p] = base;
-      r.kind[p] = hot ? kHot : kCold;
-      if (!hot && p < r.capture_picks) r.cap_tag[p] = clk;
+      r.kind[p] = hot ? kHot : (capture ? (uint8_t)(kCold | kCaptured) : kCold);
+      if (capture) r.cap_tag[p] = clk;
       if (r.ids_user) r.ids_user[p] = e;
       if (r.w_user) r.w_user[p] = w;
       if (p == 0) atomicMax(&r.ctrl->step_tokens, (uint32_t)r.T);
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
          reinterpret_cast<const uint16_t*>(base + a.lay.gate_scl), row0, a.F, lb);
   u.load(reinterpret_cast<const uint4*>(base + a.lay.up_nib), reinterpret_cast<const uint16_t*>(base + a.lay.up_scl),
          row0, a.F, lb);
-  if (!hot && p < a.capture_picks) {
+  if (capture) {
     uint8_t* cap = a.capture + (int64_t)p * a.lay.bytes;
     g.store(reinterpret_cast<uint4*>(cap + a.lay.gate_nib), reinterpret_cast<uint16_t*>(cap + a.lay.gate_scl), row0,
             a.F, lb);
@@ -330,7 +344,7 @@ __global__ __launch_bounds__(256) void gemv_down_combine_kernel(GemvArgs a) {
     RowTile<LPR, BPL, NIT> d;
     d.load(reinterpret_cast<const uint4*>(base + a.lay.down_nib),
            reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0 + rg, a.H, lb);
-    if (a.kind[p] == kCold && p < a.capture_picks) {
+    if ((a.kind[p] & kCaptured) && p < a.capture_picks) {
       uint8_t* cap = a.capture + p * a.lay.bytes;
       d.store(reinterpret_cast<uint4*>(cap + a.lay.down_nib), reinterpret_cast<uint16_t*>(cap + a.lay.down_scl),
               row0 + rg, a.H, lb);

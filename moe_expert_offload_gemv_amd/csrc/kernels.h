@@ -49,6 +49,7 @@ bool gemv_shape(int kb, GemvShape* out);
 // Tag of a pick: where its expert's weights are read from.
 constexpr uint8_t kHot = 0;   // HBM pool slot (or prefill staging)
 constexpr uint8_t kCold = 1;  // pinned host memory, zero-copy over PCIe
+constexpr uint8_t kCaptured = 2;  // flag on a cold pick: its reads are written to its capture block
 // which picks a GEMV launch computes
 enum { kAll = 0, kOnlyHot = 1, kOnlyCold = 2 };
 
@@ -81,7 +82,9 @@ struct RouteArgs {
   int32_t policy;        // 1: lookup, stamps, records, counts, step tokens; 0: routing only
                          // (fused with the gate/up GEMV: 0 = lookup without side effects)
   uint32_t* cap_tag;     // [T][k] fused: clock of a cold pick whose bytes the step captured
-  int32_t capture_picks; // picks p < capture_picks of a layer capture their cold reads
+  int32_t capture_picks; // picks p < capture_picks of a layer may capture their cold reads:
+  const uint32_t* last_miss;  // [E] the layer's last-miss clocks as the step began; a cold
+  int32_t window, admit_misses;  // pick captures when the cache step will admit it from them
 };
 hipError_t launch_route(const RouteArgs& a, const Launch& l);
 

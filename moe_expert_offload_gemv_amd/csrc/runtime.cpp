@@ -1,6 +1,7 @@
 // runtime.cpp - the host side of libmoe_offload.so behind include/moe_offload.h:
 // context, HBM pool, pinned host arena, registration (repack into the device
-// layout), seeding, the decode forward (three kernel launches), and the
+// layout), seeding, the decode forward (two kernel launches when the gate/up
+// GEMV routes by itself, else three), and the
 // between-step cache policy.
 //
 // The cache policy is the one the "a6000-custom-kernels" README describes
@@ -215,6 +216,8 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
       return fail(rc);
     if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_cap_tag, sizeof(uint32_t) * L * c->rec_stride, "capture tags")))
       return fail(rc);
+    if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_last_miss, sizeof(uint32_t) * L * E, "last-miss copy")))
+      return fail(rc);
   }
   if ((rc = moe_prefill_alloc(c))) return fail(rc);
 
@@ -227,7 +230,8 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_tbl, sizeof(int32_t) * L * E, pin, "table staging")))
     return fail(rc);
   if (c->capture_picks > 0 &&
-      (rc = moe_ctx_host_alloc(c, (void**)&c->h_cap_tag, sizeof(uint32_t) * L * c->rec_stride, pin, "tag staging")))
+      ((rc = moe_ctx_host_alloc(c, (void**)&c->h_cap_tag, sizeof(uint32_t) * L * c->rec_stride, pin, "tag staging")) ||
+       (rc = moe_ctx_host_alloc(c, (void**)&c->h_last_miss, sizeof(uint32_t) * L * E, pin, "last-miss staging"))))
     return fail(rc);
 
   // HBM pool: S slots per layer
@@ -279,6 +283,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->cap_of.assign(L * E, -1);
   if (c->d_cap_tag && hipMemset(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride) != hipSuccess)
     return fail(MOE_E_HIP);
+  if (c->d_last_miss && hipMemset(c->d_last_miss, 0, sizeof(uint32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_tbl, 0xff, sizeof(int32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_counts, 0, sizeof(uint32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride) != hipSuccess) return fail(MOE_E_HIP);
@@ -377,6 +382,7 @@ extern "C" int moe_seed(moe_ctx* c, const uint32_t* freq) {
   HIP_TRY(c, hipMemsetAsync(c->d_counts, 0, sizeof(uint32_t) * L * E, c->stream));
   HIP_TRY(c, hipMemsetAsync(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride, c->stream));
   if (c->d_cap_tag) HIP_TRY(c, hipMemsetAsync(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride, c->stream));
+  if (c->d_last_miss) HIP_TRY(c, hipMemsetAsync(c->d_last_miss, 0, sizeof(uint32_t) * L * E, c->stream));
   *c->h_ctrl = Ctrl{1, 0, {0, 0}};
   HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
@@ -439,6 +445,8 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   ra.policy = 1;
   ra.capture_picks = c->capture_picks;
   ra.cap_tag = c->d_cap_tag ? c->d_cap_tag + (int64_t)layer * c->rec_stride : nullptr;
+  ra.last_miss = c->d_last_miss ? c->d_last_miss + (int64_t)layer * c->E : nullptr;
+  ra.window = c->cfg.window_tokens, ra.admit_misses = c->cfg.admit_misses;
   // with logits at hand the gate/up GEMV routes by itself (one launch less on
   // the critical path); a router chain runs in its own launch first
   const bool fused = logits && c->E <= moe::kFusedRouteMaxExperts;
@@ -637,6 +645,11 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     }
   }
   forget_captures(c);
+  if (c->d_last_miss && misses > 0) {  // the next step's forwards decide what to capture from it
+    std::memcpy(c->h_last_miss, c->last_miss.data(), sizeof(uint32_t) * L * E);
+    HIP_TRY(c, hipMemcpyAsync(c->d_last_miss, c->h_last_miss, sizeof(uint32_t) * L * E, hipMemcpyHostToDevice,
+                              c->stream));
+  }
   if (admissions > 0) {
     std::memcpy(c->h_tbl, c->tbl.data(), sizeof(int32_t) * L * E);
     HIP_TRY(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * L * E, hipMemcpyHostToDevice, c->stream));

@@ -41,6 +41,7 @@ struct moe_ctx {
   int32_t capture_picks = 0;           // picks per layer whose cold reads are captured
   uint8_t* d_capture = nullptr;        // [L][capture_picks] expert blocks
   uint32_t* d_cap_tag = nullptr;       // [L][rec_stride] clock of a captured cold pick
+  uint32_t* d_last_miss = nullptr;     // [L][E] device copy of last_miss as the step begins
   std::vector<void*> routers;          // per layer fp32 [E][H] or null
 
   // pinned host memory (host_sets distinct sets; layer l uses set l % host_sets)
@@ -50,6 +51,7 @@ struct moe_ctx {
   moe::Ctrl* h_ctrl = nullptr;
   uint64_t* h_records = nullptr;
   uint32_t* h_cap_tag = nullptr;
+  uint32_t* h_last_miss = nullptr;
   int32_t* h_tbl = nullptr;
   uint32_t* h_stamps = nullptr;
 
