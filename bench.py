@@ -88,6 +88,9 @@ def kernel_pass(moe, torch, wl, slots, layers, steps, stream, host_alloc, logits
     return prof
 
 
+PREFILL_WORKLOADS = ("prefill-e512k8-h2048f1024-t4096", "large-e256k8-h4096f1536-t12288")
+
+
 def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3):
     """A prompt pass of one layer: end-to-end time and the grouped GEMMs against the bf16 MFMA peak."""
     import numpy as np
@@ -174,6 +177,8 @@ def main():
     ap.add_argument("--capture-picks", type=int, default=-1,
                     help="picks per layer whose cold reads are kept for promotion (-1: top_k, 0: off)")
     ap.add_argument("--profile-steps", type=int, default=64, help="steps of the kernel-timing pass")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the two prompt passes (one line of JSON each; for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (the reference for counter scaling)")
     args = ap.parse_args()
@@ -197,6 +202,13 @@ def main():
 
     import moe_expert_offload_gemv_amd as moe
     from workload import WORKLOADS, step_activations, zipf_logits
+
+    if args.prefill_only:
+        host_alloc = moe.MOE_HOST_NONCOHERENT if args.host_alloc == "noncoherent" else moe.MOE_HOST_COHERENT
+        stream = torch.cuda.Stream()
+        for name in PREFILL_WORKLOADS:
+            print(json.dumps(prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc)), flush=True)
+        return
 
     wl = WORKLOADS[args.workload]
     host_alloc = moe.MOE_HOST_NONCOHERENT if args.host_alloc == "noncoherent" else moe.MOE_HOST_COHERENT
@@ -351,8 +363,7 @@ def main():
             f"dma {result['pcie_dma_h2d_GBps']} GB/s")
 
     if not args.no_side_passes:
-        result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc)
-                             for name in ("prefill-e512k8-h2048f1024-t4096", "large-e256k8-h4096f1536-t12288")]
+        result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc) for name in PREFILL_WORKLOADS]
         log(f"prefill: {result['prefill']}")
 
     if not args.no_cpu_baseline:

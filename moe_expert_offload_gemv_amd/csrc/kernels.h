@@ -126,20 +126,23 @@ struct GemmArgs {
   const int32_t* arow;          // gate/up: perm (A row = arow[pos] / arow_div); down: nullptr (A row = pos)
   int32_t arow_div;
   const int4* tiles;            // (expert, first sorted position, rows <= BM, 0)
+  const int2* items;            // work list: (tile index, first output feature), a multiple of
+                                //   gemm_features_per_tile(mode, bm)
   const uint8_t* const* eaddr;  // [E] device address of each expert for the pass
   int32_t K, N;                 // reduction length, output features (both multiples of 64)
   ExpertLayout lay;
   _Float16* h16;                // gate/up output: h rows [P][N] fp16 in operand order
   float* y;                     // down output: y_pair [P][N]
-  int32_t work, work_padded;    // set by the launcher: tile x n-tile items, padded to a multiple of 8
+  int32_t work, work_padded;    // set by the launcher: work items, padded to a multiple of 8
 };
 hipError_t launch_expert_histogram(const int32_t* ids, int32_t n_pairs, int32_t E, int32_t* counts, hipStream_t s);
 hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E, const int32_t* offsets,
                                  int32_t* perm, int32_t* inv, hipStream_t s);
 hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, hipStream_t s);
 int gemm_features_per_tile(int mode, int bm);
-// mode 0 gate/up, 1 down; bm = 64 or 128 rows per tile (the tiles were cut to it)
-hipError_t launch_grouped_gemm(GemmArgs a, int mode, int bm, int n_tiles, const Launch& l);
+// mode 0 gate/up, 1 down; bm = 64 or 128 rows per tile (the tiles were cut to it);
+// a.items holds n_items work items
+hipError_t launch_grouped_gemm(GemmArgs a, int mode, int bm, int n_items, const Launch& l);
 hipError_t launch_combine_pairs(const float* ypair, const int32_t* inv, const float* w, int32_t T, int32_t k,
                                 int32_t H, float* y, int32_t accumulate, hipStream_t s);
 

@@ -39,7 +39,7 @@ bool capturing(hipStream_t s) {
 }  // namespace
 
 struct Prefill {
-  int64_t max_tokens = 0, max_pairs = 0, max_tiles = 0;
+  int64_t max_tokens = 0, max_pairs = 0, max_tiles = 0, max_items = 0;
   int32_t* ids = nullptr;       // [P]
   float* w = nullptr;           // [P]
   int32_t* perm = nullptr;      // [P] sorted position -> pair
@@ -47,6 +47,7 @@ struct Prefill {
   int32_t* counts = nullptr;    // [E]
   int32_t* offsets = nullptr;   // [E + 1]
   int4* tiles = nullptr;        // [max_tiles]
+  int2* items[2] = {nullptr, nullptr};    // [max_items] work lists of the gate/up and down GEMMs
   const uint8_t** eaddr = nullptr;  // [E]
   _Float16* x16 = nullptr;      // [T][H] activations, fp16 in operand order
   _Float16* h16 = nullptr;      // [P][F] SwiGLU outputs, fp16 in operand order
@@ -55,6 +56,7 @@ struct Prefill {
   int32_t* h_counts = nullptr;
   int32_t* h_offsets = nullptr;
   int4* h_tiles = nullptr;
+  int2* h_items[2] = {nullptr, nullptr};
   const uint8_t** h_eaddr = nullptr;
 };
 
@@ -72,6 +74,7 @@ int moe_prefill_alloc(moe_ctx* c) {
   const int64_t E = c->E, P = T * c->k;
   p->max_tokens = T, p->max_pairs = P;
   p->max_tiles = E + P / kMinTileRows + 1;
+  p->max_items = p->max_tiles * ((std::max(c->F, c->H) + 127) / 128);  // feature tiles are >= 128 wide
   int rc;
   auto dev = [&](void** q, size_t bytes, const char* what) { return moe_ctx_dev_alloc(c, q, bytes, what); };
   if ((rc = dev((void**)&p->ids, sizeof(int32_t) * P, "prefill ids")) ||
@@ -81,6 +84,8 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = dev((void**)&p->counts, sizeof(int32_t) * E, "prefill counts")) ||
       (rc = dev((void**)&p->offsets, sizeof(int32_t) * (E + 1), "prefill offsets")) ||
       (rc = dev((void**)&p->tiles, sizeof(int4) * p->max_tiles, "prefill tiles")) ||
+      (rc = dev((void**)&p->items[0], sizeof(int2) * p->max_items, "prefill gate/up work list")) ||
+      (rc = dev((void**)&p->items[1], sizeof(int2) * p->max_items, "prefill down work list")) ||
       (rc = dev((void**)&p->eaddr, sizeof(uint8_t*) * E, "prefill addresses")) ||
       (rc = dev((void**)&p->x16, sizeof(_Float16) * T * c->H, "prefill x fp16")) ||
       (rc = dev((void**)&p->h16, sizeof(_Float16) * P * c->F, "prefill h fp16")) ||
@@ -90,6 +95,8 @@ int moe_prefill_alloc(moe_ctx* c) {
   if ((rc = moe_ctx_host_alloc(c, (void**)&p->h_counts, sizeof(int32_t) * E, pin, "prefill count staging")) ||
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_offsets, sizeof(int32_t) * (E + 1), pin, "prefill offsets staging")) ||
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_tiles, sizeof(int4) * p->max_tiles, pin, "prefill tile staging")) ||
+      (rc = moe_ctx_host_alloc(c, (void**)&p->h_items[0], sizeof(int2) * p->max_items, pin, "prefill item staging")) ||
+      (rc = moe_ctx_host_alloc(c, (void**)&p->h_items[1], sizeof(int2) * p->max_items, pin, "prefill item staging")) ||
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_eaddr, sizeof(uint8_t*) * E, pin, "prefill address staging")))
     return rc;
   return MOE_OK;
@@ -174,6 +181,22 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   if (pos != P) return moe_ctx_fail(c, MOE_E_HIP, "prefill: pair count mismatch (%lld != %d)", (long long)pos, P);
   PF_HIP(c, hipMemcpyAsync(p->offsets, p->h_offsets, sizeof(int32_t) * (E + 1), hipMemcpyHostToDevice, s));
   PF_HIP(c, hipMemcpyAsync(p->tiles, p->h_tiles, sizeof(int4) * n_tiles, hipMemcpyHostToDevice, s));
+  // work lists: per expert, feature tiles outer and row tiles inner
+  int n_items[2] = {0, 0};
+  for (int mode = 0; mode < 2; ++mode) {
+    const int N = mode == 0 ? F : H, bnw = moe::gemm_features_per_tile(mode, bm);
+    if (n_tiles * ((N + bnw - 1) / bnw) > p->max_items)
+      return moe_ctx_fail(c, MOE_E_HIP, "prefill: work list larger than its buffer");
+    int2* it = p->h_items[mode];
+    for (int64_t t0 = 0; t0 < n_tiles;) {
+      int64_t t1 = t0;
+      while (t1 < n_tiles && p->h_tiles[t1].x == p->h_tiles[t0].x) ++t1;
+      for (int n0 = 0; n0 < N; n0 += bnw)
+        for (int64_t t = t0; t < t1; ++t) it[n_items[mode]++] = int2{(int32_t)t, n0};
+      t0 = t1;
+    }
+    PF_HIP(c, hipMemcpyAsync(p->items[mode], it, sizeof(int2) * n_items[mode], hipMemcpyHostToDevice, s));
+  }
   PF_HIP(c, hipMemcpyAsync(p->eaddr, p->h_eaddr, sizeof(uint8_t*) * E, hipMemcpyHostToDevice, s));
 
   // 4. stable sort of the pairs by expert
@@ -187,18 +210,19 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   if (c->profiling && c->prefill_events.size() >= 4) ev = c->prefill_events.data();
   moe::GemmArgs g{};
   g.a16 = p->x16, g.arow = p->perm, g.arow_div = k;
-  g.tiles = p->tiles, g.eaddr = p->eaddr;
+  g.tiles = p->tiles, g.eaddr = p->eaddr, g.items = p->items[0];
   g.K = H, g.N = F;
   g.lay = c->lay;
   g.h16 = p->h16;
   moe::Launch l1 = ls, l2 = ls;
   if (ev) l1.start = ev[0], l1.stop = ev[1], l2.start = ev[2], l2.stop = ev[3];
-  PF_HIP(c, moe::launch_grouped_gemm(g, 0, bm, (int)n_tiles, l1));
+  PF_HIP(c, moe::launch_grouped_gemm(g, 0, bm, n_items[0], l1));
   moe::GemmArgs d = g;
   d.a16 = p->h16, d.arow = nullptr, d.arow_div = 1;
   d.K = F, d.N = H;
+  d.items = p->items[1];
   d.y = p->ypair;
-  PF_HIP(c, moe::launch_grouped_gemm(d, 1, bm, (int)n_tiles, l2));
+  PF_HIP(c, moe::launch_grouped_gemm(d, 1, bm, n_items[1], l2));
 
   // 7. weighted combine in pick order
   PF_HIP(c, moe::launch_combine_pairs(p->ypair, p->inv, p->w, T, k, H, y, (flags & MOE_ACCUMULATE) ? 1 : 0, s));

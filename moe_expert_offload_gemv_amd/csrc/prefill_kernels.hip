@@ -200,24 +200,26 @@ __global__ __launch_bounds__(256) void convert_rows_kernel(const float* src, int
 // MODE 0: gate/up (two matrices, SwiGLU epilogue, writes h as fp16 rows in
 //         operand order); MODE 1: down (one matrix, writes y_pair).
 // NSUB is chosen so every wave holds at most 128 accumulators.
-// Work items are numbered so that each XCD (work item id mod 8 of the launch
-// order) gets a contiguous range: the n-tiles of one row tile, then the next
-// row tile of the same expert, share an L2.
+// Work items (row tile, first feature) come from a list the host orders per
+// expert by feature tile, then row tile: the row tiles that read the same
+// weight columns are neighbours, start together and keep in step, so each
+// weight line is fetched from HBM once. Each XCD (work group id mod 8 of the
+// launch order) gets a contiguous range of the list, so neighbours share an L2.
 template <int BM, int MODE>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   using C = GemmTile<BM, MODE>;
   constexpr int NMAT = C::NMAT, RB = C::RB, NSUB = C::NSUB, WN = C::WN, BNW = C::BNW;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * C::STAGE];
 
-  // XCD-contiguous work numbering
+  // XCD-contiguous work numbering over the host's work list
   const int L = blockIdx.x;
   const int per = a.work_padded / 8;
   const int W = (L & 7) * per + (L >> 3);
   if (W >= a.work) return;
-  const int n_tiles_n = (a.N + BNW - 1) / BNW;
-  const int4 tile = a.tiles[W / n_tiles_n];
+  const int2 item = a.items[W];
+  const int4 tile = a.tiles[item.x];
   const int e = tile.x, pos0 = tile.y, rows = tile.z;
-  const int n0 = (W % n_tiles_n) * BNW;
+  const int n0 = item.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
   const int K = a.K, N = a.N, nks = K / KS, nkb = K / 32;
@@ -380,11 +382,10 @@ int gemm_features_per_tile(int mode, int bm) {
   if (mode == 0) return bm == 64 ? GemmTile<64, 0>::BNW : GemmTile<128, 0>::BNW;
   return bm == 64 ? GemmTile<64, 1>::BNW : GemmTile<128, 1>::BNW;
 }
-hipError_t launch_grouped_gemm(GemmArgs a, int mode, int bm, int n_tiles, const Launch& l) {
-  if (a.K % KS || a.N % KS || n_tiles <= 0 || (bm != 64 && bm != 128) || (mode != 0 && mode != 1))
+hipError_t launch_grouped_gemm(GemmArgs a, int mode, int bm, int n_items, const Launch& l) {
+  if (a.K % KS || a.N % KS || n_items <= 0 || !a.items || (bm != 64 && bm != 128) || (mode != 0 && mode != 1))
     return hipErrorInvalidValue;
-  const int bnw = gemm_features_per_tile(mode, bm);
-  a.work = n_tiles * ((a.N + bnw - 1) / bnw);
+  a.work = n_items;
   a.work_padded = (a.work + 7) / 8 * 8;
   const dim3 grid(a.work_padded), block(256);
   if (mode == 0) return bm == 64 ? launch(grouped_gemm_kernel<64, 0>, grid, block, l, a)
