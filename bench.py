@@ -29,8 +29,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+# HBM bytes per launch of the roofline kernel (gemv_route_gateup_kernel<64,1,4,1>, hot picks), from two rocprofv3
+# counter runs (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, scaled by a 1 GiB copy) over launches that served 7.14 hot picks
+# each (16.85 MB algorithmic); the summary and commands are under profiles/. Set to None when the kernel changes.
+ROOFLINE_TRAFFIC = None  # re-measure after a kernel change (last: 17.19e6 B over 16.85e6 B algorithmic)
 PCIE_PEAK_GBPS = 64.0       # PCIe Gen5 x16, one direction
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA; fp16 (what the grouped GEMM runs) has the same rate
 METRIC = "MoE-layer decode tokens/s + effective weight GB/s vs HBM/PCIe roofline"
 
 
@@ -67,9 +71,10 @@ def run_steps(moe, ctx, n, step_fn, stats_acc=None):
                 stats_acc[k_] = stats_acc.get(k_, 0) + v
 
 
-def kernel_pass(moe, torch, wl, slots, layers, steps, stream, host_alloc, logits_all, x_all):
+def kernel_pass(moe, torch, wl, slots, layers, steps, stream, host_alloc, logits_all, x_all, capture_picks=None):
     """Time the forward kernels on a small context (all hot or all cold)."""
-    ctx, freq = setup_ctx(moe, wl, slots, stream, host_alloc, layers=layers, progress=False)
+    ctx, freq = setup_ctx(moe, wl, slots, stream, host_alloc, layers=layers, progress=False,
+                          capture_picks=capture_picks)
     moe.moe_seed(ctx, freq)
     T, H = wl.tokens, wl.hidden
     res = torch.empty((T, H), dtype=torch.float32, device="cuda")
@@ -130,7 +135,7 @@ def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3):
         "gateup_gemm_ms": round(gu_ms, 4), "down_gemm_ms": round(dn_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "grouped_gemm_kernel (gate/up + down), algorithmic flops 6*H*F per pair",
+                     "kernel": "grouped_gemm_kernel (gate/up + down, fp16 MFMA), algorithmic flops 6*H*F per pair",
                      "mfma_flops_per_algorithmic_flop": 1},
     }
 
@@ -314,7 +319,10 @@ def main():
         "promotion_GB": round(acc["copied_bytes"] / 1e9, 3),
         "promotion_GB_over_pcie": round(acc["copied_pcie_bytes"] / 1e9, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": ROOFLINE_TRAFFIC and int(ROOFLINE_TRAFFIC["bytes_per_launch"]),
+                     "traffic_over_algorithmic": ROOFLINE_TRAFFIC and round(
+                         ROOFLINE_TRAFFIC["bytes_per_launch"] / ROOFLINE_TRAFFIC["algorithmic_bytes_per_launch"], 3),
                      "kernel": "gemv_route_gateup_kernel, hot picks (routing + slot lookup + gate/up + SwiGLU "
                                "from the HBM pool; the launch includes the routing)",
                      "avg_launch_us": round(hot_gu_us, 2), "bytes_per_launch": int(hot_gu_bytes)},
@@ -328,8 +336,9 @@ def main():
 
     if not args.no_side_passes:
         side = min(4, L)
-        hot = kernel_pass(moe, torch, wl, E, side, 32, stream, host_alloc, logits_all, x_all)
-        cold = kernel_pass(moe, torch, wl, 0, side, 8, stream, host_alloc, logits_all, x_all)
+        cap = None if args.capture_picks < 0 else args.capture_picks
+        hot = kernel_pass(moe, torch, wl, E, side, 32, stream, host_alloc, logits_all, x_all, cap)
+        cold = kernel_pass(moe, torch, wl, 0, side, 8, stream, host_alloc, logits_all, x_all, cap)
 
         def rate(p, ms_key, picks_key, bytes_key):
             return p[picks_key] * p[bytes_key] / max(p[ms_key], 1e-9) / 1e6  # bytes / ms -> GB/s

@@ -37,6 +37,7 @@ def _prefill_check(wl: Workload, slots: int, sample=None, flags=0):
     y_ref, ids_ref, _ = oracle.moe_layer(wl.n_experts, wl.top_k, H, wl.ffn, d.experts(0, ids), x32[rows].astype(
         np.float64), logits=z[rows])
     err = token_rel_err(yh[rows], y_ref)
+    print(f"{wl.name}: worst token error {err:.2e}")
     assert err < TOL, err
     # policy neutral: tables, stamps, counts, clock untouched
     for layer in range(wl.n_layers):
