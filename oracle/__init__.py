@@ -59,7 +59,7 @@ def lib():
         L.orc_moe_layer.argtypes = [C.c_int32] * 5 + [C.c_void_p] * 3 + [C.c_void_p, C.c_void_p, C.c_void_p,
                                                                           _f64p, _f64p, _i32p, _f64p]
         L.orc_moe_layer.restype = C.c_int
-        L.orc_policy_new.argtypes = [C.c_int32] * 6 + [C.c_int64]
+        L.orc_policy_new.argtypes = [C.c_int32] * 6 + [C.c_int64, C.c_int32]
         L.orc_policy_new.restype = C.c_void_p
         L.orc_policy_free.argtypes = [C.c_void_p]
         L.orc_policy_seed.argtypes = [C.c_void_p, C.c_void_p]
@@ -177,9 +177,15 @@ def moe_layer(E: int, k: int, H: int, F: int, experts, x, logits=None, w_router=
 class Policy:
     """Step-by-step simulation of the expert cache (see moe_oracle.c)."""
 
-    def __init__(self, n_layers, n_experts, slots, top_k, window=64, admit_misses=2, log_capacity=1 << 20):
+    def __init__(self, n_layers, n_experts, slots, top_k, window=64, admit_misses=2, log_capacity=1 << 20,
+                 pool="layer"):
+        """slots: per layer (pool="layer") or in the one pool all layers share (pool="global")."""
+        assert pool in ("layer", "global")
         self.L, self.E, self.S, self.k = n_layers, n_experts, slots, top_k
-        self._p = lib().orc_policy_new(n_layers, n_experts, slots, top_k, window, admit_misses, log_capacity)
+        self.pool = pool
+        self.groups = 1 if pool == "global" else n_layers
+        self._p = lib().orc_policy_new(n_layers, n_experts, slots, top_k, window, admit_misses, log_capacity,
+                                       1 if pool == "global" else 0)
 
     def __del__(self):
         if getattr(self, "_p", None):
@@ -202,12 +208,16 @@ class Policy:
                     tokens=int(s[4]))
 
     def tables(self):
+        """table [L][E] (slot in the layer's pool, -1 cold); per pool [groups][S]: owner (expert or -1),
+        owner_layer (layer or -1), stamps; last_miss [L][E]. groups = L per layer, 1 global."""
         tbl = np.empty((self.L, self.E), np.int32)
-        own = np.empty((self.L, max(self.S, 1)), np.int32)
-        st = np.empty((self.L, max(self.S, 1)), np.uint32)
+        own = np.empty((self.groups, max(self.S, 1)), np.int32)
+        st = np.empty((self.groups, max(self.S, 1)), np.uint32)
         lm = np.empty((self.L, self.E), np.uint32)
         lib().orc_policy_tables(self._p, tbl.ctypes.data, own.ctypes.data, st.ctypes.data, lm.ctypes.data)
-        return dict(table=tbl, owner=own[:, :self.S], stamps=st[:, :self.S], last_miss=lm)
+        own = own[:, :self.S]
+        return dict(table=tbl, owner=np.where(own < 0, -1, own % self.E), owner_layer=np.where(own < 0, -1, own // self.E),
+                    stamps=st[:, :self.S], last_miss=lm)
 
     def last_log(self) -> np.ndarray:
         n = lib().orc_policy_last_log(self._p, None, 0)
@@ -216,9 +226,10 @@ class Policy:
         return out[:n]
 
     def last_admissions(self) -> np.ndarray:
-        """int32 [n][4]: (layer, expert, slot, evicted expert or -1) in walk order."""
+        """int32 [n][5]: (layer, expert, slot, evicted layer, evicted expert; -1 when the slot was free),
+        in walk order."""
         n = lib().orc_policy_last_admissions(self._p, None, 0)
-        out = np.empty((max(n, 1), 4), np.int32)
+        out = np.empty((max(n, 1), 5), np.int32)
         lib().orc_policy_last_admissions(self._p, out.ctypes.data, n)
         return out[:n]
 

@@ -199,15 +199,29 @@ ORC_EXPORT int orc_moe_layer(int32_t T, int32_t E, int32_t k, int32_t H, int32_t
  * 1 every such entry admits. An admission takes the lowest free slot, else the
  * slot with the smallest stamp (ties: highest index), evicting its expert
  * (whose lm is cleared); the new owner's stamp is t and its lm is cleared.
- * The clock then advances by the step's token count.                         */
+ * The clock then advances by the step's token count.
+ *
+ * Pool partition: per layer (S slots for each layer, above), or one global
+ * pool of S slots shared by all layers (the "llama.cpp: fork with multi gpu
+ * acceleration ..." README, "How it works": one global pool of expert blocks
+ * instead of a fixed reserve per layer). The rules are the same with the
+ * layer's slots replaced by all slots: a slot's owner is a (layer, expert)
+ * pair, the victim is the lowest free slot of the pool, else the pool's
+ * smallest stamp (ties: highest index), and seeding fills slots 0..S-1 with
+ * the (layer, expert) pairs ordered by count (descending; ties: lower layer,
+ * then lower expert).
+ * Internally both are "groups": L groups of S slots, or 1 group of S slots;
+ * own[] holds layer * E + expert.                                           */
 typedef struct {
   int32_t L, E, S, k, window, admit;
+  int32_t global;     /* 1: one pool of S slots for all layers */
+  int32_t groups;     /* L (per layer) or 1 (global) */
   uint32_t clock;
   uint32_t step_tokens;
   int64_t step;
   int32_t* tbl;      /* [L][E] */
-  int32_t* own;      /* [L][S] */
-  uint32_t* st;      /* [L][S] */
+  int32_t* own;      /* [groups][S]: layer * E + expert, or -1 */
+  uint32_t* st;      /* [groups][S] */
   uint32_t* lm;      /* [L][E] */
   uint32_t* counts;  /* [L][E] */
   uint64_t* log;     /* current step's log */
@@ -215,27 +229,30 @@ typedef struct {
   uint64_t* last_log; /* log of the last closed step, sorted */
   int64_t nlast;
   int64_t hits, misses;
-  /* admissions of the last closed step: (layer, expert, slot, evicted) */
+  /* admissions of the last closed step: (layer, expert, slot, evicted layer, evicted expert) */
   int32_t* adm;
   int64_t nadm, capadm;
 } orc_policy;
 
+/* global != 0: S is the size of the one pool shared by all layers */
 ORC_EXPORT orc_policy* orc_policy_new(int32_t L, int32_t E, int32_t S, int32_t k, int32_t window, int32_t admit,
-                                      int64_t log_capacity) {
+                                      int64_t log_capacity, int32_t global) {
   orc_policy* p = (orc_policy*)calloc(1, sizeof(orc_policy));
   p->L = L, p->E = E, p->S = S, p->k = k, p->window = window, p->admit = admit;
+  p->global = global ? 1 : 0;
+  p->groups = global ? 1 : L;
   p->tbl = (int32_t*)malloc(sizeof(int32_t) * L * E);
-  p->own = (int32_t*)malloc(sizeof(int32_t) * L * (S > 0 ? S : 1));
-  p->st = (uint32_t*)calloc((size_t)L * (S > 0 ? S : 1), sizeof(uint32_t));
+  p->own = (int32_t*)malloc(sizeof(int32_t) * p->groups * (S > 0 ? S : 1));
+  p->st = (uint32_t*)calloc((size_t)p->groups * (S > 0 ? S : 1), sizeof(uint32_t));
   p->lm = (uint32_t*)calloc((size_t)L * E, sizeof(uint32_t));
   p->counts = (uint32_t*)calloc((size_t)L * E, sizeof(uint32_t));
   p->caplog = log_capacity;
   p->log = (uint64_t*)malloc(sizeof(uint64_t) * (log_capacity > 0 ? log_capacity : 1));
   p->last_log = (uint64_t*)malloc(sizeof(uint64_t) * (log_capacity > 0 ? log_capacity : 1));
   p->capadm = log_capacity;
-  p->adm = (int32_t*)malloc(sizeof(int32_t) * 4 * (log_capacity > 0 ? log_capacity : 1));
+  p->adm = (int32_t*)malloc(sizeof(int32_t) * 5 * (log_capacity > 0 ? log_capacity : 1));
   for (int64_t i = 0; i < (int64_t)L * E; ++i) p->tbl[i] = -1;
-  for (int64_t i = 0; i < (int64_t)L * S; ++i) p->own[i] = -1;
+  for (int64_t i = 0; i < (int64_t)p->groups * S; ++i) p->own[i] = -1;
   p->clock = 1;
   return p;
 }
@@ -248,25 +265,31 @@ ORC_EXPORT void orc_policy_free(orc_policy* p) {
 }
 
 /* Seed: per layer, experts ordered by count (descending, ties: lower id)
- * fill slots 0..S-1; freq == NULL leaves every slot free. Resets stamps, last
- * misses, counts and the log; the clock restarts at 1.                       */
+ * fill slots 0..S-1 (global pool: all (layer, expert) pairs ordered by count,
+ * ties: lower layer, then lower id, fill the pool's slots 0..S-1); freq ==
+ * NULL leaves every slot free. Resets stamps, last misses, counts and the
+ * log; the clock restarts at 1. The selection is a plain repeated scan for
+ * the best pair not yet taken.                                              */
 ORC_EXPORT void orc_policy_seed(orc_policy* p, const uint32_t* freq) {
   int32_t L = p->L, E = p->E, S = p->S;
   for (int64_t i = 0; i < (int64_t)L * E; ++i) p->tbl[i] = -1, p->lm[i] = 0, p->counts[i] = 0;
-  for (int64_t i = 0; i < (int64_t)L * S; ++i) p->own[i] = -1, p->st[i] = 0;
+  for (int64_t i = 0; i < (int64_t)p->groups * S; ++i) p->own[i] = -1, p->st[i] = 0;
   if (freq) {
-    int32_t* taken = (int32_t*)calloc(E, sizeof(int32_t));
-    for (int32_t l = 0; l < L; ++l) {
-      memset(taken, 0, sizeof(int32_t) * E);
-      for (int32_t s = 0; s < S; ++s) {
-        int32_t best = -1;
-        for (int32_t e = 0; e < E; ++e) {
-          if (taken[e]) continue;
-          if (best < 0 || freq[(int64_t)l * E + e] > freq[(int64_t)l * E + best]) best = e;
+    char* taken = (char*)calloc((size_t)L * E, 1);
+    for (int32_t g = 0; g < p->groups; ++g) {
+      /* candidates of group g: layer g (per layer) or every layer (global), in (layer, expert) order */
+      int64_t lo = p->global ? 0 : (int64_t)g * E, hi = p->global ? (int64_t)L * E : (int64_t)(g + 1) * E;
+      int32_t n = S;
+      if (n > hi - lo) n = (int32_t)(hi - lo);
+      for (int32_t s = 0; s < n; ++s) {
+        int64_t best = -1;
+        for (int64_t te = lo; te < hi; ++te) {
+          if (taken[te]) continue;
+          if (best < 0 || freq[te] > freq[best]) best = te;  /* strict: the first (lowest) index wins ties */
         }
         taken[best] = 1;
-        p->tbl[(int64_t)l * E + best] = s;
-        p->own[(int64_t)l * S + s] = best;
+        p->tbl[best] = s;
+        p->own[(int64_t)g * S + s] = (int32_t)best;
       }
     }
     free(taken);
@@ -290,7 +313,7 @@ ORC_EXPORT int orc_policy_forward(orc_policy* p, int32_t layer, int32_t T, const
       p->counts[(int64_t)layer * p->E + e] += 1;
       int32_t s = p->tbl[(int64_t)layer * p->E + e];
       if (s >= 0) {
-        uint32_t* stamp = &p->st[(int64_t)layer * p->S + s];
+        uint32_t* stamp = &p->st[(int64_t)(p->global ? 0 : layer) * p->S + s];
         if (clk > *stamp) *stamp = clk;
         p->hits += 1;
       } else {
@@ -331,30 +354,33 @@ ORC_EXPORT void orc_policy_step(orc_policy* p, int64_t* stats) {
       if (!admit_now) p->lm[te] = t;
     }
     if (!admit_now || S == 0) continue;
-    /* victim: lowest free slot, else smallest stamp with ties to the highest index */
+    /* victim among the slots of the layer's group: lowest free slot, else
+     * smallest stamp with ties to the highest index */
+    const int64_t g0 = (int64_t)(p->global ? 0 : layer) * S;
     int32_t victim = -1;
     for (int32_t s = 0; s < S; ++s)
-      if (p->own[(int64_t)layer * S + s] < 0) {
+      if (p->own[g0 + s] < 0) {
         victim = s;
         break;
       }
-    int32_t evicted = -1;
+    int32_t evicted = -1;  /* layer * E + expert of the evicted owner */
     if (victim < 0) {
       for (int32_t s = 0; s < S; ++s)
-        if (victim < 0 || p->st[(int64_t)layer * S + s] <= p->st[(int64_t)layer * S + victim]) victim = s;
-      evicted = p->own[(int64_t)layer * S + victim];
-      p->tbl[(int64_t)layer * E + evicted] = -1;
-      p->lm[(int64_t)layer * E + evicted] = 0;
+        if (victim < 0 || p->st[g0 + s] <= p->st[g0 + victim]) victim = s;
+      evicted = p->own[g0 + victim];
+      p->tbl[evicted] = -1;
+      p->lm[evicted] = 0;
       evictions += 1;
     }
-    p->own[(int64_t)layer * S + victim] = e;
+    p->own[g0 + victim] = (int32_t)te;
     p->tbl[te] = victim;
-    p->st[(int64_t)layer * S + victim] = t;
+    p->st[g0 + victim] = t;
     p->lm[te] = 0;
     admissions += 1;
     if (p->nadm < p->capadm) {
-      int32_t* a = p->adm + 4 * p->nadm++;
-      a[0] = layer, a[1] = e, a[2] = victim, a[3] = evicted;
+      int32_t* a = p->adm + 5 * p->nadm++;
+      a[0] = layer, a[1] = e, a[2] = victim;
+      a[3] = evicted < 0 ? -1 : evicted / E, a[4] = evicted < 0 ? -1 : evicted % E;
     }
   }
   if (stats) {
@@ -373,8 +399,8 @@ ORC_EXPORT void orc_policy_step(orc_policy* p, int64_t* stats) {
 /* Accessors (copies into caller buffers). */
 ORC_EXPORT void orc_policy_tables(const orc_policy* p, int32_t* tbl, int32_t* own, uint32_t* st, uint32_t* lm) {
   if (tbl) memcpy(tbl, p->tbl, sizeof(int32_t) * p->L * p->E);
-  if (own) memcpy(own, p->own, sizeof(int32_t) * p->L * p->S);
-  if (st) memcpy(st, p->st, sizeof(uint32_t) * p->L * p->S);
+  if (own) memcpy(own, p->own, sizeof(int32_t) * p->groups * p->S);
+  if (st) memcpy(st, p->st, sizeof(uint32_t) * p->groups * p->S);
   if (lm) memcpy(lm, p->lm, sizeof(uint32_t) * p->L * p->E);
 }
 ORC_EXPORT int64_t orc_policy_last_log(const orc_policy* p, uint64_t* out, int64_t cap) {
@@ -384,7 +410,7 @@ ORC_EXPORT int64_t orc_policy_last_log(const orc_policy* p, uint64_t* out, int64
 }
 ORC_EXPORT int64_t orc_policy_last_admissions(const orc_policy* p, int32_t* out, int64_t cap) {
   int64_t n = p->nadm < cap ? p->nadm : cap;
-  if (out && n > 0) memcpy(out, p->adm, sizeof(int32_t) * 4 * (size_t)n);
+  if (out && n > 0) memcpy(out, p->adm, sizeof(int32_t) * 5 * (size_t)n);
   return p->nadm;
 }
 ORC_EXPORT void orc_policy_counts(const orc_policy* p, uint32_t* out) {

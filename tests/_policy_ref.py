@@ -12,22 +12,32 @@ from __future__ import annotations
 
 
 class PolicyRef:
-    def __init__(self, L, E, S, k, window=64, admit=2):
+    """pool="layer": S slots per layer; pool="global": one pool of S slots that
+    every layer draws from (owners are (layer, expert) pairs)."""
+
+    def __init__(self, L, E, S, k, window=64, admit=2, pool="layer"):
         self.L, self.E, self.S, self.k, self.window, self.admit = L, E, S, k, window, admit
+        self.pool = pool
+        self.G = 1 if pool == "global" else L
         self.seed(None)
+
+    def _group(self, layer):
+        return 0 if self.pool == "global" else layer
 
     def seed(self, freq):
         self.where = {}  # (layer, e) -> slot
-        self.owner = [[None] * self.S for _ in range(self.L)]
-        self.uses = [[[] for _ in range(self.S)] for _ in range(self.L)]
+        self.owner = [[None] * self.S for _ in range(self.G)]  # (layer, e) or None
+        self.uses = [[[] for _ in range(self.S)] for _ in range(self.G)]
         self.misses_since_reset = {}
         self.counts = [[0] * self.E for _ in range(self.L)]
         if freq is not None:
-            for layer in range(self.L):
-                order = sorted(range(self.E), key=lambda e: (-int(freq[layer][e]), e))
-                for s, e in enumerate(order[: self.S]):
-                    self.where[(layer, e)] = s
-                    self.owner[layer][s] = e
+            for g in range(self.G):
+                layers = range(self.L) if self.pool == "global" else [g]
+                cands = [(layer, e) for layer in layers for e in range(self.E)]
+                cands.sort(key=lambda le: (-int(freq[le[0]][le[1]]), le[0], le[1]))
+                for s, le in enumerate(cands[: self.S]):
+                    self.where[le] = s
+                    self.owner[g][s] = le
         self.clock = 1
         self.log = []
         self.step_tokens = 0
@@ -36,20 +46,21 @@ class PolicyRef:
 
     def forward(self, layer, ids):
         T = len(ids)
+        g = self._group(layer)
         for t in range(T):
             clk = self.clock + t
             for e in ids[t]:
                 e = int(e)
                 self.counts[layer][e] += 1
                 if (layer, e) in self.where:
-                    self.uses[layer][self.where[(layer, e)]].append(clk)
+                    self.uses[g][self.where[(layer, e)]].append(clk)
                     self.hits += 1
                 else:
                     self.log.append((clk, layer, e))
         self.step_tokens = max(self.step_tokens, T)
 
-    def _stamp(self, layer, s):
-        return max(self.uses[layer][s]) if self.uses[layer][s] else 0
+    def _stamp(self, g, s):
+        return max(self.uses[g][s]) if self.uses[g][s] else 0
 
     def step(self):
         entries = sorted(self.log)
@@ -67,22 +78,23 @@ class PolicyRef:
                     hist.append(t)
             if not ok or self.S == 0:
                 continue
-            free = [s for s in range(self.S) if self.owner[layer][s] is None]
-            evicted = -1
+            g = self._group(layer)
+            free = [s for s in range(self.S) if self.owner[g][s] is None]
+            evicted = (-1, -1)
             if free:
                 victim = min(free)
             else:
-                victim = max(range(self.S), key=lambda s: (-self._stamp(layer, s), s))
-                evicted = self.owner[layer][victim]
-                del self.where[(layer, evicted)]
-                self.misses_since_reset[(layer, evicted)] = []
+                victim = max(range(self.S), key=lambda s: (-self._stamp(g, s), s))
+                evicted = self.owner[g][victim]
+                del self.where[evicted]
+                self.misses_since_reset[evicted] = []
                 ev += 1
-            self.owner[layer][victim] = e
+            self.owner[g][victim] = (layer, e)
             self.where[(layer, e)] = victim
-            self.uses[layer][victim] = [t]
+            self.uses[g][victim] = [t]
             self.misses_since_reset[(layer, e)] = []
             adm += 1
-            admissions.append((layer, e, victim, evicted))
+            admissions.append((layer, e, victim) + tuple(evicted))
         stats = dict(hits=self.hits, misses=len(self.log), admissions=adm, evictions=ev, tokens=self.step_tokens)
         self.last_log = [(t << 32) | (layer << 12) | e for (t, layer, e) in entries]
         self.last_admissions = admissions
@@ -96,4 +108,4 @@ class PolicyRef:
         return [[self.where.get((layer, e), -1) for e in range(self.E)] for layer in range(self.L)]
 
     def stamps(self):
-        return [[self._stamp(layer, s) for s in range(self.S)] for layer in range(self.L)]
+        return [[self._stamp(g, s) for s in range(self.S)] for g in range(self.G)]

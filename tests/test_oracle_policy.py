@@ -53,7 +53,7 @@ def test_second_miss_inside_window_admits():
     assert t["table"][0].tolist() == [0, -1, 1, -1]
     assert t["stamps"][0].tolist() == [63, 64]
     assert pol.last_log().tolist() == [(64 << 32) | 2]
-    assert pol.last_admissions().tolist() == [[0, 2, 1, 1]]
+    assert pol.last_admissions().tolist() == [[0, 2, 1, 0, 1]]
     assert pol.clock == 65
 
 
@@ -147,16 +147,17 @@ def _random_trace(draw_rng, L, E, k, steps, tmax):
     return trace
 
 
-@settings(max_examples=40, deadline=None)
+@settings(max_examples=60, deadline=None)
 @given(seed=st.integers(0, 2**31 - 1), L=st.integers(1, 3), E=st.integers(2, 12), tmax=st.integers(1, 4),
-       window=st.sampled_from([2, 5, 64]), admit=st.sampled_from([1, 2]), seeded=st.booleans())
-def test_agrees_with_history_formulation(seed, L, E, tmax, window, admit, seeded):
+       window=st.sampled_from([2, 5, 64]), admit=st.sampled_from([1, 2]), seeded=st.booleans(),
+       pool=st.sampled_from(["layer", "global"]))
+def test_agrees_with_history_formulation(seed, L, E, tmax, window, admit, seeded, pool):
     rng = np.random.default_rng(seed)
     k = int(rng.integers(1, E + 1))
-    S = int(rng.integers(0, E + 1))
+    S = int(rng.integers(0, (E if pool == "layer" else L * E) + 1))
     freq = rng.integers(0, 5, size=(L, E)).astype(np.uint32) if seeded else None
-    a = oracle.Policy(L, E, S, k, window=window, admit_misses=admit)
-    b = PolicyRef(L, E, S, k, window=window, admit=admit)
+    a = oracle.Policy(L, E, S, k, window=window, admit_misses=admit, pool=pool)
+    b = PolicyRef(L, E, S, k, window=window, admit=admit, pool=pool)
     a.seed(freq)
     b.seed(freq)
     cum_adm = cum_miss = 0
@@ -171,13 +172,15 @@ def test_agrees_with_history_formulation(seed, L, E, tmax, window, admit, seeded
         assert ta["stamps"].tolist() == b.stamps()
         assert a.last_log().tolist() == b.last_log
         assert [tuple(r) for r in a.last_admissions().tolist()] == b.last_admissions
-        # invariants: the table is a bijection onto used slots, stamps never
-        # run ahead of the clock, hits + misses = picks, two misses per admission
-        for layer in range(L):
-            res = {e: s for e, s in enumerate(ta["table"][layer]) if s >= 0}
+        # invariants: the table is a bijection onto the used slots of each
+        # pool, owners agree with it, stamps never run ahead of the clock,
+        # hits + misses = picks, two misses per admission
+        for g in range(1 if pool == "global" else L):
+            layers = range(L) if pool == "global" else [g]
+            res = {(layer, e): s for layer in layers for e, s in enumerate(ta["table"][layer]) if s >= 0}
             assert len(set(res.values())) == len(res) <= S
-            assert all(ta["owner"][layer][s] == e for e, s in res.items())
-            assert all(o == -1 or ta["table"][layer][o] >= 0 for o in ta["owner"][layer])
+            assert all(ta["owner_layer"][g][s] == layer and ta["owner"][g][s] == e for (layer, e), s in res.items())
+            assert all(o == -1 or ta["table"][ol][o] >= 0 for ol, o in zip(ta["owner_layer"][g], ta["owner"][g]))
         assert ta["stamps"].size == 0 or ta["stamps"].max() < a.clock
         T = max(len(ids) for _, ids in step)
         assert sa["hits"] + sa["misses"] == sum(len(ids) for _, ids in step) * k
@@ -212,3 +215,60 @@ def test_rotation_moves_the_hot_set():
     # the frequency table is drawn from the epoch-0 popularity
     f = frequency_table(wl)[0]
     assert f.sum() == 1024 * 8 and int(np.argmax(f)) == int(rank_permutation(wl, 0, 0)[0])
+
+
+def test_global_pool_seeds_across_layers():
+    # counts: (1,1)=9 first, then the 5s by layer, then expert: (0,0), (0,2); (1,0) misses out
+    pol = oracle.Policy(2, 3, 3, 1, pool="global")
+    pol.seed(np.array([[5, 1, 5], [5, 9, 0]], np.uint32))
+    t = pol.tables()
+    assert t["table"].tolist() == [[1, -1, 2], [-1, 0, -1]]
+    assert t["owner_layer"].tolist() == [[1, 0, 0]] and t["owner"].tolist() == [[1, 0, 2]]
+
+
+def test_global_pool_evicts_across_layers():
+    pol = oracle.Policy(2, 3, 3, 1, pool="global")
+    pol.seed(np.array([[5, 1, 5], [5, 9, 0]], np.uint32))
+    # t=1: layer 0 hits (0,2) in slot 2; layer 1 misses expert 2 (remembered)
+    pol.forward(0, [[2]])
+    pol.forward(1, [[2]])
+    assert pol.step() == dict(hits=1, misses=1, admissions=0, evictions=0, tokens=1)
+    # t=2: same picks; (1,2) misses again inside the window and is admitted.
+    # slots 0 and 1 were never used (stamp 0): the tie goes to the higher
+    # index, slot 1, whose owner is layer 0's expert 0
+    pol.forward(0, [[2]])
+    pol.forward(1, [[2]])
+    assert pol.step() == dict(hits=1, misses=1, admissions=1, evictions=1, tokens=1)
+    t = pol.tables()
+    assert t["table"].tolist() == [[-1, -1, 2], [-1, 0, 1]]
+    assert t["stamps"].tolist() == [[0, 2, 2]]
+    assert pol.last_admissions().tolist() == [[1, 2, 1, 0, 0]]
+    # with a pool per layer the same trace evicts inside layer 1 instead
+    per = oracle.Policy(2, 3, 2, 1)
+    per.seed(np.array([[5, 1, 5], [5, 9, 0]], np.uint32))
+    for _ in range(2):
+        per.forward(0, [[2]])
+        per.forward(1, [[2]])
+        per.step()
+    assert per.last_admissions().tolist() == [[1, 2, 1, 1, 0]]
+
+
+@settings(max_examples=25, deadline=None)
+@given(seed=st.integers(0, 2**31 - 1), E=st.integers(2, 10), window=st.sampled_from([2, 64]))
+def test_global_pool_of_one_layer_is_the_layer_pool(seed, E, window):
+    rng = np.random.default_rng(seed)
+    k = int(rng.integers(1, E + 1))
+    S = int(rng.integers(0, E + 1))
+    freq = rng.integers(0, 5, size=(1, E)).astype(np.uint32)
+    a = oracle.Policy(1, E, S, k, window=window, pool="global")
+    b = oracle.Policy(1, E, S, k, window=window)
+    a.seed(freq)
+    b.seed(freq)
+    for step in _random_trace(rng, 1, E, k, 25, 3):
+        for layer, ids in step:
+            a.forward(layer, np.array(ids, np.int32))
+            b.forward(layer, np.array(ids, np.int32))
+        assert a.step() == b.step()
+        ta, tb = a.tables(), b.tables()
+        assert ta["table"].tolist() == tb["table"].tolist() and ta["stamps"].tolist() == tb["stamps"].tolist()
+        assert a.last_log().tolist() == b.last_log().tolist()
