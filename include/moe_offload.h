@@ -71,6 +71,14 @@ extern "C" {
 #define MOE_HOST_COHERENT     0 /* hipHostMalloc default: fine-grained      */
 #define MOE_HOST_NONCOHERENT  1 /* hipHostMallocNonCoherent: GPU may cache  */
 
+/* Pool partition (moe_config.pool_mode). */
+#define MOE_POOL_PER_LAYER    0 /* S slots for each layer                     */
+#define MOE_POOL_GLOBAL       1 /* one pool of S slots all layers draw from
+                                   ([FORK] "How it works": one global pool of
+                                   expert blocks instead of a fixed reserve per
+                                   layer); the victim is the pool's lowest free
+                                   slot, else its smallest stamp              */
+
 typedef struct moe_ctx moe_ctx;
 
 typedef struct {
@@ -82,7 +90,9 @@ typedef struct {
   int32_t quant;           /* MOE_Q4_32_F16                                   */
   int64_t pool_budget_bytes; /* >= 0: HBM pool budget; < 0: free HBM at create
                                 time minus reserve_bytes. Slots per layer
-                                S = min(E, budget / (L * expert_bytes)).      */
+                                S = min(E, budget / (L * expert_bytes)); with
+                                MOE_POOL_GLOBAL, slots of the one pool
+                                S = min(L * E, budget / expert_bytes).        */
   int64_t reserve_bytes;   /* HBM left free when pool_budget_bytes < 0        */
   int32_t window_tokens;   /* admission window in tokens (64 in [FORK])       */
   int32_t admit_misses;    /* 2: admit on the 2nd miss inside the window
@@ -110,12 +120,14 @@ typedef struct {
                               Same bytes, same decisions; applies to forwards
                               that route inside the gate/up GEMV (logits
                               given, E <= 512), others copy from pinned.     */
+  int32_t pool_mode;       /* MOE_POOL_PER_LAYER (0) or MOE_POOL_GLOBAL       */
 } moe_config;
 
 typedef struct {
-  int64_t slots_per_layer;    /* S                                            */
+  int64_t slots_per_layer;    /* S: slots of the pool a layer draws from (with
+                                 MOE_POOL_GLOBAL the one pool all share)      */
   int64_t expert_bytes;       /* bytes of gate+up+down of one expert          */
-  int64_t pool_bytes;         /* HBM pool size, L * S * expert_bytes          */
+  int64_t pool_bytes;         /* HBM pool size: L (or 1) * S * expert_bytes   */
   int64_t host_bytes;         /* pinned arena size, host_sets*E*expert_bytes  */
   int64_t staging_experts;    /* HBM blocks lent to a prefill pass            */
   int64_t clock;              /* token clock of the next step (starts at 1)   */
@@ -248,9 +260,11 @@ MOE_API int moe_profile(moe_ctx* ctx, int32_t enable, moe_profile_stats* out);
 
 /* Introspection (host outputs; each synchronises the stream). */
 MOE_API int moe_get_info(moe_ctx* ctx, moe_info* out);
-/* int32 [E]: slot of each expert of the layer, -1 when not resident. */
+/* int32 [E]: slot of each expert of the layer in the pool the layer draws
+ * from, -1 when not resident. */
 MOE_API int moe_get_slot_table(moe_ctx* ctx, int32_t layer, int32_t* out);
-/* uint32 [S]: use-stamps of the layer's slots. */
+/* uint32 [S]: use-stamps of the slots of the pool the layer draws from
+ * (with MOE_POOL_GLOBAL the same S stamps for every layer). */
 MOE_API int moe_get_stamps(moe_ctx* ctx, int32_t layer, uint32_t* out);
 /* uint64: the miss log of the last closed step, ascending; *n = its length.
  * Writes min(cap, n) entries. */

@@ -27,6 +27,8 @@ MOE_Q4_32_F16 = 1
 MOE_ACCUMULATE = 1
 MOE_HOST_COHERENT = 0
 MOE_HOST_NONCOHERENT = 1
+MOE_POOL_PER_LAYER = 0
+MOE_POOL_GLOBAL = 1
 
 EXPORTED = [
     "moe_expert_bytes", "moe_create", "moe_destroy", "moe_register_layer", "moe_register_router", "moe_seed",
@@ -41,7 +43,7 @@ class moe_config(C.Structure):
         ("ffn", C.c_int32), ("quant", C.c_int32), ("pool_budget_bytes", C.c_int64), ("reserve_bytes", C.c_int64),
         ("window_tokens", C.c_int32), ("admit_misses", C.c_int32), ("max_batch_tokens", C.c_int32),
         ("max_prefill_tokens", C.c_int32), ("device", C.c_int32), ("host_alloc", C.c_int32),
-        ("host_sets", C.c_int32), ("stream", C.c_void_p), ("capture_picks", C.c_int32),
+        ("host_sets", C.c_int32), ("stream", C.c_void_p), ("capture_picks", C.c_int32), ("pool_mode", C.c_int32),
     ]
 
 
@@ -140,12 +142,13 @@ def moe_expert_bytes(hidden: int, ffn: int) -> int:
 
 def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reserve_bytes=0, window_tokens=64,
                admit_misses=2, max_batch_tokens=64, max_prefill_tokens=0, device=0, host_alloc=MOE_HOST_COHERENT,
-               host_sets=0, stream=None, capture_picks=None):
+               host_sets=0, stream=None, capture_picks=None, pool_mode=0):
     """Returns an opaque context handle.
 
     stream: a torch.cuda.Stream, a raw hipStream_t int, or None for torch's
     current stream on the device (0, the null stream, is a valid handle).
     capture_picks: None for top_k (one token's picks per layer), 0 for off.
+    pool_mode: MOE_POOL_PER_LAYER (slots per layer) or MOE_POOL_GLOBAL (one pool for all layers).
     """
     if capture_picks is None:
         capture_picks = top_k
@@ -162,7 +165,7 @@ def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reser
         stream = stream.cuda_stream
     cfg = moe_config(n_layers, n_experts, top_k, hidden, ffn, MOE_Q4_32_F16, pool_budget_bytes, reserve_bytes,
                      window_tokens, admit_misses, max_batch_tokens, max_prefill_tokens, device, host_alloc,
-                     host_sets, stream, capture_picks)
+                     host_sets, stream, capture_picks, pool_mode)
     out = C.c_void_p()
     rc = lib().moe_create(C.byref(cfg), C.byref(out))
     if rc != MOE_OK:

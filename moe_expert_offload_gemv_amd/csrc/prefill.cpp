@@ -103,10 +103,12 @@ int moe_prefill_alloc(moe_ctx* c) {
 }
 
 // HBM blocks lent to a prompt pass for the touched experts that are not
-// resident: E - S of them hold every expert a pass can miss.
+// resident: E - S of them hold every expert a pass can miss (E with one
+// global pool, which may hold none of a layer's experts).
 int moe_prefill_alloc_staging(moe_ctx* c) {
   if (c->cfg.max_prefill_tokens <= 0) return MOE_OK;
-  c->n_staging = std::max<int64_t>(0, (int64_t)c->E - c->S);
+  // with one global pool a layer may have none of its experts resident
+  c->n_staging = c->groups == 1 && c->L > 1 ? (int64_t)c->E : std::max<int64_t>(0, (int64_t)c->E - c->S);
   return moe_ctx_dev_alloc(c, (void**)&c->staging, (size_t)(c->n_staging * c->B), "prefill staging blocks");
 }
 
@@ -163,7 +165,7 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
     if (m > 0) {
       const int32_t slot = c->tbl[(int64_t)layer * E + e];
       if (slot >= 0) {
-        p->h_eaddr[e] = c->pool + ((int64_t)layer * S + slot) * c->B;
+        p->h_eaddr[e] = c->pool + (c->group_of(layer) * S + slot) * c->B;
       } else if (staged < c->n_staging) {
         uint8_t* blk = c->staging + staged * c->B;
         PF_HIP(c, hipMemcpyAsync(blk, c->host_layers[layer] + (int64_t)e * c->B, c->B, hipMemcpyHostToDevice, s));

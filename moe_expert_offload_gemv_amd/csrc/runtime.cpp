@@ -166,6 +166,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
       k.quant != MOE_Q4_32_F16 || k.window_tokens < 1 || (k.admit_misses != 1 && k.admit_misses != 2) ||
       k.max_batch_tokens < 1 || k.max_batch_tokens > 256 || k.max_prefill_tokens < 0 || k.n_layers > (1 << 20) ||
       k.capture_picks < 0 || k.capture_picks > k.max_batch_tokens * k.top_k ||
+      (k.pool_mode != MOE_POOL_PER_LAYER && k.pool_mode != MOE_POOL_GLOBAL) ||
       (k.host_alloc != MOE_HOST_COHERENT && k.host_alloc != MOE_HOST_NONCOHERENT))
     return g_create_error = "config field out of range", MOE_E_INVAL;
   moe::GemvShape s1, s2;
@@ -234,20 +235,22 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
        (rc = moe_ctx_host_alloc(c, (void**)&c->h_last_miss, sizeof(uint32_t) * L * E, pin, "last-miss staging"))))
     return fail(rc);
 
-  // HBM pool: S slots per layer
+  // HBM pool: S slots per layer, or one pool of S slots for every layer
   int64_t budget = k.pool_budget_bytes;
   if (budget < 0) {
     size_t fr = 0, tot = 0;
     if (hipMemGetInfo(&fr, &tot) != hipSuccess) return fail(moe_ctx_fail(c, MOE_E_HIP, "hipMemGetInfo failed"));
     budget = std::max<int64_t>(0, (int64_t)fr - k.reserve_bytes);
   }
-  c->S = (int32_t)std::min<int64_t>(E, budget / (L * c->B));
-  const int64_t S = c->S;
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->pool, (size_t)(L * S * c->B), "expert pool"))) return fail(rc);
+  c->groups = k.pool_mode == MOE_POOL_GLOBAL ? 1 : (int32_t)L;
+  c->S = (int32_t)(k.pool_mode == MOE_POOL_GLOBAL ? std::min<int64_t>(L * E, budget / c->B)
+                                                  : std::min<int64_t>(E, budget / (L * c->B)));
+  const int64_t S = c->S, G = c->groups;
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->pool, (size_t)(G * S * c->B), "expert pool"))) return fail(rc);
   if ((rc = moe_prefill_alloc_staging(c))) return fail(rc);
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_stamps, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), "stamps")))
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_stamps, sizeof(uint32_t) * G * std::max<int64_t>(S, 1), "stamps")))
     return fail(rc);
-  if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_stamps, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), pin,
+  if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_stamps, sizeof(uint32_t) * G * std::max<int64_t>(S, 1), pin,
                                "stamp staging")))
     return fail(rc);
 
@@ -277,8 +280,8 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->routers.assign(L, nullptr);
   c->registered.assign(c->host_sets, 0);
   c->tbl.assign(L * E, -1);
-  c->owner.assign(L * std::max<int64_t>(S, 1), -1);
-  c->stamps.assign(L * std::max<int64_t>(S, 1), 0);
+  c->owner.assign(G * std::max<int64_t>(S, 1), -1);
+  c->stamps.assign(G * std::max<int64_t>(S, 1), 0);
   c->last_miss.assign(L * E, 0);
   c->cap_of.assign(L * E, -1);
   if (c->d_cap_tag && hipMemset(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride) != hipSuccess)
@@ -287,7 +290,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if (hipMemset(c->d_tbl, 0xff, sizeof(int32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_counts, 0, sizeof(uint32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride) != hipSuccess) return fail(MOE_E_HIP);
-  if (hipMemset(c->d_stamps, 0, sizeof(uint32_t) * L * std::max<int64_t>(S, 1)) != hipSuccess)
+  if (hipMemset(c->d_stamps, 0, sizeof(uint32_t) * G * std::max<int64_t>(S, 1)) != hipSuccess)
     return fail(MOE_E_HIP);
   Ctrl z{1, 0, {0, 0}};
   if (hipMemcpy(c->d_ctrl, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return fail(MOE_E_HIP);
@@ -362,23 +365,25 @@ extern "C" int moe_seed(moe_ctx* c, const uint32_t* freq) {
   std::fill(c->last_miss.begin(), c->last_miss.end(), 0u);
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   if (freq) {
-    std::vector<int32_t> order(E);
-    for (int64_t l = 0; l < L; ++l) {
-      for (int64_t e = 0; e < E; ++e) order[e] = (int32_t)e;
-      const uint32_t* f = freq + l * E;
-      std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return f[a] > f[b]; });
-      for (int64_t s = 0; s < S; ++s) {
-        const int32_t e = order[s];
-        c->tbl[l * E + e] = (int32_t)s;
-        c->owner[l * S + s] = e;
-        HIP_TRY(c, hipMemcpyAsync(c->pool + (l * S + s) * c->B, c->host_layers[l] + (int64_t)e * c->B, c->B,
-                                  hipMemcpyHostToDevice, c->stream));
+    // each pool takes its candidates (the layer's experts, or every layer's
+    // with one global pool) by count, descending; ties keep (layer, expert) order
+    const int64_t per = c->groups == 1 ? L * E : E;
+    std::vector<int32_t> order(per);
+    for (int64_t g = 0; g < c->groups; ++g) {
+      for (int64_t i = 0; i < per; ++i) order[i] = (int32_t)(g * E + i);  // layer * E + expert
+      std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return freq[a] > freq[b]; });
+      for (int64_t s = 0; s < std::min(S, per); ++s) {
+        const int32_t te = order[s];
+        c->tbl[te] = (int32_t)s;
+        c->owner[g * S + s] = te;
+        HIP_TRY(c, hipMemcpyAsync(c->pool + (g * S + s) * c->B, c->host_layers[te / E] + (int64_t)(te % E) * c->B,
+                                  c->B, hipMemcpyHostToDevice, c->stream));
       }
     }
   }
   std::memcpy(c->h_tbl, c->tbl.data(), sizeof(int32_t) * L * E);
   HIP_TRY(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * L * E, hipMemcpyHostToDevice, c->stream));
-  HIP_TRY(c, hipMemsetAsync(c->d_stamps, 0, sizeof(uint32_t) * L * std::max<int64_t>(S, 1), c->stream));
+  HIP_TRY(c, hipMemsetAsync(c->d_stamps, 0, sizeof(uint32_t) * c->groups * std::max<int64_t>(S, 1), c->stream));
   HIP_TRY(c, hipMemsetAsync(c->d_counts, 0, sizeof(uint32_t) * L * E, c->stream));
   HIP_TRY(c, hipMemsetAsync(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride, c->stream));
   if (c->d_cap_tag) HIP_TRY(c, hipMemsetAsync(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride, c->stream));
@@ -433,11 +438,11 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   ra.wr = (const float*)c->routers[layer];
   ra.T = n_tokens, ra.E = c->E, ra.k = c->k, ra.H = c->H, ra.S = c->S, ra.layer = layer;
   ra.tbl = c->d_tbl + (int64_t)layer * c->E;
-  ra.stamps = c->d_stamps + (int64_t)layer * std::max(c->S, 1);
+  ra.stamps = c->d_stamps + c->group_of(layer) * std::max(c->S, 1);
   ra.counts = c->d_counts + (int64_t)layer * c->E;
   ra.records = c->d_records + (int64_t)layer * c->rec_stride;
   ra.ctrl = c->d_ctrl;
-  ra.pool = c->pool + (int64_t)layer * c->S * c->B;
+  ra.pool = c->pool + c->group_of(layer) * c->S * c->B;
   ra.host = c->host_layers_dev[layer];
   ra.expert_bytes = c->B;
   ra.ids = c->d_ids, ra.w = c->d_w, ra.addr = c->d_addr, ra.kind = c->d_kind;
@@ -554,14 +559,15 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
   HIP_TRY(c, hipMemcpyAsync(c->h_ctrl, c->d_ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost, c->stream));
   HIP_TRY(c, hipMemcpyAsync(c->h_records, c->d_records, sizeof(uint64_t) * L * c->rec_stride, hipMemcpyDeviceToHost,
                             c->stream));
+  const int64_t GS = (int64_t)c->groups * S;  // slots of every pool
   if (S > 0)
-    HIP_TRY(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * L * S, hipMemcpyDeviceToHost, c->stream));
+    HIP_TRY(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * GS, hipMemcpyDeviceToHost, c->stream));
   if (c->d_cap_tag)
     HIP_TRY(c, hipMemcpyAsync(c->h_cap_tag, c->d_cap_tag, sizeof(uint32_t) * L * c->rec_stride, hipMemcpyDeviceToHost,
                               c->stream));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   const Ctrl st = *c->h_ctrl;
-  if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * L * S);
+  if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * GS);
   // records of this step carry clocks in [clock, clock + step tokens); older ones are stale
   int64_t hits = 0;
   c->last_log.clear();
@@ -614,28 +620,30 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
       if (!admit) c->last_miss[te] = t;
     }
     if (!admit || S == 0) continue;
-    // victim: lowest free slot, else the smallest stamp (ties: highest slot)
+    // victim in the layer's pool: lowest free slot, else the smallest stamp
+    // (ties: highest slot); with one global pool the owner may be any layer's
+    const int64_t g0 = c->group_of(l) * S;
     int64_t v = -1;
     for (int64_t s = 0; s < S; ++s)
-      if (c->owner[l * S + s] < 0) {
+      if (c->owner[g0 + s] < 0) {
         v = s;
         break;
       }
     if (v < 0) {
       uint32_t best = 0xffffffffu;
       for (int64_t s = 0; s < S; ++s)
-        if (c->stamps[l * S + s] <= best) best = c->stamps[l * S + s], v = s;
-      const int32_t old = c->owner[l * S + v];
-      c->tbl[l * E + old] = -1;
-      c->last_miss[l * E + old] = 0;
+        if (c->stamps[g0 + s] <= best) best = c->stamps[g0 + s], v = s;
+      const int32_t old = c->owner[g0 + v];  // layer * E + expert
+      c->tbl[old] = -1;
+      c->last_miss[old] = 0;
       ++evictions;
     }
-    c->owner[l * S + v] = (int32_t)e;
+    c->owner[g0 + v] = (int32_t)te;
     c->tbl[te] = (int32_t)v;
-    c->stamps[l * S + v] = t;
+    c->stamps[g0 + v] = t;
     c->last_miss[te] = 0;
     ++admissions;
-    uint8_t* dst = c->pool + (l * S + v) * B;
+    uint8_t* dst = c->pool + (g0 + v) * B;
     if (c->cap_of[te] >= 0) {
       HIP_TRY(c, hipMemcpyAsync(dst, c->d_capture + (l * c->capture_picks + c->cap_of[te]) * B, B,
                                 hipMemcpyDeviceToDevice, c->stream));
@@ -653,8 +661,8 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
   if (admissions > 0) {
     std::memcpy(c->h_tbl, c->tbl.data(), sizeof(int32_t) * L * E);
     HIP_TRY(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * L * E, hipMemcpyHostToDevice, c->stream));
-    std::memcpy(c->h_stamps, c->stamps.data(), sizeof(uint32_t) * L * S);
-    HIP_TRY(c, hipMemcpyAsync(c->d_stamps, c->h_stamps, sizeof(uint32_t) * L * S, hipMemcpyHostToDevice,
+    std::memcpy(c->h_stamps, c->stamps.data(), sizeof(uint32_t) * GS);
+    HIP_TRY(c, hipMemcpyAsync(c->d_stamps, c->h_stamps, sizeof(uint32_t) * GS, hipMemcpyHostToDevice,
                               c->stream));
   }
   c->clock += st.step_tokens;
@@ -684,7 +692,7 @@ extern "C" int moe_get_info(moe_ctx* c, moe_info* out) {
   if (!c || !out) return MOE_E_INVAL;
   out->slots_per_layer = c->S;
   out->expert_bytes = c->B;
-  out->pool_bytes = (int64_t)c->L * c->S * c->B;
+  out->pool_bytes = (int64_t)c->groups * c->S * c->B;
   out->host_bytes = (int64_t)c->host_sets * c->E * c->B;
   out->staging_experts = c->n_staging;
   out->clock = c->clock;
@@ -705,7 +713,7 @@ extern "C" int moe_get_stamps(moe_ctx* c, int32_t layer, uint32_t* out) {
   if (c->S == 0) return MOE_OK;
   DeviceGuard g(c->device);
   HIP_TRY(c, hipStreamSynchronize(c->stream));
-  HIP_TRY(c, hipMemcpy(out, c->d_stamps + (int64_t)layer * c->S, sizeof(uint32_t) * c->S, hipMemcpyDeviceToHost));
+  HIP_TRY(c, hipMemcpy(out, c->d_stamps + c->group_of(layer) * c->S, sizeof(uint32_t) * c->S, hipMemcpyDeviceToHost));
   return MOE_OK;
 }
 

@@ -17,7 +17,10 @@ enum { kRoute = 0, kHotGateUp, kHotDown, kColdGateUp, kColdDownCombine, kTimedKe
 struct moe_ctx {
   moe_config cfg{};
   int device = 0;
-  int32_t L = 0, E = 0, k = 0, H = 0, F = 0, S = 0;
+  int32_t L = 0, E = 0, k = 0, H = 0, F = 0;
+  int32_t S = 0;       // slots of one pool
+  int32_t groups = 0;  // pools: L (a pool per layer) or 1 (one global pool)
+  int64_t group_of(int64_t layer) const { return groups == 1 ? 0 : layer; }
   moe::ExpertLayout lay{};
   int64_t B = 0;
   hipStream_t stream = nullptr;  // caller's stream (nullptr: the null stream)
@@ -63,7 +66,7 @@ struct moe_ctx {
   std::vector<hipEvent_t> prefill_events;  // timing of the two grouped GEMMs
 
   // host mirror of the cache state
-  std::vector<int32_t> tbl, owner;
+  std::vector<int32_t> tbl, owner;   // tbl [L][E] slot; owner [groups][S] layer * E + expert or -1
   std::vector<uint32_t> stamps, last_miss;
   std::vector<uint64_t> last_log;
   std::vector<int32_t> cap_of;         // [L][E] captured pick of the expert in the step, or -1

@@ -23,23 +23,27 @@ class Decode:
     """A context with every layer of a workload registered.
 
     seed=True seeds from the workload's frequency table, False starts cold
-    (moe_seed with no table), None leaves the context unseeded.
+    (moe_seed with no table), None leaves the context unseeded. pool="global"
+    makes one pool of `slots` slots shared by every layer.
     """
 
     def __init__(self, wl: Workload, slots: int | None = None, seed=True, max_batch: int | None = None,
                  host_alloc: int = moe.MOE_HOST_COHERENT, stream=None, max_prefill: int = 0, keep_weights=True,
-                 capture_picks=None):
+                 capture_picks=None, pool="layer"):
         import torch
 
         self.wl = wl
         self.S = wl.slots if slots is None else slots
         self.B = wl.expert_bytes
         self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self.pool = pool
+        budget = (1 if pool == "global" else wl.n_layers) * self.S * self.B
         self.ctx = moe.moe_create(wl.n_layers, wl.n_experts, wl.top_k, wl.hidden, wl.ffn,
-                                  pool_budget_bytes=wl.n_layers * self.S * self.B, window_tokens=wl.window,
+                                  pool_budget_bytes=budget, window_tokens=wl.window,
                                   admit_misses=wl.admit_misses, max_batch_tokens=max_batch or max(wl.tokens, 1),
                                   max_prefill_tokens=max_prefill, host_alloc=host_alloc,
-                                  host_sets=wl.distinct_layers, stream=self.stream, capture_picks=capture_picks)
+                                  host_sets=wl.distinct_layers, stream=self.stream, capture_picks=capture_picks,
+                                  pool_mode=moe.MOE_POOL_GLOBAL if pool == "global" else moe.MOE_POOL_PER_LAYER)
         info = moe.moe_get_info(self.ctx)
         assert info["slots_per_layer"] == self.S, info
         self.weights = {}
@@ -71,8 +75,9 @@ class Decode:
             pass
 
 
-def oracle_policy(wl: Workload, slots: int, seed: bool = True):
-    pol = oracle.Policy(wl.n_layers, wl.n_experts, slots, wl.top_k, window=wl.window, admit_misses=wl.admit_misses)
+def oracle_policy(wl: Workload, slots: int, seed: bool = True, pool: str = "layer"):
+    pol = oracle.Policy(wl.n_layers, wl.n_experts, slots, wl.top_k, window=wl.window, admit_misses=wl.admit_misses,
+                        pool=pool)
     pol.seed(frequency_table(wl) if seed else None)
     return pol
 

@@ -49,3 +49,32 @@ def test_create_rejects_bad_config_without_touching_a_gpu():
         moe.moe_create(n_layers=1, n_experts=8, top_k=2, hidden=100, ffn=512, pool_budget_bytes=0)
     with pytest.raises(moe.MoeError):
         moe.moe_create(n_layers=1, n_experts=5000, top_k=2, hidden=256, ffn=512, pool_budget_bytes=0)
+
+
+def test_binding_constants_match_the_header():
+    txt = open(HEADER).read()
+    defines = dict(re.findall(r"^#define\s+(MOE_\w+)\s+(-?\d+)", txt, flags=re.M))
+    assert defines, "no constants found"
+    for name, value in defines.items():
+        assert getattr(moe, name) == int(value), name
+
+
+def _struct_fields(name):
+    txt = open(HEADER).read()
+    body = re.search(r"typedef struct \{([^{}]*)\}\s*" + name + r";", txt).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return re.findall(r"\b(\w+)\s*;", body)
+
+
+@pytest.mark.parametrize("name", ["moe_config", "moe_info", "moe_step_stats", "moe_profile_stats"])
+def test_binding_structs_mirror_the_header(name):
+    assert [f for f, _ in getattr(moe, name)._fields_] == _struct_fields(name)
+
+
+def test_create_rejects_bad_pool_mode_and_capture():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_create(n_layers=1, n_experts=8, top_k=2, hidden=256, ffn=512, pool_budget_bytes=0, pool_mode=7)
+    assert ei.value.code == moe.MOE_E_INVAL
+    with pytest.raises(moe.MoeError):
+        moe.moe_create(n_layers=1, n_experts=8, top_k=2, hidden=256, ffn=512, pool_budget_bytes=0,
+                       max_batch_tokens=1, capture_picks=3)

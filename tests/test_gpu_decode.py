@@ -30,14 +30,15 @@ def _compare_policy(d: Decode, pol, st_gpu, st_orc, layers):
     tabs = pol.tables()
     for layer in layers:
         assert np.array_equal(moe.moe_get_slot_table(d.ctx, layer, wl.n_experts), tabs["table"][layer]), layer
-        assert np.array_equal(moe.moe_get_stamps(d.ctx, layer, d.S), tabs["stamps"][layer]), layer
+        group = 0 if d.pool == "global" else layer
+        assert np.array_equal(moe.moe_get_stamps(d.ctx, layer, d.S), tabs["stamps"][group]), layer
     assert np.array_equal(moe.moe_get_miss_log(d.ctx), pol.last_log())
 
 
 def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_alloc=moe.MOE_HOST_COHERENT,
-                capture_picks=None, copies=None):
-    d = Decode(wl, slots=slots, seed=seed, host_alloc=host_alloc, capture_picks=capture_picks)
-    pol = oracle_policy(wl, slots, seed=seed)
+                capture_picks=None, copies=None, pool="layer"):
+    d = Decode(wl, slots=slots, seed=seed, host_alloc=host_alloc, capture_picks=capture_picks, pool=pool)
+    pol = oracle_policy(wl, slots, seed=seed, pool=pool)
     logits = zipf_logits(wl)
     L, T, k, H = wl.n_layers, wl.tokens, wl.top_k, wl.hidden
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
@@ -320,3 +321,19 @@ def test_kernel_timing_hook():
     assert rc == moe.MOE_E_CAPTURING
     d2.close()
     d.close()
+
+
+def test_global_pool_bit_exact_policy():
+    # one pool of 104 slots (the memory of 26 per layer) shared by the 4 layers:
+    # admissions evict whichever layer's expert holds the oldest stamp
+    copies = {}
+    worst = _run_decode(REDUCED.with_(name="decode-e64k8-h2048f1024-l4-b1-global"), slots=104, check_every=5,
+                        pool="global", copies=copies)
+    print("worst token error", worst, "promotion bytes", copies)
+    assert copies["copied"] > 0 and copies["pcie"] == 0
+
+
+def test_global_pool_cold_start_batch():
+    wl = Workload("decode-e32k4-h256f512-l3-b2-global", 113, 3, 32, 4, 256, 512, tokens=2, steps=30, zipf_s=1.1,
+                  slots=8, rotation=20)
+    _run_decode(wl, slots=24, check_every=6, seed=False, pool="global")

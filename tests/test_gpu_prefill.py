@@ -18,8 +18,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _prefill_check(wl: Workload, slots: int, sample=None, flags=0):
-    d = Decode(wl, slots=slots, max_batch=1, max_prefill=wl.tokens)
+def _prefill_check(wl: Workload, slots: int, sample=None, flags=0, pool="layer"):
+    d = Decode(wl, slots=slots, max_batch=1, max_prefill=wl.tokens, pool=pool)
     T, H = wl.tokens, wl.hidden
     x32 = activations(wl, 0, tokens=T)
     z = zipf_logits(wl, steps=1, tokens=T)[0, 0]
@@ -42,7 +42,7 @@ def _prefill_check(wl: Workload, slots: int, sample=None, flags=0):
     # policy neutral: tables, stamps, counts, clock untouched
     for layer in range(wl.n_layers):
         assert np.array_equal(moe.moe_get_slot_table(d.ctx, layer, wl.n_experts), tbl0[layer])
-        assert not moe.moe_get_stamps(d.ctx, layer, d.S).any()
+        assert d.S == 0 or not moe.moe_get_stamps(d.ctx, layer, d.S).any()
     assert not moe.moe_get_counts(d.ctx, wl.n_layers, wl.n_experts).any()
     assert moe.moe_get_info(d.ctx)["clock"] == 1
     assert prof["prefill_passes"] == 1 and prof["prefill_pairs"] == T * wl.top_k
@@ -121,3 +121,21 @@ def test_prefill_between_decode_steps_leaves_policy_identical():
         runs.append(out)
         d.close()
     assert runs[0] == runs[1]
+
+
+def test_prefill_with_global_pool():
+    # three layers share 20 slots; layer 2's pass stages whatever the pool lacks
+    wl = Workload("prefill-e16k4-h256f512-t50-global", 206, 3, 16, 4, 256, 512, tokens=50, zipf_s=1.1)
+    d = Decode(wl, slots=20, max_batch=1, max_prefill=wl.tokens, pool="global")
+    x32 = activations(wl, 0, tokens=50)
+    z = zipf_logits(wl, steps=1, tokens=50)[0, 2]
+    y = torch.empty((50, 256), dtype=torch.float32, device="cuda")
+    tbl0 = moe.moe_get_slot_table(d.ctx, 2, 16)
+    moe.moe_prefill(d.ctx, 2, 50, _dev(x32), _dev(z), y)
+    y_ref, _, _ = oracle.moe_layer(16, 4, 256, 512, d.experts(2, oracle.route(z, 4)[0]), x32.astype(np.float64),
+                                   logits=z)
+    assert token_rel_err(y.cpu().numpy(), y_ref) < TOL
+    assert np.array_equal(moe.moe_get_slot_table(d.ctx, 2, 16), tbl0)
+    info = moe.moe_get_info(d.ctx)
+    assert info["slots_per_layer"] == 20 and info["pool_bytes"] == 20 * d.B and info["staging_experts"] == 16
+    d.close()
