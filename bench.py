@@ -42,15 +42,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def setup_ctx(moe, wl, slots, stream, host_alloc, layers=None, progress=True, capture_picks=None):
+def setup_ctx(moe, wl, slots, stream, host_alloc, layers=None, progress=True, capture_picks=None, pool="layer"):
+    """slots per layer; pool="global" gives one pool of the same total size to all layers."""
     from workload import frequency_table, layer_weights
 
     L = wl.n_layers if layers is None else layers
     ctx = moe.moe_create(L, wl.n_experts, wl.top_k, wl.hidden, wl.ffn,
                          pool_budget_bytes=L * slots * wl.expert_bytes, window_tokens=wl.window,
                          admit_misses=wl.admit_misses, max_batch_tokens=wl.tokens, host_alloc=host_alloc,
-                         host_sets=min(wl.weight_layers, L), stream=stream,
-                         capture_picks=capture_picks)
+                         host_sets=min(wl.weight_layers, L), stream=stream, capture_picks=capture_picks,
+                         pool_mode=moe.MOE_POOL_GLOBAL if pool == "global" else moe.MOE_POOL_PER_LAYER)
     buf = None
     t0 = time.time()
     for layer in range(min(wl.weight_layers, L)):  # layer l reads host set l % weight_layers
@@ -179,6 +180,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-side-passes", action="store_true")
+    ap.add_argument("--pool", choices=["layer", "global"], default="layer",
+                    help="slots per layer, or one pool of the same total size shared by all layers")
+    ap.add_argument("--slots", type=int, default=0, help="pool slots per layer (0: the workload's)")
     ap.add_argument("--capture-picks", type=int, default=-1,
                     help="picks per layer whose cold reads are kept for promotion (-1: top_k, 0: off)")
     ap.add_argument("--profile-steps", type=int, default=64, help="steps of the kernel-timing pass")
@@ -226,8 +230,10 @@ def main():
     stream = torch.cuda.Stream()
     t_setup = time.time()
     log(f"creating the context: pinning {wl.weight_layers * E * B / 1e9:.1f} GB of host memory")
+    if args.slots:
+        wl = wl.with_(slots=args.slots)
     ctx, freq = setup_ctx(moe, wl, wl.slots, stream, host_alloc,
-                          capture_picks=None if args.capture_picks < 0 else args.capture_picks)
+                          capture_picks=None if args.capture_picks < 0 else args.capture_picks, pool=args.pool)
     logits_np = zipf_logits(wl)
     logits_all = torch.from_numpy(logits_np).cuda()                       # [steps][L][T][E]
     x_steps = min(wl.steps, 32)
@@ -309,6 +315,7 @@ def main():
                    "tokens_per_step": T, "pool_slots_per_layer": wl.slots, "weights": "q4 blocks (18 B / 32)",
                    "host_alloc": args.host_alloc, "host_weight_sets": wl.weight_layers,
                    "capture_picks": wl.top_k if args.capture_picks < 0 else args.capture_picks,
+                   "pool": args.pool,
                    "launch": "eager" if args.eager else "hip-graph"},
         "effective_weight_GBps": round((acc["hot_bytes"] + acc["cold_bytes"]) / elapsed / 1e9, 2),
         "hot_GBps_over_step": round(acc["hot_bytes"] / elapsed / 1e9, 2),

@@ -64,6 +64,7 @@ class Workload:
     tokens: int              # tokens per decode step, or per prefill pass
     steps: int = 1           # decode steps
     zipf_s: float = 0.0      # 0: logits come from the router instead
+    zipf_s_alt: float = 0.0  # > 0: odd layers use this exponent instead (layers of unequal skew)
     slots: int = 0           # pool slots per layer
     rotation: int = 0        # re-draw the popularity permutation every this many tokens (0: never)
     window: int = 64
@@ -109,6 +110,10 @@ WORKLOADS = {
                  zipf_s=1.0, slots=251, distinct_layers=20),
         Workload("large-e256k8-h4096f1536-t12288", 7, 1, 256, 8, 4096, 1536, tokens=12288, zipf_s=1.0,
                  slots=251, prefill=True),
+        # the decode shape with layers of unequal skew (even layers Zipf 1.4, odd 0.7) and a quarter of
+        # the experts in HBM: where one pool shared by all layers can move slots between layers
+        Workload("decode-e512k8-h2048f1024-l48-b1-mixedzipf", 8, 48, 512, 8, 2048, 1024, tokens=1, steps=256,
+                 zipf_s=1.4, zipf_s_alt=0.7, slots=128, distinct_layers=32),
     ]
 }
 
@@ -216,7 +221,8 @@ def rank_permutation(wl: Workload, layer: int, epoch: int) -> np.ndarray:
 def _epoch_log_popularity(wl: Workload, layer: int, epoch: int) -> np.ndarray:
     """fp64 [E]: ln p(rank(e)) for each expert e in the given epoch."""
     perm = rank_permutation(wl, layer, epoch)
-    logp = np.log(zipf_popularity(wl.n_experts, wl.zipf_s))
+    s = wl.zipf_s_alt if (wl.zipf_s_alt > 0 and layer % 2 == 1) else wl.zipf_s
+    logp = np.log(zipf_popularity(wl.n_experts, s))
     out = np.empty(wl.n_experts, np.float64)
     out[perm] = logp
     return out
