@@ -62,6 +62,8 @@ def lib():
         L.orc_policy_new.argtypes = [C.c_int32] * 6 + [C.c_int64, C.c_int32]
         L.orc_policy_new.restype = C.c_void_p
         L.orc_policy_free.argtypes = [C.c_void_p]
+        L.orc_policy_preheat.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]
+        L.orc_policy_preheat.restype = C.c_int32
         L.orc_policy_seed.argtypes = [C.c_void_p, C.c_void_p]
         L.orc_policy_forward.argtypes = [C.c_void_p, C.c_int32, C.c_int32, _i32p]
         L.orc_policy_forward.restype = C.c_int
@@ -206,6 +208,14 @@ class Policy:
         lib().orc_policy_step(self._p, s)
         return dict(hits=int(s[0]), misses=int(s[1]), admissions=int(s[2]), evictions=int(s[3]),
                     tokens=int(s[4]))
+
+    def preheat(self, layer: int, counts, max_experts: int) -> np.ndarray:
+        """Admit the cold experts a prompt pass of `layer` used (counts [E]: its pairs per expert);
+        returns the admission records int32 [n][5] as last_admissions."""
+        c = _c(counts, np.uint32)
+        out = np.empty((max(min(max_experts, self.S), 1), 5), np.int32)
+        n = lib().orc_policy_preheat(self._p, layer, c.ctypes.data, max_experts, out.ctypes.data)
+        return out[:n]
 
     def tables(self):
         """table [L][E] (slot in the layer's pool, -1 cold); per pool [groups][S]: owner (expert or -1),

@@ -396,6 +396,72 @@ ORC_EXPORT void orc_policy_step(orc_policy* p, int64_t* stats) {
   p->step += 1;
 }
 
+/* Preheat after a prompt pass of one layer (the "llama.cpp: fork with multi
+ * gpu acceleration ..." README, "How it works": after the pass the cache is
+ * refilled with the experts the pass used that were cold). The pass's picks
+ * count as uses at the clock of the next token, c. counts[E] holds the
+ * pass's pairs per expert.
+ * 1. Every resident expert with count > 0 gets stamp max(stamp, c).
+ * 2. Candidates: experts with count > 0 that are not resident, by count
+ *    (descending; ties: lower id). Up to min(max_n, S) of them are admitted,
+ *    each into the layer's pool's lowest free slot, else the slot with the
+ *    smallest stamp below c (ties: highest index), whose owner is evicted
+ *    (table entry and last miss cleared). The new owner's stamp is c and its
+ *    last miss is cleared. Preheat stops when no slot is free or below c: it
+ *    never evicts an expert the pass used or that it just admitted.
+ * Returns the number admitted; out (may be NULL) receives the admission
+ * records as in the cache step.                                             */
+ORC_EXPORT int32_t orc_policy_preheat(orc_policy* p, int32_t layer, const uint32_t* counts, int32_t max_n,
+                                      int32_t* out) {
+  int32_t E = p->E, S = p->S;
+  const uint32_t c = p->clock;
+  const int64_t g0 = (int64_t)(p->global ? 0 : layer) * S;
+  for (int32_t e = 0; e < E; ++e) {
+    int32_t s = p->tbl[(int64_t)layer * E + e];
+    if (counts[e] > 0 && s >= 0 && p->st[g0 + s] < c) p->st[g0 + s] = c;
+  }
+  int32_t limit = max_n < S ? max_n : S;
+  if (limit <= 0) return 0;
+  char* done = (char*)calloc((size_t)E, 1);
+  int32_t n = 0;
+  while (n < limit) {
+    int32_t best = -1;  /* the next candidate: largest count, lowest id */
+    for (int32_t e = 0; e < E; ++e) {
+      if (done[e] || counts[e] == 0 || p->tbl[(int64_t)layer * E + e] >= 0) continue;
+      if (best < 0 || counts[e] > counts[best]) best = e;
+    }
+    if (best < 0) break;
+    done[best] = 1;
+    int32_t victim = -1, evicted = -1;
+    for (int32_t s = 0; s < S; ++s)
+      if (p->own[g0 + s] < 0) {
+        victim = s;
+        break;
+      }
+    if (victim < 0) {
+      for (int32_t s = 0; s < S; ++s)
+        if (p->st[g0 + s] < c && (victim < 0 || p->st[g0 + s] <= p->st[g0 + victim])) victim = s;
+      if (victim < 0) break; /* every slot holds an expert the pass used */
+      evicted = p->own[g0 + victim];
+      p->tbl[evicted] = -1;
+      p->lm[evicted] = 0;
+    }
+    const int64_t te = (int64_t)layer * E + best;
+    p->own[g0 + victim] = (int32_t)te;
+    p->tbl[te] = victim;
+    p->st[g0 + victim] = c;
+    p->lm[te] = 0;
+    if (out) {
+      int32_t* a = out + 5 * n;
+      a[0] = layer, a[1] = best, a[2] = victim;
+      a[3] = evicted < 0 ? -1 : evicted / E, a[4] = evicted < 0 ? -1 : evicted % E;
+    }
+    ++n;
+  }
+  free(done);
+  return n;
+}
+
 /* Accessors (copies into caller buffers). */
 ORC_EXPORT void orc_policy_tables(const orc_policy* p, int32_t* tbl, int32_t* own, uint32_t* st, uint32_t* lm) {
   if (tbl) memcpy(tbl, p->tbl, sizeof(int32_t) * p->L * p->E);

@@ -272,3 +272,45 @@ def test_global_pool_of_one_layer_is_the_layer_pool(seed, E, window):
         ta, tb = a.tables(), b.tables()
         assert ta["table"].tolist() == tb["table"].tolist() and ta["stamps"].tolist() == tb["stamps"].tolist()
         assert a.last_log().tolist() == b.last_log().tolist()
+
+
+def test_preheat_admits_the_cold_experts_a_prompt_used():
+    pol = oracle.Policy(1, 6, 3, 1)
+    pol.seed(np.array([[9, 8, 7, 0, 0, 0]], np.uint32))  # slots: e0 -> 0, e1 -> 1, e2 -> 2
+    pol.forward(0, [[0]])  # t=1: stamp of slot 0 = 1
+    pol.step()             # clock 2
+    # the prompt used e1 (resident) and e3, e4, e5 (cold): e1's stamp rises to 2;
+    # e3 and e4 (3 pairs each, lower id first) take the oldest slots below 2:
+    # slot 2 (e2, stamp 0; ties go to the higher index), then slot 0 (e0, stamp 1)
+    adm = pol.preheat(0, [0, 5, 0, 3, 3, 1], max_experts=2)
+    assert adm.tolist() == [[0, 3, 2, 0, 2], [0, 4, 0, 0, 0]]
+    t = pol.tables()
+    assert t["table"][0].tolist() == [-1, 1, -1, 2, 0, -1]
+    assert t["stamps"][0].tolist() == [2, 2, 2]
+    # no slot left below the clock: e5 is not admitted, nothing the pass used is evicted
+    assert pol.preheat(0, [0, 5, 0, 3, 3, 1], max_experts=5).size == 0
+    assert pol.tables()["table"][0].tolist() == [-1, 1, -1, 2, 0, -1]
+
+
+def test_preheat_fills_free_slots_and_respects_the_limit():
+    pol = oracle.Policy(2, 5, 2, 2)
+    pol.seed(None)  # every slot free
+    adm = pol.preheat(1, [4, 0, 4, 7, 0], max_experts=5)  # at most S = 2: e3, then e0 (tie with e2)
+    assert adm.tolist() == [[1, 3, 0, -1, -1], [1, 0, 1, -1, -1]]
+    t = pol.tables()
+    assert t["table"][1].tolist() == [1, -1, -1, 0, -1] and t["stamps"][1].tolist() == [1, 1]
+    assert (t["table"][0] == -1).all()  # another layer's pool is untouched
+    assert pol.preheat(0, [0, 0, 0, 0, 0], max_experts=5).size == 0
+    # the admitted experts hit on the next step; the stamps then follow the clock
+    pol.forward(1, [[3, 0]])
+    assert pol.step()["hits"] == 2
+
+
+def test_preheat_in_a_global_pool_evicts_unused_layers_first():
+    pol = oracle.Policy(2, 3, 2, 1, pool="global")
+    pol.seed(np.array([[5, 0, 0], [4, 0, 0]], np.uint32))  # slot 0 = (0,0), slot 1 = (1,0)
+    pol.forward(0, [[0]])  # t=1: layer 0's expert stamped
+    pol.step()
+    adm = pol.preheat(1, [0, 2, 0], max_experts=1)  # layer 1's unused (1,0) goes, not layer 0's
+    assert adm.tolist() == [[1, 1, 1, 1, 0]]
+    assert pol.tables()["table"].tolist() == [[0, -1, -1], [-1, 1, -1]]
