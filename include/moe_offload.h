@@ -233,6 +233,23 @@ MOE_API int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
 MOE_API int moe_prefill(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
                 const float* x, const float* logits, float* y, uint32_t flags);
 
+/* Preheat after a prompt pass ([FORK] "How it works": after the pass the
+ * cache is refilled with the cold experts the pass used). layer must be the
+ * layer of the last moe_prefill (else MOE_E_STATE). The pass's picks count as
+ * uses at the clock c of the next token: the layer's resident experts the
+ * pass used get stamp c; the experts it used that are not resident, ordered
+ * by how many of its pairs picked them (descending; ties: lower id), are
+ * admitted into the pool the layer draws from, at most min(max_experts, S),
+ * each into the lowest free slot, else the slot whose owner has the smallest
+ * (pass picks, stamp) (ties: highest index; owners of other layers count 0
+ * picks), provided those picks are fewer than the candidate's; the owner is
+ * evicted and forgets its last miss. The new owner's stamp is c and it
+ * forgets its last miss. Preheat stops at the first candidate that finds no
+ * such slot. Bytes are copied from the staging
+ * blocks the pass filled, else from pinned memory. *admitted (may be NULL)
+ * receives the number admitted. Synchronises the stream; not capturable. */
+MOE_API int moe_preheat(moe_ctx* ctx, int32_t layer, int32_t max_experts, int32_t* admitted);
+
 /* Close the current step ([A6000]: promotion pass between decode steps, never
  * graph-captured). Waits for the stream, reads the miss log, sorts it
  * ascending, and walks it in that order: an entry whose expert became resident

@@ -33,7 +33,7 @@ MOE_POOL_GLOBAL = 1
 EXPORTED = [
     "moe_expert_bytes", "moe_create", "moe_destroy", "moe_register_layer", "moe_register_router", "moe_seed",
     "moe_forward", "moe_prefill", "moe_cache_step", "moe_get_info", "moe_get_slot_table", "moe_get_stamps",
-    "moe_get_miss_log", "moe_get_counts", "moe_last_error", "moe_profile",
+    "moe_get_miss_log", "moe_get_counts", "moe_last_error", "moe_profile", "moe_preheat",
 ]
 
 
@@ -106,6 +106,7 @@ def lib():
             "moe_get_counts": (C.c_int, [vp, vp]),
             "moe_last_error": (C.c_char_p, [vp]),
             "moe_profile": (C.c_int, [vp, i32, C.POINTER(moe_profile_stats)]),
+            "moe_preheat": (C.c_int, [vp, i32, i32, C.POINTER(i32)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -204,6 +205,13 @@ def moe_forward(ctx, layer: int, n_tokens: int, x, logits, y, ids=None, w=None, 
 
 def moe_prefill(ctx, layer: int, n_tokens: int, x, logits, y, flags: int = 0) -> None:
     _check(ctx, lib().moe_prefill(ctx, layer, n_tokens, _dptr(x), _dptr(logits), _dptr(y), flags))
+
+
+def moe_preheat(ctx, layer: int, max_experts: int) -> int:
+    """Admit the cold experts the last prompt pass (of `layer`) used; returns how many were admitted."""
+    n = C.c_int32(0)
+    _check(ctx, lib().moe_preheat(ctx, layer, max_experts, C.byref(n)))
+    return int(n.value)
 
 
 def moe_cache_step(ctx) -> dict:

@@ -40,6 +40,7 @@ bool capturing(hipStream_t s) {
 
 struct Prefill {
   int64_t max_tokens = 0, max_pairs = 0, max_tiles = 0, max_items = 0;
+  int32_t last_layer = -1;      // layer of the last completed pass (h_counts / h_eaddr describe it)
   int32_t* ids = nullptr;       // [P]
   float* w = nullptr;           // [P]
   int32_t* perm = nullptr;      // [P] sorted position -> pair
@@ -229,6 +230,7 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   // 7. weighted combine in pick order
   PF_HIP(c, moe::launch_combine_pairs(p->ypair, p->inv, p->w, T, k, H, y, (flags & MOE_ACCUMULATE) ? 1 : 0, s));
   PF_HIP(c, hipStreamSynchronize(s));  // the pass is over: the staging blocks are free again
+  p->last_layer = layer;
 
   if (ev) {
     float t1 = 0, t2 = 0;
@@ -241,5 +243,91 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
     c->prof.prefill_tiles += n_tiles;
     c->prof.prefill_staged += staged;
   }
+  return MOE_OK;
+}
+
+// Preheat (the "llama.cpp: fork with multi gpu acceleration ..." README, "How
+// it works": after a prompt pass the cache is refilled with the cold experts
+// the pass used). The same rule as the policy simulation: the pass's picks
+// count as uses at the next token's clock c; resident experts it used are
+// stamped c; its cold experts, by pair count (descending, ties: lower id),
+// take free slots or slots stamped below c (smallest stamp, ties: highest
+// index), at most min(max_experts, S). Their bytes come from the staging
+// blocks the pass filled (HBM to HBM), else from pinned memory.
+extern "C" int moe_preheat(moe_ctx* c, int32_t layer, int32_t max_experts, int32_t* admitted) {
+  if (!c) return MOE_E_INVAL;
+  if (admitted) *admitted = 0;
+  Prefill* p = c->pf;
+  if (!p || p->last_layer < 0) return moe_ctx_fail(c, MOE_E_STATE, "preheat: no prompt pass yet");
+  if (layer != p->last_layer)
+    return moe_ctx_fail(c, MOE_E_STATE, "preheat: the last prompt pass was of layer %d, not %d", p->last_layer, layer);
+  if (capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "preheat while capturing");
+  hipStream_t s = c->stream;
+  const int64_t E = c->E, S = c->S, GS = (int64_t)c->groups * S, B = c->B;
+  const int64_t g0 = c->group_of(layer) * S;
+  const uint32_t clk = (uint32_t)c->clock;
+  // the device stamps are current (forwards raise them); start from them
+  if (S > 0) {
+    PF_HIP(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * GS, hipMemcpyDeviceToHost, s));
+    PF_HIP(c, hipStreamSynchronize(s));
+    std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * GS);
+  }
+  const int32_t* cnt = p->h_counts;
+  for (int64_t e = 0; e < E; ++e) {
+    const int32_t slot = c->tbl[layer * E + e];
+    if (cnt[e] > 0 && slot >= 0 && c->stamps[g0 + slot] < clk) c->stamps[g0 + slot] = clk;
+  }
+  const int64_t limit = std::min<int64_t>(max_experts, S);
+  std::vector<int32_t> cand;
+  for (int64_t e = 0; e < E; ++e)
+    if (cnt[e] > 0 && c->tbl[layer * E + e] < 0) cand.push_back((int32_t)e);
+  std::stable_sort(cand.begin(), cand.end(), [&](int32_t a, int32_t b) { return cnt[a] > cnt[b]; });
+  int32_t n = 0;
+  for (size_t i = 0; i < cand.size() && n < limit; ++i) {
+    const int64_t e = cand[i], te = layer * E + e;
+    int64_t v = -1;
+    for (int64_t sl = 0; sl < S; ++sl)
+      if (c->owner[g0 + sl] < 0) {
+        v = sl;
+        break;
+      }
+    if (v < 0) {
+      // victim: the owner with the fewest pass picks (other layers' owners: 0), then the oldest stamp
+      int32_t vc = 0;
+      for (int64_t sl = 0; sl < S; ++sl) {
+        const int32_t o = c->owner[g0 + sl];
+        const int32_t oc = o / E == layer ? cnt[o % E] : 0;
+        if (v < 0 || oc < vc || (oc == vc && c->stamps[g0 + sl] <= c->stamps[g0 + v])) v = sl, vc = oc;
+      }
+      if (vc >= cnt[e]) break;  // every owner was used by the pass at least as often
+      const int32_t old = c->owner[g0 + v];
+      c->tbl[old] = -1;
+      c->last_miss[old] = 0;
+    }
+    c->owner[g0 + v] = (int32_t)te;
+    c->tbl[te] = (int32_t)v;
+    c->stamps[g0 + v] = clk;
+    c->last_miss[te] = 0;
+    const uint8_t* src = p->h_eaddr[e];
+    const bool staged = src >= c->staging && src < c->staging + c->n_staging * B;
+    if (staged)
+      PF_HIP(c, hipMemcpyAsync(c->pool + (g0 + v) * B, src, B, hipMemcpyDeviceToDevice, s));
+    else
+      PF_HIP(c, hipMemcpyAsync(c->pool + (g0 + v) * B, c->host_layers[layer] + e * B, B, hipMemcpyHostToDevice, s));
+    ++n;
+  }
+  // publish: table, stamps, and the last-miss copy the capture decision reads
+  std::memcpy(c->h_tbl, c->tbl.data(), sizeof(int32_t) * c->L * E);
+  PF_HIP(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * c->L * E, hipMemcpyHostToDevice, s));
+  if (S > 0) {
+    std::memcpy(c->h_stamps, c->stamps.data(), sizeof(uint32_t) * GS);
+    PF_HIP(c, hipMemcpyAsync(c->d_stamps, c->h_stamps, sizeof(uint32_t) * GS, hipMemcpyHostToDevice, s));
+  }
+  if (c->d_last_miss) {
+    std::memcpy(c->h_last_miss, c->last_miss.data(), sizeof(uint32_t) * c->L * E);
+    PF_HIP(c, hipMemcpyAsync(c->d_last_miss, c->h_last_miss, sizeof(uint32_t) * c->L * E, hipMemcpyHostToDevice, s));
+  }
+  PF_HIP(c, hipStreamSynchronize(s));  // the staging blocks may be reused by the next pass
+  if (admitted) *admitted = n;
   return MOE_OK;
 }

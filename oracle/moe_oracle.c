@@ -404,11 +404,13 @@ ORC_EXPORT void orc_policy_step(orc_policy* p, int64_t* stats) {
  * 1. Every resident expert with count > 0 gets stamp max(stamp, c).
  * 2. Candidates: experts with count > 0 that are not resident, by count
  *    (descending; ties: lower id). Up to min(max_n, S) of them are admitted,
- *    each into the layer's pool's lowest free slot, else the slot with the
- *    smallest stamp below c (ties: highest index), whose owner is evicted
- *    (table entry and last miss cleared). The new owner's stamp is c and its
- *    last miss is cleared. Preheat stops when no slot is free or below c: it
- *    never evicts an expert the pass used or that it just admitted.
+ *    each into the layer's pool's lowest free slot, else the slot whose
+ *    owner has the smallest (pass count, stamp) (ties: highest index; an
+ *    owner of another layer, in a global pool, has pass count 0) provided
+ *    that count is below the candidate's; the owner is evicted (table entry
+ *    and last miss cleared). The new owner's stamp is c and its last miss is
+ *    cleared. Preheat stops at the first candidate that finds no such slot:
+ *    an expert the pass used is only displaced by one it used more.
  * Returns the number admitted; out (may be NULL) receives the admission
  * records as in the cache step.                                             */
 ORC_EXPORT int32_t orc_policy_preheat(orc_policy* p, int32_t layer, const uint32_t* counts, int32_t max_n,
@@ -439,9 +441,13 @@ ORC_EXPORT int32_t orc_policy_preheat(orc_policy* p, int32_t layer, const uint32
         break;
       }
     if (victim < 0) {
-      for (int32_t s = 0; s < S; ++s)
-        if (p->st[g0 + s] < c && (victim < 0 || p->st[g0 + s] <= p->st[g0 + victim])) victim = s;
-      if (victim < 0) break; /* every slot holds an expert the pass used */
+      uint32_t vc = 0; /* pass count of the victim's owner */
+      for (int32_t s = 0; s < S; ++s) {
+        int32_t o = p->own[g0 + s];
+        uint32_t oc = o / E == layer ? counts[o % E] : 0;
+        if (victim < 0 || oc < vc || (oc == vc && p->st[g0 + s] <= p->st[g0 + victim])) victim = s, vc = oc;
+      }
+      if (vc >= counts[best]) break; /* every owner was used as much as the candidate */
       evicted = p->own[g0 + victim];
       p->tbl[evicted] = -1;
       p->lm[evicted] = 0;

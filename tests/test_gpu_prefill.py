@@ -139,3 +139,54 @@ def test_prefill_with_global_pool():
     info = moe.moe_get_info(d.ctx)
     assert info["slots_per_layer"] == 20 and info["pool_bytes"] == 20 * d.B and info["staging_experts"] == 16
     d.close()
+
+
+@pytest.mark.parametrize("pool", ["layer", "global"])
+def test_preheat_matches_the_oracle_and_serves_decode(pool):
+    from tests._gpu import oracle_policy
+
+    wl = Workload("prefill-e32k4-h256f512-l2-preheat", 207, 2, 32, 4, 256, 512, tokens=2, steps=12, zipf_s=1.1)
+    slots = 8 if pool == "layer" else 16
+    d = Decode(wl, slots=slots, max_batch=2, max_prefill=60, pool=pool)
+    pol = oracle_policy(wl, slots, pool=pool)
+    logits = zipf_logits(wl)
+    y = torch.empty((2, 256), dtype=torch.float32, device="cuda")
+
+    def step(s, check):
+        for layer in range(2):
+            x32 = activations(wl, s, layer=layer)
+            z = logits[s, layer]
+            moe.moe_forward(d.ctx, layer, 2, _dev(x32), _dev(z), y)
+            ids, _ = oracle.route(z, 4)
+            pol.forward(layer, ids)
+            if check:
+                y_ref, _, _ = oracle.moe_layer(32, 4, 256, 512, d.experts(layer, ids), x32.astype(np.float64), logits=z)
+                assert token_rel_err(y.cpu().numpy(), y_ref) < TOL
+        assert moe.moe_cache_step(d.ctx)["admissions"] == pol.step()["admissions"]
+
+    for s in range(4):
+        step(s, check=False)
+    # a 60-token prompt of layer 1, then preheat from its picks
+    zp = zipf_logits(wl.with_(rotation=0), steps=1, tokens=60)[0, 1] * 0.5  # a flatter prompt: more cold experts
+    xp = activations(wl, 0, tokens=60)
+    yp = torch.empty((60, 256), dtype=torch.float32, device="cuda")
+    moe.moe_prefill(d.ctx, 1, 60, _dev(xp), _dev(zp.astype(np.float32)), yp)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_preheat(d.ctx, 0, 5)
+    assert ei.value.code == moe.MOE_E_STATE
+    ids_p, _ = oracle.route(zp.astype(np.float32), 4)
+    counts = np.bincount(ids_p.ravel(), minlength=32)
+    ref = pol.preheat(1, counts, 5)
+    n = moe.moe_preheat(d.ctx, 1, 5)
+    assert n == len(ref) > 0
+    tabs = pol.tables()
+    for layer in range(2):
+        assert np.array_equal(moe.moe_get_slot_table(d.ctx, layer, 32), tabs["table"][layer])
+        g = 0 if pool == "global" else layer
+        assert np.array_equal(moe.moe_get_stamps(d.ctx, layer, slots), tabs["stamps"][g])
+    # decode goes on, reading the preheated experts from their new slots
+    for s in range(4, 12):
+        step(s, check=True)
+        for layer in range(2):
+            assert np.array_equal(moe.moe_get_slot_table(d.ctx, layer, 32), pol.tables()["table"][layer])
+    d.close()

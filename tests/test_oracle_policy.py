@@ -279,17 +279,28 @@ def test_preheat_admits_the_cold_experts_a_prompt_used():
     pol.seed(np.array([[9, 8, 7, 0, 0, 0]], np.uint32))  # slots: e0 -> 0, e1 -> 1, e2 -> 2
     pol.forward(0, [[0]])  # t=1: stamp of slot 0 = 1
     pol.step()             # clock 2
-    # the prompt used e1 (resident) and e3, e4, e5 (cold): e1's stamp rises to 2;
-    # e3 and e4 (3 pairs each, lower id first) take the oldest slots below 2:
-    # slot 2 (e2, stamp 0; ties go to the higher index), then slot 0 (e0, stamp 1)
+    # the prompt used e1 (resident, 5 pairs) and e3, e4, e5 (cold: 3, 3, 1 pairs).
+    # e1's stamp rises to 2. e3 (then e4: ties go to the lower id) displaces the
+    # owner with the smallest (pass count, stamp): e2 (0, 0) in slot 2, then e0 (0, 1)
     adm = pol.preheat(0, [0, 5, 0, 3, 3, 1], max_experts=2)
     assert adm.tolist() == [[0, 3, 2, 0, 2], [0, 4, 0, 0, 0]]
     t = pol.tables()
     assert t["table"][0].tolist() == [-1, 1, -1, 2, 0, -1]
     assert t["stamps"][0].tolist() == [2, 2, 2]
-    # no slot left below the clock: e5 is not admitted, nothing the pass used is evicted
+    # e5 (1 pair) finds only owners used as much or more (3, 5, 3): nothing changes
     assert pol.preheat(0, [0, 5, 0, 3, 3, 1], max_experts=5).size == 0
     assert pol.tables()["table"][0].tolist() == [-1, 1, -1, 2, 0, -1]
+
+
+def test_preheat_lets_a_busier_cold_expert_displace_a_lightly_used_one():
+    pol = oracle.Policy(1, 5, 2, 1)
+    pol.seed(np.array([[3, 2, 0, 0, 0]], np.uint32))  # e0 -> 0, e1 -> 1
+    # the pass used all residents (e0: 1 pair, e1: 6) and the cold e3 (4 pairs):
+    # e3 displaces e0, the owner with the fewest pairs; e4 (2 pairs) cannot
+    # displace e3 (4) or e1 (6)
+    adm = pol.preheat(0, [1, 6, 0, 4, 2], max_experts=3)
+    assert adm.tolist() == [[0, 3, 0, 0, 0]]
+    assert pol.tables()["table"][0].tolist() == [-1, 1, -1, 0, -1]
 
 
 def test_preheat_fills_free_slots_and_respects_the_limit():
