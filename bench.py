@@ -42,14 +42,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def setup_ctx(moe, wl, slots, stream, host_alloc, layers=None, progress=True, capture_picks=None, pool="layer"):
+def setup_ctx(moe, wl, slots, stream, host_alloc, layers=None, progress=True, capture_picks=None, pool="layer",
+              max_prefill_tokens=0):
     """slots per layer; pool="global" gives one pool of the same total size to all layers."""
     from workload import frequency_table, layer_weights
 
     L = wl.n_layers if layers is None else layers
     ctx = moe.moe_create(L, wl.n_experts, wl.top_k, wl.hidden, wl.ffn,
                          pool_budget_bytes=L * slots * wl.expert_bytes, window_tokens=wl.window,
-                         admit_misses=wl.admit_misses, max_batch_tokens=wl.tokens, host_alloc=host_alloc,
+                         admit_misses=wl.admit_misses, max_batch_tokens=wl.tokens,
+                         max_prefill_tokens=max_prefill_tokens, host_alloc=host_alloc,
                          host_sets=min(wl.weight_layers, L), stream=stream, capture_picks=capture_picks,
                          pool_mode=moe.MOE_POOL_GLOBAL if pool == "global" else moe.MOE_POOL_PER_LAYER)
     buf = None
@@ -141,6 +143,66 @@ def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3):
     }
 
 
+def request_pass(moe, torch, ctx, wl, freq, stream, prompt_tokens, decode_tokens, replay, xs, x_all):
+    """A prompt pass through every layer, then decode tokens, without and with preheat.
+
+    The request's expert popularity is the workload's Zipf law over a fresh
+    permutation (epoch 1), which the seeding frequency table (epoch 0) has not
+    seen; prompt and decode are one run of token clocks of that law. Each
+    variant starts from the seeded pool. With preheat, every layer's prompt
+    pass is followed by moe_preheat of that layer (at most the layer's slot
+    share). Decode replays the same forward as the main timed region.
+    """
+    import numpy as np
+
+    from workload import activations, zipf_logits
+
+    P, D, L, E = prompt_tokens, decode_tokens, wl.n_layers, wl.n_experts
+    wr = wl.with_(epoch_base=1)
+    xp = torch.from_numpy(activations(wr, 0, tokens=P)).cuda()  # one prompt input serves every layer
+    yp = torch.empty_like(xp)
+    zp = torch.empty((L, P, E), dtype=torch.float32, device="cuda")
+    zd = torch.empty((D, L, 1, E), dtype=torch.float32, device="cuda")
+    for layer in range(L):
+        lz = zipf_logits(wr, layers=[layer], steps=1, tokens=P + D)[0, 0]
+        zp[layer].copy_(torch.from_numpy(lz[:P]))
+        zd[:, layer, 0].copy_(torch.from_numpy(np.ascontiguousarray(lz[P:])))
+    x_steps = x_all.shape[0]
+    out = {"prompt_tokens": P, "decode_tokens": D,
+           "popularity": f"Zipf({wl.zipf_s}) over a permutation the frequency table has not seen"}
+    with torch.cuda.stream(stream):
+        for preheat in (False, True):
+            moe.moe_seed(ctx, freq)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            t_pre, admitted = 0.0, 0
+            for layer in range(L):
+                moe.moe_prefill(ctx, layer, P, xp, zp[layer], yp)  # synchronises
+                if preheat:
+                    t1 = time.perf_counter()
+                    admitted += moe.moe_preheat(ctx, layer, wl.slots)
+                    t_pre += time.perf_counter() - t1
+            prompt_s = time.perf_counter() - t0
+            acc = {}
+            torch.cuda.synchronize()
+            t2 = time.perf_counter()
+            run_steps(moe, ctx, D, lambda i: (xs.copy_(x_all[i % x_steps]), replay(zd[i])), acc)
+            torch.cuda.synchronize()
+            dec_s = time.perf_counter() - t2
+            r = {"decode_tokens_per_s": round(D / dec_s, 2), "hit_rate": round(
+                acc["hits"] / max(acc["hits"] + acc["misses"], 1), 4),
+                 "admissions_per_step": round(acc["admissions"] / D, 3),
+                 "prompt_tokens_per_s": round(P / prompt_s, 1), "prompt_s": round(prompt_s, 3)}
+            if preheat:
+                r.update(preheated_experts=admitted, preheat_ms=round(t_pre * 1e3, 1))
+            out["with_preheat" if preheat else "without_preheat"] = r
+            log(f"prompt {P} then decode {D}, preheat={preheat}: {r}")
+    out["decode_gain"] = round(out["with_preheat"]["decode_tokens_per_s"] /
+                               out["without_preheat"]["decode_tokens_per_s"], 4)
+    del zp, zd, xp, yp
+    return out
+
+
 def cpu_baseline(wl, seconds, logits):
     """The oracle on the host cores: decode tokens through all layers, fp64."""
     import numpy as np
@@ -188,6 +250,8 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=64, help="steps of the kernel-timing pass")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the two prompt passes (one line of JSON each; for counter runs)")
+    ap.add_argument("--prompt-tokens", type=int, default=12288,
+                    help="prompt length of the prompt-then-decode pass (0: skip it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (the reference for counter scaling)")
     args = ap.parse_args()
@@ -232,8 +296,10 @@ def main():
     log(f"creating the context: pinning {wl.weight_layers * E * B / 1e9:.1f} GB of host memory")
     if args.slots:
         wl = wl.with_(slots=args.slots)
+    prompt_tokens = 0 if args.no_side_passes else args.prompt_tokens
     ctx, freq = setup_ctx(moe, wl, wl.slots, stream, host_alloc,
-                          capture_picks=None if args.capture_picks < 0 else args.capture_picks, pool=args.pool)
+                          capture_picks=None if args.capture_picks < 0 else args.capture_picks, pool=args.pool,
+                          max_prefill_tokens=prompt_tokens)
     logits_np = zipf_logits(wl)
     logits_all = torch.from_numpy(logits_np).cuda()                       # [steps][L][T][E]
     x_steps = min(wl.steps, 32)
@@ -296,6 +362,12 @@ def main():
     cold_rate = prof["cold_picks"] * gu_bytes / max(prof["cold_gateup_ms"], 1e-9) / 1e6
     cold_dn_rate = prof["cold_picks"] * prof["down_bytes_per_pick"] / max(prof["cold_down_ms"], 1e-9) / 1e6
     log(f"kernel timing ({prof_steps} eager steps, {prof_steps * T / t_prof:.1f} tokens/s): {prof}")
+
+    request = None
+    if prompt_tokens > 0 and T == 1:
+        request = request_pass(moe, torch, ctx, wl, freq, stream, prompt_tokens, 256,
+                               lambda z: (zs.copy_(z), res.zero_(), graph.replay() if graph is not None
+                                          else forward_all()), xs, x_all)
     moe.moe_destroy(ctx)
 
     result = {
@@ -378,6 +450,8 @@ def main():
         log(f"side passes: hot {result['kernels_all_hot']} cold {result['kernels_all_cold']} "
             f"dma {result['pcie_dma_h2d_GBps']} GB/s")
 
+    if request is not None:
+        result["prompt_then_decode"] = request
     if not args.no_side_passes:
         result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc) for name in PREFILL_WORKLOADS]
         log(f"prefill: {result['prefill']}")

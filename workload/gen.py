@@ -67,6 +67,7 @@ class Workload:
     zipf_s_alt: float = 0.0  # > 0: odd layers use this exponent instead (layers of unequal skew)
     slots: int = 0           # pool slots per layer
     rotation: int = 0        # re-draw the popularity permutation every this many tokens (0: never)
+    epoch_base: int = 0      # popularity epoch of token clock 1 (the frequency table is always epoch 0)
     window: int = 64
     admit_misses: int = 2
     warmup_tokens: int = 1024
@@ -232,7 +233,7 @@ def zipf_logits(wl: Workload, layers=None, steps=None, tokens: int | None = None
     """fp32 [steps][len(layers)][T][E] router logits with Zipf(s) popularity.
 
     Token i of step s has clock t = 1 + s*T + i; with a rotation period R the
-    popularity permutation of epoch (t-1)//R applies.
+    popularity permutation of epoch epoch_base + (t-1)//R applies.
     """
     assert wl.zipf_s > 0, "workload draws its logits from a router"
     layers = range(wl.n_layers) if layers is None else list(layers)
@@ -241,7 +242,7 @@ def zipf_logits(wl: Workload, layers=None, steps=None, tokens: int | None = None
     E = wl.n_experts
     out = np.empty((n_steps, len(layers), T, E), np.float32)
     t = 1 + np.arange(n_steps)[:, None] * T + np.arange(T)[None, :]
-    epochs = (t - 1) // wl.rotation if wl.rotation else np.zeros_like(t)
+    epochs = wl.epoch_base + ((t - 1) // wl.rotation if wl.rotation else np.zeros_like(t))
     for li, layer in enumerate(layers):
         g = _rng(_P_GUMBEL, wl.wid, layer).gumbel(0.0, 1.0, size=(n_steps, T, E))
         for ep in np.unique(epochs):
