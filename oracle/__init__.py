@@ -62,6 +62,7 @@ def lib():
         L.orc_policy_new.argtypes = [C.c_int32] * 6 + [C.c_int64, C.c_int32]
         L.orc_policy_new.restype = C.c_void_p
         L.orc_policy_free.argtypes = [C.c_void_p]
+        L.orc_policy_set_swaps.argtypes = [C.c_void_p, C.c_int32, C.c_int32]
         L.orc_policy_preheat.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]
         L.orc_policy_preheat.restype = C.c_int32
         L.orc_policy_seed.argtypes = [C.c_void_p, C.c_void_p]
@@ -180,14 +181,17 @@ class Policy:
     """Step-by-step simulation of the expert cache (see moe_oracle.c)."""
 
     def __init__(self, n_layers, n_experts, slots, top_k, window=64, admit_misses=2, log_capacity=1 << 20,
-                 pool="layer"):
-        """slots: per layer (pool="layer") or in the one pool all layers share (pool="global")."""
+                 pool="layer", swaps_per_step=0, swap_lead=0):
+        """slots: per layer (pool="layer") or in the one pool all layers share (pool="global").
+        swaps_per_step: admissions allowed per step (0: any); swap_lead: steps an admission waits
+        before its table entry flips (0: at once)."""
         assert pool in ("layer", "global")
         self.L, self.E, self.S, self.k = n_layers, n_experts, slots, top_k
         self.pool = pool
         self.groups = 1 if pool == "global" else n_layers
         self._p = lib().orc_policy_new(n_layers, n_experts, slots, top_k, window, admit_misses, log_capacity,
                                        1 if pool == "global" else 0)
+        lib().orc_policy_set_swaps(self._p, swaps_per_step, swap_lead)
 
     def __del__(self):
         if getattr(self, "_p", None):

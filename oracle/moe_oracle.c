@@ -211,7 +211,20 @@ ORC_EXPORT int orc_moe_layer(int32_t T, int32_t E, int32_t k, int32_t H, int32_t
  * the (layer, expert) pairs ordered by count (descending; ties: lower layer,
  * then lower expert).
  * Internally both are "groups": L groups of S slots, or 1 group of S slots;
- * own[] holds layer * E + expert.                                           */
+ * own[] holds layer * E + expert.
+ *
+ * Swap budget and lead (the same README's tuning keys swaps-per-step and
+ * swap-lead, whose meaning it leaves open; this is the plain reading):
+ *  - budget > 0: at most budget admissions per step. An entry that would be
+ *    admitted beyond it is refused; a refused entry (budget spent, or no slot
+ *    that can be taken) remembers t as the expert's last miss.
+ *  - lead >= 0: the admission decided when step n closes takes effect when
+ *    step n + lead closes (lead 0: at once). Until then the expert is pending:
+ *    it stays cold (its picks miss and are logged, and the walk skips them),
+ *    it owns its slot, and that slot cannot be a victim. Ownership, the stamp
+ *    t and the evictee's loss of its slot and last miss happen at the
+ *    decision; only the table entry waits. Pending slots flip after the walk
+ *    of the step that closes at n + lead.                                   */
 typedef struct {
   int32_t L, E, S, k, window, admit;
   int32_t global;     /* 1: one pool of S slots for all layers */
@@ -232,6 +245,9 @@ typedef struct {
   /* admissions of the last closed step: (layer, expert, slot, evicted layer, evicted expert) */
   int32_t* adm;
   int64_t nadm, capadm;
+  int32_t budget, lead; /* swap budget per step (0: none) and lead in steps */
+  int32_t* pend;        /* [L][E]: slot of a pending admission, or -1 */
+  int64_t* flip;        /* [groups][S]: step at whose close the slot's pending owner flips in, or -1 */
 } orc_policy;
 
 /* global != 0: S is the size of the one pool shared by all layers */
@@ -251,16 +267,24 @@ ORC_EXPORT orc_policy* orc_policy_new(int32_t L, int32_t E, int32_t S, int32_t k
   p->last_log = (uint64_t*)malloc(sizeof(uint64_t) * (log_capacity > 0 ? log_capacity : 1));
   p->capadm = log_capacity;
   p->adm = (int32_t*)malloc(sizeof(int32_t) * 5 * (log_capacity > 0 ? log_capacity : 1));
-  for (int64_t i = 0; i < (int64_t)L * E; ++i) p->tbl[i] = -1;
-  for (int64_t i = 0; i < (int64_t)p->groups * S; ++i) p->own[i] = -1;
+  p->pend = (int32_t*)malloc(sizeof(int32_t) * L * E);
+  p->flip = (int64_t*)malloc(sizeof(int64_t) * p->groups * (S > 0 ? S : 1));
+  for (int64_t i = 0; i < (int64_t)L * E; ++i) p->tbl[i] = -1, p->pend[i] = -1;
+  for (int64_t i = 0; i < (int64_t)p->groups * S; ++i) p->own[i] = -1, p->flip[i] = -1;
   p->clock = 1;
   return p;
+}
+
+/* Swap budget per step (0: unlimited) and lead in steps (0: at once). */
+ORC_EXPORT void orc_policy_set_swaps(orc_policy* p, int32_t budget, int32_t lead) {
+  p->budget = budget > 0 ? budget : 0;
+  p->lead = lead > 0 ? lead : 0;
 }
 
 ORC_EXPORT void orc_policy_free(orc_policy* p) {
   if (!p) return;
   free(p->tbl), free(p->own), free(p->st), free(p->lm), free(p->counts), free(p->log), free(p->last_log);
-  free(p->adm);
+  free(p->adm), free(p->pend), free(p->flip);
   free(p);
 }
 
@@ -272,8 +296,8 @@ ORC_EXPORT void orc_policy_free(orc_policy* p) {
  * the best pair not yet taken.                                              */
 ORC_EXPORT void orc_policy_seed(orc_policy* p, const uint32_t* freq) {
   int32_t L = p->L, E = p->E, S = p->S;
-  for (int64_t i = 0; i < (int64_t)L * E; ++i) p->tbl[i] = -1, p->lm[i] = 0, p->counts[i] = 0;
-  for (int64_t i = 0; i < (int64_t)p->groups * S; ++i) p->own[i] = -1, p->st[i] = 0;
+  for (int64_t i = 0; i < (int64_t)L * E; ++i) p->tbl[i] = -1, p->lm[i] = 0, p->counts[i] = 0, p->pend[i] = -1;
+  for (int64_t i = 0; i < (int64_t)p->groups * S; ++i) p->own[i] = -1, p->st[i] = 0, p->flip[i] = -1;
   if (freq) {
     char* taken = (char*)calloc((size_t)L * E, 1);
     for (int32_t g = 0; g < p->groups; ++g) {
@@ -345,7 +369,7 @@ ORC_EXPORT void orc_policy_step(orc_policy* p, int64_t* stats) {
     int32_t layer = (int32_t)((entry >> 12) & 0xfffff);
     int32_t e = (int32_t)(entry & 0xfff);
     int64_t te = (int64_t)layer * E + e;
-    if (p->tbl[te] >= 0) continue; /* admitted earlier in this walk */
+    if (p->tbl[te] >= 0 || p->pend[te] >= 0) continue; /* admitted earlier in this walk, or pending */
     int admit_now;
     if (p->admit == 1) {
       admit_now = 1;
@@ -354,8 +378,9 @@ ORC_EXPORT void orc_policy_step(orc_policy* p, int64_t* stats) {
       if (!admit_now) p->lm[te] = t;
     }
     if (!admit_now || S == 0) continue;
-    /* victim among the slots of the layer's group: lowest free slot, else
-     * smallest stamp with ties to the highest index */
+    /* victim among the slots of the layer's group that no pending admission
+     * holds: lowest free slot, else smallest stamp with ties to the highest
+     * index */
     const int64_t g0 = (int64_t)(p->global ? 0 : layer) * S;
     int32_t victim = -1;
     for (int32_t s = 0; s < S; ++s)
@@ -363,19 +388,29 @@ ORC_EXPORT void orc_policy_step(orc_policy* p, int64_t* stats) {
         victim = s;
         break;
       }
-    int32_t evicted = -1;  /* layer * E + expert of the evicted owner */
-    if (victim < 0) {
+    if (victim < 0)
       for (int32_t s = 0; s < S; ++s)
-        if (victim < 0 || p->st[g0 + s] <= p->st[g0 + victim]) victim = s;
+        if (p->flip[g0 + s] < 0 && (victim < 0 || p->st[g0 + s] <= p->st[g0 + victim])) victim = s;
+    if (victim < 0 || (p->budget > 0 && admissions == p->budget)) {
+      p->lm[te] = t; /* refused: remembered as a miss */
+      continue;
+    }
+    int32_t evicted = -1;  /* layer * E + expert of the evicted owner */
+    if (p->own[g0 + victim] >= 0) {
       evicted = p->own[g0 + victim];
       p->tbl[evicted] = -1;
       p->lm[evicted] = 0;
       evictions += 1;
     }
     p->own[g0 + victim] = (int32_t)te;
-    p->tbl[te] = victim;
     p->st[g0 + victim] = t;
     p->lm[te] = 0;
+    if (p->lead == 0) {
+      p->tbl[te] = victim;
+    } else {
+      p->pend[te] = victim;
+      p->flip[g0 + victim] = p->step + p->lead;
+    }
     admissions += 1;
     if (p->nadm < p->capadm) {
       int32_t* a = p->adm + 5 * p->nadm++;
@@ -383,6 +418,14 @@ ORC_EXPORT void orc_policy_step(orc_policy* p, int64_t* stats) {
       a[3] = evicted < 0 ? -1 : evicted / E, a[4] = evicted < 0 ? -1 : evicted % E;
     }
   }
+  /* pending admissions whose lead ends with this step flip in */
+  for (int64_t i = 0; i < (int64_t)p->groups * S; ++i)
+    if (p->flip[i] >= 0 && p->flip[i] <= p->step) {
+      int32_t te = p->own[i];
+      p->tbl[te] = (int32_t)(i % S);
+      p->pend[te] = -1;
+      p->flip[i] = -1;
+    }
   if (stats) {
     stats[0] = p->hits, stats[1] = p->misses, stats[2] = admissions, stats[3] = evictions;
     stats[4] = p->step_tokens;
@@ -410,7 +453,8 @@ ORC_EXPORT void orc_policy_step(orc_policy* p, int64_t* stats) {
  *    that count is below the candidate's; the owner is evicted (table entry
  *    and last miss cleared). The new owner's stamp is c and its last miss is
  *    cleared. Preheat stops at the first candidate that finds no such slot:
- *    an expert the pass used is only displaced by one it used more.
+ *    an expert the pass used is only displaced by one it used more. Pending
+ *    admissions (swap lead) are neither candidates nor victims.
  * Returns the number admitted; out (may be NULL) receives the admission
  * records as in the cache step.                                             */
 ORC_EXPORT int32_t orc_policy_preheat(orc_policy* p, int32_t layer, const uint32_t* counts, int32_t max_n,
@@ -429,7 +473,8 @@ ORC_EXPORT int32_t orc_policy_preheat(orc_policy* p, int32_t layer, const uint32
   while (n < limit) {
     int32_t best = -1;  /* the next candidate: largest count, lowest id */
     for (int32_t e = 0; e < E; ++e) {
-      if (done[e] || counts[e] == 0 || p->tbl[(int64_t)layer * E + e] >= 0) continue;
+      const int64_t te = (int64_t)layer * E + e;
+      if (done[e] || counts[e] == 0 || p->tbl[te] >= 0 || p->pend[te] >= 0) continue;
       if (best < 0 || counts[e] > counts[best]) best = e;
     }
     if (best < 0) break;
@@ -443,11 +488,12 @@ ORC_EXPORT int32_t orc_policy_preheat(orc_policy* p, int32_t layer, const uint32
     if (victim < 0) {
       uint32_t vc = 0; /* pass count of the victim's owner */
       for (int32_t s = 0; s < S; ++s) {
+        if (p->flip[g0 + s] >= 0) continue; /* held by a pending admission */
         int32_t o = p->own[g0 + s];
         uint32_t oc = o / E == layer ? counts[o % E] : 0;
         if (victim < 0 || oc < vc || (oc == vc && p->st[g0 + s] <= p->st[g0 + victim])) victim = s, vc = oc;
       }
-      if (vc >= counts[best]) break; /* every owner was used as much as the candidate */
+      if (victim < 0 || vc >= counts[best]) break; /* every owner was used as much as the candidate */
       evicted = p->own[g0 + victim];
       p->tbl[evicted] = -1;
       p->lm[evicted] = 0;

@@ -7,6 +7,11 @@ Admission asks whether any remembered miss lies inside the window; a slot's
 stamp is the latest use in its history. The miss log is a list of
 (t, layer, expert) tuples sorted as tuples. Slow (quadratic), for small
 random traces.
+
+Swap budget and lead: admissions past the budget, or with every slot held
+by a pending admission, count as one more remembered miss; an admission
+with a lead waits in a pending list (owning its slot, not in the table)
+until the step it is due at closes.
 """
 from __future__ import annotations
 
@@ -15,9 +20,10 @@ class PolicyRef:
     """pool="layer": S slots per layer; pool="global": one pool of S slots that
     every layer draws from (owners are (layer, expert) pairs)."""
 
-    def __init__(self, L, E, S, k, window=64, admit=2, pool="layer"):
+    def __init__(self, L, E, S, k, window=64, admit=2, pool="layer", budget=0, lead=0):
         self.L, self.E, self.S, self.k, self.window, self.admit = L, E, S, k, window, admit
         self.pool = pool
+        self.budget, self.lead = budget, lead
         self.G = 1 if pool == "global" else L
         self.seed(None)
 
@@ -26,6 +32,8 @@ class PolicyRef:
 
     def seed(self, freq):
         self.where = {}  # (layer, e) -> slot
+        self.pending = {}  # (layer, e) -> (slot, step at whose close it enters the table)
+        self.nstep = 0
         self.owner = [[None] * self.S for _ in range(self.G)]  # (layer, e) or None
         self.uses = [[[] for _ in range(self.S)] for _ in range(self.G)]
         self.misses_since_reset = {}
@@ -67,7 +75,7 @@ class PolicyRef:
         adm = ev = 0
         admissions = []
         for (t, layer, e) in entries:
-            if (layer, e) in self.where:
+            if (layer, e) in self.where or (layer, e) in self.pending:
                 continue
             hist = self.misses_since_reset.setdefault((layer, e), [])
             if self.admit == 1:
@@ -80,21 +88,35 @@ class PolicyRef:
                 continue
             g = self._group(layer)
             free = [s for s in range(self.S) if self.owner[g][s] is None]
+            held = {s for (s, _) in self.pending.values()} if self.pool == "global" else {
+                s for (lay, _e), (s, _) in self.pending.items() if lay == layer}
+            takeable = [s for s in range(self.S) if s not in held]
+            if (not free and not takeable) or (self.budget and adm == self.budget):
+                hist.append(t)
+                continue
             evicted = (-1, -1)
             if free:
                 victim = min(free)
             else:
-                victim = max(range(self.S), key=lambda s: (-self._stamp(g, s), s))
+                victim = max(takeable, key=lambda s: (-self._stamp(g, s), s))
                 evicted = self.owner[g][victim]
                 del self.where[evicted]
                 self.misses_since_reset[evicted] = []
                 ev += 1
             self.owner[g][victim] = (layer, e)
-            self.where[(layer, e)] = victim
+            if self.lead:
+                self.pending[(layer, e)] = (victim, self.nstep + self.lead)
+            else:
+                self.where[(layer, e)] = victim
             self.uses[g][victim] = [t]
             self.misses_since_reset[(layer, e)] = []
             adm += 1
             admissions.append((layer, e, victim) + tuple(evicted))
+        for le, (s, due) in list(self.pending.items()):
+            if due <= self.nstep:
+                self.where[le] = s
+                del self.pending[le]
+        self.nstep += 1
         stats = dict(hits=self.hits, misses=len(self.log), admissions=adm, evictions=ev, tokens=self.step_tokens)
         self.last_log = [(t << 32) | (layer << 12) | e for (t, layer, e) in entries]
         self.last_admissions = admissions

@@ -150,14 +150,16 @@ def _random_trace(draw_rng, L, E, k, steps, tmax):
 @settings(max_examples=60, deadline=None)
 @given(seed=st.integers(0, 2**31 - 1), L=st.integers(1, 3), E=st.integers(2, 12), tmax=st.integers(1, 4),
        window=st.sampled_from([2, 5, 64]), admit=st.sampled_from([1, 2]), seeded=st.booleans(),
-       pool=st.sampled_from(["layer", "global"]))
-def test_agrees_with_history_formulation(seed, L, E, tmax, window, admit, seeded, pool):
+       pool=st.sampled_from(["layer", "global"]), budget=st.sampled_from([0, 0, 1, 2]),
+       lead=st.sampled_from([0, 0, 1, 2]))
+def test_agrees_with_history_formulation(seed, L, E, tmax, window, admit, seeded, pool, budget, lead):
     rng = np.random.default_rng(seed)
     k = int(rng.integers(1, E + 1))
     S = int(rng.integers(0, (E if pool == "layer" else L * E) + 1))
     freq = rng.integers(0, 5, size=(L, E)).astype(np.uint32) if seeded else None
-    a = oracle.Policy(L, E, S, k, window=window, admit_misses=admit, pool=pool)
-    b = PolicyRef(L, E, S, k, window=window, admit=admit, pool=pool)
+    a = oracle.Policy(L, E, S, k, window=window, admit_misses=admit, pool=pool, swaps_per_step=budget,
+                      swap_lead=lead)
+    b = PolicyRef(L, E, S, k, window=window, admit=admit, pool=pool, budget=budget, lead=lead)
     a.seed(freq)
     b.seed(freq)
     cum_adm = cum_miss = 0
@@ -180,16 +182,90 @@ def test_agrees_with_history_formulation(seed, L, E, tmax, window, admit, seeded
             res = {(layer, e): s for layer in layers for e, s in enumerate(ta["table"][layer]) if s >= 0}
             assert len(set(res.values())) == len(res) <= S
             assert all(ta["owner_layer"][g][s] == layer and ta["owner"][g][s] == e for (layer, e), s in res.items())
-            assert all(o == -1 or ta["table"][ol][o] >= 0 for ol, o in zip(ta["owner_layer"][g], ta["owner"][g]))
+            # an owner outside the table is an admission waiting for its lead
+            assert all(o == -1 or ta["table"][ol][o] >= 0 or lead > 0
+                       for ol, o in zip(ta["owner_layer"][g], ta["owner"][g]))
         assert ta["stamps"].size == 0 or ta["stamps"].max() < a.clock
         T = max(len(ids) for _, ids in step)
         assert sa["hits"] + sa["misses"] == sum(len(ids) for _, ids in step) * k
         assert sa["tokens"] == T
+        if budget:
+            assert sa["admissions"] <= budget
         cum_adm += sa["admissions"]
         cum_miss += sa["misses"]
         if admit == 2:
             assert cum_adm <= cum_miss // 2
     assert a.counts().tolist() == b.counts
+
+
+def test_swap_budget_defers_the_rest_of_a_step():
+    pol = oracle.Policy(1, 6, 3, 2, swaps_per_step=1)
+    pol.seed(np.array([[9, 8, 7, 0, 0, 0]], np.uint32))
+    pol.forward(0, [[3, 4]])
+    pol.step()  # t=1: first misses of e3, e4
+    pol.forward(0, [[3, 4]])
+    st = pol.step()  # t=2: both qualify; the budget admits e3 only and e4 remembers t=2
+    assert st["admissions"] == 1
+    assert pol.last_admissions().tolist() == [[0, 3, 2, 0, 2]]
+    assert pol.tables()["last_miss"][0].tolist() == [0, 0, 0, 0, 2, 0]
+    pol.forward(0, [[4, 0]])  # t=3: e4's miss is inside the window of t=2; e0 hits (stamp 3)
+    st = pol.step()  # e4 takes slot 1 (stamp 0; slot 2 holds e3 at 2), evicting e1
+    assert st["admissions"] == 1 and pol.tables()["table"][0].tolist() == [0, -1, -1, 2, 1, -1]
+
+
+def test_swap_lead_keeps_the_expert_cold_and_its_slot_reserved():
+    pol = oracle.Policy(1, 6, 2, 2, swap_lead=1)
+    pol.seed(np.array([[5, 4, 0, 0, 0, 0]], np.uint32))  # e0 -> 0, e1 -> 1
+    pol.forward(0, [[2, 3]])
+    pol.step()  # t=1: first misses of e2, e3
+    pol.forward(0, [[1, 5]])
+    pol.step()  # t=2: e1 hits (slot 1 stamped 2); first miss of e5
+    pol.forward(0, [[2, 3]])
+    st = pol.step()  # t=3: e2 takes slot 0 (stamp 0), e3 slot 1; both owners evicted now, both pending
+    assert st["admissions"] == 2 and st["evictions"] == 2
+    t = pol.tables()
+    assert t["table"][0].tolist() == [-1] * 6
+    assert t["owner"][0].tolist() == [2, 3] and t["stamps"][0].tolist() == [3, 3]
+    # t=4: e2 still misses (logged, skipped by the walk); e5 qualifies but every
+    # slot is held by a pending admission, so it is refused and remembers t=4
+    pol.forward(0, [[2, 5]])
+    st = pol.step()
+    assert st["misses"] == 2 and st["admissions"] == 0
+    assert pol.last_log().tolist() == [(4 << 32) | 2, (4 << 32) | 5]
+    t = pol.tables()
+    assert t["table"][0].tolist() == [-1, -1, 0, 1, -1, -1]  # the lead ended with this step: both flip in
+    assert t["last_miss"][0].tolist() == [0, 0, 0, 0, 0, 4]
+    pol.forward(0, [[2, 3]])
+    assert pol.step()["hits"] == 2
+
+
+def test_preheat_leaves_pending_admissions_alone():
+    pol = oracle.Policy(1, 5, 2, 1, swap_lead=2)
+    pol.seed(np.array([[5, 4, 0, 0, 0]], np.uint32))  # e0 -> 0, e1 -> 1
+    for e in (2, 2):
+        pol.forward(0, [[e]])
+        pol.step()  # t=2: e2 admitted into slot 1 (stamp 0, highest index), pending
+    assert pol.tables()["owner"][0].tolist() == [0, 2]
+    # e2 is no candidate and slot 1 no victim: e3 displaces e0, e4 finds no slot
+    adm = pol.preheat(0, [0, 0, 9, 5, 3], max_experts=2)
+    assert adm.tolist() == [[0, 3, 0, 0, 0]]
+    assert pol.tables()["table"][0].tolist() == [-1, -1, -1, 0, -1]
+
+
+def test_swap_lead_zero_is_the_plain_policy():
+    rng = np.random.default_rng(3)
+    a = oracle.Policy(2, 10, 4, 2)
+    b = oracle.Policy(2, 10, 4, 2, swaps_per_step=0, swap_lead=0)
+    freq = rng.integers(0, 9, size=(2, 10)).astype(np.uint32)
+    a.seed(freq)
+    b.seed(freq)
+    for _ in range(40):
+        for layer in range(2):
+            ids = np.stack([rng.permutation(10)[:2] for _ in range(2)]).astype(np.int32)
+            a.forward(layer, ids)
+            b.forward(layer, ids)
+        assert a.step() == b.step()
+        assert a.tables()["table"].tolist() == b.tables()["table"].tolist()
 
 
 def test_first_pick_follows_zipf():
