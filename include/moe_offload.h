@@ -67,6 +67,8 @@ extern "C" {
 
 #define MOE_ACCUMULATE    1u  /* moe_forward / moe_prefill: y += result      */
 
+#define MOE_MAX_SWAP_LEAD 8   /* largest moe_config.swap_lead                 */
+
 /* Pinned host arena flavour (moe_config.host_alloc). */
 #define MOE_HOST_COHERENT     0 /* hipHostMalloc default: fine-grained      */
 #define MOE_HOST_NONCOHERENT  1 /* hipHostMallocNonCoherent: GPU may cache  */
@@ -121,6 +123,14 @@ typedef struct {
                               that route inside the gate/up GEMV (logits
                               given, E <= 512), others copy from pinned.     */
   int32_t pool_mode;       /* MOE_POOL_PER_LAYER (0) or MOE_POOL_GLOBAL       */
+  int32_t swaps_per_step;  /* >= 0: admissions allowed per cache step (0: no
+                              limit); see moe_cache_step ([FORK] "Run": the
+                              swaps-per-step key)                            */
+  int32_t swap_lead;       /* 0..MOE_MAX_SWAP_LEAD: cache steps an admission
+                              waits before its table entry flips (0: at once;
+                              [FORK] "Run": the swap-lead key). With a lead,
+                              copies from pinned memory run on a stream of the
+                              library's own while the next steps decode     */
 } moe_config;
 
 typedef struct {
@@ -245,7 +255,8 @@ MOE_API int moe_prefill(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
  * picks), provided those picks are fewer than the candidate's; the owner is
  * evicted and forgets its last miss. The new owner's stamp is c and it
  * forgets its last miss. Preheat stops at the first candidate that finds no
- * such slot. Bytes are copied from the staging
+ * such slot. Pending admissions (swap_lead) are neither candidates nor
+ * victims. Bytes are copied from the staging
  * blocks the pass filled, else from pinned memory. *admitted (may be NULL)
  * receives the number admitted. Synchronises the stream; not capturable. */
 MOE_API int moe_preheat(moe_ctx* ctx, int32_t layer, int32_t max_experts, int32_t* admitted);
@@ -263,7 +274,21 @@ MOE_API int moe_preheat(moe_ctx* ctx, int32_t layer, int32_t max_experts, int32_
  * block when a cold read of this step captured it, see capture_picks; else
  * from pinned memory), tables, stamps and the
  * clock (advanced by the step's token count) are uploaded, and the log is
- * cleared. out may be NULL. MOE_E_CAPTURING if the stream is capturing. */
+ * cleared. out may be NULL. MOE_E_CAPTURING if the stream is capturing.
+ *
+ * Swap budget and lead (the [FORK] "Run" keys swaps-per-step and swap-lead,
+ * named there without a definition): with swaps_per_step = n > 0, an entry
+ * that would be admitted after n admissions of this step is refused; so is
+ * one for which every slot of the pool is held by a pending admission. A
+ * refused entry remembers t as its last miss. With swap_lead = d > 0 an
+ * admission decided by this call is pending until the call d steps later:
+ * the victim is evicted, the slot's owner and stamp t are set now, but the
+ * expert's table entry stays -1 (its picks read pinned memory and are
+ * recorded as misses, which the walk skips) and the slot cannot be a victim.
+ * Its copy from pinned memory starts at once on the library's swap stream;
+ * a copy from a capture block runs on the context stream. The call d steps
+ * later waits for that step's swap copies, then sets the table entries
+ * (after its own walk). */
 MOE_API int moe_cache_step(moe_ctx* ctx, moe_step_stats* out);
 
 /* Kernel timing for measurement: enable = 1 turns it on and clears the

@@ -280,7 +280,7 @@ extern "C" int moe_preheat(moe_ctx* c, int32_t layer, int32_t max_experts, int32
   const int64_t limit = std::min<int64_t>(max_experts, S);
   std::vector<int32_t> cand;
   for (int64_t e = 0; e < E; ++e)
-    if (cnt[e] > 0 && c->tbl[layer * E + e] < 0) cand.push_back((int32_t)e);
+    if (cnt[e] > 0 && c->tbl[layer * E + e] < 0 && c->pend[layer * E + e] < 0) cand.push_back((int32_t)e);
   std::stable_sort(cand.begin(), cand.end(), [&](int32_t a, int32_t b) { return cnt[a] > cnt[b]; });
   int32_t n = 0;
   for (size_t i = 0; i < cand.size() && n < limit; ++i) {
@@ -295,11 +295,12 @@ extern "C" int moe_preheat(moe_ctx* c, int32_t layer, int32_t max_experts, int32
       // victim: the owner with the fewest pass picks (other layers' owners: 0), then the oldest stamp
       int32_t vc = 0;
       for (int64_t sl = 0; sl < S; ++sl) {
+        if (c->flip[g0 + sl] >= 0) continue;  // held by a pending admission
         const int32_t o = c->owner[g0 + sl];
         const int32_t oc = o / E == layer ? cnt[o % E] : 0;
         if (v < 0 || oc < vc || (oc == vc && c->stamps[g0 + sl] <= c->stamps[g0 + v])) v = sl, vc = oc;
       }
-      if (vc >= cnt[e]) break;  // every owner was used by the pass at least as often
+      if (v < 0 || vc >= cnt[e]) break;  // every owner was used by the pass at least as often
       const int32_t old = c->owner[g0 + v];
       c->tbl[old] = -1;
       c->last_miss[old] = 0;

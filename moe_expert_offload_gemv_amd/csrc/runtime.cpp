@@ -124,6 +124,11 @@ static void ctx_release(moe_ctx* c) {
     if (r) (void)hipFree(r);
   for (hipEvent_t e : c->events) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->prefill_events) (void)hipEventDestroy(e);
+  if (c->swap_stream) {
+    (void)hipStreamSynchronize(c->swap_stream);
+    (void)hipStreamDestroy(c->swap_stream);
+  }
+  for (hipEvent_t e : c->swap_events) (void)hipEventDestroy(e);
   moe_prefill_release(c);
   delete c;
 }
@@ -166,7 +171,8 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
       k.quant != MOE_Q4_32_F16 || k.window_tokens < 1 || (k.admit_misses != 1 && k.admit_misses != 2) ||
       k.max_batch_tokens < 1 || k.max_batch_tokens > 256 || k.max_prefill_tokens < 0 || k.n_layers > (1 << 20) ||
       k.capture_picks < 0 || k.capture_picks > k.max_batch_tokens * k.top_k ||
-      (k.pool_mode != MOE_POOL_PER_LAYER && k.pool_mode != MOE_POOL_GLOBAL) ||
+      (k.pool_mode != MOE_POOL_PER_LAYER && k.pool_mode != MOE_POOL_GLOBAL) || k.swaps_per_step < 0 ||
+      k.swap_lead < 0 || k.swap_lead > MOE_MAX_SWAP_LEAD ||
       (k.host_alloc != MOE_HOST_COHERENT && k.host_alloc != MOE_HOST_NONCOHERENT))
     return g_create_error = "config field out of range", MOE_E_INVAL;
   moe::GemvShape s1, s2;
@@ -284,6 +290,18 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->stamps.assign(G * std::max<int64_t>(S, 1), 0);
   c->last_miss.assign(L * E, 0);
   c->cap_of.assign(L * E, -1);
+  c->pend.assign(L * E, -1);
+  c->flip.assign(G * std::max<int64_t>(S, 1), -1);
+  if (k.swap_lead > 0) {
+    // default priority, like every stream here
+    if (hipStreamCreateWithFlags(&c->swap_stream, hipStreamNonBlocking) != hipSuccess) return fail(MOE_E_HIP);
+    for (int i = 0; i <= k.swap_lead; ++i) {
+      hipEvent_t ev;
+      if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return fail(MOE_E_HIP);
+      c->swap_events.push_back(ev);
+    }
+    c->swap_recorded.assign(k.swap_lead + 1, 0);
+  }
   if (c->d_cap_tag && hipMemset(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride) != hipSuccess)
     return fail(MOE_E_HIP);
   if (c->d_last_miss && hipMemset(c->d_last_miss, 0, sizeof(uint32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
@@ -363,6 +381,10 @@ extern "C" int moe_seed(moe_ctx* c, const uint32_t* freq) {
   std::fill(c->owner.begin(), c->owner.end(), -1);
   std::fill(c->stamps.begin(), c->stamps.end(), 0u);
   std::fill(c->last_miss.begin(), c->last_miss.end(), 0u);
+  std::fill(c->pend.begin(), c->pend.end(), -1);
+  std::fill(c->flip.begin(), c->flip.end(), -1);
+  if (c->swap_stream) HIP_TRY(c, hipStreamSynchronize(c->swap_stream));  // copies into slots about to be reseeded
+  std::fill(c->swap_recorded.begin(), c->swap_recorded.end(), 0);
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   if (freq) {
     // each pool takes its candidates (the layer's experts, or every layer's
@@ -603,14 +625,15 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
   // canonical order: ascending 64-bit entries (clock, then layer, then expert)
   std::sort(c->last_log.begin(), c->last_log.end());
 
-  int64_t admissions = 0, evictions = 0, copied_pcie = 0;
+  int64_t admissions = 0, evictions = 0, copied_pcie = 0, swap_copies = 0;
+  const int32_t lead = c->cfg.swap_lead, budget = c->cfg.swaps_per_step;
   for (uint64_t entry : c->last_log) {
     const uint32_t t = (uint32_t)(entry >> 32);
     const int64_t l = (int64_t)((entry >> 12) & 0x7ffff);
     const int64_t e = (int64_t)(entry & 0xfff);
     if (l >= L || e >= E) continue;
     const int64_t te = l * E + e;
-    if (c->tbl[te] >= 0) continue;  // admitted earlier in this walk
+    if (c->tbl[te] >= 0 || c->pend[te] >= 0) continue;  // admitted earlier in this walk, or pending
     bool admit;
     if (c->cfg.admit_misses == 1) {
       admit = true;
@@ -621,7 +644,8 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     }
     if (!admit || S == 0) continue;
     // victim in the layer's pool: lowest free slot, else the smallest stamp
-    // (ties: highest slot); with one global pool the owner may be any layer's
+    // (ties: highest slot) among slots no pending admission holds; with one
+    // global pool the owner may be any layer's
     const int64_t g0 = c->group_of(l) * S;
     int64_t v = -1;
     for (int64_t s = 0; s < S; ++s)
@@ -632,33 +656,69 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     if (v < 0) {
       uint32_t best = 0xffffffffu;
       for (int64_t s = 0; s < S; ++s)
-        if (c->stamps[g0 + s] <= best) best = c->stamps[g0 + s], v = s;
+        if (c->flip[g0 + s] < 0 && c->stamps[g0 + s] <= best) best = c->stamps[g0 + s], v = s;
+    }
+    if (v < 0 || (budget > 0 && admissions == budget)) {
+      c->last_miss[te] = t;  // refused: remembered as a miss
+      continue;
+    }
+    if (c->owner[g0 + v] >= 0) {
       const int32_t old = c->owner[g0 + v];  // layer * E + expert
       c->tbl[old] = -1;
       c->last_miss[old] = 0;
       ++evictions;
     }
     c->owner[g0 + v] = (int32_t)te;
-    c->tbl[te] = (int32_t)v;
     c->stamps[g0 + v] = t;
     c->last_miss[te] = 0;
+    if (lead == 0) {
+      c->tbl[te] = (int32_t)v;
+    } else {
+      c->pend[te] = (int32_t)v;
+      c->flip[g0 + v] = c->steps + lead;
+    }
     ++admissions;
     uint8_t* dst = c->pool + (g0 + v) * B;
-    if (c->cap_of[te] >= 0) {
+    if (c->cap_of[te] >= 0) {  // before the next step's forwards overwrite the capture block
       HIP_TRY(c, hipMemcpyAsync(dst, c->d_capture + (l * c->capture_picks + c->cap_of[te]) * B, B,
                                 hipMemcpyDeviceToDevice, c->stream));
     } else {
-      HIP_TRY(c, hipMemcpyAsync(dst, c->host_layers[l] + e * B, B, hipMemcpyHostToDevice, c->stream));
+      // with a lead the slot is read by nobody until the flip: the copy runs beside the next steps
+      HIP_TRY(c, hipMemcpyAsync(dst, c->host_layers[l] + e * B, B, hipMemcpyHostToDevice,
+                                lead ? c->swap_stream : c->stream));
       ++copied_pcie;
+      swap_copies += lead ? 1 : 0;
     }
   }
   forget_captures(c);
+  int64_t flips = 0;
+  if (lead > 0) {
+    const int64_t ring = lead + 1;
+    if (swap_copies > 0) {
+      HIP_TRY(c, hipEventRecord(c->swap_events[c->steps % ring], c->swap_stream));
+      c->swap_recorded[c->steps % ring] = 1;
+    }
+    // admissions decided lead steps ago flip in once their copies are done
+    const int64_t due = c->steps - lead;
+    if (due >= 0 && c->swap_recorded[due % ring]) {
+      HIP_TRY(c, hipEventSynchronize(c->swap_events[due % ring]));
+      c->swap_recorded[due % ring] = 0;
+    }
+    for (int64_t i = 0; i < GS; ++i)
+      if (c->flip[i] >= 0 && c->flip[i] <= c->steps) {
+        const int32_t te = c->owner[i];
+        c->tbl[te] = (int32_t)(i % S);
+        c->pend[te] = -1;
+        c->flip[i] = -1;
+        ++flips;
+      }
+  }
   if (c->d_last_miss && misses > 0) {  // the next step's forwards decide what to capture from it
     std::memcpy(c->h_last_miss, c->last_miss.data(), sizeof(uint32_t) * L * E);
     HIP_TRY(c, hipMemcpyAsync(c->d_last_miss, c->h_last_miss, sizeof(uint32_t) * L * E, hipMemcpyHostToDevice,
                               c->stream));
   }
-  if (admissions > 0) {
+  if (admissions > 0 || flips > 0) {
     std::memcpy(c->h_tbl, c->tbl.data(), sizeof(int32_t) * L * E);
     HIP_TRY(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * L * E, hipMemcpyHostToDevice, c->stream));
     std::memcpy(c->h_stamps, c->stamps.data(), sizeof(uint32_t) * GS);

@@ -69,6 +69,12 @@ struct moe_ctx {
   std::vector<int32_t> tbl, owner;   // tbl [L][E] slot; owner [groups][S] layer * E + expert or -1
   std::vector<uint32_t> stamps, last_miss;
   std::vector<uint64_t> last_log;
+  // swap lead: admissions waiting for their copy (and the copy stream)
+  std::vector<int32_t> pend;           // [L][E] slot of a pending admission, or -1
+  std::vector<int64_t> flip;           // [groups][S] step whose cache step flips the slot's owner in, or -1
+  hipStream_t swap_stream = nullptr;   // copies from pinned memory of pending admissions
+  std::vector<hipEvent_t> swap_events; // [swap_lead + 1]: end of a step's swap copies
+  std::vector<char> swap_recorded;     // [swap_lead + 1]: the event holds a step's copies
   std::vector<int32_t> cap_of;         // [L][E] captured pick of the expert in the step, or -1
   std::vector<int64_t> cap_touched;    // entries of cap_of set in the step
   std::vector<char> registered;        // per host set

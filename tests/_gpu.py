@@ -29,7 +29,7 @@ class Decode:
 
     def __init__(self, wl: Workload, slots: int | None = None, seed=True, max_batch: int | None = None,
                  host_alloc: int = moe.MOE_HOST_COHERENT, stream=None, max_prefill: int = 0, keep_weights=True,
-                 capture_picks=None, pool="layer"):
+                 capture_picks=None, pool="layer", swaps_per_step=0, swap_lead=0):
         import torch
 
         self.wl = wl
@@ -43,7 +43,8 @@ class Decode:
                                   admit_misses=wl.admit_misses, max_batch_tokens=max_batch or max(wl.tokens, 1),
                                   max_prefill_tokens=max_prefill, host_alloc=host_alloc,
                                   host_sets=wl.distinct_layers, stream=self.stream, capture_picks=capture_picks,
-                                  pool_mode=moe.MOE_POOL_GLOBAL if pool == "global" else moe.MOE_POOL_PER_LAYER)
+                                  pool_mode=moe.MOE_POOL_GLOBAL if pool == "global" else moe.MOE_POOL_PER_LAYER,
+                                  swaps_per_step=swaps_per_step, swap_lead=swap_lead)
         info = moe.moe_get_info(self.ctx)
         assert info["slots_per_layer"] == self.S, info
         self.weights = {}
@@ -75,9 +76,9 @@ class Decode:
             pass
 
 
-def oracle_policy(wl: Workload, slots: int, seed: bool = True, pool: str = "layer"):
+def oracle_policy(wl: Workload, slots: int, seed: bool = True, pool: str = "layer", swaps_per_step=0, swap_lead=0):
     pol = oracle.Policy(wl.n_layers, wl.n_experts, slots, wl.top_k, window=wl.window, admit_misses=wl.admit_misses,
-                        pool=pool)
+                        pool=pool, swaps_per_step=swaps_per_step, swap_lead=swap_lead)
     pol.seed(frequency_table(wl) if seed else None)
     return pol
 

@@ -36,9 +36,10 @@ def _compare_policy(d: Decode, pol, st_gpu, st_orc, layers):
 
 
 def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_alloc=moe.MOE_HOST_COHERENT,
-                capture_picks=None, copies=None, pool="layer"):
-    d = Decode(wl, slots=slots, seed=seed, host_alloc=host_alloc, capture_picks=capture_picks, pool=pool)
-    pol = oracle_policy(wl, slots, seed=seed, pool=pool)
+                capture_picks=None, copies=None, pool="layer", swaps=(0, 0)):
+    d = Decode(wl, slots=slots, seed=seed, host_alloc=host_alloc, capture_picks=capture_picks, pool=pool,
+               swaps_per_step=swaps[0], swap_lead=swaps[1])
+    pol = oracle_policy(wl, slots, seed=seed, pool=pool, swaps_per_step=swaps[0], swap_lead=swaps[1])
     logits = zipf_logits(wl)
     L, T, k, H = wl.n_layers, wl.tokens, wl.top_k, wl.hidden
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
@@ -337,3 +338,20 @@ def test_global_pool_cold_start_batch():
     wl = Workload("decode-e32k4-h256f512-l3-b2-global", 113, 3, 32, 4, 256, 512, tokens=2, steps=30, zipf_s=1.1,
                   slots=8, rotation=20)
     _run_decode(wl, slots=24, check_every=6, seed=False, pool="global")
+
+
+@pytest.mark.parametrize("capture_picks,budget,lead", [(0, 3, 1), (None, 3, 1), (0, 0, 2), (None, 0, 2)])
+def test_swap_budget_and_lead_bit_exact(capture_picks, budget, lead):
+    # admit on the first miss, so every step wants more swaps than the budget
+    # allows; every step's outputs are checked, so a slot read before its copy
+    # landed (pinned copies run on the swap stream beside the next steps) shows
+    wl = REDUCED.with_(name="decode-e64k8-h2048f1024-l4-b1-swaps", steps=14, admit_misses=1)
+    copies = {}
+    _run_decode(wl, slots=26, check_every=1, capture_picks=capture_picks, copies=copies, swaps=(budget, lead))
+    assert copies["copied"] > 0
+    assert copies["pcie"] == (0 if capture_picks is None else copies["copied"]), copies
+
+
+def test_swap_lead_global_pool_window_admission():
+    _run_decode(REDUCED.with_(name="decode-e64k8-h2048f1024-l4-b1-global-lead"), slots=104, check_every=4,
+                pool="global", capture_picks=0, swaps=(4, 1))
