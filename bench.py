@@ -43,7 +43,7 @@ def log(*a):
 
 
 def setup_ctx(moe, wl, slots, stream, host_alloc, layers=None, progress=True, capture_picks=None, pool="layer",
-              max_prefill_tokens=0, swaps=(0, 0)):
+              max_prefill_tokens=0, swaps=(0, 0), cold_exec=0, cpu_threads=0):
     """slots per layer; pool="global" gives one pool of the same total size to all layers."""
     from workload import frequency_table, layer_weights
 
@@ -54,7 +54,7 @@ def setup_ctx(moe, wl, slots, stream, host_alloc, layers=None, progress=True, ca
                          max_prefill_tokens=max_prefill_tokens, host_alloc=host_alloc,
                          host_sets=min(wl.weight_layers, L), stream=stream, capture_picks=capture_picks,
                          pool_mode=moe.MOE_POOL_GLOBAL if pool == "global" else moe.MOE_POOL_PER_LAYER,
-                         swaps_per_step=swaps[0], swap_lead=swaps[1])
+                         swaps_per_step=swaps[0], swap_lead=swaps[1], cold_exec=cold_exec, cpu_threads=cpu_threads)
     buf = None
     t0 = time.time()
     for layer in range(min(wl.weight_layers, L)):  # layer l reads host set l % weight_layers
@@ -251,6 +251,9 @@ def main():
     ap.add_argument("--swaps-per-step", type=int, default=0, help="admissions per cache step (0: no limit)")
     ap.add_argument("--swap-lead", type=int, default=0,
                     help="cache steps an admission waits for its copy before its table entry flips")
+    ap.add_argument("--cold-exec", choices=["gpu", "cpu"], default="gpu",
+                    help="cold picks read zero-copy by the GPU, or computed by host threads (eager launches)")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="host threads for --cold-exec cpu (0: all but one)")
     ap.add_argument("--profile-steps", type=int, default=64, help="steps of the kernel-timing pass")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the two prompt passes (one line of JSON each; for counter runs)")
@@ -301,9 +304,16 @@ def main():
     if args.slots:
         wl = wl.with_(slots=args.slots)
     prompt_tokens = 0 if args.no_side_passes else args.prompt_tokens
+    cold_exec = moe.MOE_COLD_CPU if args.cold_exec == "cpu" else moe.MOE_COLD_GPU
+    if cold_exec == moe.MOE_COLD_CPU:
+        args.eager = True  # the host hand-off is not capturable
     ctx, freq = setup_ctx(moe, wl, wl.slots, stream, host_alloc,
                           capture_picks=None if args.capture_picks < 0 else args.capture_picks, pool=args.pool,
-                          max_prefill_tokens=prompt_tokens, swaps=(args.swaps_per_step, args.swap_lead))
+                          max_prefill_tokens=prompt_tokens, swaps=(args.swaps_per_step, args.swap_lead),
+                          cold_exec=cold_exec, cpu_threads=args.cpu_threads)
+    info = moe.moe_get_info(ctx)
+    if cold_exec == moe.MOE_COLD_CPU:
+        log(f"cold picks on {info['host_threads']} host threads (isa code {info['host_isa']})")
     logits_np = zipf_logits(wl)
     logits_all = torch.from_numpy(logits_np).cuda()                       # [steps][L][T][E]
     x_steps = min(wl.steps, 32)
@@ -390,8 +400,10 @@ def main():
         "config": {"workload": wl.name, "layers": L, "experts": E, "top_k": k, "hidden": H, "ffn": wl.ffn,
                    "tokens_per_step": T, "pool_slots_per_layer": wl.slots, "weights": "q4 blocks (18 B / 32)",
                    "host_alloc": args.host_alloc, "host_weight_sets": wl.weight_layers,
-                   "capture_picks": wl.top_k if args.capture_picks < 0 else args.capture_picks,
+                   "capture_picks": (0 if args.cold_exec == "cpu" else wl.top_k) if args.capture_picks < 0
+                   else args.capture_picks,
                    "pool": args.pool, "swaps_per_step": args.swaps_per_step, "swap_lead": args.swap_lead,
+                   "cold_exec": args.cold_exec, "host_threads": info["host_threads"],
                    "launch": "eager" if args.eager else "hip-graph"},
         "effective_weight_GBps": round((acc["hot_bytes"] + acc["cold_bytes"]) / elapsed / 1e9, 2),
         "hot_GBps_over_step": round(acc["hot_bytes"] / elapsed / 1e9, 2),

@@ -69,6 +69,10 @@ extern "C" {
 
 #define MOE_MAX_SWAP_LEAD 8   /* largest moe_config.swap_lead                 */
 
+/* Where the cold picks of a decode forward are computed (moe_config.cold_exec). */
+#define MOE_COLD_GPU      0   /* the GPU reads the pinned weights zero-copy  */
+#define MOE_COLD_CPU      1   /* host threads compute them beside the GPU    */
+
 /* Pinned host arena flavour (moe_config.host_alloc). */
 #define MOE_HOST_COHERENT     0 /* hipHostMalloc default: fine-grained      */
 #define MOE_HOST_NONCOHERENT  1 /* hipHostMallocNonCoherent: GPU may cache  */
@@ -131,6 +135,15 @@ typedef struct {
                               [FORK] "Run": the swap-lead key). With a lead,
                               copies from pinned memory run on a stream of the
                               library's own while the next steps decode     */
+  int32_t cold_exec;       /* MOE_COLD_GPU (0) or MOE_COLD_CPU ([FORK] "How
+                              it works": the GPU computes the cached experts
+                              while the CPU computes the misses, in parallel).
+                              With MOE_COLD_CPU, capture_picks must be 0 (no
+                              GPU read of cold weights exists to capture),
+                              moe_forward needs logits and E <= 512 and is not
+                              capturable; see moe_forward                    */
+  int32_t cpu_threads;     /* host threads for MOE_COLD_CPU, 0..256 (0: one
+                              per hardware thread but one)                   */
 } moe_config;
 
 typedef struct {
@@ -142,6 +155,9 @@ typedef struct {
   int64_t staging_experts;    /* HBM blocks lent to a prefill pass            */
   int64_t clock;              /* token clock of the next step (starts at 1)   */
   int64_t steps;              /* cache steps run since the last seed          */
+  int64_t host_threads;       /* threads computing cold picks (0: GPU does)   */
+  int64_t host_isa;           /* their dot products: 0 none, 1 scalar C++,
+                                 2 AVX2+FMA+F16C, 3 AVX-512                    */
 } moe_info;
 
 typedef struct {
@@ -228,7 +244,19 @@ MOE_API int moe_seed(moe_ctx* ctx, const uint32_t* freq);
  * x, y: device fp32 [T][H]; y may equal x only with MOE_ACCUMULATE (residual
  * update in place). ids (int32 [T][k]) and w (fp32 [T][k]) are optional device
  * outputs. Asynchronous on the context stream; allocates nothing and may be
- * captured into a HIP graph. Call it at most once per layer per step. */
+ * captured into a HIP graph. Call it at most once per layer per step.
+ *
+ * With cold_exec = MOE_COLD_CPU the cold picks are computed by the library's
+ * host threads instead ([FORK] "How it works"): the gate/up launch computes
+ * the hot picks and hands every pick (expert, weight, hot/cold) and the
+ * token's x to pinned host memory; the host threads compute y_pick of each
+ * cold pick (same formulas, fp32, AVX-512 where the host has it) and answer;
+ * the last launch waits for the answer (bounded) and forms y in pick order.
+ * The policy (records, stamps, misses, counts) is the same as with the GPU
+ * reading cold weights. Needs logits and E <= 512 (MOE_E_INVAL otherwise);
+ * not capturable (MOE_E_CAPTURING). If the host threads cannot answer within
+ * 10 s, y leaves those picks out and the step's moe_cache_step returns
+ * MOE_E_HIP. */
 MOE_API int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
                 const float* x, const float* logits, float* y,
                 int32_t* ids, float* w, uint32_t flags);

@@ -26,6 +26,8 @@ MOE_E_CAPTURING = -5
 MOE_Q4_32_F16 = 1
 MOE_ACCUMULATE = 1
 MOE_MAX_SWAP_LEAD = 8
+MOE_COLD_GPU = 0
+MOE_COLD_CPU = 1
 MOE_HOST_COHERENT = 0
 MOE_HOST_NONCOHERENT = 1
 MOE_POOL_PER_LAYER = 0
@@ -45,13 +47,14 @@ class moe_config(C.Structure):
         ("window_tokens", C.c_int32), ("admit_misses", C.c_int32), ("max_batch_tokens", C.c_int32),
         ("max_prefill_tokens", C.c_int32), ("device", C.c_int32), ("host_alloc", C.c_int32),
         ("host_sets", C.c_int32), ("stream", C.c_void_p), ("capture_picks", C.c_int32), ("pool_mode", C.c_int32),
-        ("swaps_per_step", C.c_int32), ("swap_lead", C.c_int32),
+        ("swaps_per_step", C.c_int32), ("swap_lead", C.c_int32), ("cold_exec", C.c_int32),
+        ("cpu_threads", C.c_int32),
     ]
 
 
 class moe_info(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("slots_per_layer", "expert_bytes", "pool_bytes", "host_bytes",
-                                        "staging_experts", "clock", "steps")]
+                                        "staging_experts", "clock", "steps", "host_threads", "host_isa")]
 
 
 class moe_step_stats(C.Structure):
@@ -145,18 +148,20 @@ def moe_expert_bytes(hidden: int, ffn: int) -> int:
 
 def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reserve_bytes=0, window_tokens=64,
                admit_misses=2, max_batch_tokens=64, max_prefill_tokens=0, device=0, host_alloc=MOE_HOST_COHERENT,
-               host_sets=0, stream=None, capture_picks=None, pool_mode=0, swaps_per_step=0, swap_lead=0):
+               host_sets=0, stream=None, capture_picks=None, pool_mode=0, swaps_per_step=0, swap_lead=0,
+               cold_exec=MOE_COLD_GPU, cpu_threads=0):
     """Returns an opaque context handle.
 
     stream: a torch.cuda.Stream, a raw hipStream_t int, or None for torch's
     current stream on the device (0, the null stream, is a valid handle).
-    capture_picks: None for top_k (one token's picks per layer), 0 for off.
+    capture_picks: None for top_k (one token's picks per layer; 0 with cold_exec=MOE_COLD_CPU), 0 for off.
+    cold_exec: MOE_COLD_GPU (zero-copy reads of cold experts) or MOE_COLD_CPU (host threads compute them).
     pool_mode: MOE_POOL_PER_LAYER (slots per layer) or MOE_POOL_GLOBAL (one pool for all layers).
     swaps_per_step: admissions per cache step (0: no limit); swap_lead: cache steps an admission waits
     for its copy before its table entry flips (0: at once).
     """
     if capture_picks is None:
-        capture_picks = top_k
+        capture_picks = 0 if cold_exec == MOE_COLD_CPU else top_k
     if stream is None:
         stream = 0
         try:
@@ -170,7 +175,7 @@ def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reser
         stream = stream.cuda_stream
     cfg = moe_config(n_layers, n_experts, top_k, hidden, ffn, MOE_Q4_32_F16, pool_budget_bytes, reserve_bytes,
                      window_tokens, admit_misses, max_batch_tokens, max_prefill_tokens, device, host_alloc,
-                     host_sets, stream, capture_picks, pool_mode, swaps_per_step, swap_lead)
+                     host_sets, stream, capture_picks, pool_mode, swaps_per_step, swap_lead, cold_exec, cpu_threads)
     out = C.c_void_p()
     rc = lib().moe_create(C.byref(cfg), C.byref(out))
     if rc != MOE_OK:

@@ -17,7 +17,11 @@ LIB = os.path.join(LIBDIR, "libmoe_offload.so")
 OBJDIR = os.path.join(ROOT, "_build", "moe_offload")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["route.hip", "decode.hip", "prefill_kernels.hip", "runtime.cpp", "prefill.cpp"]
+SOURCES = ["route.hip", "decode.hip", "prefill_kernels.hip", "runtime.cpp", "prefill.cpp", "host_experts.cpp"]
+# plain C++ with no HIP in it (x86 vector code chosen at run time), built by the host compiler
+HOST_ONLY = {"host_experts.cpp"}
+CXX = os.environ.get("CXX_HOST", "g++")
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -33,8 +37,11 @@ FLAGS = [
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(OBJDIR, src + ".o")
-    lang = [] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [HIPCC, *FLAGS, *lang, "-c", path, "-o", obj]
+    if src in HOST_ONLY:
+        cmd = [CXX, *HOST_FLAGS, "-c", path, "-o", obj]
+    else:
+        lang = [] if src.endswith(".hip") else ["-x", "hip"]
+        cmd = [HIPCC, *FLAGS, *lang, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -48,7 +55,7 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

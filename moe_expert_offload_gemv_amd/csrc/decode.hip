@@ -254,6 +254,20 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
       if (r.w_user) r.w_user[p] = w;
       if (p == 0) atomicMax(&r.ctrl->step_tokens, (uint32_t)r.T);
     }
+    if (r.pub_seq) {  // the host threads compute the cold picks: hand the pick over
+      if (pick == 0) {
+        const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)t * a.H);
+        float4* dst = reinterpret_cast<float4*>(r.pub_x + (int64_t)t * a.H);
+        for (int i = lane; i < a.H / 4; i += 64) dst[i] = src[i];
+      }
+      if (lane == 0) {
+        r.pub_e[p] = e;
+        r.pub_w[p] = w;
+        r.pub_kind[p] = hot ? 0 : 1;
+      }
+      __threadfence_system();  // the row and the entry reach host memory before the flag
+      if (lane == 0) __hip_atomic_store(&r.pub_seq[p], r.pub_value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
   }
   if (!wanted<MODE>(hot ? kHot : kCold)) return;
 
@@ -386,7 +400,47 @@ __global__ __launch_bounds__(256) void gemv_down_combine_kernel(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// combine with the cold picks computed by the host threads. grid = (row
+// chunks of 256 of H, tokens). Thread 0 of each group waits (bounded) for the
+// host's answer; the sum runs in pick order like gemv_down_combine_kernel's.
+__global__ __launch_bounds__(256) void host_combine_kernel(HostCombineArgs a) {
+  __shared__ int answered;
+  if (threadIdx.x == 0) {
+    uint32_t i = 0;
+    for (; i < a.max_polls; ++i) {
+      const uint32_t d = __hip_atomic_load(a.done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
+      if ((int32_t)(d - a.seq) >= 0) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+    const bool ok = i < a.max_polls && __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == 0;
+    answered = ok;
+    if (!ok) atomicOr(&a.ctrl->host_fault, 1u);
+  }
+  __syncthreads();
+  const int t = blockIdx.y;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.H) return;
+  float acc = 0.f;
+  for (int i = 0; i < a.k; ++i) {
+    const int64_t p = (int64_t)t * a.k + i;
+    float v;
+    if (a.kind[p] & kCold)
+      v = answered ? __hip_atomic_load(a.y_cold + p * a.H + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0.f;
+    else
+      v = a.ypick[p * a.H + r];
+    acc = fmaf(a.w[p], v, acc);
+  }
+  float* yp = a.y + (int64_t)t * a.H + r;
+  *yp = a.accumulate ? *yp + acc : acc;
+}
+
+// ---------------------------------------------------------------------------
 // launchers
+
+hipError_t launch_host_combine(const HostCombineArgs& a, const Launch& l) {
+  if (a.T < 1 || a.k < 1 || a.H < 1 || !a.done || !a.status || !a.y_cold) return hipErrorInvalidValue;
+  return launch(host_combine_kernel, dim3((a.H + 255) / 256, a.T), dim3(256), l, a);
+}
 
 bool gemv_shape(int kb, GemvShape* out) {
   if (kb <= 0) return false;

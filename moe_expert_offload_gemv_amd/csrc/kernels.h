@@ -12,7 +12,8 @@ namespace moe {
 struct Ctrl {
   uint32_t clock;        // token clock of token 0 of the current step
   uint32_t step_tokens;  // max n_tokens over the forwards of the step
-  uint32_t reserved[2];
+  uint32_t host_fault;   // set when a forward's cold picks got no answer from the host threads
+  uint32_t reserved;
 };
 
 // A pick record: (clock << 32) | hit << 31 | layer << 12 | expert. The miss
@@ -85,6 +86,16 @@ struct RouteArgs {
   int32_t capture_picks; // picks p < capture_picks of a layer may capture their cold reads:
   const uint32_t* last_miss;  // [E] the layer's last-miss clocks as the step began; a cold
   int32_t window, admit_misses;  // pick captures when the cache step will admit it from them
+  // hand-off to the host threads (cold picks computed on the CPU), device
+  // addresses of pinned memory; pub_seq == nullptr: off. The routing wave of
+  // pick p writes pub_e/pub_w/pub_kind[p] (and the token's x row into pub_x
+  // for the first pick of a token), then pub_seq[p] = pub_value.
+  uint32_t* pub_seq;
+  int32_t* pub_e;
+  float* pub_w;
+  int32_t* pub_kind;
+  float* pub_x;
+  uint32_t pub_value;
 };
 hipError_t launch_route(const RouteArgs& a, const Launch& l);
 
@@ -117,6 +128,25 @@ constexpr int kFusedRouteMaxExperts = 512;
 hipError_t launch_gemv_route_gateup(const GemvArgs& a, const RouteArgs& r, const Launch& l, int mode);
 hipError_t launch_gemv_down_pick(const GemvArgs& a, const Launch& l, int mode);
 hipError_t launch_gemv_down_combine(const GemvArgs& a, const Launch& l, int mode);
+
+// Combine when the host threads computed the cold picks: wait until *done
+// reaches seq (at most max_polls polls; then ctrl->host_fault is set and the
+// cold picks count as zero), then y[t] = (y[t] if accumulate) + sum over the
+// picks in order of w[p] * (cold ? y_cold[p] : ypick[p]).
+struct HostCombineArgs {
+  const float* ypick;     // [P][H] hot picks (device)
+  const float* w;         // [P]
+  const uint8_t* kind;    // [P]
+  const float* y_cold;    // [P][H] cold picks (pinned host memory, device address)
+  const uint32_t* done;   // pinned host memory, device address
+  const uint32_t* status; // pinned host memory, device address: nonzero = no answer
+  uint32_t seq;
+  uint32_t max_polls;
+  float* y;               // [T][H]
+  int32_t T, k, H, accumulate;
+  Ctrl* ctrl;
+};
+hipError_t launch_host_combine(const HostCombineArgs& a, const Launch& l);
 
 // ---------------------------------------------------------------------------
 // prompt pass (prefill_kernels.hip)

@@ -24,6 +24,7 @@
 #include <vector>
 
 #include "../../include/moe_offload.h"
+#include "host_experts.h"
 #include "kernels.h"
 #include "runtime.h"
 
@@ -118,6 +119,10 @@ static void ctx_release(moe_ctx* c) {
   if (!c) return;
   DeviceGuard g(c->device);
   (void)hipStreamSynchronize(c->stream);
+  // the stream is drained, so every submitted hand-off was answered; stop the
+  // host threads before their mailbox goes away
+  if (c->hx) moe_host::executor_destroy(c->hx);
+  c->hx = nullptr;
   for (void* p : c->dev_allocs) (void)hipFree(p);
   for (void* p : c->host_allocs) (void)hipHostFree(p);
   for (void* r : c->routers)
@@ -160,6 +165,8 @@ int moe_ctx_host_alloc(moe_ctx* c, void** p, size_t bytes, unsigned flags, const
   return MOE_OK;
 }
 
+static int host_exec_create(moe_ctx* c);
+
 extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   g_create_error.clear();
   if (!cfg || !out) return g_create_error = "null config or output", MOE_E_INVAL;
@@ -173,6 +180,8 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
       k.capture_picks < 0 || k.capture_picks > k.max_batch_tokens * k.top_k ||
       (k.pool_mode != MOE_POOL_PER_LAYER && k.pool_mode != MOE_POOL_GLOBAL) || k.swaps_per_step < 0 ||
       k.swap_lead < 0 || k.swap_lead > MOE_MAX_SWAP_LEAD ||
+      (k.cold_exec != MOE_COLD_GPU && k.cold_exec != MOE_COLD_CPU) || k.cpu_threads < 0 || k.cpu_threads > 256 ||
+      (k.cold_exec == MOE_COLD_CPU && k.capture_picks != 0) ||
       (k.host_alloc != MOE_HOST_COHERENT && k.host_alloc != MOE_HOST_NONCOHERENT))
     return g_create_error = "config field out of range", MOE_E_INVAL;
   moe::GemvShape s1, s2;
@@ -302,6 +311,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
     }
     c->swap_recorded.assign(k.swap_lead + 1, 0);
   }
+  if (k.cold_exec == MOE_COLD_CPU && (rc = host_exec_create(c))) return fail(rc);
   if (c->d_cap_tag && hipMemset(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride) != hipSuccess)
     return fail(MOE_E_HIP);
   if (c->d_last_miss && hipMemset(c->d_last_miss, 0, sizeof(uint32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
@@ -310,7 +320,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if (hipMemset(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_stamps, 0, sizeof(uint32_t) * G * std::max<int64_t>(S, 1)) != hipSuccess)
     return fail(MOE_E_HIP);
-  Ctrl z{1, 0, {0, 0}};
+  Ctrl z{1, 0, 0, 0};
   if (hipMemcpy(c->d_ctrl, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return fail(MOE_E_HIP);
   // events for kernel timing: a start/stop pair per kernel of a forward,
   // enough for one step of every layer
@@ -324,6 +334,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   }
   c->timed_tokens.assign(n_timed, 0);
   c->timed_fused.assign(n_timed, 0);
+  c->timed_cpu.assign(n_timed, 0);
   for (int i = 0; i < 4 && k.max_prefill_tokens > 0; ++i) {
     hipEvent_t ev;
     if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return fail(MOE_E_HIP);
@@ -410,13 +421,57 @@ extern "C" int moe_seed(moe_ctx* c, const uint32_t* freq) {
   HIP_TRY(c, hipMemsetAsync(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride, c->stream));
   if (c->d_cap_tag) HIP_TRY(c, hipMemsetAsync(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride, c->stream));
   if (c->d_last_miss) HIP_TRY(c, hipMemsetAsync(c->d_last_miss, 0, sizeof(uint32_t) * L * E, c->stream));
-  *c->h_ctrl = Ctrl{1, 0, {0, 0}};
+  *c->h_ctrl = Ctrl{1, 0, 0, 0};
   HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   c->clock = 1;
   c->steps = 0;
   c->last_log.clear();
   c->seeded = true;
+  return MOE_OK;
+}
+
+// The mailbox of the host threads (one pinned, mapped allocation) and the
+// threads themselves.
+static int host_exec_create(moe_ctx* c) {
+  const int64_t P = (int64_t)c->cfg.max_batch_tokens * c->k, T = c->cfg.max_batch_tokens;
+  auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
+  c->mb_off_done = 0;
+  c->mb_off_status = 64;
+  c->mb_off_seq = 256;
+  c->mb_off_e = c->mb_off_seq + up(4 * P);
+  c->mb_off_w = c->mb_off_e + up(4 * P);
+  c->mb_off_kind = c->mb_off_w + up(4 * P);
+  c->mb_off_x = c->mb_off_kind + up(4 * P);
+  c->mb_off_y = c->mb_off_x + up(4 * T * c->H);
+  const int64_t bytes = c->mb_off_y + up(4 * P * c->H);
+  int rc;
+  if ((rc = moe_ctx_host_alloc(c, (void**)&c->mbox, (size_t)bytes, hipHostMallocMapped | hipHostMallocCoherent,
+                               "host hand-off mailbox")))
+    return rc;
+  std::memset(c->mbox, 0, (size_t)bytes);
+  void* dp = nullptr;
+  HIP_TRY(c, hipHostGetDevicePointer(&dp, c->mbox, 0));
+  c->mbox_dev = (uint8_t*)dp;
+  moe_host::ExpertPlanes pl{c->lay.gate_nib, c->lay.gate_scl, c->lay.up_nib, c->lay.up_scl,
+                            c->lay.down_nib, c->lay.down_scl, c->lay.bytes};
+  moe_host::Mailbox mb;
+  mb.done = (uint32_t*)(c->mbox + c->mb_off_done);
+  mb.status = (uint32_t*)(c->mbox + c->mb_off_status);
+  mb.pick_seq = (const uint32_t*)(c->mbox + c->mb_off_seq);
+  mb.pick_e = (const int32_t*)(c->mbox + c->mb_off_e);
+  mb.pick_kind = (const int32_t*)(c->mbox + c->mb_off_kind);
+  mb.x = (const float*)(c->mbox + c->mb_off_x);
+  mb.y_cold = (float*)(c->mbox + c->mb_off_y);
+  int threads = c->cfg.cpu_threads;
+  if (threads == 0) {  // every hardware thread but one, which is left to the caller's launches
+    const unsigned n = std::thread::hardware_concurrency();
+    threads = (int)std::max(1u, (n ? n : 2) - 1);
+  }
+  std::string err;
+  c->hx = moe_host::executor_create(threads, c->H, c->F, c->k, (int)T, pl, mb, &err);
+  if (!c->hx) return moe_ctx_fail(c, MOE_E_NOMEM, "%s", err.c_str());
+  c->hx_threads = threads;
   return MOE_OK;
 }
 
@@ -477,7 +532,15 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   // with logits at hand the gate/up GEMV routes by itself (one launch less on
   // the critical path); a router chain runs in its own launch first
   const bool fused = logits && c->E <= moe::kFusedRouteMaxExperts;
+  if (c->hx) {
+    if (!fused)
+      return moe_ctx_fail(c, MOE_E_INVAL, "forward: with cold_exec CPU the forward needs logits and E <= %d",
+                          moe::kFusedRouteMaxExperts);
+    if (stream_capturing(c->stream))
+      return moe_ctx_fail(c, MOE_E_CAPTURING, "forward with cold_exec CPU while capturing");
+  }
   if (ev) c->timed_fused[c->timed_pending - 1] = fused ? 1 : 0;
+  if (ev) c->timed_cpu[c->timed_pending - 1] = c->hx ? 1 : 0;
   if (!fused) HIP_TRY(c, moe::launch_route(ra, on(A, kRoute)));
 
   moe::GemvArgs ga{};
@@ -495,6 +558,32 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   dn.x = c->d_h;
   dn.out = y;
   dn.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+  if (c->hx) {
+    // the GPU computes the hot picks while the host threads compute the cold
+    // ones from the routing and activations the gate/up launch hands over
+    const uint32_t seq = ++c->hx_seq ? c->hx_seq : ++c->hx_seq;  // 0 is the mailbox's initial value
+    ra.pub_seq = (uint32_t*)(c->mbox_dev + c->mb_off_seq);
+    ra.pub_e = (int32_t*)(c->mbox_dev + c->mb_off_e);
+    ra.pub_w = (float*)(c->mbox_dev + c->mb_off_w);
+    ra.pub_kind = (int32_t*)(c->mbox_dev + c->mb_off_kind);
+    ra.pub_x = (float*)(c->mbox_dev + c->mb_off_x);
+    ra.pub_value = seq;
+    HIP_TRY(c, moe::launch_gemv_route_gateup(ga, ra, on(A, kHotGateUp), moe::kOnlyHot));
+    moe_host::executor_submit(c->hx, seq, n_tokens, c->host_layers[layer]);
+    HIP_TRY(c, moe::launch_gemv_down_pick(dn, on(A, kHotDown), moe::kOnlyHot));
+    moe::HostCombineArgs hc{};
+    hc.ypick = c->d_ypick, hc.w = c->d_w, hc.kind = c->d_kind;
+    hc.y_cold = (const float*)(c->mbox_dev + c->mb_off_y);
+    hc.done = (const uint32_t*)(c->mbox_dev + c->mb_off_done);
+    hc.status = (const uint32_t*)(c->mbox_dev + c->mb_off_status);
+    hc.seq = seq;
+    hc.max_polls = 1u << 22;  // seconds at the poll rate of pinned memory; the host answers within 10 s
+    hc.y = y;
+    hc.T = n_tokens, hc.k = c->k, hc.H = c->H, hc.accumulate = dn.accumulate;
+    hc.ctrl = c->d_ctrl;
+    HIP_TRY(c, moe::launch_host_combine(hc, on(A, kColdDownCombine)));
+    return MOE_OK;
+  }
   if (!ev) {
     // hot picks stream from HBM while cold picks stream over PCIe, in one launch
     if (fused)
@@ -528,6 +617,7 @@ static int flush_profile(moe_ctx* c) {
     for (int j = 0; j < kTimedKernels; ++j) {
       t[j] = 0.f;
       if (j == kRoute && c->timed_fused[i]) continue;
+      if (j == kColdGateUp && c->timed_cpu[i]) continue;  // the host threads run the cold gate/up
       HIP_TRY(c, hipEventElapsedTime(&t[j], c->events[2 * (kTimedKernels * (size_t)i + j)],
                                      c->events[2 * (kTimedKernels * (size_t)i + j) + 1]));
     }
@@ -589,6 +679,7 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
                               c->stream));
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   const Ctrl st = *c->h_ctrl;
+  const bool host_fault = st.host_fault != 0;
   if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * GS);
   // records of this step carry clocks in [clock, clock + step tokens); older ones are stale
   int64_t hits = 0;
@@ -726,7 +817,7 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
                               c->stream));
   }
   c->clock += st.step_tokens;
-  *c->h_ctrl = Ctrl{(uint32_t)c->clock, 0, {0, 0}};
+  *c->h_ctrl = Ctrl{(uint32_t)c->clock, 0, 0, 0};
   HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
 
   if (out) {
@@ -742,6 +833,10 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     out->copied_pcie_bytes = copied_pcie * B;
   }
   c->steps += 1;
+  if (host_fault)
+    return moe_ctx_fail(c, MOE_E_HIP,
+                        "cache_step: a forward of this step got no answer from the host threads (its cold picks "
+                        "were left out of y)");
   return MOE_OK;
 }
 
@@ -755,6 +850,10 @@ extern "C" int moe_get_info(moe_ctx* c, moe_info* out) {
   out->pool_bytes = (int64_t)c->groups * c->S * c->B;
   out->host_bytes = (int64_t)c->host_sets * c->E * c->B;
   out->staging_experts = c->n_staging;
+  out->host_threads = c->hx ? c->hx_threads : 0;
+  out->host_isa = !c->hx ? 0 : std::strcmp(moe_host::executor_isa(c->hx), "avx512") == 0 ? 3
+                  : std::strcmp(moe_host::executor_isa(c->hx), "avx2") == 0           ? 2
+                                                                                      : 1;
   out->clock = c->clock;
   out->steps = c->steps;
   return MOE_OK;

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "../../include/moe_offload.h"
+#include "host_experts.h"
 #include "kernels.h"
 
 // kernels of a forward, in the order of their timing events
@@ -75,6 +76,14 @@ struct moe_ctx {
   hipStream_t swap_stream = nullptr;   // copies from pinned memory of pending admissions
   std::vector<hipEvent_t> swap_events; // [swap_lead + 1]: end of a step's swap copies
   std::vector<char> swap_recorded;     // [swap_lead + 1]: the event holds a step's copies
+  // cold picks on the host threads (cold_exec CPU): mailbox in pinned memory
+  moe_host::Executor* hx = nullptr;
+  int32_t hx_threads = 0;
+  uint32_t hx_seq = 0;                 // sequence value of the last hand-off
+  uint8_t* mbox = nullptr;             // host address
+  uint8_t* mbox_dev = nullptr;         // device address of the same
+  int64_t mb_off_done = 0, mb_off_status = 0, mb_off_seq = 0, mb_off_e = 0, mb_off_w = 0, mb_off_kind = 0,
+          mb_off_x = 0, mb_off_y = 0;
   std::vector<int32_t> cap_of;         // [L][E] captured pick of the expert in the step, or -1
   std::vector<int64_t> cap_touched;    // entries of cap_of set in the step
   std::vector<char> registered;        // per host set
@@ -87,6 +96,7 @@ struct moe_ctx {
   std::vector<hipEvent_t> events;      // start/stop per kernel per timed forward
   std::vector<int32_t> timed_tokens;   // n_tokens of each pending timed forward
   std::vector<uint8_t> timed_fused;    // 1: its routing ran inside the gate/up GEMV (no routing interval)
+  std::vector<uint8_t> timed_cpu;      // 1: its cold gate/up ran on the host threads (no interval)
   int32_t timed_pending = 0;
   moe_profile_stats prof{};
 

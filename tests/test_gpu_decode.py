@@ -36,9 +36,14 @@ def _compare_policy(d: Decode, pol, st_gpu, st_orc, layers):
 
 
 def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_alloc=moe.MOE_HOST_COHERENT,
-                capture_picks=None, copies=None, pool="layer", swaps=(0, 0)):
+                capture_picks=None, copies=None, pool="layer", swaps=(0, 0), cold_exec=moe.MOE_COLD_GPU,
+                cpu_threads=0):
     d = Decode(wl, slots=slots, seed=seed, host_alloc=host_alloc, capture_picks=capture_picks, pool=pool,
-               swaps_per_step=swaps[0], swap_lead=swaps[1])
+               swaps_per_step=swaps[0], swap_lead=swaps[1], cold_exec=cold_exec, cpu_threads=cpu_threads)
+    if cold_exec == moe.MOE_COLD_CPU:
+        info = moe.moe_get_info(d.ctx)
+        print("host threads", info["host_threads"], "isa code", info["host_isa"])
+        assert info["host_threads"] >= 1 and info["host_isa"] >= 1
     pol = oracle_policy(wl, slots, seed=seed, pool=pool, swaps_per_step=swaps[0], swap_lead=swaps[1])
     logits = zipf_logits(wl)
     L, T, k, H = wl.n_layers, wl.tokens, wl.top_k, wl.hidden
@@ -355,3 +360,66 @@ def test_swap_budget_and_lead_bit_exact(capture_picks, budget, lead):
 def test_swap_lead_global_pool_window_admission():
     _run_decode(REDUCED.with_(name="decode-e64k8-h2048f1024-l4-b1-global-lead"), slots=104, check_every=4,
                 pool="global", capture_picks=0, swaps=(4, 1))
+
+
+# ---------------------------------------------------------------------------
+# cold picks computed by the host threads (cold_exec = MOE_COLD_CPU)
+
+@pytest.mark.parametrize("cpu_threads", [0, 3])
+def test_cold_picks_on_host_threads_bit_exact_policy(cpu_threads):
+    # every step's outputs checked: cold picks come from the host's answer,
+    # hot ones from the GPU, summed in pick order
+    wl = REDUCED.with_(name="decode-e64k8-h2048f1024-l4-b1-hostcold", steps=16)
+    copies = {}
+    _run_decode(wl, slots=26, check_every=1, copies=copies, cold_exec=moe.MOE_COLD_CPU, cpu_threads=cpu_threads)
+    # nothing was captured: every promotion is a copy from pinned memory
+    assert copies["copied"] > 0 and copies["pcie"] == copies["copied"]
+
+
+def test_cold_picks_on_host_threads_batch_shared_experts():
+    # five tokens per step: tokens that picked the same cold expert share one
+    # pass of the host threads over its weights
+    wl = Workload("decode-e64k8-h2048f1024-l2-b5-hostcold", 102, 2, 64, 8, 2048, 1024, tokens=5, steps=8,
+                  zipf_s=1.1, slots=20, rotation=20)
+    _run_decode(wl, slots=20, check_every=1, cold_exec=moe.MOE_COLD_CPU)
+
+
+def test_cold_picks_on_host_threads_global_pool_swap_lead_cold_start():
+    wl = Workload("decode-e32k4-h256f512-l3-b2-hostcold", 113, 3, 32, 4, 256, 512, tokens=2, steps=24, zipf_s=1.1,
+                  slots=8, rotation=12)
+    _run_decode(wl, slots=24, check_every=3, seed=False, pool="global", swaps=(3, 1), cold_exec=moe.MOE_COLD_CPU)
+
+
+def test_cold_picks_on_host_threads_accumulate_and_errors():
+    wl = Workload("decode-e32k4-h256f512-l1-b3-hostcold", 114, 1, 32, 4, 256, 512, tokens=3, steps=1, zipf_s=1.1,
+                  slots=0)
+    d = Decode(wl, slots=0, cold_exec=moe.MOE_COLD_CPU, cpu_threads=2)  # every pick cold
+    x32 = activations(wl, 0)
+    z = zipf_logits(wl)[0, 0]
+    y0 = np.random.default_rng(1).standard_normal((3, 256)).astype(np.float32)
+    y = _dev(y0)
+    moe.moe_forward(d.ctx, 0, 3, _dev(x32), _dev(z), y, flags=moe.MOE_ACCUMULATE)
+    ids, _ = oracle.route(z, 4)
+    y_ref, _, _ = oracle.moe_layer(32, 4, 256, 512, d.experts(0, ids), x32.astype(np.float64), logits=z)
+    assert token_rel_err(y.cpu().numpy() - y0, y_ref) < TOL
+    st = moe.moe_cache_step(d.ctx)
+    assert st["misses"] == 12 and st["hits"] == 0
+    # the hand-off needs logits
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_forward(d.ctx, 0, 3, _dev(x32), None, y)
+    assert ei.value.code == moe.MOE_E_INVAL
+    # and is not capturable
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    xd, zd = _dev(x32), _dev(z)
+    d2 = Decode(wl, slots=0, cold_exec=moe.MOE_COLD_CPU, cpu_threads=2, stream=s)
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        rc = moe.lib().moe_forward(d2.ctx, 0, 3, xd.data_ptr(), zd.data_ptr(), y.data_ptr(), None, None, 0)
+        g.capture_end()
+    assert rc == moe.MOE_E_CAPTURING
+    d2.close()
+    d.close()
+    # capture of cold reads has nothing to capture with host threads
+    with pytest.raises(moe.MoeError):
+        moe.moe_create(1, 32, 4, 256, 512, 0, cold_exec=moe.MOE_COLD_CPU, capture_picks=4)
