@@ -349,11 +349,13 @@ def main():
         run_steps(moe, ctx, args.warmup, step)
         moe.moe_seed(ctx, freq)  # the timed region starts from the seeded pool at step 0
         torch.cuda.synchronize()
+        moe.moe_profile(ctx, 0)  # kernel timing off; host-thread counters start here
         acc = {}
         t0 = time.perf_counter()
         run_steps(moe, ctx, args.steps, step, acc)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+    host = moe.moe_profile(ctx, -1) if cold_exec == moe.MOE_COLD_CPU else None
     tokens = args.steps * T
     tps = tokens / elapsed
     log(f"timed: {args.steps} steps in {elapsed * 1e3:.1f} ms -> {tps:.1f} tokens/s; stats {acc}")
@@ -466,6 +468,19 @@ def main():
         log(f"side passes: hot {result['kernels_all_hot']} cold {result['kernels_all_cold']} "
             f"dma {result['pcie_dma_h2d_GBps']} GB/s")
 
+    if host is not None:
+        hb = host["host_expert_passes"] * B  # weight bytes read (tokens sharing an expert share the pass)
+        result["host_threads"] = {
+            "threads": info["host_threads"], "isa": {1: "scalar", 2: "avx2", 3: "avx512"}.get(info["host_isa"]),
+            "forwards": host["host_forwards"], "expert_passes": host["host_expert_passes"],
+            "picks": host["host_picks"],
+            "wait_us_per_forward": round(host["host_wait_ms"] / max(host["host_forwards"], 1) * 1e3, 2),
+            "compute_us_per_forward": round(host["host_compute_ms"] / max(host["host_forwards"], 1) * 1e3, 2),
+            "compute_us_per_expert_pass": round(host["host_compute_ms"] / max(host["host_expert_passes"], 1) * 1e3,
+                                                2),
+            # weight bytes of the cold picks / time computing them
+            "weight_GBps": round(hb / max(host["host_compute_ms"], 1e-9) / 1e6, 1)}
+        log(f"host threads: {result['host_threads']}")
     if request is not None:
         result["prompt_then_decode"] = request
     if not args.no_side_passes:

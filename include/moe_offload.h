@@ -191,6 +191,14 @@ typedef struct {
   int64_t prefill_pairs;      /* (token, pick) pairs the timed passes computed */
   int64_t prefill_tiles;      /* 64-row (expert, tile) pairs launched         */
   int64_t prefill_staged;     /* experts copied into borrowed staging blocks  */
+  /* cold_exec = MOE_COLD_CPU: the host threads, counted whether or not kernel
+     timing is on, since the last moe_profile with enable 0 or 1 (hand-offs
+     still in flight are counted once answered)                             */
+  int64_t host_forwards;      /* hand-offs answered                           */
+  int64_t host_expert_passes; /* distinct cold experts computed (per forward) */
+  int64_t host_picks;         /* cold picks computed                          */
+  double  host_wait_ms;       /* from taking a hand-off to seeing all picks   */
+  double  host_compute_ms;    /* computing the cold picks and answering       */
 } moe_profile_stats;
 
 /* Size in bytes of one expert (gate + up + down) in MOE_Q4_32_F16. */
@@ -248,8 +256,8 @@ MOE_API int moe_seed(moe_ctx* ctx, const uint32_t* freq);
  *
  * With cold_exec = MOE_COLD_CPU the cold picks are computed by the library's
  * host threads instead ([FORK] "How it works"): the gate/up launch computes
- * the hot picks and hands every pick (expert, weight, hot/cold) and the
- * token's x to pinned host memory; the host threads compute y_pick of each
+ * the hot picks and hands every pick (expert, hot/cold) and the token's x
+ * to pinned host memory; the host threads compute y_pick of each
  * cold pick (same formulas, fp32, AVX-512 where the host has it) and answer;
  * the last launch waits for the answer (bounded) and forms y in pick order.
  * The policy (records, stamps, misses, counts) is the same as with the GPU

@@ -254,20 +254,28 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
       if (r.w_user) r.w_user[p] = w;
       if (p == 0) atomicMax(&r.ctrl->step_tokens, (uint32_t)r.T);
     }
-    if (r.pub_seq) {  // the host threads compute the cold picks: hand the pick over
+  }
+  if (r.pub_seq && blockIdx.x == gridDim.x - 1) {
+    // the host threads compute the cold picks: the last work-group of each
+    // pick only hands the pick over (so no GEMV wave waits on host writes).
+    // System-scope stores write through the caches to host memory; once they
+    // are acknowledged the flag follows them. No cache-wide write-back (a
+    // system-scope release would write back all of L2).
+    if (wave == 0) {
       if (pick == 0) {
-        const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)t * a.H);
-        float4* dst = reinterpret_cast<float4*>(r.pub_x + (int64_t)t * a.H);
-        for (int i = lane; i < a.H / 4; i += 64) dst[i] = src[i];
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(a.x + (int64_t)t * a.H);
+        uint64_t* dst = reinterpret_cast<uint64_t*>(r.pub_x + (int64_t)t * a.H);
+        for (int i = lane; i < a.H / 2; i += 64)
+          __hip_atomic_store(dst + i, src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       }
-      if (lane == 0) {
-        r.pub_e[p] = e;
-        r.pub_w[p] = w;
-        r.pub_kind[p] = hot ? 0 : 1;
+      if (lane == 0) {  // the routing weight stays here: the host answers unweighted outputs
+        __hip_atomic_store(&r.pub_e[p], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&r.pub_kind[p], hot ? 0 : 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       }
-      __threadfence_system();  // the row and the entry reach host memory before the flag
-      if (lane == 0) __hip_atomic_store(&r.pub_seq[p], r.pub_value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      if (lane == 0) __hip_atomic_store(&r.pub_seq[p], r.pub_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
+    return;
   }
   if (!wanted<MODE>(hot ? kHot : kCold)) return;
 
@@ -401,23 +409,33 @@ __global__ __launch_bounds__(256) void gemv_down_combine_kernel(GemvArgs a) {
 
 // ---------------------------------------------------------------------------
 // combine with the cold picks computed by the host threads. grid = (row
-// chunks of 256 of H, tokens). Thread 0 of each group waits (bounded) for the
-// host's answer; the sum runs in pick order like gemv_down_combine_kernel's.
+// chunks of 256 of H, tokens). A token with a cold pick waits (bounded) for
+// the host's answer, polled by thread 0 of each group (a few groups: many
+// pollers of one host line slow the host threads' memory); the sum runs in
+// pick order like gemv_down_combine_kernel's. System-scope loads read host
+// memory past the caches; no acquire (that would invalidate the caches on
+// every poll).
 __global__ __launch_bounds__(256) void host_combine_kernel(HostCombineArgs a) {
   __shared__ int answered;
+  const int t = blockIdx.y;
   if (threadIdx.x == 0) {
-    uint32_t i = 0;
-    for (; i < a.max_polls; ++i) {
-      const uint32_t d = __hip_atomic_load(a.done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
-      if ((int32_t)(d - a.seq) >= 0) break;
-      __builtin_amdgcn_s_sleep(4);
+    bool cold = false;
+    for (int i = 0; i < a.k; ++i) cold |= (a.kind[(int64_t)t * a.k + i] & kCold) != 0;
+    bool ok = true;
+    if (cold) {
+      uint32_t n = 0;
+      uint64_t d = 0;
+      for (; n < a.max_polls; ++n) {
+        d = __hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if ((int32_t)((uint32_t)d - a.seq) >= 0) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      ok = n < a.max_polls && (d >> 32) == 0;
+      if (!ok) atomicOr(&a.ctrl->host_fault, 1u);
     }
-    const bool ok = i < a.max_polls && __hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == 0;
     answered = ok;
-    if (!ok) atomicOr(&a.ctrl->host_fault, 1u);
   }
   __syncthreads();
-  const int t = blockIdx.y;
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= a.H) return;
   float acc = 0.f;
@@ -438,9 +456,10 @@ __global__ __launch_bounds__(256) void host_combine_kernel(HostCombineArgs a) {
 // launchers
 
 hipError_t launch_host_combine(const HostCombineArgs& a, const Launch& l) {
-  if (a.T < 1 || a.k < 1 || a.H < 1 || !a.done || !a.status || !a.y_cold) return hipErrorInvalidValue;
+  if (a.T < 1 || a.k < 1 || a.H < 1 || !a.done || !a.y_cold || !a.ctrl) return hipErrorInvalidValue;
   return launch(host_combine_kernel, dim3((a.H + 255) / 256, a.T), dim3(256), l, a);
 }
+
 
 bool gemv_shape(int kb, GemvShape* out) {
   if (kb <= 0) return false;
@@ -469,7 +488,8 @@ hipError_t gateup_t(const GemvArgs& a, const Launch& l, int mode) {
 template <int LPR, int BPL>
 hipError_t route_gateup_t(const GemvArgs& a, const RouteArgs& r, const Launch& l, int mode) {
   constexpr int ROWS_WG = 4 * kNitGateUp * (64 / LPR);
-  const dim3 grid((a.F + ROWS_WG - 1) / ROWS_WG, a.T * a.k);
+  // one more work-group per pick hands the pick to the host threads
+  const dim3 grid((a.F + ROWS_WG - 1) / ROWS_WG + (r.pub_seq ? 1 : 0), a.T * a.k);
   if (mode == kOnlyHot)
     return launch(gemv_route_gateup_kernel<LPR, BPL, kNitGateUp, kOnlyHot>, grid, dim3(256), l, a, r);
   if (mode == kOnlyCold)

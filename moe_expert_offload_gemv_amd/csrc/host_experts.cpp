@@ -261,6 +261,7 @@ class Executor {
     {
       std::lock_guard<std::mutex> lk(qm_);
       q_.push_back(Job{seq, T, base});
+      queued_.fetch_add(1, std::memory_order_release);
     }
     qcv_.notify_one();
   }
@@ -270,12 +271,16 @@ class Executor {
   void coordinate() {
     for (;;) {
       Job j;
+      // a hand-off usually follows within microseconds: spin before sleeping
+      for (int spins = 0; spins < kSpinsBeforeSleep && queued_.load(std::memory_order_acquire) == 0; ++spins)
+        cpu_relax();
       {
         std::unique_lock<std::mutex> lk(qm_);
         qcv_.wait(lk, [&] { return quit_ || !q_.empty(); });
         if (q_.empty()) return;  // quit with nothing left
         j = q_.front();
         q_.pop_front();
+        queued_.fetch_sub(1, std::memory_order_relaxed);
       }
       run_job(j);
     }
@@ -285,13 +290,23 @@ class Executor {
 
   void run_job(const Job& j) {
     const int P = j.T * k_;
+    const auto w0 = std::chrono::steady_clock::now();
     // wait for every pick of the forward (bounded: a forward whose picks
-    // never arrive is answered with status 1 so the GPU's combine goes on)
+    // never arrive is answered with status 1 so the GPU's combine goes on).
+    // A pick already carrying a later forward's value means the GPU went on
+    // without this answer, which it does only for a forward with no cold
+    // pick: nothing to compute.
     uint32_t status = 0;
+    bool superseded = false;
     const auto t0 = std::chrono::steady_clock::now();
-    for (int p = 0; p < P && !status; ++p) {
+    for (int p = 0; p < P && !status && !superseded; ++p) {
       int spins = 0;
-      while (load_acquire(&mb_.pick_seq[p]) != j.seq) {
+      uint32_t v;
+      while ((v = load_acquire(&mb_.pick_seq[p])) != j.seq) {
+        if ((int32_t)(v - j.seq) > 0) {
+          superseded = true;
+          break;
+        }
         cpu_relax();
         if (++spins == 4096) {
           spins = 0;
@@ -302,10 +317,32 @@ class Executor {
         }
       }
     }
-    if (!status) compute(j, P);
-    __atomic_store_n(mb_.status, status, __ATOMIC_RELAXED);
-    __atomic_store_n(mb_.done, j.seq, __ATOMIC_RELEASE);
+    const auto c0 = std::chrono::steady_clock::now();
+    // (if the GPU overtakes while this runs, the forward had no cold pick and
+    // nobody reads what this writes)
+    if (!status && !superseded) compute(j, P);
+    __atomic_store_n(mb_.done, ((uint64_t)status << 32) | j.seq, __ATOMIC_RELEASE);
+    const auto c1 = std::chrono::steady_clock::now();
+    st_forwards_.fetch_add(1, std::memory_order_relaxed);
+    st_wait_ns_.fetch_add(std::chrono::duration_cast<std::chrono::nanoseconds>(c0 - w0).count(),
+                          std::memory_order_relaxed);
+    st_compute_ns_.fetch_add(std::chrono::duration_cast<std::chrono::nanoseconds>(c1 - c0).count(),
+                             std::memory_order_relaxed);
   }
+
+ public:
+  void stats(ExecStats* out, bool reset) {
+    if (out) {
+      out->forwards = st_forwards_.load();
+      out->expert_passes = st_passes_.load();
+      out->picks = st_picks_.load();
+      out->wait_ms = st_wait_ns_.load() * 1e-6;
+      out->compute_ms = st_compute_ns_.load() * 1e-6;
+    }
+    if (reset) st_forwards_ = 0, st_passes_ = 0, st_picks_ = 0, st_wait_ns_ = 0, st_compute_ns_ = 0;
+  }
+
+ private:
 
   void compute(const Job& j, int P) {
     // group the cold picks by expert, in order of first appearance
@@ -326,6 +363,8 @@ class Executor {
     }
     if (groups_.empty()) return;
     const int G = (int)groups_.size();
+    st_passes_.fetch_add(G, std::memory_order_relaxed);
+    for (const auto& g : groups_) st_picks_.fetch_add(g.n, std::memory_order_relaxed);
     const int kbh = H_ / 32, kbf = F_ / 32;
     // phase 1: gate/up rows of every group
     pool_.run([&](int i, int n) {
@@ -371,6 +410,9 @@ class Executor {
   }
 
   static constexpr int kPickTimeoutS = 10;
+  static constexpr int kSpinsBeforeSleep = 1 << 15;  // about a millisecond of pause instructions
+  std::atomic<int> queued_{0};
+  std::atomic<int64_t> st_forwards_{0}, st_passes_{0}, st_picks_{0}, st_wait_ns_{0}, st_compute_ns_{0};
   int H_, F_, k_, P_;
   ExpertPlanes pl_;
   Mailbox mb_;
@@ -405,5 +447,7 @@ void executor_destroy(Executor* ex) { delete ex; }
 void executor_submit(Executor* ex, uint32_t seq, int T, const uint8_t* layer_base) { ex->submit(seq, T, layer_base); }
 
 const char* executor_isa(const Executor* ex) { return ex->isa(); }
+
+void executor_stats(Executor* ex, ExecStats* out, bool reset) { ex->stats(out, reset); }
 
 }  // namespace moe_host

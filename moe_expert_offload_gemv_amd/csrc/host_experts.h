@@ -9,14 +9,17 @@
 // writes host memory.
 //
 // Hand-off per forward, numbered by a sequence value s:
-//   GPU: the routing wave of pick p writes expert, weight and kind of the pick
-//        (and, for the first pick of a token, the token's activations), then
-//        pick_seq[p] = s (system-scope release).
+//   GPU: a work-group of pick p writes expert and kind of the pick (and, for
+//        the first pick of a token, the token's activations) with stores that
+//        write through to host memory, waits for them, then pick_seq[p] = s.
 //   CPU: the coordinator thread waits until pick_seq[p] == s for every pick,
 //        computes y_cold[p] = W_down (silu(W_gate x) * (W_up x)) of every cold
-//        pick p (unweighted), writes status, then done = s (release).
-//   GPU: the combine waits (bounded) for done == s and adds the weighted
-//        picks in pick order, cold ones from y_cold.
+//        pick p (unweighted), then done = status << 32 | s (release).
+//   GPU: the combine of a token with a cold pick waits (bounded) for done ==
+//        s and adds the weighted picks in pick order, cold ones from y_cold.
+//        A forward with no cold pick does not wait, so the next forward may
+//        overwrite the mailbox before this side has read it: a pick flag
+//        already past s tells the coordinator that s needs nothing.
 // Forwards are answered in the order they were submitted.
 #pragma once
 #include <stdint.h>
@@ -33,8 +36,8 @@ struct ExpertPlanes {
 
 // Host addresses inside the pinned mailbox.
 struct Mailbox {
-  uint32_t* done;            // last answered sequence value
-  uint32_t* status;          // 0 ok; 1 the picks of a forward never arrived (timeout)
+  uint64_t* done;            // status << 32 | last answered sequence value; status 0 ok,
+                             // 1 the picks of the forward never arrived (timeout)
   const uint32_t* pick_seq;  // [P]
   const int32_t* pick_e;     // [P]
   const int32_t* pick_kind;  // [P] bit 0 set: cold
@@ -54,5 +57,14 @@ void executor_destroy(Executor* ex);
 void executor_submit(Executor* ex, uint32_t seq, int T, const uint8_t* layer_base);
 // Vector width the dot products use: "avx512", "avx2" or "scalar".
 const char* executor_isa(const Executor* ex);
+
+// Totals since the last reset: forwards answered, expert passes (one per
+// distinct cold expert of a forward), cold picks computed, time from taking a
+// forward to seeing all its picks, and time computing.
+struct ExecStats {
+  int64_t forwards, expert_passes, picks;
+  double wait_ms, compute_ms;
+};
+void executor_stats(Executor* ex, ExecStats* out, bool reset);
 
 }  // namespace moe_host

@@ -87,12 +87,11 @@ struct RouteArgs {
   const uint32_t* last_miss;  // [E] the layer's last-miss clocks as the step began; a cold
   int32_t window, admit_misses;  // pick captures when the cache step will admit it from them
   // hand-off to the host threads (cold picks computed on the CPU), device
-  // addresses of pinned memory; pub_seq == nullptr: off. The routing wave of
-  // pick p writes pub_e/pub_w/pub_kind[p] (and the token's x row into pub_x
+  // addresses of pinned memory; pub_seq == nullptr: off. An extra work-group
+  // per pick p writes pub_e/pub_kind[p] (and the token's x row into pub_x
   // for the first pick of a token), then pub_seq[p] = pub_value.
   uint32_t* pub_seq;
   int32_t* pub_e;
-  float* pub_w;
   int32_t* pub_kind;
   float* pub_x;
   uint32_t pub_value;
@@ -129,17 +128,17 @@ hipError_t launch_gemv_route_gateup(const GemvArgs& a, const RouteArgs& r, const
 hipError_t launch_gemv_down_pick(const GemvArgs& a, const Launch& l, int mode);
 hipError_t launch_gemv_down_combine(const GemvArgs& a, const Launch& l, int mode);
 
-// Combine when the host threads computed the cold picks: wait until *done
-// reaches seq (at most max_polls polls; then ctrl->host_fault is set and the
-// cold picks count as zero), then y[t] = (y[t] if accumulate) + sum over the
+// Combine when the host threads computed the cold picks: a token with a cold
+// pick waits until the low half of *done reaches seq (at most max_polls
+// polls; a nonzero high half, or no answer, sets ctrl->host_fault and counts
+// its cold picks as zero), then y[t] = (y[t] if accumulate) + sum over the
 // picks in order of w[p] * (cold ? y_cold[p] : ypick[p]).
 struct HostCombineArgs {
   const float* ypick;     // [P][H] hot picks (device)
   const float* w;         // [P]
   const uint8_t* kind;    // [P]
   const float* y_cold;    // [P][H] cold picks (pinned host memory, device address)
-  const uint32_t* done;   // pinned host memory, device address
-  const uint32_t* status; // pinned host memory, device address: nonzero = no answer
+  const uint64_t* done;   // pinned host memory, device address: status << 32 | last answered seq
   uint32_t seq;
   uint32_t max_polls;
   float* y;               // [T][H]
@@ -147,6 +146,7 @@ struct HostCombineArgs {
   Ctrl* ctrl;
 };
 hipError_t launch_host_combine(const HostCombineArgs& a, const Launch& l);
+
 
 // ---------------------------------------------------------------------------
 // prompt pass (prefill_kernels.hip)

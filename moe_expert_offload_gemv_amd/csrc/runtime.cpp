@@ -437,11 +437,9 @@ static int host_exec_create(moe_ctx* c) {
   const int64_t P = (int64_t)c->cfg.max_batch_tokens * c->k, T = c->cfg.max_batch_tokens;
   auto up = [](int64_t v) { return (v + 255) / 256 * 256; };
   c->mb_off_done = 0;
-  c->mb_off_status = 64;
   c->mb_off_seq = 256;
   c->mb_off_e = c->mb_off_seq + up(4 * P);
-  c->mb_off_w = c->mb_off_e + up(4 * P);
-  c->mb_off_kind = c->mb_off_w + up(4 * P);
+  c->mb_off_kind = c->mb_off_e + up(4 * P);
   c->mb_off_x = c->mb_off_kind + up(4 * P);
   c->mb_off_y = c->mb_off_x + up(4 * T * c->H);
   const int64_t bytes = c->mb_off_y + up(4 * P * c->H);
@@ -456,8 +454,7 @@ static int host_exec_create(moe_ctx* c) {
   moe_host::ExpertPlanes pl{c->lay.gate_nib, c->lay.gate_scl, c->lay.up_nib, c->lay.up_scl,
                             c->lay.down_nib, c->lay.down_scl, c->lay.bytes};
   moe_host::Mailbox mb;
-  mb.done = (uint32_t*)(c->mbox + c->mb_off_done);
-  mb.status = (uint32_t*)(c->mbox + c->mb_off_status);
+  mb.done = (uint64_t*)(c->mbox + c->mb_off_done);
   mb.pick_seq = (const uint32_t*)(c->mbox + c->mb_off_seq);
   mb.pick_e = (const int32_t*)(c->mbox + c->mb_off_e);
   mb.pick_kind = (const int32_t*)(c->mbox + c->mb_off_kind);
@@ -564,7 +561,6 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
     const uint32_t seq = ++c->hx_seq ? c->hx_seq : ++c->hx_seq;  // 0 is the mailbox's initial value
     ra.pub_seq = (uint32_t*)(c->mbox_dev + c->mb_off_seq);
     ra.pub_e = (int32_t*)(c->mbox_dev + c->mb_off_e);
-    ra.pub_w = (float*)(c->mbox_dev + c->mb_off_w);
     ra.pub_kind = (int32_t*)(c->mbox_dev + c->mb_off_kind);
     ra.pub_x = (float*)(c->mbox_dev + c->mb_off_x);
     ra.pub_value = seq;
@@ -574,8 +570,7 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
     moe::HostCombineArgs hc{};
     hc.ypick = c->d_ypick, hc.w = c->d_w, hc.kind = c->d_kind;
     hc.y_cold = (const float*)(c->mbox_dev + c->mb_off_y);
-    hc.done = (const uint32_t*)(c->mbox_dev + c->mb_off_done);
-    hc.status = (const uint32_t*)(c->mbox_dev + c->mb_off_status);
+    hc.done = (const uint64_t*)(c->mbox_dev + c->mb_off_done);
     hc.seq = seq;
     hc.max_polls = 1u << 22;  // seconds at the poll rate of pinned memory; the host answers within 10 s
     hc.y = y;
@@ -647,6 +642,13 @@ extern "C" int moe_profile(moe_ctx* c, int32_t enable, moe_profile_stats* out) {
     c->prof.down_bytes_per_pick = c->lay.bytes - c->lay.down_nib;
   } else if (enable == 0) {
     c->profiling = false;
+  }
+  if (c->hx && enable != -1) moe_host::executor_stats(c->hx, nullptr, true);
+  if (c->hx) {
+    moe_host::ExecStats hs{};
+    moe_host::executor_stats(c->hx, &hs, false);
+    c->prof.host_forwards = hs.forwards, c->prof.host_expert_passes = hs.expert_passes;
+    c->prof.host_picks = hs.picks, c->prof.host_wait_ms = hs.wait_ms, c->prof.host_compute_ms = hs.compute_ms;
   }
   if (out) *out = c->prof;
   return MOE_OK;

@@ -82,8 +82,7 @@ struct moe_ctx {
   uint32_t hx_seq = 0;                 // sequence value of the last hand-off
   uint8_t* mbox = nullptr;             // host address
   uint8_t* mbox_dev = nullptr;         // device address of the same
-  int64_t mb_off_done = 0, mb_off_status = 0, mb_off_seq = 0, mb_off_e = 0, mb_off_w = 0, mb_off_kind = 0,
-          mb_off_x = 0, mb_off_y = 0;
+  int64_t mb_off_done = 0, mb_off_seq = 0, mb_off_e = 0, mb_off_kind = 0, mb_off_x = 0, mb_off_y = 0;
   std::vector<int32_t> cap_of;         // [L][E] captured pick of the expert in the step, or -1
   std::vector<int64_t> cap_touched;    // entries of cap_of set in the step
   std::vector<char> registered;        // per host set

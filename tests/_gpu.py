@@ -90,28 +90,39 @@ class GraphDecode:
     forward, every layer adding its output into one residual buffer
     (MOE_ACCUMULATE), replayed per step, then the cache step. With
     snapshots the graph also copies the residual after every layer, so each
-    layer's output is the difference of two snapshots."""
+    layer's output is the difference of two snapshots. With cold_exec CPU
+    (not capturable) the same launches run eagerly each step, as bench.py
+    runs that mode."""
 
-    def __init__(self, wl: Workload, snapshots: bool = True, max_batch: int | None = None):
+    def __init__(self, wl: Workload, snapshots: bool = True, max_batch: int | None = None,
+                 cold_exec=moe.MOE_COLD_GPU, swaps=(0, 0)):
         import torch
 
         self.torch = torch
         self.wl = wl
         self.stream = torch.cuda.Stream()
-        self.d = Decode(wl, stream=self.stream, max_batch=max_batch or wl.tokens, keep_weights=False)
+        self.d = Decode(wl, stream=self.stream, max_batch=max_batch or wl.tokens, keep_weights=False,
+                        cold_exec=cold_exec, swaps_per_step=swaps[0], swap_lead=swaps[1])
         L, T, H, E = wl.n_layers, wl.tokens, wl.hidden, wl.n_experts
         self.xs = torch.zeros((L, T, H), dtype=torch.float32, device="cuda")
         self.zs = torch.zeros((L, T, E), dtype=torch.float32, device="cuda")
         self.res = torch.zeros((T, H), dtype=torch.float32, device="cuda")
         self.snap = torch.zeros((L, T, H), dtype=torch.float32, device="cuda") if snapshots else None
-        self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(self.stream):
-            with torch.cuda.graph(self.graph, stream=self.stream):
-                for layer in range(L):
-                    moe.moe_forward(self.d.ctx, layer, T, self.xs[layer], self.zs[layer], self.res,
-                                    flags=moe.MOE_ACCUMULATE)
-                    if snapshots:
-                        self.snap[layer].copy_(self.res)
+
+        def forward_all():
+            for layer in range(L):
+                moe.moe_forward(self.d.ctx, layer, T, self.xs[layer], self.zs[layer], self.res,
+                                flags=moe.MOE_ACCUMULATE)
+                if snapshots:
+                    self.snap[layer].copy_(self.res)
+
+        self.forward_all = forward_all
+        self.graph = None
+        if cold_exec == moe.MOE_COLD_GPU:
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(self.stream):
+                with torch.cuda.graph(self.graph, stream=self.stream):
+                    forward_all()
 
     def step(self, xs_step, logits_step):
         torch = self.torch
@@ -119,7 +130,10 @@ class GraphDecode:
             self.xs.copy_(torch.from_numpy(np.ascontiguousarray(xs_step)).cuda())
             self.zs.copy_(torch.from_numpy(np.ascontiguousarray(logits_step)).cuda())
             self.res.zero_()
-            self.graph.replay()
+            if self.graph is not None:
+                self.graph.replay()
+            else:
+                self.forward_all()
             st = moe.moe_cache_step(self.d.ctx)
         return st
 

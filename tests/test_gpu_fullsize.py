@@ -28,16 +28,17 @@ def _check_tables(g: GraphDecode, pol):
         assert np.array_equal(moe.moe_get_stamps(g.d.ctx, layer, g.d.S), tabs["stamps"][layer]), layer
 
 
-def _run(wl, steps, sample_steps, table_every, max_batch=None, sample_rows=None):
-    g = GraphDecode(wl, max_batch=max_batch)
+def _run(wl, steps, sample_steps, table_every, max_batch=None, sample_rows=None, cold_exec=moe.MOE_COLD_GPU,
+         swaps=(0, 0)):
+    g = GraphDecode(wl, max_batch=max_batch, cold_exec=cold_exec, swaps=swaps)
     try:
-        return _steps(g, wl, steps, sample_steps, table_every, sample_rows)
+        return _steps(g, wl, steps, sample_steps, table_every, sample_rows, swaps)
     finally:
         g.close()
 
 
-def _steps(g, wl, steps, sample_steps, table_every, sample_rows):
-    pol = oracle_policy(wl, wl.slots)
+def _steps(g, wl, steps, sample_steps, table_every, sample_rows, swaps=(0, 0)):
+    pol = oracle_policy(wl, wl.slots, swaps_per_step=swaps[0], swap_lead=swaps[1])
     logits = zipf_logits(wl, steps=steps)
     worst = 0.0
     hits = misses = 0
@@ -71,6 +72,16 @@ def test_decode_48_layers_512_experts_all_256_steps():
     worst, hit_rate = _run(wl, wl.steps, sample_steps={0, 131, 255}, table_every=32)
     print(f"worst layer error {worst:.2e}, hit rate {hit_rate:.4f}")
     assert 0.85 < hit_rate < 0.95
+
+
+def test_decode_48_layers_cold_picks_on_host_threads():
+    # the bench's host-thread configuration: eager launches, swap lead 1, 8
+    # swaps per step; most forwards have no cold pick and do not wait for the
+    # host, so later forwards overtake the host's reading of the mailbox
+    wl = WORKLOADS["decode-e512k8-h2048f1024-l48-b1"]
+    worst, hit_rate = _run(wl, 96, sample_steps={0, 50, 95}, table_every=16, cold_exec=moe.MOE_COLD_CPU,
+                           swaps=(8, 1))
+    print(f"worst layer error {worst:.2e}, hit rate {hit_rate:.4f}")
 
 
 def test_policy_2048_steps_with_rotation():
