@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 # HBM bytes per launch of the roofline kernel (gemv_route_gateup_kernel<64,1,4,1>, hot picks), from two rocprofv3
 # counter runs (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, scaled by a 1 GiB copy) over launches that served 7.14 hot picks
 # each (16.85 MB algorithmic); the summary and commands are under profiles/. Set to None when the kernel changes.
-ROOFLINE_TRAFFIC = None  # re-measure after a kernel change (last: 17.19e6 B over 16.85e6 B algorithmic)
+ROOFLINE_TRAFFIC = {"bytes_per_launch": 17193637, "algorithmic_bytes_per_launch": 16852979}
 PCIE_PEAK_GBPS = 64.0       # PCIe Gen5 x16, one direction
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA; fp16 (what the grouped GEMM runs) has the same rate
 METRIC = "MoE-layer decode tokens/s + effective weight GB/s vs HBM/PCIe roofline"
@@ -202,6 +202,49 @@ def request_pass(moe, torch, ctx, wl, freq, stream, prompt_tokens, decode_tokens
                                out["without_preheat"]["decode_tokens_per_s"], 4)
     del zp, zd, xp, yp
     return out
+
+
+def host_cold_pass(moe, torch, wl, stream, host_alloc, pool, x_all, logits_all, steps, warmup, swap_lead=1):
+    """The same decode with the cold picks computed by the host threads (eager launches: the hand-off is not
+    capturable), swap lead 1 (promotions are pinned-to-HBM copies here: no cold read to capture)."""
+    T, L = wl.tokens, wl.n_layers
+    ctx, freq = setup_ctx(moe, wl, wl.slots, stream, host_alloc, progress=False, capture_picks=0, pool=pool,
+                          swaps=(0, swap_lead), cold_exec=moe.MOE_COLD_CPU)
+    info = moe.moe_get_info(ctx)
+    x_steps = x_all.shape[0]
+    res = torch.zeros((T, wl.hidden), dtype=torch.float32, device="cuda")
+    xv = [[x_all[s, layer] for layer in range(L)] for s in range(x_steps)]
+    zv = [[logits_all[s, layer] for layer in range(L)] for s in range(wl.steps)]
+
+    def step(i):
+        res.zero_()
+        for layer in range(L):
+            moe.moe_forward(ctx, layer, T, xv[i % x_steps][layer], zv[i % wl.steps][layer], res,
+                            flags=moe.MOE_ACCUMULATE)
+
+    moe.moe_seed(ctx, freq)
+    with torch.cuda.stream(stream):
+        run_steps(moe, ctx, warmup, step)
+        moe.moe_seed(ctx, freq)
+        torch.cuda.synchronize()
+        moe.moe_profile(ctx, 0)
+        acc = {}
+        t0 = time.perf_counter()
+        run_steps(moe, ctx, steps, step, acc)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        host = moe.moe_profile(ctx, -1)
+    moe.moe_destroy(ctx)
+    passes = max(host["host_expert_passes"], 1)
+    return {
+        "tokens_per_s": round(steps * T / elapsed, 2), "ms_per_step": round(elapsed / steps * 1e3, 4),
+        "hit_rate": round(acc["hits"] / max(acc["hits"] + acc["misses"], 1), 4), "swap_lead": swap_lead,
+        "threads": info["host_threads"], "isa": {1: "scalar", 2: "avx2", 3: "avx512"}.get(info["host_isa"]),
+        "compute_us_per_expert_pass": round(host["host_compute_ms"] / passes * 1e3, 2),
+        "wait_us_per_forward": round(host["host_wait_ms"] / max(host["host_forwards"], 1) * 1e3, 2),
+        # weight bytes of the cold experts the host threads read / time computing them
+        "weight_GBps": round(passes * wl.expert_bytes / max(host["host_compute_ms"], 1e-9) / 1e6, 1),
+        "launch": "eager"}
 
 
 def cpu_baseline(wl, seconds, logits):
@@ -483,6 +526,11 @@ def main():
         log(f"host threads: {result['host_threads']}")
     if request is not None:
         result["prompt_then_decode"] = request
+    if not args.no_side_passes and cold_exec == moe.MOE_COLD_GPU and T == 1:
+        # the method's other way to serve misses, same workload, measured here (a context of its own)
+        result["cold_picks_on_host_threads"] = host_cold_pass(moe, torch, wl, stream, host_alloc, args.pool, x_all,
+                                                              logits_all, args.steps, args.warmup)
+        log(f"host-thread cold picks: {result['cold_picks_on_host_threads']}")
     if not args.no_side_passes:
         result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc) for name in PREFILL_WORKLOADS]
         log(f"prefill: {result['prefill']}")
