@@ -191,6 +191,8 @@ typedef struct {
   int64_t prefill_pairs;      /* (token, pick) pairs the timed passes computed */
   int64_t prefill_tiles;      /* 64-row (expert, tile) pairs launched         */
   int64_t prefill_staged;     /* experts copied into borrowed staging blocks  */
+  double  prefill_prep_ms;    /* block-scale transposition before the GEMMs
+                                 (passes of short tiles only)                 */
   /* cold_exec = MOE_COLD_CPU: the host threads, counted whether or not kernel
      timing is on, since the last moe_profile with enable 0 or 1 (hand-offs
      still in flight are counted once answered)                             */

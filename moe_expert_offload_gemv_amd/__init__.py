@@ -71,7 +71,8 @@ class moe_profile_stats(C.Structure):
                 ("hot_picks", C.c_int64), ("cold_picks", C.c_int64), ("gateup_bytes_per_pick", C.c_int64),
                 ("down_bytes_per_pick", C.c_int64), ("prefill_passes", C.c_int64),
                 ("prefill_gateup_ms", C.c_double), ("prefill_down_ms", C.c_double), ("prefill_pairs", C.c_int64),
-                ("prefill_tiles", C.c_int64), ("prefill_staged", C.c_int64), ("host_forwards", C.c_int64),
+                ("prefill_tiles", C.c_int64), ("prefill_staged", C.c_int64), ("prefill_prep_ms", C.c_double),
+                ("host_forwards", C.c_int64),
                 ("host_expert_passes", C.c_int64), ("host_picks", C.c_int64), ("host_wait_ms", C.c_double),
                 ("host_compute_ms", C.c_double)]
 

@@ -163,12 +163,20 @@ struct GemmArgs {
   ExpertLayout lay;
   _Float16* h16;                // gate/up output: h rows [P][N] fp16 in operand order
   float* y;                     // down output: y_pair [P][N]
+  const uint16_t* sclT;         // 64-row tiles: the pass's block scales transposed, expert e at
+  int64_t sclT_per_expert;      //   sclT + e * sclT_per_expert: gate [H/32][F], up [H/32][F], down
+                                //   [F/32][H]; 128-row tiles: nullptr (scales from the expert's planes)
   int32_t work, work_padded;    // set by the launcher: work items, padded to a multiple of 8
 };
 hipError_t launch_expert_histogram(const int32_t* ids, int32_t n_pairs, int32_t E, int32_t* counts, hipStream_t s);
 hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E, const int32_t* offsets,
                                  int32_t* perm, int32_t* inv, hipStream_t s);
 hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, hipStream_t s);
+// Scale planes of every expert with eaddr[e] != nullptr, transposed into
+// out + e * per_expert (layout of GemmArgs::sclT); per_expert = sclT_elements(lay).
+int64_t sclT_elements(const ExpertLayout& lay);
+hipError_t launch_transpose_scales(const uint8_t* const* eaddr, int32_t E, const ExpertLayout& lay, uint16_t* out,
+                                   const Launch& l);
 int gemm_features_per_tile(int mode, int bm);
 // mode 0 gate/up, 1 down; bm = 64 or 128 rows per tile (the tiles were cut to it);
 // a.items holds n_items work items

@@ -53,6 +53,7 @@ struct Prefill {
   _Float16* x16 = nullptr;      // [T][H] activations, fp16 in operand order
   _Float16* h16 = nullptr;      // [P][F] SwiGLU outputs, fp16 in operand order
   float* ypair = nullptr;       // [P][H]
+  uint16_t* sclT = nullptr;     // [E][sclT_elements]: the pass's block scales, transposed
   // pinned staging of the small transfers
   int32_t* h_counts = nullptr;
   int32_t* h_offsets = nullptr;
@@ -90,7 +91,8 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = dev((void**)&p->eaddr, sizeof(uint8_t*) * E, "prefill addresses")) ||
       (rc = dev((void**)&p->x16, sizeof(_Float16) * T * c->H, "prefill x fp16")) ||
       (rc = dev((void**)&p->h16, sizeof(_Float16) * P * c->F, "prefill h fp16")) ||
-      (rc = dev((void**)&p->ypair, sizeof(float) * P * c->H, "prefill pair outputs")))
+      (rc = dev((void**)&p->ypair, sizeof(float) * P * c->H, "prefill pair outputs")) ||
+      (rc = dev((void**)&p->sclT, sizeof(uint16_t) * E * moe::sclT_elements(c->lay), "prefill transposed scales")))
     return rc;
   const unsigned pin = hipHostMallocDefault;
   if ((rc = moe_ctx_host_alloc(c, (void**)&p->h_counts, sizeof(int32_t) * E, pin, "prefill count staging")) ||
@@ -202,21 +204,34 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   }
   PF_HIP(c, hipMemcpyAsync(p->eaddr, p->h_eaddr, sizeof(uint8_t*) * E, hipMemcpyHostToDevice, s));
 
-  // 4. stable sort of the pairs by expert
+  // 4. short tiles (few rows per expert) are bound by weight fetches: give
+  // their GEMMs the block scales of the used experts transposed, so each
+  // K step reads whole lines of them
+  const bool tscl = bm == 64;
+  hipEvent_t* ev = nullptr;
+  if (c->profiling && c->prefill_events.size() >= 6) ev = c->prefill_events.data();
+  if (tscl) {
+    moe::Launch lt;
+    lt.stream = s;
+    if (ev) lt.start = ev[4], lt.stop = ev[5];
+    PF_HIP(c, moe::launch_transpose_scales(p->eaddr, E, c->lay, p->sclT, lt));
+  }
+
+  // stable sort of the pairs by expert
   PF_HIP(c, moe::launch_expert_scatter(p->ids, P, E, p->offsets, p->perm, p->inv, s));
 
   // 5. activations as fp16 rows in operand order
   PF_HIP(c, moe::launch_convert_rows(x, T, H, p->x16, s));
 
   // 6. grouped GEMMs over the used tiles
-  hipEvent_t* ev = nullptr;
-  if (c->profiling && c->prefill_events.size() >= 4) ev = c->prefill_events.data();
   moe::GemmArgs g{};
   g.a16 = p->x16, g.arow = p->perm, g.arow_div = k;
   g.tiles = p->tiles, g.eaddr = p->eaddr, g.items = p->items[0];
   g.K = H, g.N = F;
   g.lay = c->lay;
   g.h16 = p->h16;
+  g.sclT = tscl ? p->sclT : nullptr;
+  g.sclT_per_expert = moe::sclT_elements(c->lay);
   moe::Launch l1 = ls, l2 = ls;
   if (ev) l1.start = ev[0], l1.stop = ev[1], l2.start = ev[2], l2.stop = ev[3];
   PF_HIP(c, moe::launch_grouped_gemm(g, 0, bm, n_items[0], l1));
@@ -233,9 +248,11 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   p->last_layer = layer;
 
   if (ev) {
-    float t1 = 0, t2 = 0;
+    float t1 = 0, t2 = 0, t0 = 0;
     PF_HIP(c, hipEventElapsedTime(&t1, ev[0], ev[1]));
     PF_HIP(c, hipEventElapsedTime(&t2, ev[2], ev[3]));
+    if (tscl) PF_HIP(c, hipEventElapsedTime(&t0, ev[4], ev[5]));
+    c->prof.prefill_prep_ms += t0;
     c->prof.prefill_passes += 1;
     c->prof.prefill_gateup_ms += t1;
     c->prof.prefill_down_ms += t2;
@@ -251,9 +268,11 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
 // the pass used). The same rule as the policy simulation: the pass's picks
 // count as uses at the next token's clock c; resident experts it used are
 // stamped c; its cold experts, by pair count (descending, ties: lower id),
-// take free slots or slots stamped below c (smallest stamp, ties: highest
-// index), at most min(max_experts, S). Their bytes come from the staging
-// blocks the pass filled (HBM to HBM), else from pinned memory.
+// take the lowest free slot, else the slot whose owner has the fewest pass
+// picks, then the oldest stamp (ties: highest index), if those picks are
+// fewer than the candidate's; at most min(max_experts, S); pending
+// admissions are neither candidates nor victims. Their bytes come from the
+// staging blocks the pass filled (HBM to HBM), else from pinned memory.
 extern "C" int moe_preheat(moe_ctx* c, int32_t layer, int32_t max_experts, int32_t* admitted) {
   if (!c) return MOE_E_INVAL;
   if (admitted) *admitted = 0;

@@ -21,6 +21,16 @@
 // the first MFMA and the high nibbles to the second. The activation rows are
 // stored in the matching order (step_pos), so LDS reads are 16-byte vectors.
 //
+// Block scales: a scale line of the expert blob holds 32 K steps of one
+// column, so a K step reading 4 B of it leaves the line to be fetched again
+// for each step once other traffic has evicted it. A pass of short tiles
+// (64 rows, chosen when experts have few rows: bound by these fetches)
+// therefore first transposes the scale planes of its experts
+// (transpose_scales_kernel) into [K/32][columns]: a K step's scales of a
+// column tile are then one contiguous run, every fetched line used at once.
+// Passes of 128-row tiles (bound by the matrix cores) read the planes as they
+// are. The layout is fixed per tile height at compile time.
+//
 // Staging: every operand byte of a K step (the A rows, the weight nibbles,
 // the block scales) travels global -> LDS by the LDS-DMA form of the global
 // load (global_load_lds_dwordx4 / _dword: lane l of a wave writes 16 or 4
@@ -111,7 +121,7 @@ constexpr int kStages = 3;  // LDS ring: loads run two K steps ahead
 
 // Shape of a workgroup tile: BM rows x 4 waves x NSUB x 16 features of NMAT
 // matrices, and the LDS stage holding one K step of its operands:
-//   [A: BM rows x 128 B][nibbles: NMAT x BNW features x 32 B][scales: NMAT x BNW x 4 B]
+//   [A: BM rows x 128 B][nibbles: NMAT x BNW features x 32 B][scales: NMAT x 2 blocks x BNW x 2 B]
 // DA, DB, DS: LDS-DMA instructions per wave and step for each part.
 template <int BM, int MODE>
 struct GemmTile {
@@ -242,7 +252,6 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   // q / (BNW/32); lane l fetches block half l / 32 of feature l % 32 (slot l).
   // Features past N fetch feature 0 and are never stored.
   const int64_t nib_plane[2] = {MODE == 1 ? a.lay.down_nib : a.lay.gate_nib, a.lay.up_nib};
-  const int64_t scl_plane[2] = {MODE == 1 ? a.lay.down_scl : a.lay.gate_scl, a.lay.up_scl};
   uint32_t bsrc[C::DB];
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) {
@@ -251,15 +260,34 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     col = col < N ? col : 0;
     bsrc[i] = (uint32_t)(nib_plane[m] + ((int64_t)col * nkb + (lane >> 5)) * 16);
   }
-  // scales: instruction q covers features 64 (q % (BNW/64)) .. +63 of matrix
-  // q / (BNW/64); lane l fetches the two scales of feature l
+  // scales. Transposed planes (64-row tiles, [K/32][N] per matrix): instruction
+  // q covers features 128 c .. +127 of block b of the step for matrix m, with
+  // q = (2 m + b) * (BNW / 128) + c; lane l fetches features 2 l, 2 l + 1; the
+  // LDS part is [matrix][block][feature]. The expert's own planes: instruction
+  // q covers features 64 (q % (BNW/64)) .. +63 of matrix q / (BNW/64); lane l
+  // fetches the two scales of feature l; the LDS part is [matrix][feature][block].
+  // Features past N fetch feature 0 and are never stored.
+  constexpr bool tscl = BM == 64;  // the host transposes the scales for passes of 64-row tiles
+  const uint8_t* sbase = tscl ? reinterpret_cast<const uint8_t*>(a.sclT + (int64_t)e * a.sclT_per_expert) : base;
+  const uint32_t sstep = tscl ? 4u * (uint32_t)N : 4u;  // bytes per K step
+  const int64_t sclT_plane[2] = {MODE == 1 ? 2 * (int64_t)a.lay.F * (a.lay.H / 32) : 0,
+                                 (int64_t)a.lay.F * (a.lay.H / 32)};
+  const int64_t scl_plane[2] = {MODE == 1 ? a.lay.down_scl : a.lay.gate_scl, a.lay.up_scl};
   uint32_t ssrc[C::DS];
 #pragma unroll
   for (int i = 0; i < C::DS; ++i) {
-    const int q = wave * C::DS + i, m = q / (BNW / 64);
-    int col = n0 + 64 * (q % (BNW / 64)) + lane;
-    col = col < N ? col : 0;
-    ssrc[i] = (uint32_t)(scl_plane[m] + (int64_t)col * nkb * 2);
+    const int q = wave * C::DS + i;
+    if (tscl) {
+      const int m = q / (2 * (BNW / 128)), bq = (q / (BNW / 128)) % 2;
+      int col = n0 + 128 * (q % (BNW / 128)) + 2 * lane;
+      col = col < N ? col : 0;
+      ssrc[i] = (uint32_t)((sclT_plane[m] + (int64_t)bq * N + col) * 2);
+    } else {
+      const int m = q / (BNW / 64);
+      int col = n0 + 64 * (q % (BNW / 64)) + lane;
+      col = col < N ? col : 0;
+      ssrc[i] = (uint32_t)(scl_plane[m] + (int64_t)col * nkb * 2);
+    }
   }
 
   auto issue = [&](int j) __attribute__((always_inline)) {
@@ -269,7 +297,8 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < C::DB; ++i) dma16(base + bsrc[i] + 32u * (uint32_t)j, S + C::OFF_BN + (wave * C::DB + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < C::DS; ++i) dma4(base + ssrc[i] + 4u * (uint32_t)j, S + C::OFF_BS + (wave * C::DS + i) * 256);
+    for (int i = 0; i < C::DS; ++i)
+      dma4(sbase + ssrc[i] + sstep * (uint32_t)j, S + C::OFF_BS + (wave * C::DS + i) * 256);
   };
 
   f32x4_t acc[NMAT][NSUB][RB];
@@ -300,7 +329,8 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
         const int wn = wave * WN + ns * 16 + (lane & 15);
         const u32x2_t w = *reinterpret_cast<const u32x2_t*>(S + C::OFF_BN + m * C::BN_BYTES + (wn >> 5) * 1024 +
                                                             ((wn & 31) + 32 * (g >> 1)) * 16 + 8 * (g & 1));
-        const uint32_t d = *reinterpret_cast<const uint16_t*>(S + C::OFF_BS + m * C::BS_BYTES + wn * 4 + 2 * (g >> 1));
+        const uint32_t d = *reinterpret_cast<const uint16_t*>(
+            S + C::OFF_BS + m * C::BS_BYTES + (tscl ? (g >> 1) * BNW * 2 + wn * 2 : wn * 4 + 2 * (g >> 1)));
         weight_operands(w, as_h2(d | (d << 16)), bop[m][ns][0], bop[m][ns][1]);
       }
 #pragma unroll
@@ -345,6 +375,40 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
   }
 }
 
+// Scale planes [rows][K/32] (fp16) of the experts with eaddr[e] set ->
+// [K/32][rows] at out + e * per. A work-group moves 64 rows: it reads them
+// whole (one contiguous run), then writes 128-byte row pieces of the
+// transposed plane, 128 blocks of K at a time. grid = (row chunks of the
+// largest matrix, 3 matrices, E).
+__global__ __launch_bounds__(256) void transpose_scales_kernel(const uint8_t* const* eaddr, ExpertLayout lay,
+                                                               uint16_t* out, int64_t per) {
+  __shared__ uint16_t tile[64][129];  // odd row stride (in 16-bit words): the column reads spread over banks
+  const uint8_t* base = eaddr[blockIdx.z];
+  if (!base) return;
+  const int m = blockIdx.y;  // 0 gate, 1 up, 2 down
+  const int R = m < 2 ? lay.F : lay.H, KB = (m < 2 ? lay.H : lay.F) / 32;
+  const int r0 = blockIdx.x * 64;
+  if (r0 >= R) return;
+  const int nr = R - r0 < 64 ? R - r0 : 64;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(base + (m == 0 ? lay.gate_scl : m == 1 ? lay.up_scl
+                                                                                            : lay.down_scl)) +
+                        (int64_t)r0 * KB;
+  uint16_t* dst = out + (int64_t)blockIdx.z * per + (int64_t)m * lay.F * (lay.H / 32) + r0;
+  for (int k0 = 0; k0 < KB; k0 += 128) {
+    const int nk = KB - k0 < 128 ? KB - k0 : 128;
+    for (int i = threadIdx.x; i < nr * nk; i += 256) {
+      const int r = i / nk, kb = i - r * nk;
+      tile[r][kb] = src[(int64_t)r * KB + k0 + kb];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nk * 64; i += 256) {
+      const int kb = i >> 6, r = i & 63;
+      if (r < nr) dst[(int64_t)(k0 + kb) * R + r] = tile[r][kb];
+    }
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_pairs_kernel(const float* ypair, const int32_t* inv, const float* w,
                                                             int32_t k, int32_t H, float* y, int32_t accumulate) {
   const int t = blockIdx.y;
@@ -378,12 +442,23 @@ hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float
                      reinterpret_cast<uint4*>(dst));
   return hipGetLastError();
 }
+int64_t sclT_elements(const ExpertLayout& lay) {
+  return 2 * (int64_t)lay.F * (lay.H / 32) + (int64_t)lay.H * (lay.F / 32);
+}
+hipError_t launch_transpose_scales(const uint8_t* const* eaddr, int32_t E, const ExpertLayout& lay, uint16_t* out,
+                                   const Launch& l) {
+  if (E <= 0 || lay.H % 32 || lay.F % 32) return hipErrorInvalidValue;
+  const int rmax = lay.F > lay.H ? lay.F : lay.H;
+  return launch(transpose_scales_kernel, dim3((rmax + 63) / 64, 3, E), dim3(256), l, eaddr, lay, out,
+                sclT_elements(lay));
+}
 int gemm_features_per_tile(int mode, int bm) {
   if (mode == 0) return bm == 64 ? GemmTile<64, 0>::BNW : GemmTile<128, 0>::BNW;
   return bm == 64 ? GemmTile<64, 1>::BNW : GemmTile<128, 1>::BNW;
 }
 hipError_t launch_grouped_gemm(GemmArgs a, int mode, int bm, int n_items, const Launch& l) {
-  if (a.K % KS || a.N % KS || n_items <= 0 || !a.items || (bm != 64 && bm != 128) || (mode != 0 && mode != 1))
+  if (a.K % KS || a.N % KS || n_items <= 0 || !a.items || (bm != 64 && bm != 128) || (mode != 0 && mode != 1) ||
+      (bm == 64) != (a.sclT != nullptr))  // 64-row tiles read the transposed scales, 128-row tiles the planes
     return hipErrorInvalidValue;
   a.work = n_items;
   a.work_padded = (a.work + 7) / 8 * 8;

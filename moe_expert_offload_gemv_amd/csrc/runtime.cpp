@@ -335,7 +335,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->timed_tokens.assign(n_timed, 0);
   c->timed_fused.assign(n_timed, 0);
   c->timed_cpu.assign(n_timed, 0);
-  for (int i = 0; i < 4 && k.max_prefill_tokens > 0; ++i) {
+  for (int i = 0; i < 6 && k.max_prefill_tokens > 0; ++i) {
     hipEvent_t ev;
     if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return fail(MOE_E_HIP);
     c->prefill_events.push_back(ev);
