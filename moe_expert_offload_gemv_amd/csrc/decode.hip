@@ -162,6 +162,16 @@ struct RowTile {
       }
     }
   }
+  // Loop-carried use (several activations against the same rows): stops the
+  // compiler from hoisting the nibble-to-float conversions out of the loop,
+  // which would keep 32 floats per block live instead of 4 packed words.
+  __device__ __forceinline__ void keep_packed() {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+#pragma unroll
+      for (int j = 0; j < BPL; ++j)
+        __asm__ volatile("" : "+v"(q[it][j].x), "+v"(q[it][j].y), "+v"(q[it][j].z), "+v"(q[it][j].w), "+v"(d[it][j]));
+  }
   __device__ __forceinline__ float dot(int it, const float (&xs)[BPL][32], const float (&sx)[BPL]) const {
     float acc = 0.f;
 #pragma unroll
@@ -408,6 +418,134 @@ __global__ __launch_bounds__(256) void gemv_down_combine_kernel(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped decode (batches of kGroupedMinTokens tokens or more).
+//
+// group_picks_kernel: one work-group counts the picks per expert in LDS,
+// scans the counts, lists the experts with picks (ascending) and places
+// every pick in its expert's range of `order` (the order inside a range is
+// not fixed; every pick is computed on its own, so results do not depend on
+// it).
+__global__ __launch_bounds__(256) void group_picks_kernel(GroupArgs a) {
+  __shared__ int32_t cnt[4096], fill[4096];
+  __shared__ int32_t part[256], gpart[256];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < a.E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < a.P; p += 256) atomicAdd(&cnt[a.ids[p]], 1);
+  __syncthreads();
+  // thread tid scans experts [tid * per, (tid + 1) * per)
+  const int per = (a.E + 255) / 256, e0 = tid * per, e1 = min(a.E, e0 + per);
+  int s = 0, gs = 0;
+  for (int e = e0; e < e1; ++e) s += cnt[e], gs += cnt[e] > 0;
+  part[tid] = s, gpart[tid] = gs;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0, gacc = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = part[i], gv = gpart[i];
+      part[i] = acc, gpart[i] = gacc;
+      acc += v, gacc += gv;
+    }
+    *a.n_groups = gacc;
+  }
+  __syncthreads();
+  int pos = part[tid], gi = gpart[tid];
+  for (int e = e0; e < e1; ++e) {
+    const int c = cnt[e];
+    fill[e] = pos;
+    if (c > 0) a.groups[gi++] = make_int4(e, pos, c, 0);
+    pos += c;
+  }
+  __syncthreads();
+  for (int p = tid; p < a.P; p += 256) a.order[atomicAdd(&fill[a.ids[p]], 1)] = p;
+}
+
+// gate/up of one expert group: grid = (row chunks of F, up to P groups);
+// the weight rows are loaded once and dotted with the activations of every
+// pick of the group.
+template <int LPR, int BPL, int NIT>
+__global__ __launch_bounds__(256) void grouped_gateup_kernel(GemvArgs a, GroupArgs gr) {
+  constexpr int RPW = 64 / LPR;
+  constexpr int ROWS_WG = 4 * NIT * RPW;
+  if ((int)blockIdx.y >= *gr.n_groups) return;
+  const int4 grp = gr.groups[blockIdx.y];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lb = lane % LPR, rg = lane / LPR;
+  const int p0 = gr.order[grp.y];
+  const uint8_t* base = a.addr[p0];
+  const bool cold = (a.kind[p0] & kCold) != 0;
+  const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
+  RowTile<LPR, BPL, NIT> g, u;
+  g.load(reinterpret_cast<const uint4*>(base + a.lay.gate_nib),
+         reinterpret_cast<const uint16_t*>(base + a.lay.gate_scl), row0, a.F, lb, cold);
+  u.load(reinterpret_cast<const uint4*>(base + a.lay.up_nib), reinterpret_cast<const uint16_t*>(base + a.lay.up_scl),
+         row0, a.F, lb, cold);
+  // one pick at a time: the weights stay in registers, each pick's slice replaces the last
+#pragma unroll 1
+  for (int i = 0; i < grp.z; ++i) {
+    const int p = gr.order[grp.y + i];
+    g.keep_packed();
+    u.keep_packed();
+    float xs[BPL][32], sx[BPL];
+    load_slice<LPR, BPL>(a.x + (int64_t)(p / a.k) * a.H, lb, xs, sx);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const float gv = g.dot(it, xs, sx);
+      const float uv = u.dot(it, xs, sx);
+      const int r = row0 + it * RPW;
+      if (lb == 0 && r < a.F) a.out[(int64_t)p * a.F + r] = silu(gv) * uv;
+    }
+  }
+}
+
+// down of one expert group: ypick[p] = W_down h[p] for every pick p of the
+// group; grid = (row chunks of H, up to P groups).
+template <int LPR, int BPL, int NIT>
+__global__ __launch_bounds__(256) void grouped_down_kernel(GemvArgs a, GroupArgs gr) {
+  constexpr int RPW = 64 / LPR;
+  constexpr int ROWS_WG = 4 * NIT * RPW;
+  if ((int)blockIdx.y >= *gr.n_groups) return;
+  const int4 grp = gr.groups[blockIdx.y];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lb = lane % LPR, rg = lane / LPR;
+  const int p0 = gr.order[grp.y];
+  const uint8_t* base = a.addr[p0];
+  const bool cold = (a.kind[p0] & kCold) != 0;
+  const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
+  RowTile<LPR, BPL, NIT> d;
+  d.load(reinterpret_cast<const uint4*>(base + a.lay.down_nib),
+         reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0, a.H, lb, cold);
+#pragma unroll 1
+  for (int i = 0; i < grp.z; ++i) {
+    const int p = gr.order[grp.y + i];
+    d.keep_packed();
+    float hs[BPL][32], sh[BPL];
+    load_slice<LPR, BPL>(a.x + (int64_t)p * a.F, lb, hs, sh);
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const float v = d.dot(it, hs, sh);
+      const int r = row0 + it * RPW;
+      if (lb == 0 && r < a.H) a.ypick[(int64_t)p * a.H + r] = v;
+    }
+  }
+}
+
+// y[t] (=|+=) sum over the picks of token t in pick order of w * ypick;
+// grid = (chunks of 256 of H, tokens).
+__global__ __launch_bounds__(256) void combine_picks_kernel(GemvArgs a) {
+  const int t = blockIdx.y;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.H) return;
+  float acc = 0.f;
+  for (int i = 0; i < a.k; ++i) {
+    const int64_t p = (int64_t)t * a.k + i;
+    acc = fmaf(a.w[p], a.ypick[p * a.H + r], acc);
+  }
+  float* yp = a.out + (int64_t)t * a.H + r;
+  *yp = a.accumulate ? *yp + acc : acc;
+}
+
+// ---------------------------------------------------------------------------
 // combine with the cold picks computed by the host threads. grid = (row
 // chunks of 256 of H, tokens). A token with a cold pick waits (bounded) for
 // the host's answer, polled by thread 0 of each group (a few groups: many
@@ -513,6 +651,19 @@ hipError_t down_combine_t(const GemvArgs& a, const Launch& l, int mode) {
   return launch(gemv_down_combine_kernel<LPR, BPL, kNitCombine, kAll>, grid, dim3(256), l, a);
 }
 
+template <int LPR, int BPL>
+hipError_t grouped_gateup_t(const GemvArgs& a, const GroupArgs& g, const Launch& l, int) {
+  constexpr int ROWS_WG = 4 * kNitGateUp * (64 / LPR);
+  return launch(grouped_gateup_kernel<LPR, BPL, kNitGateUp>, dim3((a.F + ROWS_WG - 1) / ROWS_WG, g.P), dim3(256), l,
+                a, g);
+}
+template <int LPR, int BPL>
+hipError_t grouped_down_t(const GemvArgs& a, const GroupArgs& g, const Launch& l, int) {
+  constexpr int ROWS_WG = 4 * kNitDown * (64 / LPR);
+  return launch(grouped_down_kernel<LPR, BPL, kNitDown>, dim3((a.H + ROWS_WG - 1) / ROWS_WG, g.P), dim3(256), l, a,
+                g);
+}
+
 #define MOE_DISPATCH_GEMV(FN, KB, ARGS, L, MODE, ...)         \
   do {                                                        \
     GemvShape sh;                                             \
@@ -546,6 +697,23 @@ hipError_t launch_gemv_route_gateup(const GemvArgs& a, const RouteArgs& r, const
   if (!r.logits || r.E < 1 || r.E > kFusedRouteMaxExperts || a.k < 1 || a.k > 32 || a.k > r.E || a.T < 1)
     return hipErrorInvalidValue;
   MOE_DISPATCH_GEMV(route_gateup_t, a.H / 32, a, l, mode, r);
+}
+hipError_t launch_group_picks(const GroupArgs& a, hipStream_t s) {
+  if (a.P < 1 || a.E < 1 || a.E > 4096) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(group_picks_kernel, dim3(1), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_grouped_gateup(const GemvArgs& a, const GroupArgs& g, const Launch& l) {
+  if (g.P < 1) return hipErrorInvalidValue;
+  MOE_DISPATCH_GEMV(grouped_gateup_t, a.H / 32, a, l, 0, g);
+}
+hipError_t launch_grouped_down(const GemvArgs& a, const GroupArgs& g, const Launch& l) {
+  if (g.P < 1) return hipErrorInvalidValue;
+  MOE_DISPATCH_GEMV(grouped_down_t, a.F / 32, a, l, 0, g);
+}
+hipError_t launch_combine_picks(const GemvArgs& a, const Launch& l) {
+  if (a.T < 1 || a.k < 1 || a.H < 1) return hipErrorInvalidValue;
+  return launch(combine_picks_kernel, dim3((a.H + 255) / 256, a.T), dim3(256), l, a);
 }
 hipError_t launch_gemv_down_pick(const GemvArgs& a, const Launch& l, int mode) {
   MOE_DISPATCH_GEMV(down_pick_t, a.F / 32, a, l, mode);

@@ -128,6 +128,24 @@ hipError_t launch_gemv_route_gateup(const GemvArgs& a, const RouteArgs& r, const
 hipError_t launch_gemv_down_pick(const GemvArgs& a, const Launch& l, int mode);
 hipError_t launch_gemv_down_combine(const GemvArgs& a, const Launch& l, int mode);
 
+// Decode batches of kGroupedMinTokens tokens or more: the picks are grouped
+// by expert on the device and every expert's weight rows are read once for
+// all the tokens that picked it (routing and policy as route_kernel's).
+constexpr int kGroupedMinTokens = 8;
+struct GroupArgs {
+  const int32_t* ids;    // [P] expert of each pick
+  int32_t P, E;
+  int4* groups;          // [P] (expert, first position in order, picks, 0), in expert order
+  int32_t* order;        // [P] picks by expert
+  int32_t* n_groups;     // [1]
+};
+hipError_t launch_group_picks(const GroupArgs& a, hipStream_t s);
+// grouped gate/up (h [P][F] from x) or down (ypick [P][H] from h): a.x / a.out as in
+// GemvArgs, the groups from GroupArgs; then a pick-order combine into y.
+hipError_t launch_grouped_gateup(const GemvArgs& a, const GroupArgs& g, const Launch& l);
+hipError_t launch_grouped_down(const GemvArgs& a, const GroupArgs& g, const Launch& l);
+hipError_t launch_combine_picks(const GemvArgs& a, const Launch& l);
+
 // Combine when the host threads computed the cold picks: a token with a cold
 // pick waits until the low half of *done reaches seq (at most max_polls
 // polls; a nonzero high half, or no answer, sets ctrl->host_fault and counts

@@ -226,6 +226,10 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_h, sizeof(float) * P * c->F, "h"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_kind, P, "pick tags"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ypick, sizeof(float) * P * c->H, "pick outputs"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_groups, sizeof(int4) * P, "pick groups")) ||
+      (rc = moe_ctx_dev_alloc(c, (void**)&c->d_order, sizeof(int32_t) * P, "picks by expert")) ||
+      (rc = moe_ctx_dev_alloc(c, (void**)&c->d_ngroups, sizeof(int32_t), "group count")))
+    return fail(rc);
   c->capture_picks = k.capture_picks;
   if (c->capture_picks > 0) {
     if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_capture, (size_t)(L * c->capture_picks * c->B), "capture blocks")))
@@ -335,6 +339,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->timed_tokens.assign(n_timed, 0);
   c->timed_fused.assign(n_timed, 0);
   c->timed_cpu.assign(n_timed, 0);
+  c->timed_grouped.assign(n_timed, 0);
   for (int i = 0; i < 6 && k.max_prefill_tokens > 0; ++i) {
     hipEvent_t ev;
     if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return fail(MOE_E_HIP);
@@ -536,9 +541,14 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
     if (stream_capturing(c->stream))
       return moe_ctx_fail(c, MOE_E_CAPTURING, "forward with cold_exec CPU while capturing");
   }
-  if (ev) c->timed_fused[c->timed_pending - 1] = fused ? 1 : 0;
+  // a batch of many tokens groups its picks by expert (each expert's weights
+  // read once for all the tokens that picked it); the host-thread mode keeps
+  // one pass per pick
+  const bool grouped = !c->hx && n_tokens >= moe::kGroupedMinTokens;
+  if (ev) c->timed_fused[c->timed_pending - 1] = fused && !grouped ? 1 : 0;
   if (ev) c->timed_cpu[c->timed_pending - 1] = c->hx ? 1 : 0;
-  if (!fused) HIP_TRY(c, moe::launch_route(ra, on(A, kRoute)));
+  if (ev) c->timed_grouped[c->timed_pending - 1] = grouped ? 1 : 0;
+  if (!fused || grouped) HIP_TRY(c, moe::launch_route(ra, on(A, kRoute)));
 
   moe::GemvArgs ga{};
   ga.x = x;
@@ -555,6 +565,16 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   dn.x = c->d_h;
   dn.out = y;
   dn.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+  if (grouped) {
+    moe::GroupArgs gr{};
+    gr.ids = c->d_ids, gr.P = n_tokens * c->k, gr.E = c->E;
+    gr.groups = c->d_groups, gr.order = c->d_order, gr.n_groups = c->d_ngroups;
+    HIP_TRY(c, moe::launch_group_picks(gr, A));
+    HIP_TRY(c, moe::launch_grouped_gateup(ga, gr, on(A, kHotGateUp)));
+    HIP_TRY(c, moe::launch_grouped_down(dn, gr, on(A, kHotDown)));
+    HIP_TRY(c, moe::launch_combine_picks(dn, on(A, kColdDownCombine)));
+    return MOE_OK;
+  }
   if (c->hx) {
     // the GPU computes the hot picks while the host threads compute the cold
     // ones from the routing and activations the gate/up launch hands over
@@ -612,7 +632,7 @@ static int flush_profile(moe_ctx* c) {
     for (int j = 0; j < kTimedKernels; ++j) {
       t[j] = 0.f;
       if (j == kRoute && c->timed_fused[i]) continue;
-      if (j == kColdGateUp && c->timed_cpu[i]) continue;  // the host threads run the cold gate/up
+      if (j == kColdGateUp && (c->timed_cpu[i] || c->timed_grouped[i])) continue;  // no separate cold gate/up
       HIP_TRY(c, hipEventElapsedTime(&t[j], c->events[2 * (kTimedKernels * (size_t)i + j)],
                                      c->events[2 * (kTimedKernels * (size_t)i + j) + 1]));
     }

@@ -42,6 +42,9 @@ struct moe_ctx {
   float* d_h = nullptr;                // [max_batch*k][F]
   uint8_t* d_kind = nullptr;           // [max_batch*k] hot / cold tag
   float* d_ypick = nullptr;            // [max_batch*k][H] down output of hot picks
+  int4* d_groups = nullptr;            // [max_batch*k] grouped decode: (expert, start, picks, 0)
+  int32_t* d_order = nullptr;          // [max_batch*k] picks by expert
+  int32_t* d_ngroups = nullptr;        // [1]
   int32_t capture_picks = 0;           // picks per layer whose cold reads are captured
   uint8_t* d_capture = nullptr;        // [L][capture_picks] expert blocks
   uint32_t* d_cap_tag = nullptr;       // [L][rec_stride] clock of a captured cold pick
@@ -96,6 +99,7 @@ struct moe_ctx {
   std::vector<int32_t> timed_tokens;   // n_tokens of each pending timed forward
   std::vector<uint8_t> timed_fused;    // 1: its routing ran inside the gate/up GEMV (no routing interval)
   std::vector<uint8_t> timed_cpu;      // 1: its cold gate/up ran on the host threads (no interval)
+  std::vector<uint8_t> timed_grouped;  // 1: grouped by expert (no separate cold gate/up interval)
   int32_t timed_pending = 0;
   moe_profile_stats prof{};
 

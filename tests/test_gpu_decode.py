@@ -423,3 +423,21 @@ def test_cold_picks_on_host_threads_accumulate_and_errors():
     # capture of cold reads has nothing to capture with host threads
     with pytest.raises(moe.MoeError):
         moe.moe_create(1, 32, 4, 256, 512, 0, cold_exec=moe.MOE_COLD_CPU, capture_picks=4)
+
+
+# ---------------------------------------------------------------------------
+# grouped decode: batches of 8 tokens or more read each expert's weights once
+
+@pytest.mark.parametrize("tokens", [8, 12])
+def test_grouped_batch_bit_exact_policy(tokens):
+    wl = Workload(f"decode-e64k8-h2048f1024-l2-b{tokens}-grouped", 115, 2, 64, 8, 2048, 1024, tokens=tokens, steps=10,
+                  zipf_s=1.1, slots=20, rotation=40)
+    copies = {}
+    _run_decode(wl, slots=20, check_every=1, copies=copies)
+    assert copies["copied"] > 0  # promotions happen (from pinned memory: the grouped path captures nothing)
+
+
+def test_grouped_batch_global_pool_cold_start_swap_lead():
+    wl = Workload("decode-e32k4-h256f512-l3-b16-grouped", 116, 3, 32, 4, 256, 512, tokens=16, steps=16, zipf_s=0.9,
+                  slots=8, rotation=24)
+    _run_decode(wl, slots=24, check_every=2, seed=False, pool="global", swaps=(4, 1))
