@@ -132,8 +132,10 @@ hipError_t launch_gemv_down_combine(const GemvArgs& a, const Launch& l, int mode
 // by expert on the device and every expert's weight rows are read once for
 // all the tokens that picked it (routing and policy as route_kernel's).
 constexpr int kGroupedMinTokens = 8;
+constexpr int kMaxGroupsSorted = 1024;  // more groups than this stay in expert order
 struct GroupArgs {
   const int32_t* ids;    // [P] expert of each pick
+  const int32_t* tbl;    // [E] the layer's slot table (cold experts: -1), as the routing read it
   int32_t P, E;
   int4* groups;          // [P] (expert, first position in order, picks, 0), in expert order
   int32_t* order;        // [P] picks by expert

@@ -567,7 +567,7 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   dn.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
   if (grouped) {
     moe::GroupArgs gr{};
-    gr.ids = c->d_ids, gr.P = n_tokens * c->k, gr.E = c->E;
+    gr.ids = c->d_ids, gr.tbl = ra.tbl, gr.P = n_tokens * c->k, gr.E = c->E;
     gr.groups = c->d_groups, gr.order = c->d_order, gr.n_groups = c->d_ngroups;
     HIP_TRY(c, moe::launch_group_picks(gr, A));
     HIP_TRY(c, moe::launch_grouped_gateup(ga, gr, on(A, kHotGateUp)));
