@@ -528,16 +528,24 @@ struct SharedVec {
   }
 };
 
+// Picks whose rows fit the work-group's LDS budget (64 KiB) at once, 1..16.
+template <int LPR, int BPL>
+constexpr int chunk_picks() {
+  constexpr int n = 65536 / (16 * SharedVec<LPR, BPL>::KV);
+  return n < 1 ? 1 : (n > 16 ? 16 : n);
+}
+
 // gate/up of one expert group: grid = (row chunks of F, up to P groups);
 // the weight rows are loaded once and dotted with the activations of every
-// pick of the group. The picks' rows pass through LDS, the next one loading
-// while the current one is used.
+// pick of the group. The picks' rows pass through LDS, a chunk of them at a
+// time (usually the whole group): one wait per chunk.
 template <int LPR, int BPL, int NIT>
 __global__ __launch_bounds__(256) void grouped_gateup_kernel(GemvArgs a, GroupArgs gr) {
   constexpr int RPW = 64 / LPR;
   constexpr int ROWS_WG = 4 * NIT * RPW;
   using V = SharedVec<LPR, BPL>;
-  __shared__ float4 xsh[2][V::KV];
+  constexpr int NB = chunk_picks<LPR, BPL>();
+  __shared__ float4 xsh[NB][V::KV];
   if ((int)blockIdx.y >= *gr.n_groups) return;
   const int4 grp = gr.groups[blockIdx.y];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -546,31 +554,33 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GemvArgs a, GroupAr
   const uint8_t* base = a.addr[p0];
   const bool cold = (a.kind[p0] & kCold) != 0;
   const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
-  V::issue(a.x + (int64_t)(p0 / a.k) * a.H, xsh[0], wave, lane);
   RowTile<LPR, BPL, NIT> g, u;
   g.load(reinterpret_cast<const uint4*>(base + a.lay.gate_nib),
          reinterpret_cast<const uint16_t*>(base + a.lay.gate_scl), row0, a.F, lb, cold);
   u.load(reinterpret_cast<const uint4*>(base + a.lay.up_nib), reinterpret_cast<const uint16_t*>(base + a.lay.up_scl),
          row0, a.F, lb, cold);
-  V::wait();
-  // one pick at a time: the weights stay in registers (packed)
 #pragma unroll 1
-  for (int i = 0; i < grp.z; ++i) {
-    const int p = gr.order[grp.y + i];
-    const bool more = i + 1 < grp.z;
-    if (more) V::issue(a.x + (int64_t)(gr.order[grp.y + i + 1] / a.k) * a.H, xsh[(i + 1) & 1], wave, lane);
-    g.keep_packed();
-    u.keep_packed();
-    float xs[BPL][32], sx[BPL];
-    V::slice(xsh[i & 1], lb, xs, sx);
+  for (int c0 = 0; c0 < grp.z; c0 += NB) {
+    const int nc = grp.z - c0 < NB ? grp.z - c0 : NB;
+    for (int b = 0; b < nc; ++b) V::issue(a.x + (int64_t)(gr.order[grp.y + c0 + b] / a.k) * a.H, xsh[b], wave, lane);
+    V::wait();  // the chunk's rows (and, the first time, the weights) are in
+    // one pick at a time: the weights stay in registers (packed)
+#pragma unroll 1
+    for (int b = 0; b < nc; ++b) {
+      const int p = gr.order[grp.y + c0 + b];
+      g.keep_packed();
+      u.keep_packed();
+      float xs[BPL][32], sx[BPL];
+      V::slice(xsh[b], lb, xs, sx);
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const float gv = g.dot(it, xs, sx);
-      const float uv = u.dot(it, xs, sx);
-      const int r = row0 + it * RPW;
-      if (lb == 0 && r < a.F) a.out[(int64_t)p * a.F + r] = silu(gv) * uv;
+      for (int it = 0; it < NIT; ++it) {
+        const float gv = g.dot(it, xs, sx);
+        const float uv = u.dot(it, xs, sx);
+        const int r = row0 + it * RPW;
+        if (lb == 0 && r < a.F) a.out[(int64_t)p * a.F + r] = silu(gv) * uv;
+      }
     }
-    V::wait();  // the next pick's row is in; everyone is done with this one
+    if (c0 + NB < grp.z) __syncthreads();  // everyone is done with the chunk before it is overwritten
   }
 }
 
@@ -581,7 +591,8 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GemvArgs a, GroupArgs
   constexpr int RPW = 64 / LPR;
   constexpr int ROWS_WG = 4 * NIT * RPW;
   using V = SharedVec<LPR, BPL>;
-  __shared__ float4 hsh[2][V::KV];
+  constexpr int NB = chunk_picks<LPR, BPL>();
+  __shared__ float4 hsh[NB][V::KV];
   if ((int)blockIdx.y >= *gr.n_groups) return;
   const int4 grp = gr.groups[blockIdx.y];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -590,26 +601,28 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GemvArgs a, GroupArgs
   const uint8_t* base = a.addr[p0];
   const bool cold = (a.kind[p0] & kCold) != 0;
   const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
-  V::issue(a.x + (int64_t)p0 * a.F, hsh[0], wave, lane);
   RowTile<LPR, BPL, NIT> d;
   d.load(reinterpret_cast<const uint4*>(base + a.lay.down_nib),
          reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0, a.H, lb, cold);
-  V::wait();
 #pragma unroll 1
-  for (int i = 0; i < grp.z; ++i) {
-    const int p = gr.order[grp.y + i];
-    const bool more = i + 1 < grp.z;
-    if (more) V::issue(a.x + (int64_t)gr.order[grp.y + i + 1] * a.F, hsh[(i + 1) & 1], wave, lane);
-    d.keep_packed();
-    float hs[BPL][32], sh[BPL];
-    V::slice(hsh[i & 1], lb, hs, sh);
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const float v = d.dot(it, hs, sh);
-      const int r = row0 + it * RPW;
-      if (lb == 0 && r < a.H) a.ypick[(int64_t)p * a.H + r] = v;
-    }
+  for (int c0 = 0; c0 < grp.z; c0 += NB) {
+    const int nc = grp.z - c0 < NB ? grp.z - c0 : NB;
+    for (int b = 0; b < nc; ++b) V::issue(a.x + (int64_t)gr.order[grp.y + c0 + b] * a.F, hsh[b], wave, lane);
     V::wait();
+#pragma unroll 1
+    for (int b = 0; b < nc; ++b) {
+      const int p = gr.order[grp.y + c0 + b];
+      d.keep_packed();
+      float hs[BPL][32], sh[BPL];
+      V::slice(hsh[b], lb, hs, sh);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const float v = d.dot(it, hs, sh);
+        const int r = row0 + it * RPW;
+        if (lb == 0 && r < a.H) a.ypick[(int64_t)p * a.H + r] = v;
+      }
+    }
+    if (c0 + NB < grp.z) __syncthreads();
   }
 }
 
