@@ -206,12 +206,13 @@ def request_pass(moe, torch, ctx, wl, freq, stream, prompt_tokens, decode_tokens
     return out
 
 
-def host_cold_pass(moe, torch, wl, stream, host_alloc, pool, x_all, logits_all, steps, warmup, swap_lead=1):
+def host_cold_pass(moe, torch, wl, stream, host_alloc, pool, x_all, logits_all, steps, warmup, swap_lead=1,
+                   cpu_threads=0):
     """The same decode with the cold picks computed by the host threads (eager launches: the hand-off is not
     capturable), swap lead 1 (promotions are pinned-to-HBM copies here: no cold read to capture)."""
     T, L = wl.tokens, wl.n_layers
     ctx, freq = setup_ctx(moe, wl, wl.slots, stream, host_alloc, progress=False, capture_picks=0, pool=pool,
-                          swaps=(0, swap_lead), cold_exec=moe.MOE_COLD_CPU)
+                          swaps=(0, swap_lead), cold_exec=moe.MOE_COLD_CPU, cpu_threads=cpu_threads)
     info = moe.moe_get_info(ctx)
     x_steps = x_all.shape[0]
     res = torch.zeros((T, wl.hidden), dtype=torch.float32, device="cuda")
@@ -247,6 +248,63 @@ def host_cold_pass(moe, torch, wl, stream, host_alloc, pool, x_all, logits_all, 
         # weight bytes of the cold experts the host threads read / time computing them
         "weight_GBps": round(passes * wl.expert_bytes / max(host["host_compute_ms"], 1e-9) / 1e6, 1),
         "launch": "eager"}
+
+
+LARGE_WORKLOADS = ("large-e256k8-h4096f1536-l60-b1", "large-e256k8-h4096f1536-l60-b32")
+
+
+def large_pass(moe, torch, stream, host_alloc, steps=32, warmup=4):
+    """The 60-layer, 256-expert model at decode batch 1 and 32 on one context (pool of 251 slots per layer in
+    160 GB of HBM; batch 32 takes the grouped path). HIP graph per step, as the main run."""
+    import numpy as np
+
+    from workload import WORKLOADS, frequency_table, step_activations, zipf_logits
+
+    out = {}
+    wl1, wl32 = (WORKLOADS[n] for n in LARGE_WORKLOADS)
+    ctx, _ = setup_ctx(moe, wl32, wl32.slots, stream, host_alloc, progress=False)
+    L, H, E = wl32.n_layers, wl32.hidden, wl32.n_experts
+    try:
+        for wl in (wl1, wl32):
+            T = wl.tokens
+            freq = frequency_table(wl)  # each workload's own popularity
+            logits = torch.from_numpy(zipf_logits(wl, steps=steps)).cuda()
+            x_all = torch.from_numpy(np.stack([step_activations(wl, s) for s in range(4)])).cuda()
+            xs = torch.zeros((L, T, H), dtype=torch.float32, device="cuda")
+            zs = torch.zeros((L, T, E), dtype=torch.float32, device="cuda")
+            res = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+            moe.moe_seed(ctx, freq)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(graph, stream=stream):
+                    for layer in range(L):
+                        moe.moe_forward(ctx, layer, T, xs[layer], zs[layer], res, flags=moe.MOE_ACCUMULATE)
+
+                def step(i):
+                    xs.copy_(x_all[i % 4])
+                    zs.copy_(logits[i % steps])
+                    res.zero_()
+                    graph.replay()
+
+                run_steps(moe, ctx, warmup, step)
+                moe.moe_seed(ctx, freq)
+                torch.cuda.synchronize()
+                acc = {}
+                t0 = time.perf_counter()
+                run_steps(moe, ctx, steps, step, acc)
+                torch.cuda.synchronize()
+                elapsed = time.perf_counter() - t0
+            out[wl.name] = {"tokens_per_s": round(steps * T / elapsed, 2),
+                            "ms_per_step": round(elapsed / steps * 1e3, 3),
+                            "hit_rate": round(acc["hits"] / max(acc["hits"] + acc["misses"], 1), 4),
+                            "path": "grouped by expert" if T >= 8 else "one GEMV pass per pick",
+                            # expert bytes per pick served / time (a pick's bytes counted again for every pick)
+                            "pick_weight_GBps": round((acc["hot_bytes"] + acc["cold_bytes"]) / elapsed / 1e9, 1)}
+            log(f"{wl.name}: {out[wl.name]}")
+            del graph, logits, x_all, xs, zs, res
+    finally:
+        moe.moe_destroy(ctx)
+    return out
 
 
 def cpu_baseline(wl, seconds, logits):
@@ -298,7 +356,7 @@ def main():
                     help="cache steps an admission waits for its copy before its table entry flips")
     ap.add_argument("--cold-exec", choices=["gpu", "cpu"], default="gpu",
                     help="cold picks read zero-copy by the GPU, or computed by host threads (eager launches)")
-    ap.add_argument("--cpu-threads", type=int, default=0, help="host threads for --cold-exec cpu (0: all but one)")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="host threads for --cold-exec cpu (0: all CPUs of the affinity mask but two)")
     ap.add_argument("--profile-steps", type=int, default=64, help="steps of the kernel-timing pass")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the two prompt passes (one line of JSON each; for counter runs)")
@@ -531,8 +589,11 @@ def main():
     if not args.no_side_passes and cold_exec == moe.MOE_COLD_GPU and T == 1:
         # the method's other way to serve misses, same workload, measured here (a context of its own)
         result["cold_picks_on_host_threads"] = host_cold_pass(moe, torch, wl, stream, host_alloc, args.pool, x_all,
-                                                              logits_all, args.steps, args.warmup)
+                                                              logits_all, args.steps, args.warmup,
+                                                              cpu_threads=args.cpu_threads)
         log(f"host-thread cold picks: {result['cold_picks_on_host_threads']}")
+    if not args.no_side_passes and wl.name == "decode-e512k8-h2048f1024-l48-b1":
+        result["large_model"] = large_pass(moe, torch, stream, host_alloc)
     if not args.no_side_passes:
         result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc) for name in PREFILL_WORKLOADS]
         log(f"prefill: {result['prefill']}")

@@ -143,7 +143,9 @@ typedef struct {
                               moe_forward needs logits and E <= 512 and is not
                               capturable; see moe_forward                    */
   int32_t cpu_threads;     /* host threads for MOE_COLD_CPU, 0..256 (0: one
-                              per hardware thread but one)                   */
+                              per CPU the process may run on, but two: one
+                              left to the thread that launches the forwards,
+                              one to the HIP runtime's completion thread)    */
 } moe_config;
 
 typedef struct {

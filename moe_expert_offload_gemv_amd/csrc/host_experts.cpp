@@ -246,6 +246,7 @@ class Executor {
       dot_ = row_dot_scalar, isa_ = "scalar";
     }
     h_.assign((size_t)P_ * F_, 0.f);
+    x_.assign((size_t)max_tokens * H_, 0.f);
     groups_.reserve(P_);
     coord_ = std::thread([this] { coordinate(); });
   }
@@ -345,6 +346,10 @@ class Executor {
  private:
 
   void compute(const Job& j, int P) {
+    // the activations, once, into private memory: the dot products read each
+    // row once per weight row, and the mailbox is pinned memory the host may
+    // map uncached
+    std::memcpy(x_.data(), mb_.x, sizeof(float) * (size_t)j.T * H_);
     // group the cold picks by expert, in order of first appearance
     groups_.clear();
     for (int p = 0; p < P; ++p) {
@@ -381,7 +386,7 @@ class Executor {
         const uint16_t* us = reinterpret_cast<const uint16_t*>(g.w + pl_.up_scl) + (int64_t)row * kbh;
         for (int c = 0; c < g.n; c += kMaxNt) {
           const int nt = std::min(kMaxNt, g.n - c);
-          for (int t = 0; t < nt; ++t) v[t] = mb_.x + (int64_t)(g.pick[c + t] / k_) * H_;
+          for (int t = 0; t < nt; ++t) v[t] = x_.data() + (int64_t)(g.pick[c + t] / k_) * H_;
           dot_(gn, gs, kbh, v, nt, gv);
           dot_(un, us, kbh, v, nt, uv);
           for (int t = 0; t < nt; ++t) h_[(size_t)g.pick[c + t] * F_ + row] = gv[t] / (1.0f + std::exp(-gv[t])) * uv[t];
@@ -418,7 +423,7 @@ class Executor {
   Mailbox mb_;
   RowDotFn dot_ = row_dot_scalar;
   const char* isa_ = "scalar";
-  std::vector<float> h_;
+  std::vector<float> h_, x_;
   std::vector<Group> groups_;
   Pool pool_;
   std::mutex qm_;

@@ -14,6 +14,7 @@
 // acceleration ..." README ("How it works": admission only after repeated use
 // within the last 64 tokens).
 #include <hip/hip_runtime.h>
+#include <sched.h>
 
 #include <algorithm>
 #include <cstdarg>
@@ -466,9 +467,14 @@ static int host_exec_create(moe_ctx* c) {
   mb.x = (const float*)(c->mbox + c->mb_off_x);
   mb.y_cold = (float*)(c->mbox + c->mb_off_y);
   int threads = c->cfg.cpu_threads;
-  if (threads == 0) {  // every hardware thread but one, which is left to the caller's launches
-    const unsigned n = std::thread::hardware_concurrency();
-    threads = (int)std::max(1u, (n ? n : 2) - 1);
+  if (threads == 0) {
+    // every CPU of the affinity mask but two: the thread launching the
+    // forwards and the HIP runtime's completion thread each keep a CPU busy,
+    // and a pool helper that loses its CPU to them stalls every phase
+    // barrier for a whole scheduler time slice
+    cpu_set_t set;
+    int n = sched_getaffinity(0, sizeof(set), &set) == 0 ? CPU_COUNT(&set) : (int)std::thread::hardware_concurrency();
+    threads = std::max(1, n - 2);
   }
   std::string err;
   c->hx = moe_host::executor_create(threads, c->H, c->F, c->k, (int)T, pl, mb, &err);
