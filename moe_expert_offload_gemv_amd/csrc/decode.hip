@@ -81,11 +81,37 @@ __device__ __forceinline__ float block_qdot(uint4 q, const float* __restrict__ x
   return a0 + a1;
 }
 
-template <int LPR>
-__device__ __forceinline__ float row_reduce(float v) {
+// Sums the per-lane partials of a wave's 4 rows (W values per row) over the
+// LPR lanes of each row group at once: two butterfly steps (xor 1, xor 2, by
+// DPP) in which each lane keeps half of its rows and adds its partner's
+// copies of them, then xor shuffles over the rest of the group. Row i ends
+// in the lanes with (lb & 3) == i. Against one full butterfly per row (24
+// shuffles through the LDS crossbar per value pair), 2 (LPR = 8) to 8
+// (LPR = 64) shuffles per wave.
+template <int LPR, int W>
+__device__ __forceinline__ void reduce4_rows(const float (&v)[W][4], float (&out)[W]) {
+  static_assert(LPR >= 8 && LPR <= 64, "row groups of 8 to 64 lanes");
+  const int lane = threadIdx.x & 63;
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  float k[W][2];
 #pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  for (int w = 0; w < W; ++w)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float keep = b0 ? v[w][2 * i + 1] : v[w][2 * i];
+      const float send = b0 ? v[w][2 * i] : v[w][2 * i + 1];
+      k[w][i] = keep + __uint_as_float(route_dev::dpp32<route_dev::kDppQuadXor1>(__float_as_uint(send)));
+    }
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const float keep = b1 ? k[w][1] : k[w][0];
+    const float send = b1 ? k[w][0] : k[w][1];
+    out[w] = keep + __uint_as_float(route_dev::dpp32<route_dev::kDppQuadXor2>(__float_as_uint(send)));
+  }
+#pragma unroll
+  for (int m = 4; m < LPR; m <<= 1)
+#pragma unroll
+    for (int w = 0; w < W; ++w) out[w] += __shfl_xor(out[w], m, 64);
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -172,12 +198,13 @@ struct RowTile {
       for (int j = 0; j < BPL; ++j)
         __asm__ volatile("" : "+v"(q[it][j].x), "+v"(q[it][j].y), "+v"(q[it][j].z), "+v"(q[it][j].w), "+v"(d[it][j]));
   }
-  __device__ __forceinline__ float dot(int it, const float (&xs)[BPL][32], const float (&sx)[BPL]) const {
+  // this lane's share of row group it's dot product (reduce4_rows sums it)
+  __device__ __forceinline__ float partial(int it, const float (&xs)[BPL][32], const float (&sx)[BPL]) const {
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < BPL; ++j)
       acc = fmaf(half_bits_to_float(d[it][j]), fmaf(-8.0f, sx[j], block_qdot(q[it][j], xs[j])), acc);
-    return row_reduce<LPR>(acc);
+    return acc;
   }
 };
 
@@ -187,10 +214,41 @@ __device__ __forceinline__ bool wanted(uint8_t kind) {
   return MODE == kAll || (MODE == kOnlyHot && (kind & kCold) == 0) || (MODE == kOnlyCold && (kind & kCold) != 0);
 }
 
+// h rows of one pick: lane lb < 4 of each row group stores row row0 + lb RPW
+template <int LPR, int BPL, int NIT>
+__device__ __forceinline__ void gateup_store(const RowTile<LPR, BPL, NIT>& g, const RowTile<LPR, BPL, NIT>& u,
+                                             const float (&xs)[BPL][32], const float (&sx)[BPL], int row0, int lb,
+                                             int nrows, float* __restrict__ out) {
+  static_assert(NIT == 4, "reduce4_rows sums 4 rows per lane");
+  float pv[2][4], sv[2];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) pv[0][it] = g.partial(it, xs, sx), pv[1][it] = u.partial(it, xs, sx);
+  reduce4_rows<LPR, 2>(pv, sv);
+  const int r = row0 + lb * (64 / LPR);
+  if (lb < NIT && r < nrows) out[r] = silu(sv[0]) * sv[1];
+}
+template <int LPR, int BPL, int NIT>
+__device__ __forceinline__ void down_store(const RowTile<LPR, BPL, NIT>& d, const float (&hs)[BPL][32],
+                                           const float (&sh)[BPL], int row0, int lb, int nrows,
+                                           float* __restrict__ out) {
+  static_assert(NIT == 4, "reduce4_rows sums 4 rows per lane");
+  float pv[1][4], sv[1];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) pv[0][it] = d.partial(it, hs, sh);
+  reduce4_rows<LPR, 1>(pv, sv);
+  const int r = row0 + lb * (64 / LPR);
+  if (lb < NIT && r < nrows) out[r] = sv[0];
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // routing + lookup + gate/up GEMV + SwiGLU; grid = (row chunks of F, picks).
+// Wave 0 of each work-group routes the token and looks the pick up (once per
+// work-group, not per wave: 2048 waves repeating the top-k and the loads of
+// the logits and the table row contended for each CU's scalar unit and
+// memory pipeline) while all four waves stage the token's activations in
+// LDS; the pick reaches the other waves through LDS.
 // r.policy = 1: wave 0 of work-group x = 0 of each pick applies the pick's
 // side effects (the same as route_kernel's); 0: none (a second launch of the
 // same step, in the timing split).
@@ -199,44 +257,101 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
   constexpr int NJ = kFusedRouteMaxExperts / 64;
   constexpr int RPW = 64 / LPR;
   constexpr int ROWS_WG = 4 * NIT * RPW;
+  constexpr int KB = LPR * BPL;  // blocks per row: H / 32
+  // the activations, float4 c of block b at 8 b + (c ^ (b & 7)): the
+  // staging writes (8 lanes per block) and the slice reads (one block per
+  // lane) both hit distinct banks
+  __shared__ float4 s_x[KB * 8];
+  __shared__ int32_t s_pick[3];  // expert, slot (-1: cold), last-miss clock
   const int p = blockIdx.y;
   const int t = p / a.k, pick = p - t * a.k;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lb = lane % LPR, rg = lane / LPR;
   const int E = r.E;
-
-  // loads that do not depend on the routing: logits, table entries, activations
-  float z[NJ];
-  int32_t tb[NJ];
-  uint32_t lm[NJ];
   const bool may_capture = p < r.capture_picks;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int e = lane + 64 * j;
-    z[j] = e < E ? r.logits[(int64_t)t * E + e] : 0.f;
-    tb[j] = e < E ? r.tbl[e] : -1;
-    lm[j] = (may_capture && e < E) ? r.last_miss[e] : 0u;
+
+  {
+    const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)t * a.H);
+    for (int q = threadIdx.x; q < KB * 8; q += 256) {
+      const int b = q >> 3, c = q & 7;
+      s_x[b * 8 + (c ^ (b & 7))] = src[q];
+    }
   }
   const uint32_t clk = r.ctrl->clock + (uint32_t)t;
-  float xs[BPL][32], sx[BPL];
-  load_slice<LPR, BPL>(a.x + (int64_t)t * a.H, lb, xs, sx);
-
-  uint64_t key[NJ];
+  // wave 0 of work-group x = 0 applies the side effects and needs every
+  // pick's logit for the weight; the others route up to their own pick
+  const bool policy_wave = r.policy && blockIdx.x == 0 && wave == 0;
+  if (wave == 0) {
+    float z[NJ];
+    int32_t tb[NJ];
+    uint32_t lm[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) key[j] = (lane + 64 * j < E) ? route_dev::route_key(z[j], lane + 64 * j) : 0;
-  int my_e;
-  uint64_t my_key;
-  route_dev::wave_topk<NJ>(key, E, a.k, lane, my_e, my_key);
-  const int e = __builtin_amdgcn_readlane(my_e, pick);
-  int slot_l = -1;
-  uint32_t lm_l = 0;
+    for (int j = 0; j < NJ; ++j) {
+      const int e = lane + 64 * j;
+      z[j] = e < E ? r.logits[(int64_t)t * E + e] : 0.f;
+      tb[j] = e < E ? r.tbl[e] : -1;
+      lm[j] = (may_capture && e < E) ? r.last_miss[e] : 0u;
+    }
+    static_assert(NJ == 8, "the fused routing holds 8 experts per lane");
+    uint32_t v[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    slot_l = j == (e >> 6) ? tb[j] : slot_l;
-    lm_l = j == (e >> 6) ? lm[j] : lm_l;
+    for (int j = 0; j < NJ; ++j) v[j] = lane + 64 * j < E ? route_dev::order_bits(z[j]) : 0u;
+    // lane i < k ends with pick i's order bits (the weight needs them all)
+    uint32_t my_bits = 0;
+    int e;
+    if (a.k <= 8) {
+      uint32_t top[8];
+      route_dev::wave_top8(v, top);
+      uint32_t bits;
+      e = route_dev::top8_expert(v, top, pick, E, bits);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) my_bits = lane == i ? top[i] : my_bits;
+    } else {
+      route_dev::WaveTopK<NJ> tk;
+      tk.init_bits(v);
+      int my_e;
+      route_dev::wave_topk_rounds(tk, E, policy_wave ? a.k : pick + 1, lane, my_e, my_bits);
+      e = __builtin_amdgcn_readlane(my_e, pick);
+    }
+    int slot_l = -1;
+    uint32_t lm_l = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      slot_l = j == (e >> 6) ? tb[j] : slot_l;
+      lm_l = j == (e >> 6) ? lm[j] : lm_l;
+    }
+    const int slot = __builtin_amdgcn_readlane(slot_l, e & 63);
+    const uint32_t prev = (uint32_t)__builtin_amdgcn_readlane((int)lm_l, e & 63);
+    if (lane == 0) s_pick[0] = e, s_pick[1] = slot, s_pick[2] = (int32_t)prev;
+    if (policy_wave) {
+      const bool hot = slot >= 0;
+      const bool capture = !hot && may_capture && r.S > 0 &&
+                           (r.admit_misses == 1 || (prev != 0 && clk - prev < (uint32_t)r.window));
+      const float wl = route_dev::wave_pick_weight(my_bits, a.k, lane);
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), pick));
+      if (lane == 0) {
+        uint64_t rec = ((uint64_t)clk << 32) | ((uint64_t)r.layer << 12) | (uint64_t)e;
+        if (hot) {
+          rec |= kRecordHit;
+          atomicMax(&r.stamps[slot], clk);
+        }
+        r.records[p] = rec;
+        atomicAdd(&r.counts[e], 1u);
+        r.ids[p] = e;
+        r.w[p] = w;
+        r.addr[p] = hot ? r.pool + (int64_t)slot * r.expert_bytes : r.host + (int64_t)e * r.expert_bytes;
+        r.kind[p] = hot ? kHot : (capture ? (uint8_t)(kCold | kCaptured) : kCold);
+        if (capture) r.cap_tag[p] = clk;
+        if (r.ids_user) r.ids_user[p] = e;
+        if (r.w_user) r.w_user[p] = w;
+        if (p == 0) atomicMax(&r.ctrl->step_tokens, (uint32_t)r.T);
+      }
+    }
   }
-  const int slot = __builtin_amdgcn_readlane(slot_l, e & 63);
-  const uint32_t prev = (uint32_t)__builtin_amdgcn_readlane((int)lm_l, e & 63);
+  __syncthreads();
+  const int e = __builtin_amdgcn_readfirstlane(s_pick[0]);
+  const int slot = __builtin_amdgcn_readfirstlane(s_pick[1]);
+  const uint32_t prev = (uint32_t)__builtin_amdgcn_readfirstlane(s_pick[2]);
   const bool hot = slot >= 0;
   // the cache step admits a cold pick on its first miss, or on a repeat
   // inside the window (a repeat earlier in this same step is not seen here)
@@ -244,27 +359,6 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
                        (r.admit_misses == 1 || (prev != 0 && clk - prev < (uint32_t)r.window));
   const uint8_t* base = hot ? r.pool + (int64_t)slot * r.expert_bytes : r.host + (int64_t)e * r.expert_bytes;
 
-  if (r.policy && blockIdx.x == 0 && wave == 0) {
-    const float wl = route_dev::wave_pick_weight(my_key, a.k, lane);
-    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), pick));
-    if (lane == 0) {
-      uint64_t rec = ((uint64_t)clk << 32) | ((uint64_t)r.layer << 12) | (uint64_t)e;
-      if (hot) {
-        rec |= kRecordHit;
-        atomicMax(&r.stamps[slot], clk);
-      }
-      r.records[p] = rec;
-      atomicAdd(&r.counts[e], 1u);
-      r.ids[p] = e;
-      r.w[p] = w;
-      r.addr[p] = base;
-      r.kind[p] = hot ? kHot : (capture ? (uint8_t)(kCold | kCaptured) : kCold);
-      if (capture) r.cap_tag[p] = clk;
-      if (r.ids_user) r.ids_user[p] = e;
-      if (r.w_user) r.w_user[p] = w;
-      if (p == 0) atomicMax(&r.ctrl->step_tokens, (uint32_t)r.T);
-    }
-  }
   if (r.pub_seq && blockIdx.x == gridDim.x - 1) {
     // the host threads compute the cold picks: the last work-group of each
     // pick only hands the pick over (so no GEMV wave waits on host writes).
@@ -295,13 +389,22 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
          reinterpret_cast<const uint16_t*>(base + a.lay.gate_scl), row0, a.F, lb, !hot);
   u.load(reinterpret_cast<const uint4*>(base + a.lay.up_nib), reinterpret_cast<const uint16_t*>(base + a.lay.up_scl),
          row0, a.F, lb, !hot);
+  // the lane's activation slice from LDS (blocks lb + LPR j), with the
+  // per-block sums of the -8 offset, added in the order load_slice uses
+  float xs[BPL][32], sx[BPL];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const float gv = g.dot(it, xs, sx);
-    const float uv = u.dot(it, xs, sx);
-    const int rr = row0 + it * RPW;
-    if (lb == 0 && rr < a.F) a.out[(int64_t)p * a.F + rr] = silu(gv) * uv;
+  for (int j = 0; j < BPL; ++j) {
+    const int b = lb + LPR * j;
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float4 q = s_x[b * 8 + (c ^ (b & 7))];
+      xs[j][4 * c + 0] = q.x, xs[j][4 * c + 1] = q.y, xs[j][4 * c + 2] = q.z, xs[j][4 * c + 3] = q.w;
+      s += (q.x + q.y) + (q.z + q.w);
+    }
+    sx[j] = s;
   }
+  gateup_store<LPR, BPL, NIT>(g, u, xs, sx, row0, lb, a.F, a.out + (int64_t)p * a.F);
   // after the arithmetic, so the loads are consumed as they arrive
   if (capture) {
     uint8_t* cap = a.capture + (int64_t)p * a.lay.bytes;
@@ -334,13 +437,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(GemvArgs a) {
          row0, a.F, lb, cold);
   float xs[BPL][32], sx[BPL];
   load_slice<LPR, BPL>(a.x + (int64_t)t * a.H, lb, xs, sx);
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const float gv = g.dot(it, xs, sx);
-    const float uv = u.dot(it, xs, sx);
-    const int r = row0 + it * RPW;
-    if (lb == 0 && r < a.F) a.out[(int64_t)p * a.F + r] = silu(gv) * uv;
-  }
+  gateup_store<LPR, BPL, NIT>(g, u, xs, sx, row0, lb, a.F, a.out + (int64_t)p * a.F);
 }
 
 // ---------------------------------------------------------------------------
@@ -361,12 +458,7 @@ __global__ __launch_bounds__(256) void gemv_down_pick_kernel(GemvArgs a) {
          reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0, a.H, lb);
   float hs[BPL][32], sh[BPL];
   load_slice<LPR, BPL>(a.x + (int64_t)p * a.F, lb, hs, sh);
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const float v = d.dot(it, hs, sh);
-    const int r = row0 + it * RPW;
-    if (lb == 0 && r < a.H) a.ypick[(int64_t)p * a.H + r] = v;
-  }
+  down_store<LPR, BPL, NIT>(d, hs, sh, row0, lb, a.H, a.ypick + (int64_t)p * a.H);
 }
 
 // ---------------------------------------------------------------------------
@@ -391,10 +483,12 @@ __global__ __launch_bounds__(256) void gemv_down_combine_kernel(GemvArgs a) {
            reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0 + rg, a.H, lb, (a.kind[p] & kCold) != 0);
     float hs[BPL][32], sh[BPL];
     load_slice<LPR, BPL>(a.x + p * a.F, lb, hs, sh);
+    {
+      float pv[1][4], sv[1];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const float v = d.dot(it, hs, sh);
-      if (lb == 0) part[i][it * RPW + rg] = v;
+      for (int it = 0; it < NIT; ++it) pv[0][it] = d.partial(it, hs, sh);
+      reduce4_rows<LPR, 1>(pv, sv);
+      if (lb < NIT) part[i][lb * RPW + rg] = sv[0];
     }
     if ((a.kind[p] & kCaptured) && p < a.capture_picks) {  // after the arithmetic, as in the gate/up GEMV
       uint8_t* cap = a.capture + p * a.lay.bytes;
@@ -572,13 +666,7 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GemvArgs a, GroupAr
       u.keep_packed();
       float xs[BPL][32], sx[BPL];
       V::slice(xsh[b], lb, xs, sx);
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const float gv = g.dot(it, xs, sx);
-        const float uv = u.dot(it, xs, sx);
-        const int r = row0 + it * RPW;
-        if (lb == 0 && r < a.F) a.out[(int64_t)p * a.F + r] = silu(gv) * uv;
-      }
+      gateup_store<LPR, BPL, NIT>(g, u, xs, sx, row0, lb, a.F, a.out + (int64_t)p * a.F);
     }
     if (c0 + NB < grp.z) __syncthreads();  // everyone is done with the chunk before it is overwritten
   }
@@ -615,12 +703,7 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GemvArgs a, GroupArgs
       d.keep_packed();
       float hs[BPL][32], sh[BPL];
       V::slice(hsh[b], lb, hs, sh);
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const float v = d.dot(it, hs, sh);
-        const int r = row0 + it * RPW;
-        if (lb == 0 && r < a.H) a.ypick[(int64_t)p * a.H + r] = v;
-      }
+      down_store<LPR, BPL, NIT>(d, hs, sh, row0, lb, a.H, a.ypick + (int64_t)p * a.H);
     }
     if (c0 + NB < grp.z) __syncthreads();
   }

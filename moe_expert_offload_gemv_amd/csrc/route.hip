@@ -60,15 +60,11 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
     for (int e = lane; e < E; e += 64) s_tbl[e] = a.tbl[e];
   }
 
-  uint64_t key[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) key[j] = (lane + 64 * j < E) ? route_key(z[j], lane + 64 * j) : 0;
-
   // k rounds; lane i keeps pick i, then its softmax weight
   int my_e;
-  uint64_t my_key;
-  wave_topk<NJ>(key, E, a.k, lane, my_e, my_key);
-  const float w = wave_pick_weight(my_key, a.k, lane);
+  uint32_t my_bits;
+  wave_topk<NJ>(z, E, a.k, lane, my_e, my_bits);
+  const float w = wave_pick_weight(my_bits, a.k, lane);
   __syncthreads();  // the table row in LDS
 
   if (a.policy && t == 0 && lane == 0) atomicMax(&a.ctrl->step_tokens, (uint32_t)a.T);

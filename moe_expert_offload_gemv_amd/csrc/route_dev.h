@@ -1,9 +1,9 @@
 // route_dev.h - device helpers of top-k routing shared by the routing
 // kernel and the fused routing + gate/up GEMV (internal to the library).
 //
-// The argmax of each round is a wave-wide max of one 64-bit key per lane
-// (order-preserving float bits, then 0xFFFFFFFF - id) reduced with DPP
-// butterflies inside 16-lane rows and four lane reads across rows.
+// Each round of the top-k is a wave-wide max of order-preserving logit bits
+// (DPP butterflies inside 16-lane rows, four lane reads across rows); the
+// lowest expert id holding the max comes from ballots.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -21,26 +21,6 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  return ((uint64_t)dpp32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp32<CTRL>((uint32_t)v);
-}
-__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// all 64 lanes must be active
-__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
-  v = max64(v, dpp64<kDppQuadXor1>(v));
-  v = max64(v, dpp64<kDppQuadXor2>(v));
-  v = max64(v, dpp64<kDppRowHalfMirror>(v));
-  v = max64(v, dpp64<kDppRowMirror>(v));  // every lane of a 16-lane row holds the row max
-  return max64(max64(readlane64(v, 0), readlane64(v, 16)), max64(readlane64(v, 32), readlane64(v, 48)));
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
   v += __uint_as_float(dpp32<kDppQuadXor1>(__float_as_uint(v)));
   v += __uint_as_float(dpp32<kDppQuadXor2>(__float_as_uint(v)));
@@ -53,44 +33,190 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-// order-preserving key: larger logit first, then lower expert id; 0 = none
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
+// order-preserving bits of a logit: a larger logit gives a larger value, -0
+// counts as +0; 0 stands for "no expert" (past E, or picked already)
+__device__ __forceinline__ uint32_t order_bits(float v) {
   if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t u = (uint32_t)(key >> 32);
+__device__ __forceinline__ float order_logit(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-
-// top-k of one token by one wave (all 64 lanes active): key[j] is the key of
-// expert lane + 64 j (0 when past E). Lane i < k ends with pick i's expert
-// and key; picks are in descending logit order, equal logits lower id first.
-template <int NJ>
-__device__ __forceinline__ void wave_topk(const uint64_t (&key)[NJ], int E, int k, int lane, int& my_e,
-                                          uint64_t& my_key) {
-  uint64_t taken = 0;  // bit j: expert lane + 64 j already picked
-  my_e = 0;
-  my_key = 0;
-  for (int i = 0; i < k; ++i) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) best = ((taken >> j) & 1) ? best : max64(best, key[j]);
-    best = wave_max64(best);
-    int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    e = (e >= 0 && e < E) ? e : 0;  // always an expert of the layer, so every address stays in bounds
-    if ((e & 63) == lane) taken |= 1ull << (e >> 6);
-    if (lane == i) my_e = e, my_key = best;
-  }
+// all 64 lanes must be active
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp32<kDppQuadXor1>(v));
+  v = max(v, dpp32<kDppQuadXor2>(v));
+  v = max(v, dpp32<kDppRowHalfMirror>(v));
+  v = max(v, dpp32<kDppRowMirror>(v));  // every lane of a 16-lane row holds the row max
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
-// softmax over the k chosen logits (lane i < k holds pick i's key; pick 0
-// holds the largest): the weight of this lane's pick, 0 on lanes >= k
-__device__ __forceinline__ float wave_pick_weight(uint64_t my_key, int k, int lane) {
-  const float my_z = key_logit(my_key);
+// Top-k of one token by one wave (all 64 lanes active), one pick per round:
+// the largest remaining logit, and among equal ones the lowest expert id.
+// Lane l holds the order bits of experts l + 64 j. A round is a 32-bit
+// wave max; the lowest id holding it comes from the ballots of the equal
+// entries (expert 64 j + lane: the first slot j with a match, then its
+// lowest lane), so no 64-bit (value, id) key is reduced.
+template <int NJ>
+struct WaveTopK {
+  uint32_t v[NJ];
+  __device__ __forceinline__ void init(const float (&z)[NJ], int E, int lane) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) v[j] = lane + 64 * j < E ? order_bits(z[j]) : 0u;
+  }
+  __device__ __forceinline__ void init_bits(const uint32_t (&bits)[NJ]) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) v[j] = bits[j];
+  }
+  // the next pick's expert (wave-uniform; always an expert of the layer, so
+  // every address stays in bounds) and its order bits
+  __device__ __forceinline__ int next(int E, int lane, uint32_t& bits) {
+    uint32_t m = v[0];
+#pragma unroll
+    for (int j = 1; j < NJ; ++j) m = max(m, v[j]);
+    m = wave_max_u32(m);
+    int e = 0;
+    if (m != 0) {
+#pragma unroll
+      for (int j = NJ - 1; j >= 0; --j) {
+        const uint64_t b = __ballot(v[j] == m);
+        if (b) e = 64 * j + (int)__builtin_ctzll(b);
+      }
+    }
+    e = e < E ? e : 0;
+    const bool mine = lane == (e & 63);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) v[j] = (mine && j == (e >> 6)) ? 0u : v[j];
+    bits = m;
+    return e;
+  }
+};
+
+// The first `rounds` picks: lane i < rounds ends with pick i's expert and
+// order bits; picks are in descending logit order, equal logits lower id first.
+template <int NJ>
+__device__ __forceinline__ void wave_topk_rounds(WaveTopK<NJ>& tk, int E, int rounds, int lane, int& my_e,
+                                                 uint32_t& my_bits) {
+  my_e = 0;
+  my_bits = 0;
+  for (int i = 0; i < rounds; ++i) {
+    uint32_t bits;
+    const int e = tk.next(E, lane, bits);
+    if (lane == i) my_e = e, my_bits = bits;
+  }
+}
+template <int NJ>
+__device__ __forceinline__ void wave_topk(const float (&z)[NJ], int E, int rounds, int lane, int& my_e,
+                                          uint32_t& my_bits) {
+  WaveTopK<NJ> tk;
+  tk.init(z, E, lane);
+  wave_topk_rounds(tk, E, rounds, lane, my_e, my_bits);
+}
+
+// ---------------------------------------------------------------------------
+// Top-8 by sorting networks (k <= 8, E <= 512), for the latency-bound decode
+// path: the rounds above are a chain of dependent steps each, this is a few
+// dozen steps with eight independent operations apiece. Lane l sorts its 8
+// order bits (Batcher's odd-even merge sort, 19 compare-exchanges), then six
+// butterfly steps each merge a lane's list with a partner's from the other
+// half of a group twice the size (lane ^ 1, ^ 2, the mirror within 8 and
+// within 16 lanes, ^ 16, ^ 32): the elementwise max of one sorted list and
+// the other reversed holds the 8 largest of both as a bitonic sequence,
+// which three half-cleaner stages sort. Every lane ends with the 8 largest
+// order bits of the wave, descending, ties repeated.
+
+__device__ __forceinline__ void cas_desc(uint32_t& a, uint32_t& b) {
+  const uint32_t hi = max(a, b), lo = min(a, b);
+  a = hi, b = lo;
+}
+__device__ __forceinline__ void sort8_desc(uint32_t (&a)[8]) {
+  cas_desc(a[0], a[1]), cas_desc(a[2], a[3]), cas_desc(a[4], a[5]), cas_desc(a[6], a[7]);
+  cas_desc(a[0], a[2]), cas_desc(a[1], a[3]), cas_desc(a[4], a[6]), cas_desc(a[5], a[7]);
+  cas_desc(a[1], a[2]), cas_desc(a[5], a[6]);
+  cas_desc(a[0], a[4]), cas_desc(a[1], a[5]), cas_desc(a[2], a[6]), cas_desc(a[3], a[7]);
+  cas_desc(a[2], a[4]), cas_desc(a[3], a[5]);
+  cas_desc(a[1], a[2]), cas_desc(a[3], a[4]), cas_desc(a[5], a[6]);
+}
+__device__ __forceinline__ void clean8_desc(uint32_t (&c)[8]) {
+  cas_desc(c[0], c[4]), cas_desc(c[1], c[5]), cas_desc(c[2], c[6]), cas_desc(c[3], c[7]);
+  cas_desc(c[0], c[2]), cas_desc(c[1], c[3]), cas_desc(c[4], c[6]), cas_desc(c[5], c[7]);
+  cas_desc(c[0], c[1]), cas_desc(c[2], c[3]), cas_desc(c[4], c[5]), cas_desc(c[6], c[7]);
+}
+template <int CTRL>
+__device__ __forceinline__ void merge8_dpp(uint32_t (&t)[8]) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = max(t[i], dpp32<CTRL>(t[7 - i]));
+  clean8_desc(c);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = c[i];
+}
+__device__ __forceinline__ void merge8_xor(uint32_t (&t)[8], int mask) {
+  uint32_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = max(t[i], (uint32_t)__shfl_xor((int)t[7 - i], mask, 64));
+  clean8_desc(c);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = c[i];
+}
+// all 64 lanes must be active; v[j]: order bits of expert lane + 64 j
+__device__ __forceinline__ void wave_top8(const uint32_t (&v)[8], uint32_t (&t)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t[j] = v[j];
+  sort8_desc(t);
+  merge8_dpp<kDppQuadXor1>(t);
+  merge8_dpp<kDppQuadXor2>(t);
+  merge8_dpp<kDppRowHalfMirror>(t);
+  merge8_dpp<kDppRowMirror>(t);
+  merge8_xor(t, 16);
+  merge8_xor(t, 32);
+}
+// The expert of pick `rank` (wave-uniform, < 8) and its order bits, from the
+// lane's order bits v and their wave_top8 t. With m = t[rank] and r the
+// number of earlier picks of the same value, the pick is the r-th lowest
+// expert id holding m (ids 64 j + lane: slots j in order, then lanes).
+__device__ __forceinline__ int top8_expert(const uint32_t (&v)[8], const uint32_t (&t)[8], int rank, int E,
+                                           uint32_t& bits) {
+  uint32_t mv = t[0];
+  int rv = 0;
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mv = rank == i ? t[i] : mv;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) rv += (i < rank && t[i] == mv) ? 1 : 0;
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)mv);
+  int r = __builtin_amdgcn_readfirstlane(rv);
+  int e = 0;
+  if (m != 0) {
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint64_t b = __ballot(v[j] == m);
+      const int c = __builtin_popcountll(b);
+      if (!found) {
+        if (r < c) {
+          for (int q = 0; q < r; ++q) b &= b - 1;
+          e = 64 * j + (int)__builtin_ctzll(b);
+          found = true;
+        } else {
+          r -= c;
+        }
+      }
+    }
+  }
+  bits = m;
+  return e < E ? e : 0;  // always an expert of the layer, so every address stays in bounds
+}
+
+// softmax over the k chosen logits (lane i < k holds pick i's order bits;
+// pick 0 holds the largest): the weight of this lane's pick, 0 on lanes >= k
+__device__ __forceinline__ float wave_pick_weight(uint32_t my_bits, int k, int lane) {
+  const float my_z = order_logit(my_bits);
   const float z0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_z), 0));
   const float ex = lane < k ? expf(my_z - z0) : 0.f;
   return ex / wave_sum(ex);
