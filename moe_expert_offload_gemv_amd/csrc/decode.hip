@@ -114,6 +114,19 @@ __device__ __forceinline__ void reduce4_rows(const float (&v)[W][4], float (&out
     for (int w = 0; w < W; ++w) out[w] += __shfl_xor(out[w], m, 64);
 }
 
+// Full butterfly of one value over the LPR lanes of its row group. The
+// grouped kernels reduce row by row with it: they run one pick after another
+// at two work-groups per CU, where the shuffles of row i overlap the
+// arithmetic of row i + 1; a 4-row reduce4_rows chain at the end of every
+// pick measured slower there (gate/up 436 -> 470 us, down 205 -> 242 us per
+// layer at batch 32 on the 256-expert model).
+template <int LPR>
+__device__ __forceinline__ float row_reduce(float v) {
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // Loads a cold pick's wave keeps in flight after issuing each row of a
@@ -666,7 +679,13 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GemvArgs a, GroupAr
       u.keep_packed();
       float xs[BPL][32], sx[BPL];
       V::slice(xsh[b], lb, xs, sx);
-      gateup_store<LPR, BPL, NIT>(g, u, xs, sx, row0, lb, a.F, a.out + (int64_t)p * a.F);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const float gv = row_reduce<LPR>(g.partial(it, xs, sx));
+        const float uv = row_reduce<LPR>(u.partial(it, xs, sx));
+        const int r = row0 + it * RPW;
+        if (lb == 0 && r < a.F) a.out[(int64_t)p * a.F + r] = silu(gv) * uv;
+      }
     }
     if (c0 + NB < grp.z) __syncthreads();  // everyone is done with the chunk before it is overwritten
   }
@@ -703,7 +722,12 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GemvArgs a, GroupArgs
       d.keep_packed();
       float hs[BPL][32], sh[BPL];
       V::slice(hsh[b], lb, hs, sh);
-      down_store<LPR, BPL, NIT>(d, hs, sh, row0, lb, a.H, a.ypick + (int64_t)p * a.H);
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const float v = row_reduce<LPR>(d.partial(it, hs, sh));
+        const int r = row0 + it * RPW;
+        if (lb == 0 && r < a.H) a.ypick[(int64_t)p * a.H + r] = v;
+      }
     }
     if (c0 + NB < grp.z) __syncthreads();
   }
