@@ -330,9 +330,15 @@ def cpu_baseline(wl, seconds, logits):
             spent += time.perf_counter() - t0
         tokens += wl.tokens
         step += 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return dict(value=tokens / spent, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"first {tokens} decode tokens through all {wl.n_layers} layers (fp64 oracle, "
-                       f"{spent:.1f} s of oracle time; weight generation excluded)")
+                       f"{spent:.1f} s of oracle time; weight generation excluded)", cpu_model=model)
 
 
 def main():
@@ -568,6 +574,19 @@ def main():
         torch.cuda.synchronize()
         result["pcie_dma_h2d_GBps"] = round(3 * (1 << 30) / (time.perf_counter() - t2) / 1e9, 2)
         del src, dst
+        # read ceilings of a plain 128-bit streaming kernel: 8 GiB of HBM, 1 GiB of pinned host memory zero-copy
+        buf = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+        hbm_ceiling = moe.moe_measure_read_bandwidth(buf, reps=5)
+        del buf
+        result["ceilings"] = {
+            "hbm_stream_read_GBps": round(hbm_ceiling, 1),
+            "zero_copy_read_GBps": {
+                k_: round(moe.moe_measure_read_bandwidth(None, 1 << 30, reps=3, host_coherent=c_), 2)
+                for k_, c_ in (("coherent", True), ("noncoherent", False))},
+            "dma_h2d_GBps": result["pcie_dma_h2d_GBps"],
+            "spec": {"hbm_GBps": HBM_PEAK_GBPS, "pcie_GBps": PCIE_PEAK_GBPS}}
+        if result.get("roofline") and result["roofline"].get("unit") == "GB/s":
+            result["roofline"]["frac_of_measured_ceiling"] = round(result["roofline"]["achieved"] / hbm_ceiling, 4)
         log(f"side passes: hot {result['kernels_all_hot']} cold {result['kernels_all_cold']} "
             f"dma {result['pcie_dma_h2d_GBps']} GB/s")
 

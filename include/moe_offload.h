@@ -356,6 +356,23 @@ MOE_API int moe_get_counts(moe_ctx* ctx, uint32_t* out);
 
 MOE_API const char* moe_last_error(moe_ctx* ctx);  /* ctx NULL: the last failed moe_create of this thread */
 
+/* Measurement aid, outside the MoE path: the read bandwidth a plain
+ * streaming kernel (128-bit loads, grid-stride, 8 work-groups per CU)
+ * achieves on the current device, the ceiling the GEMVs are compared with
+ * beside the spec figures.
+ *   ptr != NULL: a device address of `bytes` readable bytes (caller-owned,
+ *                e.g. HBM); host_coherent is ignored.
+ *   ptr == NULL: the call allocates `bytes` of pinned host memory (mapped;
+ *                coherent if host_coherent != 0, else non-coherent), reads
+ *                it zero-copy over PCIe and frees it before returning.
+ * bytes > 0 and a multiple of 16; reps >= 1 timed launches after one
+ * untimed one, on `stream` (a hipStream_t; NULL = the default stream). The
+ * call synchronises with the stream. *gbps = bytes * reps / time / 1e9.
+ * Returns MOE_E_INVAL on bad arguments, MOE_E_NOMEM when an allocation
+ * fails, MOE_E_HIP on a HIP error; there is no context, so no message. */
+MOE_API int moe_measure_read_bandwidth(const void* ptr, int64_t bytes, int32_t reps, int32_t host_coherent,
+                                       void* stream, double* gbps);
+
 #ifdef __cplusplus
 }
 #endif

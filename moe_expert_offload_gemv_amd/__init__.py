@@ -36,7 +36,7 @@ MOE_POOL_GLOBAL = 1
 EXPORTED = [
     "moe_expert_bytes", "moe_create", "moe_destroy", "moe_register_layer", "moe_register_router", "moe_seed",
     "moe_forward", "moe_prefill", "moe_cache_step", "moe_get_info", "moe_get_slot_table", "moe_get_stamps",
-    "moe_get_miss_log", "moe_get_counts", "moe_last_error", "moe_profile", "moe_preheat",
+    "moe_get_miss_log", "moe_get_counts", "moe_last_error", "moe_profile", "moe_preheat", "moe_measure_read_bandwidth",
 ]
 
 
@@ -115,6 +115,7 @@ def lib():
             "moe_last_error": (C.c_char_p, [vp]),
             "moe_profile": (C.c_int, [vp, i32, C.POINTER(moe_profile_stats)]),
             "moe_preheat": (C.c_int, [vp, i32, i32, C.POINTER(i32)]),
+            "moe_measure_read_bandwidth": (C.c_int, [vp, i64, i32, i32, vp, C.POINTER(C.c_double)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -268,6 +269,24 @@ def moe_profile(ctx, enable: int = -1) -> dict:
     s = moe_profile_stats()
     _check(ctx, lib().moe_profile(ctx, enable, C.byref(s)))
     return s.as_dict()
+
+
+def moe_measure_read_bandwidth(buf=None, nbytes: int = 0, reps: int = 3, host_coherent: bool = True,
+                               stream=None) -> float:
+    """GB/s of a plain 128-bit streaming read kernel: over the cuda tensor buf
+    (HBM), or with buf None over nbytes of pinned host memory the library
+    allocates (zero-copy over PCIe). A measurement aid, not the MoE path."""
+    import torch
+
+    if buf is not None:
+        nbytes = buf.numel() * buf.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    out = C.c_double(0.0)
+    rc = lib().moe_measure_read_bandwidth(_dptr(buf), int(nbytes), int(reps), 1 if host_coherent else 0,
+                                          s.cuda_stream, C.byref(out))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_measure_read_bandwidth failed")
+    return out.value
 
 
 def moe_last_error(ctx) -> str:

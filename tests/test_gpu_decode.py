@@ -441,3 +441,19 @@ def test_grouped_batch_global_pool_cold_start_swap_lead():
     wl = Workload("decode-e32k4-h256f512-l3-b16-grouped", 116, 3, 32, 4, 256, 512, tokens=16, steps=16, zipf_s=0.9,
                   slots=8, rotation=24)
     _run_decode(wl, slots=24, check_every=2, seed=False, pool="global", swaps=(4, 1))
+
+
+@pytest.mark.gpu
+def test_read_bandwidth_ceilings():
+    """The streaming-read measurement aid: HBM from a device buffer, PCIe from
+    pinned host memory in both coherence modes; bad arguments rejected on the host."""
+    buf = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    hbm = moe.moe_measure_read_bandwidth(buf, reps=2)
+    assert 100.0 < hbm < 20000.0, hbm
+    for coherent in (True, False):
+        pcie = moe.moe_measure_read_bandwidth(None, 16 << 20, reps=1, host_coherent=coherent)
+        assert 1.0 < pcie < 200.0, (coherent, pcie)
+    with pytest.raises(moe.MoeError):
+        moe.moe_measure_read_bandwidth(None, 15, reps=1)  # not a multiple of 16
+    with pytest.raises(moe.MoeError):
+        moe.moe_measure_read_bandwidth(buf, reps=0)
