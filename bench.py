@@ -100,7 +100,23 @@ def kernel_pass(moe, torch, wl, slots, layers, steps, stream, host_alloc, logits
 PREFILL_WORKLOADS = ("prefill-e512k8-h2048f1024-t4096", "large-e256k8-h4096f1536-t12288")
 
 
-def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3):
+def fp16_gemm_ceiling(torch, n=8192, reps=20):
+    """TFLOP/s of a plain fp16 n^3 GEMM by the vendor library (hipBLASLt through torch.matmul): the matrix
+    rate this chip sustains under a GEMM load, at the clock it holds there. A reference beside the spec peak,
+    not part of the MoE path."""
+    a = torch.randn(n, n, dtype=torch.float16, device="cuda")
+    b = torch.randn(n, n, dtype=torch.float16, device="cuda")
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        a @ b
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 * reps / (time.perf_counter() - t0) / 1e12
+
+
+def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3, gemm_ceiling=None):
     """A prompt pass of one layer: end-to-end time and the grouped GEMMs against the bf16 MFMA peak."""
     import numpy as np
 
@@ -142,7 +158,9 @@ def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3):
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "grouped_gemm_kernel (gate/up + down, fp16 MFMA; time includes the scale "
                                "transposition before them), algorithmic flops 6*H*F per pair",
-                     "mfma_flops_per_algorithmic_flop": 1},
+                     "mfma_flops_per_algorithmic_flop": 1,
+                     "measured_fp16_gemm_ceiling": gemm_ceiling and round(gemm_ceiling, 1),
+                     "frac_of_measured_ceiling": gemm_ceiling and round(tflops / gemm_ceiling, 4)},
     }
 
 
@@ -396,7 +414,8 @@ def main():
         host_alloc = moe.MOE_HOST_NONCOHERENT if args.host_alloc == "noncoherent" else moe.MOE_HOST_COHERENT
         stream = torch.cuda.Stream()
         for name in PREFILL_WORKLOADS:
-            print(json.dumps(prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc)), flush=True)
+            print(json.dumps(prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc,
+                                          gemm_ceiling=fp16_gemm_ceiling(torch))), flush=True)
         return
 
     wl = WORKLOADS[args.workload]
@@ -614,7 +633,11 @@ def main():
     if not args.no_side_passes and wl.name == "decode-e512k8-h2048f1024-l48-b1":
         result["large_model"] = large_pass(moe, torch, stream, host_alloc)
     if not args.no_side_passes:
-        result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc) for name in PREFILL_WORKLOADS]
+        gemm_ceiling = fp16_gemm_ceiling(torch)
+        result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc, gemm_ceiling=gemm_ceiling)
+                             for name in PREFILL_WORKLOADS]
+        if "ceilings" in result:
+            result["ceilings"]["fp16_gemm_TFLOPs"] = round(gemm_ceiling, 1)
         log(f"prefill: {result['prefill']}")
 
     if not args.no_cpu_baseline:

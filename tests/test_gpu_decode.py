@@ -457,3 +457,35 @@ def test_read_bandwidth_ceilings():
         moe.moe_measure_read_bandwidth(None, 15, reps=1)  # not a multiple of 16
     with pytest.raises(moe.MoeError):
         moe.moe_measure_read_bandwidth(buf, reps=0)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("E,k", [(64, 8), (96, 12), (600, 6), (8, 2)])
+def test_routing_exact_ties_and_signed_zeros(E, k):
+    """Every top-k path: the sorting-network top-8 of the fused launch (k <= 8,
+    E <= 512), its rounds (k > 8) and the routing kernel (E > 512), on logits
+    full of exact ties and signed zeros. Ids bit-exact against the oracle
+    (larger logit first, equal logits lower id first, -0 equal to +0); weights
+    and outputs within tolerance."""
+    T, H, F = 4, 256, 512
+    wl = Workload(f"route-ties-e{E}k{k}", 117, 1, E, k, H, F, tokens=T, steps=1, zipf_s=1.1, slots=E // 2)
+    d = Decode(wl, slots=E // 2)
+    rng = np.random.default_rng(1000 * E + k)
+    z = (np.round(rng.standard_normal((T, E)) * 2.0) / 2.0).astype(np.float32)  # steps of 0.5: many ties
+    z[0, : k + 3] = 3.0  # more equal maxima than picks
+    z[1] = -np.abs(z[1]) - 0.5
+    z[1, ::5], z[1, 2::5] = -0.0, 0.0  # the largest values are signed zeros
+    z[3] = 1.0  # every logit equal
+    x32 = activations(wl, 0)
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_forward(d.ctx, 0, T, _dev(x32), _dev(z), y, ids, w)
+    ids_ref, w_ref = oracle.route(z, k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=2e-6)
+    g, u, dn = d.weights[0]
+    y_ref, _, _ = oracle.moe_layer(E, k, H, F, {int(e): (g[e], u[e], dn[e]) for e in np.unique(ids_ref)},
+                                   x32.astype(np.float64), logits=z)
+    assert token_rel_err(y.cpu().numpy(), y_ref) < TOL
+    d.close()
