@@ -478,10 +478,13 @@ __global__ __launch_bounds__(256) void gemv_down_pick_kernel(GemvArgs a) {
 
 // ---------------------------------------------------------------------------
 // down GEMV of the cold picks + weighted combine of every pick. grid = (row
-// chunks of H, tokens); the 4 waves take picks wave, wave+4, ... of the token
-// over the same rows; hot picks come from y_pick. Sum in pick order.
+// chunks of H, tokens); the kCombineWaves waves take picks wave, wave +
+// kCombineWaves, ... of the token over the same rows (at top-8 one pick per
+// wave, every pick's loads in flight at once); hot picks come from y_pick.
+// Sum in pick order.
+constexpr int kCombineWaves = 8;
 template <int LPR, int BPL, int NIT, int MODE>
-__global__ __launch_bounds__(256) void gemv_down_combine_kernel(GemvArgs a) {
+__global__ __launch_bounds__(64 * kCombineWaves) void gemv_down_combine_kernel(GemvArgs a) {
   constexpr int RPW = 64 / LPR;
   constexpr int ROWS = NIT * RPW;
   __shared__ float part[32][ROWS];
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(256) void gemv_down_combine_kernel(GemvArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lb = lane % LPR, rg = lane / LPR;
   const int row0 = blockIdx.x * ROWS;
-  for (int i = wave; i < a.k; i += 4) {
+  for (int i = wave; i < a.k; i += kCombineWaves) {
     const int64_t p = (int64_t)t * a.k + i;
     if (!wanted<MODE>(a.kind[p])) continue;
     const uint8_t* base = a.addr[p];
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(256) void gemv_down_combine_kernel(GemvArgs a) {
     }
   }
   __syncthreads();
-  for (int rr = threadIdx.x; rr < ROWS; rr += 256) {
+  for (int rr = threadIdx.x; rr < ROWS; rr += 64 * kCombineWaves) {
     const int r = row0 + rr;
     if (r >= a.H) continue;
     float acc = 0.f;
@@ -851,9 +854,9 @@ hipError_t down_combine_t(const GemvArgs& a, const Launch& l, int mode) {
   constexpr int ROWS = kNitCombine * (64 / LPR);
   const dim3 grid((a.H + ROWS - 1) / ROWS, a.T);
   if (mode == kOnlyCold)
-    return launch(gemv_down_combine_kernel<LPR, BPL, kNitCombine, kOnlyCold>, grid, dim3(256), l, a);
+    return launch(gemv_down_combine_kernel<LPR, BPL, kNitCombine, kOnlyCold>, grid, dim3(64 * kCombineWaves), l, a);
   if (mode != kAll) return hipErrorInvalidValue;
-  return launch(gemv_down_combine_kernel<LPR, BPL, kNitCombine, kAll>, grid, dim3(256), l, a);
+  return launch(gemv_down_combine_kernel<LPR, BPL, kNitCombine, kAll>, grid, dim3(64 * kCombineWaves), l, a);
 }
 
 // grouped kernels: as many rows per wave as the per-pick GEMVs (measured at
