@@ -455,6 +455,54 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(GemvArgs a) {
   gateup_store<LPR, BPL, NIT>(g, u, xs, sx, row0, lb, a.F, a.out + (int64_t)p * a.F);
 }
 
+// A K-vector (activation row or h row) staged in LDS for every wave of the
+// work-group (or for one wave): float4 chunk c of block lb + LPR j sits at
+// [(8 j + c) LPR + lb], so a wave's 16-byte reads of one chunk are
+// consecutive. KV = K / 4 float4s, a multiple of 64. The copy goes global ->
+// LDS by the LDS-DMA form of the global load (lane l writes 16 bytes at
+// M0 + 16 l): instruction q fills LDS chunks 64 q .. 64 q + 63, each lane
+// fetching the source chunk that belongs there; the waves that share the
+// copy take the instructions in turn.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int LPR, int BPL>
+struct SharedVec {
+  static constexpr int KV = 8 * LPR * BPL;
+  static_assert(KV % 64 == 0, "whole DMA instructions");
+  // instructions first, first + step, ... of the copy
+  __device__ __forceinline__ static void issue(const float* src, float4* dst, int first, int step, int lane) {
+    for (int q = first; q < KV / 64; q += step) {
+      const int d = 64 * q + lane;
+      const int j = d / (8 * LPR), ch = (d / LPR) % 8, lb = d % LPR;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + 4 * (8 * (lb + LPR * j) + ch)),
+                                       (lds_void_t*)(dst + 64 * q), 16, 0, 0);
+    }
+  }
+  // the lane's slice (blocks lb + LPR j) and its block sums, from LDS
+  __device__ __forceinline__ static void slice(const float4* src, int lb, float (&xs)[BPL][32], float (&sx)[BPL]) {
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float4 q = src[(j * 8 + c) * LPR + lb];
+        xs[j][4 * c + 0] = q.x, xs[j][4 * c + 1] = q.y, xs[j][4 * c + 2] = q.z, xs[j][4 * c + 3] = q.w;
+        acc += (q.x + q.y) + (q.z + q.w);
+      }
+      sx[j] = acc;
+    }
+  }
+  // this wave's copies (and every other memory access it issued) are done,
+  // then every wave's: the buffer is complete
+  __device__ __forceinline__ static void wait() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+  }
+  // a copy this wave made alone is complete
+  __device__ __forceinline__ static void wait_wave() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); }
+};
+
 // ---------------------------------------------------------------------------
 // down GEMV of the hot picks: y_pick[p] = W_down h[p]. grid = (row chunks of
 // H, picks).
@@ -468,11 +516,17 @@ __global__ __launch_bounds__(256) void gemv_down_pick_kernel(GemvArgs a) {
   const int lb = lane % LPR, rg = lane / LPR;
   const uint8_t* base = a.addr[p];
   const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
+  // the pick's h row, once per work-group (with LPR < 64 every row group of
+  // a wave would load it again)
+  using V = SharedVec<LPR, BPL>;
+  __shared__ float4 hsh[V::KV];
+  V::issue(a.x + (int64_t)p * a.F, hsh, wave, 4, lane);
   RowTile<LPR, BPL, NIT> d;
   d.load(reinterpret_cast<const uint4*>(base + a.lay.down_nib),
          reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0, a.H, lb);
+  V::wait();
   float hs[BPL][32], sh[BPL];
-  load_slice<LPR, BPL>(a.x + (int64_t)p * a.F, lb, hs, sh);
+  V::slice(hsh, lb, hs, sh);
   down_store<LPR, BPL, NIT>(d, hs, sh, row0, lb, a.H, a.ypick + (int64_t)p * a.H);
 }
 
@@ -488,6 +542,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemv_down_combine_kernel(G
   constexpr int RPW = 64 / LPR;
   constexpr int ROWS = NIT * RPW;
   __shared__ float part[32][ROWS];
+  // each wave stages its pick's h row in LDS once (with LPR < 64 every row
+  // group would load it again), while the 8 copies fit in 64 KiB
+  using V = SharedVec<LPR, BPL>;
+  constexpr bool kStage = V::KV <= 512;
+  __shared__ float4 hsh[kStage ? kCombineWaves : 1][kStage ? V::KV : 1];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lb = lane % LPR, rg = lane / LPR;
@@ -499,8 +558,15 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemv_down_combine_kernel(G
     RowTile<LPR, BPL, NIT> d;
     d.load(reinterpret_cast<const uint4*>(base + a.lay.down_nib),
            reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0 + rg, a.H, lb, (a.kind[p] & kCold) != 0);
+    // after the weight loads: a cold pick's pacing waits must not wait for it
+    if (kStage) V::issue(a.x + p * a.F, hsh[wave], 0, 1, lane);
     float hs[BPL][32], sh[BPL];
-    load_slice<LPR, BPL>(a.x + p * a.F, lb, hs, sh);
+    if (kStage) {
+      V::wait_wave();
+      V::slice(hsh[wave], lb, hs, sh);
+    } else {
+      load_slice<LPR, BPL>(a.x + p * a.F, lb, hs, sh);
+    }
     {
       float pv[1][4], sv[1];
 #pragma unroll
@@ -596,50 +662,6 @@ __global__ __launch_bounds__(256) void group_picks_kernel(GroupArgs a) {
   for (int p = tid; p < a.P; p += 256) a.order[atomicAdd(&fill[a.ids[p]], 1)] = p;
 }
 
-// A K-vector (activation row or h row) staged in LDS for every wave of the
-// work-group: float4 chunk c of block lb + LPR j sits at [(8 j + c) LPR + lb],
-// so a wave's 16-byte reads of one chunk are consecutive. KV = K / 4 float4s,
-// a multiple of 64. The copy goes global -> LDS by the LDS-DMA form of the
-// global load (lane l writes 16 bytes at M0 + 16 l): instruction q fills LDS
-// chunks 64 q .. 64 q + 63, each lane fetching the source chunk that belongs
-// there; the waves take the instructions in turn.
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-template <int LPR, int BPL>
-struct SharedVec {
-  static constexpr int KV = 8 * LPR * BPL;
-  static_assert(KV % 64 == 0, "whole DMA instructions");
-  __device__ __forceinline__ static void issue(const float* src, float4* dst, int wave, int lane) {
-    for (int q = wave; q < KV / 64; q += 4) {
-      const int d = 64 * q + lane;
-      const int j = d / (8 * LPR), ch = (d / LPR) % 8, lb = d % LPR;
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(src + 4 * (8 * (lb + LPR * j) + ch)),
-                                       (lds_void_t*)(dst + 64 * q), 16, 0, 0);
-    }
-  }
-  // the lane's slice (blocks lb + LPR j) and its block sums, from LDS
-  __device__ __forceinline__ static void slice(const float4* src, int lb, float (&xs)[BPL][32], float (&sx)[BPL]) {
-#pragma unroll
-    for (int j = 0; j < BPL; ++j) {
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float4 q = src[(j * 8 + c) * LPR + lb];
-        xs[j][4 * c + 0] = q.x, xs[j][4 * c + 1] = q.y, xs[j][4 * c + 2] = q.z, xs[j][4 * c + 3] = q.w;
-        acc += (q.x + q.y) + (q.z + q.w);
-      }
-      sx[j] = acc;
-    }
-  }
-  // this wave's copies (and every other memory access it issued) are done,
-  // then every wave's: the buffer is complete
-  __device__ __forceinline__ static void wait() {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
-  }
-};
-
 // Picks whose rows fit the work-group's LDS budget (64 KiB) at once, 1..16.
 template <int LPR, int BPL>
 constexpr int chunk_picks() {
@@ -674,7 +696,7 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GemvArgs a, GroupAr
 #pragma unroll 1
   for (int c0 = 0; c0 < grp.z; c0 += NB) {
     const int nc = grp.z - c0 < NB ? grp.z - c0 : NB;
-    for (int b = 0; b < nc; ++b) V::issue(a.x + (int64_t)(gr.order[grp.y + c0 + b] / a.k) * a.H, xsh[b], wave, lane);
+    for (int b = 0; b < nc; ++b) V::issue(a.x + (int64_t)(gr.order[grp.y + c0 + b] / a.k) * a.H, xsh[b], wave, 4, lane);
     V::wait();  // the chunk's rows (and, the first time, the weights) are in
     // one pick at a time: the weights stay in registers (packed)
 #pragma unroll 1
@@ -719,7 +741,7 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GemvArgs a, GroupArgs
 #pragma unroll 1
   for (int c0 = 0; c0 < grp.z; c0 += NB) {
     const int nc = grp.z - c0 < NB ? grp.z - c0 : NB;
-    for (int b = 0; b < nc; ++b) V::issue(a.x + (int64_t)gr.order[grp.y + c0 + b] * a.F, hsh[b], wave, lane);
+    for (int b = 0; b < nc; ++b) V::issue(a.x + (int64_t)gr.order[grp.y + c0 + b] * a.F, hsh[b], wave, 4, lane);
     V::wait();
 #pragma unroll 1
     for (int b = 0; b < nc; ++b) {
