@@ -67,8 +67,12 @@ __device__ __forceinline__ float block_qdot(uint4 q, const float* __restrict__ x
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = w[i] & 0x0F0F0F0Fu;
-    const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+    // the masks go through v_bitop3 (truth table 0xC0: S0 & S1), whose
+    // result the compiler does not see through: with a plain AND it folds
+    // each mask into a 4-bit extract per element (extract, convert and FMA
+    // per weight) instead of converting the bytes in place (ubyte0..3)
+    const uint32_t lo = __builtin_amdgcn_bitop3_b32(w[i], 0x0F0F0F0Fu, 0u, 0xC0);
+    const uint32_t hi = __builtin_amdgcn_bitop3_b32(w[i] >> 4, 0x0F0F0F0Fu, 0u, 0xC0);
     a0 = fmaf((float)(lo & 0xffu), x[4 * i + 0], a0);
     a1 = fmaf((float)((lo >> 8) & 0xffu), x[4 * i + 1], a1);
     a0 = fmaf((float)((lo >> 16) & 0xffu), x[4 * i + 2], a0);
