@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 # HBM bytes per launch of the roofline kernel (gemv_route_gateup_kernel<64,1,4,1>, hot picks), from two rocprofv3
 # counter runs (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, scaled by a 1 GiB copy) over launches that served 7.14 hot picks
 # each (16.85 MB algorithmic); the summary and commands are under profiles/. Set to None when the kernel changes.
-ROOFLINE_TRAFFIC = {"bytes_per_launch": 17223717, "algorithmic_bytes_per_launch": 16852979}
+ROOFLINE_TRAFFIC = {"bytes_per_launch": 17189832, "algorithmic_bytes_per_launch": 16852979}
 PCIE_PEAK_GBPS = 64.0       # PCIe Gen5 x16, one direction
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA; fp16 (what the grouped GEMM runs) has the same rate
 METRIC = "MoE-layer decode tokens/s + effective weight GB/s vs HBM/PCIe roofline"
@@ -116,7 +116,31 @@ def fp16_gemm_ceiling(torch, n=8192, reps=20):
     return 2.0 * n ** 3 * reps / (time.perf_counter() - t0) / 1e12
 
 
-def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3, gemm_ceiling=None):
+def prefill_cpu_baseline(wl, weights, x_np, z_np, seconds):
+    """The oracle on the host cores over the first tokens of the same prompt, same layer (fp64)."""
+    import numpy as np
+
+    import oracle
+
+    oracle.lib()
+    g, u, d = weights
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    spent, tokens, chunk = 0.0, 0, 16
+    while spent < seconds and tokens < wl.tokens:
+        xs = x_np[tokens:tokens + chunk].astype(np.float64)
+        zs = np.ascontiguousarray(z_np[tokens:tokens + chunk])
+        ids, _ = oracle.route(zs, wl.top_k)
+        experts = {int(e): (g[e], u[e], d[e]) for e in np.unique(ids)}
+        t0 = time.perf_counter()
+        oracle.moe_layer(wl.n_experts, wl.top_k, wl.hidden, wl.ffn, experts, xs, logits=zs)
+        spent += time.perf_counter() - t0
+        tokens += xs.shape[0]
+    return dict(value=round(tokens / spent, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"first {tokens} of the {wl.tokens} prompt tokens through the layer (fp64 oracle, "
+                       f"{spent:.1f} s of oracle time)")
+
+
+def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3, gemm_ceiling=None, cpu_seconds=0.0):
     """A prompt pass of one layer: end-to-end time and the grouped GEMMs against the bf16 MFMA peak."""
     import numpy as np
 
@@ -125,10 +149,13 @@ def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3, gemm_ceiling=None):
     T, H, F, E, k = wl.tokens, wl.hidden, wl.ffn, wl.n_experts, wl.top_k
     ctx = moe.moe_create(1, E, k, H, F, pool_budget_bytes=wl.slots * wl.expert_bytes, max_batch_tokens=1,
                          max_prefill_tokens=T, host_alloc=host_alloc, host_sets=1, stream=stream)
-    moe.moe_register_layer(ctx, 0, *layer_weights(wl, 0))
+    weights = layer_weights(wl, 0)
+    moe.moe_register_layer(ctx, 0, *weights)
     moe.moe_seed(ctx, frequency_table(wl))
-    x = torch.from_numpy(activations(wl, 0, tokens=T)).cuda()
-    z = torch.from_numpy(np.ascontiguousarray(zipf_logits(wl, steps=1, tokens=T)[0, 0])).cuda()
+    x_np = activations(wl, 0, tokens=T)
+    z_np = np.ascontiguousarray(zipf_logits(wl, steps=1, tokens=T)[0, 0])
+    x = torch.from_numpy(x_np).cuda()
+    z = torch.from_numpy(z_np).cuda()
     y = torch.empty_like(x)
     with torch.cuda.stream(stream):
         moe.moe_prefill(ctx, 0, T, x, z, y)  # warm-up
@@ -161,6 +188,7 @@ def prefill_pass(moe, torch, wl, stream, host_alloc, reps=3, gemm_ceiling=None):
                      "mfma_flops_per_algorithmic_flop": 1,
                      "measured_fp16_gemm_ceiling": gemm_ceiling and round(gemm_ceiling, 1),
                      "frac_of_measured_ceiling": gemm_ceiling and round(tflops / gemm_ceiling, 4)},
+        "cpu_baseline": prefill_cpu_baseline(wl, weights, x_np, z_np, cpu_seconds) if cpu_seconds > 0 else None,
     }
 
 
@@ -415,7 +443,8 @@ def main():
         stream = torch.cuda.Stream()
         for name in PREFILL_WORKLOADS:
             print(json.dumps(prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc,
-                                          gemm_ceiling=fp16_gemm_ceiling(torch))), flush=True)
+                                          gemm_ceiling=fp16_gemm_ceiling(torch),
+                                          cpu_seconds=0.0 if args.no_cpu_baseline else 10.0)), flush=True)
         return
 
     wl = WORKLOADS[args.workload]
@@ -634,7 +663,8 @@ def main():
         result["large_model"] = large_pass(moe, torch, stream, host_alloc)
     if not args.no_side_passes:
         gemm_ceiling = fp16_gemm_ceiling(torch)
-        result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc, gemm_ceiling=gemm_ceiling)
+        result["prefill"] = [prefill_pass(moe, torch, WORKLOADS[name], stream, host_alloc, gemm_ceiling=gemm_ceiling,
+                                          cpu_seconds=0.0 if args.no_cpu_baseline else 10.0)
                              for name in PREFILL_WORKLOADS]
         if "ceilings" in result:
             result["ceilings"]["fp16_gemm_TFLOPs"] = round(gemm_ceiling, 1)
