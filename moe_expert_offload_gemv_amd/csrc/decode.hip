@@ -1,10 +1,11 @@
 // decode.hip - gfx950 GEMV kernels of the decode path of one MoE layer.
 //
 //   gemv_route_gateup_kernel
-//                         with logits given (E <= 512): every wave routes its
-//                         token itself (top-k, slot-table lookup) while its
-//                         activation loads are in flight, then runs the
-//                         gate/up GEMV below; one wave per pick applies the
+//                         with logits given (E <= 512): wave 0 of every
+//                         work-group routes the token (top-k, slot-table
+//                         lookup) while the work-group stages the activations
+//                         in LDS, then all waves run the gate/up GEMV
+//                         below; one wave per pick applies the
 //                         lookup's side effects (stamp, pick record, count)
 //                         and publishes the pick for the down GEMV. This
 //                         saves the routing launch and the dependent read of
