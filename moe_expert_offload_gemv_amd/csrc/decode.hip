@@ -612,9 +612,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemv_down_combine_kernel(G
 // depend on it).
 __global__ __launch_bounds__(256) void group_picks_kernel(GroupArgs a) {
   __shared__ int32_t cnt[4096], fill[4096];
-  __shared__ int32_t part[256], gpart[256];
+  __shared__ int32_t wsum[4], gwsum[4];
   __shared__ int4 lst[kMaxGroupsSorted];
-  __shared__ int32_t s_ng;
   const int tid = threadIdx.x;
   for (int e = tid; e < a.E; e += 256) cnt[e] = 0;
   __syncthreads();
@@ -624,21 +623,24 @@ __global__ __launch_bounds__(256) void group_picks_kernel(GroupArgs a) {
   const int per = (a.E + 255) / 256, e0 = tid * per, e1 = min(a.E, e0 + per);
   int s = 0, gs = 0;
   for (int e = e0; e < e1; ++e) s += cnt[e], gs += cnt[e] > 0;
-  part[tid] = s, gpart[tid] = gs;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0, gacc = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int v = part[i], gv = gpart[i];
-      part[i] = acc, gpart[i] = gacc;
-      acc += v, gacc += gv;
-    }
-    *a.n_groups = gacc;
-    s_ng = gacc;
+  // exclusive prefix sums of s and gs over the 256 threads: a shuffle scan
+  // in each wave, then the wave totals (a serial scan by one thread was
+  // 256 dependent LDS round trips, most of the kernel's time)
+  int incl = s, gincl = gs;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64), gv = __shfl_up(gincl, o, 64);
+    if ((tid & 63) >= o) incl += v, gincl += gv;
   }
+  if ((tid & 63) == 63) wsum[tid >> 6] = incl, gwsum[tid >> 6] = gincl;
   __syncthreads();
-  int pos = part[tid], gi = gpart[tid];
-  const int ng = s_ng;
+  int pos = incl - s, gi = gincl - gs, ng = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < (tid >> 6)) pos += wsum[w], gi += gwsum[w];
+    ng += gwsum[w];
+  }
+  if (tid == 0) *a.n_groups = ng;
   for (int e = e0; e < e1; ++e) {
     const int c = cnt[e];
     fill[e] = pos;
