@@ -201,6 +201,11 @@ int gemm_features_per_tile(int mode, int bm);
 // mode 0 gate/up, 1 down; bm = 64 or 128 rows per tile (the tiles were cut to it);
 // a.items holds n_items work items
 hipError_t launch_grouped_gemm(GemmArgs a, int mode, int bm, int n_items, const Launch& l);
+// staging block i of `staging` (blocks of `bytes`, a multiple of 16) <- expert
+// experts[i] of the layer whose pinned weights start at host_layer (the
+// device-visible address of the mapped allocation), i < n
+hipError_t launch_stage_experts(const uint8_t* host_layer, const int32_t* experts, int32_t n, int64_t bytes,
+                               uint8_t* staging, hipStream_t s);
 hipError_t launch_combine_pairs(const float* ypair, const int32_t* inv, const float* w, int32_t T, int32_t k,
                                 int32_t H, float* y, int32_t accumulate, hipStream_t s);
 

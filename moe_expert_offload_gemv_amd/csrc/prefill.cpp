@@ -50,6 +50,7 @@ struct Prefill {
   int4* tiles = nullptr;        // [max_tiles]
   int2* items[2] = {nullptr, nullptr};    // [max_items] work lists of the gate/up and down GEMMs
   const uint8_t** eaddr = nullptr;  // [E]
+  int32_t* stage = nullptr;     // [E] experts copied into the staging blocks, in block order
   _Float16* x16 = nullptr;      // [T][H] activations, fp16 in operand order
   _Float16* h16 = nullptr;      // [P][F] SwiGLU outputs, fp16 in operand order
   float* ypair = nullptr;       // [P][H]
@@ -60,6 +61,7 @@ struct Prefill {
   int4* h_tiles = nullptr;
   int2* h_items[2] = {nullptr, nullptr};
   const uint8_t** h_eaddr = nullptr;
+  int32_t* h_stage = nullptr;
 };
 
 #define PF_HIP(ctx, expr)                                                                                \
@@ -89,6 +91,7 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = dev((void**)&p->items[0], sizeof(int2) * p->max_items, "prefill gate/up work list")) ||
       (rc = dev((void**)&p->items[1], sizeof(int2) * p->max_items, "prefill down work list")) ||
       (rc = dev((void**)&p->eaddr, sizeof(uint8_t*) * E, "prefill addresses")) ||
+      (rc = dev((void**)&p->stage, sizeof(int32_t) * E, "prefill staging list")) ||
       (rc = dev((void**)&p->x16, sizeof(_Float16) * T * c->H, "prefill x fp16")) ||
       (rc = dev((void**)&p->h16, sizeof(_Float16) * P * c->F, "prefill h fp16")) ||
       (rc = dev((void**)&p->ypair, sizeof(float) * P * c->H, "prefill pair outputs")) ||
@@ -100,7 +103,8 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_tiles, sizeof(int4) * p->max_tiles, pin, "prefill tile staging")) ||
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_items[0], sizeof(int2) * p->max_items, pin, "prefill item staging")) ||
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_items[1], sizeof(int2) * p->max_items, pin, "prefill item staging")) ||
-      (rc = moe_ctx_host_alloc(c, (void**)&p->h_eaddr, sizeof(uint8_t*) * E, pin, "prefill address staging")))
+      (rc = moe_ctx_host_alloc(c, (void**)&p->h_eaddr, sizeof(uint8_t*) * E, pin, "prefill address staging")) ||
+      (rc = moe_ctx_host_alloc(c, (void**)&p->h_stage, sizeof(int32_t) * E, pin, "prefill staging list")))
     return rc;
   return MOE_OK;
 }
@@ -170,10 +174,8 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
       if (slot >= 0) {
         p->h_eaddr[e] = c->pool + (c->group_of(layer) * S + slot) * c->B;
       } else if (staged < c->n_staging) {
-        uint8_t* blk = c->staging + staged * c->B;
-        PF_HIP(c, hipMemcpyAsync(blk, c->host_layers[layer] + (int64_t)e * c->B, c->B, hipMemcpyHostToDevice, s));
-        p->h_eaddr[e] = blk;
-        ++staged;
+        p->h_eaddr[e] = c->staging + staged * c->B;
+        p->h_stage[staged++] = e;
       } else {
         p->h_eaddr[e] = c->host_layers_dev[layer] + (int64_t)e * c->B;  // no block left: read zero-copy
       }
@@ -184,6 +186,10 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   p->h_offsets[E] = (int32_t)pos;
   c->last_prefill_staged = staged;
   if (pos != P) return moe_ctx_fail(c, MOE_E_HIP, "prefill: pair count mismatch (%lld != %d)", (long long)pos, P);
+  if (staged > 0) {
+    PF_HIP(c, hipMemcpyAsync(p->stage, p->h_stage, sizeof(int32_t) * staged, hipMemcpyHostToDevice, s));
+    PF_HIP(c, moe::launch_stage_experts(c->host_layers_dev[layer], p->stage, (int32_t)staged, c->B, c->staging, s));
+  }
   PF_HIP(c, hipMemcpyAsync(p->offsets, p->h_offsets, sizeof(int32_t) * (E + 1), hipMemcpyHostToDevice, s));
   PF_HIP(c, hipMemcpyAsync(p->tiles, p->h_tiles, sizeof(int4) * n_tiles, hipMemcpyHostToDevice, s));
   // work lists: per expert, feature tiles outer and row tiles inner
