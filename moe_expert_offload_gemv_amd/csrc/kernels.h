@@ -192,11 +192,12 @@ hipError_t launch_expert_histogram(const int32_t* ids, int32_t n_pairs, int32_t 
 hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E, const int32_t* offsets,
                                  int32_t* perm, int32_t* inv, hipStream_t s);
 hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, hipStream_t s);
-// Scale planes of every expert with eaddr[e] != nullptr, transposed into
-// out + e * per_expert (layout of GemmArgs::sclT); per_expert = sclT_elements(lay).
+// Scale planes of the experts e = experts[0..n) with eaddr[e] != nullptr,
+// transposed into out + e * per_expert (layout of GemmArgs::sclT);
+// per_expert = sclT_elements(lay).
 int64_t sclT_elements(const ExpertLayout& lay);
-hipError_t launch_transpose_scales(const uint8_t* const* eaddr, int32_t E, const ExpertLayout& lay, uint16_t* out,
-                                   const Launch& l);
+hipError_t launch_transpose_scales(const uint8_t* const* eaddr, const int32_t* experts, int32_t n,
+                                   const ExpertLayout& lay, uint16_t* out, const Launch& l);
 int gemm_features_per_tile(int mode, int bm);
 // mode 0 gate/up, 1 down; bm = 64 or 128 rows per tile (the tiles were cut to it);
 // a.items holds n_items work items

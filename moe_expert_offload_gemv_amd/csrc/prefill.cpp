@@ -17,6 +17,23 @@
 
 namespace {
 constexpr int kMinTileRows = 64;  // tiles hold 64 or 128 pairs of one expert
+// The staging copy runs on a stream of its own; the GEMMs of the experts
+// that need no copy run meanwhile, those of the staged ones once their copy
+// has landed. Two ways to copy, picked per pass from rough time estimates:
+// * the copy would outlast the GEMMs of the experts already in HBM: one
+//   gather kernel per chunk (up to kStageChunks of at least kMinChunkExperts
+//   experts) reading the pinned weights zero-copy, at the PCIe ceiling; each
+//   chunk's GEMMs run while the next chunk is in flight;
+// * else DMA copies, one per run of consecutive experts, which take no
+//   compute units: the gather kernel's PCIe reads hold up the memory
+//   pipelines of the CUs they share with a GEMM, so beside a long GEMM the
+//   DMA engines are the better choice even at their lower rate.
+constexpr int kStageChunks = 8;
+constexpr int kMinChunkExperts = 16;
+constexpr double kPcieBytesPerS = 55e9;      // staging rate, either way (measured 49-57.5 GB/s)
+constexpr double kGemmFlopsPerS = 600e12;    // grouped GEMMs on long tiles (measured 600-860 TFLOP/s)
+constexpr int kMaxGroups = 1 + kStageChunks;  // group 0: experts read where they are
+constexpr int kTimed = 3;                     // per group: scale transposition, gate/up, down
 
 // Rows per tile for a pass: 128-row tiles halve the weight conversions per
 // MFMA but pad small experts further. A 64-row tile step is taken to cost
@@ -61,7 +78,13 @@ struct Prefill {
   int4* h_tiles = nullptr;
   int2* h_items[2] = {nullptr, nullptr};
   const uint8_t** h_eaddr = nullptr;
-  int32_t* h_stage = nullptr;
+  int32_t* h_stage = nullptr;   // [E] staged experts in block order, then the experts of group 0
+  std::vector<int64_t> tile_begin;  // [E + 1] first tile of each expert
+  std::vector<int32_t> direct;      // used experts read where they are
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t lists_ready = nullptr;              // the staging list is on the device
+  hipEvent_t chunk_done[kStageChunks] = {};      // chunk c of the staging copy has landed
+  hipEvent_t timing[2 * kTimed * kMaxGroups] = {};  // start/stop of each timed launch
 };
 
 #define PF_HIP(ctx, expr)                                                                                \
@@ -106,6 +129,18 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_eaddr, sizeof(uint8_t*) * E, pin, "prefill address staging")) ||
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_stage, sizeof(int32_t) * E, pin, "prefill staging list")))
     return rc;
+  p->tile_begin.assign(E + 1, 0);
+  p->direct.reserve(E);
+  // default priority, like every stream here
+  if (hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&p->lists_ready, hipEventDisableTiming) != hipSuccess)
+    return moe_ctx_fail(c, MOE_E_HIP, "prefill: stream or event creation failed");
+  for (hipEvent_t& ev : p->chunk_done)
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
+      return moe_ctx_fail(c, MOE_E_HIP, "prefill: event creation failed");
+  for (hipEvent_t& ev : p->timing)
+    if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess)
+      return moe_ctx_fail(c, MOE_E_HIP, "prefill: event creation failed");
   return MOE_OK;
 }
 
@@ -120,7 +155,18 @@ int moe_prefill_alloc_staging(moe_ctx* c) {
 }
 
 void moe_prefill_release(moe_ctx* c) {
-  delete c->pf;
+  Prefill* p = c->pf;
+  if (!p) return;
+  if (p->copy_stream) {
+    (void)hipStreamSynchronize(p->copy_stream);
+    (void)hipStreamDestroy(p->copy_stream);
+  }
+  if (p->lists_ready) (void)hipEventDestroy(p->lists_ready);
+  for (hipEvent_t ev : p->chunk_done)
+    if (ev) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : p->timing)
+    if (ev) (void)hipEventDestroy(ev);
+  delete p;
   c->pf = nullptr;
 }
 
@@ -139,6 +185,8 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   if (!logits && !c->routers[layer]) return moe_ctx_fail(c, MOE_E_INVAL, "prefill: no logits and no router");
   if (!c->seeded) return moe_ctx_fail(c, MOE_E_STATE, "prefill before moe_seed");
   if (capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "prefill while capturing");
+  // a pass that failed part-way may have left staging copies running
+  PF_HIP(c, hipStreamSynchronize(p->copy_stream));
   hipStream_t s = c->stream;
   const int32_t E = c->E, k = c->k, H = c->H, F = c->F, T = n_tokens;
   const int32_t P = T * k;
@@ -165,103 +213,165 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   int64_t n_tiles = 0, staged = 0, pos = 0;
   const int64_t S = c->S;
   const int bm = tile_rows(p->h_counts, E);
+  std::vector<int64_t>& tb = p->tile_begin;
+  std::vector<int32_t>& direct = p->direct;
+  direct.clear();
   for (int32_t e = 0; e < E; ++e) {
     const int32_t m = p->h_counts[e];
     p->h_offsets[e] = (int32_t)pos;
     p->h_eaddr[e] = nullptr;
+    tb[e] = n_tiles;
     if (m > 0) {
       const int32_t slot = c->tbl[(int64_t)layer * E + e];
       if (slot >= 0) {
         p->h_eaddr[e] = c->pool + (c->group_of(layer) * S + slot) * c->B;
+        direct.push_back(e);
       } else if (staged < c->n_staging) {
         p->h_eaddr[e] = c->staging + staged * c->B;
         p->h_stage[staged++] = e;
       } else {
         p->h_eaddr[e] = c->host_layers_dev[layer] + (int64_t)e * c->B;  // no block left: read zero-copy
+        direct.push_back(e);
       }
       for (int32_t m0 = 0; m0 < m; m0 += bm) p->h_tiles[n_tiles++] = int4{e, (int32_t)(pos + m0), std::min(bm, m - m0), 0};
     }
     pos += m;
   }
+  tb[E] = n_tiles;
   p->h_offsets[E] = (int32_t)pos;
   c->last_prefill_staged = staged;
   if (pos != P) return moe_ctx_fail(c, MOE_E_HIP, "prefill: pair count mismatch (%lld != %d)", (long long)pos, P);
-  if (staged > 0) {
-    PF_HIP(c, hipMemcpyAsync(p->stage, p->h_stage, sizeof(int32_t) * staged, hipMemcpyHostToDevice, s));
-    PF_HIP(c, moe::launch_stage_experts(c->host_layers_dev[layer], p->stage, (int32_t)staged, c->B, c->staging, s));
+
+  // Groups of experts: 0 = those read where they are (resident, or zero-copy
+  // when no staging block is left), 1.. = the chunks of the staging copy in
+  // block order. h_stage holds the staged experts, then group 0's.
+  const int64_t n_direct = (int64_t)direct.size();
+  int64_t direct_pairs = 0;
+  for (int32_t e : direct) direct_pairs += p->h_counts[e];
+  const double copy_s = (double)staged * c->B / kPcieBytesPerS;
+  const double gemm_s = 6.0 * H * F * (double)direct_pairs / kGemmFlopsPerS;
+  const bool dma = copy_s < gemm_s;
+  const int n_chunks = staged == 0 ? 0
+                       : dma      ? 1
+                                  : (int)std::min<int64_t>(kStageChunks, std::max<int64_t>(1, staged / kMinChunkExperts));
+  const int64_t chunk = n_chunks ? (staged + n_chunks - 1) / n_chunks : 0;
+  const int G = 1 + n_chunks;
+  std::copy(direct.begin(), direct.end(), p->h_stage + staged);
+  int64_t g_first[kMaxGroups], g_count[kMaxGroups];
+  g_first[0] = staged, g_count[0] = n_direct;
+  for (int g = 1; g < G; ++g) {
+    g_first[g] = (g - 1) * chunk;
+    g_count[g] = std::max<int64_t>(0, std::min<int64_t>(chunk, staged - g_first[g]));
   }
-  PF_HIP(c, hipMemcpyAsync(p->offsets, p->h_offsets, sizeof(int32_t) * (E + 1), hipMemcpyHostToDevice, s));
-  PF_HIP(c, hipMemcpyAsync(p->tiles, p->h_tiles, sizeof(int4) * n_tiles, hipMemcpyHostToDevice, s));
-  // work lists: per expert, feature tiles outer and row tiles inner
-  int n_items[2] = {0, 0};
+  // work lists, group by group: per expert, feature tiles outer and row tiles inner
+  int64_t item_first[2][kMaxGroups + 1];
   for (int mode = 0; mode < 2; ++mode) {
     const int N = mode == 0 ? F : H, bnw = moe::gemm_features_per_tile(mode, bm);
     if (n_tiles * ((N + bnw - 1) / bnw) > p->max_items)
       return moe_ctx_fail(c, MOE_E_HIP, "prefill: work list larger than its buffer");
     int2* it = p->h_items[mode];
-    for (int64_t t0 = 0; t0 < n_tiles;) {
-      int64_t t1 = t0;
-      while (t1 < n_tiles && p->h_tiles[t1].x == p->h_tiles[t0].x) ++t1;
-      for (int n0 = 0; n0 < N; n0 += bnw)
-        for (int64_t t = t0; t < t1; ++t) it[n_items[mode]++] = int2{(int32_t)t, n0};
-      t0 = t1;
+    int64_t n = 0;
+    for (int g = 0; g < G; ++g) {
+      item_first[mode][g] = n;
+      for (int64_t i = 0; i < g_count[g]; ++i) {
+        const int32_t e = p->h_stage[g_first[g] + i];
+        for (int n0 = 0; n0 < N; n0 += bnw)
+          for (int64_t t = tb[e]; t < tb[e + 1]; ++t) it[n++] = int2{(int32_t)t, n0};
+      }
     }
-    PF_HIP(c, hipMemcpyAsync(p->items[mode], it, sizeof(int2) * n_items[mode], hipMemcpyHostToDevice, s));
+    item_first[mode][G] = n;
+    PF_HIP(c, hipMemcpyAsync(p->items[mode], it, sizeof(int2) * n, hipMemcpyHostToDevice, s));
   }
+  PF_HIP(c, hipMemcpyAsync(p->stage, p->h_stage, sizeof(int32_t) * (staged + n_direct), hipMemcpyHostToDevice, s));
+  PF_HIP(c, hipMemcpyAsync(p->offsets, p->h_offsets, sizeof(int32_t) * (E + 1), hipMemcpyHostToDevice, s));
+  PF_HIP(c, hipMemcpyAsync(p->tiles, p->h_tiles, sizeof(int4) * n_tiles, hipMemcpyHostToDevice, s));
   PF_HIP(c, hipMemcpyAsync(p->eaddr, p->h_eaddr, sizeof(uint8_t*) * E, hipMemcpyHostToDevice, s));
 
-  // 4. short tiles (few rows per expert) are bound by weight fetches: give
-  // their GEMMs the block scales of the used experts transposed, so each
-  // K step reads whole lines of them
-  const bool tscl = bm == 64;
-  hipEvent_t* ev = nullptr;
-  if (c->profiling && c->prefill_events.size() >= 6) ev = c->prefill_events.data();
-  if (tscl) {
-    moe::Launch lt;
-    lt.stream = s;
-    if (ev) lt.start = ev[4], lt.stop = ev[5];
-    PF_HIP(c, moe::launch_transpose_scales(p->eaddr, E, c->lay, p->sclT, lt));
+  // 4. the staging copy, chunk by chunk on its own stream, after everything
+  // already queued on the pass's stream (earlier readers of the blocks)
+  if (n_chunks > 0) {
+    PF_HIP(c, hipEventRecord(p->lists_ready, s));
+    PF_HIP(c, hipStreamWaitEvent(p->copy_stream, p->lists_ready, 0));
+    for (int g = 1; g < G; ++g) {
+      if (dma) {
+        for (int64_t i = g_first[g], end = g_first[g] + g_count[g]; i < end;) {
+          int64_t j = i + 1;
+          while (j < end && p->h_stage[j] == p->h_stage[j - 1] + 1) ++j;
+          PF_HIP(c, hipMemcpyAsync(c->staging + i * c->B, c->host_layers[layer] + (int64_t)p->h_stage[i] * c->B,
+                                   (j - i) * c->B, hipMemcpyHostToDevice, p->copy_stream));
+          i = j;
+        }
+      } else {
+        PF_HIP(c, moe::launch_stage_experts(c->host_layers_dev[layer], p->stage + g_first[g], (int32_t)g_count[g],
+                                            c->B, c->staging + g_first[g] * c->B, p->copy_stream));
+      }
+      PF_HIP(c, hipEventRecord(p->chunk_done[g - 1], p->copy_stream));
+    }
   }
 
-  // stable sort of the pairs by expert
+  // 5. stable sort of the pairs by expert; activations as fp16 rows in operand order
   PF_HIP(c, moe::launch_expert_scatter(p->ids, P, E, p->offsets, p->perm, p->inv, s));
-
-  // 5. activations as fp16 rows in operand order
   PF_HIP(c, moe::launch_convert_rows(x, T, H, p->x16, s));
 
-  // 6. grouped GEMMs over the used tiles
+  // 6. per group (a chunk once its copy has landed): short tiles (few rows
+  // per expert) are bound by weight fetches, so their GEMMs get the block
+  // scales of the group's experts transposed, each K step reading whole
+  // lines of them; then the grouped gate/up and down GEMMs
+  const bool tscl = bm == 64;
+  const bool timed = c->profiling;
+  bool launched[kMaxGroups][kTimed] = {};
   moe::GemmArgs g{};
   g.a16 = p->x16, g.arow = p->perm, g.arow_div = k;
-  g.tiles = p->tiles, g.eaddr = p->eaddr, g.items = p->items[0];
+  g.tiles = p->tiles, g.eaddr = p->eaddr;
   g.K = H, g.N = F;
   g.lay = c->lay;
   g.h16 = p->h16;
   g.sclT = tscl ? p->sclT : nullptr;
   g.sclT_per_expert = moe::sclT_elements(c->lay);
-  moe::Launch l1 = ls, l2 = ls;
-  if (ev) l1.start = ev[0], l1.stop = ev[1], l2.start = ev[2], l2.stop = ev[3];
-  PF_HIP(c, moe::launch_grouped_gemm(g, 0, bm, n_items[0], l1));
   moe::GemmArgs d = g;
   d.a16 = p->h16, d.arow = nullptr, d.arow_div = 1;
   d.K = F, d.N = H;
-  d.items = p->items[1];
   d.y = p->ypair;
-  PF_HIP(c, moe::launch_grouped_gemm(d, 1, bm, n_items[1], l2));
+  for (int gi = 0; gi < G; ++gi) {
+    if (gi > 0) PF_HIP(c, hipStreamWaitEvent(s, p->chunk_done[gi - 1], 0));
+    if (g_count[gi] == 0) continue;
+    auto timer = [&](int kind) {
+      moe::Launch l = ls;
+      if (timed) {
+        l.start = p->timing[2 * (gi * kTimed + kind)], l.stop = p->timing[2 * (gi * kTimed + kind) + 1];
+        launched[gi][kind] = true;
+      }
+      return l;
+    };
+    if (tscl)
+      PF_HIP(c, moe::launch_transpose_scales(p->eaddr, p->stage + g_first[gi], (int32_t)g_count[gi], c->lay, p->sclT,
+                                             timer(0)));
+    const int64_t gu0 = item_first[0][gi], gu1 = item_first[0][gi + 1];
+    const int64_t dn0 = item_first[1][gi], dn1 = item_first[1][gi + 1];
+    g.items = p->items[0] + gu0;
+    d.items = p->items[1] + dn0;
+    PF_HIP(c, moe::launch_grouped_gemm(g, 0, bm, (int)(gu1 - gu0), timer(1)));
+    PF_HIP(c, moe::launch_grouped_gemm(d, 1, bm, (int)(dn1 - dn0), timer(2)));
+  }
 
   // 7. weighted combine in pick order
   PF_HIP(c, moe::launch_combine_pairs(p->ypair, p->inv, p->w, T, k, H, y, (flags & MOE_ACCUMULATE) ? 1 : 0, s));
-  PF_HIP(c, hipStreamSynchronize(s));  // the pass is over: the staging blocks are free again
+  PF_HIP(c, hipStreamSynchronize(s));  // the pass is over (it waited for every chunk): the staging blocks are free again
   p->last_layer = layer;
 
-  if (ev) {
-    float t1 = 0, t2 = 0, t0 = 0;
-    PF_HIP(c, hipEventElapsedTime(&t1, ev[0], ev[1]));
-    PF_HIP(c, hipEventElapsedTime(&t2, ev[2], ev[3]));
-    if (tscl) PF_HIP(c, hipEventElapsedTime(&t0, ev[4], ev[5]));
-    c->prof.prefill_prep_ms += t0;
+  if (timed) {
+    float ms[kTimed] = {};
+    for (int gi = 0; gi < G; ++gi)
+      for (int kind = 0; kind < kTimed; ++kind) {
+        if (!launched[gi][kind]) continue;
+        float t = 0;
+        PF_HIP(c, hipEventElapsedTime(&t, p->timing[2 * (gi * kTimed + kind)], p->timing[2 * (gi * kTimed + kind) + 1]));
+        ms[kind] += t;
+      }
+    c->prof.prefill_prep_ms += ms[0];
     c->prof.prefill_passes += 1;
-    c->prof.prefill_gateup_ms += t1;
-    c->prof.prefill_down_ms += t2;
+    c->prof.prefill_gateup_ms += ms[1];
+    c->prof.prefill_down_ms += ms[2];
     c->prof.prefill_pairs += P;
     c->prof.prefill_tiles += n_tiles;
     c->prof.prefill_staged += staged;
@@ -287,6 +397,7 @@ extern "C" int moe_preheat(moe_ctx* c, int32_t layer, int32_t max_experts, int32
   if (layer != p->last_layer)
     return moe_ctx_fail(c, MOE_E_STATE, "preheat: the last prompt pass was of layer %d, not %d", p->last_layer, layer);
   if (capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "preheat while capturing");
+  PF_HIP(c, hipStreamSynchronize(p->copy_stream));  // the staging blocks are read below
   hipStream_t s = c->stream;
   const int64_t E = c->E, S = c->S, GS = (int64_t)c->groups * S, B = c->B;
   const int64_t g0 = c->group_of(layer) * S;

@@ -382,10 +382,11 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 // whole (one contiguous run), then writes 128-byte row pieces of the
 // transposed plane, 128 blocks of K at a time. grid = (row chunks of the
 // largest matrix, 3 matrices, E).
-__global__ __launch_bounds__(256) void transpose_scales_kernel(const uint8_t* const* eaddr, ExpertLayout lay,
-                                                               uint16_t* out, int64_t per) {
+__global__ __launch_bounds__(256) void transpose_scales_kernel(const uint8_t* const* eaddr, const int32_t* experts,
+                                                               ExpertLayout lay, uint16_t* out, int64_t per) {
   __shared__ uint16_t tile[64][129];  // odd row stride (in 16-bit words): the column reads spread over banks
-  const uint8_t* base = eaddr[blockIdx.z];
+  const int e = experts[blockIdx.z];
+  const uint8_t* base = eaddr[e];
   if (!base) return;
   const int m = blockIdx.y;  // 0 gate, 1 up, 2 down
   const int R = m < 2 ? lay.F : lay.H, KB = (m < 2 ? lay.H : lay.F) / 32;
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(256) void transpose_scales_kernel(const uint8_t* co
   const uint16_t* src = reinterpret_cast<const uint16_t*>(base + (m == 0 ? lay.gate_scl : m == 1 ? lay.up_scl
                                                                                             : lay.down_scl)) +
                         (int64_t)r0 * KB;
-  uint16_t* dst = out + (int64_t)blockIdx.z * per + (int64_t)m * lay.F * (lay.H / 32) + r0;
+  uint16_t* dst = out + (int64_t)e * per + (int64_t)m * lay.F * (lay.H / 32) + r0;
   for (int k0 = 0; k0 < KB; k0 += 128) {
     const int nk = KB - k0 < 128 ? KB - k0 : 128;
     for (int i = threadIdx.x; i < nr * nk; i += 256) {
@@ -474,11 +475,11 @@ hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float
 int64_t sclT_elements(const ExpertLayout& lay) {
   return 2 * (int64_t)lay.F * (lay.H / 32) + (int64_t)lay.H * (lay.F / 32);
 }
-hipError_t launch_transpose_scales(const uint8_t* const* eaddr, int32_t E, const ExpertLayout& lay, uint16_t* out,
-                                   const Launch& l) {
-  if (E <= 0 || lay.H % 32 || lay.F % 32) return hipErrorInvalidValue;
+hipError_t launch_transpose_scales(const uint8_t* const* eaddr, const int32_t* experts, int32_t n,
+                                   const ExpertLayout& lay, uint16_t* out, const Launch& l) {
+  if (n <= 0 || !experts || lay.H % 32 || lay.F % 32) return hipErrorInvalidValue;
   const int rmax = lay.F > lay.H ? lay.F : lay.H;
-  return launch(transpose_scales_kernel, dim3((rmax + 63) / 64, 3, E), dim3(256), l, eaddr, lay, out,
+  return launch(transpose_scales_kernel, dim3((rmax + 63) / 64, 3, n), dim3(256), l, eaddr, experts, lay, out,
                 sclT_elements(lay));
 }
 int gemm_features_per_tile(int mode, int bm) {

@@ -124,18 +124,17 @@ static void ctx_release(moe_ctx* c) {
   // host threads before their mailbox goes away
   if (c->hx) moe_host::executor_destroy(c->hx);
   c->hx = nullptr;
+  moe_prefill_release(c);  // drains the staging stream before its blocks are freed
   for (void* p : c->dev_allocs) (void)hipFree(p);
   for (void* p : c->host_allocs) (void)hipHostFree(p);
   for (void* r : c->routers)
     if (r) (void)hipFree(r);
   for (hipEvent_t e : c->events) (void)hipEventDestroy(e);
-  for (hipEvent_t e : c->prefill_events) (void)hipEventDestroy(e);
   if (c->swap_stream) {
     (void)hipStreamSynchronize(c->swap_stream);
     (void)hipStreamDestroy(c->swap_stream);
   }
   for (hipEvent_t e : c->swap_events) (void)hipEventDestroy(e);
-  moe_prefill_release(c);
   delete c;
 }
 
@@ -341,11 +340,6 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->timed_fused.assign(n_timed, 0);
   c->timed_cpu.assign(n_timed, 0);
   c->timed_grouped.assign(n_timed, 0);
-  for (int i = 0; i < 6 && k.max_prefill_tokens > 0; ++i) {
-    hipEvent_t ev;
-    if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return fail(MOE_E_HIP);
-    c->prefill_events.push_back(ev);
-  }
   if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_E_HIP);
   c->clock = 1;
   *out = c;

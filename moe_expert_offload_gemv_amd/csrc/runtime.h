@@ -67,7 +67,6 @@ struct moe_ctx {
   uint8_t* staging = nullptr;
   struct Prefill* pf = nullptr;
   int64_t last_prefill_staged = 0;
-  std::vector<hipEvent_t> prefill_events;  // timing of the two grouped GEMMs
 
   // host mirror of the cache state
   std::vector<int32_t> tbl, owner;   // tbl [L][E] slot; owner [groups][S] layer * E + expert or -1

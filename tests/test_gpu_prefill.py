@@ -63,6 +63,14 @@ def test_prefill_many_tiles_per_expert():
     assert prof["prefill_tiles"] > 8
 
 
+def test_prefill_dma_staging_beside_long_gemms():
+    # one staged expert against ~7000 pairs of resident ones: the copy hides
+    # behind the GEMMs, so it goes to the DMA engines instead of the gather kernel
+    wl = Workload("prefill-e8k2-h256f512-t4000", 208, 1, 8, 2, 256, 512, tokens=4000, zipf_s=1.1)
+    err, prof = _prefill_check(wl, slots=7, sample=160)
+    assert prof["prefill_staged"] == 1
+
+
 def test_prefill_decode_shape():
     wl = Workload("prefill-e64k8-h2048f1024-t300", 203, 1, 64, 8, 2048, 1024, tokens=300, zipf_s=1.1)
     _prefill_check(wl, slots=26, sample=48)
