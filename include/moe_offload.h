@@ -278,8 +278,10 @@ MOE_API int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
  * ([MAC]: only (expert, tile) pairs that hold tokens are computed). Experts
  * the pass touches that are not resident are copied into borrowed HBM staging
  * blocks for the pass and the blocks are returned at its end ([FORK]). The
- * cache policy is untouched: no stamps, no miss log, no counts, no clock.
- * Synchronises the stream; not capturable (MOE_E_CAPTURING). */
+ * copy runs on a stream the library owns, beside the GEMMs of the resident
+ * experts; the pass waits for it before it returns. The cache policy is
+ * untouched: no stamps, no miss log, no counts, no clock. Synchronises the
+ * stream; not capturable (MOE_E_CAPTURING). */
 MOE_API int moe_prefill(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
                 const float* x, const float* logits, float* y, uint32_t flags);
 
