@@ -188,9 +188,17 @@ struct GemmArgs {
                                 //   [F/32][H]; 128-row tiles: nullptr (scales from the expert's planes)
   int32_t work, work_padded;    // set by the launcher: work items, padded to a multiple of 8
 };
-hipError_t launch_expert_histogram(const int32_t* ids, int32_t n_pairs, int32_t E, int32_t* counts, hipStream_t s);
+// Stable counting sort of pairs by expert (E <= 4096). launch_expert_counts
+// fills rank [n_pairs], ccount [E][sort_chunks(n_pairs)] (chunk starts within
+// each expert) and counts [E]; launch_expert_scatter, given the offsets (the
+// exclusive prefix of counts), writes perm [n_pairs] (sorted position ->
+// pair) and inv (pair -> sorted position).
+int32_t sort_chunks(int32_t n_pairs);
+hipError_t launch_expert_counts(const int32_t* ids, int32_t n_pairs, int32_t E, int32_t* rank, int32_t* ccount,
+                                int32_t* counts, hipStream_t s);
 hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E, const int32_t* offsets,
-                                 int32_t* perm, int32_t* inv, hipStream_t s);
+                                 const int32_t* ccount, const int32_t* rank, int32_t* perm, int32_t* inv,
+                                 hipStream_t s);
 hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, hipStream_t s);
 // Scale planes of the experts e = experts[0..n) with eaddr[e] != nullptr,
 // transposed into out + e * per_expert (layout of GemmArgs::sclT);

@@ -63,6 +63,8 @@ struct Prefill {
   int32_t* perm = nullptr;      // [P] sorted position -> pair
   int32_t* inv = nullptr;       // [P] pair -> sorted position
   int32_t* counts = nullptr;    // [E]
+  int32_t* rank = nullptr;      // [P] rank of a pair among its chunk's pairs of the same expert
+  int32_t* ccount = nullptr;    // [E][P / 256 chunks] counts, then starts, per chunk
   int32_t* offsets = nullptr;   // [E + 1]
   int4* tiles = nullptr;        // [max_tiles]
   int2* items[2] = {nullptr, nullptr};    // [max_items] work lists of the gate/up and down GEMMs
@@ -109,6 +111,8 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = dev((void**)&p->perm, sizeof(int32_t) * P, "prefill perm")) ||
       (rc = dev((void**)&p->inv, sizeof(int32_t) * P, "prefill inverse perm")) ||
       (rc = dev((void**)&p->counts, sizeof(int32_t) * E, "prefill counts")) ||
+      (rc = dev((void**)&p->rank, sizeof(int32_t) * P, "prefill ranks")) ||
+      (rc = dev((void**)&p->ccount, sizeof(int32_t) * E * moe::sort_chunks((int32_t)P), "prefill chunk counts")) ||
       (rc = dev((void**)&p->offsets, sizeof(int32_t) * (E + 1), "prefill offsets")) ||
       (rc = dev((void**)&p->tiles, sizeof(int4) * p->max_tiles, "prefill tiles")) ||
       (rc = dev((void**)&p->items[0], sizeof(int2) * p->max_items, "prefill gate/up work list")) ||
@@ -204,8 +208,7 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   PF_HIP(c, moe::launch_route(ra, ls));
 
   // 2. pairs per expert, to the host
-  PF_HIP(c, hipMemsetAsync(p->counts, 0, sizeof(int32_t) * E, s));
-  PF_HIP(c, moe::launch_expert_histogram(p->ids, P, E, p->counts, s));
+  PF_HIP(c, moe::launch_expert_counts(p->ids, P, E, p->rank, p->ccount, p->counts, s));
   PF_HIP(c, hipMemcpyAsync(p->h_counts, p->counts, sizeof(int32_t) * E, hipMemcpyDeviceToHost, s));
   PF_HIP(c, hipStreamSynchronize(s));
 
@@ -310,7 +313,7 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   }
 
   // 5. stable sort of the pairs by expert; activations as fp16 rows in operand order
-  PF_HIP(c, moe::launch_expert_scatter(p->ids, P, E, p->offsets, p->perm, p->inv, s));
+  PF_HIP(c, moe::launch_expert_scatter(p->ids, P, E, p->offsets, p->ccount, p->rank, p->perm, p->inv, s));
   PF_HIP(c, moe::launch_convert_rows(x, T, H, p->x16, s));
 
   // 6. per group (a chunk once its copy has landed): short tiles (few rows

@@ -4,7 +4,11 @@
 // on a 64 GB Mac" README ("Metal kernels": MUL_MAT_ID over used tiles only)
 // launches only (expert, tile) pairs that hold tokens.
 //
-//   expert_histogram_kernel  pair counts per expert
+//   chunk_rank_kernel        per chunk of 256 pairs: each pair's rank among the
+//                            chunk's earlier pairs of its expert, and the chunk's
+//                            count per expert
+//   chunk_scan_kernel        per expert: where each chunk's pairs start among the
+//                            expert's pairs, and the expert's pair count
 //   expert_scatter_kernel    stable counting sort: perm[pos] = pair, inv[pair] = pos
 //   convert_rows_kernel      fp32 rows -> fp16 rows in operand order
 //   grouped_gemm_kernel      per tile of one expert: gate/up -> h = silu(g) * u
@@ -120,6 +124,7 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >
 __device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 constexpr int kStages = 3;  // LDS ring: loads run two K steps ahead
+constexpr int kSortChunk = 256;  // pairs per chunk of the counting sort
 
 // Shape of a workgroup tile: BM rows x 4 waves x NSUB x 16 features of NMAT
 // matrices, and the LDS stage holding one K step of its operands:
@@ -150,39 +155,74 @@ struct GemmTile {
 
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void expert_histogram_kernel(const int32_t* ids, int32_t n_pairs, int32_t E,
-                                                               int32_t* counts) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n_pairs) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
+// Counting sort of the pairs by expert, stable, in three passes over chunks
+// of kSortChunk consecutive pairs (no atomics, no pass over all pairs per
+// expert). ccount is [E][n_chunks]: counts per chunk, then (in place) where
+// each chunk's pairs start among the expert's. Pair ids outside 0..E-1 are
+// left out of every count, so the host's total check catches them.
+//
+// One wave per chunk, 64 pairs per round in order. Within a round, each
+// distinct expert in turn (the lowest pending lane's) takes a ballot of its
+// lanes: their ranks are the count so far plus the lanes below them, so the
+// order of the pairs is kept.
+__global__ __launch_bounds__(64) void chunk_rank_kernel(const int32_t* ids, int32_t n_pairs, int32_t E,
+                                                        int32_t n_chunks, int32_t* rank, int32_t* ccount) {
+  extern __shared__ int32_t s_cnt[];  // [E]
+  const int c = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) s_cnt[e] = 0;
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int r = 0; r < kSortChunk / 64; ++r) {
+    const int i = c * kSortChunk + r * 64 + lane;
+    int e = i < n_pairs ? ids[i] : -1;
+    e = e >= 0 && e < E ? e : -1;
+    uint64_t todo = __ballot(e >= 0);
+    while (todo) {
+      const int leader = (int)__builtin_ctzll(todo);
+      const int le = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t m = __ballot(e == le);
+      const int base = s_cnt[le];
+      if (e == le) rank[i] = base + __popcll(m & below);
+      __syncthreads();  // every lane has read the count before it moves on
+      if (lane == leader) s_cnt[le] = base + __popcll(m);
+      __syncthreads();
+      todo &= ~m;
+    }
   }
+  for (int e = lane; e < E; e += 64) ccount[(int64_t)e * n_chunks + c] = s_cnt[e];
 }
 
-// one workgroup per expert walks every pair in order (stable)
-__global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* ids, int32_t n_pairs,
-                                                             const int32_t* offsets, int32_t* perm, int32_t* inv) {
-  __shared__ int s_wave[4];
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int base = offsets[e];
-  for (int c = 0; c < n_pairs; c += 256) {
-    const int i = c + threadIdx.x;
-    const bool hit = i < n_pairs && ids[i] == e;
-    const uint64_t m = __ballot(hit);
-    const int before_in_wave = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wave[wave] = __popcll(m);
-    __syncthreads();
-    int before = before_in_wave;
-    for (int w = 0; w < wave; ++w) before += s_wave[w];
-    const int total = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
-    if (hit) {
-      perm[base + before] = i;
-      inv[i] = base + before;
+// one wave per expert: exclusive prefix of its chunk counts, and its total
+__global__ __launch_bounds__(64) void chunk_scan_kernel(int32_t* ccount, int32_t n_chunks, int32_t* counts) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  int32_t* row = ccount + (int64_t)e * n_chunks;
+  int run = 0;
+  for (int c0 = 0; c0 < n_chunks; c0 += 64) {
+    const int c = c0 + lane;
+    const int v = c < n_chunks ? row[c] : 0;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      x += lane >= d ? y : 0;
     }
-    base += total;
-    __syncthreads();
+    if (c < n_chunks) row[c] = run + x - v;
+    run += __shfl(x, 63, 64);
   }
+  if (lane == 0) counts[e] = run;
+}
+
+__global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* ids, int32_t n_pairs, int32_t E,
+                                                             int32_t n_chunks, const int32_t* offsets,
+                                                             const int32_t* cbase, const int32_t* rank,
+                                                             int32_t* perm, int32_t* inv) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_pairs) return;
+  const int e = ids[i];
+  if (e < 0 || e >= E) return;
+  const int pos = offsets[e] + cbase[(int64_t)e * n_chunks + i / kSortChunk] + rank[i];
+  perm[pos] = i;
+  inv[i] = pos;
 }
 
 // fp32 rows [R][K] -> fp16 rows [R][K] in operand order; one thread per 8
@@ -455,14 +495,22 @@ __global__ __launch_bounds__(256) void combine_pairs_kernel(const float* ypair, 
 
 // ---------------------------------------------------------------------------
 
-hipError_t launch_expert_histogram(const int32_t* ids, int32_t n_pairs, int32_t E, int32_t* counts,
-                                   hipStream_t s) {
-  hipLaunchKernelGGL(expert_histogram_kernel, dim3((n_pairs + 255) / 256), dim3(256), 0, s, ids, n_pairs, E, counts);
+int32_t sort_chunks(int32_t n_pairs) { return (n_pairs + kSortChunk - 1) / kSortChunk; }
+hipError_t launch_expert_counts(const int32_t* ids, int32_t n_pairs, int32_t E, int32_t* rank, int32_t* ccount,
+                                int32_t* counts, hipStream_t s) {
+  if (n_pairs <= 0 || E <= 0 || E > 4096) return hipErrorInvalidValue;
+  const int32_t nc = sort_chunks(n_pairs);
+  hipLaunchKernelGGL(chunk_rank_kernel, dim3(nc), dim3(64), sizeof(int32_t) * E, s, ids, n_pairs, E, nc, rank,
+                     ccount);
+  hipLaunchKernelGGL(chunk_scan_kernel, dim3(E), dim3(64), 0, s, ccount, nc, counts);
   return hipGetLastError();
 }
 hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E, const int32_t* offsets,
-                                 int32_t* perm, int32_t* inv, hipStream_t s) {
-  hipLaunchKernelGGL(expert_scatter_kernel, dim3(E), dim3(256), 0, s, ids, n_pairs, offsets, perm, inv);
+                                 const int32_t* ccount, const int32_t* rank, int32_t* perm, int32_t* inv,
+                                 hipStream_t s) {
+  if (n_pairs <= 0 || E <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(expert_scatter_kernel, dim3((n_pairs + 255) / 256), dim3(256), 0, s, ids, n_pairs, E,
+                     sort_chunks(n_pairs), offsets, ccount, rank, perm, inv);
   return hipGetLastError();
 }
 hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, hipStream_t s) {
