@@ -479,18 +479,43 @@ __global__ __launch_bounds__(256) void stage_experts_kernel(const uint4* __restr
   }
 }
 
+// y[t] = sum_i w_i y_pair[inv[t, i]] in pick order (one fmaf chain from 0),
+// four columns per thread. Up to KMAX picks, every row's load is issued
+// before the sum, so a thread has all of them in flight at once.
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_pairs_kernel(const float* ypair, const int32_t* inv, const float* w,
                                                             int32_t k, int32_t H, float* y, int32_t accumulate) {
   const int t = blockIdx.y;
-  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int j = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (j >= H) return;
-  float acc = 0.f;
-  for (int i = 0; i < k; ++i) {
-    const int64_t p = (int64_t)t * k + i;
-    acc = fmaf(w[p], ypair[(int64_t)inv[p] * H + j], acc);
+  const int64_t p0 = (int64_t)t * k;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (k <= KMAX) {
+    float4 v[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+      if (i < k) v[i] = *reinterpret_cast<const float4*>(ypair + (int64_t)inv[p0 + i] * H + j);
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+      if (i < k) {
+        const float wi = w[p0 + i];
+        acc.x = fmaf(wi, v[i].x, acc.x), acc.y = fmaf(wi, v[i].y, acc.y);
+        acc.z = fmaf(wi, v[i].z, acc.z), acc.w = fmaf(wi, v[i].w, acc.w);
+      }
+  } else {
+    for (int i = 0; i < k; ++i) {
+      const float wi = w[p0 + i];
+      const float4 v = *reinterpret_cast<const float4*>(ypair + (int64_t)inv[p0 + i] * H + j);
+      acc.x = fmaf(wi, v.x, acc.x), acc.y = fmaf(wi, v.y, acc.y);
+      acc.z = fmaf(wi, v.z, acc.z), acc.w = fmaf(wi, v.w, acc.w);
+    }
   }
-  float* yp = y + (int64_t)t * H + j;
-  *yp = accumulate ? *yp + acc : acc;
+  float4* yp = reinterpret_cast<float4*>(y + (int64_t)t * H + j);
+  if (accumulate) {
+    const float4 o = *yp;
+    acc.x += o.x, acc.y += o.y, acc.z += o.z, acc.w += o.w;
+  }
+  *yp = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -557,7 +582,8 @@ hipError_t launch_stage_experts(const uint8_t* host_layer, const int32_t* expert
 }
 hipError_t launch_combine_pairs(const float* ypair, const int32_t* inv, const float* w, int32_t T, int32_t k,
                                 int32_t H, float* y, int32_t accumulate, hipStream_t s) {
-  hipLaunchKernelGGL(combine_pairs_kernel, dim3((H + 255) / 256, T), dim3(256), 0, s, ypair, inv, w, k, H, y,
+  if (H % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_pairs_kernel<8>, dim3((H / 4 + 255) / 256, T), dim3(256), 0, s, ypair, inv, w, k, H, y,
                      accumulate);
   return hipGetLastError();
 }
