@@ -104,7 +104,8 @@ typedef struct {
   int32_t admit_misses;    /* 2: admit on the 2nd miss inside the window
                               ([A6000] "2nd sighting"); 1: admit every miss  */
   int32_t max_batch_tokens;   /* largest T for moe_forward, 1..256            */
-  int32_t max_prefill_tokens; /* largest T for moe_prefill (0: no prefill)    */
+  int32_t max_prefill_tokens; /* largest T for moe_prefill (0: no prefill);
+                                 T * top_k at most 2^26 pairs               */
   int32_t device;          /* HIP device ordinal                              */
   int32_t host_alloc;      /* MOE_HOST_COHERENT or MOE_HOST_NONCOHERENT       */
   int32_t host_sets;       /* distinct pinned expert sets, 1..L (0: L). Layer

@@ -176,7 +176,8 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if (k.n_layers < 1 || k.n_layers > (1 << 19) || k.n_experts < 1 || k.n_experts > 4096 || k.top_k < 1 || k.top_k > 32 ||
       k.top_k > k.n_experts || k.hidden < 32 || k.ffn < 32 || k.hidden % 32 || k.ffn % 32 ||
       k.quant != MOE_Q4_32_F16 || k.window_tokens < 1 || (k.admit_misses != 1 && k.admit_misses != 2) ||
-      k.max_batch_tokens < 1 || k.max_batch_tokens > 256 || k.max_prefill_tokens < 0 || k.n_layers > (1 << 20) ||
+      k.max_batch_tokens < 1 || k.max_batch_tokens > 256 || k.max_prefill_tokens < 0 ||
+      (int64_t)k.max_prefill_tokens * k.top_k > (1 << 26) || k.n_layers > (1 << 20) ||
       k.capture_picks < 0 || k.capture_picks > k.max_batch_tokens * k.top_k ||
       (k.pool_mode != MOE_POOL_PER_LAYER && k.pool_mode != MOE_POOL_GLOBAL) || k.swaps_per_step < 0 ||
       k.swap_lead < 0 || k.swap_lead > MOE_MAX_SWAP_LEAD ||

@@ -49,6 +49,9 @@ def test_create_rejects_bad_config_without_touching_a_gpu():
         moe.moe_create(n_layers=1, n_experts=8, top_k=2, hidden=100, ffn=512, pool_budget_bytes=0)
     with pytest.raises(moe.MoeError):
         moe.moe_create(n_layers=1, n_experts=5000, top_k=2, hidden=256, ffn=512, pool_budget_bytes=0)
+    with pytest.raises(moe.MoeError):  # more than 2^26 prompt pairs per pass
+        moe.moe_create(n_layers=1, n_experts=8, top_k=2, hidden=256, ffn=512, pool_budget_bytes=0,
+                       max_prefill_tokens=(1 << 25) + 1)
 
 
 def test_binding_constants_match_the_header():
