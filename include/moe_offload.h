@@ -192,10 +192,12 @@ typedef struct {
   double  prefill_gateup_ms;  /* grouped gate/up GEMM (+ SwiGLU)              */
   double  prefill_down_ms;    /* grouped down GEMM                            */
   int64_t prefill_pairs;      /* (token, pick) pairs the timed passes computed */
-  int64_t prefill_tiles;      /* 64-row (expert, tile) pairs launched         */
+  int64_t prefill_tiles;      /* (expert, row tile) pairs launched            */
   int64_t prefill_staged;     /* experts copied into borrowed staging blocks  */
   double  prefill_prep_ms;    /* block-scale transposition before the GEMMs
                                  (passes of short tiles only)                 */
+  double  prefill_stage_ms;   /* the staging copy (gather kernels or DMA),
+                                 start of its first chunk to end of its last  */
   /* cold_exec = MOE_COLD_CPU: the host threads, counted whether or not kernel
      timing is on, since the last moe_profile with enable 0 or 1 (hand-offs
      still in flight are counted once answered)                             */

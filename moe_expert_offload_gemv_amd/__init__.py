@@ -72,7 +72,7 @@ class moe_profile_stats(C.Structure):
                 ("down_bytes_per_pick", C.c_int64), ("prefill_passes", C.c_int64),
                 ("prefill_gateup_ms", C.c_double), ("prefill_down_ms", C.c_double), ("prefill_pairs", C.c_int64),
                 ("prefill_tiles", C.c_int64), ("prefill_staged", C.c_int64), ("prefill_prep_ms", C.c_double),
-                ("host_forwards", C.c_int64),
+                ("prefill_stage_ms", C.c_double), ("host_forwards", C.c_int64),
                 ("host_expert_passes", C.c_int64), ("host_picks", C.c_int64), ("host_wait_ms", C.c_double),
                 ("host_compute_ms", C.c_double)]
 

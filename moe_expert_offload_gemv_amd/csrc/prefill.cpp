@@ -87,6 +87,7 @@ struct Prefill {
   hipEvent_t lists_ready = nullptr;              // the staging list is on the device
   hipEvent_t chunk_done[kStageChunks] = {};      // chunk c of the staging copy has landed
   hipEvent_t timing[2 * kTimed * kMaxGroups] = {};  // start/stop of each timed launch
+  hipEvent_t stage_timing[2] = {};                  // first and last chunk of the staging copy
 };
 
 #define PF_HIP(ctx, expr)                                                                                \
@@ -145,6 +146,9 @@ int moe_prefill_alloc(moe_ctx* c) {
   for (hipEvent_t& ev : p->timing)
     if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess)
       return moe_ctx_fail(c, MOE_E_HIP, "prefill: event creation failed");
+  for (hipEvent_t& ev : p->stage_timing)
+    if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess)
+      return moe_ctx_fail(c, MOE_E_HIP, "prefill: event creation failed");
   return MOE_OK;
 }
 
@@ -169,6 +173,8 @@ void moe_prefill_release(moe_ctx* c) {
   for (hipEvent_t ev : p->chunk_done)
     if (ev) (void)hipEventDestroy(ev);
   for (hipEvent_t ev : p->timing)
+    if (ev) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : p->stage_timing)
     if (ev) (void)hipEventDestroy(ev);
   delete p;
   c->pf = nullptr;
@@ -292,9 +298,11 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
 
   // 4. the staging copy, chunk by chunk on its own stream, after everything
   // already queued on the pass's stream (earlier readers of the blocks)
+  const bool timed = c->profiling;
   if (n_chunks > 0) {
     PF_HIP(c, hipEventRecord(p->lists_ready, s));
     PF_HIP(c, hipStreamWaitEvent(p->copy_stream, p->lists_ready, 0));
+    if (timed) PF_HIP(c, hipEventRecord(p->stage_timing[0], p->copy_stream));
     for (int g = 1; g < G; ++g) {
       if (dma) {
         for (int64_t i = g_first[g], end = g_first[g] + g_count[g]; i < end;) {
@@ -310,6 +318,7 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
       }
       PF_HIP(c, hipEventRecord(p->chunk_done[g - 1], p->copy_stream));
     }
+    if (timed) PF_HIP(c, hipEventRecord(p->stage_timing[1], p->copy_stream));
   }
 
   // 5. stable sort of the pairs by expert; activations as fp16 rows in operand order
@@ -321,7 +330,6 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   // scales of the group's experts transposed, each K step reading whole
   // lines of them; then the grouped gate/up and down GEMMs
   const bool tscl = bm == 64;
-  const bool timed = c->profiling;
   bool launched[kMaxGroups][kTimed] = {};
   moe::GemmArgs g{};
   g.a16 = p->x16, g.arow = p->perm, g.arow_div = k;
@@ -371,6 +379,11 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
         PF_HIP(c, hipEventElapsedTime(&t, p->timing[2 * (gi * kTimed + kind)], p->timing[2 * (gi * kTimed + kind) + 1]));
         ms[kind] += t;
       }
+    if (n_chunks > 0) {
+      float t = 0;
+      PF_HIP(c, hipEventElapsedTime(&t, p->stage_timing[0], p->stage_timing[1]));
+      c->prof.prefill_stage_ms += t;
+    }
     c->prof.prefill_prep_ms += ms[0];
     c->prof.prefill_passes += 1;
     c->prof.prefill_gateup_ms += ms[1];

@@ -46,6 +46,7 @@ def _prefill_check(wl: Workload, slots: int, sample=None, flags=0, pool="layer")
     assert not moe.moe_get_counts(d.ctx, wl.n_layers, wl.n_experts).any()
     assert moe.moe_get_info(d.ctx)["clock"] == 1
     assert prof["prefill_passes"] == 1 and prof["prefill_pairs"] == T * wl.top_k
+    assert (prof["prefill_stage_ms"] > 0) == (prof["prefill_staged"] > 0)
     d.close()
     return err, prof
 
