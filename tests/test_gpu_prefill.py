@@ -18,8 +18,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _prefill_check(wl: Workload, slots: int, sample=None, flags=0, pool="layer"):
-    d = Decode(wl, slots=slots, max_batch=1, max_prefill=wl.tokens, pool=pool)
+def _prefill_check(wl: Workload, slots: int, sample=None, flags=0, pool="layer", seed=True):
+    d = Decode(wl, slots=slots, max_batch=1, max_prefill=wl.tokens, pool=pool, seed=seed)
     T, H = wl.tokens, wl.hidden
     x32 = activations(wl, 0, tokens=T)
     z = zipf_logits(wl, steps=1, tokens=T)[0, 0]
@@ -70,6 +70,14 @@ def test_prefill_dma_staging_beside_long_gemms():
     wl = Workload("prefill-e8k2-h256f512-t4000", 208, 1, 8, 2, 256, 512, tokens=4000, zipf_s=1.1)
     err, prof = _prefill_check(wl, slots=7, sample=160)
     assert prof["prefill_staged"] == 1
+
+
+def test_prefill_cold_pool_more_misses_than_staging_blocks():
+    # cold start: every slot free, so all 16 experts miss but only E - S = 8
+    # staging blocks exist; the other 8 are read zero-copy beside the gathers
+    wl = Workload("prefill-e16k4-h256f512-t100-coldpool", 209, 1, 16, 4, 256, 512, tokens=100, zipf_s=0.6)
+    err, prof = _prefill_check(wl, slots=8, seed=False)
+    assert prof["prefill_staged"] == 8
 
 
 def test_prefill_decode_shape():
