@@ -80,6 +80,14 @@ def test_prefill_cold_pool_more_misses_than_staging_blocks():
     assert prof["prefill_staged"] == 8
 
 
+def test_prefill_most_experts_the_layout_allows():
+    # E = 4096: the counting sort's per-chunk counters fill 16 KiB of LDS, and
+    # ~500 staged experts go through all eight gather chunks
+    wl = Workload("prefill-e4096k8-h256f512-t64", 210, 1, 4096, 8, 256, 512, tokens=64, zipf_s=0.8)
+    err, prof = _prefill_check(wl, slots=64)
+    assert prof["prefill_staged"] > 8 * 16
+
+
 def test_prefill_decode_shape():
     wl = Workload("prefill-e64k8-h2048f1024-t300", 203, 1, 64, 8, 2048, 1024, tokens=300, zipf_s=1.1)
     _prefill_check(wl, slots=26, sample=48)
