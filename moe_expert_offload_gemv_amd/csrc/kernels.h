@@ -218,4 +218,19 @@ hipError_t launch_stage_experts(const uint8_t* host_layer, const int32_t* expert
 hipError_t launch_combine_pairs(const float* ypair, const int32_t* inv, const float* w, int32_t T, int32_t k,
                                 int32_t H, float* y, int32_t accumulate, hipStream_t s);
 
+// Copies of the cache step, one launch: transfer i moves op[i].bytes (a
+// multiple of 4, 4-byte aligned ends) from op[i].src to op[i].dst, both
+// device-accessible (HBM, or pinned host memory mapped for the device).
+struct CopyOp {
+  const void* src;
+  void* dst;
+  int64_t bytes;
+};
+constexpr int kMaxCopyOps = 48;
+struct CopyList {
+  CopyOp op[kMaxCopyOps];
+  int32_t n;
+};
+hipError_t launch_copy_list(const CopyList& l, hipStream_t s);
+
 }  // namespace moe

@@ -418,12 +418,11 @@ extern "C" int moe_preheat(moe_ctx* c, int32_t layer, int32_t max_experts, int32
   const int64_t E = c->E, S = c->S, GS = (int64_t)c->groups * S, B = c->B;
   const int64_t g0 = c->group_of(layer) * S;
   const uint32_t clk = (uint32_t)c->clock;
-  // the device stamps are current (forwards raise them); start from them
-  if (S > 0) {
-    PF_HIP(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * GS, hipMemcpyDeviceToHost, s));
-    PF_HIP(c, hipStreamSynchronize(s));
-    std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * GS);
-  }
+  // the device stamps are current (forwards raise them); start from them. The
+  // sync also retires any earlier launch still reading the host staging.
+  if (S > 0) PF_HIP(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * GS, hipMemcpyDeviceToHost, s));
+  PF_HIP(c, hipStreamSynchronize(s));
+  if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * GS);
   const int32_t* cnt = p->h_counts;
   for (int64_t e = 0; e < E; ++e) {
     const int32_t slot = c->tbl[layer * E + e];

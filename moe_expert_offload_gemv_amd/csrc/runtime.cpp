@@ -242,8 +242,16 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   }
   if ((rc = moe_prefill_alloc(c))) return fail(rc);
 
-  // pinned host staging for the small transfers of the cache step
-  const unsigned pin = hipHostMallocDefault;
+  // pinned host staging for the small transfers of the cache step: mapped
+  // and coherent, so the step's copy launch reads the uploads in place
+  const unsigned pin = hipHostMallocMapped | hipHostMallocCoherent;
+  auto dev_view = [&](const void* host, const void** out) {
+    void* dp = nullptr;
+    if (host && hipHostGetDevicePointer(&dp, const_cast<void*>(host), 0) != hipSuccess)
+      return moe_ctx_fail(c, MOE_E_HIP, "hipHostGetDevicePointer failed for cache-step staging");
+    *out = dp;
+    return (int)MOE_OK;
+  };
   if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_ctrl, sizeof(Ctrl), pin, "ctrl staging"))) return fail(rc);
   if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_records, sizeof(uint64_t) * L * c->rec_stride, pin,
                                "record staging")))
@@ -253,6 +261,9 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if (c->capture_picks > 0 &&
       ((rc = moe_ctx_host_alloc(c, (void**)&c->h_cap_tag, sizeof(uint32_t) * L * c->rec_stride, pin, "tag staging")) ||
        (rc = moe_ctx_host_alloc(c, (void**)&c->h_last_miss, sizeof(uint32_t) * L * E, pin, "last-miss staging"))))
+    return fail(rc);
+  if ((rc = dev_view(c->h_ctrl, &c->h_ctrl_dev)) || (rc = dev_view(c->h_tbl, &c->h_tbl_dev)) ||
+      (rc = dev_view(c->h_last_miss, &c->h_last_miss_dev)))
     return fail(rc);
 
   // HBM pool: S slots per layer, or one pool of S slots for every layer
@@ -271,7 +282,8 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_stamps, sizeof(uint32_t) * G * std::max<int64_t>(S, 1), "stamps")))
     return fail(rc);
   if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_stamps, sizeof(uint32_t) * G * std::max<int64_t>(S, 1), pin,
-                               "stamp staging")))
+                               "stamp staging")) ||
+      (rc = dev_view(c->h_stamps, &c->h_stamps_dev)))
     return fail(rc);
 
   // pinned host arena, one allocation per host set, mapped for zero-copy reads
@@ -741,6 +753,26 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
 
   int64_t admissions = 0, evictions = 0, copied_pcie = 0, swap_copies = 0;
   const int32_t lead = c->cfg.swap_lead, budget = c->cfg.swaps_per_step;
+  // the step's copies on the context stream go out in one launch (several
+  // when there are more than a launch holds). The transfers of a launch run
+  // at once, so a slot admitted twice in one walk (its first newcomer evicted
+  // again) keeps only the later transfer, as sequential copies would leave it.
+  moe::CopyList cl;
+  cl.n = 0;
+  auto add_copy = [&](const void* src, void* dst, int64_t bytes) -> int {
+    for (int i = 0; i < cl.n; ++i)
+      if (cl.op[i].dst == dst) {
+        cl.op[i] = moe::CopyOp{src, dst, bytes};
+        return MOE_OK;
+      }
+    if (cl.n == moe::kMaxCopyOps) {
+      HIP_TRY(c, moe::launch_copy_list(cl, c->stream));
+      cl.n = 0;
+    }
+    cl.op[cl.n++] = moe::CopyOp{src, dst, bytes};
+    return MOE_OK;
+  };
+  int crc;
   for (uint64_t entry : c->last_log) {
     const uint32_t t = (uint32_t)(entry >> 32);
     const int64_t l = (int64_t)((entry >> 12) & 0x7ffff);
@@ -794,14 +826,15 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     ++admissions;
     uint8_t* dst = c->pool + (g0 + v) * B;
     if (c->cap_of[te] >= 0) {  // before the next step's forwards overwrite the capture block
-      HIP_TRY(c, hipMemcpyAsync(dst, c->d_capture + (l * c->capture_picks + c->cap_of[te]) * B, B,
-                                hipMemcpyDeviceToDevice, c->stream));
+      if ((crc = add_copy(c->d_capture + (l * c->capture_picks + c->cap_of[te]) * B, dst, B))) return crc;
+    } else if (lead == 0) {
+      if ((crc = add_copy(c->host_layers_dev[l] + e * B, dst, B))) return crc;  // zero-copy read of the pinned weights
+      ++copied_pcie;
     } else {
       // with a lead the slot is read by nobody until the flip: the copy runs beside the next steps
-      HIP_TRY(c, hipMemcpyAsync(dst, c->host_layers[l] + e * B, B, hipMemcpyHostToDevice,
-                                lead ? c->swap_stream : c->stream));
+      HIP_TRY(c, hipMemcpyAsync(dst, c->host_layers[l] + e * B, B, hipMemcpyHostToDevice, c->swap_stream));
       ++copied_pcie;
-      swap_copies += lead ? 1 : 0;
+      ++swap_copies;
     }
   }
   forget_captures(c);
@@ -827,21 +860,23 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
         ++flips;
       }
   }
+  // uploads, read in place from the mapped staging by the same launch
   if (c->d_last_miss && misses > 0) {  // the next step's forwards decide what to capture from it
     std::memcpy(c->h_last_miss, c->last_miss.data(), sizeof(uint32_t) * L * E);
-    HIP_TRY(c, hipMemcpyAsync(c->d_last_miss, c->h_last_miss, sizeof(uint32_t) * L * E, hipMemcpyHostToDevice,
-                              c->stream));
+    if ((crc = add_copy(c->h_last_miss_dev, c->d_last_miss, sizeof(uint32_t) * L * E))) return crc;
   }
   if (admissions > 0 || flips > 0) {
     std::memcpy(c->h_tbl, c->tbl.data(), sizeof(int32_t) * L * E);
-    HIP_TRY(c, hipMemcpyAsync(c->d_tbl, c->h_tbl, sizeof(int32_t) * L * E, hipMemcpyHostToDevice, c->stream));
-    std::memcpy(c->h_stamps, c->stamps.data(), sizeof(uint32_t) * GS);
-    HIP_TRY(c, hipMemcpyAsync(c->d_stamps, c->h_stamps, sizeof(uint32_t) * GS, hipMemcpyHostToDevice,
-                              c->stream));
+    if ((crc = add_copy(c->h_tbl_dev, c->d_tbl, sizeof(int32_t) * L * E))) return crc;
+    if (S > 0) {
+      std::memcpy(c->h_stamps, c->stamps.data(), sizeof(uint32_t) * GS);
+      if ((crc = add_copy(c->h_stamps_dev, c->d_stamps, sizeof(uint32_t) * GS))) return crc;
+    }
   }
   c->clock += st.step_tokens;
   *c->h_ctrl = Ctrl{(uint32_t)c->clock, 0, 0, 0};
-  HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
+  if ((crc = add_copy(c->h_ctrl_dev, c->d_ctrl, sizeof(Ctrl)))) return crc;
+  HIP_TRY(c, moe::launch_copy_list(cl, c->stream));
 
   if (out) {
     out->step = c->steps;

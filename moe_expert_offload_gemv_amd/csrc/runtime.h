@@ -61,6 +61,12 @@ struct moe_ctx {
   uint32_t* h_last_miss = nullptr;
   int32_t* h_tbl = nullptr;
   uint32_t* h_stamps = nullptr;
+  // device-side addresses of the same staging (mapped), read by the cache
+  // step's copy launch
+  const void* h_ctrl_dev = nullptr;
+  const void* h_last_miss_dev = nullptr;
+  const void* h_tbl_dev = nullptr;
+  const void* h_stamps_dev = nullptr;
 
   // prefill (borrowed staging blocks and per-pass scratch)
   int64_t n_staging = 0;
