@@ -226,7 +226,7 @@ struct CopyOp {
   void* dst;
   int64_t bytes;
 };
-constexpr int kMaxCopyOps = 48;
+constexpr int kMaxCopyOps = 16;  // a step's usual promotions and its uploads; more take further launches
 struct CopyList {
   CopyOp op[kMaxCopyOps];
   int32_t n;

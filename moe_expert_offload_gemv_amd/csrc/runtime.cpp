@@ -262,9 +262,14 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
       ((rc = moe_ctx_host_alloc(c, (void**)&c->h_cap_tag, sizeof(uint32_t) * L * c->rec_stride, pin, "tag staging")) ||
        (rc = moe_ctx_host_alloc(c, (void**)&c->h_last_miss, sizeof(uint32_t) * L * E, pin, "last-miss staging"))))
     return fail(rc);
+  const void* rec_view = nullptr;
+  const void* tag_view = nullptr;
   if ((rc = dev_view(c->h_ctrl, &c->h_ctrl_dev)) || (rc = dev_view(c->h_tbl, &c->h_tbl_dev)) ||
-      (rc = dev_view(c->h_last_miss, &c->h_last_miss_dev)))
+      (rc = dev_view(c->h_last_miss, &c->h_last_miss_dev)) || (rc = dev_view(c->h_records, &rec_view)) ||
+      (rc = dev_view(c->h_cap_tag, &tag_view)))
     return fail(rc);
+  c->h_records_dev = const_cast<void*>(rec_view);
+  c->h_cap_tag_dev = const_cast<void*>(tag_view);
 
   // HBM pool: S slots per layer, or one pool of S slots for every layer
   int64_t budget = k.pool_budget_bytes;
@@ -702,16 +707,19 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
   if (stream_capturing(c->stream)) return moe_ctx_fail(c, MOE_E_CAPTURING, "cache_step while capturing");
   const int64_t L = c->L, E = c->E, S = c->S, B = c->B;
 
-  // one round trip: the control words, every layer's pick records, the stamps
-  HIP_TRY(c, hipMemcpyAsync(c->h_ctrl, c->d_ctrl, sizeof(Ctrl), hipMemcpyDeviceToHost, c->stream));
-  HIP_TRY(c, hipMemcpyAsync(c->h_records, c->d_records, sizeof(uint64_t) * L * c->rec_stride, hipMemcpyDeviceToHost,
-                            c->stream));
+  // one round trip: the control words, every layer's pick records, the
+  // stamps and capture tags, written into the mapped staging by one launch
   const int64_t GS = (int64_t)c->groups * S;  // slots of every pool
-  if (S > 0)
-    HIP_TRY(c, hipMemcpyAsync(c->h_stamps, c->d_stamps, sizeof(uint32_t) * GS, hipMemcpyDeviceToHost, c->stream));
-  if (c->d_cap_tag)
-    HIP_TRY(c, hipMemcpyAsync(c->h_cap_tag, c->d_cap_tag, sizeof(uint32_t) * L * c->rec_stride, hipMemcpyDeviceToHost,
-                              c->stream));
+  {
+    moe::CopyList rb;
+    rb.n = 0;
+    rb.op[rb.n++] = moe::CopyOp{c->d_ctrl, const_cast<void*>(c->h_ctrl_dev), (int64_t)sizeof(Ctrl)};
+    rb.op[rb.n++] = moe::CopyOp{c->d_records, c->h_records_dev, (int64_t)sizeof(uint64_t) * L * c->rec_stride};
+    if (S > 0) rb.op[rb.n++] = moe::CopyOp{c->d_stamps, const_cast<void*>(c->h_stamps_dev), (int64_t)sizeof(uint32_t) * GS};
+    if (c->d_cap_tag)
+      rb.op[rb.n++] = moe::CopyOp{c->d_cap_tag, c->h_cap_tag_dev, (int64_t)sizeof(uint32_t) * L * c->rec_stride};
+    HIP_TRY(c, moe::launch_copy_list(rb, c->stream));
+  }
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   const Ctrl st = *c->h_ctrl;
   const bool host_fault = st.host_fault != 0;

@@ -67,6 +67,8 @@ struct moe_ctx {
   const void* h_last_miss_dev = nullptr;
   const void* h_tbl_dev = nullptr;
   const void* h_stamps_dev = nullptr;
+  void* h_records_dev = nullptr;
+  void* h_cap_tag_dev = nullptr;
 
   // prefill (borrowed staging blocks and per-pass scratch)
   int64_t n_staging = 0;
