@@ -11,11 +11,14 @@
 namespace moe {
 namespace {
 
-constexpr int64_t kCopyChunk = 65536;  // bytes per work-group
+// Bytes per work-group: 64 per lane, all loaded before any is stored, so a
+// chunk read from pinned host memory costs one PCIe round trip, not one per
+// 4 KiB (the uploads are host reads of up to ~100 KB each).
+constexpr int64_t kCopyChunk = 256 * 64;
 
 // grid = (chunks of the longest transfer, transfers); a work-group moves one
-// chunk of one transfer, 16 bytes per lane and iteration when the transfer
-// allows it, else 4
+// chunk of one transfer, in 16-byte words when the transfer allows it, else
+// in 4-byte words
 __global__ __launch_bounds__(256) void copy_list_kernel(CopyList l) {
   const int o = blockIdx.y;
   if (o >= l.n) return;
@@ -26,11 +29,25 @@ __global__ __launch_bounds__(256) void copy_list_kernel(CopyList l) {
   if ((((uintptr_t)op.src | (uintptr_t)op.dst | (uint64_t)op.bytes) & 15) == 0) {
     const uint4* s = reinterpret_cast<const uint4*>(op.src);
     uint4* d = reinterpret_cast<uint4*>(op.dst);
-    for (int64_t i = b0 / 16 + threadIdx.x; i < b1 / 16; i += 256) d[i] = s[i];
+    const int64_t i0 = b0 / 16 + threadIdx.x, n = b1 / 16;
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + 256 * u < n) v[u] = s[i0 + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + 256 * u < n) d[i0 + 256 * u] = v[u];
   } else {
     const uint32_t* s = reinterpret_cast<const uint32_t*>(op.src);
     uint32_t* d = reinterpret_cast<uint32_t*>(op.dst);
-    for (int64_t i = b0 / 4 + threadIdx.x; i < b1 / 4; i += 256) d[i] = s[i];
+    const int64_t i0 = b0 / 4 + threadIdx.x, n = b1 / 4;
+    uint32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (i0 + 256 * u < n) v[u] = s[i0 + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (i0 + 256 * u < n) d[i0 + 256 * u] = v[u];
   }
 }
 
