@@ -133,6 +133,15 @@ def test_promotions_every_miss_checked_every_step(capture_picks):
     assert copies["pcie"] == (0 if capture_picks is None else copies["copied"]), copies
 
 
+def test_cold_start_admit_every_miss_many_copies_per_step():
+    # every slot free and every miss admitted: the first steps admit dozens of
+    # experts per layer, evicting some of their own newcomers again, so the
+    # cache step's copies span several launches and repeat slots
+    wl = Workload("decode-e64k8-h256f512-l3-b16-admit1", 108, 3, 64, 8, 256, 512, tokens=16, steps=6, zipf_s=0.9,
+                  slots=24, rotation=5, admit_misses=1)
+    _run_decode(wl, slots=24, check_every=1, seed=False)
+
+
 def test_decode_batch_of_five_tokens():
     wl = Workload("decode-e64k8-h2048f1024-l2-b5", 102, 2, 64, 8, 2048, 1024, tokens=5, steps=12, zipf_s=1.1,
                   slots=20, rotation=20)
