@@ -43,25 +43,38 @@ def log(*a):
 
 
 def setup_ctx(moe, wl, slots, stream, host_alloc, layers=None, progress=True, capture_picks=None, pool="layer",
-              max_prefill_tokens=0, swaps=(0, 0), cold_exec=0, cpu_threads=0):
-    """slots per layer; pool="global" gives one pool of the same total size to all layers."""
+              max_prefill_tokens=0, swaps=(0, 0), cold_exec=0, cpu_threads=0, budget=None, reserve=0, timing=None):
+    """slots per layer; pool="global" gives one pool of the same total size to all layers. budget/reserve:
+    the pool's capacity rule instead (budget -1: free HBM minus reserve; both: the smaller). timing: a dict
+    that receives the seconds spent creating the context (pinning the host arena, allocating the pool) and
+    registering the weights (generating them, repacking into pinned memory)."""
     from workload import frequency_table, layer_weights
 
     L = wl.n_layers if layers is None else layers
+    t0 = time.time()
     ctx = moe.moe_create(L, wl.n_experts, wl.top_k, wl.hidden, wl.ffn,
-                         pool_budget_bytes=L * slots * wl.expert_bytes, window_tokens=wl.window,
+                         pool_budget_bytes=L * slots * wl.expert_bytes if budget is None else int(budget),
+                         reserve_bytes=int(reserve), window_tokens=wl.window,
                          admit_misses=wl.admit_misses, max_batch_tokens=wl.tokens,
                          max_prefill_tokens=max_prefill_tokens, host_alloc=host_alloc,
                          host_sets=min(wl.weight_layers, L), stream=stream, capture_picks=capture_picks,
                          pool_mode=moe.MOE_POOL_GLOBAL if pool == "global" else moe.MOE_POOL_PER_LAYER,
                          swaps_per_step=swaps[0], swap_lead=swaps[1], cold_exec=cold_exec, cpu_threads=cpu_threads)
+    t1 = time.time()
     buf = None
-    t0 = time.time()
+    gen_s = 0.0
     for layer in range(min(wl.weight_layers, L)):  # layer l reads host set l % weight_layers
+        tg = time.time()
         buf = layer_weights(wl, layer, out=buf)
+        gen_s += time.time() - tg
         moe.moe_register_layer(ctx, layer, *buf)
         if progress and (layer % 8 == 7 or layer == min(wl.weight_layers, L) - 1):
-            log(f"registered host set {layer + 1}/{min(wl.weight_layers, L)} ({time.time() - t0:.1f} s)")
+            log(f"registered host set {layer + 1}/{min(wl.weight_layers, L)} ({time.time() - t1:.1f} s)")
+    if timing is not None:
+        info = moe.moe_get_info(ctx)
+        timing.update(create_s=round(t1 - t0, 2), register_s=round(time.time() - t1 - gen_s, 2),
+                      generate_weights_s=round(gen_s, 2), pinned_GB=round(info["host_bytes"] / 1e9, 2),
+                      pool_GB=round(info["pool_bytes"] / 1e9, 2))
     freq = frequency_table(wl)[:L]
     return ctx, freq
 
@@ -330,16 +343,27 @@ def host_cold_pass(moe, torch, wl, stream, host_alloc, pool, x_all, logits_all, 
 LARGE_WORKLOADS = ("large-e256k8-h4096f1536-l60-b1", "large-e256k8-h4096f1536-l60-b32")
 
 
+LARGE_POOL_CAP = 160e9       # the large model's HBM pool cap ...
+LARGE_RESERVE = 16e9         # ... after a reservation for the KV cache and dense weights
+
+
 def large_pass(moe, torch, stream, host_alloc, steps=32, warmup=4):
-    """The 60-layer, 256-expert model at decode batch 1 and 32 on one context (pool of 251 slots per layer in
-    160 GB of HBM; batch 32 takes the grouped path). HIP graph per step, as the main run."""
+    """The 60-layer, 256-expert model at decode batch 1 and 32 on one context (pool capped at 160 GB after a
+    16 GB reservation: min(160e9, free HBM - 16e9), 251 slots per layer; batch 32 takes the grouped path).
+    HIP graph per step, as the main run."""
     import numpy as np
 
     from workload import WORKLOADS, frequency_table, step_activations, zipf_logits
 
-    out = {}
     wl1, wl32 = (WORKLOADS[n] for n in LARGE_WORKLOADS)
-    ctx, _ = setup_ctx(moe, wl32, wl32.slots, stream, host_alloc, progress=False)
+    setup = {}
+    ctx, _ = setup_ctx(moe, wl32, wl32.slots, stream, host_alloc, progress=False, budget=LARGE_POOL_CAP,
+                       reserve=LARGE_RESERVE, timing=setup)
+    info = moe.moe_get_info(ctx)
+    out = {"pool": {"rule": "min(160e9, free HBM - 16e9)", "free_GB_at_sizing": round(info["free_bytes_at_sizing"] / 1e9, 2),
+                    "budget_GB": round(info["pool_budget_bytes"] / 1e9, 2), "slots_per_layer": info["slots_per_layer"]},
+           "setup": setup}
+    log(f"large model pool: {out['pool']}")
     L, H, E = wl32.n_layers, wl32.hidden, wl32.n_experts
     try:
         for wl in (wl1, wl32):
@@ -371,14 +395,80 @@ def large_pass(moe, torch, stream, host_alloc, steps=32, warmup=4):
                 run_steps(moe, ctx, steps, step, acc)
                 torch.cuda.synchronize()
                 elapsed = time.perf_counter() - t0
+            distinct_gbps = acc["distinct_experts"] * wl.expert_bytes / elapsed / 1e9
             out[wl.name] = {"tokens_per_s": round(steps * T / elapsed, 2),
                             "ms_per_step": round(elapsed / steps * 1e3, 3),
                             "hit_rate": round(acc["hits"] / max(acc["hits"] + acc["misses"], 1), 4),
                             "path": "grouped by expert" if T >= 8 else "one GEMV pass per pick",
-                            # expert bytes per pick served / time (a pick's bytes counted again for every pick)
-                            "pick_weight_GBps": round((acc["hot_bytes"] + acc["cold_bytes"]) / elapsed / 1e9, 1)}
+                            "distinct_experts_per_layer_step": round(acc["distinct_experts"] / (steps * L), 2),
+                            # bytes of the distinct (layer, expert) pairs each step read / time: the weight bytes
+                            # the step has to move at least (tokens picking one expert share its read)
+                            "distinct_weight_GBps": round(distinct_gbps, 1),
+                            "distinct_frac_of_hbm": round(distinct_gbps / HBM_PEAK_GBPS, 4)}
             log(f"{wl.name}: {out[wl.name]}")
             del graph, logits, x_all, xs, zs, res
+    finally:
+        moe.moe_destroy(ctx)
+    return out
+
+
+POLICY_WORKLOAD = "policy-e512k8-h2048f1024-l48-rot512"
+
+
+def policy_pass(moe, torch, stream, host_alloc, warmup=8):
+    """The cache-policy workload end to end (2048 decode steps of 48 layers, popularity permutation re-drawn
+    every 512 tokens, 40 % pool, admission on the second miss within 64 tokens), from the seeded pool and, as
+    the ablation, from an empty one (moe_seed with no table). HIP graph per step, cache step between steps,
+    as the main run. Each run starts at step 0 of the workload."""
+    import numpy as np
+
+    from workload import WORKLOADS, step_activations, zipf_logits
+
+    wl = WORKLOADS[POLICY_WORKLOAD]
+    L, T, H, E = wl.n_layers, wl.tokens, wl.hidden, wl.n_experts
+    setup = {}
+    ctx, freq = setup_ctx(moe, wl, wl.slots, stream, host_alloc, progress=False, timing=setup)
+    out = {"workload": wl.name, "steps": wl.steps, "slots_per_layer": wl.slots, "setup": setup}
+    try:
+        logits = torch.from_numpy(zipf_logits(wl)).cuda()                      # [2048][L][1][E]
+        x_all = torch.from_numpy(np.stack([step_activations(wl, s) for s in range(16)])).cuda()
+        xs = torch.zeros((L, T, H), dtype=torch.float32, device="cuda")
+        zs = torch.zeros((L, T, E), dtype=torch.float32, device="cuda")
+        res = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+        moe.moe_seed(ctx, freq)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                for layer in range(L):
+                    moe.moe_forward(ctx, layer, T, xs[layer], zs[layer], res, flags=moe.MOE_ACCUMULATE)
+
+            def step(i):
+                xs.copy_(x_all[i % 16])
+                zs.copy_(logits[i])
+                res.zero_()
+                graph.replay()
+
+            for seeded in (True, False):
+                moe.moe_seed(ctx, freq)
+                run_steps(moe, ctx, warmup, step)
+                moe.moe_seed(ctx, freq if seeded else None)
+                torch.cuda.synchronize()
+                acc = {}
+                t0 = time.perf_counter()
+                run_steps(moe, ctx, wl.steps, step, acc)
+                torch.cuda.synchronize()
+                elapsed = time.perf_counter() - t0
+                r = {"tokens_per_s": round(wl.steps * T / elapsed, 2), "ms_per_step": round(elapsed / wl.steps * 1e3, 4),
+                     "hit_rate": round(acc["hits"] / max(acc["hits"] + acc["misses"], 1), 4),
+                     "admissions_per_step": round(acc["admissions"] / wl.steps, 3),
+                     "promotion_GB_over_pcie": round(acc["copied_pcie_bytes"] / 1e9, 3)}
+                log(f"policy workload, {'seeded' if seeded else 'no seed'}: {r}")
+                if seeded:
+                    out.update(r)
+                else:
+                    out["no_seed"] = r
+        out["seed_gain"] = round(out["tokens_per_s"] / out["no_seed"]["tokens_per_s"], 4)
+        del graph, logits, x_all, xs, zs, res
     finally:
         moe.moe_destroy(ctx)
     return out
@@ -495,10 +585,11 @@ def main():
     cold_exec = moe.MOE_COLD_CPU if args.cold_exec == "cpu" else moe.MOE_COLD_GPU
     if cold_exec == moe.MOE_COLD_CPU:
         args.eager = True  # the host hand-off is not capturable
+    setup = {}
     ctx, freq = setup_ctx(moe, wl, wl.slots, stream, host_alloc,
                           capture_picks=None if args.capture_picks < 0 else args.capture_picks, pool=args.pool,
                           max_prefill_tokens=prompt_tokens, swaps=(args.swaps_per_step, args.swap_lead),
-                          cold_exec=cold_exec, cpu_threads=args.cpu_threads)
+                          cold_exec=cold_exec, cpu_threads=args.cpu_threads, timing=setup)
     info = moe.moe_get_info(ctx)
     if cold_exec == moe.MOE_COLD_CPU:
         log(f"cold picks on {info['host_threads']} host threads (isa code {info['host_isa']})")
@@ -509,8 +600,11 @@ def main():
     xs = torch.zeros((L, T, H), dtype=torch.float32, device="cuda")
     zs = torch.zeros((L, T, E), dtype=torch.float32, device="cuda")
     res = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+    t_seed = time.time()
     moe.moe_seed(ctx, freq)
-    log(f"setup {time.time() - t_setup:.1f} s")
+    setup["seed_s"] = round(time.time() - t_seed, 2)
+    setup["total_s"] = round(time.time() - t_setup, 2)
+    log(f"setup {setup}")
 
     def forward_all():
         for layer in range(L):
@@ -595,6 +689,8 @@ def main():
                    "pool": args.pool, "swaps_per_step": args.swaps_per_step, "swap_lead": args.swap_lead,
                    "cold_exec": args.cold_exec, "host_threads": info["host_threads"],
                    "launch": "eager" if args.eager else "hip-graph"},
+        # outside the timed region: pinning and allocating, weight generation, registration, seeding
+        "setup": setup,
         "effective_weight_GBps": round((acc["hot_bytes"] + acc["cold_bytes"]) / elapsed / 1e9, 2),
         "hot_GBps_over_step": round(acc["hot_bytes"] / elapsed / 1e9, 2),
         "cold_GBps_over_step": round(acc["cold_bytes"] / elapsed / 1e9, 2),
@@ -691,6 +787,7 @@ def main():
                                                               cpu_threads=args.cpu_threads)
         log(f"host-thread cold picks: {result['cold_picks_on_host_threads']}")
     if not args.no_side_passes and wl.name == "decode-e512k8-h2048f1024-l48-b1":
+        result["policy"] = policy_pass(moe, torch, stream, host_alloc)
         result["large_model"] = large_pass(moe, torch, stream, host_alloc)
     if not args.no_side_passes:
         gemm_ceiling = fp16_gemm_ceiling(torch)

@@ -94,12 +94,21 @@ typedef struct {
   int32_t hidden;          /* H, multiple of 32                               */
   int32_t ffn;             /* F, multiple of 32                               */
   int32_t quant;           /* MOE_Q4_32_F16                                   */
-  int64_t pool_budget_bytes; /* >= 0: HBM pool budget; < 0: free HBM at create
-                                time minus reserve_bytes. Slots per layer
+  int64_t pool_budget_bytes; /* >= 0: HBM pool budget; < 0: free HBM at the
+                                time the pool is sized minus reserve_bytes
+                                ([A6000]: capacity from free memory minus a
+                                safety margin). With both a budget >= 0 and
+                                reserve_bytes > 0 the budget is the smaller
+                                of the two (a cap on the pool after a
+                                reservation). Slots per layer
                                 S = min(E, budget / (L * expert_bytes)); with
                                 MOE_POOL_GLOBAL, slots of the one pool
-                                S = min(L * E, budget / expert_bytes).        */
-  int64_t reserve_bytes;   /* HBM left free when pool_budget_bytes < 0        */
+                                S = min(L * E, budget / expert_bytes). The
+                                small device state and the capture blocks are
+                                allocated before the pool is sized.          */
+  int64_t reserve_bytes;   /* >= 0: HBM left free for other users (KV cache,
+                              dense weights) when the budget comes from free
+                              memory; 0 with an explicit budget: no cap      */
   int32_t window_tokens;   /* admission window in tokens (64 in [FORK])       */
   int32_t admit_misses;    /* 2: admit on the 2nd miss inside the window
                               ([A6000] "2nd sighting"); 1: admit every miss  */
@@ -161,6 +170,10 @@ typedef struct {
   int64_t host_threads;       /* threads computing cold picks (0: GPU does)   */
   int64_t host_isa;           /* their dot products: 0 none, 1 scalar C++,
                                  2 AVX2+FMA+F16C, 3 AVX-512                    */
+  int64_t pool_budget_bytes;  /* the budget S was sized from (after the rule
+                                 of moe_config.pool_budget_bytes)             */
+  int64_t free_bytes_at_sizing; /* free HBM when the pool was sized (-1: not
+                                 queried: explicit budget, no reserve)        */
 } moe_info;
 
 typedef struct {
@@ -175,6 +188,12 @@ typedef struct {
   int64_t copied_bytes;       /* promotion copies into pool slots issued      */
   int64_t copied_pcie_bytes;  /* the part copied from pinned host memory (the
                                  rest came from capture blocks in HBM)        */
+  int64_t distinct_experts;   /* distinct (layer, expert) pairs the step read:
+                                 the expert bytes a step must move at least
+                                 are distinct_experts * expert_bytes (several
+                                 tokens of a batch picking one expert share
+                                 its read)                                    */
+  int64_t distinct_cold_experts; /* of those, the ones read over PCIe          */
 } moe_step_stats;
 
 typedef struct {

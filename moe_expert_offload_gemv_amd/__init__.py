@@ -54,12 +54,14 @@ class moe_config(C.Structure):
 
 class moe_info(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("slots_per_layer", "expert_bytes", "pool_bytes", "host_bytes",
-                                        "staging_experts", "clock", "steps", "host_threads", "host_isa")]
+                                        "staging_experts", "clock", "steps", "host_threads", "host_isa",
+                                        "pool_budget_bytes", "free_bytes_at_sizing")]
 
 
 class moe_step_stats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("step", "tokens", "hits", "misses", "admissions", "evictions",
-                                        "hot_bytes", "cold_bytes", "copied_bytes", "copied_pcie_bytes")]
+                                        "hot_bytes", "cold_bytes", "copied_bytes", "copied_pcie_bytes",
+                                        "distinct_experts", "distinct_cold_experts")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}

@@ -361,7 +361,9 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
         r.w[p] = w;
         r.addr[p] = hot ? r.pool + (int64_t)slot * r.expert_bytes : r.host + (int64_t)e * r.expert_bytes;
         r.kind[p] = hot ? kHot : (capture ? (uint8_t)(kCold | kCaptured) : kCold);
-        if (capture) r.cap_tag[p] = clk;
+        // every pick that may capture rewrites its tag, so a tag is never
+        // left over from an earlier forward of the same layer in the step
+        if (may_capture) r.cap_tag[p] = capture ? clk : 0u;
         if (r.ids_user) r.ids_user[p] = e;
         if (r.w_user) r.w_user[p] = w;
         if (p == 0) atomicMax(&r.ctrl->step_tokens, (uint32_t)r.T);

@@ -173,6 +173,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   *out = nullptr;
   const moe_config& k = *cfg;
   if (k.host_sets < 0 || k.host_sets > k.n_layers) return g_create_error = "host_sets outside 0..n_layers", MOE_E_INVAL;
+  if (k.reserve_bytes < 0) return g_create_error = "reserve_bytes < 0", MOE_E_INVAL;
   if (k.n_layers < 1 || k.n_layers > (1 << 19) || k.n_experts < 1 || k.n_experts > 4096 || k.top_k < 1 || k.top_k > 32 ||
       k.top_k > k.n_experts || k.hidden < 32 || k.ffn < 32 || k.hidden % 32 || k.ffn % 32 ||
       k.quant != MOE_Q4_32_F16 || k.window_tokens < 1 || (k.admit_misses != 1 && k.admit_misses != 2) ||
@@ -272,12 +273,17 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->h_cap_tag_dev = const_cast<void*>(tag_view);
 
   // HBM pool: S slots per layer, or one pool of S slots for every layer
+  // capacity: an explicit budget, or free HBM minus the reserve, or (both
+  // given) the smaller of the two: a cap on the pool after a reservation
   int64_t budget = k.pool_budget_bytes;
-  if (budget < 0) {
+  if (budget < 0 || k.reserve_bytes > 0) {
     size_t fr = 0, tot = 0;
     if (hipMemGetInfo(&fr, &tot) != hipSuccess) return fail(moe_ctx_fail(c, MOE_E_HIP, "hipMemGetInfo failed"));
-    budget = std::max<int64_t>(0, (int64_t)fr - k.reserve_bytes);
+    c->free_at_sizing = (int64_t)fr;
+    const int64_t avail = std::max<int64_t>(0, (int64_t)fr - k.reserve_bytes);
+    budget = budget < 0 ? avail : std::min(budget, avail);
   }
+  c->budget = budget;
   c->groups = k.pool_mode == MOE_POOL_GLOBAL ? 1 : (int32_t)L;
   c->S = (int32_t)(k.pool_mode == MOE_POOL_GLOBAL ? std::min<int64_t>(L * E, budget / c->B)
                                                   : std::min<int64_t>(E, budget / (L * c->B)));
@@ -321,6 +327,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->stamps.assign(G * std::max<int64_t>(S, 1), 0);
   c->last_miss.assign(L * E, 0);
   c->cap_of.assign(L * E, -1);
+  c->seen.assign(L * E, 0u);
   c->pend.assign(L * E, -1);
   c->flip.assign(G * std::max<int64_t>(S, 1), -1);
   if (k.swap_lead > 0) {
@@ -410,6 +417,7 @@ extern "C" int moe_seed(moe_ctx* c, const uint32_t* freq) {
   std::fill(c->owner.begin(), c->owner.end(), -1);
   std::fill(c->stamps.begin(), c->stamps.end(), 0u);
   std::fill(c->last_miss.begin(), c->last_miss.end(), 0u);
+  std::fill(c->seen.begin(), c->seen.end(), 0u);  // the step count restarts
   std::fill(c->pend.begin(), c->pend.end(), -1);
   std::fill(c->flip.begin(), c->flip.end(), -1);
   if (c->swap_stream) HIP_TRY(c, hipStreamSynchronize(c->swap_stream));  // copies into slots about to be reseeded
@@ -725,7 +733,8 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
   const bool host_fault = st.host_fault != 0;
   if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * GS);
   // records of this step carry clocks in [clock, clock + step tokens); older ones are stale
-  int64_t hits = 0;
+  int64_t hits = 0, distinct = 0, distinct_cold = 0;
+  const uint32_t mark = (uint32_t)(c->steps + 1);  // seen[te] == mark: (layer, expert) already read this step
   c->last_log.clear();
   forget_captures(c);  // left over if an earlier step stopped on an error
   const uint64_t t_lo = (uint64_t)c->clock, t_hi = (uint64_t)c->clock + st.step_tokens;
@@ -733,6 +742,14 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     const uint64_t r = c->h_records[i];
     const uint64_t t = r >> 32;
     if (t < t_lo || t >= t_hi) continue;
+    {
+      const int64_t te = (i / c->rec_stride) * E + (int64_t)(r & 0xfff);
+      if ((r & 0xfff) < (uint64_t)E && c->seen[te] != mark) {
+        c->seen[te] = mark;
+        ++distinct;
+        distinct_cold += (r & moe::kRecordHit) ? 0 : 1;
+      }
+    }
     if (r & moe::kRecordHit) {
       ++hits;
       continue;
@@ -897,6 +914,8 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     out->cold_bytes = misses * B;
     out->copied_bytes = admissions * B;
     out->copied_pcie_bytes = copied_pcie * B;
+    out->distinct_experts = distinct;
+    out->distinct_cold_experts = distinct_cold;
   }
   c->steps += 1;
   if (host_fault)
@@ -922,6 +941,8 @@ extern "C" int moe_get_info(moe_ctx* c, moe_info* out) {
                                                                                       : 1;
   out->clock = c->clock;
   out->steps = c->steps;
+  out->pool_budget_bytes = c->budget;
+  out->free_bytes_at_sizing = c->free_at_sizing;
   return MOE_OK;
 }
 

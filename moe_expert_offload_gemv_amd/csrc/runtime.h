@@ -20,6 +20,8 @@ struct moe_ctx {
   int device = 0;
   int32_t L = 0, E = 0, k = 0, H = 0, F = 0;
   int32_t S = 0;       // slots of one pool
+  int64_t budget = 0;          // HBM budget the slots were sized from
+  int64_t free_at_sizing = -1; // free HBM when the pool was sized (-1: not queried)
   int32_t groups = 0;  // pools: L (a pool per layer) or 1 (one global pool)
   int64_t group_of(int64_t layer) const { return groups == 1 ? 0 : layer; }
   moe::ExpertLayout lay{};
@@ -94,6 +96,7 @@ struct moe_ctx {
   uint8_t* mbox_dev = nullptr;         // device address of the same
   int64_t mb_off_done = 0, mb_off_seq = 0, mb_off_e = 0, mb_off_kind = 0, mb_off_x = 0, mb_off_y = 0;
   std::vector<int32_t> cap_of;         // [L][E] captured pick of the expert in the step, or -1
+  std::vector<uint32_t> seen;          // [L][E] last step (+1) whose records read the expert
   std::vector<int64_t> cap_touched;    // entries of cap_of set in the step
   std::vector<char> registered;        // per host set
   bool seeded = false;

@@ -147,17 +147,43 @@ class GraphDecode:
         self.d.close()
 
 
-def oracle_layers(wl: Workload, xs_step, logits_step, layers=None):
-    """fp64 outputs [L][T][H] of the layers of one step through the oracle,
-    regenerating the picked experts' weights."""
+def picked_weights(wl: Workload, layer: int, ids) -> dict:
+    """expert id -> (gate, up, down) for the experts in ids, regenerated on a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from workload import expert_weights
 
+    todo = [int(e) for e in np.unique(ids)]
+    with ThreadPoolExecutor(max(1, min(16, len(todo)))) as ex:
+        mats = list(ex.map(lambda e: expert_weights(wl, layer, e), todo))
+    return dict(zip(todo, mats))
+
+
+def oracle_layers(wl: Workload, xs_step, logits_step, layers=None):
+    """fp64 outputs [len(layers)][T][H] of the layers of one step through the
+    oracle (every layer when layers is None), regenerating the picked experts' weights."""
     out = []
     for layer in range(wl.n_layers) if layers is None else layers:
         z = logits_step[layer]
         ids, _ = oracle.route(z, wl.top_k)
-        experts = {int(e): expert_weights(wl, layer, int(e)) for e in np.unique(ids)}
-        y, _, _ = oracle.moe_layer(wl.n_experts, wl.top_k, wl.hidden, wl.ffn, experts,
+        y, _, _ = oracle.moe_layer(wl.n_experts, wl.top_k, wl.hidden, wl.ffn, picked_weights(wl, layer, ids),
                                    np.asarray(xs_step[layer], np.float64), logits=z)
         out.append(y)
     return np.stack(out)
+
+
+def tile_edge_tokens(ids: np.ndarray, tile_rows=(64, 128)) -> np.ndarray:
+    """Tokens of the first and last pair of every (expert, tile) of a prompt pass, for each tile height:
+    the pairs (token t, pick i) numbered t * k + i, stably sorted by expert, cut per expert into tiles."""
+    k = ids.shape[1]
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=int(flat.max()) + 1)
+    starts = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    pos = []
+    for bm in tile_rows:
+        for e in np.nonzero(counts)[0]:
+            for m0 in range(0, int(counts[e]), bm):
+                first = starts[e] + m0
+                pos += [first, first + min(bm, int(counts[e]) - m0) - 1]
+    return np.unique(order[np.asarray(pos, np.int64)] // k)

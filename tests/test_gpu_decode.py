@@ -37,7 +37,9 @@ def _compare_policy(d: Decode, pol, st_gpu, st_orc, layers):
 
 def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_alloc=moe.MOE_HOST_COHERENT,
                 capture_picks=None, copies=None, pool="layer", swaps=(0, 0), cold_exec=moe.MOE_COLD_GPU,
-                cpu_threads=0):
+                cpu_threads=0, repeats=None):
+    """repeats: a list that receives, per step, how many admissions took a slot that an earlier admission
+    of the same step (same pool) had already taken."""
     d = Decode(wl, slots=slots, seed=seed, host_alloc=host_alloc, capture_picks=capture_picks, pool=pool,
                swaps_per_step=swaps[0], swap_lead=swaps[1], cold_exec=cold_exec, cpu_threads=cpu_threads)
     if cold_exec == moe.MOE_COLD_CPU:
@@ -72,6 +74,10 @@ def _run_decode(wl: Workload, slots: int, check_every: int, seed=True, host_allo
         st_g = moe.moe_cache_step(d.ctx)
         st_o = pol.step()
         _compare_policy(d, pol, st_g, st_o, range(L))
+        if repeats is not None:
+            adm = pol.last_admissions()
+            keys = [(0 if pool == "global" else int(a[0]), int(a[2])) for a in adm]
+            repeats.append(len(keys) - len(set(keys)))
         assert 0 <= st_g["copied_pcie_bytes"] <= st_g["copied_bytes"] == st_o["admissions"] * d.B
         if copies is not None:
             copies["copied"] = copies.get("copied", 0) + st_g["copied_bytes"]
@@ -498,3 +504,53 @@ def test_routing_exact_ties_and_signed_zeros(E, k):
                                    x32.astype(np.float64), logits=z)
     assert token_rel_err(y.cpu().numpy(), y_ref) < TOL
     d.close()
+
+
+def test_fused_path_slot_taken_twice_in_one_step_copies_from_capture():
+    # 4 tokens (the fused routing + gate/up path), every pick may capture, every miss admitted, 3 slots per
+    # layer: a step admits more experts than a layer has slots, so one copy list holds two transfers to one
+    # slot (only the later one must land), and every promotion copies a capture block, none crosses PCIe
+    wl = Workload("decode-e32k4-h256f512-l2-b4-admit1-s3", 117, 2, 32, 4, 256, 512, tokens=4, steps=8,
+                  zipf_s=0.6, slots=3, admit_misses=1)
+    copies, repeats = {}, []
+    _run_decode(wl, slots=3, check_every=1, capture_picks=16, copies=copies, repeats=repeats)
+    print("repeated slots per step", repeats, "promotion bytes", copies)
+    assert sum(repeats) > 0
+    assert copies["copied"] > 0 and copies["pcie"] == 0
+
+
+def test_second_forward_of_a_layer_in_a_step_leaves_no_stale_capture():
+    # A fused forward captures expert 3 (cold, second miss) into capture block 0; a second forward of the
+    # same layer in the same step (8 tokens: routed by the routing kernel) puts expert 5 at pick 0, and 5 is
+    # admitted by its second miss. Its promotion must not copy block 0 (expert 3's bytes) into 5's slot.
+    E, k, H, F = 16, 2, 256, 512
+    wl = Workload("decode-e16k2-h256f512-l1-twice", 118, 1, E, k, H, F, tokens=8, zipf_s=1.1, slots=4)
+    d = Decode(wl, slots=4, seed=False, max_batch=8, capture_picks=8 * k)
+    try:
+        def logits(rows):
+            z = np.zeros((len(rows), E), np.float32)
+            for t, (a, b) in enumerate(rows):
+                z[t, a], z[t, b] = 10.0, 9.0
+            return z
+
+        def forward(rows, step):
+            z = logits(rows)
+            x32 = activations(wl, step, tokens=len(rows))
+            y = torch.empty((len(rows), H), dtype=torch.float32, device="cuda")
+            moe.moe_forward(d.ctx, 0, len(rows), _dev(x32), _dev(z), y)
+            return x32, z, y
+
+        forward([(3, 5)], 0)
+        st = moe.moe_cache_step(d.ctx)
+        assert st["misses"] == 2 and st["admissions"] == 0
+        forward([(3, 7)], 1)                                  # 3 captured at pick 0
+        forward([(5, 9)] + [(10 + t % 6, 2) for t in range(7)], 2)  # same layer, same step: pick 0 is 5
+        st = moe.moe_cache_step(d.ctx)
+        table = moe.moe_get_slot_table(d.ctx, 0, E)
+        assert table[5] >= 0 and table[3] < 0, table
+        x32, z, y = forward([(5, 3)], 3)                      # 5 from its new slot
+        y_ref, _, _ = oracle.moe_layer(E, k, H, F, d.experts(0, [5, 3]), x32.astype(np.float64), logits=z)
+        err = token_rel_err(y.cpu().numpy(), y_ref)
+        assert err < TOL, err
+    finally:
+        d.close()
