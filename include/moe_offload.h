@@ -62,6 +62,8 @@ extern "C" {
 #define MOE_E_HIP        (-3) /* a HIP runtime call failed                   */
 #define MOE_E_STATE      (-4) /* call not allowed in the current state       */
 #define MOE_E_CAPTURING  (-5) /* call not allowed while the stream captures  */
+#define MOE_E_RANGE      (-6) /* moe_prefill: a value left the range of the
+                                 prompt pass's fp16 operands                 */
 
 #define MOE_Q4_32_F16     1   /* the only weight format */
 
@@ -303,7 +305,14 @@ MOE_API int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
  * copy runs on a stream the library owns, beside the GEMMs of the resident
  * experts; the pass waits for it before it returns. The cache policy is
  * untouched: no stamps, no miss log, no counts, no clock. Synchronises the
- * stream; not capturable (MOE_E_CAPTURING). */
+ * stream; not capturable (MOE_E_CAPTURING).
+ * Precision: the GEMMs run on fp16 operands with fp32 accumulation (weights
+ * d * (q - 8) rounded once to fp16). Each token's row of x is scaled by a
+ * power of two so its largest magnitude lies in [4, 8) before the cast, and
+ * the SwiGLU output by the square of that factor; both are undone exactly in
+ * fp32. If a scaled SwiGLU output is not finite or exceeds 65504 (non-finite
+ * activations, or weights far beyond Q4 scales), the pass returns
+ * MOE_E_RANGE and y is not valid. */
 MOE_API int moe_prefill(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
                 const float* x, const float* logits, float* y, uint32_t flags);
 

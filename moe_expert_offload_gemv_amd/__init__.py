@@ -23,6 +23,7 @@ MOE_E_NOMEM = -2
 MOE_E_HIP = -3
 MOE_E_STATE = -4
 MOE_E_CAPTURING = -5
+MOE_E_RANGE = -6
 MOE_Q4_32_F16 = 1
 MOE_ACCUMULATE = 1
 MOE_MAX_SWAP_LEAD = 8

@@ -172,7 +172,7 @@ hipError_t launch_host_combine(const HostCombineArgs& a, const Launch& l);
 // prompt pass (prefill_kernels.hip)
 
 struct GemmArgs {
-  const _Float16* a16;          // A rows [rows][K] fp16 in operand order (convert_rows layout)
+  const _Float16* a16;          // A rows [rows][K] fp16 in operand order (scale_rows layout)
   const int32_t* arow;          // gate/up: perm (A row = arow[pos] / arow_div); down: nullptr (A row = pos)
   int32_t arow_div;
   const int4* tiles;            // (expert, first sorted position, rows <= BM, 0)
@@ -186,6 +186,10 @@ struct GemmArgs {
   const uint16_t* sclT;         // 64-row tiles: the pass's block scales transposed, expert e at
   int64_t sclT_per_expert;      //   sclT + e * sclT_per_expert: gate [H/32][F], up [H/32][F], down
                                 //   [F/32][H]; 128-row tiles: nullptr (scales from the expert's planes)
+  const int32_t* perm;          // [P] sorted position -> pair; token of a pair = pair / perm_div
+  int32_t perm_div;
+  const int32_t* sig;           // [T] exponent s of each token's row scale 2^s (scale_rows)
+  uint32_t* range_flag;         // gate/up: set when a scaled h is not finite or above 65504
   int32_t work, work_padded;    // set by the launcher: work items, padded to a multiple of 8
 };
 // Stable counting sort of pairs by expert (E <= 4096). launch_expert_counts
@@ -199,7 +203,9 @@ hipError_t launch_expert_counts(const int32_t* ids, int32_t n_pairs, int32_t E, 
 hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E, const int32_t* offsets,
                                  const int32_t* ccount, const int32_t* rank, int32_t* perm, int32_t* inv,
                                  hipStream_t s);
-hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, hipStream_t s);
+// fp32 rows [rows][K] -> fp16 rows in the GEMM's operand order, row r scaled
+// by 2^sig[r] so its largest magnitude lies in [4, 8) (sig written here)
+hipError_t launch_scale_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, int32_t* sig, hipStream_t s);
 // Scale planes of the experts e = experts[0..n) with eaddr[e] != nullptr,
 // transposed into out + e * per_expert (layout of GemmArgs::sclT);
 // per_expert = sclT_elements(lay).

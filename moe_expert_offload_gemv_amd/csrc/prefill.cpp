@@ -70,7 +70,10 @@ struct Prefill {
   int2* items[2] = {nullptr, nullptr};    // [max_items] work lists of the gate/up and down GEMMs
   const uint8_t** eaddr = nullptr;  // [E]
   int32_t* stage = nullptr;     // [E] experts copied into the staging blocks, in block order
-  _Float16* x16 = nullptr;      // [T][H] activations, fp16 in operand order
+  _Float16* x16 = nullptr;      // [T][H] activations, fp16 in operand order, row t scaled by 2^sig[t]
+  int32_t* sig = nullptr;       // [T] row scale exponents
+  uint32_t* range_flag = nullptr;    // set by the gate/up GEMM when a scaled h leaves the fp16 range
+  uint32_t* h_range_flag = nullptr;  // pinned copy read after the pass
   _Float16* h16 = nullptr;      // [P][F] SwiGLU outputs, fp16 in operand order
   float* ypair = nullptr;       // [P][H]
   uint16_t* sclT = nullptr;     // [E][sclT_elements]: the pass's block scales, transposed
@@ -121,6 +124,8 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = dev((void**)&p->eaddr, sizeof(uint8_t*) * E, "prefill addresses")) ||
       (rc = dev((void**)&p->stage, sizeof(int32_t) * E, "prefill staging list")) ||
       (rc = dev((void**)&p->x16, sizeof(_Float16) * T * c->H, "prefill x fp16")) ||
+      (rc = dev((void**)&p->sig, sizeof(int32_t) * T, "prefill row scales")) ||
+      (rc = dev((void**)&p->range_flag, sizeof(uint32_t), "prefill range flag")) ||
       (rc = dev((void**)&p->h16, sizeof(_Float16) * P * c->F, "prefill h fp16")) ||
       (rc = dev((void**)&p->ypair, sizeof(float) * P * c->H, "prefill pair outputs")) ||
       (rc = dev((void**)&p->sclT, sizeof(uint16_t) * E * moe::sclT_elements(c->lay), "prefill transposed scales")))
@@ -132,7 +137,8 @@ int moe_prefill_alloc(moe_ctx* c) {
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_items[0], sizeof(int2) * p->max_items, pin, "prefill item staging")) ||
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_items[1], sizeof(int2) * p->max_items, pin, "prefill item staging")) ||
       (rc = moe_ctx_host_alloc(c, (void**)&p->h_eaddr, sizeof(uint8_t*) * E, pin, "prefill address staging")) ||
-      (rc = moe_ctx_host_alloc(c, (void**)&p->h_stage, sizeof(int32_t) * E, pin, "prefill staging list")))
+      (rc = moe_ctx_host_alloc(c, (void**)&p->h_stage, sizeof(int32_t) * E, pin, "prefill staging list")) ||
+      (rc = moe_ctx_host_alloc(c, (void**)&p->h_range_flag, sizeof(uint32_t), pin, "prefill range flag")))
     return rc;
   p->tile_begin.assign(E + 1, 0);
   p->direct.reserve(E);
@@ -321,9 +327,11 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
     if (timed) PF_HIP(c, hipEventRecord(p->stage_timing[1], p->copy_stream));
   }
 
-  // 5. stable sort of the pairs by expert; activations as fp16 rows in operand order
+  // 5. stable sort of the pairs by expert; activations as fp16 rows in
+  // operand order, each row scaled by a power of two into the fp16 range
   PF_HIP(c, moe::launch_expert_scatter(p->ids, P, E, p->offsets, p->ccount, p->rank, p->perm, p->inv, s));
-  PF_HIP(c, moe::launch_convert_rows(x, T, H, p->x16, s));
+  PF_HIP(c, moe::launch_scale_rows(x, T, H, p->x16, p->sig, s));
+  PF_HIP(c, hipMemsetAsync(p->range_flag, 0, sizeof(uint32_t), s));
 
   // 6. per group (a chunk once its copy has landed): short tiles (few rows
   // per expert) are bound by weight fetches, so their GEMMs get the block
@@ -339,6 +347,7 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   g.h16 = p->h16;
   g.sclT = tscl ? p->sclT : nullptr;
   g.sclT_per_expert = moe::sclT_elements(c->lay);
+  g.perm = p->perm, g.perm_div = k, g.sig = p->sig, g.range_flag = p->range_flag;
   moe::GemmArgs d = g;
   d.a16 = p->h16, d.arow = nullptr, d.arow_div = 1;
   d.K = F, d.N = H;
@@ -367,8 +376,14 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
 
   // 7. weighted combine in pick order
   PF_HIP(c, moe::launch_combine_pairs(p->ypair, p->inv, p->w, T, k, H, y, (flags & MOE_ACCUMULATE) ? 1 : 0, s));
+  PF_HIP(c, hipMemcpyAsync(p->h_range_flag, p->range_flag, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
   PF_HIP(c, hipStreamSynchronize(s));  // the pass is over (it waited for every chunk): the staging blocks are free again
   p->last_layer = layer;
+  if (*p->h_range_flag)
+    return moe_ctx_fail(c, MOE_E_RANGE,
+                        "prefill: a SwiGLU output left the fp16 operand range after the row's power-of-two scaling "
+                        "(non-finite activations, or weights too large for the fp16 prompt-pass GEMM); y is not "
+                        "valid");
 
   if (timed) {
     float ms[kTimed] = {};

@@ -10,12 +10,23 @@
 //   chunk_scan_kernel        per expert: where each chunk's pairs start among the
 //                            expert's pairs, and the expert's pair count
 //   expert_scatter_kernel    stable counting sort: perm[pos] = pair, inv[pair] = pos
-//   convert_rows_kernel      fp32 rows -> fp16 rows in operand order
+//   scale_rows_kernel        fp32 rows -> fp16 rows in operand order, each row
+//                            scaled by a power of two (its exponent kept)
 //   grouped_gemm_kernel      per tile of one expert: gate/up -> h = silu(g) * u
 //                            (fp16 rows in operand order), or down -> y_pair (fp32)
 //   combine_pairs_kernel     y[t] = sum_i w_i y_pair[inv[t, i]] in pick order
 //   stage_experts_kernel     the pass's non-resident experts, read zero-copy
 //                            from pinned host memory into HBM staging blocks
+//
+// Range: fp16 holds 6.1e-5 .. 65504 at full precision, while the API takes
+// any fp32 activations. Each token's row is therefore scaled by 2^s (exact)
+// so that its largest magnitude lies in [4, 8) before the cast; the gate/up
+// epilogue undoes 2^s on the accumulators (exact) and stores h scaled by
+// 2^(2s), since silu(g) * u grows like the square of the token's scale in
+// both of its regimes (silu(g) ~ g for large positive g, ~ g / 2 near 0);
+// the down epilogue multiplies by 2^(-2s). A scaled h that is not finite or
+// exceeds 65504 sets a flag that fails the pass (weights far larger than the
+// blocks' fp16 scales admit in practice).
 //
 // MFMA form: v_mfma_f32_16x16x32_f16 with fp32 accumulation straight through
 // K. The weight operand is built in registers from the quant blocks as
@@ -225,25 +236,56 @@ __global__ __launch_bounds__(256) void expert_scatter_kernel(const int32_t* ids,
   inv[i] = pos;
 }
 
-// fp32 rows [R][K] -> fp16 rows [R][K] in operand order; one thread per 8
-// stored halves, which come from 8 consecutive elements (in ord8 order)
-__global__ __launch_bounds__(256) void convert_rows_kernel(const float* src, int64_t n_oct, uint4* dst) {
-  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (o >= n_oct) return;
-  const int64_t step = o >> 3;       // K % 64 == 0: steps never straddle rows
-  const int oq = (int)(o & 7);       // stored positions 8*oq .. 8*oq+7
-  const int h = oq >> 2, g = oq & 3;
-  const int e0 = 32 * (g >> 1) + 16 * h + 8 * (g & 1);
-  const float4* s4 = reinterpret_cast<const float4*>(src + step * KS + e0);
-  const float4 a = s4[0], b = s4[1];
-  const float v[8] = {a.x, a.z, a.y, a.w, b.x, b.z, b.y, b.w};  // ord8
-  uint32_t u[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const f16x2_t t = {(_Float16)v[2 * j], (_Float16)v[2 * j + 1]};
-    __builtin_memcpy(&u[j], &t, 4);
+// Exponent s of a row's scale 2^s: its largest magnitude m times 2^s lies in
+// [4, 8) (m = f * 2^e with f in [0.5, 1): s = 3 - e). A zero or non-finite m
+// keeps the row as it is.
+__device__ __forceinline__ int row_scale_exp(float m) {
+  if (!(m > 0.f) || !(m <= 3.4028235e38f)) return 0;
+  int e;
+  (void)frexpf(m, &e);
+  return 3 - e;
+}
+
+// fp32 rows [R][K] -> fp16 rows [R][K] in operand order, row r scaled by
+// 2^sig[r] (sig[r] written here). One work-group per row: the row's largest
+// magnitude first, then each thread converts 8 stored halves at a time,
+// which come from 8 consecutive elements (in ord8 order).
+__global__ __launch_bounds__(256) void scale_rows_kernel(const float* src, int32_t K, uint4* dst, int32_t* sig) {
+  __shared__ float s_max[4];
+  const int64_t r = blockIdx.x;
+  const float* row = src + r * K;
+  const int n_oct = K / 8;
+  float m = 0.f;
+  for (int o = threadIdx.x; o < n_oct; o += 256) {
+    const float4 a = reinterpret_cast<const float4*>(row)[2 * o], b = reinterpret_cast<const float4*>(row)[2 * o + 1];
+    m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                       fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w)))));
+    // a NaN compares false everywhere: keep it visible as +inf
+    if (a.x != a.x || a.y != a.y || a.z != a.z || a.w != a.w || b.x != b.x || b.y != b.y || b.z != b.z || b.w != b.w)
+      m = __builtin_inff();
   }
-  dst[o] = make_uint4(u[0], u[1], u[2], u[3]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const int e = row_scale_exp(fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])));
+  if (threadIdx.x == 0) sig[r] = e;
+  for (int o = threadIdx.x; o < n_oct; o += 256) {
+    const int step = o >> 3;      // K % 64 == 0: steps never straddle rows
+    const int oq = o & 7;         // stored positions 8*oq .. 8*oq+7
+    const int h = oq >> 2, g = oq & 3;
+    const int e0 = 32 * (g >> 1) + 16 * h + 8 * (g & 1);
+    const float4* s4 = reinterpret_cast<const float4*>(row + step * KS + e0);
+    const float4 a = s4[0], b = s4[1];
+    const float v[8] = {a.x, a.z, a.y, a.w, b.x, b.z, b.y, b.w};  // ord8
+    uint32_t u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16x2_t t = {(_Float16)ldexpf(v[2 * j], e), (_Float16)ldexpf(v[2 * j + 1], e)};
+      __builtin_memcpy(&u[j], &t, 4);
+    }
+    dst[r * n_oct + o] = make_uint4(u[0], u[1], u[2], u[3]);
+  }
 }
 
 // One workgroup computes a BM-row tile of one expert's pairs against
@@ -390,7 +432,17 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
       }
   }
 
-  // epilogue: lane holds rows s*16 + g*4 + i of feature n0 + wave*WN + ns*16 + lane%16
+  // epilogue: lane holds rows s*16 + g*4 + i of feature n0 + wave*WN + ns*16 + lane%16.
+  // Row scale: the token's activations entered as x * 2^sx
+  int sx[RB][4];
+#pragma unroll
+  for (int s = 0; s < RB; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = s * 16 + g * 4 + i;
+      sx[s][i] = r < rows ? a.sig[a.perm[pos0 + r] / a.perm_div] : 0;
+    }
+  bool bad = false;
 #pragma unroll
   for (int ns = 0; ns < NSUB; ++ns) {
     const int bn = n0 + wave * WN + ns * 16 + (lane & 15);
@@ -402,8 +454,13 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = s * 16 + g * 4 + i;
-          if (r < rows)
-            a.h16[(int64_t)(pos0 + r) * N + col] = (_Float16)(silu(acc[0][ns][s][i]) * acc[NMAT - 1][ns][s][i]);
+          if (r < rows) {
+            // g and u at the token's own scale, h stored at 2^(2 sx)
+            const float gv = ldexpf(acc[0][ns][s][i], -sx[s][i]), uv = ldexpf(acc[NMAT - 1][ns][s][i], -sx[s][i]);
+            const float hv = ldexpf(silu(gv) * uv, 2 * sx[s][i]);
+            bad |= !(fabsf(hv) <= 65504.f);
+            a.h16[(int64_t)(pos0 + r) * N + col] = (_Float16)hv;
+          }
         }
     } else {
 #pragma unroll
@@ -411,10 +468,11 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = s * 16 + g * 4 + i;
-          if (r < rows) a.y[(int64_t)(pos0 + r) * N + bn] = acc[0][ns][s][i];
+          if (r < rows) a.y[(int64_t)(pos0 + r) * N + bn] = ldexpf(acc[0][ns][s][i], -2 * sx[s][i]);
         }
     }
   }
+  if (MODE == 0 && __ballot(bad) != 0 && lane == 0) atomicOr(a.range_flag, 1u);
 }
 
 // Scale planes [rows][K/32] (fp16) of the experts with eaddr[e] set ->
@@ -538,11 +596,10 @@ hipError_t launch_expert_scatter(const int32_t* ids, int32_t n_pairs, int32_t E,
                      sort_chunks(n_pairs), offsets, ccount, rank, perm, inv);
   return hipGetLastError();
 }
-hipError_t launch_convert_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, hipStream_t s) {
-  if (K % KS || rows <= 0) return hipErrorInvalidValue;
-  const int64_t n_oct = rows * (K / 8);
-  hipLaunchKernelGGL(convert_rows_kernel, dim3((unsigned)((n_oct + 255) / 256)), dim3(256), 0, s, src, n_oct,
-                     reinterpret_cast<uint4*>(dst));
+hipError_t launch_scale_rows(const float* src, int64_t rows, int32_t K, _Float16* dst, int32_t* sig, hipStream_t s) {
+  if (K % KS || rows <= 0 || rows > 0x7fffffff || ((uintptr_t)src & 15)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scale_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, src, K, reinterpret_cast<uint4*>(dst),
+                     sig);
   return hipGetLastError();
 }
 int64_t sclT_elements(const ExpertLayout& lay) {

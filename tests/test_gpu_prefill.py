@@ -18,10 +18,13 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _prefill_check(wl: Workload, slots: int, sample=None, flags=0, pool="layer", seed=True):
+def _prefill_check(wl: Workload, slots: int, sample=None, flags=0, pool="layer", seed=True, x_scale=None):
+    """x_scale: a factor for every activation, or an array of one factor per token."""
     d = Decode(wl, slots=slots, max_batch=1, max_prefill=wl.tokens, pool=pool, seed=seed)
     T, H = wl.tokens, wl.hidden
     x32 = activations(wl, 0, tokens=T)
+    if x_scale is not None:
+        x32 = (x32 * np.asarray(x_scale, np.float32).reshape(-1, 1)).astype(np.float32)
     z = zipf_logits(wl, steps=1, tokens=T)[0, 0]
     x = _dev(x32)
     y = _dev(np.full((T, H), 0.25, np.float32)) if flags else torch.empty((T, H), dtype=torch.float32, device="cuda")
@@ -215,3 +218,48 @@ def test_preheat_matches_the_oracle_and_serves_decode(pool):
         for layer in range(2):
             assert np.array_equal(moe.moe_get_slot_table(d.ctx, layer, 32), pol.tables()["table"][layer])
     d.close()
+
+
+@pytest.mark.parametrize("scale", [1e3, 1e-4, "mixed"])
+def test_prefill_activations_far_from_unit_scale(scale):
+    # fp16 operands: each token's row is scaled by a power of two into [4, 8) before the cast and the
+    # SwiGLU output by its square, so activations 1e3 or 1e-4 times N(0, 1) (h ~ 1e6 or 1e-9 unscaled, past
+    # either end of fp16) keep the same relative error; "mixed" gives every token its own magnitude
+    wl = Workload("prefill-e64k8-h2048f1024-t300-scaled", 211, 1, 64, 8, 2048, 1024, tokens=300, zipf_s=1.1)
+    if scale == "mixed":
+        scale = 10.0 ** np.random.default_rng(5).uniform(-5, 4, size=wl.tokens)
+    err, prof = _prefill_check(wl, slots=26, sample=64, x_scale=scale)
+    assert prof["prefill_staged"] > 0
+
+
+def test_prefill_reports_values_beyond_the_fp16_operand_range():
+    # block scales of 1000 (q - 8 times 1000 still fits fp16, but the SwiGLU output grows ~1e10 even after
+    # the row scaling): the pass fails with MOE_E_RANGE instead of returning infinities
+    wl = Workload("prefill-e8k2-h256f512-t16-range", 212, 1, 8, 2, 256, 512, tokens=16, zipf_s=1.1)
+    from workload import layer_weights
+
+    g, u, dn = (m.copy() for m in layer_weights(wl, 0))
+    big = np.array([1000.0], "<f2").view(np.uint8)
+    for m in (g, u, dn):  # experts 0..3 only
+        m[:4, ..., 0], m[:4, ..., 1] = big[0], big[1]
+    ctx = moe.moe_create(1, 8, 2, 256, 512, pool_budget_bytes=8 * wl.expert_bytes, max_batch_tokens=1,
+                         max_prefill_tokens=16)
+    try:
+        moe.moe_register_layer(ctx, 0, g, u, dn)
+        moe.moe_seed(ctx, None)
+        x32 = activations(wl, 0, tokens=16)
+        x = _dev(x32)
+        z = zipf_logits(wl, steps=1, tokens=16)[0, 0]
+        z[0, 0] = 50.0  # token 0 picks expert 0
+        y = torch.empty_like(x)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_prefill(ctx, 0, 16, x, _dev(z), y)
+        assert ei.value.code == moe.MOE_E_RANGE
+        # a pass that routes to experts 4..7 only is valid again (the flag is cleared per pass)
+        z[:, :4] = -50.0
+        moe.moe_prefill(ctx, 0, 16, x, _dev(z), y)
+        experts = {e: (g[e], u[e], dn[e]) for e in range(4, 8)}
+        y_ref, _, _ = oracle.moe_layer(8, 2, 256, 512, experts, x32.astype(np.float64), logits=z)
+        assert token_rel_err(y.cpu().numpy(), y_ref) < TOL
+    finally:
+        moe.moe_destroy(ctx)
