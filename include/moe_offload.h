@@ -71,6 +71,8 @@ extern "C" {
 
 #define MOE_MAX_SWAP_LEAD 8   /* largest moe_config.swap_lead                 */
 
+#define MOE_STATIC_SCRATCH_BYTES 16777216 /* moe_forward_static_scratch's array */
+
 /* Where the cold picks of a decode forward are computed (moe_config.cold_exec). */
 #define MOE_COLD_GPU      0   /* the GPU reads the pinned weights zero-copy  */
 #define MOE_COLD_CPU      1   /* host threads compute them beside the GPU    */
@@ -294,6 +296,26 @@ MOE_API int moe_seed(moe_ctx* ctx, const uint32_t* freq);
  * 10 s, y leaves those picks out and the step's moe_cache_step returns
  * MOE_E_HIP. */
 MOE_API int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
+                const float* x, const float* logits, float* y,
+                int32_t* ids, float* w, uint32_t flags);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as moe_forward, same arguments, results and policy side effects,
+ * with its per-call scratch (pick ids, weights, addresses and tags, the h
+ * rows, per-pick outputs, the grouping by expert) in a static device array of
+ * 16 MiB (MOE_STATIC_SCRATCH_BYTES) instead of the context's buffers. The
+ * array is the library's, one per device, from the first moe_create on that
+ * device until the process ends; moe_create takes its address. Every call on
+ * a device shares that device's array and leaves its contents behind
+ * (nothing in it needs to start at zero): calls that overlap on one device,
+ * on any streams or contexts, race. A forward needs
+ *   256-byte-aligned parts for T*k picks: 17 bytes per pick plus 4*(F + H)
+ *   bytes per pick for h and the per-pick outputs,
+ * MOE_E_INVAL if that exceeds the array (for example T = 32, k = 8 at
+ * H = 4096, F = 1536 needs 5.8 MB; T = 256 there does not fit). Calls no
+ * allocating routine; capturable like moe_forward. */
+MOE_API int moe_forward_static_scratch(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
                 const float* x, const float* logits, float* y,
                 int32_t* ids, float* w, uint32_t flags);
 

@@ -27,6 +27,7 @@ MOE_E_RANGE = -6
 MOE_Q4_32_F16 = 1
 MOE_ACCUMULATE = 1
 MOE_MAX_SWAP_LEAD = 8
+MOE_STATIC_SCRATCH_BYTES = 16777216
 MOE_COLD_GPU = 0
 MOE_COLD_CPU = 1
 MOE_HOST_COHERENT = 0
@@ -38,6 +39,7 @@ EXPORTED = [
     "moe_expert_bytes", "moe_create", "moe_destroy", "moe_register_layer", "moe_register_router", "moe_seed",
     "moe_forward", "moe_prefill", "moe_cache_step", "moe_get_info", "moe_get_slot_table", "moe_get_stamps",
     "moe_get_miss_log", "moe_get_counts", "moe_last_error", "moe_profile", "moe_preheat", "moe_measure_read_bandwidth",
+    "moe_forward_static_scratch",
 ]
 
 
@@ -108,6 +110,7 @@ def lib():
             "moe_register_router": (C.c_int, [vp, i32, vp]),
             "moe_seed": (C.c_int, [vp, vp]),
             "moe_forward": (C.c_int, [vp, i32, i32, vp, vp, vp, vp, vp, u32]),
+            "moe_forward_static_scratch": (C.c_int, [vp, i32, i32, vp, vp, vp, vp, vp, u32]),
             "moe_prefill": (C.c_int, [vp, i32, i32, vp, vp, vp, u32]),
             "moe_cache_step": (C.c_int, [vp, C.POINTER(moe_step_stats)]),
             "moe_get_info": (C.c_int, [vp, C.POINTER(moe_info)]),
@@ -217,6 +220,12 @@ def moe_seed(ctx, freq=None) -> None:
 def moe_forward(ctx, layer: int, n_tokens: int, x, logits, y, ids=None, w=None, flags: int = 0) -> None:
     _check(ctx, lib().moe_forward(ctx, layer, n_tokens, _dptr(x), _dptr(logits), _dptr(y), _dptr(ids), _dptr(w),
                                   flags))
+
+
+def moe_forward_static_scratch(ctx, layer: int, n_tokens: int, x, logits, y, ids=None, w=None,
+                               flags: int = 0) -> None:
+    _check(ctx, lib().moe_forward_static_scratch(ctx, layer, n_tokens, _dptr(x), _dptr(logits), _dptr(y),
+                                                 _dptr(ids), _dptr(w), flags))
 
 
 def moe_prefill(ctx, layer: int, n_tokens: int, x, logits, y, flags: int = 0) -> None:

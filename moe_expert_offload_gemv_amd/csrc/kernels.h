@@ -239,4 +239,28 @@ struct CopyList {
 };
 hipError_t launch_copy_list(const CopyList& l, hipStream_t s);
 
+// Per-call scratch of a decode forward: device memory beyond its inputs and
+// outputs, carved from one block at 256-byte boundaries for P picks.
+struct ForwardScratch {
+  int32_t* ids;          // [P] expert of each pick
+  float* w;              // [P] routing weight
+  const uint8_t** addr;  // [P] expert base address
+  uint8_t* kind;         // [P] kHot / kCold (+ kCaptured)
+  float* h;              // [P][F] SwiGLU outputs
+  float* ypick;          // [P][H] down outputs of picks another launch combines
+  int4* groups;          // [P] grouped decode: (expert, start, picks, 0)
+  int32_t* order;        // [P] picks by expert
+  int32_t* n_groups;     // [1]
+};
+int64_t forward_scratch_bytes(int64_t P, int32_t H, int32_t F);
+ForwardScratch forward_scratch_carve(uint8_t* base, int64_t P, int32_t H, int32_t F);
+
+// The forward's scratch in a static device array (scratch.hip), for the
+// entry point that allocates nothing. static_scratch_init takes the array's
+// address on `device`, which must be current; static_scratch returns it
+// (null before init).
+constexpr int64_t kStaticScratchBytes = 16ll << 20;
+hipError_t static_scratch_init(int device);
+uint8_t* static_scratch(int device);
+
 }  // namespace moe

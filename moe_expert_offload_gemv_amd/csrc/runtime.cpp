@@ -222,16 +222,16 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ctrl, sizeof(Ctrl), "control"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_host_base, sizeof(uint8_t*) * L, "host bases"))) return fail(rc);
   const int64_t P = (int64_t)k.max_batch_tokens * K;
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ids, sizeof(int32_t) * P, "ids"))) return fail(rc);
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_w, sizeof(float) * P, "weights"))) return fail(rc);
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_addr, sizeof(uint8_t*) * P, "addresses"))) return fail(rc);
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_h, sizeof(float) * P * c->F, "h"))) return fail(rc);
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_kind, P, "pick tags"))) return fail(rc);
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ypick, sizeof(float) * P * c->H, "pick outputs"))) return fail(rc);
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_groups, sizeof(int4) * P, "pick groups")) ||
-      (rc = moe_ctx_dev_alloc(c, (void**)&c->d_order, sizeof(int32_t) * P, "picks by expert")) ||
-      (rc = moe_ctx_dev_alloc(c, (void**)&c->d_ngroups, sizeof(int32_t), "group count")))
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_scratch, (size_t)moe::forward_scratch_bytes(P, c->H, c->F),
+                              "forward scratch")))
     return fail(rc);
+  c->sc = moe::forward_scratch_carve(c->d_scratch, P, c->H, c->F);
+  // the allocation-free forward's static scratch: its address on this device,
+  // taken once; without it only moe_forward_static_scratch is unavailable
+  if (hipError_t e = moe::static_scratch_init(c->device); e != hipSuccess) {
+    (void)hipGetLastError();
+    c->static_scratch_err = std::string("hipGetSymbolAddress of the static scratch: ") + hipGetErrorString(e);
+  }
   c->capture_picks = k.capture_picks;
   if (c->capture_picks > 0) {
     if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_capture, (size_t)(L * c->capture_picks * c->B), "capture blocks")))
@@ -503,14 +503,73 @@ static int host_exec_create(moe_ctx* c) {
   return MOE_OK;
 }
 
+static_assert(moe::kStaticScratchBytes == MOE_STATIC_SCRATCH_BYTES, "the header states the static scratch size");
+
+// Layout of a forward's scratch for P picks: every part at a 256-byte boundary.
+namespace moe {
+namespace {
+int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
+}  // namespace
+int64_t forward_scratch_bytes(int64_t P, int32_t H, int32_t F) {
+  return up256(4 * P) + up256(4 * P) + up256(8 * P) + up256(P) + up256(4 * P * F) + up256(4 * P * H) +
+         up256(16 * P) + up256(4 * P) + up256(4);
+}
+ForwardScratch forward_scratch_carve(uint8_t* base, int64_t P, int32_t H, int32_t F) {
+  ForwardScratch s{};
+  int64_t o = 0;
+  auto take = [&](int64_t bytes) {
+    uint8_t* p = base + o;
+    o += up256(bytes);
+    return p;
+  };
+  s.ids = reinterpret_cast<int32_t*>(take(4 * P));
+  s.w = reinterpret_cast<float*>(take(4 * P));
+  s.addr = reinterpret_cast<const uint8_t**>(take(8 * P));
+  s.kind = take(P);
+  s.h = reinterpret_cast<float*>(take(4 * P * F));
+  s.ypick = reinterpret_cast<float*>(take(4 * P * H));
+  s.groups = reinterpret_cast<int4*>(take(16 * P));
+  s.order = reinterpret_cast<int32_t*>(take(4 * P));
+  s.n_groups = reinterpret_cast<int32_t*>(take(4));
+  return s;
+}
+}  // namespace moe
+
 static int check_act(moe_ctx* c, const void* p, const char* what) {
   if (!p || ((uintptr_t)p & 15)) return moe_ctx_fail(c, MOE_E_INVAL, "%s must be a non-null 16-byte aligned pointer", what);
   return MOE_OK;
 }
 
+static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float* x, const float* logits, float* y,
+                        int32_t* ids, float* w, uint32_t flags, const moe::ForwardScratch& sc);
+
 extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const float* x, const float* logits,
                            float* y, int32_t* ids, float* w, uint32_t flags) {
   if (!c) return MOE_E_INVAL;
+  return forward_impl(c, layer, n_tokens, x, logits, y, ids, w, flags, c->sc);
+}
+
+extern "C" int moe_forward_static_scratch(moe_ctx* c, int32_t layer, int32_t n_tokens, const float* x,
+                                          const float* logits, float* y, int32_t* ids, float* w, uint32_t flags) {
+  if (!c) return MOE_E_INVAL;
+  if (n_tokens < 1 || n_tokens > c->cfg.max_batch_tokens)
+    return moe_ctx_fail(c, MOE_E_INVAL, "forward: n_tokens %d outside 1..%d", n_tokens, c->cfg.max_batch_tokens);
+  const int64_t P = (int64_t)n_tokens * c->k;
+  const int64_t need = moe::forward_scratch_bytes(P, c->H, c->F);
+  if (need > moe::kStaticScratchBytes)
+    return moe_ctx_fail(c, MOE_E_INVAL,
+                        "forward_static_scratch: %d tokens x top-%d at hidden %d, ffn %d need %lld bytes of scratch, "
+                        "more than the static %lld",
+                        n_tokens, c->k, c->H, c->F, (long long)need, (long long)moe::kStaticScratchBytes);
+  uint8_t* base = moe::static_scratch(c->device);
+  if (!base)
+    return moe_ctx_fail(c, MOE_E_HIP, "forward_static_scratch: no static scratch on device %d (%s)", c->device,
+                        c->static_scratch_err.c_str());
+  return forward_impl(c, layer, n_tokens, x, logits, y, ids, w, flags, moe::forward_scratch_carve(base, P, c->H, c->F));
+}
+
+static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float* x, const float* logits, float* y,
+                        int32_t* ids, float* w, uint32_t flags, const moe::ForwardScratch& sc) {
   if (layer < 0 || layer >= c->L) return moe_ctx_fail(c, MOE_E_INVAL, "forward: bad layer %d", layer);
   if (n_tokens < 1 || n_tokens > c->cfg.max_batch_tokens)
     return moe_ctx_fail(c, MOE_E_INVAL, "forward: n_tokens %d outside 1..%d", n_tokens, c->cfg.max_batch_tokens);
@@ -550,7 +609,7 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   ra.pool = c->pool + c->group_of(layer) * c->S * c->B;
   ra.host = c->host_layers_dev[layer];
   ra.expert_bytes = c->B;
-  ra.ids = c->d_ids, ra.w = c->d_w, ra.addr = c->d_addr, ra.kind = c->d_kind;
+  ra.ids = sc.ids, ra.w = sc.w, ra.addr = sc.addr, ra.kind = sc.kind;
   ra.ids_user = ids, ra.w_user = w;
   ra.policy = 1;
   ra.capture_picks = c->capture_picks;
@@ -578,23 +637,23 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
 
   moe::GemvArgs ga{};
   ga.x = x;
-  ga.addr = c->d_addr;
-  ga.kind = c->d_kind;
-  ga.w = c->d_w;
-  ga.out = c->d_h;
-  ga.ypick = c->d_ypick;
+  ga.addr = sc.addr;
+  ga.kind = sc.kind;
+  ga.w = sc.w;
+  ga.out = sc.h;
+  ga.ypick = sc.ypick;
   ga.T = n_tokens, ga.k = c->k, ga.H = c->H, ga.F = c->F;
   ga.lay = c->lay;
   ga.capture_picks = c->capture_picks;
   ga.capture = c->d_capture ? c->d_capture + (int64_t)layer * c->capture_picks * c->B : nullptr;
   moe::GemvArgs dn = ga;
-  dn.x = c->d_h;
+  dn.x = sc.h;
   dn.out = y;
   dn.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
   if (grouped) {
     moe::GroupArgs gr{};
-    gr.ids = c->d_ids, gr.tbl = ra.tbl, gr.P = n_tokens * c->k, gr.E = c->E;
-    gr.groups = c->d_groups, gr.order = c->d_order, gr.n_groups = c->d_ngroups;
+    gr.ids = sc.ids, gr.tbl = ra.tbl, gr.P = n_tokens * c->k, gr.E = c->E;
+    gr.groups = sc.groups, gr.order = sc.order, gr.n_groups = sc.n_groups;
     HIP_TRY(c, moe::launch_group_picks(gr, A));
     HIP_TRY(c, moe::launch_grouped_gateup(ga, gr, on(A, kHotGateUp)));
     HIP_TRY(c, moe::launch_grouped_down(dn, gr, on(A, kHotDown)));
@@ -614,7 +673,7 @@ extern "C" int moe_forward(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
     moe_host::executor_submit(c->hx, seq, n_tokens, c->host_layers[layer]);
     HIP_TRY(c, moe::launch_gemv_down_pick(dn, on(A, kHotDown), moe::kOnlyHot));
     moe::HostCombineArgs hc{};
-    hc.ypick = c->d_ypick, hc.w = c->d_w, hc.kind = c->d_kind;
+    hc.ypick = sc.ypick, hc.w = sc.w, hc.kind = sc.kind;
     hc.y_cold = (const float*)(c->mbox_dev + c->mb_off_y);
     hc.done = (const uint64_t*)(c->mbox_dev + c->mb_off_done);
     hc.seq = seq;

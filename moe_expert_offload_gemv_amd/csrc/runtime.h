@@ -38,15 +38,9 @@ struct moe_ctx {
   int64_t rec_stride = 0;              // records per layer
   moe::Ctrl* d_ctrl = nullptr;
   uint8_t** d_host_base = nullptr;     // [L] device addresses of the pinned layers
-  int32_t* d_ids = nullptr;            // [max_batch][k]
-  float* d_w = nullptr;
-  const uint8_t** d_addr = nullptr;
-  float* d_h = nullptr;                // [max_batch*k][F]
-  uint8_t* d_kind = nullptr;           // [max_batch*k] hot / cold tag
-  float* d_ypick = nullptr;            // [max_batch*k][H] down output of hot picks
-  int4* d_groups = nullptr;            // [max_batch*k] grouped decode: (expert, start, picks, 0)
-  int32_t* d_order = nullptr;          // [max_batch*k] picks by expert
-  int32_t* d_ngroups = nullptr;        // [1]
+  uint8_t* d_scratch = nullptr;        // per-forward scratch for max_batch*k picks, carved into sc
+  moe::ForwardScratch sc{};
+  std::string static_scratch_err;      // why the static scratch's address is unknown, if it is
   int32_t capture_picks = 0;           // picks per layer whose cold reads are captured
   uint8_t* d_capture = nullptr;        // [L][capture_picks] expert blocks
   uint32_t* d_cap_tag = nullptr;       // [L][rec_stride] clock of a captured cold pick
