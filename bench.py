@@ -404,7 +404,10 @@ def large_pass(moe, torch, stream, host_alloc, steps=32, warmup=4):
                             # bytes of the distinct (layer, expert) pairs each step read / time: the weight bytes
                             # the step has to move at least (tokens picking one expert share its read)
                             "distinct_weight_GBps": round(distinct_gbps, 1),
-                            "distinct_frac_of_hbm": round(distinct_gbps / HBM_PEAK_GBPS, 4)}
+                            "distinct_frac_of_hbm": round(distinct_gbps / HBM_PEAK_GBPS, 4),
+                            "cold_experts_per_layer_step": round(acc["distinct_cold_experts"] / (steps * L), 3),
+                            "admissions_per_step": round(acc["admissions"] / steps, 2),
+                            "promotion_GB_over_pcie_per_step": round(acc["copied_pcie_bytes"] / steps / 1e9, 4)}
             log(f"{wl.name}: {out[wl.name]}")
             del graph, logits, x_all, xs, zs, res
     finally:

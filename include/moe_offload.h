@@ -139,7 +139,14 @@ typedef struct {
                               (HBM to HBM) instead of from pinned memory.
                               Same bytes, same decisions; applies to forwards
                               that route inside the gate/up GEMV (logits
-                              given, E <= 512), others copy from pinned.     */
+                              given, E <= 512). Batches of 8 tokens or more
+                              on the grouped matrix-core path instead stage
+                              each cold expert group g < capture_picks into
+                              block g (its weights cross PCIe once, in long
+                              contiguous reads, before its products), so its
+                              promotion copies that block too. A directory
+                              names the expert and clock of each block's
+                              last writer. Other forwards copy from pinned. */
   int32_t pool_mode;       /* MOE_POOL_PER_LAYER (0) or MOE_POOL_GLOBAL       */
   int32_t swaps_per_step;  /* >= 0: admissions allowed per cache step (0: no
                               limit); see moe_cache_step ([FORK] "Run": the
@@ -310,10 +317,11 @@ MOE_API int moe_forward(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
  * a device shares that device's array and leaves its contents behind
  * (nothing in it needs to start at zero): calls that overlap on one device,
  * on any streams or contexts, race. A forward needs
- *   256-byte-aligned parts for T*k picks: 17 bytes per pick plus 4*(F + H)
- *   bytes per pick for h and the per-pick outputs,
+ *   256-byte-aligned parts for T*k picks: 41 bytes per pick, 8*F + 4*H bytes
+ *   per pick for h (fp32 and split) and the per-pick outputs, and 4*H + 4
+ *   bytes per token for the split activations,
  * MOE_E_INVAL if that exceeds the array (for example T = 32, k = 8 at
- * H = 4096, F = 1536 needs 5.8 MB; T = 256 there does not fit). Calls no
+ * H = 4096, F = 1536 needs 7.9 MB; T = 256 there does not fit). Calls no
  * allocating routine; capturable like moe_forward. */
 MOE_API int moe_forward_static_scratch(moe_ctx* ctx, int32_t layer, int32_t n_tokens,
                 const float* x, const float* logits, float* y,

@@ -17,7 +17,7 @@ LIB = os.path.join(LIBDIR, "libmoe_offload.so")
 OBJDIR = os.path.join(ROOT, "_build", "moe_offload")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["route.hip", "decode.hip", "prefill_kernels.hip", "measure.hip", "step_copy.hip", "scratch.hip",
+SOURCES = ["route.hip", "decode.hip", "prefill_kernels.hip", "measure.hip", "step_copy.hip", "scratch.hip", "grouped_mfma.hip",
            "runtime.cpp", "prefill.cpp", "host_experts.cpp"]
 # plain C++ with no HIP in it (x86 vector code chosen at run time), built by the host compiler
 HOST_ONLY = {"host_experts.cpp"}
@@ -35,6 +35,12 @@ FLAGS = [
 ]
 
 
+# per-file code generation options: the grouped MFMA kernels scale each MFMA
+# result in VALU right away, so their results go to VGPRs (the AGPR form
+# would add a v_accvgpr_read per result element)
+EXTRA_FLAGS = {"grouped_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(OBJDIR, src + ".o")
@@ -42,7 +48,7 @@ def _compile(src: str) -> str:
         cmd = [CXX, *HOST_FLAGS, "-c", path, "-o", obj]
     else:
         lang = [] if src.endswith(".hip") else ["-x", "hip"]
-        cmd = [HIPCC, *FLAGS, *lang, "-c", path, "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

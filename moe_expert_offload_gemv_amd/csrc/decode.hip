@@ -15,7 +15,8 @@
 //                         window, from the last-miss clocks the step began
 //                         with) also writes the bytes it reads over PCIe into
 //                         the layer's capture block p (the down GEMV adds the
-//                         down matrix), so its promotion is an HBM-to-HBM copy
+//                         down matrix) and names it in the layer's capture
+//                         directory, so its promotion is an HBM-to-HBM copy
 //                         instead of a second PCIe transfer.
 //   gemv_gateup_kernel    h = silu(W_gate x) * (W_up x) per pick, picks routed
 //                         by route.hip; hot picks stream from HBM while cold
@@ -361,9 +362,8 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
         r.w[p] = w;
         r.addr[p] = hot ? r.pool + (int64_t)slot * r.expert_bytes : r.host + (int64_t)e * r.expert_bytes;
         r.kind[p] = hot ? kHot : (capture ? (uint8_t)(kCold | kCaptured) : kCold);
-        // every pick that may capture rewrites its tag, so a tag is never
-        // left over from an earlier forward of the same layer in the step
-        if (may_capture) r.cap_tag[p] = capture ? clk : 0u;
+        // the directory entry names what block p will hold after this forward
+        if (capture) r.cap_dir[p] = ((uint64_t)clk << 32) | (uint64_t)e;
         if (r.ids_user) r.ids_user[p] = e;
         if (r.w_user) r.w_user[p] = w;
         if (p == 0) atomicMax(&r.ctrl->step_tokens, (uint32_t)r.T);

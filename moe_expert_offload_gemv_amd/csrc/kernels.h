@@ -82,7 +82,8 @@ struct RouteArgs {
   float* w_user;
   int32_t policy;        // 1: lookup, stamps, records, counts, step tokens; 0: routing only
                          // (fused with the gate/up GEMV: 0 = lookup without side effects)
-  uint32_t* cap_tag;     // [T][k] fused: clock of a cold pick whose bytes the step captured
+  uint64_t* cap_dir;     // [capture_picks] the layer's capture directory: block b holds the expert
+                         //   (clock << 32) | e whose bytes a forward wrote into it at that clock
   int32_t capture_picks; // picks p < capture_picks of a layer may capture their cold reads:
   const uint32_t* last_miss;  // [E] the layer's last-miss clocks as the step began; a cold
   int32_t window, admit_misses;  // pick captures when the cache step will admit it from them
@@ -119,7 +120,10 @@ struct GemvArgs {
   int32_t accumulate;           // combine: y += result
   ExpertLayout lay;
   uint8_t* capture;             // layer's capture blocks: a cold pick p < capture_picks writes the
-  int32_t capture_picks;        //   weight bytes it reads into block p (same layout as a slot)
+  int32_t capture_picks;        //   weight bytes it reads into block p (same layout as a slot);
+                                //   grouped decode: cold group g < capture_picks is staged in block g
+  uint64_t* cap_dir;            // [capture_picks] the layer's capture directory (see RouteArgs)
+  const Ctrl* ctrl;             // the step's token clock (directory entries)
 };
 hipError_t launch_gemv_gateup(const GemvArgs& a, const Launch& l, int mode);
 // routing fused into the gate/up GEMV: needs logits and E <= kFusedRouteMaxExperts
@@ -147,6 +151,21 @@ hipError_t launch_group_picks(const GroupArgs& a, hipStream_t s);
 hipError_t launch_grouped_gateup(const GemvArgs& a, const GroupArgs& g, const Launch& l);
 hipError_t launch_grouped_down(const GemvArgs& a, const GroupArgs& g, const Launch& l);
 hipError_t launch_combine_picks(const GemvArgs& a, const Launch& l);
+
+// Grouped decode on the matrix cores (grouped_mfma.hip), for H and F
+// multiples of 128: activation rows split into scaled fp16 hi/lo operands.
+struct SplitArgs {
+  const uint8_t* x;      // [T][H/32][128 B] split activations
+  const int32_t* xsig;   // [T] their exponents (row scaled by 2^xsig)
+  const uint8_t* h;      // [P][F/32][128 B] split SwiGLU outputs
+  const int32_t* hsig;   // [P]
+};
+bool mfma_grouped_shape_ok(int32_t H, int32_t F);
+// rows fp32 [rows][K] -> dst [rows][K/32][128 B], sig [rows]
+hipError_t launch_split_rows(const float* src, int32_t rows, int32_t K, uint8_t* dst, int32_t* sig, hipStream_t s);
+// h [P][F] (a.out) from the split x; y_pick [P][H] (a.ypick) from the split h
+hipError_t launch_mfma_gateup(const GemvArgs& a, const GroupArgs& g, const SplitArgs& sp, const Launch& l);
+hipError_t launch_mfma_down(const GemvArgs& a, const GroupArgs& g, const SplitArgs& sp, const Launch& l);
 
 // Combine when the host threads computed the cold picks: a token with a cold
 // pick waits until the low half of *done reaches seq (at most max_polls
@@ -251,9 +270,14 @@ struct ForwardScratch {
   int4* groups;          // [P] grouped decode: (expert, start, picks, 0)
   int32_t* order;        // [P] picks by expert
   int32_t* n_groups;     // [1]
+  uint8_t* xs;           // [T][H/32][128 B] grouped decode: split activations
+  int32_t* xsig;         // [T]
+  uint8_t* hs;           // [P][F/32][128 B] split SwiGLU outputs
+  int32_t* hsig;         // [P]
 };
-int64_t forward_scratch_bytes(int64_t P, int32_t H, int32_t F);
-ForwardScratch forward_scratch_carve(uint8_t* base, int64_t P, int32_t H, int32_t F);
+// scratch of a forward of T tokens with top-k (P = T k picks)
+int64_t forward_scratch_bytes(int64_t T, int32_t k, int32_t H, int32_t F);
+ForwardScratch forward_scratch_carve(uint8_t* base, int64_t T, int32_t k, int32_t H, int32_t F);
 
 // The forward's scratch in a static device array (scratch.hip), for the
 // entry point that allocates nothing. static_scratch_init takes the array's

@@ -87,9 +87,6 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
         kind = kCold;
       }
       a.records[p] = rec;
-      // no capture here: a tag left by an earlier forward of the step must
-      // not make the cache step copy that forward's bytes for this pick
-      if (a.cap_tag && p < a.capture_picks) a.cap_tag[p] = 0u;
       atomicAdd(&a.counts[e], 1u);
     } else {
       addr = nullptr;  // a prompt pass addresses experts after sorting

@@ -222,10 +222,11 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ctrl, sizeof(Ctrl), "control"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_host_base, sizeof(uint8_t*) * L, "host bases"))) return fail(rc);
   const int64_t P = (int64_t)k.max_batch_tokens * K;
-  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_scratch, (size_t)moe::forward_scratch_bytes(P, c->H, c->F),
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_scratch,
+                              (size_t)moe::forward_scratch_bytes(k.max_batch_tokens, c->k, c->H, c->F),
                               "forward scratch")))
     return fail(rc);
-  c->sc = moe::forward_scratch_carve(c->d_scratch, P, c->H, c->F);
+  c->sc = moe::forward_scratch_carve(c->d_scratch, k.max_batch_tokens, c->k, c->H, c->F);
   // the allocation-free forward's static scratch: its address on this device,
   // taken once; without it only moe_forward_static_scratch is unavailable
   if (hipError_t e = moe::static_scratch_init(c->device); e != hipSuccess) {
@@ -236,7 +237,8 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if (c->capture_picks > 0) {
     if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_capture, (size_t)(L * c->capture_picks * c->B), "capture blocks")))
       return fail(rc);
-    if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_cap_tag, sizeof(uint32_t) * L * c->rec_stride, "capture tags")))
+    if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_cap_dir, sizeof(uint64_t) * L * c->capture_picks,
+                                "capture directory")))
       return fail(rc);
     if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_last_miss, sizeof(uint32_t) * L * E, "last-miss copy")))
       return fail(rc);
@@ -260,17 +262,18 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if ((rc = moe_ctx_host_alloc(c, (void**)&c->h_tbl, sizeof(int32_t) * L * E, pin, "table staging")))
     return fail(rc);
   if (c->capture_picks > 0 &&
-      ((rc = moe_ctx_host_alloc(c, (void**)&c->h_cap_tag, sizeof(uint32_t) * L * c->rec_stride, pin, "tag staging")) ||
+      ((rc = moe_ctx_host_alloc(c, (void**)&c->h_cap_dir, sizeof(uint64_t) * L * c->capture_picks, pin,
+                                "capture directory staging")) ||
        (rc = moe_ctx_host_alloc(c, (void**)&c->h_last_miss, sizeof(uint32_t) * L * E, pin, "last-miss staging"))))
     return fail(rc);
   const void* rec_view = nullptr;
   const void* tag_view = nullptr;
   if ((rc = dev_view(c->h_ctrl, &c->h_ctrl_dev)) || (rc = dev_view(c->h_tbl, &c->h_tbl_dev)) ||
       (rc = dev_view(c->h_last_miss, &c->h_last_miss_dev)) || (rc = dev_view(c->h_records, &rec_view)) ||
-      (rc = dev_view(c->h_cap_tag, &tag_view)))
+      (rc = dev_view(c->h_cap_dir, &tag_view)))
     return fail(rc);
   c->h_records_dev = const_cast<void*>(rec_view);
-  c->h_cap_tag_dev = const_cast<void*>(tag_view);
+  c->h_cap_dir_dev = const_cast<void*>(tag_view);
 
   // HBM pool: S slots per layer, or one pool of S slots for every layer
   // capacity: an explicit budget, or free HBM minus the reserve, or (both
@@ -341,7 +344,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
     c->swap_recorded.assign(k.swap_lead + 1, 0);
   }
   if (k.cold_exec == MOE_COLD_CPU && (rc = host_exec_create(c))) return fail(rc);
-  if (c->d_cap_tag && hipMemset(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride) != hipSuccess)
+  if (c->d_cap_dir && hipMemset(c->d_cap_dir, 0, sizeof(uint64_t) * L * c->capture_picks) != hipSuccess)
     return fail(MOE_E_HIP);
   if (c->d_last_miss && hipMemset(c->d_last_miss, 0, sizeof(uint32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
   if (hipMemset(c->d_tbl, 0xff, sizeof(int32_t) * L * E) != hipSuccess) return fail(MOE_E_HIP);
@@ -445,7 +448,7 @@ extern "C" int moe_seed(moe_ctx* c, const uint32_t* freq) {
   HIP_TRY(c, hipMemsetAsync(c->d_stamps, 0, sizeof(uint32_t) * c->groups * std::max<int64_t>(S, 1), c->stream));
   HIP_TRY(c, hipMemsetAsync(c->d_counts, 0, sizeof(uint32_t) * L * E, c->stream));
   HIP_TRY(c, hipMemsetAsync(c->d_records, 0, sizeof(uint64_t) * L * c->rec_stride, c->stream));
-  if (c->d_cap_tag) HIP_TRY(c, hipMemsetAsync(c->d_cap_tag, 0, sizeof(uint32_t) * L * c->rec_stride, c->stream));
+  if (c->d_cap_dir) HIP_TRY(c, hipMemsetAsync(c->d_cap_dir, 0, sizeof(uint64_t) * L * c->capture_picks, c->stream));
   if (c->d_last_miss) HIP_TRY(c, hipMemsetAsync(c->d_last_miss, 0, sizeof(uint32_t) * L * E, c->stream));
   *c->h_ctrl = Ctrl{1, 0, 0, 0};
   HIP_TRY(c, hipMemcpyAsync(c->d_ctrl, c->h_ctrl, sizeof(Ctrl), hipMemcpyHostToDevice, c->stream));
@@ -510,11 +513,14 @@ namespace moe {
 namespace {
 int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
 }  // namespace
-int64_t forward_scratch_bytes(int64_t P, int32_t H, int32_t F) {
+int64_t forward_scratch_bytes(int64_t T, int32_t k, int32_t H, int32_t F) {
+  const int64_t P = T * k;
   return up256(4 * P) + up256(4 * P) + up256(8 * P) + up256(P) + up256(4 * P * F) + up256(4 * P * H) +
-         up256(16 * P) + up256(4 * P) + up256(4);
+         up256(16 * P) + up256(4 * P) + up256(4) + up256(4 * T * H) + up256(4 * T) + up256(4 * P * F) +
+         up256(4 * P);
 }
-ForwardScratch forward_scratch_carve(uint8_t* base, int64_t P, int32_t H, int32_t F) {
+ForwardScratch forward_scratch_carve(uint8_t* base, int64_t T, int32_t k, int32_t H, int32_t F) {
+  const int64_t P = T * k;
   ForwardScratch s{};
   int64_t o = 0;
   auto take = [&](int64_t bytes) {
@@ -531,6 +537,10 @@ ForwardScratch forward_scratch_carve(uint8_t* base, int64_t P, int32_t H, int32_
   s.groups = reinterpret_cast<int4*>(take(16 * P));
   s.order = reinterpret_cast<int32_t*>(take(4 * P));
   s.n_groups = reinterpret_cast<int32_t*>(take(4));
+  s.xs = take(4 * T * H);  // 128 bytes per 32 values: hi and lo fp16
+  s.xsig = reinterpret_cast<int32_t*>(take(4 * T));
+  s.hs = take(4 * P * F);
+  s.hsig = reinterpret_cast<int32_t*>(take(4 * P));
   return s;
 }
 }  // namespace moe
@@ -554,8 +564,7 @@ extern "C" int moe_forward_static_scratch(moe_ctx* c, int32_t layer, int32_t n_t
   if (!c) return MOE_E_INVAL;
   if (n_tokens < 1 || n_tokens > c->cfg.max_batch_tokens)
     return moe_ctx_fail(c, MOE_E_INVAL, "forward: n_tokens %d outside 1..%d", n_tokens, c->cfg.max_batch_tokens);
-  const int64_t P = (int64_t)n_tokens * c->k;
-  const int64_t need = moe::forward_scratch_bytes(P, c->H, c->F);
+  const int64_t need = moe::forward_scratch_bytes(n_tokens, c->k, c->H, c->F);
   if (need > moe::kStaticScratchBytes)
     return moe_ctx_fail(c, MOE_E_INVAL,
                         "forward_static_scratch: %d tokens x top-%d at hidden %d, ffn %d need %lld bytes of scratch, "
@@ -565,7 +574,8 @@ extern "C" int moe_forward_static_scratch(moe_ctx* c, int32_t layer, int32_t n_t
   if (!base)
     return moe_ctx_fail(c, MOE_E_HIP, "forward_static_scratch: no static scratch on device %d (%s)", c->device,
                         c->static_scratch_err.c_str());
-  return forward_impl(c, layer, n_tokens, x, logits, y, ids, w, flags, moe::forward_scratch_carve(base, P, c->H, c->F));
+  return forward_impl(c, layer, n_tokens, x, logits, y, ids, w, flags,
+                      moe::forward_scratch_carve(base, n_tokens, c->k, c->H, c->F));
 }
 
 static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float* x, const float* logits, float* y,
@@ -613,7 +623,7 @@ static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float
   ra.ids_user = ids, ra.w_user = w;
   ra.policy = 1;
   ra.capture_picks = c->capture_picks;
-  ra.cap_tag = c->d_cap_tag ? c->d_cap_tag + (int64_t)layer * c->rec_stride : nullptr;
+  ra.cap_dir = c->d_cap_dir ? c->d_cap_dir + (int64_t)layer * c->capture_picks : nullptr;
   ra.last_miss = c->d_last_miss ? c->d_last_miss + (int64_t)layer * c->E : nullptr;
   ra.window = c->cfg.window_tokens, ra.admit_misses = c->cfg.admit_misses;
   // with logits at hand the gate/up GEMV routes by itself (one launch less on
@@ -646,6 +656,8 @@ static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float
   ga.lay = c->lay;
   ga.capture_picks = c->capture_picks;
   ga.capture = c->d_capture ? c->d_capture + (int64_t)layer * c->capture_picks * c->B : nullptr;
+  ga.cap_dir = ra.cap_dir;
+  ga.ctrl = c->d_ctrl;
   moe::GemvArgs dn = ga;
   dn.x = sc.h;
   dn.out = y;
@@ -655,8 +667,17 @@ static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float
     gr.ids = sc.ids, gr.tbl = ra.tbl, gr.P = n_tokens * c->k, gr.E = c->E;
     gr.groups = sc.groups, gr.order = sc.order, gr.n_groups = sc.n_groups;
     HIP_TRY(c, moe::launch_group_picks(gr, A));
-    HIP_TRY(c, moe::launch_grouped_gateup(ga, gr, on(A, kHotGateUp)));
-    HIP_TRY(c, moe::launch_grouped_down(dn, gr, on(A, kHotDown)));
+    if (moe::mfma_grouped_shape_ok(c->H, c->F)) {
+      // each expert's weights dequantised once for all its picks, products on the matrix cores
+      moe::SplitArgs sp{sc.xs, sc.xsig, sc.hs, sc.hsig};
+      HIP_TRY(c, moe::launch_split_rows(x, n_tokens, c->H, sc.xs, sc.xsig, A));
+      HIP_TRY(c, moe::launch_mfma_gateup(ga, gr, sp, on(A, kHotGateUp)));
+      HIP_TRY(c, moe::launch_split_rows(sc.h, n_tokens * c->k, c->F, sc.hs, sc.hsig, A));
+      HIP_TRY(c, moe::launch_mfma_down(dn, gr, sp, on(A, kHotDown)));
+    } else {
+      HIP_TRY(c, moe::launch_grouped_gateup(ga, gr, on(A, kHotGateUp)));
+      HIP_TRY(c, moe::launch_grouped_down(dn, gr, on(A, kHotDown)));
+    }
     HIP_TRY(c, moe::launch_combine_picks(dn, on(A, kColdDownCombine)));
     return MOE_OK;
   }
@@ -783,8 +804,8 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     rb.op[rb.n++] = moe::CopyOp{c->d_ctrl, const_cast<void*>(c->h_ctrl_dev), (int64_t)sizeof(Ctrl)};
     rb.op[rb.n++] = moe::CopyOp{c->d_records, c->h_records_dev, (int64_t)sizeof(uint64_t) * L * c->rec_stride};
     if (S > 0) rb.op[rb.n++] = moe::CopyOp{c->d_stamps, const_cast<void*>(c->h_stamps_dev), (int64_t)sizeof(uint32_t) * GS};
-    if (c->d_cap_tag)
-      rb.op[rb.n++] = moe::CopyOp{c->d_cap_tag, c->h_cap_tag_dev, (int64_t)sizeof(uint32_t) * L * c->rec_stride};
+    if (c->d_cap_dir)
+      rb.op[rb.n++] = moe::CopyOp{c->d_cap_dir, c->h_cap_dir_dev, (int64_t)sizeof(uint64_t) * L * c->capture_picks};
     HIP_TRY(c, moe::launch_copy_list(rb, c->stream));
   }
   HIP_TRY(c, hipStreamSynchronize(c->stream));
@@ -814,14 +835,15 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
       continue;
     }
     c->last_log.push_back(r);
-    // a cold pick p < capture_picks whose tag carries its clock left the
-    // expert's bytes in capture block p of its layer
-    const int64_t p = i % c->rec_stride;
-    const int64_t e = (int64_t)(r & 0xfff);
-    if (p < c->capture_picks && c->h_cap_tag[i] == (uint32_t)t && e < E) {
-      const int64_t te = (i / c->rec_stride) * E + e;
-      if (c->cap_of[te] < 0) c->cap_of[te] = (int32_t)p, c->cap_touched.push_back(te);
-    }
+  }
+  // capture blocks written during this step hold the experts their directory
+  // entries name (the last forward to write a block also wrote its entry)
+  for (int64_t i = 0; i < L * c->capture_picks; ++i) {
+    const uint64_t d = c->h_cap_dir[i];
+    const uint64_t t = d >> 32, e = d & 0xffffffffu;
+    if (t < t_lo || t >= t_hi || e >= (uint64_t)E) continue;
+    const int64_t te = (i / c->capture_picks) * E + (int64_t)e;
+    if (c->cap_of[te] < 0) c->cap_of[te] = (int32_t)(i % c->capture_picks), c->cap_touched.push_back(te);
   }
   const int64_t misses = (int64_t)c->last_log.size();
   if (c->profiling) {

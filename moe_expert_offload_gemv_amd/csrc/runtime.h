@@ -43,7 +43,8 @@ struct moe_ctx {
   std::string static_scratch_err;      // why the static scratch's address is unknown, if it is
   int32_t capture_picks = 0;           // picks per layer whose cold reads are captured
   uint8_t* d_capture = nullptr;        // [L][capture_picks] expert blocks
-  uint32_t* d_cap_tag = nullptr;       // [L][rec_stride] clock of a captured cold pick
+  uint64_t* d_cap_dir = nullptr;       // [L][capture_picks] capture directory: (clock << 32) | expert of
+                                       //   the bytes a forward last wrote into each capture block
   uint32_t* d_last_miss = nullptr;     // [L][E] device copy of last_miss as the step begins
   std::vector<void*> routers;          // per layer fp32 [E][H] or null
 
@@ -53,7 +54,7 @@ struct moe_ctx {
   std::vector<uint8_t*> host_layers_dev;  // device addresses of the same
   moe::Ctrl* h_ctrl = nullptr;
   uint64_t* h_records = nullptr;
-  uint32_t* h_cap_tag = nullptr;
+  uint64_t* h_cap_dir = nullptr;
   uint32_t* h_last_miss = nullptr;
   int32_t* h_tbl = nullptr;
   uint32_t* h_stamps = nullptr;
@@ -64,7 +65,7 @@ struct moe_ctx {
   const void* h_tbl_dev = nullptr;
   const void* h_stamps_dev = nullptr;
   void* h_records_dev = nullptr;
-  void* h_cap_tag_dev = nullptr;
+  void* h_cap_dir_dev = nullptr;
 
   // prefill (borrowed staging blocks and per-pass scratch)
   int64_t n_staging = 0;

@@ -554,3 +554,16 @@ def test_second_forward_of_a_layer_in_a_step_leaves_no_stale_capture():
         assert err < TOL, err
     finally:
         d.close()
+
+
+def test_grouped_cold_experts_staged_then_promoted_from_capture():
+    # 16 tokens at hidden 2048 / ffn 1024 take the grouped matrix-core path; every miss is admitted and
+    # every cold group has a capture block, so each cold expert crosses PCIe once (staged into its block
+    # before its products) and every promotion copies that block: no promotion bytes over PCIe, and the
+    # promoted experts are read from their new slots by the next step, checked every step
+    wl = Workload("decode-e64k8-h2048f1024-l2-b16-stage", 120, 2, 64, 8, 2048, 1024, tokens=16, steps=6,
+                  zipf_s=0.8, slots=16, admit_misses=1)
+    copies = {}
+    _run_decode(wl, slots=16, check_every=1, capture_picks=16 * 8, copies=copies)
+    print("promotion bytes", copies)
+    assert copies["copied"] > 0 and copies["pcie"] == 0
