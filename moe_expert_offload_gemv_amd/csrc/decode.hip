@@ -614,10 +614,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemv_down_combine_kernel(G
 // depend on it).
 __global__ __launch_bounds__(256) void group_picks_kernel(GroupArgs a) {
   __shared__ int32_t cnt[4096], fill[4096];
+  __shared__ uint8_t hot[4096];
   __shared__ int32_t wsum[4], gwsum[4];
   __shared__ int4 lst[kMaxGroupsSorted];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kMaxGroupsSorted + 4];
   const int tid = threadIdx.x;
-  for (int e = tid; e < a.E; e += 256) cnt[e] = 0;
+  for (int e = tid; e < a.E; e += 256) cnt[e] = 0, hot[e] = a.tbl[e] >= 0;  // the table read overlaps the count
   __syncthreads();
   for (int p = tid; p < a.P; p += 256) atomicAdd(&cnt[a.ids[p]], 1);
   __syncthreads();
@@ -643,29 +645,36 @@ __global__ __launch_bounds__(256) void group_picks_kernel(GroupArgs a) {
     ng += gwsum[w];
   }
   if (tid == 0) *a.n_groups = ng;
+  const bool ranked = ng <= kMaxGroupsSorted;
   for (int e = e0; e < e1; ++e) {
     const int c = cnt[e];
     fill[e] = pos;
     if (c > 0) {
-      if (ng <= kMaxGroupsSorted)
-        lst[gi] = make_int4(e, pos, c, a.tbl[e] < 0 ? 1 : 0);
-      else
+      if (ranked) {
+        // sort key, smaller first: cold before hot, then more picks, then a lower expert (unique)
+        keys[gi] = ((uint32_t)hot[e] << 31) | ((uint32_t)(8191 - min(c, 8191)) << 12) | (uint32_t)e;
+        lst[gi] = make_int4(e, pos, c, 0);
+      } else {
         a.groups[gi] = make_int4(e, pos, c, 0);  // too many to rank: expert order
+      }
       ++gi;
     }
     pos += c;
   }
+  if (ranked && tid < 4) keys[ng + tid] = 0xffffffffu;  // padding: ranks below no key
   __syncthreads();
-  if (ng <= kMaxGroupsSorted) {
-    // rank = groups before this one: cold before hot, then more picks, then a lower expert
+  if (ranked) {
+    // rank = keys below this group's: four keys per LDS read, the reads unrolled
+    const uint4* k4 = reinterpret_cast<const uint4*>(keys);
     for (int g = tid; g < ng; g += 256) {
-      const int4 me = lst[g];
+      const uint32_t me = keys[g];
       int rank = 0;
-      for (int h = 0; h < ng; ++h) {
-        const int4 o = lst[h];
-        rank += o.w > me.w || (o.w == me.w && (o.z > me.z || (o.z == me.z && o.x < me.x)));
+#pragma unroll 4
+      for (int h = 0; h < (ng + 3) / 4; ++h) {
+        const uint4 o = k4[h];
+        rank += (o.x < me) + (o.y < me) + (o.z < me) + (o.w < me);
       }
-      a.groups[rank] = make_int4(me.x, me.y, me.z, 0);
+      a.groups[rank] = lst[g];
     }
   }
   for (int p = tid; p < a.P; p += 256) a.order[atomicAdd(&fill[a.ids[p]], 1)] = p;

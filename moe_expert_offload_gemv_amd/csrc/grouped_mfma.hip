@@ -17,7 +17,8 @@
 // hi), 22 significant bits, the scale undone exactly in fp32 afterwards. The
 // result matches the fp32 GEMV to about 1e-7 relative.
 //
-//   split_rows_kernel   fp32 rows -> scaled fp16 hi/lo in operand order
+//   split_rows_kernel   fp32 rows -> scaled fp16 hi/lo in operand order (the
+//                       activations are split by the routing kernel itself)
 //   mfma_grouped_kernel per (expert group, feature tile): gate/up -> h =
 //                       silu(g) * u, or down -> y_pick = W_down h
 //
@@ -43,6 +44,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "split_dev.h"
 
 namespace moe {
 
@@ -54,7 +56,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
-constexpr int kSplitTop = 14;  // a split row's largest magnitude lies in [2^(kSplitTop-1), 2^kSplitTop)
 
 __device__ __forceinline__ f16x2_t as_h2(uint32_t u) {
   f16x2_t v;
@@ -102,14 +103,6 @@ __device__ __forceinline__ float half_hi(uint32_t u) { return (float)as_h2(u)[1]
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-// Exponent s with the row's largest magnitude m times 2^s in [2^13, 2^14)
-// (m = f * 2^e, f in [0.5, 1): s = 14 - e); a zero or non-finite m keeps 0.
-__device__ __forceinline__ int split_exp(float m) {
-  if (!(m > 0.f) || !(m <= 3.4028235e38f)) return 0;
-  int e;
-  (void)frexpf(m, &e);
-  return kSplitTop - e;
-}
 
 // One block of the wave's weight tiles: the MFMA pair on hi and lo, then the
 // block scale d in fp32 into the accumulator (4 rows x 1 column per lane).
@@ -179,45 +172,28 @@ __device__ __forceinline__ int a_pos(int r, int g) { return g ^ ((r & 3) << 2); 
 
 // ---------------------------------------------------------------------------
 
-// fp32 rows [R][K] -> split rows [R][K/32][128 B] (see the file comment) and
-// their exponents; one work-group per row, each thread one chunk of a block
-// at a time.
+// fp32 rows [R][K] -> split rows [R][K/32][128 B] (split_dev.h) and their
+// exponents; one work-group per row, each thread one chunk of a block at a
+// time.
 __global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ src, int32_t K,
                                                          uint4* __restrict__ dst, int32_t* __restrict__ sig) {
   __shared__ float s_max[4];
   const int64_t r = blockIdx.x;
   const float4* row = reinterpret_cast<const float4*>(src + r * K);
   float m = 0.f;
-  for (int q = threadIdx.x; q < K / 4; q += 256) {
-    const float4 v = row[q];
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    if (v.x != v.x || v.y != v.y || v.z != v.z || v.w != v.w) m = __builtin_inff();  // NaN: keep it visible
-  }
+  for (int q = threadIdx.x; q < K / 4; q += 256) m = split_dev::abs_max4(row[q], m);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
   __syncthreads();
-  const int e = split_exp(fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])));
+  const int e = split_dev::scale_exp(fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])));
   if (threadIdx.x == 0) sig[r] = e;
   const float* rf = src + r * K;
   const int KB = K / 32;
   uint4* out = dst + r * (int64_t)KB * 8;
   for (int q = threadIdx.x; q < KB * 4; q += 256) {
     const int b = q >> 2, c = q & 3;
-    const float* blk = rf + 32 * b + 4 * c;
-    const float v[8] = {blk[0], blk[2], blk[1], blk[3], blk[16], blk[18], blk[17], blk[19]};
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s0 = ldexpf(v[2 * i], e), s1 = ldexpf(v[2 * i + 1], e);
-      const _Float16 h0 = (_Float16)s0, h1 = (_Float16)s1;
-      const f16x2_t h = {h0, h1};
-      const f16x2_t l = {(_Float16)(s0 - (float)h0), (_Float16)(s1 - (float)h1)};
-      hi[i] = as_u32(h);
-      lo[i] = as_u32(l);
-    }
-    out[8 * b + c] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    out[8 * b + 4 + c] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    split_dev::chunk(rf + 32 * b, c, e, out[8 * b + c], out[8 * b + 4 + c]);
   }
 }
 

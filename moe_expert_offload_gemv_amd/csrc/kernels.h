@@ -82,6 +82,8 @@ struct RouteArgs {
   float* w_user;
   int32_t policy;        // 1: lookup, stamps, records, counts, step tokens; 0: routing only
                          // (fused with the gate/up GEMV: 0 = lookup without side effects)
+  uint8_t* xs;           // route_kernel: also split the tokens' activations x (split_dev.h) into
+  int32_t* xsig;         //   xs [T][H/32][128 B] and their exponents xsig [T] (nullptr: no)
   uint64_t* cap_dir;     // [capture_picks] the layer's capture directory: block b holds the expert
                          //   (clock << 32) | e whose bytes a forward wrote into it at that clock
   int32_t capture_picks; // picks p < capture_picks of a layer may capture their cold reads:

@@ -20,55 +20,66 @@
 
 #include "kernels.h"
 #include "route_dev.h"
+#include "split_dev.h"
 
 namespace moe {
 
 using namespace route_dev;
 
+// One work-group per token: wave 0 routes (64 threads, or 256 when the
+// work-group also splits the token's activations for the grouped
+// matrix-core decode, which all four waves then do).
 template <int NJ>
-__global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   __shared__ int32_t s_tbl[4096];
+  __shared__ float s_max[4];
   const int t = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const bool router = tid < 64;  // wave 0
   const int E = a.E;
 
   // issue every load first: logits (or the router chain), the table row, the clock
   float z[NJ];
-  if (a.logits) {
+  if (router) {
+    if (a.logits) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = lane + 64 * j;
-      z[j] = e < E ? a.logits[(int64_t)t * E + e] : 0.f;
-    }
-  } else {
-    // z_e = fmaf chain over i = 0..H-1 of x_i * W[e][i], starting from 0
-    const float* xt = a.x + (int64_t)t * a.H;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = lane + 64 * j;
-      float acc = 0.f;
-      if (e < E) {
-        const float* we = a.wr + (int64_t)e * a.H;
-        for (int i = 0; i < a.H; ++i) acc = fmaf(xt[i], we[i], acc);
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + 64 * j;
+        z[j] = e < E ? a.logits[(int64_t)t * E + e] : 0.f;
       }
-      z[j] = acc;
+    } else {
+      // z_e = fmaf chain over i = 0..H-1 of x_i * W[e][i], starting from 0
+      const float* xt = a.x + (int64_t)t * a.H;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + 64 * j;
+        float acc = 0.f;
+        if (e < E) {
+          const float* we = a.wr + (int64_t)e * a.H;
+          for (int i = 0; i < a.H; ++i) acc = fmaf(xt[i], we[i], acc);
+        }
+        z[j] = acc;
+      }
     }
   }
   uint32_t clock0 = 0;
   if (a.policy) {
     clock0 = a.ctrl->clock;
-    for (int e = lane; e < E; e += 64) s_tbl[e] = a.tbl[e];
+    for (int e = tid; e < E; e += blockDim.x) s_tbl[e] = a.tbl[e];
   }
 
   // k rounds; lane i keeps pick i, then its softmax weight
-  int my_e;
-  uint32_t my_bits;
-  wave_topk<NJ>(z, E, a.k, lane, my_e, my_bits);
-  const float w = wave_pick_weight(my_bits, a.k, lane);
+  int my_e = 0;
+  uint32_t my_bits = 0;
+  float w = 0.f;
+  if (router) {
+    wave_topk<NJ>(z, E, a.k, lane, my_e, my_bits);
+    w = wave_pick_weight(my_bits, a.k, lane);
+  }
   __syncthreads();  // the table row in LDS
 
-  if (a.policy && t == 0 && lane == 0) atomicMax(&a.ctrl->step_tokens, (uint32_t)a.T);
-  if (lane < a.k) {
+  if (router && a.policy && t == 0 && lane == 0) atomicMax(&a.ctrl->step_tokens, (uint32_t)a.T);
+  if (router && lane < a.k) {
     const int e = my_e;
     const int64_t p = (int64_t)t * a.k + lane;
     const uint8_t* addr;
@@ -98,11 +109,30 @@ __global__ __launch_bounds__(64) void route_kernel(RouteArgs a) {
     if (a.ids_user) a.ids_user[p] = e;
     if (a.w_user) a.w_user[p] = w;
   }
+  if (a.xs) {
+    // the token's activations as split fp16 operands for the grouped matrix-core decode
+    const float* xr = a.x + (int64_t)t * a.H;
+    float m = 0.f;
+    for (int q = tid; q < a.H / 4; q += blockDim.x) m = split_dev::abs_max4(reinterpret_cast<const float4*>(xr)[q], m);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (lane == 0) s_max[tid >> 6] = m;
+    __syncthreads();
+    for (int i = 0; i < (int)blockDim.x / 64; ++i) m = fmaxf(m, s_max[i]);
+    const int s = split_dev::scale_exp(m);
+    if (tid == 0) a.xsig[t] = s;
+    const int KB = a.H / 32;
+    uint4* out = reinterpret_cast<uint4*>(a.xs) + (int64_t)t * KB * 8;
+    for (int q = tid; q < KB * 4; q += blockDim.x) {
+      const int b = q >> 2, c = q & 3;
+      split_dev::chunk(xr + 32 * b, c, s, out[8 * b + c], out[8 * b + 4 + c]);
+    }
+  }
 }
 
 hipError_t launch_route(const RouteArgs& a, const Launch& l) {
   if (a.E < 1 || a.E > 4096 || a.k < 1 || a.k > 32 || a.k > a.E || a.T < 1) return hipErrorInvalidValue;
-  const dim3 grid(a.T), block(64);
+  const dim3 grid(a.T), block(a.xs ? 256 : 64);
   if (a.E <= 64) return launch(route_kernel<1>, grid, block, l, a);
   if (a.E <= 128) return launch(route_kernel<2>, grid, block, l, a);
   if (a.E <= 256) return launch(route_kernel<4>, grid, block, l, a);

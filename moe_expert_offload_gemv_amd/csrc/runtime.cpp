@@ -643,6 +643,8 @@ static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float
   if (ev) c->timed_fused[c->timed_pending - 1] = fused && !grouped ? 1 : 0;
   if (ev) c->timed_cpu[c->timed_pending - 1] = c->hx ? 1 : 0;
   if (ev) c->timed_grouped[c->timed_pending - 1] = grouped ? 1 : 0;
+  // the grouped matrix-core path takes the activations split into fp16 operands, from the routing kernel
+  if (grouped && moe::mfma_grouped_shape_ok(c->H, c->F)) ra.xs = sc.xs, ra.xsig = sc.xsig;
   if (!fused || grouped) HIP_TRY(c, moe::launch_route(ra, on(A, kRoute)));
 
   moe::GemvArgs ga{};
@@ -670,7 +672,6 @@ static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float
     if (moe::mfma_grouped_shape_ok(c->H, c->F)) {
       // each expert's weights dequantised once for all its picks, products on the matrix cores
       moe::SplitArgs sp{sc.xs, sc.xsig, sc.hs, sc.hsig};
-      HIP_TRY(c, moe::launch_split_rows(x, n_tokens, c->H, sc.xs, sc.xsig, A));
       HIP_TRY(c, moe::launch_mfma_gateup(ga, gr, sp, on(A, kHotGateUp)));
       HIP_TRY(c, moe::launch_split_rows(sc.h, n_tokens * c->k, c->F, sc.hs, sc.hsig, A));
       HIP_TRY(c, moe::launch_mfma_down(dn, gr, sp, on(A, kHotDown)));
