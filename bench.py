@@ -29,13 +29,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
-# HBM bytes per launch of the roofline kernel (gemv_route_gateup_kernel<64,1,4,1>, hot picks), from two rocprofv3
-# counter runs (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, scaled by a 1 GiB copy) over launches that served 7.14 hot picks
-# each (16.85 MB algorithmic); the summary and commands are under profiles/. Set to None when the kernel changes.
-ROOFLINE_TRAFFIC = {"bytes_per_launch": 17189832, "algorithmic_bytes_per_launch": 16852979}
+# HBM bytes per launch of the roofline kernel (the hot launch of decode_layer_kernel), from two rocprofv3 counter
+# runs (FETCH_SIZE, WRITE_SIZE, scaled by a copy of known size); the summary and commands are under profiles/.
+# None until counters are taken on the kernel as it stands.
+ROOFLINE_TRAFFIC = None
 PCIE_PEAK_GBPS = 64.0       # PCIe Gen5 x16, one direction
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA; fp16 (what the grouped GEMM runs) has the same rate
 METRIC = "MoE-layer decode tokens/s + effective weight GB/s vs HBM/PCIe roofline"
+# decode batches of 1..7 tokens: 1 = one launch per layer where the shape allows it, 2 = two launches
+DECODE_LAUNCHES = 2
 
 
 def log(*a):
@@ -59,7 +61,8 @@ def setup_ctx(moe, wl, slots, stream, host_alloc, layers=None, progress=True, ca
                          max_prefill_tokens=max_prefill_tokens, host_alloc=host_alloc,
                          host_sets=min(wl.weight_layers, L), stream=stream, capture_picks=capture_picks,
                          pool_mode=moe.MOE_POOL_GLOBAL if pool == "global" else moe.MOE_POOL_PER_LAYER,
-                         swaps_per_step=swaps[0], swap_lead=swaps[1], cold_exec=cold_exec, cpu_threads=cpu_threads)
+                         swaps_per_step=swaps[0], swap_lead=swaps[1], cold_exec=cold_exec, cpu_threads=cpu_threads,
+                         decode_launches=DECODE_LAUNCHES)
     t1 = time.time()
     buf = None
     gen_s = 0.0
@@ -512,6 +515,7 @@ def cpu_baseline(wl, seconds, logits):
 
 
 def main():
+    global DECODE_LAUNCHES
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
@@ -534,6 +538,8 @@ def main():
                     help="cold picks read zero-copy by the GPU, or computed by host threads (eager launches)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="host threads for --cold-exec cpu (0: all CPUs of the affinity mask but two)")
     ap.add_argument("--profile-steps", type=int, default=64, help="steps of the kernel-timing pass")
+    ap.add_argument("--decode-launches", type=int, choices=[1, 2], default=DECODE_LAUNCHES,
+                    help="decode batches of 1..7 tokens: 1 one launch per layer, 2 two launches")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the two prompt passes (one line of JSON each; for counter runs)")
     ap.add_argument("--prompt-tokens", type=int, default=12288,
@@ -541,6 +547,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (the reference for counter scaling)")
     args = ap.parse_args()
+    DECODE_LAUNCHES = args.decode_launches
     if args.copy_calibration:
         import torch
 
@@ -657,11 +664,27 @@ def main():
         prof = moe.moe_profile(ctx, 0)
     fw = max(prof["forwards"], 1)
     gu_bytes = prof["gateup_bytes_per_pick"]
-    hot_gu_us = prof["hot_gateup_ms"] / fw * 1e3
-    hot_gu_bytes = prof["hot_picks"] * gu_bytes / fw
+    pick_bytes = gu_bytes + prof["down_bytes_per_pick"]
+    one_launch = prof["layer_forwards"] == prof["forwards"] and prof["forwards"] > 0
+    if one_launch:
+        # one launch per layer, timed as a hot launch (routing, lookup, gate/up and down of the hot picks)
+        # and a cold one (the cold picks, then the combine)
+        hot_gu_us = prof["hot_layer_ms"] / fw * 1e3
+        hot_gu_bytes = prof["hot_picks"] * pick_bytes / fw
+        cold_rate = prof["cold_picks"] * pick_bytes / max(prof["cold_layer_ms"], 1e-9) / 1e6
+        cold_dn_rate = None
+        roof_kernel = ("decode_layer_kernel, hot launch (routing + slot lookup + gate/up + SwiGLU + down of the hot "
+                       "picks from the HBM pool, one launch per layer)")
+        pcie_kernel = "decode_layer_kernel, cold launch (zero-copy reads of pinned host memory, then the combine)"
+    else:
+        hot_gu_us = prof["hot_gateup_ms"] / fw * 1e3
+        hot_gu_bytes = prof["hot_picks"] * gu_bytes / fw
+        cold_rate = prof["cold_picks"] * gu_bytes / max(prof["cold_gateup_ms"], 1e-9) / 1e6
+        cold_dn_rate = prof["cold_picks"] * prof["down_bytes_per_pick"] / max(prof["cold_down_ms"], 1e-9) / 1e6
+        roof_kernel = ("gemv_route_gateup_kernel, hot picks (routing + slot lookup + gate/up + SwiGLU from the HBM "
+                       "pool; the launch includes the routing)")
+        pcie_kernel = "gemv_route_gateup_kernel, cold picks (zero-copy reads of pinned host memory)"
     achieved = hot_gu_bytes / (hot_gu_us * 1e-6) / 1e9
-    cold_rate = prof["cold_picks"] * gu_bytes / max(prof["cold_gateup_ms"], 1e-9) / 1e6
-    cold_dn_rate = prof["cold_picks"] * prof["down_bytes_per_pick"] / max(prof["cold_down_ms"], 1e-9) / 1e6
     log(f"kernel timing ({prof_steps} eager steps, {prof_steps * T / t_prof:.1f} tokens/s): {prof}")
 
     request = None
@@ -691,7 +714,8 @@ def main():
                    else args.capture_picks,
                    "pool": args.pool, "swaps_per_step": args.swaps_per_step, "swap_lead": args.swap_lead,
                    "cold_exec": args.cold_exec, "host_threads": info["host_threads"],
-                   "launch": "eager" if args.eager else "hip-graph"},
+                   "launch": "eager" if args.eager else "hip-graph",
+                   "decode_launches_per_layer": DECODE_LAUNCHES},
         # outside the timed region: pinning and allocating, weight generation, registration, seeding
         "setup": setup,
         "effective_weight_GBps": round((acc["hot_bytes"] + acc["cold_bytes"]) / elapsed / 1e9, 2),
@@ -707,15 +731,16 @@ def main():
                      "traffic": ROOFLINE_TRAFFIC and int(ROOFLINE_TRAFFIC["bytes_per_launch"]),
                      "traffic_over_algorithmic": ROOFLINE_TRAFFIC and round(
                          ROOFLINE_TRAFFIC["bytes_per_launch"] / ROOFLINE_TRAFFIC["algorithmic_bytes_per_launch"], 3),
-                     "kernel": "gemv_route_gateup_kernel, hot picks (routing + slot lookup + gate/up + SwiGLU "
-                               "from the HBM pool; the launch includes the routing)",
+                     "kernel": roof_kernel,
                      "avg_launch_us": round(hot_gu_us, 2), "bytes_per_launch": int(hot_gu_bytes)},
-        "pcie": {"cold_gateup_GBps": round(cold_rate, 2), "cold_down_GBps": round(cold_dn_rate, 2),
-                 "peak": PCIE_PEAK_GBPS, "frac": round(cold_rate / PCIE_PEAK_GBPS, 4),
-                 "kernel": "gemv_route_gateup_kernel, cold picks (zero-copy reads of pinned host memory)"},
-        # route is 0 where the routing runs inside the gate/up launches (logits given, E <= 512)
+        "pcie": ({"cold_layer_GBps": round(cold_rate, 2)} if one_launch else
+                 {"cold_gateup_GBps": round(cold_rate, 2), "cold_down_GBps": round(cold_dn_rate, 2)}) | {
+                 "peak": PCIE_PEAK_GBPS, "frac": round(cold_rate / PCIE_PEAK_GBPS, 4), "kernel": pcie_kernel},
+        # route is 0 where the routing runs inside the gate/up launches (logits given, E <= 512); with one
+        # launch per layer only hot_layer and cold_layer are nonzero
         "per_layer_us": {k_: round(prof[k_ + "_ms"] / fw * 1e3, 2)
-                         for k_ in ("route", "hot_gateup", "hot_down", "cold_gateup", "cold_down")},
+                         for k_ in ("route", "hot_gateup", "hot_down", "cold_gateup", "cold_down", "hot_layer",
+                                    "cold_layer")},
     }
 
     if not args.no_side_passes:
@@ -727,20 +752,22 @@ def main():
         def rate(p, ms_key, picks_key, bytes_key):
             return p[picks_key] * p[bytes_key] / max(p[ms_key], 1e-9) / 1e6  # bytes / ms -> GB/s
 
-        hgu = rate(hot, "hot_gateup_ms", "hot_picks", "gateup_bytes_per_pick")
-        result["kernels_all_hot"] = {
-            "gateup_GBps": round(hgu, 1),
-            "down_GBps": round(rate(hot, "hot_down_ms", "hot_picks", "down_bytes_per_pick"), 1),
-            "per_layer_us": {k_: round(hot[k_ + "_ms"] / hot["forwards"] * 1e3, 2)
-                             for k_ in ("route", "hot_gateup", "hot_down", "cold_gateup", "cold_down")},
-            "frac_of_hbm": round(hgu / HBM_PEAK_GBPS, 4)}
-        cgu = rate(cold, "cold_gateup_ms", "cold_picks", "gateup_bytes_per_pick")
-        result["kernels_all_cold"] = {
-            "gateup_GBps": round(cgu, 2),
-            "down_GBps": round(rate(cold, "cold_down_ms", "cold_picks", "down_bytes_per_pick"), 2),
-            "per_layer_us": {k_: round(cold[k_ + "_ms"] / cold["forwards"] * 1e3, 2)
-                             for k_ in ("route", "hot_gateup", "hot_down", "cold_gateup", "cold_down")},
-            "frac_of_pcie": round(cgu / PCIE_PEAK_GBPS, 4)}
+        def side(p, tag, peak):
+            keys = ("route", "hot_gateup", "hot_down", "cold_gateup", "cold_down", "hot_layer", "cold_layer")
+            out = {"per_layer_us": {k_: round(p[k_ + "_ms"] / p["forwards"] * 1e3, 2) for k_ in keys}}
+            if p["layer_forwards"]:
+                p = dict(p, pick_bytes=p["gateup_bytes_per_pick"] + p["down_bytes_per_pick"])
+                r = rate(p, tag + "_layer_ms", tag + "_picks", "pick_bytes")
+                out["layer_GBps"] = round(r, 2)
+            else:
+                r = rate(p, tag + "_gateup_ms", tag + "_picks", "gateup_bytes_per_pick")
+                out["gateup_GBps"] = round(r, 2)
+                out["down_GBps"] = round(rate(p, tag + "_down_ms", tag + "_picks", "down_bytes_per_pick"), 2)
+            out["frac_of_" + ("hbm" if tag == "hot" else "pcie")] = round(r / peak, 4)
+            return out
+
+        result["kernels_all_hot"] = side(hot, "hot", HBM_PEAK_GBPS)
+        result["kernels_all_cold"] = side(cold, "cold", PCIE_PEAK_GBPS)
         # DMA ceiling: pinned host -> HBM copy of 1 GiB
         src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
         dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -167,6 +167,26 @@ typedef struct {
                               per CPU the process may run on, but two: one
                               left to the thread that launches the forwards,
                               one to the HIP runtime's completion thread)    */
+  int32_t decode_launches; /* launches per layer for decode batches of 1..7
+                              tokens (0 or 2: two, gate/up then down +
+                              combine; 1: one, where logits are given,
+                              E <= 512, top-k <= 8 and hidden/ffn is
+                              2048/1024, 4096/1536 or 256/512: the down
+                              work-groups issue their weight loads at once
+                              and wait on device counters for h). Same
+                              picks, records, decisions and outputs either
+                              way (the same sums in the same order:
+                              bit-identical). Two is the default: on MI355X
+                              the h hand-over inside one launch (coherent
+                              stores, a counter, polls, coherent loads
+                              across XCDs) cost more than the launch
+                              boundary it saves                            */
+  int32_t decode_sync_polls; /* bound of a one-launch down work-group's wait
+                              for its token's gate/up work-groups, in polls
+                              of at least one memory round trip (0: 2^20,
+                              about half a second). Past it the work-group
+                              sets a flag, goes on, and the next
+                              moe_cache_step returns MOE_E_HIP             */
 } moe_config;
 
 typedef struct {
@@ -236,6 +256,13 @@ typedef struct {
   int64_t host_picks;         /* cold picks computed                          */
   double  host_wait_ms;       /* from taking a hand-off to seeing all picks   */
   double  host_compute_ms;    /* computing the cold picks and answering       */
+  /* forwards run as one launch per layer (decode_launches 1): timed as a hot
+     launch (routing, gate/up and down of the hot picks) and a cold launch
+     (the cold picks, then the combine of all); the per-kernel fields above
+     stay 0 for them                                                        */
+  int64_t layer_forwards;     /* timed forwards of one launch per layer       */
+  double  hot_layer_ms;       /* summed hot launches                          */
+  double  cold_layer_ms;      /* summed cold launches                         */
 } moe_profile_stats;
 
 /* Size in bytes of one expert (gate + up + down) in MOE_Q4_32_F16. */

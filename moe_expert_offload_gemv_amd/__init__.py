@@ -51,7 +51,7 @@ class moe_config(C.Structure):
         ("max_prefill_tokens", C.c_int32), ("device", C.c_int32), ("host_alloc", C.c_int32),
         ("host_sets", C.c_int32), ("stream", C.c_void_p), ("capture_picks", C.c_int32), ("pool_mode", C.c_int32),
         ("swaps_per_step", C.c_int32), ("swap_lead", C.c_int32), ("cold_exec", C.c_int32),
-        ("cpu_threads", C.c_int32),
+        ("cpu_threads", C.c_int32), ("decode_launches", C.c_int32), ("decode_sync_polls", C.c_int32),
     ]
 
 
@@ -79,7 +79,8 @@ class moe_profile_stats(C.Structure):
                 ("prefill_tiles", C.c_int64), ("prefill_staged", C.c_int64), ("prefill_prep_ms", C.c_double),
                 ("prefill_stage_ms", C.c_double), ("host_forwards", C.c_int64),
                 ("host_expert_passes", C.c_int64), ("host_picks", C.c_int64), ("host_wait_ms", C.c_double),
-                ("host_compute_ms", C.c_double)]
+                ("host_compute_ms", C.c_double), ("layer_forwards", C.c_int64), ("hot_layer_ms", C.c_double),
+                ("cold_layer_ms", C.c_double)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -159,7 +160,7 @@ def moe_expert_bytes(hidden: int, ffn: int) -> int:
 def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reserve_bytes=0, window_tokens=64,
                admit_misses=2, max_batch_tokens=64, max_prefill_tokens=0, device=0, host_alloc=MOE_HOST_COHERENT,
                host_sets=0, stream=None, capture_picks=None, pool_mode=0, swaps_per_step=0, swap_lead=0,
-               cold_exec=MOE_COLD_GPU, cpu_threads=0):
+               cold_exec=MOE_COLD_GPU, cpu_threads=0, decode_launches=0, decode_sync_polls=0):
     """Returns an opaque context handle.
 
     stream: a torch.cuda.Stream, a raw hipStream_t int, or None for torch's
@@ -169,6 +170,8 @@ def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reser
     pool_mode: MOE_POOL_PER_LAYER (slots per layer) or MOE_POOL_GLOBAL (one pool for all layers).
     swaps_per_step: admissions per cache step (0: no limit); swap_lead: cache steps an admission waits
     for its copy before its table entry flips (0: at once).
+    decode_launches: 1 for one launch per layer where the decode shape allows it, 0 or 2 for two (the default).
+    decode_sync_polls: bound of the one-launch down work-groups' wait (0: the default, 2^20 polls).
     """
     if capture_picks is None:
         capture_picks = 0 if cold_exec == MOE_COLD_CPU else top_k
@@ -185,7 +188,8 @@ def moe_create(n_layers, n_experts, top_k, hidden, ffn, pool_budget_bytes, reser
         stream = stream.cuda_stream
     cfg = moe_config(n_layers, n_experts, top_k, hidden, ffn, MOE_Q4_32_F16, pool_budget_bytes, reserve_bytes,
                      window_tokens, admit_misses, max_batch_tokens, max_prefill_tokens, device, host_alloc,
-                     host_sets, stream, capture_picks, pool_mode, swaps_per_step, swap_lead, cold_exec, cpu_threads)
+                     host_sets, stream, capture_picks, pool_mode, swaps_per_step, swap_lead, cold_exec, cpu_threads,
+                     decode_launches, decode_sync_polls)
     out = C.c_void_p()
     rc = lib().moe_create(C.byref(cfg), C.byref(out))
     if rc != MOE_OK:

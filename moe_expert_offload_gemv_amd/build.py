@@ -17,7 +17,7 @@ LIB = os.path.join(LIBDIR, "libmoe_offload.so")
 OBJDIR = os.path.join(ROOT, "_build", "moe_offload")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["route.hip", "decode.hip", "prefill_kernels.hip", "measure.hip", "step_copy.hip", "scratch.hip", "grouped_mfma.hip",
+SOURCES = ["route.hip", "decode.hip", "decode_layer.hip", "prefill_kernels.hip", "measure.hip", "step_copy.hip", "scratch.hip", "grouped_mfma.hip",
            "runtime.cpp", "prefill.cpp", "host_experts.cpp"]
 # plain C++ with no HIP in it (x86 vector code chosen at run time), built by the host compiler
 HOST_ONLY = {"host_experts.cpp"}

@@ -200,10 +200,7 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
 
   const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
   RowTile<LPR, BPL, NIT> g, u;
-  g.load(reinterpret_cast<const uint4*>(base + a.lay.gate_nib),
-         reinterpret_cast<const uint16_t*>(base + a.lay.gate_scl), row0, a.F, lb, !hot);
-  u.load(reinterpret_cast<const uint4*>(base + a.lay.up_nib), reinterpret_cast<const uint16_t*>(base + a.lay.up_scl),
-         row0, a.F, lb, !hot);
+  load_gateup(g, u, base, a.lay, row0, a.F, lb, !hot);
   // the lane's activation slice from LDS (blocks lb + LPR j), with the
   // per-block sums of the -8 offset, added in the order load_slice uses
   float xs[BPL][32], sx[BPL];
@@ -246,10 +243,7 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(GemvArgs a) {
   const bool cold = (a.kind[p] & kCold) != 0;
   const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
   RowTile<LPR, BPL, NIT> g, u;
-  g.load(reinterpret_cast<const uint4*>(base + a.lay.gate_nib),
-         reinterpret_cast<const uint16_t*>(base + a.lay.gate_scl), row0, a.F, lb, cold);
-  u.load(reinterpret_cast<const uint4*>(base + a.lay.up_nib), reinterpret_cast<const uint16_t*>(base + a.lay.up_scl),
-         row0, a.F, lb, cold);
+  load_gateup(g, u, base, a.lay, row0, a.F, lb, cold);
   float xs[BPL][32], sx[BPL];
   load_slice<LPR, BPL>(a.x + (int64_t)t * a.H, lb, xs, sx);
   gateup_store<LPR, BPL, NIT>(g, u, xs, sx, row0, lb, a.F, a.out + (int64_t)p * a.F);
@@ -269,15 +263,18 @@ __global__ __launch_bounds__(256) void gemv_down_pick_kernel(GemvArgs a) {
   const int lb = lane % LPR, rg = lane / LPR;
   const uint8_t* base = a.addr[p];
   const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
-  // the pick's h row, once per work-group (with LPR < 64 every row group of
-  // a wave would load it again)
-  using V = SharedVec<LPR, BPL>;
+  // the pick's h row in LDS, once per work-group (with LPR < 64 every row
+  // group of a wave would load it again), the work-group sharing the copy,
+  // its loads issued before the weight loads
+  using V = SwizVec<LPR, BPL, 256>;
   __shared__ float4 hsh[V::KV];
-  V::issue(a.x + (int64_t)p * a.F, hsh, wave, 4, lane);
+  V hv;
+  hv.load(a.x + (int64_t)p * a.F, threadIdx.x);
   RowTile<LPR, BPL, NIT> d;
   d.load(reinterpret_cast<const uint4*>(base + a.lay.down_nib),
          reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0, a.H, lb);
-  V::wait();
+  hv.store(hsh, threadIdx.x);
+  __syncthreads();
   float hs[BPL][32], sh[BPL];
   V::slice(hsh, lb, hs, sh);
   down_store<LPR, BPL, NIT>(d, hs, sh, row0, lb, a.H, a.ypick + (int64_t)p * a.H);
@@ -290,6 +287,52 @@ __global__ __launch_bounds__(256) void gemv_down_pick_kernel(GemvArgs a) {
 // wave, every pick's loads in flight at once); hot picks come from y_pick.
 // Sum in pick order.
 constexpr int kCombineWaves = 8;
+
+// One pick's down rows for gemv_down_combine_kernel, into part[i].
+// Hot picks (PACE false) stage the h row through registers, its loads issued
+// before the weight loads, so each row's arithmetic waits for that row only.
+// Cold picks pace their zero-copy reads with explicit waits, next to which the
+// compiler kept a register-staged row in scratch memory; they are bound by
+// PCIe anyway and stage h by the LDS-DMA copy, issued after their weights.
+template <int LPR, int BPL, int NIT, bool PACE, bool STAGE>
+__device__ __forceinline__ void down_pick_rows(const GemvArgs& a, int64_t p, int i, int row0, int lane,
+                                               float4* hsh, float (*part)[NIT * (64 / LPR)]) {
+  constexpr int RPW = 64 / LPR;
+  using V = SwizVec<LPR, BPL>;
+  using D = SharedVec<LPR, BPL>;
+  const int lb = lane % LPR, rg = lane / LPR;
+  const uint8_t* base = a.addr[p];
+  V hv;
+  if (STAGE && !PACE) hv.load(a.x + p * a.F, lane);
+  RowTile<LPR, BPL, NIT> d;
+  d.load(reinterpret_cast<const uint4*>(base + a.lay.down_nib),
+         reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0 + rg, a.H, lb, PACE);
+  float hs[BPL][32], sh[BPL];
+  if (STAGE && !PACE) {
+    hv.store(hsh, lane);
+    V::slice(hsh, lb, hs, sh);
+  } else if (STAGE) {
+    D::issue(a.x + p * a.F, hsh, 0, 1, lane);
+    D::wait_wave();
+    D::slice(hsh, lb, hs, sh);
+  } else {
+    load_slice<LPR, BPL>(a.x + p * a.F, lb, hs, sh);
+  }
+  float pv[1][4], sv[1];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    pv[0][it] = d.partial(it, hs, sh);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  reduce4_rows<LPR, 1>(pv, sv);
+  if (lb < NIT) part[i][lb * RPW + rg] = sv[0];
+  if ((a.kind[p] & kCaptured) && p < a.capture_picks) {  // after the arithmetic, as in the gate/up GEMV
+    uint8_t* cap = a.capture + p * a.lay.bytes;
+    d.store(reinterpret_cast<uint4*>(cap + a.lay.down_nib), reinterpret_cast<uint16_t*>(cap + a.lay.down_scl),
+            row0 + rg, a.H, lb);
+  }
+}
+
 template <int LPR, int BPL, int NIT, int MODE>
 __global__ __launch_bounds__(64 * kCombineWaves) void gemv_down_combine_kernel(GemvArgs a) {
   constexpr int RPW = 64 / LPR;
@@ -297,41 +340,19 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemv_down_combine_kernel(G
   __shared__ float part[32][ROWS];
   // each wave stages its pick's h row in LDS once (with LPR < 64 every row
   // group would load it again), while the 8 copies fit in 64 KiB
-  using V = SharedVec<LPR, BPL>;
+  using V = SwizVec<LPR, BPL>;
   constexpr bool kStage = V::KV <= 512;
   __shared__ float4 hsh[kStage ? kCombineWaves : 1][kStage ? V::KV : 1];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lb = lane % LPR, rg = lane / LPR;
   const int row0 = blockIdx.x * ROWS;
   for (int i = wave; i < a.k; i += kCombineWaves) {
     const int64_t p = (int64_t)t * a.k + i;
     if (!wanted<MODE>(a.kind[p])) continue;
-    const uint8_t* base = a.addr[p];
-    RowTile<LPR, BPL, NIT> d;
-    d.load(reinterpret_cast<const uint4*>(base + a.lay.down_nib),
-           reinterpret_cast<const uint16_t*>(base + a.lay.down_scl), row0 + rg, a.H, lb, (a.kind[p] & kCold) != 0);
-    // after the weight loads: a cold pick's pacing waits must not wait for it
-    if (kStage) V::issue(a.x + p * a.F, hsh[wave], 0, 1, lane);
-    float hs[BPL][32], sh[BPL];
-    if (kStage) {
-      V::wait_wave();
-      V::slice(hsh[wave], lb, hs, sh);
-    } else {
-      load_slice<LPR, BPL>(a.x + p * a.F, lb, hs, sh);
-    }
-    {
-      float pv[1][4], sv[1];
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) pv[0][it] = d.partial(it, hs, sh);
-      reduce4_rows<LPR, 1>(pv, sv);
-      if (lb < NIT) part[i][lb * RPW + rg] = sv[0];
-    }
-    if ((a.kind[p] & kCaptured) && p < a.capture_picks) {  // after the arithmetic, as in the gate/up GEMV
-      uint8_t* cap = a.capture + p * a.lay.bytes;
-      d.store(reinterpret_cast<uint4*>(cap + a.lay.down_nib), reinterpret_cast<uint16_t*>(cap + a.lay.down_scl),
-              row0 + rg, a.H, lb);
-    }
+    if (a.kind[p] & kCold)
+      down_pick_rows<LPR, BPL, NIT, true, kStage>(a, p, i, row0, lane, hsh[kStage ? wave : 0], part);
+    else
+      down_pick_rows<LPR, BPL, NIT, false, kStage>(a, p, i, row0, lane, hsh[kStage ? wave : 0], part);
   }
   __syncthreads();
   for (int rr = threadIdx.x; rr < ROWS; rr += 64 * kCombineWaves) {
@@ -453,10 +474,7 @@ __global__ __launch_bounds__(256) void grouped_gateup_kernel(GemvArgs a, GroupAr
   const bool cold = (a.kind[p0] & kCold) != 0;
   const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
   RowTile<LPR, BPL, NIT> g, u;
-  g.load(reinterpret_cast<const uint4*>(base + a.lay.gate_nib),
-         reinterpret_cast<const uint16_t*>(base + a.lay.gate_scl), row0, a.F, lb, cold);
-  u.load(reinterpret_cast<const uint4*>(base + a.lay.up_nib), reinterpret_cast<const uint16_t*>(base + a.lay.up_scl),
-         row0, a.F, lb, cold);
+  load_gateup(g, u, base, a.lay, row0, a.F, lb, cold);
 #pragma unroll 1
   for (int c0 = 0; c0 < grp.z; c0 += NB) {
     const int nc = grp.z - c0 < NB ? grp.z - c0 : NB;

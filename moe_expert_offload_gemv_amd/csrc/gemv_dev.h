@@ -129,25 +129,38 @@ template <int LPR, int BPL, int NIT>
 struct RowTile {
   uint4 q[NIT][BPL];
   uint32_t d[NIT][BPL];
+  // Row it of the tile. Rows past the matrix load its last row instead
+  // (their results are never stored): no branch around a load, so the
+  // compiler can count the loads in flight and let each row's arithmetic
+  // start as soon as that row is in, instead of waiting for the whole tile.
+  // The weights are device memory (the HBM pool, a capture block or mapped
+  // pinned host memory): loaded as global, not flat, accesses, which an
+  // address read from a table would otherwise get (flat loads also count
+  // against the LDS counter, so every LDS read would wait for them).
+  __device__ __forceinline__ void load_row(const uint4* __restrict__ nib, const uint16_t* __restrict__ scl, int it,
+                                           int row0, int nrows, int lb) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+    typedef __attribute__((address_space(1))) const uint16_t g_u16;
+    constexpr int RPW = 64 / LPR;
+    const int r = min(row0 + it * RPW, nrows - 1);
+    const g_u32x4* gn = (const g_u32x4*)nib;
+    const g_u16* gs = (const g_u16*)scl;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int64_t idx = (int64_t)r * (LPR * BPL) + lb + LPR * j;
+      const u32x4 w = gn[idx];
+      q[it][j] = make_uint4(w.x, w.y, w.z, w.w);
+      d[it][j] = gs[idx];
+    }
+  }
   // pace (wave-uniform): wait after each row until at most
   // kColdLoadsInFlight loads are outstanding
   __device__ __forceinline__ void load(const uint4* __restrict__ nib, const uint16_t* __restrict__ scl, int row0,
                                        int nrows, int lb, bool pace = false) {
-    constexpr int RPW = 64 / LPR;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int r = row0 + it * RPW;
-#pragma unroll
-      for (int j = 0; j < BPL; ++j) {
-        if (r < nrows) {
-          const int64_t idx = (int64_t)r * (LPR * BPL) + lb + LPR * j;
-          q[it][j] = nib[idx];
-          d[it][j] = scl[idx];
-        } else {
-          q[it][j] = make_uint4(0, 0, 0, 0);
-          d[it][j] = 0;
-        }
-      }
+      load_row(nib, scl, it, row0, nrows, lb);
       if (pace) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kColdLoadsInFlight));
     }
   }
@@ -188,6 +201,24 @@ struct RowTile {
   }
 };
 
+// The gate and up tiles of the same rows, issued row by row alternately (the
+// order gateup_store consumes them), paced as RowTile::load.
+template <int LPR, int BPL, int NIT>
+__device__ __forceinline__ void load_gateup(RowTile<LPR, BPL, NIT>& g, RowTile<LPR, BPL, NIT>& u, const uint8_t* base,
+                                            const ExpertLayout& lay, int row0, int nrows, int lb, bool pace) {
+  const uint4* gn = reinterpret_cast<const uint4*>(base + lay.gate_nib);
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(base + lay.gate_scl);
+  const uint4* un = reinterpret_cast<const uint4*>(base + lay.up_nib);
+  const uint16_t* us = reinterpret_cast<const uint16_t*>(base + lay.up_scl);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    g.load_row(gn, gs, it, row0, nrows, lb);
+    if (pace) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kColdLoadsInFlight));
+    u.load_row(un, us, it, row0, nrows, lb);
+    if (pace) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kColdLoadsInFlight));
+  }
+}
+
 // which picks a launch computes: every pick, or only the hot / cold ones
 template <int MODE>
 __device__ __forceinline__ bool wanted(uint8_t kind) {
@@ -201,8 +232,14 @@ __device__ __forceinline__ void gateup_store(const RowTile<LPR, BPL, NIT>& g, co
                                              int nrows, float* __restrict__ out) {
   static_assert(NIT == 4, "reduce4_rows sums 4 rows per lane");
   float pv[2][4], sv[2];
+  // row by row in load order (load_gateup): each row waits for its own loads only
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) pv[0][it] = g.partial(it, xs, sx), pv[1][it] = u.partial(it, xs, sx);
+  for (int it = 0; it < NIT; ++it) {
+    pv[0][it] = g.partial(it, xs, sx);
+    __builtin_amdgcn_sched_barrier(0);
+    pv[1][it] = u.partial(it, xs, sx);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   reduce4_rows<LPR, 2>(pv, sv);
   const int r = row0 + lb * (64 / LPR);
   if (lb < NIT && r < nrows) out[r] = silu(sv[0]) * sv[1];
@@ -214,7 +251,10 @@ __device__ __forceinline__ void down_store(const RowTile<LPR, BPL, NIT>& d, cons
   static_assert(NIT == 4, "reduce4_rows sums 4 rows per lane");
   float pv[1][4], sv[1];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) pv[0][it] = d.partial(it, hs, sh);
+  for (int it = 0; it < NIT; ++it) {
+    pv[0][it] = d.partial(it, hs, sh);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   reduce4_rows<LPR, 1>(pv, sv);
   const int r = row0 + lb * (64 / LPR);
   if (lb < NIT && r < nrows) out[r] = sv[0];
@@ -230,19 +270,25 @@ __device__ __forceinline__ void down_store(const RowTile<LPR, BPL, NIT>& d, cons
 // fetching the source chunk that belongs there; the waves that share the
 // copy take the instructions in turn.
 typedef __attribute__((address_space(3))) void lds_void_t;
+// cache-policy bit SC1 of a gfx950 memory instruction: device (agent) scope,
+// the form an agent-scope atomic load takes
+constexpr int kReadCoherent = 16;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
 template <int LPR, int BPL>
 struct SharedVec {
   static constexpr int KV = 8 * LPR * BPL;
   static_assert(KV % 64 == 0, "whole DMA instructions");
-  // instructions first, first + step, ... of the copy
+  // instructions first, first + step, ... of the copy. AUX: the loads'
+  // cache-policy bits (kReadCoherent: device-coherent reads of data another
+  // work-group of the same launch wrote, on any XCD)
+  template <int AUX = 0>
   __device__ __forceinline__ static void issue(const float* src, float4* dst, int first, int step, int lane) {
     for (int q = first; q < KV / 64; q += step) {
       const int d = 64 * q + lane;
       const int j = d / (8 * LPR), ch = (d / LPR) % 8, lb = d % LPR;
       __builtin_amdgcn_global_load_lds((glb_void_t*)(src + 4 * (8 * (lb + LPR * j) + ch)),
-                                       (lds_void_t*)(dst + 64 * q), 16, 0, 0);
+                                       (lds_void_t*)(dst + 64 * q), 16, 0, AUX);
     }
   }
   // the lane's slice (blocks lb + LPR j) and its block sums, from LDS
@@ -267,6 +313,55 @@ struct SharedVec {
   }
   // a copy this wave made alone is complete
   __device__ __forceinline__ static void wait_wave() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); }
+};
+
+// A K-vector in LDS in its own order with an XOR swizzle: float4 c of block
+// b at 8 b + (c ^ (b & 7)). Copied by one wave through registers: coalesced
+// 16-byte global loads (lane l takes float4s 64 q + l), LDS writes that hit
+// distinct banks, and slice reads (a lane's blocks lb + LPR j) that do too.
+// Plain loads, unlike the LDS-DMA form, are tracked one by one by the
+// compiler's wait counting: issued before the weight loads, they let each
+// weight row's arithmetic wait for that row only.
+// THREADS: the threads sharing the copy (a wave, or a work-group), thread t
+// taking float4s t, t + THREADS, ... (the last index repeats past the end, so
+// no load sits behind a branch; the repeats are not stored).
+template <int LPR, int BPL, int THREADS = 64>
+struct SwizVec {
+  static constexpr int KV = 8 * LPR * BPL;                  // float4s of the vector
+  static constexpr int NQ = (KV + THREADS - 1) / THREADS;  // per thread
+  float4 v[NQ];
+  __device__ __forceinline__ void load(const float* __restrict__ src, int t) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(1))) const f32x4 g_f32x4;
+    const g_f32x4* s4 = (const g_f32x4*)src;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const f32x4 x = s4[min(THREADS * q + t, KV - 1)];
+      v[q] = make_float4(x.x, x.y, x.z, x.w);
+    }
+  }
+  __device__ __forceinline__ void store(float4* dst, int t) const {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int s = THREADS * q + t, b = s >> 3, c = s & 7;
+      if (KV % THREADS == 0 || s < KV) dst[b * 8 + (c ^ (b & 7))] = v[q];
+    }
+  }
+  // the lane's slice and its block sums (the -8 offset), summed in load_slice's order
+  __device__ __forceinline__ static void slice(const float4* src, int lb, float (&xs)[BPL][32], float (&sx)[BPL]) {
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int b = lb + LPR * j;
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float4 q = src[b * 8 + (c ^ (b & 7))];
+        xs[j][4 * c + 0] = q.x, xs[j][4 * c + 1] = q.y, xs[j][4 * c + 2] = q.z, xs[j][4 * c + 3] = q.w;
+        acc += (q.x + q.y) + (q.z + q.w);
+      }
+      sx[j] = acc;
+    }
+  }
 };
 
 }  // namespace

@@ -13,7 +13,7 @@ struct Ctrl {
   uint32_t clock;        // token clock of token 0 of the current step
   uint32_t step_tokens;  // max n_tokens over the forwards of the step
   uint32_t host_fault;   // set when a forward's cold picks got no answer from the host threads
-  uint32_t reserved;
+  uint32_t sync_fault;   // set when a one-launch layer kernel's down work-group gave up waiting for h
 };
 
 // A pick record: (clock << 32) | hit << 31 | layer << 12 | expert. The miss
@@ -153,6 +153,24 @@ hipError_t launch_group_picks(const GroupArgs& a, hipStream_t s);
 hipError_t launch_grouped_gateup(const GemvArgs& a, const GroupArgs& g, const Launch& l);
 hipError_t launch_grouped_down(const GemvArgs& a, const GroupArgs& g, const Launch& l);
 hipError_t launch_combine_picks(const GemvArgs& a, const Launch& l);
+
+// One launch per layer for decode batches of 1 .. kLayerMaxTokens tokens
+// (top-k <= 8, logits given, E <= kFusedRouteMaxExperts): gate/up work-groups
+// and down + combine work-groups in one grid, the down ones waiting on a
+// per-token counter of finished gate/up work-groups (decode_layer.hip).
+constexpr int kLayerMaxTokens = kGroupedMinTokens - 1;
+struct LayerArgs {
+  float* h;              // [T*k][F] exchange buffer of the h rows
+  float* y;              // [T][H] layer output
+  int32_t accumulate;    // y += result
+  uint32_t* sync;        // [kLayerMaxTokens] token counters: 0 between launches, each launch leaves them 0
+  uint32_t max_polls;    // bound of a down work-group's wait; past it ctrl->sync_fault is set
+};
+// the shapes that have a one-launch instantiation (others take the two-launch path)
+bool layer_shape_ok(int H, int F, int k, int T, int E);
+// mode kAll: the layer; kOnlyHot: hot picks, y_pick rows of a.ypick, no y;
+// kOnlyCold: cold picks, combined with the hot picks' a.ypick rows into y
+hipError_t launch_decode_layer(const GemvArgs& a, const RouteArgs& r, const LayerArgs& l, const Launch& ln, int mode);
 
 // Grouped decode on the matrix cores (grouped_mfma.hip), for H and F
 // multiples of 128: activation rows split into scaled fp16 hi/lo operands.

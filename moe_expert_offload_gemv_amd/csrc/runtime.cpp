@@ -183,6 +183,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
       (k.pool_mode != MOE_POOL_PER_LAYER && k.pool_mode != MOE_POOL_GLOBAL) || k.swaps_per_step < 0 ||
       k.swap_lead < 0 || k.swap_lead > MOE_MAX_SWAP_LEAD ||
       (k.cold_exec != MOE_COLD_GPU && k.cold_exec != MOE_COLD_CPU) || k.cpu_threads < 0 || k.cpu_threads > 256 ||
+      k.decode_launches < 0 || k.decode_launches > 2 || k.decode_sync_polls < 0 ||
       (k.cold_exec == MOE_COLD_CPU && k.capture_picks != 0) ||
       (k.host_alloc != MOE_HOST_COHERENT && k.host_alloc != MOE_HOST_NONCOHERENT))
     return g_create_error = "config field out of range", MOE_E_INVAL;
@@ -220,6 +221,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_records, sizeof(uint64_t) * L * c->rec_stride, "pick records")))
     return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_ctrl, sizeof(Ctrl), "control"))) return fail(rc);
+  if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_layer_sync, kLayerSyncBytes, "layer counters"))) return fail(rc);
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_host_base, sizeof(uint8_t*) * L, "host bases"))) return fail(rc);
   const int64_t P = (int64_t)k.max_batch_tokens * K;
   if ((rc = moe_ctx_dev_alloc(c, (void**)&c->d_scratch,
@@ -354,6 +356,8 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
     return fail(MOE_E_HIP);
   Ctrl z{1, 0, 0, 0};
   if (hipMemcpy(c->d_ctrl, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return fail(MOE_E_HIP);
+  // the one-launch layer kernels leave their token counters at 0; they start there
+  if (hipMemset(c->d_layer_sync, 0, kLayerSyncBytes) != hipSuccess) return fail(MOE_E_HIP);
   // events for kernel timing: a start/stop pair per kernel of a forward,
   // enough for one step of every layer
   const int64_t n_timed = L + 16;
@@ -368,6 +372,7 @@ extern "C" int moe_create(const moe_config* cfg, moe_ctx** out) {
   c->timed_fused.assign(n_timed, 0);
   c->timed_cpu.assign(n_timed, 0);
   c->timed_grouped.assign(n_timed, 0);
+  c->timed_layer.assign(n_timed, 0);
   if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_E_HIP);
   c->clock = 1;
   *out = c;
@@ -643,6 +648,10 @@ static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float
   if (ev) c->timed_fused[c->timed_pending - 1] = fused && !grouped ? 1 : 0;
   if (ev) c->timed_cpu[c->timed_pending - 1] = c->hx ? 1 : 0;
   if (ev) c->timed_grouped[c->timed_pending - 1] = grouped ? 1 : 0;
+  // a few tokens with logits at hand: one launch per layer where the shape has an instantiation
+  const bool one_launch = fused && !grouped && !c->hx && c->cfg.decode_launches == 1 &&
+                          moe::layer_shape_ok(c->H, c->F, c->k, n_tokens, c->E);
+  if (ev) c->timed_layer[c->timed_pending - 1] = one_launch ? 1 : 0;
   // the grouped matrix-core path takes the activations split into fp16 operands, from the routing kernel
   if (grouped && moe::mfma_grouped_shape_ok(c->H, c->F)) ra.xs = sc.xs, ra.xsig = sc.xsig;
   if (!fused || grouped) HIP_TRY(c, moe::launch_route(ra, on(A, kRoute)));
@@ -706,6 +715,24 @@ static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float
     HIP_TRY(c, moe::launch_host_combine(hc, on(A, kColdDownCombine)));
     return MOE_OK;
   }
+  if (one_launch) {
+    moe::LayerArgs la{};
+    la.h = sc.h;
+    la.y = y;
+    la.accumulate = dn.accumulate;
+    la.sync = c->d_layer_sync;
+    la.max_polls = c->cfg.decode_sync_polls > 0 ? (uint32_t)c->cfg.decode_sync_polls : kLayerMaxPolls;
+    if (!ev) {
+      HIP_TRY(c, moe::launch_decode_layer(ga, ra, la, on(A, 0), moe::kAll));
+    } else {
+      // timing: the hot picks (with the side effects), then the cold ones and the combine
+      moe::RouteArgs quiet = ra;
+      quiet.policy = 0;
+      HIP_TRY(c, moe::launch_decode_layer(ga, ra, la, on(A, kHotGateUp), moe::kOnlyHot));
+      HIP_TRY(c, moe::launch_decode_layer(ga, quiet, la, on(A, kColdDownCombine), moe::kOnlyCold));
+    }
+    return MOE_OK;
+  }
   if (!ev) {
     // hot picks stream from HBM while cold picks stream over PCIe, in one launch
     if (fused)
@@ -736,6 +763,18 @@ static int forward_impl(moe_ctx* c, int32_t layer, int32_t n_tokens, const float
 static int flush_profile(moe_ctx* c) {
   for (int32_t i = 0; i < c->timed_pending; ++i) {
     float t[kTimedKernels];
+    if (c->timed_layer[i]) {
+      float hot = 0.f, cold = 0.f;
+      HIP_TRY(c, hipEventElapsedTime(&hot, c->events[2 * (kTimedKernels * (size_t)i + kHotGateUp)],
+                                     c->events[2 * (kTimedKernels * (size_t)i + kHotGateUp) + 1]));
+      HIP_TRY(c, hipEventElapsedTime(&cold, c->events[2 * (kTimedKernels * (size_t)i + kColdDownCombine)],
+                                     c->events[2 * (kTimedKernels * (size_t)i + kColdDownCombine) + 1]));
+      c->prof.forwards += 1;
+      c->prof.layer_forwards += 1;
+      c->prof.hot_layer_ms += hot;
+      c->prof.cold_layer_ms += cold;
+      continue;
+    }
     for (int j = 0; j < kTimedKernels; ++j) {
       t[j] = 0.f;
       if (j == kRoute && c->timed_fused[i]) continue;
@@ -812,6 +851,7 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
   HIP_TRY(c, hipStreamSynchronize(c->stream));
   const Ctrl st = *c->h_ctrl;
   const bool host_fault = st.host_fault != 0;
+  const bool sync_fault = st.sync_fault != 0;
   if (S > 0) std::memcpy(c->stamps.data(), c->h_stamps, sizeof(uint32_t) * GS);
   // records of this step carry clocks in [clock, clock + step tokens); older ones are stale
   int64_t hits = 0, distinct = 0, distinct_cold = 0;
@@ -1000,6 +1040,14 @@ extern "C" int moe_cache_step(moe_ctx* c, moe_step_stats* out) {
     out->distinct_cold_experts = distinct_cold;
   }
   c->steps += 1;
+  if (sync_fault) {
+    // a wait ran out: the counters may hold a count the protocol did not end at 0
+    HIP_TRY(c, hipMemsetAsync(c->d_layer_sync, 0, kLayerSyncBytes, c->stream));
+    HIP_TRY(c, hipStreamSynchronize(c->stream));
+    return moe_ctx_fail(c, MOE_E_HIP,
+                        "cache_step: a one-launch layer forward of this step gave up waiting for its gate/up "
+                        "work-groups (its outputs are not valid)");
+  }
   if (host_fault)
     return moe_ctx_fail(c, MOE_E_HIP,
                         "cache_step: a forward of this step got no answer from the host threads (its cold picks "

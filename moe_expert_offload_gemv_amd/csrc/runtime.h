@@ -14,6 +14,13 @@
 
 // kernels of a forward, in the order of their timing events
 enum { kRoute = 0, kHotGateUp, kHotDown, kColdGateUp, kColdDownCombine, kTimedKernels };
+// token counters of the one-launch layer kernels (one 64-byte line)
+constexpr size_t kLayerSyncBytes = 64;
+static_assert(moe::kLayerMaxTokens * sizeof(uint32_t) <= kLayerSyncBytes, "a counter per token");
+// bound of a down work-group's wait, in polls of at least a memory round trip
+// each (about half a second); a legitimate wait is one gate/up pass, cold
+// picks over PCIe included (well under a millisecond)
+constexpr uint32_t kLayerMaxPolls = 1u << 20;
 
 struct moe_ctx {
   moe_config cfg{};
@@ -45,6 +52,7 @@ struct moe_ctx {
   uint8_t* d_capture = nullptr;        // [L][capture_picks] expert blocks
   uint64_t* d_cap_dir = nullptr;       // [L][capture_picks] capture directory: (clock << 32) | expert of
                                        //   the bytes a forward last wrote into each capture block
+  uint32_t* d_layer_sync = nullptr;    // token counters of the one-launch layer kernels
   uint32_t* d_last_miss = nullptr;     // [L][E] device copy of last_miss as the step begins
   std::vector<void*> routers;          // per layer fp32 [E][H] or null
 
@@ -105,6 +113,7 @@ struct moe_ctx {
   std::vector<uint8_t> timed_fused;    // 1: its routing ran inside the gate/up GEMV (no routing interval)
   std::vector<uint8_t> timed_cpu;      // 1: its cold gate/up ran on the host threads (no interval)
   std::vector<uint8_t> timed_grouped;  // 1: grouped by expert (no separate cold gate/up interval)
+  std::vector<uint8_t> timed_layer;    // 1: one launch per layer (a hot and a cold launch when timed)
   int32_t timed_pending = 0;
   moe_profile_stats prof{};
 

@@ -30,7 +30,7 @@ class Decode:
     def __init__(self, wl: Workload, slots: int | None = None, seed=True, max_batch: int | None = None,
                  host_alloc: int = moe.MOE_HOST_COHERENT, stream=None, max_prefill: int = 0, keep_weights=True,
                  capture_picks=None, pool="layer", swaps_per_step=0, swap_lead=0, cold_exec=moe.MOE_COLD_GPU,
-                 cpu_threads=0):
+                 cpu_threads=0, decode_launches=0, decode_sync_polls=0):
         import torch
 
         self.wl = wl
@@ -46,7 +46,8 @@ class Decode:
                                   host_sets=wl.distinct_layers, stream=self.stream, capture_picks=capture_picks,
                                   pool_mode=moe.MOE_POOL_GLOBAL if pool == "global" else moe.MOE_POOL_PER_LAYER,
                                   swaps_per_step=swaps_per_step, swap_lead=swap_lead, cold_exec=cold_exec,
-                                  cpu_threads=cpu_threads)
+                                  cpu_threads=cpu_threads, decode_launches=decode_launches,
+                                  decode_sync_polls=decode_sync_polls)
         info = moe.moe_get_info(self.ctx)
         assert info["slots_per_layer"] == self.S, info
         self.weights = {}

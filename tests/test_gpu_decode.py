@@ -294,10 +294,11 @@ def test_shared_host_sets():
     _run_decode(wl, slots=10, check_every=3)
 
 
-def test_kernel_timing_hook():
+@pytest.mark.parametrize("launches", [1, 2])
+def test_kernel_timing_hook(launches):
     wl = Workload("decode-e32k8-h2048f1024-l3-b2-prof", 112, 3, 32, 8, 2048, 1024, tokens=2, steps=4, zipf_s=1.1,
                   slots=12)
-    d = Decode(wl)
+    d = Decode(wl, decode_launches=launches)
     logits = zipf_logits(wl)
     y = torch.empty((2, 2048), dtype=torch.float32, device="cuda")
     moe.moe_profile(d.ctx, 1)
@@ -313,8 +314,15 @@ def test_kernel_timing_hook():
     assert prof["forwards"] == 3 * wl.steps
     assert prof["hot_picks"] == tot["hits"] and prof["cold_picks"] == tot["misses"]
     assert tot["hits"] + tot["misses"] == wl.steps * 3 * 2 * 8
-    for key in ("hot_gateup_ms", "hot_down_ms", "cold_gateup_ms", "cold_down_ms"):
-        assert prof[key] > 0, key
+    if launches == 2:
+        for key in ("hot_gateup_ms", "hot_down_ms", "cold_gateup_ms", "cold_down_ms"):
+            assert prof[key] > 0, key
+        assert prof["layer_forwards"] == 0 and prof["hot_layer_ms"] == 0 and prof["cold_layer_ms"] == 0
+    else:  # one launch per layer: timed as a hot and a cold launch
+        assert prof["layer_forwards"] == 3 * wl.steps
+        assert prof["hot_layer_ms"] > 0 and prof["cold_layer_ms"] > 0
+        for key in ("hot_gateup_ms", "hot_down_ms", "cold_gateup_ms", "cold_down_ms"):
+            assert prof[key] == 0, key
     assert prof["route_ms"] == 0  # with logits the gate/up launches route by themselves
     assert prof["gateup_bytes_per_pick"] + prof["down_bytes_per_pick"] == wl.expert_bytes
     # a router chain runs (and is timed) in its own launch
@@ -567,3 +575,81 @@ def test_grouped_cold_experts_staged_then_promoted_from_capture():
     _run_decode(wl, slots=16, check_every=1, capture_picks=16 * 8, copies=copies)
     print("promotion bytes", copies)
     assert copies["copied"] > 0 and copies["pcie"] == 0
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("E,k,H,F,T,slots", [(64, 8, 2048, 1024, 1, 24), (64, 8, 2048, 1024, 3, 24),
+                                            (16, 4, 4096, 1536, 2, 6), (32, 4, 256, 512, 7, 10),
+                                            (8, 2, 256, 512, 4, 3)])
+def test_one_launch_layer_matches_two_launches_bitwise(E, k, H, F, T, slots):
+    """The one-launch layer kernel (gate/up and down work-groups in one grid, the down ones waiting on
+    a device counter) against the two-launch path on the same inputs: picks, weights, outputs (every
+    forward, MOE_ACCUMULATE on odd layers), tables, stamps and miss logs bit-identical, hot and cold
+    picks mixed, captures on; the first step also against the oracle."""
+    wl = Workload(f"layer-ab-e{E}k{k}-h{H}f{F}-b{T}", 121, 2, E, k, H, F, tokens=T, steps=5, zipf_s=1.0,
+                  slots=slots)
+    one = Decode(wl, slots=slots, decode_launches=1)
+    two = Decode(wl, slots=slots, decode_launches=2)
+    logits = zipf_logits(wl)
+    outs = {}
+    try:
+        for step in range(wl.steps):
+            for layer in range(wl.n_layers):
+                x32 = activations(wl, step, layer=layer)
+                flags = moe.MOE_ACCUMULATE if layer % 2 else 0
+                base = torch.from_numpy(activations(wl, step + 100, layer=layer)).cuda()
+                for name, d in (("one", one), ("two", two)):
+                    y = base.clone()
+                    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+                    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+                    moe.moe_forward(d.ctx, layer, T, _dev(x32), _dev(logits[step, layer]), y, ids, w, flags=flags)
+                    outs[name] = (y.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy())
+                for a, b in zip(outs["one"], outs["two"]):
+                    assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                          b.view(np.uint32) if b.dtype == np.float32 else b), (step, layer)
+                if step == 0:
+                    ids_o, _ = oracle.route(logits[step, layer], k)
+                    y_ref, _, _ = oracle.moe_layer(E, k, H, F, one.experts(layer, ids_o), x32.astype(np.float64),
+                                                   logits=logits[step, layer])
+                    y_one = outs["one"][0] - (base.cpu().numpy() if flags else 0)
+                    assert token_rel_err(y_one, y_ref) < TOL, (layer, token_rel_err(y_one, y_ref))
+            s1, s2 = moe.moe_cache_step(one.ctx), moe.moe_cache_step(two.ctx)
+            assert s1 == s2, (step, s1, s2)
+            for layer in range(wl.n_layers):
+                assert np.array_equal(moe.moe_get_slot_table(one.ctx, layer, E), moe.moe_get_slot_table(two.ctx, layer, E))
+                assert np.array_equal(moe.moe_get_stamps(one.ctx, layer, slots), moe.moe_get_stamps(two.ctx, layer, slots))
+            assert np.array_equal(moe.moe_get_miss_log(one.ctx), moe.moe_get_miss_log(two.ctx))
+            assert s1["misses"] > 0 or step > 0
+    finally:
+        one.close()
+        two.close()
+
+
+@pytest.mark.gpu
+def test_one_launch_layer_wait_bound_is_reported():
+    # A wait bound of one poll, every pick cold (an empty pool: gate/up reads cross PCIe, tens of
+    # microseconds): the down work-groups give up at once, go on, and the cache step reports it. Every
+    # kernel still ends; the counters are cleared by the step that reports the error.
+    wl = Workload("layer-bound-e32k8-h2048f1024", 122, 1, 32, 8, 2048, 1024, tokens=1, steps=1, zipf_s=1.0,
+                  slots=4)
+    d = Decode(wl, slots=4, seed=False, decode_launches=1, decode_sync_polls=1)
+    try:
+        z = zipf_logits(wl)[0, 0]
+        y = torch.empty((1, 2048), dtype=torch.float32, device="cuda")
+        moe.moe_forward(d.ctx, 0, 1, _dev(activations(wl, 0)), _dev(z), y)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_cache_step(d.ctx)
+        assert ei.value.code == moe.MOE_E_HIP and "gave up waiting" in str(ei.value)
+    finally:
+        d.close()
+    # a default bound on the same work is exact
+    d = Decode(wl, slots=4, seed=False, decode_launches=1)
+    try:
+        x32 = activations(wl, 0)
+        moe.moe_forward(d.ctx, 0, 1, _dev(x32), _dev(z), y)
+        moe.moe_cache_step(d.ctx)
+        ids_o, _ = oracle.route(z, 8)
+        y_ref, _, _ = oracle.moe_layer(32, 8, 2048, 1024, d.experts(0, ids_o), x32.astype(np.float64), logits=z)
+        assert token_rel_err(y.cpu().numpy(), y_ref) < TOL
+    finally:
+        d.close()
