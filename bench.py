@@ -514,6 +514,53 @@ def cpu_baseline(wl, seconds, logits):
                        f"{spent:.1f} s of oracle time; weight generation excluded)", cpu_model=model)
 
 
+def pcie_reads():
+    """The workload of the PCIe read counters: (1) calibration, read_stream_kernel over 256 MiB of pinned host
+    memory (one untimed and two timed launches); (2) a cold-only decode of the 512-expert top-8 hidden 2048 /
+    ffn 1024 shape, empty pool, batch 1, 2 layers x 8 steps, capture off (every gate/up and down launch serves 8
+    cold picks); (3) its 4096-token prompt pass with an empty pool (every used expert staged over PCIe)."""
+    import numpy as np
+    import torch
+
+    import moe_expert_offload_gemv_amd as moe
+    from workload import WORKLOADS, activations, layer_weights, zipf_logits
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        g = moe.moe_measure_read_bandwidth(None, 256 << 20, reps=2, host_coherent=True)
+        log(f"calibration: 3 launches x 268435456 B pinned zero-copy, {g:.2f} GB/s")
+        wl = WORKLOADS["decode-e512k8-h2048f1024-l48-b1"]
+        E, k, H, F = wl.n_experts, wl.top_k, wl.hidden, wl.ffn
+        ctx = moe.moe_create(2, E, k, H, F, pool_budget_bytes=0, max_batch_tokens=1, host_sets=1, capture_picks=0,
+                             stream=stream)
+        moe.moe_register_layer(ctx, 0, *layer_weights(wl, 0))
+        moe.moe_seed(ctx, None)
+        z = torch.from_numpy(zipf_logits(wl, layers=[0, 1], steps=8)).cuda()
+        x = torch.from_numpy(np.stack([activations(wl, s) for s in range(8)])).cuda()
+        y = torch.zeros((1, H), dtype=torch.float32, device="cuda")
+        picks = 0
+        for s in range(8):
+            for layer in range(2):
+                moe.moe_forward(ctx, layer, 1, x[s], z[s, layer], y, flags=moe.MOE_ACCUMULATE)
+            picks += moe.moe_cache_step(ctx)["misses"]
+        torch.cuda.synchronize()
+        moe.moe_destroy(ctx)
+        log(f"cold decode: 16 forwards, {picks} cold picks")
+        wlp = WORKLOADS["prefill-e512k8-h2048f1024-t4096"]
+        T = wlp.tokens
+        ctx = moe.moe_create(1, E, k, H, F, pool_budget_bytes=0, max_batch_tokens=1, max_prefill_tokens=T,
+                             host_sets=1, stream=stream)
+        moe.moe_register_layer(ctx, 0, *layer_weights(wlp, 0))
+        moe.moe_seed(ctx, None)
+        xp = torch.from_numpy(activations(wlp, 0, tokens=T)).cuda()
+        zp = torch.from_numpy(np.ascontiguousarray(zipf_logits(wlp, steps=1, tokens=T)[0, 0])).cuda()
+        yp = torch.empty_like(xp)
+        moe.moe_prefill(ctx, 0, T, xp, zp, yp)
+        torch.cuda.synchronize()
+        moe.moe_destroy(ctx)
+        log("prompt pass: 4096 tokens, every used expert staged")
+
+
 def main():
     global DECODE_LAUNCHES
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -546,6 +593,9 @@ def main():
                     help="prompt length of the prompt-then-decode pass (0: skip it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 4 times (the reference for counter scaling)")
+    ap.add_argument("--pcie-reads", action="store_true",
+                    help="only run the PCIe counter workload: a pinned-memory read of known size, a cold-only decode "
+                         "and a staged prompt pass (for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     DECODE_LAUNCHES = args.decode_launches
     if args.copy_calibration:
@@ -557,6 +607,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copied 4 x 1 GiB")
+        return
+    if args.pcie_reads:
+        pcie_reads()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards per GPU with no "

@@ -653,3 +653,35 @@ def test_one_launch_layer_wait_bound_is_reported():
         assert token_rel_err(y.cpu().numpy(), y_ref) < TOL
     finally:
         d.close()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T", [1, 5])
+def test_decode_activations_of_mixed_magnitude(T):
+    """Decode activations far from unit scale: rows scaled by 1e3 and 1e-4, single huge values inside a
+    block of small ones, blocks of exact zeros and of subnormal values. Every output within the tolerance
+    of the oracle (fp64), on hot and cold picks."""
+    E, k, H, F = 32, 8, 2048, 1024
+    wl = Workload(f"decode-mixed-e{E}k{k}-b{T}", 123, 1, E, k, H, F, tokens=T, steps=1, zipf_s=1.0, slots=16)
+    d = Decode(wl, slots=16)
+    try:
+        rng = np.random.default_rng(77 + T)
+        x32 = activations(wl, 0)
+        x32[0] *= 1e3
+        if T > 1:
+            x32[1] *= 1e-4
+            x32[2, ::32] = 5e4           # one huge value per block, the rest N(0, 1)
+            x32[3, 64:256] = 0.0         # whole blocks of zeros
+            x32[4, :32] = rng.standard_normal(32).astype(np.float32) * 1e-40  # subnormal block
+        z = zipf_logits(wl)[0, 0]
+        y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        moe.moe_forward(d.ctx, 0, T, _dev(x32), _dev(z), y)
+        ids_o, _ = oracle.route(z, k)
+        y_ref, _, _ = oracle.moe_layer(E, k, H, F, d.experts(0, ids_o), x32.astype(np.float64), logits=z)
+        err = token_rel_err(y.cpu().numpy(), y_ref)
+        print("mixed-magnitude decode error", err)
+        assert err < TOL, err
+        st = moe.moe_cache_step(d.ctx)
+        assert st["hits"] > 0 and st["misses"] > 0, st
+    finally:
+        d.close()
