@@ -417,8 +417,11 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
             S + C::OFF_BS + m * C::BS_BYTES + (tscl ? (g >> 1) * BNW * 2 + wn * 2 : wn * 4 + 2 * (g >> 1)));
         weight_operands(w, as_h2(d | (d << 16)), bop[m][ns][0], bop[m][ns][1]);
       }
+    // 16-row blocks past the tile's last row are skipped (their A rows are
+    // still fetched, as the DMA count per step must stay the same)
 #pragma unroll
-    for (int s = 0; s < RB; ++s)
+    for (int s = 0; s < RB; ++s) {
+      if (s * 16 >= rows) continue;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // row s*16 + lane%16 (row & 7 == lane & 7), logical chunk 4h + g
@@ -430,6 +433,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
           for (int ns = 0; ns < NSUB; ++ns)
             acc[m][ns][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bop[m][ns][h], acc[m][ns][s], 0, 0, 0);
       }
+    }
   }
 
   // epilogue: lane holds rows s*16 + g*4 + i of feature n0 + wave*WN + ns*16 + lane%16.
