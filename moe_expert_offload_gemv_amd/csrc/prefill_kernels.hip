@@ -92,21 +92,31 @@ __device__ __forceinline__ f16x2_t as_h2(uint32_t u) {
 // 16 weights of one column from 8 bytes of a quant block: bytes jb..jb+7
 // hold elements jb..jb+7 (low nibbles) and jb+16..jb+23 (high nibbles).
 // lo gets jb + (0,2,1,3,4,6,5,7), hi the same + 16; value fp16(d * (q - 8)).
+// One 3-input bit operation (v_bitop3, (S0 & S1) | S2) places two nibbles in
+// the mantissas of two fp16 halves of exponent 1024: a low nibble gives
+// 1024 + q, a high nibble where it stands 1024 + 16 q, so the odd bytes need
+// the only shift. 1024 + q - 1032 and (1024 + 16 q) / 16 - 72 are q - 8
+// exactly; the multiplication by d rounds once.
 __device__ __forceinline__ void weight_operands(u32x2_t w, f16x2_t d2, f16x8_t& lo, f16x8_t& hi) {
-  constexpr uint32_t M = 0x000F000Fu, MAGIC = 0x64006400u;  // fp16 1024 in both halves
+  constexpr uint32_t ML = 0x000F000Fu, MH = 0x00F000F0u, MAGIC = 0x64006400u;  // MAGIC: fp16 1024 in both halves
+  constexpr int OR_AND = 0xEA;  // truth table of (S0 & S1) | S2
   const f16x2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f}, off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t x8 = w.x >> 8, y8 = w.y >> 8;
   uint32_t p[8];
-  p[0] = (w.x & M) | MAGIC;
-  p[1] = ((w.x >> 8) & M) | MAGIC;
-  p[2] = (w.y & M) | MAGIC;
-  p[3] = ((w.y >> 8) & M) | MAGIC;
-  p[4] = ((w.x >> 4) & M) | MAGIC;
-  p[5] = ((w.x >> 12) & M) | MAGIC;
-  p[6] = ((w.y >> 4) & M) | MAGIC;
-  p[7] = ((w.y >> 12) & M) | MAGIC;
+  p[0] = __builtin_amdgcn_bitop3_b32(w.x, ML, MAGIC, OR_AND);
+  p[1] = __builtin_amdgcn_bitop3_b32(x8, ML, MAGIC, OR_AND);
+  p[2] = __builtin_amdgcn_bitop3_b32(w.y, ML, MAGIC, OR_AND);
+  p[3] = __builtin_amdgcn_bitop3_b32(y8, ML, MAGIC, OR_AND);
+  p[4] = __builtin_amdgcn_bitop3_b32(w.x, MH, MAGIC, OR_AND);
+  p[5] = __builtin_amdgcn_bitop3_b32(x8, MH, MAGIC, OR_AND);
+  p[6] = __builtin_amdgcn_bitop3_b32(w.y, MH, MAGIC, OR_AND);
+  p[7] = __builtin_amdgcn_bitop3_b32(y8, MH, MAGIC, OR_AND);
   f16x2_t v[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (as_h2(p[j]) - off) * d2;  // q - 8 exact, one rounding
+  for (int j = 0; j < 4; ++j) v[j] = (as_h2(p[j]) - off) * d2;
+#pragma unroll
+  for (int j = 4; j < 8; ++j) v[j] = __builtin_elementwise_fma(as_h2(p[j]), sixteenth, off16) * d2;
   __builtin_memcpy(&lo, &v[0], 16);
   __builtin_memcpy(&hi, &v[4], 16);
 }
@@ -134,7 +144,7 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >
 // The memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-constexpr int kStages = 3;  // LDS ring: loads run two K steps ahead
+constexpr int kStages = 3;       // LDS ring: loads run two K steps ahead
 constexpr int kSortChunk = 256;  // pairs per chunk of the counting sort
 
 // Shape of a workgroup tile: BM rows x 4 waves x NSUB x 16 features of NMAT
@@ -160,6 +170,7 @@ struct GemmTile {
   static constexpr int D = DA + DB + DS;
   static_assert(DA * 4096 == A_BYTES && DB * 4096 == NMAT * BN_BYTES && DS * 1024 == NMAT * BS_BYTES,
                 "every wave issues whole DMA instructions");
+  static_assert(2 * kStages * STAGE <= 160 * 1024, "two work-groups per CU");
 };
 
 }  // namespace
@@ -294,26 +305,16 @@ __global__ __launch_bounds__(256) void scale_rows_kernel(const float* src, int32
 // MODE 0: gate/up (two matrices, SwiGLU epilogue, writes h as fp16 rows in
 //         operand order); MODE 1: down (one matrix, writes y_pair).
 // NSUB is chosen so every wave holds at most 128 accumulators.
-// Work items (row tile, first feature) come from a list the host orders per
-// expert by feature tile, then row tile: the row tiles that read the same
-// weight columns are neighbours, start together and keep in step, so each
-// weight line is fetched from HBM once. Each XCD (work group id mod 8 of the
-// launch order) gets a contiguous range of the list, so neighbours share an L2.
-template <int BM, int MODE>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
+// NRB (1..RB): the tile's 16-row blocks that hold rows. Blocks past them are
+// left out at compile time (their A rows are still fetched: the DMA count per
+// step is the same for every tile), so the product loop of a step is one
+// straight run in which the A fragments of the next block are read while the
+// current block's MFMAs execute.
+template <int BM, int MODE, int NRB>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* smem, int e, int pos0, int rows, int n0) {
   using C = GemmTile<BM, MODE>;
-  constexpr int NMAT = C::NMAT, RB = C::RB, NSUB = C::NSUB, WN = C::WN, BNW = C::BNW;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * C::STAGE];
-
-  // XCD-contiguous work numbering over the host's work list
-  const int L = blockIdx.x;
-  const int per = a.work_padded / 8;
-  const int W = (L & 7) * per + (L >> 3);
-  if (W >= a.work) return;
-  const int2 item = a.items[W];
-  const int4 tile = a.tiles[item.x];
-  const int e = tile.x, pos0 = tile.y, rows = tile.z;
-  const int n0 = item.y;
+  constexpr int NMAT = C::NMAT, NSUB = C::NSUB, WN = C::WN, BNW = C::BNW;
+  static_assert(NRB >= 1 && NRB <= C::RB, "active row blocks");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4;
   const int K = a.K, N = a.N, nks = K / KS, nkb = K / 32;
@@ -385,13 +386,18 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
       dma4(sbase + ssrc[i] + sstep * (uint32_t)j, S + C::OFF_BS + (wave * C::DS + i) * 256);
   };
 
-  f32x4_t acc[NMAT][NSUB][RB];
+  f32x4_t acc[NMAT][NSUB][NRB];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
     for (int ns = 0; ns < NSUB; ++ns)
 #pragma unroll
-      for (int s = 0; s < RB; ++s) acc[m][ns][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < NRB; ++s) acc[m][ns][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // this lane's A fragment of row block s, half h: row s*16 + lane%16 (row & 7
+  // == lane & 7), logical chunk 4h + g
+  const int a_off = (lane & 15) * (2 * KS);
+  const int a_chunk[2] = {16 * (g ^ (lane & 7)), 16 * ((4 + g) ^ (lane & 7))};
 
   issue(0);
   if (nks > 1) issue(1);
@@ -405,6 +411,9 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     if (j + 2 < nks) issue(j + 2);
     const uint8_t* S = smem + (j % kStages) * C::STAGE;
 
+    f16x8_t av[2][2];
+    av[0][0] = *reinterpret_cast<const f16x8_t*>(S + a_off + a_chunk[0]);
+    av[0][1] = *reinterpret_cast<const f16x8_t*>(S + a_off + a_chunk[1]);
     f16x8_t bop[NMAT][NSUB][2];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
@@ -417,30 +426,28 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
             S + C::OFF_BS + m * C::BS_BYTES + (tscl ? (g >> 1) * BNW * 2 + wn * 2 : wn * 4 + 2 * (g >> 1)));
         weight_operands(w, as_h2(d | (d << 16)), bop[m][ns][0], bop[m][ns][1]);
       }
-    // 16-row blocks past the tile's last row are skipped (their A rows are
-    // still fetched, as the DMA count per step must stay the same)
 #pragma unroll
-    for (int s = 0; s < RB; ++s) {
-      if (s * 16 >= rows) continue;
+    for (int s = 0; s < NRB; ++s) {
+      if (s + 1 < NRB) {  // next block's fragments, read while this block's MFMAs run
+        const uint8_t* An = S + (s + 1) * 16 * (2 * KS) + a_off;
+        av[(s + 1) & 1][0] = *reinterpret_cast<const f16x8_t*>(An + a_chunk[0]);
+        av[(s + 1) & 1][1] = *reinterpret_cast<const f16x8_t*>(An + a_chunk[1]);
+      }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // row s*16 + lane%16 (row & 7 == lane & 7), logical chunk 4h + g
-        const f16x8_t av = *reinterpret_cast<const f16x8_t*>(S + (s * 16 + (lane & 15)) * (2 * KS) +
-                                                             16 * ((4 * h + g) ^ (lane & 7)));
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
           for (int ns = 0; ns < NSUB; ++ns)
-            acc[m][ns][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bop[m][ns][h], acc[m][ns][s], 0, 0, 0);
-      }
+            acc[m][ns][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[s & 1][h], bop[m][ns][h], acc[m][ns][s], 0, 0, 0);
     }
   }
 
   // epilogue: lane holds rows s*16 + g*4 + i of feature n0 + wave*WN + ns*16 + lane%16.
   // Row scale: the token's activations entered as x * 2^sx
-  int sx[RB][4];
+  int sx[NRB][4];
 #pragma unroll
-  for (int s = 0; s < RB; ++s)
+  for (int s = 0; s < NRB; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = s * 16 + g * 4 + i;
@@ -454,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     if (MODE == 0) {
       const int64_t col = (bn & ~(KS - 1)) + step_pos(bn & (KS - 1));
 #pragma unroll
-      for (int s = 0; s < RB; ++s)
+      for (int s = 0; s < NRB; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = s * 16 + g * 4 + i;
@@ -468,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
         }
     } else {
 #pragma unroll
-      for (int s = 0; s < RB; ++s)
+      for (int s = 0; s < NRB; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = s * 16 + g * 4 + i;
@@ -477,6 +484,39 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
     }
   }
   if (MODE == 0 && __ballot(bad) != 0 && lane == 0) atomicOr(a.range_flag, 1u);
+}
+
+// the tile body for the tile's count of active 16-row blocks, nrb in 1..N
+template <int BM, int MODE, int N>
+__device__ __forceinline__ void gemm_tile_rows(int nrb, const GemmArgs& a, uint8_t* smem, int e, int pos0, int rows,
+                                               int n0) {
+  if constexpr (N > 1) {
+    if (nrb < N) {
+      gemm_tile_rows<BM, MODE, N - 1>(nrb, a, smem, e, pos0, rows, n0);
+      return;
+    }
+  }
+  gemm_tile<BM, MODE, N>(a, smem, e, pos0, rows, n0);
+}
+
+// Work items (row tile, first feature) come from a list the host orders per
+// expert by feature tile, then row tile: the row tiles that read the same
+// weight columns are neighbours, start together and keep in step, so each
+// weight line is fetched from HBM once. Each XCD (work group id mod 8 of the
+// launch order) gets a contiguous range of the list, so neighbours share an L2.
+template <int BM, int MODE>
+__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
+  using C = GemmTile<BM, MODE>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * C::STAGE];
+  // XCD-contiguous work numbering over the host's work list
+  const int L = blockIdx.x;
+  const int per = a.work_padded / 8;
+  const int W = (L & 7) * per + (L >> 3);
+  if (W >= a.work) return;
+  const int2 item = a.items[W];
+  const int4 tile = a.tiles[item.x];
+  const int rows = tile.z;
+  gemm_tile_rows<BM, MODE, C::RB>((rows + 15) / 16, a, smem, tile.x, tile.y, rows, item.y);
 }
 
 // Scale planes [rows][K/32] (fp16) of the experts with eaddr[e] set ->
