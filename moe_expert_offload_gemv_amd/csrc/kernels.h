@@ -222,9 +222,8 @@ struct GemmArgs {
   ExpertLayout lay;
   _Float16* h16;                // gate/up output: h rows [P][N] fp16 in operand order
   float* y;                     // down output: y_pair [P][N]
-  const uint16_t* sclT;         // 64-row tiles: the pass's block scales transposed, expert e at
-  int64_t sclT_per_expert;      //   sclT + e * sclT_per_expert: gate [H/32][F], up [H/32][F], down
-                                //   [F/32][H]; 128-row tiles: nullptr (scales from the expert's planes)
+  const uint16_t* sclT;         // the pass's block scales transposed, expert e at sclT + e *
+  int64_t sclT_per_expert;      //   sclT_per_expert: gate [H/32][F], up [H/32][F], down [F/32][H]
   const int32_t* perm;          // [P] sorted position -> pair; token of a pair = pair / perm_div
   int32_t perm_div;
   const int32_t* sig;           // [T] exponent s of each token's row scale 2^s (scale_rows)

@@ -333,11 +333,9 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   PF_HIP(c, moe::launch_scale_rows(x, T, H, p->x16, p->sig, s));
   PF_HIP(c, hipMemsetAsync(p->range_flag, 0, sizeof(uint32_t), s));
 
-  // 6. per group (a chunk once its copy has landed): short tiles (few rows
-  // per expert) are bound by weight fetches, so their GEMMs get the block
-  // scales of the group's experts transposed, each K step reading whole
-  // lines of them; then the grouped gate/up and down GEMMs
-  const bool tscl = bm == 64;
+  // 6. per group (a chunk once its copy has landed): the block scales of the
+  // group's experts transposed, so each K step of a GEMM reads whole lines of
+  // them; then the grouped gate/up and down GEMMs
   bool launched[kMaxGroups][kTimed] = {};
   moe::GemmArgs g{};
   g.a16 = p->x16, g.arow = p->perm, g.arow_div = k;
@@ -345,7 +343,7 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
   g.K = H, g.N = F;
   g.lay = c->lay;
   g.h16 = p->h16;
-  g.sclT = tscl ? p->sclT : nullptr;
+  g.sclT = p->sclT;
   g.sclT_per_expert = moe::sclT_elements(c->lay);
   g.perm = p->perm, g.perm_div = k, g.sig = p->sig, g.range_flag = p->range_flag;
   moe::GemmArgs d = g;
@@ -363,9 +361,8 @@ extern "C" int moe_prefill(moe_ctx* c, int32_t layer, int32_t n_tokens, const fl
       }
       return l;
     };
-    if (tscl)
-      PF_HIP(c, moe::launch_transpose_scales(p->eaddr, p->stage + g_first[gi], (int32_t)g_count[gi], c->lay, p->sclT,
-                                             timer(0)));
+    PF_HIP(c, moe::launch_transpose_scales(p->eaddr, p->stage + g_first[gi], (int32_t)g_count[gi], c->lay, p->sclT,
+                                           timer(0)));
     const int64_t gu0 = item_first[0][gi], gu1 = item_first[0][gi + 1];
     const int64_t dn0 = item_first[1][gi], dn1 = item_first[1][gi + 1];
     g.items = p->items[0] + gu0;

@@ -40,13 +40,11 @@
 //
 // Block scales: a scale line of the expert blob holds 32 K steps of one
 // column, so a K step reading 4 B of it leaves the line to be fetched again
-// for each step once other traffic has evicted it. A pass of short tiles
-// (64 rows, chosen when experts have few rows: bound by these fetches)
-// therefore first transposes the scale planes of its experts
-// (transpose_scales_kernel) into [K/32][columns]: a K step's scales of a
-// column tile are then one contiguous run, every fetched line used at once.
-// Passes of 128-row tiles (bound by the matrix cores) read the planes as they
-// are. The layout is fixed per tile height at compile time.
+// for each step once other traffic has evicted it, and costs one memory
+// request per column. A pass therefore first transposes the scale planes of
+// its experts (transpose_scales_kernel) into [K/32][columns]: a K step's
+// scales of a column tile are then one contiguous run, every fetched line
+// used at once.
 //
 // Staging: every operand byte of a K step (the A rows, the weight nibbles,
 // the block scales) travels global -> LDS by the LDS-DMA form of the global
@@ -345,34 +343,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* smem, int 
     col = col < N ? col : 0;
     bsrc[i] = (uint32_t)(nib_plane[m] + ((int64_t)col * nkb + (lane >> 5)) * 16);
   }
-  // scales. Transposed planes (64-row tiles, [K/32][N] per matrix): instruction
-  // q covers features 128 c .. +127 of block b of the step for matrix m, with
-  // q = (2 m + b) * (BNW / 128) + c; lane l fetches features 2 l, 2 l + 1; the
-  // LDS part is [matrix][block][feature]. The expert's own planes: instruction
-  // q covers features 64 (q % (BNW/64)) .. +63 of matrix q / (BNW/64); lane l
-  // fetches the two scales of feature l; the LDS part is [matrix][feature][block].
-  // Features past N fetch feature 0 and are never stored.
-  constexpr bool tscl = BM == 64;  // the host transposes the scales for passes of 64-row tiles
-  const uint8_t* sbase = tscl ? reinterpret_cast<const uint8_t*>(a.sclT + (int64_t)e * a.sclT_per_expert) : base;
-  const uint32_t sstep = tscl ? 4u * (uint32_t)N : 4u;  // bytes per K step
+  // scales, from the pass's transposed planes ([K/32][N] per matrix):
+  // instruction q covers features 128 c .. +127 of block b of the step for
+  // matrix m, with q = (2 m + b) * (BNW / 128) + c; lane l fetches features
+  // 2 l, 2 l + 1; the LDS part is [matrix][block][feature]. Features past N
+  // fetch feature 0 and are never stored.
+  const uint8_t* sbase = reinterpret_cast<const uint8_t*>(a.sclT + (int64_t)e * a.sclT_per_expert);
+  const uint32_t sstep = 4u * (uint32_t)N;  // bytes per K step
   const int64_t sclT_plane[2] = {MODE == 1 ? 2 * (int64_t)a.lay.F * (a.lay.H / 32) : 0,
                                  (int64_t)a.lay.F * (a.lay.H / 32)};
-  const int64_t scl_plane[2] = {MODE == 1 ? a.lay.down_scl : a.lay.gate_scl, a.lay.up_scl};
   uint32_t ssrc[C::DS];
 #pragma unroll
   for (int i = 0; i < C::DS; ++i) {
     const int q = wave * C::DS + i;
-    if (tscl) {
-      const int m = q / (2 * (BNW / 128)), bq = (q / (BNW / 128)) % 2;
-      int col = n0 + 128 * (q % (BNW / 128)) + 2 * lane;
-      col = col < N ? col : 0;
-      ssrc[i] = (uint32_t)((sclT_plane[m] + (int64_t)bq * N + col) * 2);
-    } else {
-      const int m = q / (BNW / 64);
-      int col = n0 + 64 * (q % (BNW / 64)) + lane;
-      col = col < N ? col : 0;
-      ssrc[i] = (uint32_t)(scl_plane[m] + (int64_t)col * nkb * 2);
-    }
+    const int m = q / (2 * (BNW / 128)), bq = (q / (BNW / 128)) % 2;
+    int col = n0 + 128 * (q % (BNW / 128)) + 2 * lane;
+    col = col < N ? col : 0;
+    ssrc[i] = (uint32_t)((sclT_plane[m] + (int64_t)bq * N + col) * 2);
   }
 
   auto issue = [&](int j) __attribute__((always_inline)) {
@@ -423,7 +410,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, uint8_t* smem, int 
         const u32x2_t w = *reinterpret_cast<const u32x2_t*>(S + C::OFF_BN + m * C::BN_BYTES + (wn >> 5) * 1024 +
                                                             ((wn & 31) + 32 * (g >> 1)) * 16 + 8 * (g & 1));
         const uint32_t d = *reinterpret_cast<const uint16_t*>(
-            S + C::OFF_BS + m * C::BS_BYTES + (tscl ? (g >> 1) * BNW * 2 + wn * 2 : wn * 4 + 2 * (g >> 1)));
+            S + C::OFF_BS + m * C::BS_BYTES + (g >> 1) * BNW * 2 + wn * 2);
         weight_operands(w, as_h2(d | (d << 16)), bop[m][ns][0], bop[m][ns][1]);
       }
 #pragma unroll
@@ -520,13 +507,16 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
 }
 
 // Scale planes [rows][K/32] (fp16) of the experts with eaddr[e] set ->
-// [K/32][rows] at out + e * per. A work-group moves 64 rows: it reads them
-// whole (one contiguous run), then writes 128-byte row pieces of the
-// transposed plane, 128 blocks of K at a time. grid = (row chunks of the
+// [K/32][rows] at out + e * per. A work-group moves 64 rows, 128 blocks of K
+// at a time: it reads them (one contiguous run per row), writes them
+// transposed into LDS, then writes 128-byte pieces of the transposed plane.
+// When the rows are whole multiples of 16 bytes (K a multiple of 256) both
+// global sides move 16 bytes per lane; otherwise 2. grid = (row chunks of the
 // largest matrix, 3 matrices, E).
 __global__ __launch_bounds__(256) void transpose_scales_kernel(const uint8_t* const* eaddr, const int32_t* experts,
                                                                ExpertLayout lay, uint16_t* out, int64_t per) {
-  __shared__ uint16_t tile[64][129];  // odd row stride (in 16-bit words): the column reads spread over banks
+  constexpr int TS = 64 + 8;  // LDS row of the transposed tile (u16): 144 bytes, 16-byte aligned
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * TS];  // [block][row]
   const int e = experts[blockIdx.z];
   const uint8_t* base = eaddr[e];
   if (!base) return;
@@ -539,16 +529,37 @@ __global__ __launch_bounds__(256) void transpose_scales_kernel(const uint8_t* co
                                                                                             : lay.down_scl)) +
                         (int64_t)r0 * KB;
   uint16_t* dst = out + (int64_t)e * per + (int64_t)m * lay.F * (lay.H / 32) + r0;
+  const bool vec = KB % 8 == 0 && nr == 64 && ((uintptr_t)src & 15) == 0 && ((uintptr_t)dst & 15) == 0 && R % 8 == 0;
   for (int k0 = 0; k0 < KB; k0 += 128) {
     const int nk = KB - k0 < 128 ? KB - k0 : 128;
-    for (int i = threadIdx.x; i < nr * nk; i += 256) {
-      const int r = i / nk, kb = i - r * nk;
-      tile[r][kb] = src[(int64_t)r * KB + k0 + kb];
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < nk * 64; i += 256) {
-      const int kb = i >> 6, r = i & 63;
-      if (r < nr) dst[(int64_t)(k0 + kb) * R + r] = tile[r][kb];
+    if (vec) {
+      const int cpr = nk / 8;  // 16-byte pieces per row
+      for (int c = threadIdx.x; c < 64 * cpr; c += 256) {
+        const int r = c / cpr, kb = 8 * (c - r * cpr);
+        const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)r * KB + k0 + kb);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          tile[(kb + 2 * i) * TS + r] = (uint16_t)(w[i] & 0xffffu);
+          tile[(kb + 2 * i + 1) * TS + r] = (uint16_t)(w[i] >> 16);
+        }
+      }
+      __syncthreads();
+      for (int c = threadIdx.x; c < nk * 8; c += 256) {
+        const int kb = c >> 3, rc = c & 7;
+        *reinterpret_cast<uint4*>(dst + (int64_t)(k0 + kb) * R + 8 * rc) =
+            *reinterpret_cast<const uint4*>(tile + kb * TS + 8 * rc);
+      }
+    } else {
+      for (int i = threadIdx.x; i < nr * nk; i += 256) {
+        const int r = i / nk, kb = i - r * nk;
+        tile[kb * TS + r] = src[(int64_t)r * KB + k0 + kb];
+      }
+      __syncthreads();
+      for (int i = threadIdx.x; i < nk * 64; i += 256) {
+        const int kb = i >> 6, r = i & 63;
+        if (r < nr) dst[(int64_t)(k0 + kb) * R + r] = tile[kb * TS + r];
+      }
     }
     __syncthreads();
   }
@@ -662,7 +673,7 @@ int gemm_features_per_tile(int mode, int bm) {
 }
 hipError_t launch_grouped_gemm(GemmArgs a, int mode, int bm, int n_items, const Launch& l) {
   if (a.K % KS || a.N % KS || n_items <= 0 || !a.items || (bm != 64 && bm != 128) || (mode != 0 && mode != 1) ||
-      (bm == 64) != (a.sclT != nullptr))  // 64-row tiles read the transposed scales, 128-row tiles the planes
+      !a.sclT)
     return hipErrorInvalidValue;
   a.work = n_items;
   a.work_padded = (a.work + 7) / 8 * 8;
