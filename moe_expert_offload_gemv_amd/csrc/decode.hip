@@ -84,9 +84,12 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
   const int E = r.E;
   const bool may_capture = p < r.capture_picks;
 
-  {
+  if (wave != 0) {
+    // waves 1-3 stage the activations; wave 0 goes straight to the routing
+    // (behind these loads and their LDS writes its routing loads would wait
+    // out a memory round trip first)
     const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)t * a.H);
-    for (int q = threadIdx.x; q < KB * 8; q += 256) {
+    for (int q = threadIdx.x - 64; q < KB * 8; q += 192) {
       const int b = q >> 3, c = q & 7;
       s_x[b * 8 + (c ^ (b & 7))] = src[q];
     }
@@ -99,12 +102,30 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
     float z[NJ];
     int32_t tb[NJ];
     uint32_t lm[NJ];
+    // the loads are issued without per-lane branches (index clamped into
+    // the layer's experts, the value dropped afterwards), so none waits
+    // behind one; the last-miss row exists only when picks may be captured
+    // (a work-group-uniform condition)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int e = lane + 64 * j;
-      z[j] = e < E ? r.logits[(int64_t)t * E + e] : 0.f;
-      tb[j] = e < E ? r.tbl[e] : -1;
-      lm[j] = (may_capture && e < E) ? r.last_miss[e] : 0u;
+      const int e = lane + 64 * j, ec = e < E ? e : E - 1;
+      z[j] = r.logits[(int64_t)t * E + ec];
+      tb[j] = r.tbl[ec];
+      lm[j] = 0u;
+    }
+    if (may_capture) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int e = lane + 64 * j;
+        lm[j] = r.last_miss[e < E ? e : E - 1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const bool in = lane + 64 * j < E;
+      z[j] = in ? z[j] : 0.f;
+      tb[j] = in ? tb[j] : -1;
+      lm[j] = in ? lm[j] : 0u;
     }
     static_assert(NJ == 8, "the fused routing holds 8 experts per lane");
     uint32_t v[NJ];

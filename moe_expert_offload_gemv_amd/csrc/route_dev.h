@@ -126,7 +126,7 @@ __device__ __forceinline__ void wave_topk(const float (&z)[NJ], int E, int round
 // order bits (Batcher's odd-even merge sort, 19 compare-exchanges), then six
 // butterfly steps each merge a lane's list with a partner's from the other
 // half of a group twice the size (lane ^ 1, ^ 2, the mirror within 8 and
-// within 16 lanes, ^ 16, ^ 32): the elementwise max of one sorted list and
+// within 16 lanes, ^ 16, ^ 32; the last two by half-swap instructions): the elementwise max of one sorted list and
 // the other reversed holds the 8 largest of both as a bitonic sequence,
 // which three half-cleaner stages sort. Every lane ends with the 8 largest
 // order bits of the wave, descending, ties repeated.
@@ -157,10 +157,24 @@ __device__ __forceinline__ void merge8_dpp(uint32_t (&t)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) t[i] = c[i];
 }
-__device__ __forceinline__ void merge8_xor(uint32_t (&t)[8], int mask) {
+// partner lane ^ 16 or ^ 32 through one half-swap instruction
+// (v_permlane16_swap / v_permlane32_swap: swap the odd 16-lane rows of the
+// first operand with the even rows of the second, or the upper 32 lanes of
+// the first with the lower 32 of the second). With both operands x the first
+// result holds the even rows (lower half) twice and the second the odd rows
+// (upper half) twice, so a lane in an even row (lower half) takes its
+// partner's value from the second result, the others from the first.
+template <int MASK>
+__device__ __forceinline__ void merge8_swap(uint32_t (&t)[8]) {
+  static_assert(MASK == 16 || MASK == 32, "half-swap partners");
+  const bool upper = (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & MASK) != 0;
   uint32_t c[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = max(t[i], (uint32_t)__shfl_xor((int)t[7 - i], mask, 64));
+  for (int i = 0; i < 8; ++i) {
+    const auto s = MASK == 32 ? __builtin_amdgcn_permlane32_swap(t[7 - i], t[7 - i], false, false)
+                              : __builtin_amdgcn_permlane16_swap(t[7 - i], t[7 - i], false, false);
+    c[i] = max(t[i], (uint32_t)(upper ? s[0] : s[1]));
+  }
   clean8_desc(c);
 #pragma unroll
   for (int i = 0; i < 8; ++i) t[i] = c[i];
@@ -174,8 +188,8 @@ __device__ __forceinline__ void wave_top8(const uint32_t (&v)[8], uint32_t (&t)[
   merge8_dpp<kDppQuadXor2>(t);
   merge8_dpp<kDppRowHalfMirror>(t);
   merge8_dpp<kDppRowMirror>(t);
-  merge8_xor(t, 16);
-  merge8_xor(t, 32);
+  merge8_swap<16>(t);
+  merge8_swap<32>(t);
 }
 // The expert of pick `rank` (wave-uniform, < 8) and its order bits, from the
 // lane's order bits v and their wave_top8 t. With m = t[rank] and r the
