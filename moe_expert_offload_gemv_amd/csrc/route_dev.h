@@ -148,11 +148,18 @@ __device__ __forceinline__ void clean8_desc(uint32_t (&c)[8]) {
   cas_desc(c[0], c[2]), cas_desc(c[1], c[3]), cas_desc(c[4], c[6]), cas_desc(c[5], c[7]);
   cas_desc(c[0], c[1]), cas_desc(c[2], c[3]), cas_desc(c[4], c[5]), cas_desc(c[6], c[7]);
 }
+// the partner value through a DPP move whose lanes all read (full row and
+// bank masks), with 0 (the identity of unsigned max) as the "old" operand, so
+// the compiler can fold the move into the max as its DPP source
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32_max_src(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
 template <int CTRL>
 __device__ __forceinline__ void merge8_dpp(uint32_t (&t)[8]) {
   uint32_t c[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = max(t[i], dpp32<CTRL>(t[7 - i]));
+  for (int i = 0; i < 8; ++i) c[i] = max(t[i], dpp32_max_src<CTRL>(t[7 - i]));
   clean8_desc(c);
 #pragma unroll
   for (int i = 0; i < 8; ++i) t[i] = c[i];
@@ -206,7 +213,16 @@ __device__ __forceinline__ int top8_expert(const uint32_t (&v)[8], const uint32_
   const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)mv);
   int r = __builtin_amdgcn_readfirstlane(rv);
   int e = 0;
-  if (m != 0) {
+  if (m != 0 && r == 0) {
+    // no equal value ranks ahead of this pick (the usual case): the lowest id
+    // holding m, slots from the highest down so the lowest nonempty slot
+    // decides last (no branches)
+#pragma unroll
+    for (int j = 7; j >= 0; --j) {
+      const uint64_t b = __ballot(v[j] == m);
+      e = b ? 64 * j + (int)__builtin_ctzll(b) : e;
+    }
+  } else if (m != 0) {
     bool found = false;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
