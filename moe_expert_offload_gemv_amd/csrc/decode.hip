@@ -57,7 +57,8 @@ namespace moe {
 using namespace gemv_dev;
 
 // ---------------------------------------------------------------------------
-// routing + lookup + gate/up GEMV + SwiGLU; grid = (row chunks of F, picks).
+// routing + lookup + gate/up GEMV + SwiGLU; grid = (row chunks of F, picks of a
+// token, tokens).
 // Wave 0 of each work-group routes the token and looks the pick up (once per
 // work-group, not per wave: 2048 waves repeating the top-k and the loads of
 // the logits and the table row contended for each CU's scalar unit and
@@ -75,10 +76,20 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
   // the activations, float4 c of block b at 8 b + (c ^ (b & 7)): the
   // staging writes (8 lanes per block) and the slice reads (one block per
   // lane) both hit distinct banks
-  __shared__ float4 s_x[KB * 8];
-  __shared__ int32_t s_pick[3];  // expert, slot (-1: cold), last-miss clock
-  const int p = blockIdx.y;
-  const int t = p / a.k, pick = p - t * a.k;
+  __shared__ float4 s_x[KB * 8 + 1];  // + a spare entry
+  __shared__ int32_t s_pick[3];  // expert, slot (-1: cold), capture (1) or not
+  // the arguments the routing needs, fetched at entry in one scalar round
+  // trip (fetched where first used, the later ones would each add a
+  // dependent round trip ahead of the routing loads)
+  const float* logits = r.logits;
+  const int32_t* tbl = r.tbl;
+  const uint32_t* last_miss = r.last_miss;
+  const Ctrl* ctrl = r.ctrl;
+  asm volatile("" ::"s"(logits), "s"(tbl), "s"(last_miss), "s"(ctrl), "s"(r.E), "s"(a.k), "s"(r.capture_picks),
+               "s"(r.policy), "s"(r.S), "s"(r.window), "s"(r.admit_misses), "s"(r.pub_seq), "s"(r.pub_value),
+               "s"(a.out), "s"(a.x));
+  // grid (row chunks, pick, token): no division for the pick index
+  const int t = blockIdx.z, pick = blockIdx.y, p = t * a.k + pick;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lb = lane % LPR, rg = lane / LPR;
   const int E = r.E;
@@ -88,13 +99,22 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
     // waves 1-3 stage the activations; wave 0 goes straight to the routing
     // (behind these loads and their LDS writes its routing loads would wait
     // out a memory round trip first)
+    // (every load issued, index clamped, before the first LDS write, so the
+    // loads overlap)
     const float4* src = reinterpret_cast<const float4*>(a.x + (int64_t)t * a.H);
-    for (int q = threadIdx.x - 64; q < KB * 8; q += 192) {
-      const int b = q >> 3, c = q & 7;
-      s_x[b * 8 + (c ^ (b & 7))] = src[q];
+    constexpr int NQ = (KB * 8 + 191) / 192;
+    float4 xq[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int q = threadIdx.x - 64 + 192 * i;
+      xq[i] = src[q < KB * 8 ? q : KB * 8 - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {  // lanes past the end write the spare entry
+      const int q = threadIdx.x - 64 + 192 * i, b = q >> 3, c = q & 7;
+      s_x[q < KB * 8 ? b * 8 + (c ^ (b & 7)) : KB * 8] = xq[i];
     }
   }
-  const uint32_t clk = r.ctrl->clock + (uint32_t)t;
   // wave 0 of work-group x = 0 applies the side effects and needs every
   // pick's logit for the weight; the others route up to their own pick
   const bool policy_wave = r.policy && blockIdx.x == 0 && wave == 0;
@@ -109,28 +129,28 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j, ec = e < E ? e : E - 1;
-      z[j] = r.logits[(int64_t)t * E + ec];
-      tb[j] = r.tbl[ec];
+      z[j] = logits[(int64_t)t * E + ec];
+      tb[j] = tbl[ec];
       lm[j] = 0u;
     }
     if (may_capture) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int e = lane + 64 * j;
-        lm[j] = r.last_miss[e < E ? e : E - 1];
+        lm[j] = last_miss[e < E ? e : E - 1];
       }
     }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const bool in = lane + 64 * j < E;
-      z[j] = in ? z[j] : 0.f;
-      tb[j] = in ? tb[j] : -1;
-      lm[j] = in ? lm[j] : 0u;
-    }
+    // the step's clock, loaded behind the routing loads and needed only
+    // once the pick is known
+    const uint32_t clk = ctrl->clock + (uint32_t)t;
     static_assert(NJ == 8, "the fused routing holds 8 experts per lane");
+    // order bits, 0 past the layer's experts (the mask is all ones where
+    // lane + 64 j < E); the table and last-miss values past E are never
+    // read, as every pick is an expert of the layer
     uint32_t v[NJ];
+    const int past = lane - E;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) v[j] = lane + 64 * j < E ? route_dev::order_bits(z[j]) : 0u;
+    for (int j = 0; j < NJ; ++j) v[j] = route_dev::order_bits(z[j]) & (uint32_t)((past + 64 * j) >> 31);
     // lane i < k ends with pick i's order bits (the weight needs them all)
     uint32_t my_bits = 0;
     int e;
@@ -157,11 +177,13 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
     }
     const int slot = __builtin_amdgcn_readlane(slot_l, e & 63);
     const uint32_t prev = (uint32_t)__builtin_amdgcn_readlane((int)lm_l, e & 63);
-    if (lane == 0) s_pick[0] = e, s_pick[1] = slot, s_pick[2] = (int32_t)prev;
+    // the cache step admits a cold pick on its first miss, or on a repeat
+    // inside the window (a repeat earlier in this same step is not seen here)
+    const bool hot = slot >= 0;
+    const bool capture = !hot && may_capture && r.S > 0 &&
+                         (r.admit_misses == 1 || (prev != 0 && clk - prev < (uint32_t)r.window));
+    if (lane == 0) s_pick[0] = e, s_pick[1] = slot, s_pick[2] = capture ? 1 : 0;
     if (policy_wave) {
-      const bool hot = slot >= 0;
-      const bool capture = !hot && may_capture && r.S > 0 &&
-                           (r.admit_misses == 1 || (prev != 0 && clk - prev < (uint32_t)r.window));
       const float wl = route_dev::wave_pick_weight(my_bits, a.k, lane);
       const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), pick));
       if (lane == 0) {
@@ -187,12 +209,8 @@ __global__ __launch_bounds__(256) void gemv_route_gateup_kernel(GemvArgs a, Rout
   __syncthreads();
   const int e = __builtin_amdgcn_readfirstlane(s_pick[0]);
   const int slot = __builtin_amdgcn_readfirstlane(s_pick[1]);
-  const uint32_t prev = (uint32_t)__builtin_amdgcn_readfirstlane(s_pick[2]);
+  const bool capture = __builtin_amdgcn_readfirstlane(s_pick[2]) != 0;
   const bool hot = slot >= 0;
-  // the cache step admits a cold pick on its first miss, or on a repeat
-  // inside the window (a repeat earlier in this same step is not seen here)
-  const bool capture = !hot && may_capture && r.S > 0 &&
-                       (r.admit_misses == 1 || (prev != 0 && clk - prev < (uint32_t)r.window));
   const uint8_t* base = hot ? r.pool + (int64_t)slot * r.expert_bytes : r.host + (int64_t)e * r.expert_bytes;
 
   if (r.pub_seq && blockIdx.x == gridDim.x - 1) {
@@ -660,7 +678,7 @@ template <int LPR, int BPL>
 hipError_t route_gateup_t(const GemvArgs& a, const RouteArgs& r, const Launch& l, int mode) {
   constexpr int ROWS_WG = 4 * kNitGateUp * (64 / LPR);
   // one more work-group per pick hands the pick to the host threads
-  const dim3 grid((a.F + ROWS_WG - 1) / ROWS_WG + (r.pub_seq ? 1 : 0), a.T * a.k);
+  const dim3 grid((a.F + ROWS_WG - 1) / ROWS_WG + (r.pub_seq ? 1 : 0), a.k, a.T);
   if (mode == kOnlyHot)
     return launch(gemv_route_gateup_kernel<LPR, BPL, kNitGateUp, kOnlyHot>, grid, dim3(256), l, a, r);
   if (mode == kOnlyCold)
@@ -730,7 +748,8 @@ hipError_t launch_gemv_gateup(const GemvArgs& a, const Launch& l, int mode) {
   MOE_DISPATCH_GEMV(gateup_t, a.H / 32, a, l, mode);
 }
 hipError_t launch_gemv_route_gateup(const GemvArgs& a, const RouteArgs& r, const Launch& l, int mode) {
-  if (!r.logits || r.E < 1 || r.E > kFusedRouteMaxExperts || a.k < 1 || a.k > 32 || a.k > r.E || a.T < 1)
+  if (!r.logits || r.E < 1 || r.E > kFusedRouteMaxExperts || a.k < 1 || a.k > 32 || a.k > r.E || a.T < 1 ||
+      a.T > 65535)
     return hipErrorInvalidValue;
   MOE_DISPATCH_GEMV(route_gateup_t, a.H / 32, a, l, mode, r);
 }

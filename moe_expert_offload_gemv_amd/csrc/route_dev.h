@@ -36,9 +36,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 // order-preserving bits of a logit: a larger logit gives a larger value, -0
 // counts as +0; 0 stands for "no expert" (past E, or picked already)
 __device__ __forceinline__ uint32_t order_bits(float v) {
-  if (v == 0.0f) v = 0.0f;  // -0 and +0 compare equal
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // v + 0 is +0 for -0 (round to nearest) and v for every other number, so
+  // -0 and +0 get the same bits
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  // negative: every bit flipped; otherwise the sign bit set
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float order_logit(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
