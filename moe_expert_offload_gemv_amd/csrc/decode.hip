@@ -297,10 +297,17 @@ __global__ __launch_bounds__(256) void gemv_down_pick_kernel(GemvArgs a) {
   constexpr int RPW = 64 / LPR;
   constexpr int ROWS_WG = 4 * NIT * RPW;
   const int p = blockIdx.y;
-  if (!wanted<MODE>(a.kind[p])) return;
+  // the arguments in one scalar fetch at entry, then the pick's tag and
+  // expert address in one round trip (the address fetched after the tag
+  // test would be a second one ahead of the weight loads)
+  asm volatile("" ::"s"(a.kind), "s"(a.addr), "s"(a.x), "s"(a.ypick), "s"(a.H), "s"(a.F), "s"(a.lay.down_nib),
+               "s"(a.lay.down_scl));
+  const int kd = a.kind[p];
+  const uint8_t* base = a.addr[p];
+  asm volatile("" ::"v"(kd), "s"(base));
+  if (!wanted<MODE>((uint8_t)kd)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lb = lane % LPR, rg = lane / LPR;
-  const uint8_t* base = a.addr[p];
   const int row0 = blockIdx.x * ROWS_WG + wave * NIT * RPW + rg;
   // the pick's h row in LDS, once per work-group (with LPR < 64 every row
   // group of a wave would load it again), the work-group sharing the copy,
@@ -382,6 +389,11 @@ __global__ __launch_bounds__(64 * kCombineWaves) void gemv_down_combine_kernel(G
   using V = SwizVec<LPR, BPL>;
   constexpr bool kStage = V::KV <= 512;
   __shared__ float4 hsh[kStage ? kCombineWaves : 1][kStage ? V::KV : 1];
+  // the arguments in one scalar fetch at entry (fetched where first used,
+  // a second batch would be a dependent round trip ahead of the picks' tags
+  // and addresses)
+  asm volatile("" ::"s"(a.kind), "s"(a.addr), "s"(a.x), "s"(a.k), "s"(a.H), "s"(a.F), "s"(a.lay.down_nib),
+               "s"(a.lay.down_scl), "s"(a.capture), "s"(a.capture_picks), "s"(a.ypick), "s"(a.w), "s"(a.out));
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row0 = blockIdx.x * ROWS;
