@@ -32,7 +32,7 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 # HBM bytes per launch of the roofline kernel (gemv_route_gateup_kernel<64,1,4,1>, hot picks), from two rocprofv3
 # counter runs (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, scaled by a 1 GiB copy) over launches that served 7.167 hot picks
 # each (16.91 MB algorithmic); the summary and commands are under profiles/. Set to None when the kernel changes.
-ROOFLINE_TRAFFIC = {"bytes_per_launch": 17142170, "algorithmic_bytes_per_launch": 16908288}
+ROOFLINE_TRAFFIC = {"bytes_per_launch": 17120226, "algorithmic_bytes_per_launch": 16908288}
 PCIE_PEAK_GBPS = 64.0       # PCIe Gen5 x16, one direction
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA; fp16 (what the grouped GEMM runs) has the same rate
 METRIC = "MoE-layer decode tokens/s + effective weight GB/s vs HBM/PCIe roofline"
