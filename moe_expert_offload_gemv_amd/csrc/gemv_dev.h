@@ -97,11 +97,13 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 // Loads a cold pick's wave keeps in flight after issuing each row of a
 // RowTile (a row is one nibble and one scale load per block). Hot picks
 // issue every row at once (HBM wants depth); cold picks pace their
-// zero-copy reads row by row. Measured on the 48-layer decode workload, the
-// deeper the pacing the slower the PCIe reads, in cold-only launches too:
-// cold gate/up per layer 41.3 us at 2, 42.2 at 4, 44.0 at 6, 45.5 at 8,
-// 48.0 at 12; unpaced reads also slowed the hot picks sharing the launch.
-constexpr int kColdLoadsInFlight = 2;
+// zero-copy reads row by row. The deeper the pacing the slower the PCIe
+// reads: on the 48-layer decode workload, cold gate/up per layer 41.3 us at
+// 2, 42.2 at 4, 44.0 at 6, 45.5 at 8, 48.0 at 12; with about 8 cold picks
+// per launch (18.9 MB), gate/up 364 us at 2, 326 us (58 GB/s) at 1 and at
+// 0, down + combine 171 us at 2, 164 at 1 and 0. Unpaced reads also slowed
+// the hot picks sharing the launch.
+constexpr int kColdLoadsInFlight = 1;
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // The activation slice of a lane: blocks b_j = lb + LPR*j of a vector of
