@@ -161,6 +161,28 @@ def test_decode_other_shapes_ragged_lanes():
     _run_decode(wl, slots=6, check_every=2)
 
 
+# (E, k, H, F, tokens, slots): every routing path and lane layout the launches choose between
+_SWEEP = [
+    (3, 1, 256, 256, 1, 1),         # the smallest: one pick, one slot, 8 blocks per row (8 lanes x 1)
+    (130, 3, 768, 512, 2, 40),      # E not a multiple of 64; 24 blocks per row (8 lanes x 3)
+    (512, 8, 256, 256, 1, 100),     # the largest E the fused routing takes
+    (64, 8, 1024, 3072, 1, 20),     # down rows of 96 blocks (32 lanes x 3)
+    (33, 8, 512, 1024, 7, 12),      # the largest batch of the fused path
+    (40, 5, 2048, 768, 9, 16),      # a grouped batch with an odd k
+    (700, 4, 256, 256, 1, 100),     # E past the fused routing: the routing kernel
+    (24, 12, 6144, 256, 2, 8),      # k > 8 (top-k by rounds); 192 blocks per row (64 lanes x 3)
+    (20, 6, 1024, 1536, 12, 8),     # a grouped batch on the matrix cores, 72 picks over 20 experts
+]
+
+
+@pytest.mark.parametrize("i", range(len(_SWEEP)))
+def test_decode_shape_sweep(i):
+    E, k, H, F, T, slots = _SWEEP[i]
+    wl = Workload(f"sweep-e{E}k{k}-h{H}f{F}-b{T}", 300 + i, 2, E, k, H, F, tokens=T, steps=4, zipf_s=1.0,
+                  slots=slots)
+    _run_decode(wl, slots=slots, check_every=1)
+
+
 def test_forced_cold_every_pick_over_pcie():
     wl = Workload("decode-e32k8-h2048f1024-l2-b2-cold", 104, 2, 32, 8, 2048, 1024, tokens=2, steps=6, zipf_s=1.1)
     _run_decode(wl, slots=0, check_every=2)

@@ -61,6 +61,24 @@ def test_prefill_small_ragged_tiles_with_staging():
     print("err", err, prof)
 
 
+# (E, k, H, F, tokens, slots): ragged tiles, the routing paths, the lane layouts of the decode kernels the
+# context shares
+_SWEEP = [
+    (3, 1, 256, 256, 1, 1),       # one token, one pick
+    (130, 3, 768, 512, 65, 40),   # E not a multiple of 64, a 65-row expert at most
+    (64, 8, 1024, 3072, 20, 20),  # K of the down GEMM 3072
+    (24, 12, 6144, 256, 33, 8),   # k > 8, K of the gate/up GEMM 6144
+    (700, 4, 256, 256, 50, 100),  # E past the fused routing
+]
+
+
+@pytest.mark.parametrize("i", range(len(_SWEEP)))
+def test_prefill_shape_sweep(i):
+    E, k, H, F, T, slots = _SWEEP[i]
+    wl = Workload(f"pf-sweep-e{E}k{k}-h{H}f{F}-t{T}", 320 + i, 1, E, k, H, F, tokens=T, zipf_s=1.0)
+    _prefill_check(wl, slots=slots)
+
+
 def test_prefill_many_tiles_per_expert():
     wl = Workload("prefill-e8k2-h256f512-t1000", 202, 1, 8, 2, 256, 512, tokens=1000, zipf_s=1.1)
     err, prof = _prefill_check(wl, slots=3, sample=200)
