@@ -153,7 +153,12 @@ template <int BM, int MODE>
 struct GemmTile {
   static constexpr int NMAT = MODE == 0 ? 2 : 1;
   static constexpr int RB = BM / 16;
-  static constexpr int NSUB = 32 / (RB * NMAT) < 4 ? 32 / (RB * NMAT) : 4;
+  // at most 128 accumulators per wave; the 64-row gate/up tile takes half
+  // that (128 features of each matrix), so that its registers and LDS allow
+  // three work-groups per CU: its gate/up GEMM of the 4096-token decode-shape
+  // pass took 0.68 ms at 256 features and two per CU, 0.62 ms now
+  static constexpr int NSUB = (BM == 64 && MODE == 0) ? 2 : (32 / (RB * NMAT) < 4 ? 32 / (RB * NMAT) : 4);
+  static constexpr int WGS_PER_CU = BM == 64 ? 3 : 2;
   static constexpr int WN = 16 * NSUB;
   static constexpr int BNW = 4 * WN;
   static constexpr int A_BYTES = BM * 2 * KS;
@@ -168,7 +173,7 @@ struct GemmTile {
   static constexpr int D = DA + DB + DS;
   static_assert(DA * 4096 == A_BYTES && DB * 4096 == NMAT * BN_BYTES && DS * 1024 == NMAT * BS_BYTES,
                 "every wave issues whole DMA instructions");
-  static_assert(2 * kStages * STAGE <= 160 * 1024, "two work-groups per CU");
+  static_assert(WGS_PER_CU * kStages * STAGE <= 160 * 1024, "the work-groups per CU fit in LDS");
 };
 
 }  // namespace
@@ -302,7 +307,8 @@ __global__ __launch_bounds__(256) void scale_rows_kernel(const float* src, int32
 // covers all BM rows, so each weight is converted once per workgroup.
 // MODE 0: gate/up (two matrices, SwiGLU epilogue, writes h as fp16 rows in
 //         operand order); MODE 1: down (one matrix, writes y_pair).
-// NSUB is chosen so every wave holds at most 128 accumulators.
+// NSUB: every wave holds at most 128 accumulators (64 in the 64-row gate/up
+// tile, see GemmTile).
 // NRB (1..RB): the tile's 16-row blocks that hold rows. Blocks past them are
 // left out at compile time (their A rows are still fetched: the DMA count per
 // step is the same for every tile), so the product loop of a step is one
@@ -492,7 +498,7 @@ __device__ __forceinline__ void gemm_tile_rows(int nrb, const GemmArgs& a, uint8
 // weight line is fetched from HBM once. Each XCD (work group id mod 8 of the
 // launch order) gets a contiguous range of the list, so neighbours share an L2.
 template <int BM, int MODE>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, (GemmTile<BM, MODE>::WGS_PER_CU)) void grouped_gemm_kernel(GemmArgs a) {
   using C = GemmTile<BM, MODE>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * C::STAGE];
   // XCD-contiguous work numbering over the host's work list
