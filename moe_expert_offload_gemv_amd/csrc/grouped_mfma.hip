@@ -126,22 +126,18 @@ struct AStep {
   u32x4_t a[2];  // the two 16-byte pieces of a step's A rows this lane stages
 };
 
-// bytes [off, off + n) of an expert blob from src to dst, by the whole
-// work-group: 16-byte pieces, four in flight per thread (n and off multiples
-// of 16)
+// Copies bytes [off, off + n) of src to dst, cooperatively in one
+// work-group: 16-byte pieces, one in flight per thread (n and off multiples
+// of 16). Fewer reads in flight cross PCIe faster here: with about one cold
+// expert per layer (its 24 work-groups copying at once) the large model's
+// batch-32 step took 22.3 ms at 8 pieces per thread in flight, 21.7 at 4,
+// 21.4 at 2 and 21.2 at 1; 128 or 64 copying threads per work-group instead
+// of 256 took 23.1 and 31.3 ms.
 __device__ __forceinline__ void stage_run(const uint8_t* src, uint8_t* dst, int64_t off, int64_t n) {
   const uint4* s = reinterpret_cast<const uint4*>(src + off);
   uint4* d = reinterpret_cast<uint4*>(dst + off);
   const int64_t n16 = n / 16;
-  for (int64_t i = threadIdx.x; i < n16; i += 4 * 256) {
-    const int64_t j1 = i + 256 < n16 ? i + 256 : i, j2 = i + 512 < n16 ? i + 512 : i,
-                  j3 = i + 768 < n16 ? i + 768 : i;  // past the run: piece i again (stored once)
-    const uint4 v0 = s[i], v1 = s[j1], v2 = s[j2], v3 = s[j3];
-    d[i] = v0;
-    if (j1 != i) d[j1] = v1;
-    if (j2 != i) d[j2] = v2;
-    if (j3 != i) d[j3] = v3;
-  }
+  for (int64_t i = threadIdx.x; i < n16; i += 256) d[i] = s[i];
 }
 
 // Each lane group's value of x in every lane of its 16-lane column: out[g]
