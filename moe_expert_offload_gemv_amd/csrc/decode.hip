@@ -3,7 +3,7 @@
 //   gemv_route_gateup_kernel
 //                         with logits given (E <= 512): wave 0 of every
 //                         work-group routes the token (top-k, slot-table
-//                         lookup) while the work-group stages the activations
+//                         lookup) while waves 1-3 stage the activations
 //                         in LDS, then all waves run the gate/up GEMV
 //                         below; one wave per pick applies the
 //                         lookup's side effects (stamp, pick record, count)
@@ -62,8 +62,9 @@ using namespace gemv_dev;
 // Wave 0 of each work-group routes the token and looks the pick up (once per
 // work-group, not per wave: 2048 waves repeating the top-k and the loads of
 // the logits and the table row contended for each CU's scalar unit and
-// memory pipeline) while all four waves stage the token's activations in
-// LDS; the pick reaches the other waves through LDS.
+// memory pipeline) while waves 1-3 stage the token's activations in LDS;
+// the pick, its slot and the capture decision reach the other waves through
+// LDS.
 // r.policy = 1: wave 0 of work-group x = 0 of each pick applies the pick's
 // side effects (the same as route_kernel's); 0: none (a second launch of the
 // same step, in the timing split).
