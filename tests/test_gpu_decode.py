@@ -172,6 +172,8 @@ _SWEEP = [
     (700, 4, 256, 256, 1, 100),     # E past the fused routing: the routing kernel
     (24, 12, 6144, 256, 2, 8),      # k > 8 (top-k by rounds); 192 blocks per row (64 lanes x 3)
     (20, 6, 1024, 1536, 12, 8),     # a grouped batch on the matrix cores, 72 picks over 20 experts
+    (8, 8, 512, 512, 3, 4),         # k = E: every expert picked by every token
+    (64, 4, 512, 512, 256, 16),     # the largest batch a context takes (grouped, 1024 picks)
 ]
 
 

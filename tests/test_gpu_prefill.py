@@ -69,6 +69,7 @@ _SWEEP = [
     (64, 8, 1024, 3072, 20, 20),  # K of the down GEMM 3072
     (24, 12, 6144, 256, 33, 8),   # k > 8, K of the gate/up GEMM 6144
     (700, 4, 256, 256, 50, 100),  # E past the fused routing
+    (8, 8, 512, 512, 40, 4),      # k = E: every expert picked by every token
 ]
 
 
